@@ -1,0 +1,283 @@
+"""CPU oracle for the column-sparse cross-step delta.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or call anything in this package.
+The product path (``dynamic_column_sparse_amd`` and its HIP library) never imports
+it and shares no code with it.
+
+Source of the method: "Chipmunk: Training-Free Acceleration of Diffusion
+Transformers with Dynamic Column-Sparse Deltas" (Silveria, Govande, Fu; Together AI
+research post, 2025), called "the Chipmunk post" below.  Its section "Activation
+Deltas Across Diffusion Steps are Very Sparse" gives
+
+* the two ops: attention ``softmax(Q K^T) V`` and MLP ``gelu(x W1) W2``;
+* the reading of each as a linear combination of value vectors (rows of V for
+  attention, rows of W2 plus one static bias vector for the MLP);
+* the cache of value vectors and scalar coefficients, with a per-step choice of
+  which ones to recompute;
+* the delta reformulation: a dense step n equals "remove all of step n-1's output
+  vectors from the output cache and add all of step n's"; the sparse step replaces
+  only a subset (single hidden units / single keys) and keeps the rest.
+
+The row-block granularity (128 tokens), top-k per block, GELU in its tanh form and
+the cached attention state (row max, numerator, denominator) are the workloads'
+operational definition of that method.
+
+Arithmetic is float64 throughout.  Values the kernels store in bfloat16 (inputs,
+weights, the MLP activation cache) are rounded to bf16 (nearest, ties to even) at
+exactly those storage points, so both sides start from the same bits.  Scores are
+handed to top-k as float32, the precision the kernels rank in.
+
+Readings of points the post leaves open (each is listed with its reason in the
+design notes of this repository):
+  R1 MLP score = per-block column L1 of (A_new - A_cache) at the latest dense step
+     (cache starts at zero).
+  R2 attention score = per-block key probability mass sum_i p_ij / den_i at the
+     dense refresh.
+  R3 S is fixed from a refresh to the next; the attention "old" S-part is the
+     refresh step's, so the refresh stores num_rest / den_rest.
+  R4 top-k order: score descending, then index ascending; -0 == +0; NaN lowest;
+     output ascending.
+  R6 softmax scale 1/sqrt(head_dim).
+  R8 D is the exact difference of the stored bf16 values (no rounding of D here).
+  R9 a partial last row block is scored over its real rows only.
+  R10 sparse attention steps keep the refresh-step row max (no re-normalisation).
+
+Parity pins for every function live in ``tests/test_oracle_*.py``.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+ROW_BLOCK = 128
+
+
+# --------------------------------------------------------------------------- #
+# Storage rounding
+# --------------------------------------------------------------------------- #
+def bf16_round(x) -> np.ndarray:
+    """Nearest bfloat16 value of each element (ties to even), returned as float64.
+
+    bfloat16 = 1 sign, 8 exponent, 7 stored mantissa bits.  Normal numbers keep 8
+    significant bits; below 2**-126 the spacing is 2**-133 (subnormals); a result
+    at or above 2**128 overflows to infinity.  NaN and infinities pass through.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    mant, expo = np.frexp(x)                      # x = mant * 2**expo, 0.5 <= |mant| < 1
+    r = np.ldexp(np.rint(np.ldexp(mant, 8)), expo - 8)   # np.rint rounds half to even
+    tiny = np.abs(x) < 2.0 ** -126
+    r = np.where(tiny, np.ldexp(np.rint(np.ldexp(x, 133)), -133), r)
+    r = np.where(np.abs(r) >= 2.0 ** 128, np.copysign(np.inf, x), r)
+    return np.where(np.isfinite(x), r, x)
+
+
+def bf16_bits(x) -> np.ndarray:
+    """bf16 bit patterns (uint16) of ``bf16_round(x)``."""
+    v = bf16_round(x).astype(np.float32)          # exact: every bf16 value is an fp32 value
+    return (v.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def from_bf16_bits(b) -> np.ndarray:
+    """float64 values of bf16 bit patterns."""
+    u = np.asarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    with np.errstate(invalid="ignore"):
+        return u.view(np.float32).astype(np.float64)
+
+
+# --------------------------------------------------------------------------- #
+# Non-linearity
+# --------------------------------------------------------------------------- #
+def gelu_tanh(z) -> np.ndarray:
+    """GELU in its tanh form (Hendrycks & Gimpel 2016):
+    0.5 z (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3))).
+
+    The Chipmunk post writes the MLP as gelu(x W1) W2; the workloads name the tanh
+    form.
+    """
+    z = np.asarray(z, dtype=np.float64)
+    c = np.sqrt(2.0 / np.pi)
+    return 0.5 * z * (1.0 + np.tanh(c * (z + 0.044715 * z * z * z)))
+
+
+def _blocks(n: int):
+    for b in range((n + ROW_BLOCK - 1) // ROW_BLOCK):
+        r0 = b * ROW_BLOCK
+        yield b, r0, min(n, r0 + ROW_BLOCK)
+
+
+# --------------------------------------------------------------------------- #
+# Sparsity identification
+# --------------------------------------------------------------------------- #
+def identify_topk(score, k: int) -> np.ndarray:
+    """Per row, the k columns to recompute: largest score first, ties to the lower
+    column index; returned ascending, int32 [rows, k].
+
+    The post says each step chooses which vectors to recompute; the workloads fix
+    the choice as top-k per 128-token block.  Ranking is on float32 values (the
+    kernels' precision), -0 equals +0, NaN ranks below everything, +inf above
+    every finite value.
+    """
+    s = np.asarray(score, dtype=np.float32)
+    if s.ndim != 2:
+        raise ValueError("score must be 2-D [rows, cols]")
+    rows, cols = s.shape
+    if not 0 <= k <= cols:
+        raise ValueError("k out of range")
+    out = np.empty((rows, k), dtype=np.int32)
+    col = np.arange(cols)
+    for r in range(rows):
+        v = s[r].astype(np.float64)
+        nan = np.isnan(v)
+        v = np.where(nan, 0.0, v) + 0.0             # + 0.0 maps -0 to +0
+        order = np.lexsort((col, -v, nan))          # NaN last, then score desc, then index asc
+        out[r] = np.sort(order[:k])
+    return out
+
+
+# --------------------------------------------------------------------------- #
+# MLP
+# --------------------------------------------------------------------------- #
+def mlp_dense(x, w1t, b1, w2, b2, a_old):
+    """Dense refresh step of the MLP: the "normal dense forward pass" that fills
+    the caches (Chipmunk post, Activation Deltas section).
+
+    x [n,d] (bf16 values), w1t [h,d] (row j = hidden unit j's input weights),
+    w2 [h,d] (row j = hidden unit j's output vector), b1 [h] / b2 [d] or None,
+    a_old [n,h] = the activation cache before this step.
+
+    Returns (a_new [n,h] bf16 values, y [n,d], score [nb,h]) where
+      z = x w1t^T + b1, a_new = bf16(gelu(z)), y = a_new w2 + b2 and
+      score[b,j] = sum over the block's real rows of |a_new - a_old| (reading R1).
+    """
+    x = np.asarray(x, np.float64)
+    w1t = np.asarray(w1t, np.float64)
+    w2 = np.asarray(w2, np.float64)
+    z = x @ w1t.T
+    if b1 is not None:
+        z = z + np.asarray(b1, np.float64)[None, :]
+    a_new = bf16_round(gelu_tanh(z))
+    n, h = a_new.shape
+    score = np.zeros(((n + ROW_BLOCK - 1) // ROW_BLOCK, h))
+    diff = np.abs(a_new - np.asarray(a_old, np.float64))
+    for b, r0, r1 in _blocks(n):
+        score[b] = diff[r0:r1].sum(axis=0)
+    y = a_new @ w2
+    if b2 is not None:
+        y = y + np.asarray(b2, np.float64)[None, :]
+    return a_new, y, score
+
+
+def mlp_sparse(x, w1t, b1, w2, a, y, idx):
+    """One sparse MLP step (Chipmunk post, Activation Deltas section: "replace a
+    subset of the output vectors and reuse the rest from the previous step").
+
+    The MLP output is a sum over hidden units j of coefficient a[i,j] times the
+    static vector w2[j] (plus a bias that every step shares, so it cancels).  Per
+    128-row block b with column set S = idx[b]:
+      a_S   = bf16(gelu(x_b w1t[S]^T + b1[S]))     recompute only the chosen units
+      D     = a_S - a[b rows, S]                    exact difference of stored values (R8)
+      y_b  += D w2[S]                               swap old vectors for new ones
+      a[b rows, S] = a_S                            cache writeback
+    Returns new copies (a, y); the inputs are not modified.
+    """
+    x = np.asarray(x, np.float64)
+    w1t = np.asarray(w1t, np.float64)
+    w2 = np.asarray(w2, np.float64)
+    a = np.array(a, dtype=np.float64, copy=True)
+    y = np.array(y, dtype=np.float64, copy=True)
+    idx = np.asarray(idx)
+    n = x.shape[0]
+    for b, r0, r1 in _blocks(n):
+        s = idx[b]
+        if s.size == 0:
+            continue
+        z = x[r0:r1] @ w1t[s].T
+        if b1 is not None:
+            z = z + np.asarray(b1, np.float64)[s][None, :]
+        a_s = bf16_round(gelu_tanh(z))
+        d = a_s - a[r0:r1][:, s]
+        y[r0:r1] += d @ w2[s]
+        a[r0:r1, s] = a_s
+    return a, y
+
+
+# --------------------------------------------------------------------------- #
+# Attention (one head; any set of whole query blocks against all keys)
+# --------------------------------------------------------------------------- #
+def attn_dense(q, k, v, scale: float):
+    """Dense refresh of one head (Chipmunk post, Activation Deltas section: the
+    output is a sum of rows of V weighted by softmax(Q K^T)).
+
+    q [nq,hd] query rows of whole 128-row blocks (nq may end in a partial block),
+    k, v [n,hd] all keys of the head.  With s = scale q k^T:
+      m = rowmax(s), p = exp(s - m), den = sum_j p, num = p v, o = num / den,
+      score[b, j] = sum over the block's rows of p_ij / den_i   (reading R2).
+    Returns (m [nq], den [nq], num [nq,hd], o [nq,hd], score [nbq, n]).
+    """
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    s = scale * (q @ k.T)
+    m = s.max(axis=1)
+    p = np.exp(s - m[:, None])
+    den = p.sum(axis=1)
+    num = p @ v
+    o = num / den[:, None]
+    nq = q.shape[0]
+    score = np.zeros(((nq + ROW_BLOCK - 1) // ROW_BLOCK, k.shape[0]))
+    pn = p / den[:, None]
+    for b, r0, r1 in _blocks(nq):
+        score[b] = pn[r0:r1].sum(axis=0)
+    return m, den, num, o, score
+
+
+def attn_rest(q, k, v, m, idx, scale: float):
+    """What the refresh leaves in the attention cache (reading R3): for each query
+    row i of block b, the numerator and denominator over the keys NOT in S_b,
+    num_rest = sum_{j not in S_b} p_ij v_j and den_rest = sum_{j not in S_b} p_ij,
+    with p from the refresh inputs and the refresh row max m.  Computed directly
+    as masked sums.
+    """
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    m = np.asarray(m, np.float64)
+    nq, n = q.shape[0], k.shape[0]
+    num_rest = np.zeros((nq, v.shape[1]))
+    den_rest = np.zeros(nq)
+    for b, r0, r1 in _blocks(nq):
+        keep = np.ones(n, dtype=bool)
+        keep[np.asarray(idx[b])] = False
+        p = np.exp(scale * (q[r0:r1] @ k[keep].T) - m[r0:r1, None])
+        num_rest[r0:r1] = p @ v[keep]
+        den_rest[r0:r1] = p.sum(axis=1)
+    return num_rest, den_rest
+
+
+def attn_sparse(q, k, v, m, num_rest, den_rest, idx, scale: float):
+    """One sparse attention step: recompute only the chosen keys' vectors and
+    reuse the rest from the refresh (Chipmunk post, Activation Deltas section),
+    with the refresh row max kept fixed (reading R10):
+      p_S = exp(scale q_b k[S_b]^T - m_b)
+      o_b = (num_rest_b + p_S v[S_b]) / (den_rest_b + sum_j p_S).
+    """
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    m = np.asarray(m, np.float64)
+    nq = q.shape[0]
+    o = np.zeros((nq, v.shape[1]))
+    for b, r0, r1 in _blocks(nq):
+        s = np.asarray(idx[b])
+        p = np.exp(scale * (q[r0:r1] @ k[s].T) - m[r0:r1, None])
+        o[r0:r1] = (num_rest[r0:r1] + p @ v[s]) / (den_rest[r0:r1] + p.sum(axis=1))[:, None]
+    return o
+
+
+def rel_frobenius(a, b) -> float:
+    """||a - b||_F / ||b||_F (0 when both are zero)."""
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    nb = np.linalg.norm(b)
+    na = np.linalg.norm(a - b)
+    return float(na / nb) if nb > 0 else float(na)

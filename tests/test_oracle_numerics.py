@@ -1,0 +1,72 @@
+"""Pins of the oracle's storage rounding and GELU against facts fixed outside it:
+a library conversion, hand-derived values of the bf16 format, and closed-form
+identities of the tanh-form GELU."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import bf16_bits, bf16_round, from_bf16_bits, gelu_tanh
+
+
+def _torch_bf16(x32: np.ndarray) -> np.ndarray:
+    return torch.from_numpy(x32).to(torch.bfloat16).to(torch.float64).numpy()
+
+
+def test_bf16_round_matches_torch_conversion():
+    # torch's fp32 -> bf16 conversion is round-to-nearest-even: a library pin.
+    g = np.random.default_rng(0)
+    x = np.concatenate([
+        g.standard_normal(100000).astype(np.float32),
+        (g.standard_normal(20000) * 1e-38).astype(np.float32),      # bf16 subnormal range
+        (g.standard_normal(20000) * 1e38).astype(np.float32),       # near overflow
+        (g.integers(-2**20, 2**20, 20000) * 2.0**-12).astype(np.float32),
+    ])
+    # exact ties: 1 + odd multiples of 2^-8
+    ties = (1.0 + (2 * np.arange(64) + 1) * 2.0**-8).astype(np.float32)
+    x = np.concatenate([x, ties, -ties])
+    np.testing.assert_array_equal(bf16_round(x.astype(np.float64)), _torch_bf16(x))
+
+
+@pytest.mark.parametrize("x,expect", [
+    (1.0 + 2.0**-8, 1.0),                      # tie -> even mantissa (0)
+    (1.0 + 3 * 2.0**-8, 1.0 + 2.0**-6),        # tie -> even mantissa (2)
+    (1.0 + 2.0**-8 + 2.0**-30, 1.0 + 2.0**-7), # just above the tie
+    (-(1.0 + 2.0**-8), -1.0),
+    ((2 - 2.0**-7) * 2.0**127, (2 - 2.0**-7) * 2.0**127),    # largest finite bf16
+    ((2 - 2.0**-8) * 2.0**127, math.inf),      # halfway to 2^128 rounds to even -> overflow
+    (2.0**-133, 2.0**-133),                    # smallest subnormal
+    (2.0**-134, 0.0),                          # tie at half the smallest subnormal -> even (0)
+    (3 * 2.0**-134, 2.0**-132),                # 1.5 subnormal quanta -> 2 (even)
+    (0.0, 0.0),
+])
+def test_bf16_round_hand_values(x, expect):
+    assert bf16_round(np.array([x]))[0] == expect
+
+
+def test_bf16_bits_roundtrip_and_specials():
+    b = np.arange(0, 65536, dtype=np.uint32).astype(np.uint16)
+    v = from_bf16_bits(b)
+    finite = np.isfinite(v)
+    np.testing.assert_array_equal(bf16_bits(v[finite]), b[finite])
+    assert np.isnan(bf16_round(np.array([np.nan]))[0])
+    assert bf16_round(np.array([-np.inf]))[0] == -np.inf
+    assert math.copysign(1.0, bf16_round(np.array([-0.0]))[0]) == -1.0
+    assert from_bf16_bits(np.array([0x3F80], np.uint16))[0] == 1.0
+    assert from_bf16_bits(np.array([0xC000], np.uint16))[0] == -2.0
+
+
+def test_gelu_tanh_library_and_identities():
+    z = np.linspace(-12, 12, 20001)
+    ref = torch.nn.functional.gelu(torch.from_numpy(z), approximate="tanh").numpy()
+    np.testing.assert_allclose(gelu_tanh(z), ref, rtol=1e-14, atol=1e-15)
+    assert gelu_tanh(np.array([0.0]))[0] == 0.0
+    # gelu(x) - gelu(-x) = x exactly in real arithmetic for the tanh form
+    np.testing.assert_allclose(gelu_tanh(z) - gelu_tanh(-z), z, rtol=1e-14, atol=1e-14)
+    # limits
+    assert abs(gelu_tanh(np.array([40.0]))[0] - 40.0) < 1e-12
+    assert abs(gelu_tanh(np.array([-40.0]))[0]) < 1e-12
+    # a value computed by hand: u = sqrt(2/pi) * (1 + 0.044715) at z = 1
+    u = math.sqrt(2 / math.pi) * 1.044715
+    assert abs(gelu_tanh(np.array([1.0]))[0] - 0.5 * (1 + math.tanh(u))) < 1e-15
