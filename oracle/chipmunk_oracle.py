@@ -15,9 +15,10 @@ Deltas Across Diffusion Steps are Very Sparse" gives
   attention, rows of W2 plus one static bias vector for the MLP);
 * the cache of value vectors and scalar coefficients, with a per-step choice of
   which ones to recompute;
-* the delta reformulation: a dense step n equals "remove all of step n-1's output
-  vectors from the output cache and add all of step n's"; the sparse step replaces
-  only a subset (single hidden units / single keys) and keeps the rest.
+* the delta reformulation: with an output cache, a dense step n is the same as
+  taking every one of step n-1's output vectors out of the cache and putting every
+  one of step n's in; the sparse step swaps only a chosen subset (single hidden
+  units or single keys) and keeps the others from the earlier step.
 
 The row-block granularity (128 tokens), top-k per block, GELU in its tanh form and
 the cached attention state (row max, numerator, denominator) are the workloads'
@@ -138,8 +139,8 @@ def identify_topk(score, k: int) -> np.ndarray:
 # MLP
 # --------------------------------------------------------------------------- #
 def mlp_dense(x, w1t, b1, w2, b2, a_old):
-    """Dense refresh step of the MLP: the "normal dense forward pass" that fills
-    the caches (Chipmunk post, Activation Deltas section).
+    """Dense refresh step of the MLP: the ordinary full forward pass, which also
+    fills the caches (Chipmunk post, Activation Deltas section).
 
     x [n,d] (bf16 values), w1t [h,d] (row j = hidden unit j's input weights),
     w2 [h,d] (row j = hidden unit j's output vector), b1 [h] / b2 [d] or None,
@@ -168,8 +169,8 @@ def mlp_dense(x, w1t, b1, w2, b2, a_old):
 
 
 def mlp_sparse(x, w1t, b1, w2, a, y, idx):
-    """One sparse MLP step (Chipmunk post, Activation Deltas section: "replace a
-    subset of the output vectors and reuse the rest from the previous step").
+    """One sparse MLP step (Chipmunk post, Activation Deltas section: only the
+    chosen output vectors are swapped for new ones, the others are kept).
 
     The MLP output is a sum over hidden units j of coefficient a[i,j] times the
     static vector w2[j] (plus a bias that every step shares, so it cancels).  Per
@@ -256,7 +257,7 @@ def attn_rest(q, k, v, m, idx, scale: float):
 
 def attn_sparse(q, k, v, m, num_rest, den_rest, idx, scale: float):
     """One sparse attention step: recompute only the chosen keys' vectors and
-    reuse the rest from the refresh (Chipmunk post, Activation Deltas section),
+    keep the other keys' share from the refresh (Chipmunk post, Activation Deltas section),
     with the refresh row max kept fixed (reading R10):
       p_S = exp(scale q_b k[S_b]^T - m_b)
       o_b = (num_rest_b + p_S v[S_b]) / (den_rest_b + sum_j p_S).
