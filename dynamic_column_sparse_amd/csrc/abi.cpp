@@ -1,0 +1,326 @@
+// C ABI of the column-sparse delta library: argument validation (before any
+// HIP call), kernel launches, status codes, thread-local error text, and the
+// optional per-kernel event timer.  Declarations and contracts: chipmunk.h.
+#include "chipmunk.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return CHIPMUNK_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+constexpr int64_t kMaxGridY = 65535;
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(CHIPMUNK_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Common MLP layer checks.  need_score: the dense step writes the scores.
+int check_mlp(const chipmunk_mlp* L, bool need_score) {
+  if (!L) return fail(CHIPMUNK_E_NULLPTR, "layer is NULL");
+  if (L->n < 1) return fail(CHIPMUNK_E_SHAPE, "n must be >= 1 (got %lld)", (long long)L->n);
+  if (L->d < 128 || L->d % 128 != 0) return fail(CHIPMUNK_E_SHAPE, "d must be a positive multiple of 128 (got %d)", L->d);
+  if (L->h < 1) return fail(CHIPMUNK_E_SHAPE, "h must be >= 1 (got %d)", L->h);
+  if (chipmunk::row_blocks(L->n) > kMaxGridY)
+    return fail(CHIPMUNK_E_SHAPE, "n too large: %lld row blocks exceed %lld", (long long)chipmunk::row_blocks(L->n),
+                (long long)kMaxGridY);
+  if (!L->w1t || !L->w2 || !L->a_cache) return fail(CHIPMUNK_E_NULLPTR, "layer w1t, w2 and a_cache are required");
+  if (need_score && !L->score) return fail(CHIPMUNK_E_NULLPTR, "layer score is required by the dense step");
+  if (!aligned(L->w1t, 16) || !aligned(L->w2, 16) || !aligned(L->a_cache, 16))
+    return fail(CHIPMUNK_E_ALIGN, "w1t, w2 and a_cache must be 16-byte aligned");
+  if ((L->b1 && !aligned(L->b1, 4)) || (L->b2 && !aligned(L->b2, 4)) || (L->score && !aligned(L->score, 4)))
+    return fail(CHIPMUNK_E_ALIGN, "b1, b2 and score must be 4-byte aligned");
+  return CHIPMUNK_OK;
+}
+
+int check_attn(const chipmunk_attn* L) {
+  if (!L) return fail(CHIPMUNK_E_NULLPTR, "layer is NULL");
+  if (L->n < 1) return fail(CHIPMUNK_E_SHAPE, "n must be >= 1 (got %lld)", (long long)L->n);
+  if (L->heads < 1) return fail(CHIPMUNK_E_SHAPE, "heads must be >= 1 (got %d)", L->heads);
+  if (L->head_dim != CHIPMUNK_HEAD_DIM)
+    return fail(CHIPMUNK_E_UNSUPPORTED, "head_dim must be %d (got %d)", CHIPMUNK_HEAD_DIM, L->head_dim);
+  if (!std::isfinite(L->scale)) return fail(CHIPMUNK_E_SHAPE, "scale must be finite");
+  if (L->n > INT32_MAX) return fail(CHIPMUNK_E_SHAPE, "n must fit in int32");
+  if (chipmunk::row_blocks(L->n) * (int64_t)L->heads > INT32_MAX)
+    return fail(CHIPMUNK_E_SHAPE, "heads * row blocks exceeds the grid limit");
+  if (!L->m || !L->num || !L->den) return fail(CHIPMUNK_E_NULLPTR, "layer m, num and den are required");
+  if (!aligned(L->m, 4) || !aligned(L->den, 4) || !aligned(L->num, 16) || (L->score && !aligned(L->score, 4)))
+    return fail(CHIPMUNK_E_ALIGN, "num must be 16-byte aligned; m, den, score 4-byte aligned");
+  return CHIPMUNK_OK;
+}
+
+int check_bf16_in(const void* p, const char* name) {
+  if (!p) return fail(CHIPMUNK_E_NULLPTR, "%s is NULL", name);
+  if (!aligned(p, 16)) return fail(CHIPMUNK_E_ALIGN, "%s must be 16-byte aligned", name);
+  return CHIPMUNK_OK;
+}
+
+size_t sparse_mlp_ws(int64_t n, int32_t k) {
+  return (size_t)chipmunk::row_blocks(n) * (size_t)k * chipmunk::kRowBlock * sizeof(uint16_t);
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ timer ---
+namespace chipmunk {
+namespace {
+struct Rec {
+  int kid;
+  hipEvent_t a, b;
+};
+std::mutex g_tmu;
+bool g_ton = false;
+std::vector<Rec> g_recs;
+std::vector<hipEvent_t> g_pool;
+thread_local hipEvent_t g_open = nullptr;
+
+hipEvent_t take_event() {
+  if (!g_pool.empty()) {
+    hipEvent_t e = g_pool.back();
+    g_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+}  // namespace
+
+const char* kernel_name(int kid) {
+  static const char* names[K_COUNT] = {"mlp_gemm1_sparse", "mlp_gemm1_dense", "mlp_gemm2_sparse", "mlp_gemm2_dense",
+                                       "topk_rows",        "cache_writeback", "attn_stats",       "attn_dense",
+                                       "attn_sparse",      "attn_refresh"};
+  return (kid >= 0 && kid < K_COUNT) ? names[kid] : "";
+}
+
+void timing_before(int kid, hipStream_t s) {
+  (void)kid;
+  std::lock_guard<std::mutex> g(g_tmu);
+  if (!g_ton) return;
+  g_open = take_event();
+  if (g_open) hipEventRecord(g_open, s);
+}
+
+void timing_after(int kid, hipStream_t s) {
+  std::lock_guard<std::mutex> g(g_tmu);
+  if (!g_ton || !g_open) return;
+  hipEvent_t e = take_event();
+  if (!e) return;
+  hipEventRecord(e, s);
+  g_recs.push_back({kid, g_open, e});
+  g_open = nullptr;
+}
+}  // namespace chipmunk
+
+extern "C" int chipmunk_timing_enable(int on) {
+  using namespace chipmunk;
+  std::lock_guard<std::mutex> g(g_tmu);
+  if (on) {
+    for (auto& r : g_recs) {
+      hipEventSynchronize(r.b);
+      g_pool.push_back(r.a);
+      g_pool.push_back(r.b);
+    }
+    g_recs.clear();
+  }
+  g_ton = on != 0;
+  return ok();
+}
+
+extern "C" int chipmunk_timing_read(int kid, double* total_ms, int64_t* launches) {
+  using namespace chipmunk;
+  if (kid < 0 || kid >= K_COUNT) return fail(CHIPMUNK_E_SHAPE, "kernel id %d out of range", kid);
+  if (!total_ms || !launches) return fail(CHIPMUNK_E_NULLPTR, "total_ms and launches are required");
+  std::lock_guard<std::mutex> g(g_tmu);
+  double sum = 0.0;
+  int64_t cnt = 0;
+  for (auto& r : g_recs) {
+    if (r.kid != kid) continue;
+    hipError_t e = hipEventSynchronize(r.b);
+    if (e != hipSuccess) return hip_status(e, "hipEventSynchronize");
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, r.a, r.b);
+    if (e != hipSuccess) return hip_status(e, "hipEventElapsedTime");
+    sum += ms;
+    ++cnt;
+  }
+  *total_ms = sum;
+  *launches = cnt;
+  return ok();
+}
+
+extern "C" int chipmunk_kernel_count(void) { return chipmunk::K_COUNT; }
+extern "C" const char* chipmunk_kernel_name(int kid) { return chipmunk::kernel_name(kid); }
+
+// ------------------------------------------------------------ entry points ---
+extern "C" const char* chipmunk_last_error(void) { return g_err.c_str(); }
+extern "C" int chipmunk_abi_version(void) { return CHIPMUNK_ABI_VERSION; }
+
+extern "C" size_t chipmunk_workspace_bytes(int op, int64_t n, int32_t d, int32_t h, int32_t k) {
+  (void)d;
+  (void)h;
+  if (n < 1 || k < 0) return 0;
+  switch (op) {
+    case CHIPMUNK_OP_SPARSE_MLP:
+      return sparse_mlp_ws(n, k);
+    default:
+      return 0;
+  }
+}
+
+extern "C" int chipmunk_dense_step(int kind, const void* layer, const uint16_t* x_or_q, const uint16_t* k,
+                                   const uint16_t* v, float* out, void* ws, size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  try {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (!layer) return fail(CHIPMUNK_E_NULLPTR, "layer is NULL");
+    if (kind == CHIPMUNK_MLP) {
+      const chipmunk_mlp* L = static_cast<const chipmunk_mlp*>(layer);
+      int rc = check_mlp(L, true);
+      if (rc) return rc;
+      if ((rc = check_bf16_in(x_or_q, "x"))) return rc;
+      if (k || v) return fail(CHIPMUNK_E_SHAPE, "k and v must be NULL for an MLP layer");
+      if (!out) return fail(CHIPMUNK_E_NULLPTR, "out (y) is NULL");
+      if (!aligned(out, 16)) return fail(CHIPMUNK_E_ALIGN, "out (y) must be 16-byte aligned");
+      hipError_t e = chipmunk::launch_mlp_gemm1(true, x_or_q, L->w1t, L->b1, nullptr, L->a_cache, nullptr, nullptr,
+                                                L->score, L->n, L->d, L->h, L->h, s);
+      if (e != hipSuccess) return hip_status(e, "mlp_gemm1 (dense) launch");
+      e = chipmunk::launch_mlp_gemm2(true, L->a_cache, L->w2, nullptr, L->b2, out, L->n, L->d, L->h, L->h, L->h, s);
+      return hip_status(e, "mlp_gemm2 (dense) launch");
+    }
+    if (kind == CHIPMUNK_ATTN) {
+      const chipmunk_attn* L = static_cast<const chipmunk_attn*>(layer);
+      int rc = check_attn(L);
+      if (rc) return rc;
+      if ((rc = check_bf16_in(x_or_q, "q")) || (rc = check_bf16_in(k, "k")) || (rc = check_bf16_in(v, "v"))) return rc;
+      if (!out || !L->score) return fail(CHIPMUNK_E_NULLPTR, "out (o) and layer score are required");
+      if (!aligned(out, 16)) return fail(CHIPMUNK_E_ALIGN, "out (o) must be 16-byte aligned");
+      hipError_t e = chipmunk::launch_attn_dense(x_or_q, k, v, L->m, L->num, L->den, out, L->score, L->n, L->heads,
+                                                 L->scale, s);
+      return hip_status(e, "attention refresh launch");
+    }
+    return fail(CHIPMUNK_E_SHAPE, "unknown kind %d", kind);
+  } catch (...) {
+    return fail(CHIPMUNK_E_INTERNAL, "internal error in chipmunk_dense_step");
+  }
+}
+
+extern "C" int chipmunk_identify_topk(const float* score, int64_t rows, int64_t cols, int32_t k, int32_t* idx,
+                                      void* ws, size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  try {
+    if (rows < 0) return fail(CHIPMUNK_E_SHAPE, "rows must be >= 0");
+    if (cols < 1) return fail(CHIPMUNK_E_SHAPE, "cols must be >= 1");
+    if (k < 0 || k > cols) return fail(CHIPMUNK_E_SHAPE, "k must be in [0, cols] (k=%d, cols=%lld)", k, (long long)cols);
+    if (rows > INT32_MAX) return fail(CHIPMUNK_E_SHAPE, "rows exceeds the grid limit");
+    if (!score || !idx) return fail(CHIPMUNK_E_NULLPTR, "score and idx are required");
+    if (!aligned(score, 4) || !aligned(idx, 4)) return fail(CHIPMUNK_E_ALIGN, "score and idx must be 4-byte aligned");
+    if (rows == 0 || k == 0) return ok();
+    return hip_status(chipmunk::launch_topk(score, rows, cols, k, idx, static_cast<hipStream_t>(stream)),
+                      "topk launch");
+  } catch (...) {
+    return fail(CHIPMUNK_E_INTERNAL, "internal error in chipmunk_identify_topk");
+  }
+}
+
+extern "C" int chipmunk_sparse_mlp_delta(const chipmunk_mlp* L, const uint16_t* x, const int32_t* idx, int32_t k,
+                                         float* y, uint16_t* a_new_packed, void* ws, size_t ws_bytes, void* stream) {
+  try {
+    int rc = check_mlp(L, false);
+    if (rc) return rc;
+    if (k < 0 || k > L->h) return fail(CHIPMUNK_E_SHAPE, "k must be in [0, h] (k=%d, h=%d)", k, L->h);
+    if ((rc = check_bf16_in(x, "x"))) return rc;
+    if (!y) return fail(CHIPMUNK_E_NULLPTR, "y is NULL");
+    if (!aligned(y, 16)) return fail(CHIPMUNK_E_ALIGN, "y must be 16-byte aligned");
+    if (k > 0 && !idx) return fail(CHIPMUNK_E_NULLPTR, "idx is NULL");
+    if (idx && !aligned(idx, 4)) return fail(CHIPMUNK_E_ALIGN, "idx must be 4-byte aligned");
+    if (a_new_packed && !aligned(a_new_packed, 16)) return fail(CHIPMUNK_E_ALIGN, "a_new_packed must be 16-byte aligned");
+    const size_t need = sparse_mlp_ws(L->n, k);
+    if (k > 0 && (!ws || ws_bytes < need))
+      return fail(CHIPMUNK_E_WORKSPACE, "workspace of %zu bytes required (got %zu)", need, ws ? ws_bytes : (size_t)0);
+    if (ws && !aligned(ws, 16)) return fail(CHIPMUNK_E_ALIGN, "ws must be 16-byte aligned");
+    if (k == 0) return ok();
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint16_t* dbuf = static_cast<uint16_t*>(ws);
+    hipError_t e = chipmunk::launch_mlp_gemm1(false, x, L->w1t, L->b1, idx, L->a_cache, dbuf, a_new_packed, nullptr,
+                                              L->n, L->d, L->h, k, s);
+    if (e != hipSuccess) return hip_status(e, "mlp_gemm1 (sparse) launch");
+    e = chipmunk::launch_mlp_gemm2(false, dbuf, L->w2, idx, nullptr, y, L->n, L->d, L->h, k, k, s);
+    return hip_status(e, "mlp_gemm2 (sparse) launch");
+  } catch (...) {
+    return fail(CHIPMUNK_E_INTERNAL, "internal error in chipmunk_sparse_mlp_delta");
+  }
+}
+
+extern "C" int chipmunk_sparse_attn_delta(const chipmunk_attn* L, const uint16_t* q, const uint16_t* k,
+                                          const uint16_t* v, const int32_t* idx, int32_t kk, int mode, float* o,
+                                          void* stream) {
+  try {
+    int rc = check_attn(L);
+    if (rc) return rc;
+    if (mode != CHIPMUNK_ATTN_SPARSE && mode != CHIPMUNK_ATTN_REFRESH)
+      return fail(CHIPMUNK_E_SHAPE, "mode must be CHIPMUNK_ATTN_SPARSE or CHIPMUNK_ATTN_REFRESH (got %d)", mode);
+    if (kk < 0 || (int64_t)kk > L->n) return fail(CHIPMUNK_E_SHAPE, "kk must be in [0, n] (kk=%d)", kk);
+    if ((rc = check_bf16_in(q, "q")) || (rc = check_bf16_in(k, "k")) || (rc = check_bf16_in(v, "v"))) return rc;
+    if (kk > 0 && !idx) return fail(CHIPMUNK_E_NULLPTR, "idx is NULL");
+    if (idx && !aligned(idx, 4)) return fail(CHIPMUNK_E_ALIGN, "idx must be 4-byte aligned");
+    if (mode == CHIPMUNK_ATTN_SPARSE) {
+      if (!o) return fail(CHIPMUNK_E_NULLPTR, "o is NULL");
+      if (!aligned(o, 16)) return fail(CHIPMUNK_E_ALIGN, "o must be 16-byte aligned");
+    }
+    if (mode == CHIPMUNK_ATTN_REFRESH && kk == 0) return ok();
+    hipError_t e = chipmunk::launch_attn_sparse(mode == CHIPMUNK_ATTN_REFRESH, q, k, v, idx, L->m, L->num, L->den, o,
+                                                L->n, L->heads, kk, L->scale, static_cast<hipStream_t>(stream));
+    return hip_status(e, "attention delta launch");
+  } catch (...) {
+    return fail(CHIPMUNK_E_INTERNAL, "internal error in chipmunk_sparse_attn_delta");
+  }
+}
+
+extern "C" int chipmunk_cache_writeback(const chipmunk_mlp* L, const uint16_t* a_new_packed, const int32_t* idx,
+                                        int32_t k, void* stream) {
+  try {
+    int rc = check_mlp(L, false);
+    if (rc) return rc;
+    if (k < 0 || k > L->h) return fail(CHIPMUNK_E_SHAPE, "k must be in [0, h] (k=%d, h=%d)", k, L->h);
+    if (k == 0) return ok();
+    if ((rc = check_bf16_in(a_new_packed, "a_new_packed"))) return rc;
+    if (!idx) return fail(CHIPMUNK_E_NULLPTR, "idx is NULL");
+    if (!aligned(idx, 4)) return fail(CHIPMUNK_E_ALIGN, "idx must be 4-byte aligned");
+    return hip_status(chipmunk::launch_writeback(a_new_packed, idx, L->a_cache, L->n, L->h, k,
+                                                 static_cast<hipStream_t>(stream)),
+                      "writeback launch");
+  } catch (...) {
+    return fail(CHIPMUNK_E_INTERNAL, "internal error in chipmunk_cache_writeback");
+  }
+}

@@ -1,0 +1,54 @@
+// Internal launch interface between the C ABI (validation, timing) and the
+// kernel translation units.  Not part of the public header.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace chipmunk {
+
+constexpr int kRowBlock = 128;
+constexpr int kHeadDim = 128;
+
+// Kernel ids for the optional per-kernel timer (order = chipmunk_kernel_name ids).
+enum KernelId {
+  K_MLP_GEMM1_SPARSE = 0,
+  K_MLP_GEMM1_DENSE,
+  K_MLP_GEMM2_SPARSE,
+  K_MLP_GEMM2_DENSE,
+  K_TOPK,
+  K_WRITEBACK,
+  K_ATTN_STATS,
+  K_ATTN_DENSE,
+  K_ATTN_SPARSE,
+  K_ATTN_REFRESH,
+  K_COUNT
+};
+const char* kernel_name(int kid);
+
+// Timer hooks (no-ops unless chipmunk_timing_enable(1)).
+void timing_before(int kid, hipStream_t s);
+void timing_after(int kid, hipStream_t s);
+
+__host__ __device__ inline int64_t row_blocks(int64_t n) { return (n + kRowBlock - 1) / kRowBlock; }
+
+// MLP phase 1: gathered x W1[:,S] + GELU, then either the sparse epilogue
+// (D tiles, cache writeback) or the dense one (score, full cache write).
+hipError_t launch_mlp_gemm1(bool dense, const uint16_t* x, const uint16_t* w1t, const float* b1,
+                            const int32_t* idx, uint16_t* a_cache, uint16_t* dbuf, uint16_t* a_packed,
+                            float* score, int64_t n, int d, int h, int k, hipStream_t s);
+// MLP phase 2: y (+)= src[b] W2[S] where src is [nb][kc][128] (D tiles, or the cache).
+hipError_t launch_mlp_gemm2(bool dense, const uint16_t* src, const uint16_t* w2, const int32_t* idx,
+                            const float* b2, float* y, int64_t n, int d, int h, int k, int kc,
+                            hipStream_t s);
+hipError_t launch_writeback(const uint16_t* packed, const int32_t* idx, uint16_t* a_cache, int64_t n, int h,
+                            int k, hipStream_t s);
+hipError_t launch_topk(const float* score, int64_t rows, int64_t cols, int k, int32_t* idx, hipStream_t s);
+hipError_t launch_attn_dense(const uint16_t* q, const uint16_t* k, const uint16_t* v, float* m, float* num,
+                             float* den, float* o, float* score, int64_t n, int heads, float scale,
+                             hipStream_t s);
+hipError_t launch_attn_sparse(bool refresh, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                              const int32_t* idx, const float* m, float* num, float* den, float* o, int64_t n,
+                              int heads, int kk, float scale, hipStream_t s);
+
+}  // namespace chipmunk

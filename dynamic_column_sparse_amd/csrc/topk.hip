@@ -1,0 +1,136 @@
+// Sparsity identification: exact top-k per score row (gfx950).
+//
+// One workgroup (512 threads, 8 waves) per row.  Scores become monotone 32-bit
+// keys (NaN -> 0, the lowest; -0 -> +0; sign-magnitude -> offset binary), so the
+// choice is integer work and matches any exact reference bit for bit.
+//   1. Radix select, 8 bits per pass from the top: an LDS histogram of the
+//      candidates that still match the prefix finds the k-th largest key T and
+//      how many keys equal to T must still be taken (ties go to the lower index).
+//   2. One pass in index order emits key > T plus the first `need` keys == T,
+//      using wave ballots for the in-order ranks, so the output is ascending.
+// Rows of up to kLdsCap scores are staged in LDS once; longer rows (attention
+// at long sequence lengths) are re-read from global memory on each pass.
+#include "device_common.h"
+#include "internal.h"
+
+namespace chipmunk {
+namespace {
+
+constexpr int kThreads = 512;
+constexpr int kWaves = kThreads / 64;
+constexpr int kLdsCap = 15360;  // 60 KB of keys
+
+__device__ __forceinline__ uint32_t score_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0u;  // NaN ranks lowest
+  if (u == 0x80000000u) u = 0u;                     // -0 == +0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+template <bool IN_LDS>
+__global__ __launch_bounds__(kThreads) void topk_rows(const float* __restrict__ score, int64_t cols, int k,
+                                                      int32_t* __restrict__ idx) {
+  extern __shared__ uint32_t skey[];
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t wtot[kWaves];
+  __shared__ uint32_t wtot2[kWaves];
+  __shared__ uint32_t sh_prefix, sh_remaining;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t row = blockIdx.x;
+  const float* srow = score + row * cols;
+  int32_t* orow = idx + row * (int64_t)k;
+
+  if (IN_LDS) {
+    for (int64_t i = tid; i < cols; i += kThreads) skey[i] = score_key(srow[i]);
+  }
+  __syncthreads();
+  auto key_at = [&](int64_t i) -> uint32_t { return IN_LDS ? skey[i] : score_key(srow[i]); };
+
+  uint32_t prefix = 0, mask = 0, remaining = (uint32_t)k;
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    for (int i = tid; i < 256; i += kThreads) hist[i] = 0;
+    __syncthreads();
+    for (int64_t i = tid; i < cols; i += kThreads) {
+      const uint32_t key = key_at(i);
+      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    // Inclusive scan of the counts from the top digit down (threads 0..255).
+    uint32_t hv = 0, incl = 0;
+    if (tid < 256) {
+      hv = hist[255 - tid];
+      incl = hv;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t t = __shfl_up(incl, o);
+        if (lane >= o) incl += t;
+      }
+      if (lane == 63) wtot[wave] = incl;
+    }
+    __syncthreads();
+    if (tid < 256) {
+      for (int w = 0; w < wave; ++w) incl += wtot[w];
+      const uint32_t excl = incl - hv;
+      if (excl < remaining && remaining <= incl) {
+        sh_prefix = prefix | ((uint32_t)(255 - tid) << shift);
+        sh_remaining = remaining - excl;
+      }
+    }
+    __syncthreads();
+    prefix = sh_prefix;
+    remaining = sh_remaining;
+    mask |= 255u << shift;
+  }
+
+  const uint32_t T = prefix, need = remaining;
+  uint32_t taken = 0, eq_seen = 0;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : ((~0ull) >> (64 - lane));
+  for (int64_t base = 0; base < cols && taken < (uint32_t)k; base += kThreads) {
+    const int64_t i = base + tid;
+    const bool in = i < cols;
+    const uint32_t key = in ? key_at(i) : 0u;
+    const bool gt = in && key > T;
+    const bool eq = in && key == T;
+    const uint64_t em = __ballot(eq);
+    if (lane == 0) wtot[wave] = (uint32_t)__popcll(em);
+    __syncthreads();
+    uint32_t eq_before = eq_seen, eq_chunk = 0;
+    for (int w = 0; w < kWaves; ++w) {
+      if (w < wave) eq_before += wtot[w];
+      eq_chunk += wtot[w];
+    }
+    const uint32_t eq_rank = eq_before + (uint32_t)__popcll(em & lt_mask);
+    const bool take = gt || (eq && eq_rank < need);
+    const uint64_t tm = __ballot(take);
+    if (lane == 0) wtot2[wave] = (uint32_t)__popcll(tm);
+    __syncthreads();
+    uint32_t t_before = taken, t_chunk = 0;
+    for (int w = 0; w < kWaves; ++w) {
+      if (w < wave) t_before += wtot2[w];
+      t_chunk += wtot2[w];
+    }
+    const uint32_t pos = t_before + (uint32_t)__popcll(tm & lt_mask);
+    if (take && pos < (uint32_t)k) orow[pos] = (int32_t)i;
+    taken += t_chunk;
+    eq_seen += eq_chunk;
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+hipError_t launch_topk(const float* score, int64_t rows, int64_t cols, int k, int32_t* idx, hipStream_t s) {
+  timing_before(K_TOPK, s);
+  if (cols <= kLdsCap)
+    hipLaunchKernelGGL((topk_rows<true>), dim3((unsigned)rows), dim3(kThreads), (size_t)cols * 4, s, score, cols, k,
+                       idx);
+  else
+    hipLaunchKernelGGL((topk_rows<false>), dim3((unsigned)rows), dim3(kThreads), 0, s, score, cols, k, idx);
+  hipError_t e = hipGetLastError();
+  timing_after(K_TOPK, s);
+  return e;
+}
+
+}  // namespace chipmunk

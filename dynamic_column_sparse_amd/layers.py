@@ -1,0 +1,106 @@
+"""Per-layer device state for a sampler loop: buffers plus the order of C-ABI
+calls.  Allocation and call sequencing only; every computation is a call into
+``libchipmunk.so``.
+
+Schedule per layer and diffusion step (the Chipmunk post, section "Activation
+Deltas Across Diffusion Steps are Very Sparse": cache the value vectors and
+their coefficients, then recompute a chosen subset each step):
+  MLP        refresh: dense step (fills the activation cache, output cache and
+             per-block column scores); sparse: identify top-k from the scores,
+             then the sparse delta with fused cache writeback.
+  attention  refresh: dense step (m, num, den, o, key-mass scores), identify the
+             top-k keys per query block, then REFRESH (num, den keep only the
+             part outside S); sparse: the sparse delta writes o.
+"""
+from __future__ import annotations
+
+import math
+
+import torch
+
+from . import lib
+
+ROW_BLOCK = lib.ROW_BLOCK
+
+
+def row_blocks(n: int) -> int:
+    return (n + ROW_BLOCK - 1) // ROW_BLOCK
+
+
+class MLPDelta:
+    """One MLP layer: w1t [h,d], w2 [h,d] bf16 device tensors; k kept columns per block."""
+
+    def __init__(self, w1t: torch.Tensor, w2: torch.Tensor, n: int, k: int, b1=None, b2=None):
+        h, d = w1t.shape
+        assert w2.shape == (h, d) and w1t.dtype == torch.bfloat16 and w2.dtype == torch.bfloat16
+        dev = w1t.device
+        self.n, self.d, self.h, self.k = n, d, h, k
+        self.nb = row_blocks(n)
+        self.w1t, self.w2, self.b1, self.b2 = w1t, w2, b1, b2
+        self.a_cache = torch.zeros(self.nb, h, ROW_BLOCK, dtype=torch.bfloat16, device=dev)
+        self.score = torch.zeros(self.nb, h, dtype=torch.float32, device=dev)
+        self.y = torch.zeros(n, d, dtype=torch.float32, device=dev)
+        self.idx = torch.zeros(self.nb, max(k, 1), dtype=torch.int32, device=dev)
+        ws = lib.chipmunk_workspace_bytes(lib.OP_SPARSE_MLP, n, d, h, k)
+        self.ws = torch.empty(max(ws, 16), dtype=torch.uint8, device=dev)
+        self.layer = lib.mlp_layer(n, d, h, w1t, w2, self.a_cache, self.score, b1, b2)
+
+    def dense(self, x: torch.Tensor, stream=None):
+        lib.chipmunk_dense_step(lib.MLP, self.layer, x, None, None, self.y, stream=stream)
+
+    def identify(self, stream=None):
+        lib.chipmunk_identify_topk(self.score, self.nb, self.h, self.k, self.idx, stream=stream)
+
+    def sparse(self, x: torch.Tensor, idx=None, a_new_packed=None, stream=None):
+        lib.chipmunk_sparse_mlp_delta(self.layer, x, self.idx if idx is None else idx, self.k, self.y,
+                                      a_new_packed, self.ws, stream=stream)
+
+    def writeback(self, a_new_packed, idx=None, stream=None):
+        lib.chipmunk_cache_writeback(self.layer, a_new_packed, self.idx if idx is None else idx, self.k,
+                                     stream=stream)
+
+    def step(self, x: torch.Tensor, refresh: bool, stream=None):
+        if refresh:
+            self.dense(x, stream)
+        else:
+            self.identify(stream)
+            self.sparse(x, stream=stream)
+
+
+class AttnDelta:
+    """One attention layer (all heads), head_dim 128; kk kept keys per query block."""
+
+    def __init__(self, n: int, heads: int, kk: int, device, scale=None):
+        self.n, self.heads, self.kk = n, heads, kk
+        self.nb = row_blocks(n)
+        self.scale = 1.0 / math.sqrt(lib.HEAD_DIM) if scale is None else scale
+        f32 = dict(dtype=torch.float32, device=device)
+        self.m = torch.zeros(heads, n, **f32)
+        self.den = torch.zeros(heads, n, **f32)
+        self.num = torch.zeros(heads, n, lib.HEAD_DIM, **f32)
+        self.score = torch.zeros(heads, self.nb, n, **f32)
+        self.o = torch.zeros(heads, n, lib.HEAD_DIM, **f32)
+        self.idx = torch.zeros(heads * self.nb, max(kk, 1), dtype=torch.int32, device=device)
+        self.layer = lib.attn_layer(n, heads, self.m, self.num, self.den, self.score, self.scale)
+
+    def dense(self, q, k, v, stream=None):
+        lib.chipmunk_dense_step(lib.ATTN, self.layer, q, k, v, self.o, stream=stream)
+
+    def identify(self, stream=None):
+        lib.chipmunk_identify_topk(self.score, self.heads * self.nb, self.n, self.kk, self.idx, stream=stream)
+
+    def refresh_rest(self, q, k, v, idx=None, stream=None):
+        lib.chipmunk_sparse_attn_delta(self.layer, q, k, v, self.idx if idx is None else idx, self.kk,
+                                       lib.ATTN_REFRESH, None, stream=stream)
+
+    def sparse(self, q, k, v, idx=None, stream=None):
+        lib.chipmunk_sparse_attn_delta(self.layer, q, k, v, self.idx if idx is None else idx, self.kk,
+                                       lib.ATTN_SPARSE, self.o, stream=stream)
+
+    def step(self, q, k, v, refresh: bool, stream=None):
+        if refresh:
+            self.dense(q, k, v, stream)
+            self.identify(stream)
+            self.refresh_rest(q, k, v, stream=stream)
+        else:
+            self.sparse(q, k, v, stream=stream)

@@ -1,0 +1,177 @@
+"""Thin ctypes binding of ``libchipmunk.so`` (argument marshalling only).
+
+Each function has the C entry point's name and takes torch tensors (or None)
+where the C call takes device pointers; every step of the computation runs in
+the library's HIP kernels.  A missing library raises at import time: there is
+no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libchipmunk.so")
+
+ROW_BLOCK = 128
+HEAD_DIM = 128
+MLP, ATTN = 0, 1
+ATTN_SPARSE, ATTN_REFRESH = 0, 1
+OP_DENSE_MLP, OP_SPARSE_MLP, OP_TOPK, OP_DENSE_ATTN, OP_SPARSE_ATTN = 0, 1, 2, 3, 4
+
+STATUS = {0: "CHIPMUNK_OK", 1: "CHIPMUNK_E_NULLPTR", 2: "CHIPMUNK_E_SHAPE", 3: "CHIPMUNK_E_UNSUPPORTED",
+          4: "CHIPMUNK_E_ALIGN", 5: "CHIPMUNK_E_WORKSPACE", 6: "CHIPMUNK_E_HIP", 7: "CHIPMUNK_E_INTERNAL"}
+
+EXPORTS = ("chipmunk_dense_step", "chipmunk_identify_topk", "chipmunk_sparse_mlp_delta",
+           "chipmunk_sparse_attn_delta", "chipmunk_cache_writeback", "chipmunk_workspace_bytes",
+           "chipmunk_last_error", "chipmunk_abi_version", "chipmunk_timing_enable", "chipmunk_timing_read",
+           "chipmunk_kernel_count", "chipmunk_kernel_name")
+
+
+class ChipmunkError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{STATUS.get(code, code)}: {msg}")
+        self.code = code
+
+
+class MLPLayer(ctypes.Structure):
+    """``chipmunk_mlp``: sizes and device pointers of one MLP layer."""
+    _fields_ = [("n", ctypes.c_int64), ("d", ctypes.c_int32), ("h", ctypes.c_int32),
+                ("w1t", ctypes.c_void_p), ("b1", ctypes.c_void_p), ("w2", ctypes.c_void_p),
+                ("b2", ctypes.c_void_p), ("a_cache", ctypes.c_void_p), ("score", ctypes.c_void_p)]
+
+
+class AttnLayer(ctypes.Structure):
+    """``chipmunk_attn``: sizes and device pointers of one attention layer's cache."""
+    _fields_ = [("n", ctypes.c_int64), ("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("scale", ctypes.c_float), ("m", ctypes.c_void_p), ("num", ctypes.c_void_p),
+                ("den", ctypes.c_void_p), ("score", ctypes.c_void_p)]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                          "(python -m dynamic_column_sparse_amd.build)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    sig = {
+        "chipmunk_dense_step": (ctypes.c_int, [ctypes.c_int, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "chipmunk_identify_topk": (ctypes.c_int, [vp, i64, i64, i32, vp, vp, sz, vp]),
+        "chipmunk_sparse_mlp_delta": (ctypes.c_int, [vp, vp, vp, i32, vp, vp, vp, sz, vp]),
+        "chipmunk_sparse_attn_delta": (ctypes.c_int, [vp, vp, vp, vp, vp, i32, ctypes.c_int, vp, vp]),
+        "chipmunk_cache_writeback": (ctypes.c_int, [vp, vp, vp, i32, vp]),
+        "chipmunk_workspace_bytes": (sz, [ctypes.c_int, i64, i32, i32, i32]),
+        "chipmunk_last_error": (ctypes.c_char_p, []),
+        "chipmunk_abi_version": (ctypes.c_int, []),
+        "chipmunk_timing_enable": (ctypes.c_int, [ctypes.c_int]),
+        "chipmunk_timing_read": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_double),
+                                                ctypes.POINTER(ctypes.c_int64)]),
+        "chipmunk_kernel_count": (ctypes.c_int, []),
+        "chipmunk_kernel_name": (ctypes.c_char_p, [ctypes.c_int]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype, f.argtypes = res, args
+    return lib
+
+
+_lib = _load()
+
+
+def raw() -> ctypes.CDLL:
+    """The loaded ctypes library (for tests that call the C ABI directly)."""
+    return _lib
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream if torch.cuda.is_available() else None
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _nbytes(ws, ws_bytes):
+    if ws_bytes is not None:
+        return int(ws_bytes)
+    if ws is None or isinstance(ws, int):
+        return 0
+    return ws.numel() * ws.element_size()
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise ChipmunkError(rc, chipmunk_last_error())
+
+
+def chipmunk_last_error() -> str:
+    return (_lib.chipmunk_last_error() or b"").decode()
+
+
+def chipmunk_abi_version() -> int:
+    return _lib.chipmunk_abi_version()
+
+
+def chipmunk_workspace_bytes(op: int, n: int, d: int, h: int, k: int) -> int:
+    return int(_lib.chipmunk_workspace_bytes(op, n, d, h, k))
+
+
+def mlp_layer(n, d, h, w1t, w2, a_cache, score=None, b1=None, b2=None) -> MLPLayer:
+    return MLPLayer(n, d, h, _ptr(w1t), _ptr(b1), _ptr(w2), _ptr(b2), _ptr(a_cache), _ptr(score))
+
+
+def attn_layer(n, heads, m, num, den, score=None, scale=None, head_dim=HEAD_DIM) -> AttnLayer:
+    if scale is None:
+        scale = 1.0 / float(head_dim) ** 0.5
+    return AttnLayer(n, heads, head_dim, scale, _ptr(m), _ptr(num), _ptr(den), _ptr(score))
+
+
+def chipmunk_dense_step(kind: int, layer, x_or_q, k=None, v=None, out=None, ws=None, stream=None, ws_bytes=None):
+    nbytes = _nbytes(ws, ws_bytes)
+    _check(_lib.chipmunk_dense_step(kind, ctypes.byref(layer), _ptr(x_or_q), _ptr(k), _ptr(v), _ptr(out),
+                                    _ptr(ws), nbytes, _stream(stream)))
+
+
+def chipmunk_identify_topk(score, rows: int, cols: int, k: int, idx, ws=None, stream=None, ws_bytes=None):
+    nbytes = _nbytes(ws, ws_bytes)
+    _check(_lib.chipmunk_identify_topk(_ptr(score), rows, cols, k, _ptr(idx), _ptr(ws), nbytes, _stream(stream)))
+
+
+def chipmunk_sparse_mlp_delta(layer: MLPLayer, x, idx, k: int, y, a_new_packed=None, ws=None, stream=None, ws_bytes=None):
+    nbytes = _nbytes(ws, ws_bytes)
+    _check(_lib.chipmunk_sparse_mlp_delta(ctypes.byref(layer), _ptr(x), _ptr(idx), k, _ptr(y), _ptr(a_new_packed),
+                                          _ptr(ws), nbytes, _stream(stream)))
+
+
+def chipmunk_sparse_attn_delta(layer: AttnLayer, q, k, v, idx, kk: int, mode: int, o=None, stream=None):
+    _check(_lib.chipmunk_sparse_attn_delta(ctypes.byref(layer), _ptr(q), _ptr(k), _ptr(v), _ptr(idx), kk, mode,
+                                           _ptr(o), _stream(stream)))
+
+
+def chipmunk_cache_writeback(layer: MLPLayer, a_new_packed, idx, k: int, stream=None):
+    _check(_lib.chipmunk_cache_writeback(ctypes.byref(layer), _ptr(a_new_packed), _ptr(idx), k, _stream(stream)))
+
+
+def chipmunk_timing_enable(on: bool):
+    _check(_lib.chipmunk_timing_enable(1 if on else 0))
+
+
+def chipmunk_timing_read(kid: int):
+    """(total_ms, launches) of kernel `kid` since the last enable."""
+    ms, cnt = ctypes.c_double(), ctypes.c_int64()
+    _check(_lib.chipmunk_timing_read(kid, ctypes.byref(ms), ctypes.byref(cnt)))
+    return ms.value, cnt.value
+
+
+def kernel_names() -> list:
+    return [_lib.chipmunk_kernel_name(i).decode() for i in range(_lib.chipmunk_kernel_count())]

@@ -1,0 +1,220 @@
+/*
+ * chipmunk.h -- C ABI of the column-sparse cross-step delta library (MI355X, gfx950).
+ *
+ * Method: "Chipmunk: Training-Free Acceleration of Diffusion Transformers with
+ * Dynamic Column-Sparse Deltas" (Silveria, Govande, Fu; Together AI research post,
+ * 2025), called "the Chipmunk post" here.  Section "Activation Deltas Across
+ * Diffusion Steps are Very Sparse" writes attention as softmax(Q K^T) V and the
+ * MLP as gelu(x W1) W2, reads both as sums of value vectors weighted by
+ * coefficients from a non-linearity (rows of V; rows of W2 plus a static bias),
+ * caches those vectors and coefficients, and turns each step into a delta: only
+ * a chosen subset of vectors (single hidden units, single keys) is recomputed,
+ * the others are kept from the earlier step.  Its section "Motivation" asks for
+ * dense on-chip tiles packed from non-contiguous columns in global memory.
+ *
+ * Operational shape used here: tokens are grouped in row blocks of 128
+ * (CHIPMUNK_ROW_BLOCK); each block recomputes its own top-k columns (MLP hidden
+ * units) or keys (attention); GELU is the tanh form; the attention cache holds
+ * the refresh-step row max, numerator and denominator.
+ *
+ * Conventions (all entry points)
+ *  - Every tensor is a caller-owned HIP DEVICE pointer on the current device.
+ *    bf16 tensors are passed as their raw 16-bit patterns (uint16_t).  The
+ *    library allocates no device memory; scratch space is caller-provided and
+ *    sized by chipmunk_workspace_bytes().
+ *  - Every compute call only ENQUEUES work on `stream` (a hipStream_t passed as
+ *    void*; NULL = the null stream) and returns without synchronising.
+ *    CHIPMUNK_OK means "validated and enqueued"; a fault during execution shows
+ *    up at the caller's next synchronisation.
+ *  - Every argument is validated before any HIP call, so a rejected call has
+ *    touched nothing.  On a non-zero return, chipmunk_last_error() gives a
+ *    thread-local message.  No C++ exception crosses this boundary.
+ *  - Row blocks: nb = ceil(n / 128); the last block may be partial.  Rows past
+ *    n inside it are padding: they are never read from inputs, never written to
+ *    outputs, and are kept at zero in the activation cache.
+ *  - Index sets (`idx`): int32 [rows][k], each row ascending and unique, every
+ *    value in [0, cols).  Kernels clamp out-of-range values into range (so a
+ *    bad index cannot fault) but the result is then meaningless.
+ *  - Offsets are 64-bit throughout.  Calls are re-entrant; the only shared
+ *    mutable state is the optional kernel timer (chipmunk_timing_*), which
+ *    takes a lock.
+ *  - Two calls that write the same buffers must be ordered by the caller
+ *    (same stream, or events).
+ */
+#ifndef CHIPMUNK_H
+#define CHIPMUNK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CHIPMUNK_ABI_VERSION 1
+#define CHIPMUNK_ROW_BLOCK 128
+#define CHIPMUNK_HEAD_DIM 128
+
+/* Return codes. */
+enum chipmunk_status {
+  CHIPMUNK_OK = 0,
+  CHIPMUNK_E_NULLPTR = 1,     /* a required pointer is NULL */
+  CHIPMUNK_E_SHAPE = 2,       /* a size is out of range or misaligned to the tiling */
+  CHIPMUNK_E_UNSUPPORTED = 3, /* valid request this build does not implement (head_dim != 128) */
+  CHIPMUNK_E_ALIGN = 4,       /* a pointer is not 16-byte aligned */
+  CHIPMUNK_E_WORKSPACE = 5,   /* workspace missing or smaller than chipmunk_workspace_bytes() */
+  CHIPMUNK_E_HIP = 6,         /* a HIP runtime call (launch, event) failed */
+  CHIPMUNK_E_INTERNAL = 7     /* unexpected internal failure */
+};
+
+enum chipmunk_kind { CHIPMUNK_MLP = 0, CHIPMUNK_ATTN = 1 };
+enum chipmunk_attn_mode { CHIPMUNK_ATTN_SPARSE = 0, CHIPMUNK_ATTN_REFRESH = 1 };
+enum chipmunk_op {
+  CHIPMUNK_OP_DENSE_MLP = 0,
+  CHIPMUNK_OP_SPARSE_MLP = 1,
+  CHIPMUNK_OP_TOPK = 2,
+  CHIPMUNK_OP_DENSE_ATTN = 3,
+  CHIPMUNK_OP_SPARSE_ATTN = 4
+};
+
+/* One MLP layer: y = gelu(x W1 + b1) W2 + b2, plus its caches.
+ *   n      tokens (>= 1)
+ *   d      model width, a multiple of 128
+ *   h      hidden width (>= 1)
+ *   w1t    [h][d] bf16, row j = hidden unit j's input weights (an nn.Linear
+ *          fc1.weight as stored); column j of W1 is row j here, so a gathered
+ *          hidden unit is one contiguous row
+ *   b1     [h] fp32 or NULL (= zero)
+ *   w2     [h][d] bf16, row j = hidden unit j's output vector (fc2.weight
+ *          transposed once), again one contiguous row per hidden unit
+ *   b2     [d] fp32 or NULL (= zero); only the dense step adds it -- a static
+ *          vector cancels from every delta
+ *   a_cache [nb][h][128] bf16 activation cache, block-column-major: hidden unit
+ *          j of block b is 128 contiguous values (256 bytes), one per row
+ *   score  [nb][h] fp32 per-block column scores written by the dense step
+ */
+typedef struct chipmunk_mlp {
+  int64_t n;
+  int32_t d;
+  int32_t h;
+  const uint16_t* w1t;
+  const float* b1;
+  const uint16_t* w2;
+  const float* b2;
+  uint16_t* a_cache;
+  float* score;
+} chipmunk_mlp;
+
+/* One attention layer's cache (all heads).
+ *   n        tokens (queries = keys, >= 1)
+ *   heads    number of heads (>= 1)
+ *   head_dim must be 128
+ *   scale    softmax scale (usually 1/sqrt(head_dim))
+ *   m        [heads][n] fp32 row max of scale*q.k at the latest refresh
+ *   num      [heads][n][128] fp32 softmax numerator sum_j exp(s_ij - m_i) v_j;
+ *            after a REFRESH call only the part over keys outside S
+ *   den      [heads][n] fp32 denominator sum_j exp(s_ij - m_i); after REFRESH
+ *            only the part outside S
+ *   score    [heads][nb][n] fp32 key-mass scores of the latest refresh
+ */
+typedef struct chipmunk_attn {
+  int64_t n;
+  int32_t heads;
+  int32_t head_dim;
+  float scale;
+  float* m;
+  float* num;
+  float* den;
+  float* score;
+} chipmunk_attn;
+
+/* Dense refresh step (the ordinary full forward pass that also fills the
+ * caches; Chipmunk post, Activation Deltas section).
+ *
+ * kind = CHIPMUNK_MLP: layer is a const chipmunk_mlp*; x_or_q = x [n][d] bf16;
+ *   k and v must be NULL; out = the output cache y [n][d] fp32.  Computes
+ *   z = x W1 + b1, a = bf16(gelu_tanh(z)) (fp32 math, round to nearest even),
+ *   score[b][j] = sum over block b's real rows of |a - a_cache_old| (fp32),
+ *   then a_cache <- a and y = a W2 + b2 (fp32 accumulate).  ws may be NULL.
+ * kind = CHIPMUNK_ATTN: layer is a const chipmunk_attn*; x_or_q, k, v =
+ *   q, k, v [heads][n][128] bf16; out = o [heads][n][128] fp32.  Per head, with
+ *   s = scale q k^T: m = rowmax(s), den = sum_j exp(s - m), num = exp(s - m) v,
+ *   o = num / den, score[h][b][j] = sum over block b's rows of exp(s_ij - m_i)
+ *   / den_i.  Follow it with chipmunk_identify_topk on the scores and
+ *   chipmunk_sparse_attn_delta(mode = CHIPMUNK_ATTN_REFRESH) to leave only the
+ *   part outside S in num/den.  ws may be NULL.
+ */
+int chipmunk_dense_step(int kind, const void* layer, const uint16_t* x_or_q, const uint16_t* k,
+                        const uint16_t* v, float* out, void* ws, size_t ws_bytes, void* stream);
+
+/* Sparsity identification: for each of `rows` score rows of length `cols`
+ * (row-major fp32, row stride = cols), the k columns with the largest score,
+ * written ascending to idx [rows][k].  Order: larger score first, equal scores
+ * to the lower column index, -0 equal to +0, NaN below everything, +inf above
+ * every finite value.  Integer work on monotone 32-bit keys, so the result is
+ * exact and deterministic.  0 <= k <= cols; k = 0 or rows = 0 enqueues nothing.
+ * ws may be NULL. */
+int chipmunk_identify_topk(const float* score, int64_t rows, int64_t cols, int32_t k, int32_t* idx,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/* Sparse MLP delta step (Chipmunk post, Activation Deltas section): per block b
+ * with S = idx[b] (k hidden units), gather the rows W1^T[S], W2[S] and the cache
+ * columns a_cache[b][S] into on-chip tiles and compute
+ *   a_S = bf16(gelu_tanh(x_b W1[:,S] + b1[S]))
+ *   D   = a_S - a_cache[b][:,S]       (exact in fp32, then bf16 as the matrix operand)
+ *   y_b = y_b + D W2[S,:]             (fp32 accumulate, in place)
+ * and write a_S back: into a_cache[b][S] when a_new_packed is NULL (fused
+ * writeback), else into a_new_packed [nb][k][128] bf16 (same block-column-major
+ * order, for chipmunk_cache_writeback) leaving the cache unchanged.
+ * x [n][d] bf16, idx [nb][k] int32, y [n][d] fp32.  0 <= k <= h; k = 0 leaves
+ * every buffer bit-unchanged.  ws must hold chipmunk_workspace_bytes(
+ * CHIPMUNK_OP_SPARSE_MLP, n, d, h, k) bytes (the D tiles). */
+int chipmunk_sparse_mlp_delta(const chipmunk_mlp* layer, const uint16_t* x, const int32_t* idx,
+                              int32_t k, float* y, uint16_t* a_new_packed, void* ws, size_t ws_bytes,
+                              void* stream);
+
+/* Sparse attention delta (Chipmunk post, Activation Deltas section): per head h
+ * and query block b with S = idx[h*nb + b] (kk keys), gather K[S], V[S] into
+ * on-chip tiles, p = exp(scale q_b K[S]^T - m) with the refresh row max m,
+ * num_S = p V[S], den_S = sum p, then
+ *   mode SPARSE : o = (num + num_S) / (den + den_S)   (num, den hold the part
+ *                 outside S, as left by REFRESH; they are not modified)
+ *   mode REFRESH: num <- num - num_S, den <- den - den_S (o may be NULL; called
+ *                 once after the dense step, on the dense step's q, k, v)
+ * q, k, v [heads][n][128] bf16; idx [heads][nb][kk] int32; o [heads][n][128]
+ * fp32.  0 <= kk <= n; kk = 0 in SPARSE mode writes o = num / den. */
+int chipmunk_sparse_attn_delta(const chipmunk_attn* layer, const uint16_t* q, const uint16_t* k,
+                               const uint16_t* v, const int32_t* idx, int32_t kk, int mode, float* o,
+                               void* stream);
+
+/* Cache writeback (the separate form of the fused writeback above): copy the
+ * packed new activations a_new_packed [nb][k][128] into a_cache[b][idx[b][p]]
+ * for every block b and position p.  Contiguous 256-byte segments. */
+int chipmunk_cache_writeback(const chipmunk_mlp* layer, const uint16_t* a_new_packed, const int32_t* idx,
+                             int32_t k, void* stream);
+
+/* Scratch bytes an op needs for these sizes (0 when none).  op: chipmunk_op. */
+size_t chipmunk_workspace_bytes(int op, int64_t n, int32_t d, int32_t h, int32_t k);
+
+/* Thread-local text of the last failure on this thread ("" if none). */
+const char* chipmunk_last_error(void);
+
+/* CHIPMUNK_ABI_VERSION of the loaded library. */
+int chipmunk_abi_version(void);
+
+/* Optional per-kernel timer.  While enabled, every kernel the library launches
+ * is bracketed by a pair of HIP events on its own stream.  chipmunk_timing_read
+ * waits for the recorded events and returns, for kernel id `kid` (0 <=
+ * kid < chipmunk_kernel_count()), the summed duration in milliseconds and the
+ * launch count since the last enable.  Names: chipmunk_kernel_name(kid).
+ * Enabling clears earlier records.  Guarded by a process-wide lock. */
+int chipmunk_timing_enable(int on);
+int chipmunk_timing_read(int kid, double* total_ms, int64_t* launches);
+int chipmunk_kernel_count(void);
+const char* chipmunk_kernel_name(int kid);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CHIPMUNK_H */

@@ -1,0 +1,157 @@
+"""The C-ABI library loads, exports every symbol include/chipmunk.h declares,
+and rejects bad arguments before any HIP call (so these run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "chipmunk.h")
+LIBSO = os.path.join(ROOT, "dynamic_column_sparse_amd", "libchipmunk.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIBSO), reason="libchipmunk.so not built")
+
+
+@pytest.fixture(scope="module")
+def L():
+    from dynamic_column_sparse_amd import lib
+    return lib
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]*?\b(chipmunk_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_five_entry_points():
+    decl = _declared()
+    for name in ("chipmunk_dense_step", "chipmunk_identify_topk", "chipmunk_sparse_mlp_delta",
+                 "chipmunk_sparse_attn_delta", "chipmunk_cache_writeback"):
+        assert name in decl
+
+
+def test_every_declared_symbol_is_exported(L):
+    so = ctypes.CDLL(LIBSO)
+    decl = _declared()
+    assert len(decl) >= 12
+    for name in decl:
+        assert hasattr(so, name), name
+    assert set(L.EXPORTS) <= set(decl)
+
+
+def test_version_names_workspace(L):
+    assert L.chipmunk_abi_version() == 1
+    names = L.kernel_names()
+    assert "mlp_gemm1_sparse" in names and "attn_sparse" in names and "topk_rows" in names
+    assert L.chipmunk_workspace_bytes(L.OP_SPARSE_MLP, 4352, 3072, 12288, 3686) == 34 * 3686 * 128 * 2
+    assert L.chipmunk_workspace_bytes(L.OP_SPARSE_MLP, 300, 128, 640, 0) == 0
+    assert L.chipmunk_workspace_bytes(L.OP_DENSE_MLP, 300, 128, 640, 200) == 0
+
+
+FAKE = 0x7f0000000000  # aligned, never dereferenced: every case below fails validation first
+
+
+def _mlp(L, n=300, d=256, h=640, **kw):
+    args = dict(w1t=FAKE, w2=FAKE, a_cache=FAKE, score=FAKE)
+    args.update(kw)
+    return L.mlp_layer(n, d, h, **args)
+
+
+def _code(L, fn, *a, **kw):
+    try:
+        fn(*a, **kw)
+    except L.ChipmunkError as e:
+        assert L.chipmunk_last_error() != ""
+        return e.code
+    return 0
+
+
+@pytest.mark.parametrize("case,code", [
+    (dict(n=0), 2), (dict(d=100), 2), (dict(d=64), 2), (dict(h=0), 2),
+    (dict(w1t=None), 1), (dict(a_cache=None), 1), (dict(w2=FAKE + 8), 4),
+])
+def test_sparse_mlp_rejects_bad_layer(L, case, code):
+    lay = _mlp(L, **case)
+    assert _code(L, L.chipmunk_sparse_mlp_delta, lay, FAKE, FAKE, 10, FAKE, None, FAKE, stream=0, ws_bytes=1 << 40) == code
+
+
+def test_sparse_mlp_argument_checks(L):
+    lay = _mlp(L)
+    f = L.chipmunk_sparse_mlp_delta
+    big = 1 << 40
+    assert _code(L, f, lay, FAKE, FAKE, 641, FAKE, None, FAKE, stream=0, ws_bytes=big) == 2   # k > h
+    assert _code(L, f, lay, FAKE, FAKE, -1, FAKE, None, FAKE, stream=0, ws_bytes=big) == 2    # k < 0
+    assert _code(L, f, lay, None, FAKE, 10, FAKE, None, FAKE, stream=0, ws_bytes=big) == 1    # x NULL
+    assert _code(L, f, lay, FAKE + 2, FAKE, 10, FAKE, None, FAKE, stream=0, ws_bytes=big) == 4  # x misaligned
+    assert _code(L, f, lay, FAKE, None, 10, FAKE, None, FAKE, stream=0, ws_bytes=big) == 1    # idx NULL
+    assert _code(L, f, lay, FAKE, FAKE, 10, None, None, FAKE, stream=0, ws_bytes=big) == 1    # y NULL
+    assert _code(L, f, lay, FAKE, FAKE, 10, FAKE, FAKE + 4, FAKE, stream=0, ws_bytes=big) == 4  # packed misaligned
+    assert _code(L, f, lay, FAKE, FAKE, 10, FAKE, None, None, stream=0) == 5         # no workspace
+    raw = L.raw()
+    small = L.chipmunk_workspace_bytes(L.OP_SPARSE_MLP, 300, 256, 640, 10) - 1
+    rc = raw.chipmunk_sparse_mlp_delta(ctypes.byref(lay), FAKE, FAKE, 10, FAKE, None, FAKE, small, None)
+    assert rc == 5
+    # k = 0 is a valid no-op: validated, nothing enqueued
+    assert _code(L, f, lay, FAKE, None, 0, FAKE, None, None, stream=0) == 0
+
+
+def test_dense_step_checks(L):
+    lay = _mlp(L)
+    f = L.chipmunk_dense_step
+    assert _code(L, f, L.MLP, lay, FAKE, FAKE, None, FAKE, stream=0) == 2          # k given for an MLP
+    assert _code(L, f, L.MLP, lay, FAKE, None, None, None, stream=0) == 1          # out NULL
+    assert _code(L, f, L.MLP, _mlp(L, score=None), FAKE, None, None, FAKE, stream=0) == 1
+    assert _code(L, f, 7, lay, FAKE, None, None, FAKE, stream=0) == 2              # unknown kind
+    att = L.attn_layer(300, 2, FAKE, FAKE, FAKE, FAKE, head_dim=64)
+    assert _code(L, f, L.ATTN, att, FAKE, FAKE, FAKE, FAKE, stream=0) == 3         # head_dim 64
+    att = L.attn_layer(300, 2, FAKE, FAKE, FAKE, None)
+    assert _code(L, f, L.ATTN, att, FAKE, FAKE, FAKE, FAKE, stream=0) == 1         # no score buffer
+    att = L.attn_layer(300, 2, FAKE, FAKE, FAKE, FAKE)
+    assert _code(L, f, L.ATTN, att, FAKE, None, FAKE, FAKE, stream=0) == 1         # k NULL
+    rc = L.raw().chipmunk_dense_step(0, None, FAKE, None, None, FAKE, None, 0, None)
+    assert rc == 1
+
+
+def test_topk_and_attn_checks(L):
+    t = L.chipmunk_identify_topk
+    assert _code(L, t, FAKE, 4, 10, 11, FAKE, stream=0) == 2
+    assert _code(L, t, FAKE, 4, 0, 0, FAKE, stream=0) == 2
+    assert _code(L, t, None, 4, 10, 3, FAKE, stream=0) == 1
+    assert _code(L, t, FAKE + 2, 4, 10, 3, FAKE, stream=0) == 4
+    assert _code(L, t, FAKE, 0, 10, 3, FAKE, stream=0) == 0      # no rows: no-op
+    assert _code(L, t, FAKE, 4, 10, 0, FAKE, stream=0) == 0      # k = 0: no-op
+    att = L.attn_layer(300, 2, FAKE, FAKE, FAKE, FAKE)
+    s = L.chipmunk_sparse_attn_delta
+    assert _code(L, s, att, FAKE, FAKE, FAKE, FAKE, 301, L.ATTN_SPARSE, FAKE, stream=0) == 2
+    assert _code(L, s, att, FAKE, FAKE, FAKE, FAKE, 10, 5, FAKE, stream=0) == 2
+    assert _code(L, s, att, FAKE, FAKE, FAKE, FAKE, 10, L.ATTN_SPARSE, None, stream=0) == 1
+    assert _code(L, s, att, FAKE, FAKE, FAKE, None, 10, L.ATTN_SPARSE, FAKE, stream=0) == 1
+    assert _code(L, s, att, FAKE, FAKE, FAKE, None, 0, L.ATTN_REFRESH, None, stream=0) == 0
+    assert _code(L, s, L.attn_layer(300, 0, FAKE, FAKE, FAKE), FAKE, FAKE, FAKE, FAKE, 1, 0, FAKE, stream=0) == 2
+    w = L.chipmunk_cache_writeback
+    assert _code(L, w, _mlp(L), FAKE, FAKE, 700, stream=0) == 2
+    assert _code(L, w, _mlp(L), None, FAKE, 10, stream=0) == 1
+    assert _code(L, w, _mlp(L), FAKE, FAKE, 0, stream=0) == 0
+
+
+def test_timer_api_without_launches(L):
+    L.chipmunk_timing_enable(True)
+    for kid in range(len(L.kernel_names())):
+        assert L.chipmunk_timing_read(kid) == (0.0, 0)
+    L.chipmunk_timing_enable(False)
+    assert _code(L, L.chipmunk_timing_read, 99) == 2
+
+
+def test_product_path_does_not_import_oracle():
+    pkg = os.path.join(ROOT, "dynamic_column_sparse_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(from|import)\s+oracle\b", text, re.M), f
+                assert "chipmunk_oracle" not in text, f
+    for f in os.listdir(os.path.join(ROOT, "oracle")):
+        if f.endswith(".py"):
+            text = open(os.path.join(ROOT, "oracle", f)).read()
+            assert not re.search(r"^\s*(from|import)\s+(dynamic_column_sparse_amd|synthetic)\b", text, re.M), f

@@ -1,0 +1,249 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+Bars: top-k index sets bit-exact on the same fp32 score bits; float outputs
+within relative Frobenius error 2e-2 (bf16 operands, fp32 accumulation);
+k = 0 leaves every buffer bit-unchanged; runs are bit-reproducible.
+Sizes span several tiles with ragged tails (300 rows = 2 full blocks + 44)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic as syn
+from tests.gpu_helpers import (bf16_values, bits_of, cache_to_rows, idx_sets_valid, up_bf16, up_f32)
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-2
+SCALE = 1.0 / np.sqrt(128.0)
+
+
+@pytest.fixture(scope="module")
+def L(gpu_lib):
+    return gpu_lib
+
+
+# ------------------------------------------------------------------ top-k ---
+@pytest.mark.parametrize("kind", ["normal", "ties", "special", "abs"])
+@pytest.mark.parametrize("rows,cols,k", [
+    (5, 1, 1), (7, 7, 3), (9, 100, 1), (9, 100, 50), (9, 100, 99), (9, 100, 100),
+    (4, 4352, 718), (3, 12288, 3686), (3, 12288, 860), (2, 20000, 1400), (1, 118800, 8316),
+])
+def test_topk_bit_exact(L, kind, rows, cols, k):
+    print(f"topk kind={kind} rows={rows} cols={cols} k={k}", flush=True)
+    s = syn.scores(7, rows, cols, kind)
+    idx = torch.full((rows, k), -1, dtype=torch.int32, device="cuda")
+    L.chipmunk_identify_topk(up_f32(s), rows, cols, k, idx)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(idx.cpu().numpy(), oracle.identify_topk(s, k))
+
+
+# -------------------------------------------------------------------- MLP ---
+def _mlp_inputs(n, d, h, seed=0, bias=True, steps=2):
+    w1t_b, w2_b = syn.mlp_weights(seed, d, h)
+    g = np.random.default_rng(seed + 100)
+    b1 = (g.standard_normal(h) * 0.1).astype(np.float32) if bias else None
+    b2 = (g.standard_normal(d) * 0.1).astype(np.float32) if bias else None
+    xs = [syn.activations(seed, "X", t, n, d) for t in range(steps)]
+    return w1t_b, w2_b, b1, b2, xs
+
+
+def _mlp_layer(L, n, d, h, k, w1t_b, w2_b, b1, b2):
+    from dynamic_column_sparse_amd.layers import MLPDelta
+    return MLPDelta(up_bf16(w1t_b), up_bf16(w2_b), n, k,
+                    None if b1 is None else up_f32(b1), None if b2 is None else up_f32(b2))
+
+
+@pytest.mark.parametrize("n,d,h,k", [(300, 256, 640, 200), (256, 128, 512, 128), (130, 384, 1024, 1000)])
+def test_mlp_dense_then_sparse_matches_oracle(L, n, d, h, k):
+    print(f"mlp parity n={n} d={d} h={h} k={k}", flush=True)
+    w1t_b, w2_b, b1, b2, xs = _mlp_inputs(n, d, h)
+    lay = _mlp_layer(L, n, d, h, k, w1t_b, w2_b, b1, b2)
+    lay.dense(up_bf16(xs[0]))
+    torch.cuda.synchronize()
+    w1t, w2 = oracle.from_bf16_bits(w1t_b), oracle.from_bf16_bits(w2_b)
+    x0, x1 = oracle.from_bf16_bits(xs[0]), oracle.from_bf16_bits(xs[1])
+    a0, y0, sc0 = oracle.mlp_dense(x0, w1t, b1, w2, b2, np.zeros((n, h)))
+    a_gpu = cache_to_rows(lay.a_cache, n)
+    assert np.mean(a_gpu != a0) < 2e-3              # one-ulp bf16 splits at rounding ties only
+    assert oracle.rel_frobenius(a_gpu, a0) < 1e-3
+    assert oracle.rel_frobenius(lay.y.cpu().numpy(), y0) < TOL
+    assert oracle.rel_frobenius(lay.score.cpu().numpy(), sc0) < 1e-3
+    pad = bits_of(lay.a_cache).reshape(lay.nb, h, 128)[-1][:, n - (lay.nb - 1) * 128:]
+    assert np.all(pad == 0)
+
+    # sparse step on the oracle's index sets (lockstep)
+    idx = oracle.identify_topk(sc0.astype(np.float32), k)
+    y_before = lay.y.clone()
+    lay.sparse(up_bf16(xs[1]), idx=torch.from_numpy(idx).cuda())
+    torch.cuda.synchronize()
+    a1, y1 = oracle.mlp_sparse(x1, w1t, b1, w2, a0, y0, idx)
+    y_gpu = lay.y.cpu().numpy()
+    assert oracle.rel_frobenius(y_gpu, y1) < TOL
+    assert oracle.rel_frobenius(y_gpu - y_before.cpu().numpy(), y1 - y0) < TOL
+    assert oracle.rel_frobenius(cache_to_rows(lay.a_cache, n), a1) < 1e-3
+
+
+def test_mlp_k_zero_is_bit_identity_and_k_h_is_dense(L):
+    n, d, h = 300, 256, 640
+    w1t_b, w2_b, b1, b2, xs = _mlp_inputs(n, d, h, seed=3)
+    lay0 = _mlp_layer(L, n, d, h, 0, w1t_b, w2_b, b1, b2)
+    lay0.dense(up_bf16(xs[0]))
+    torch.cuda.synchronize()
+    ybits, abits = lay0.y.clone(), lay0.a_cache.clone()
+    lay0.sparse(up_bf16(xs[1]))
+    torch.cuda.synchronize()
+    assert torch.equal(lay0.y.view(torch.int32), ybits.view(torch.int32))
+    assert torch.equal(lay0.a_cache.view(torch.int16), abits.view(torch.int16))
+
+    layh = _mlp_layer(L, n, d, h, h, w1t_b, w2_b, b1, b2)
+    layh.dense(up_bf16(xs[0]))
+    every = torch.arange(h, dtype=torch.int32, device="cuda").repeat(layh.nb, 1)
+    layh.sparse(up_bf16(xs[1]), idx=every)
+    torch.cuda.synchronize()
+    w1t, w2 = oracle.from_bf16_bits(w1t_b), oracle.from_bf16_bits(w2_b)
+    a0, _, _ = oracle.mlp_dense(oracle.from_bf16_bits(xs[0]), w1t, b1, w2, b2, np.zeros((n, h)))
+    _, y1d, _ = oracle.mlp_dense(oracle.from_bf16_bits(xs[1]), w1t, b1, w2, b2, a0)
+    assert oracle.rel_frobenius(layh.y.cpu().numpy(), y1d) < TOL
+
+
+def test_mlp_unfused_writeback_matches_fused_bit_exact(L):
+    n, d, h, k = 300, 256, 640, 250
+    w1t_b, w2_b, b1, b2, xs = _mlp_inputs(n, d, h, seed=5)
+    fa = _mlp_layer(L, n, d, h, k, w1t_b, w2_b, b1, b2)
+    fb = _mlp_layer(L, n, d, h, k, w1t_b, w2_b, b1, b2)
+    for lay in (fa, fb):
+        lay.dense(up_bf16(xs[0]))
+        lay.identify()
+    fa.sparse(up_bf16(xs[1]))
+    packed = torch.zeros(fb.nb, k, 128, dtype=torch.bfloat16, device="cuda")
+    a_before = fb.a_cache.clone()
+    fb.sparse(up_bf16(xs[1]), a_new_packed=packed)
+    torch.cuda.synchronize()
+    assert torch.equal(fb.a_cache.view(torch.int16), a_before.view(torch.int16))   # cache untouched
+    fb.writeback(packed)
+    torch.cuda.synchronize()
+    assert torch.equal(fa.a_cache.view(torch.int16), fb.a_cache.view(torch.int16))
+    assert torch.equal(fa.y.view(torch.int32), fb.y.view(torch.int32))
+
+
+def test_mlp_free_running_tiny_workload(L):
+    # 256 tokens, d 128, h 512, keep 128 per block, GPU's own identification.
+    n, d, h, k = 256, 128, 512, 128
+    w1t_b, w2_b, _, _, xs = _mlp_inputs(n, d, h, seed=0, bias=False)
+    lay = _mlp_layer(L, n, d, h, k, w1t_b, w2_b, None, None)
+    lay.dense(up_bf16(xs[0]))
+    lay.identify()
+    lay.sparse(up_bf16(xs[1]))
+    torch.cuda.synchronize()
+    w1t, w2 = oracle.from_bf16_bits(w1t_b), oracle.from_bf16_bits(w2_b)
+    a0, y0, sc0 = oracle.mlp_dense(oracle.from_bf16_bits(xs[0]), w1t, None, w2, None, np.zeros((n, h)))
+    ridx = oracle.identify_topk(sc0.astype(np.float32), k)
+    jac = idx_sets_valid(lay.idx.cpu().numpy(), ridx, sc0.astype(np.float32))
+    print(f"tiny workload index-set Jaccard {jac:.4f}")
+    _, y1 = oracle.mlp_sparse(oracle.from_bf16_bits(xs[1]), w1t, None, w2, a0, y0, ridx)
+    assert oracle.rel_frobenius(lay.y.cpu().numpy(), y1) < TOL
+
+
+def test_mlp_deterministic(L):
+    n, d, h, k = 300, 256, 640, 200
+    w1t_b, w2_b, b1, b2, xs = _mlp_inputs(n, d, h, seed=9, steps=3)
+    outs = []
+    for _ in range(2):
+        lay = _mlp_layer(L, n, d, h, k, w1t_b, w2_b, b1, b2)
+        lay.step(up_bf16(xs[0]), True)
+        lay.step(up_bf16(xs[1]), False)
+        lay.step(up_bf16(xs[2]), False)
+        torch.cuda.synchronize()
+        outs.append((lay.y.clone(), lay.a_cache.clone(), lay.idx.clone(), lay.score.clone()))
+    for a, b in zip(*outs):
+        assert torch.equal(a.view(torch.int32) if a.dtype == torch.float32 else a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
+                           b.view(torch.int32) if b.dtype == torch.float32 else b.view(torch.int16) if b.dtype == torch.bfloat16 else b)
+
+
+# -------------------------------------------------------------- attention ---
+def _qkv(H, n, step, seed=0):
+    return [syn.heads_activations(seed, t, step, H, n) for t in "QKV"]
+
+
+@pytest.mark.parametrize("n,H,kk", [(300, 2, 100), (256, 8, 64), (200, 1, 200)])
+def test_attention_refresh_and_sparse_match_oracle(L, n, H, kk):
+    print(f"attention parity n={n} H={H} kk={kk}", flush=True)
+    from dynamic_column_sparse_amd.layers import AttnDelta
+    b0, b1_ = _qkv(H, n, 0), _qkv(H, n, 1)
+    att = AttnDelta(n, H, kk, "cuda")
+    g0 = [up_bf16(a) for a in b0]
+    g1 = [up_bf16(a) for a in b1_]
+    att.dense(*g0)
+    torch.cuda.synchronize()
+    m_g, den_g, num_g = att.m.cpu().numpy(), att.den.cpu().numpy(), att.num.cpu().numpy()
+    o_g, sc_g = att.o.cpu().numpy(), att.score.cpu().numpy()
+    refs = []
+    for hh in range(H):
+        q0, k0, v0 = (oracle.from_bf16_bits(a[hh]) for a in b0)
+        m, den, num, o, score = oracle.attn_dense(q0, k0, v0, SCALE)
+        np.testing.assert_allclose(m_g[hh], m, rtol=1e-5, atol=1e-5)
+        assert oracle.rel_frobenius(den_g[hh], den) < 1e-3
+        assert oracle.rel_frobenius(num_g[hh], num) < TOL
+        assert oracle.rel_frobenius(o_g[hh], o) < TOL
+        assert oracle.rel_frobenius(sc_g[hh], score) < 1e-3
+        refs.append((m, score))
+    # refresh with the oracle's index sets, then a sparse step on drifted inputs
+    idx = np.concatenate([oracle.identify_topk(refs[hh][1].astype(np.float32), kk) for hh in range(H)], axis=0)
+    att.refresh_rest(*g0, idx=torch.from_numpy(idx).cuda())
+    att.sparse(*g1, idx=torch.from_numpy(idx).cuda())
+    torch.cuda.synchronize()
+    nb = (n + 127) // 128
+    num_g, den_g, o_g = att.num.cpu().numpy(), att.den.cpu().numpy(), att.o.cpu().numpy()
+    for hh in range(H):
+        q0, k0, v0 = (oracle.from_bf16_bits(a[hh]) for a in b0)
+        q1, k1, v1 = (oracle.from_bf16_bits(a[hh]) for a in b1_)
+        sidx = idx[hh * nb:(hh + 1) * nb]
+        nr, dr = oracle.attn_rest(q0, k0, v0, refs[hh][0], sidx, SCALE)
+        assert oracle.rel_frobenius(den_g[hh], dr) < 1e-3
+        assert oracle.rel_frobenius(num_g[hh], nr) < TOL
+        o1 = oracle.attn_sparse(q1, k1, v1, refs[hh][0], nr, dr, sidx, SCALE)
+        assert oracle.rel_frobenius(o_g[hh], o1) < TOL
+
+
+def test_attention_free_running_and_deterministic(L):
+    from dynamic_column_sparse_amd.layers import AttnDelta
+    n, H, kk = 300, 8, 50
+    b0, b1_ = _qkv(H, n, 0, seed=4), _qkv(H, n, 1, seed=4)
+    outs = []
+    for _ in range(2):
+        att = AttnDelta(n, H, kk, "cuda")
+        att.step(*[up_bf16(a) for a in b0], refresh=True)
+        att.step(*[up_bf16(a) for a in b1_], refresh=False)
+        torch.cuda.synchronize()
+        outs.append((att.o.clone(), att.idx.clone()))
+    assert torch.equal(outs[0][0].view(torch.int32), outs[1][0].view(torch.int32))
+    assert torch.equal(outs[0][1], outs[1][1])
+    nb = (n + 127) // 128
+    gidx = outs[0][1].cpu().numpy()
+    o_g = outs[0][0].cpu().numpy()
+    for hh in range(H):
+        q0, k0, v0 = (oracle.from_bf16_bits(a[hh]) for a in b0)
+        q1, k1, v1 = (oracle.from_bf16_bits(a[hh]) for a in b1_)
+        m, den, num, o, score = oracle.attn_dense(q0, k0, v0, SCALE)
+        ridx = oracle.identify_topk(score.astype(np.float32), kk)
+        idx_sets_valid(gidx[hh * nb:(hh + 1) * nb], ridx, score.astype(np.float32))
+        nr, dr = oracle.attn_rest(q0, k0, v0, m, ridx, SCALE)
+        o1 = oracle.attn_sparse(q1, k1, v1, m, nr, dr, ridx, SCALE)
+        assert oracle.rel_frobenius(o_g[hh], o1) < TOL
+
+
+def test_attention_no_keys_returns_cached_output(L):
+    from dynamic_column_sparse_amd.layers import AttnDelta
+    n, H = 300, 2
+    b0, b1_ = _qkv(H, n, 0, seed=6), _qkv(H, n, 1, seed=6)
+    att = AttnDelta(n, H, 0, "cuda")
+    att.dense(*[up_bf16(a) for a in b0])
+    torch.cuda.synchronize()
+    o_ref = att.o.clone()
+    num_b, den_b = att.num.clone(), att.den.clone()
+    att.refresh_rest(*[up_bf16(a) for a in b0])       # kk = 0: nothing subtracted
+    att.sparse(*[up_bf16(a) for a in b1_])
+    torch.cuda.synchronize()
+    assert torch.equal(att.num.view(torch.int32), num_b.view(torch.int32))
+    assert torch.equal(att.den.view(torch.int32), den_b.view(torch.int32))
+    assert torch.equal(att.o.view(torch.int32), o_ref.view(torch.int32))
