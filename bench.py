@@ -1,0 +1,316 @@
+#!/usr/bin/env python3
+"""Benchmark of the column-sparse delta hot path on one MI355X.
+
+One step = one sparse diffusion step of a FLUX.1-dev-shaped DiT layer: identify
+the top-k MLP hidden units per 128-token block, the sparse MLP delta (gathered
+GEMM1 + GELU + delta + fused cache writeback, gathered GEMM2 into y) and the
+sparse attention delta over the top-k keys of every (head, query block).
+Inputs are seeded synthetic tensors of the real shapes (random-init weights,
+drifting activations), resident in HBM before the timed region.
+
+Prints one JSON line (last line of stdout).  Progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak (published)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E bandwidth (published)
+HEAD_DIM = 128
+
+WORKLOADS = {
+    # FLUX.1-dev at 1280x768: 3840 image + 512 text tokens, d 3072, h 12288;
+    # MLP 70% sparse (keep 3686 of 12288), attention 83.5% sparse (keep 718 of 4352 keys).
+    "flux": dict(n=4352, d=3072, h=12288, k=3686, heads=24, kk=718, steps=10),
+    "tiny": dict(n=256, d=128, h=512, k=128, heads=0, kk=0, steps=2),
+    # HunyuanVideo 720x1280x129: 33x45x80 latent patches, 93% sparse.
+    "hunyuan_mlp": dict(n=118800, d=3072, h=12288, k=860, heads=0, kk=0, steps=3),
+    "hunyuan_attn": dict(n=118800, d=0, h=0, k=0, heads=24, kk=8316, steps=2),
+}
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def flops_mlp(w):
+    return 4.0 * w["n"] * w["d"] * w["k"]
+
+
+def flops_attn(w):
+    return 4.0 * w["n"] * w["kk"] * HEAD_DIM * w["heads"]
+
+
+def kernel_work(name, w):
+    """(amount, bound) of algorithmic work in ONE launch of kernel `name`."""
+    n, d, h, k, H, kk = w["n"], w["d"], w["h"], w["k"], w["heads"], w["kk"]
+    nb = (n + 127) // 128
+    if name == "mlp_gemm1_sparse":
+        return 2.0 * n * d * k, "mfma"
+    if name == "mlp_gemm2_sparse":
+        return 2.0 * n * k * d, "mfma"
+    if name == "attn_sparse":
+        return 4.0 * n * kk * HEAD_DIM * H, "mfma"
+    if name == "topk_rows":
+        return float(nb * h * 4 + nb * k * 4), "hbm"
+    return None, None
+
+
+def source_digest():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "dynamic_column_sparse_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel, workload):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+        ent = rec.get(workload, {}).get(kernel)
+        if ent and ent.get("source_digest") == source_digest():
+            return ent["bytes_per_launch"]
+    except (OSError, ValueError, KeyError):
+        return None
+    return None
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        th = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+        if th:
+            return int(max(th))
+    except Exception:
+        pass
+    return len(os.sched_getaffinity(0))
+
+
+def cpu_baseline(w, inputs, budget_s):
+    """The CPU oracle, as it stands, on a bounded sample of the same sparse step.
+    MLP: whole 128-row blocks until half the budget is used; attention: whole
+    (head, query block) pairs of the first heads until the rest is used.  The
+    time per block / pair scales to the full step."""
+    import oracle
+    t_mlp = t_att = 0.0
+    n_mlp = n_att = 0
+    desc = []
+    if w["k"]:
+        n, h, k = w["n"], w["h"], w["k"]
+        w1t = oracle.from_bf16_bits(inputs["w1t"])
+        w2 = oracle.from_bf16_bits(inputs["w2"])
+        nb = (n + 127) // 128
+        x0 = oracle.from_bf16_bits(inputs["x"][0])
+        x1 = oracle.from_bf16_bits(inputs["x"][1])
+        for b in range(nb):
+            r0, r1 = b * 128, min(n, b * 128 + 128)
+            a0, y0, sc = oracle.mlp_dense(x0[r0:r1], w1t, None, w2, None, np.zeros((r1 - r0, h)))
+            t0 = time.perf_counter()
+            idx = oracle.identify_topk(sc.astype(np.float32), k)
+            oracle.mlp_sparse(x1[r0:r1], w1t, None, w2, a0, y0, idx)
+            t_mlp += time.perf_counter() - t0
+            n_mlp += 1
+            if t_mlp > budget_s / 2:
+                break
+        desc.append(f"MLP {n_mlp}/{nb} row blocks")
+    if w["kk"]:
+        n, H, kk = w["n"], w["heads"], w["kk"]
+        nb = (n + 127) // 128
+        scale = 1.0 / np.sqrt(HEAD_DIM)
+        done = False
+        for hh in range(H):
+            q0, k0, v0 = (oracle.from_bf16_bits(a[hh]) for a in inputs["qkv"][0])
+            q1, k1, v1 = (oracle.from_bf16_bits(a[hh]) for a in inputs["qkv"][1])
+            for b in range(nb):
+                r0, r1 = b * 128, min(n, b * 128 + 128)
+                m, den, num, o, sc = oracle.attn_dense(q0[r0:r1], k0, v0, scale)
+                idx = oracle.identify_topk(sc.astype(np.float32), kk)
+                nr, dr = oracle.attn_rest(q0[r0:r1], k0, v0, m, idx, scale)
+                t0 = time.perf_counter()
+                oracle.attn_sparse(q1[r0:r1], k1, v1, m, nr, dr, idx, scale)
+                t_att += time.perf_counter() - t0
+                n_att += 1
+                if t_att > budget_s / 2:
+                    done = True
+                    break
+            if done:
+                break
+        desc.append(f"attention {n_att}/{H * nb} (head, query block) pairs")
+    t_full = 0.0
+    if n_mlp:
+        t_full += t_mlp / n_mlp * ((w["n"] + 127) // 128)
+    if n_att:
+        t_full += t_att / n_att * (w["heads"] * ((w["n"] + 127) // 128))
+    fl = flops_mlp(w) + flops_attn(w)
+    return {"value": round(fl / t_full / 1e12, 6), "unit": "TFLOP/s", "cores": blas_threads(),
+            "kind": "oracle",
+            "sample": "; ".join(desc) + f" of one sparse step, fp64 NumPy, scaled to the full step "
+                      f"({t_full * 1e3:.0f} ms/step extrapolated; sampled {t_mlp + t_att:.1f} s)",
+            "ms_per_step": round(t_full * 1e3, 3)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="flux", choices=sorted(WORKLOADS))
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synthetic as syn
+    from dynamic_column_sparse_amd import lib
+    from dynamic_column_sparse_amd.layers import AttnDelta, MLPDelta
+
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    T = w["steps"]
+
+    def up(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    t0 = time.time()
+    inputs = {}
+    mlp = att = None
+    xs = qkv = []
+    if w["k"]:
+        inputs["w1t"], inputs["w2"] = syn.mlp_weights(0, w["d"], w["h"])
+        inputs["x"] = syn.activation_walk(0, "X", T, w["n"], w["d"])
+        xs = [up(x) for x in inputs["x"]]
+        mlp = MLPDelta(up(inputs["w1t"]), up(inputs["w2"]), w["n"], w["k"])
+    if w["kk"]:
+        walks = [syn.heads_walk(0, t, T, w["heads"], w["n"]) for t in "QKV"]
+        inputs["qkv"] = [[walks[i][s] for i in range(3)] for s in range(T)]
+        qkv = [[up(a) for a in step] for step in inputs["qkv"]]
+        att = AttnDelta(w["n"], w["heads"], w["kk"], dev)
+    torch.cuda.synchronize()
+    log(f"inputs ready ({time.time() - t0:.1f} s): workload {args.workload} {w}")
+
+    stream = torch.cuda.current_stream()
+
+    def refresh(t):
+        if mlp:
+            mlp.step(xs[t], refresh=True)
+        if att:
+            att.step(*qkv[t], refresh=True)
+
+    def sparse(t):
+        if mlp:
+            mlp.step(xs[t], refresh=False)
+        if att:
+            att.step(*qkv[t], refresh=False)
+
+    refresh(0)
+    for i in range(args.warmup):
+        sparse(1 + i % (T - 1))
+    torch.cuda.synchronize()
+    log("warmup done")
+
+    lib.chipmunk_timing_enable(True)
+    torch.cuda.synchronize()
+    ts = time.perf_counter()
+    for i in range(args.steps):
+        sparse(1 + i % (T - 1))
+    torch.cuda.synchronize()
+    te = time.perf_counter()
+    lib.chipmunk_timing_enable(False)
+    ms_per_step = (te - ts) * 1e3 / args.steps
+    names = lib.kernel_names()
+    kern = {}
+    for kid, name in enumerate(names):
+        tot, cnt = lib.chipmunk_timing_read(kid)
+        if cnt:
+            kern[name] = {"ms_total": tot, "launches": cnt, "avg_us": tot / cnt * 1e3}
+    log(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step")
+
+    # dense refresh step, for the loop total (not part of the sparse-step metric)
+    torch.cuda.synchronize()
+    tr = time.perf_counter()
+    reps = 2
+    for _ in range(reps):
+        refresh(0)
+    torch.cuda.synchronize()
+    refresh_ms = (time.perf_counter() - tr) * 1e3 / reps
+
+    fl = flops_mlp(w) + flops_attn(w)
+    tflops = fl / (ms_per_step * 1e-3) / 1e12
+
+    table = {}
+    for name, r in kern.items():
+        amount, bound = kernel_work(name, w)
+        ent = {"avg_us": round(r["avg_us"], 3), "launches": r["launches"],
+               "share": round(r["ms_total"] / max(1e-12, sum(v["ms_total"] for v in kern.values())), 4)}
+        if amount is not None:
+            ach = amount / (r["avg_us"] * 1e-6)
+            if bound == "mfma":
+                ent.update(achieved=round(ach / 1e12, 2), unit="TFLOP/s", frac=round(ach / 1e12 / PEAK_BF16_TFLOPS, 4))
+            else:
+                ent.update(achieved=round(ach / 1e9, 1), unit="GB/s", frac=round(ach / 1e9 / PEAK_HBM_GBS, 4))
+        table[name] = ent
+    dom = max((n for n in kern if kernel_work(n, w)[0] is not None), key=lambda n: kern[n]["ms_total"])
+    amount, bound = kernel_work(dom, w)
+    avg_s = kern[dom]["avg_us"] * 1e-6
+    if bound == "mfma":
+        roof = {"bound": "mfma", "achieved": round(amount / avg_s / 1e12, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(amount / avg_s / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    else:
+        roof = {"bound": "hbm", "achieved": round(amount / avg_s / 1e9, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(amount / avg_s / 1e9 / PEAK_HBM_GBS, 4)}
+    roof["kernel"] = dom
+    roof["avg_us"] = round(kern[dom]["avg_us"], 3)
+    roof["traffic"] = traffic_for(dom, args.workload)
+
+    out = {
+        "metric": "ms/step and effective TFLOP/s (% bf16 MFMA peak) for sparse MLP/attn delta",
+        "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded Gaussian weights and drifting activations, real shapes)",
+        "config": {"workload": {"flux": "FLUX.1-dev-shaped sparse step (MLP + attention delta)",
+                                "tiny": "tiny MLP delta", "hunyuan_mlp": "HunyuanVideo-shaped MLP delta",
+                                "hunyuan_attn": "HunyuanVideo-shaped attention delta"}[args.workload],
+                   "tokens": w["n"], "d_model": w["d"], "d_hidden": w["h"], "mlp_keep": w["k"],
+                   "heads": w["heads"], "head_dim": HEAD_DIM if w["heads"] else 0, "attn_keep": w["kk"],
+                   "row_block": 128},
+        "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "flop_per_step": fl,
+        "roofline": roof,
+        "kernels": table,
+        "refresh_ms": round(refresh_ms, 4),
+        "loop_ms": {"steps": T, "dense": 1, "sparse": T - 1,
+                    "total": round(refresh_ms + (T - 1) * ms_per_step, 4)},
+        "source_digest": source_digest(),
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        cb = cpu_baseline(w, {**inputs, "x": inputs.get("x", [None, None])[:2],
+                              "qkv": inputs.get("qkv", [None, None])[:2]}, args.cpu_budget)
+        out["cpu_baseline"] = cb
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -107,6 +107,46 @@ def heads_activations(seed: int, tag: str, step: int, heads: int, n: int, dim: i
     return out
 
 
+def activation_walk(seed: int, tag: str, steps: int, n: int, cols: int, head: int = 0) -> list:
+    """bf16 bits [n, cols] of a drifting activation at steps 0 .. steps-1, generated
+    incrementally (same values as ``activations`` at each step)."""
+    nb = (n + ROW_BLOCK - 1) // ROW_BLOCK
+    out = [np.empty((n, cols), np.uint16) for _ in range(steps)]
+    t = TAG[tag]
+
+    def one(b):
+        r0, r1 = _block_rows(n, b)
+        x = stream(seed, t, 0, head, b).standard_normal((r1 - r0, cols), dtype=np.float32)
+        out[0][r0:r1] = f32_to_bf16_bits(x)
+        for s in range(1, steps):
+            x = x + DRIFT * stream(seed, t, s, head, b).standard_normal((r1 - r0, cols), dtype=np.float32)
+            out[s][r0:r1] = f32_to_bf16_bits(x)
+
+    with ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(one, range(nb)))
+    return out
+
+
+def heads_walk(seed: int, tag: str, steps: int, heads: int, n: int, dim: int = 128) -> list:
+    """bf16 bits [heads, n, dim] of Q, K or V at steps 0 .. steps-1 (incremental)."""
+    nb = (n + ROW_BLOCK - 1) // ROW_BLOCK
+    out = [np.empty((heads, n, dim), np.uint16) for _ in range(steps)]
+    t = TAG[tag]
+
+    def one(job):
+        h, b = job
+        r0, r1 = _block_rows(n, b)
+        x = stream(seed, t, 0, h, b).standard_normal((r1 - r0, dim), dtype=np.float32)
+        out[0][h, r0:r1] = f32_to_bf16_bits(x)
+        for s in range(1, steps):
+            x = x + DRIFT * stream(seed, t, s, h, b).standard_normal((r1 - r0, dim), dtype=np.float32)
+            out[s][h, r0:r1] = f32_to_bf16_bits(x)
+
+    with ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(one, [(h, b) for h in range(heads) for b in range(nb)]))
+    return out
+
+
 def weight(seed: int, tag: str, rows: int, cols: int, fan_in: int) -> np.ndarray:
     """bf16 bits [rows, cols] of N(0,1) * 1/sqrt(fan_in) (standard deviation 1/sqrt(fan_in))."""
     nb = (rows + ROW_BLOCK - 1) // ROW_BLOCK

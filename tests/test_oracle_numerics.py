@@ -70,3 +70,17 @@ def test_gelu_tanh_library_and_identities():
     # a value computed by hand: u = sqrt(2/pi) * (1 + 0.044715) at z = 1
     u = math.sqrt(2 / math.pi) * 1.044715
     assert abs(gelu_tanh(np.array([1.0]))[0] - 0.5 * (1 + math.tanh(u))) < 1e-15
+
+
+def test_incremental_walk_matches_per_step_generation():
+    import synthetic as syn
+    w = syn.activation_walk(3, "X", 4, 300, 64)
+    for t in range(4):
+        np.testing.assert_array_equal(w[t], syn.activations(3, "X", t, 300, 64))
+    hw = syn.heads_walk(3, "K", 3, 2, 200)
+    for t in range(3):
+        np.testing.assert_array_equal(hw[t], syn.heads_activations(3, "K", t, 2, 200))
+    # bf16 packing of the generator agrees with torch's conversion
+    x = syn.walk_block(3, 1, 2, 0, 0, 128, 64)
+    np.testing.assert_array_equal(syn.f32_to_bf16_bits(x).view(np.int16),
+                                  torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy())
