@@ -48,7 +48,7 @@ int check_mlp(const chipmunk_mlp* L, bool need_score) {
   if (!L) return fail(CHIPMUNK_E_NULLPTR, "layer is NULL");
   if (L->n < 1) return fail(CHIPMUNK_E_SHAPE, "n must be >= 1 (got %lld)", (long long)L->n);
   if (L->d < 128 || L->d % 128 != 0) return fail(CHIPMUNK_E_SHAPE, "d must be a positive multiple of 128 (got %d)", L->d);
-  if (L->h < 1) return fail(CHIPMUNK_E_SHAPE, "h must be >= 1 (got %d)", L->h);
+  if (L->h < 64 || L->h % 64 != 0) return fail(CHIPMUNK_E_SHAPE, "h must be a positive multiple of 64 (got %d)", L->h);
   if (chipmunk::row_blocks(L->n) > kMaxGridY)
     return fail(CHIPMUNK_E_SHAPE, "n too large: %lld row blocks exceed %lld", (long long)chipmunk::row_blocks(L->n),
                 (long long)kMaxGridY);
@@ -83,9 +83,11 @@ int check_bf16_in(const void* p, const char* name) {
   return CHIPMUNK_OK;
 }
 
+// D tiles [nb][kp][128] (kp = k rounded up to 64).
 size_t sparse_mlp_ws(int64_t n, int32_t k) {
-  return (size_t)chipmunk::row_blocks(n) * (size_t)k * chipmunk::kRowBlock * sizeof(uint16_t);
+  return (size_t)chipmunk::row_blocks(n) * (size_t)chipmunk::padded_k(k) * chipmunk::kRowBlock * sizeof(uint16_t);
 }
+
 
 }  // namespace
 
@@ -198,8 +200,6 @@ extern "C" size_t chipmunk_workspace_bytes(int op, int64_t n, int32_t d, int32_t
 
 extern "C" int chipmunk_dense_step(int kind, const void* layer, const uint16_t* x_or_q, const uint16_t* k,
                                    const uint16_t* v, float* out, void* ws, size_t ws_bytes, void* stream) {
-  (void)ws;
-  (void)ws_bytes;
   try {
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (!layer) return fail(CHIPMUNK_E_NULLPTR, "layer is NULL");
@@ -211,6 +211,10 @@ extern "C" int chipmunk_dense_step(int kind, const void* layer, const uint16_t* 
       if (k || v) return fail(CHIPMUNK_E_SHAPE, "k and v must be NULL for an MLP layer");
       if (!out) return fail(CHIPMUNK_E_NULLPTR, "out (y) is NULL");
       if (!aligned(out, 16)) return fail(CHIPMUNK_E_ALIGN, "out (y) must be 16-byte aligned");
+      (void)ws;
+      (void)ws_bytes;
+      // The second product reads the freshly written activation cache directly
+      // ([nb][h][128] is the [unit][row] layout it streams).
       hipError_t e = chipmunk::launch_mlp_gemm1(true, x_or_q, L->w1t, L->b1, nullptr, L->a_cache, nullptr, nullptr,
                                                 L->score, L->n, L->d, L->h, L->h, s);
       if (e != hipSuccess) return hip_status(e, "mlp_gemm1 (dense) launch");
@@ -275,7 +279,7 @@ extern "C" int chipmunk_sparse_mlp_delta(const chipmunk_mlp* L, const uint16_t* 
     hipError_t e = chipmunk::launch_mlp_gemm1(false, x, L->w1t, L->b1, idx, L->a_cache, dbuf, a_new_packed, nullptr,
                                               L->n, L->d, L->h, k, s);
     if (e != hipSuccess) return hip_status(e, "mlp_gemm1 (sparse) launch");
-    e = chipmunk::launch_mlp_gemm2(false, dbuf, L->w2, idx, nullptr, y, L->n, L->d, L->h, k, k, s);
+    e = chipmunk::launch_mlp_gemm2(false, dbuf, L->w2, idx, nullptr, y, L->n, L->d, L->h, k, chipmunk::padded_k(k), s);
     return hip_status(e, "mlp_gemm2 (sparse) launch");
   } catch (...) {
     return fail(CHIPMUNK_E_INTERNAL, "internal error in chipmunk_sparse_mlp_delta");

@@ -279,6 +279,7 @@ __global__ __launch_bounds__(256, 1) void attn_sparse(const uint16_t* __restrict
   __shared__ __align__(16) uint16_t sK[2][KT][LDK];
   __shared__ __align__(16) uint16_t sV[2][KT][LDV];
   __shared__ float sDen[kRowBlock];
+  __shared__ int sIdx[3][KT];   // gathered key ids of the next three tiles
   const int nb = (int)row_blocks(n);
   int hh, b;
   head_block(heads, nb, hh, b);
@@ -304,7 +305,7 @@ __global__ __launch_bounds__(256, 1) void attn_sparse(const uint16_t* __restrict
     const int c = tid + 256 * i, row = c >> 4, col = (c & 15) * 8;                            \
     const int j = (t_) * KT + row;                                                            \
     if (j < kk) {                                                                             \
-      const int64_t key = clamp_index(S[j], nn);                                              \
+      const int64_t key = sIdx[(t_) % 3][row];                                                \
       rk[i] = *(const uint4*)(kh + key * 128 + col);                                          \
       rv[i] = *(const uint4*)(vh + key * 128 + col);                                          \
     } else {                                                                                  \
@@ -320,6 +321,18 @@ __global__ __launch_bounds__(256, 1) void attn_sparse(const uint16_t* __restrict
     for (int r = 0; r < 16; ++r) acc[ni][r] = 0.f;
   float dpart = 0.f;
   const int ntiles = (kk + KT - 1) / KT;
+  // Index ring: slot t%3 holds the key ids of tile t, loaded two tiles ahead so
+  // no K/V row load waits on its index load.
+  auto key_of = [&](int t, int r) -> int {
+    const int j = t * KT + r;
+    return j < kk ? clamp_index(S[j], nn) : 0;
+  };
+  if (tid < KT) {
+    sIdx[0][tid] = key_of(0, tid);
+    sIdx[1][tid] = key_of(1, tid);
+    sIdx[2][tid] = key_of(2, tid);
+  }
+  __syncthreads();
   if (ntiles > 0) {
     SP_LOAD(0);
     KV_STORE(0);
@@ -327,9 +340,11 @@ __global__ __launch_bounds__(256, 1) void attn_sparse(const uint16_t* __restrict
   __syncthreads();
   for (int t = 0; t < ntiles; ++t) {
     const int buf = t & 1;
+    int pre = 0;
     if (t + 1 < ntiles) {
       SP_LOAD(t + 1);
     }
+    if (tid < KT) pre = key_of(t + 3, tid);
 #pragma unroll
     for (int kt2 = 0; kt2 < 2; ++kt2) {
       const f32x16_t sacc = scores_t(&sK[buf][0][0], kt2 * 32, qf, lane);
@@ -355,6 +370,7 @@ __global__ __launch_bounds__(256, 1) void attn_sparse(const uint16_t* __restrict
     if (t + 1 < ntiles) {
       KV_STORE(buf ^ 1);
     }
+    if (tid < KT) sIdx[t % 3][tid] = pre;
     __syncthreads();
   }
 #undef SP_LOAD

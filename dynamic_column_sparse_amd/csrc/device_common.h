@@ -59,16 +59,120 @@ __device__ __forceinline__ bf16x8_t tr_operand(const uint16_t* tile, int ld, int
   return __builtin_bit_cast(bf16x8_t, v);
 }
 
+// ---- direct global -> LDS loads (gfx950 global_load_lds_dwordx4) ----------
+// Each lane's 16 bytes land at lds + 16 * lane: one instruction fills 1 KB of
+// LDS (wave-uniform destination, passed in M0) from 64 arbitrary 16-byte
+// global chunks, with no register staging.  Completion is tracked by vmcnt like
+// any vector load.
+//
+// Issued through inline assembly on purpose: the compiler cannot tell which
+// LDS bytes such a load writes, so for the builtin form it drains every
+// outstanding vector load (vmcnt(0)) before any later LDS read of the same
+// buffer, which would empty the prefetch ring each K-step.  Here the kernels
+// order these loads themselves: wait_vmcnt for the stage, then barrier(), and
+// only then read it.  The instruction has no register outputs; the compiler's
+// own vmcnt waits stay correct because extra loads it does not count can only
+// make a vmcnt(N) wait stricter.
+__device__ __forceinline__ void dma16(const void* g, void* lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds);
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, off"
+      :
+      : "v"(g), "s"(m0)
+      : "memory", "m0");
+}
+// 4-byte variant: 64 lanes x 4 bytes = 256 contiguous LDS bytes (e.g. 64 ids).
+__device__ __forceinline__ void dma4(const void* g, void* lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds);
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %0, off"
+      :
+      : "v"(g), "s"(m0)
+      : "memory", "m0");
+}
+
+// Wait until at most N vector-memory instructions of this wave are in flight
+// (also waits for this wave's LDS instructions).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
+}
+// Workgroup barrier without the release/acquire fences of __syncthreads (which
+// would wait for every outstanding global load, draining the prefetch ring).
+// Callers order their own LDS traffic with wait_vmcnt before it.
+__device__ __forceinline__ void barrier() { __builtin_amdgcn_s_barrier(); }
+
+// K-contiguous tiles (rows of 64 bf16 = 8 chunks of 16 bytes): chunk c of row r
+// is stored at chunk c ^ swz8(r).  16-byte reads of one chunk by consecutive
+// rows then hit distinct banks in groups of 8 and of 16 lanes.
+__device__ __forceinline__ int swz8(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+// Tiles read with the transposing read ([k][col] rows): 32-byte column pairs
+// (q = col / 16) of row r are stored at pair q ^ swzp(r).  The 4 rows x 2 pairs
+// that 32 lanes of one transposing read touch then land in distinct banks.
+__device__ __forceinline__ int swzp(int r) { return (r & 3) << 1; }
+
+// One 32x32x16 operand from a swizzled [k][col] tile (row_bytes per row), in
+// the reduction order of tr_operand.
+__device__ __forceinline__ bf16x8_t tr_operand_swz(const unsigned char* tile, int row_bytes, int k0, int cb,
+                                                   int lane) {
+  const int G = lane >> 4, i = lane & 15;
+  const int col = cb + (G & 1) * 16 + (i & 3) * 4;
+  const int kr = k0 + (G >> 1) * 4 + (i >> 2);
+  const int off = (((col >> 4) ^ swzp(kr)) << 5) + ((col & 15) << 1);
+  i16x4_t lo = lds_read_tr16((const uint16_t*)(tile + kr * row_bytes + off));
+  i16x4_t hi = lds_read_tr16((const uint16_t*)(tile + (kr + 8) * row_bytes + off));
+  typedef short i16x8_t __attribute__((ext_vector_type(8)));
+  i16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+__device__ __forceinline__ uint32_t word_of(const uint4& v, int i) {
+  return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
+}
+
+// 8x8 transpose of bf16: in[r] holds elements (r, 0..7) of an 8x8 block as 4
+// dwords; out[c] receives elements (0..7, c).  32 byte permutes.
+__device__ __forceinline__ void transpose8x8_bf16(const uint4 (&in)[8], uint4 (&out)[8]) {
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+    const uint32_t o0 = __builtin_amdgcn_perm(word_of(in[1], c >> 1), word_of(in[0], c >> 1), sel);
+    const uint32_t o1 = __builtin_amdgcn_perm(word_of(in[3], c >> 1), word_of(in[2], c >> 1), sel);
+    const uint32_t o2 = __builtin_amdgcn_perm(word_of(in[5], c >> 1), word_of(in[4], c >> 1), sel);
+    const uint32_t o3 = __builtin_amdgcn_perm(word_of(in[7], c >> 1), word_of(in[6], c >> 1), sel);
+    out[c] = make_uint4(o0, o1, o2, o3);
+  }
+}
+
 // GELU, tanh form: 0.5 z (1 + tanh(u)), u = sqrt(2/pi) (z + 0.044715 z^3),
 // evaluated as z / (1 + exp(-2u)) (the same function: 0.5 (1 + tanh u) is the
-// logistic function of 2u).
+// logistic function of 2u), with the hardware reciprocal (about 1 ulp; the
+// result is rounded to bf16 next).  exp(-2u) overflowing to +inf gives z * 0.
 __device__ __forceinline__ float gelu_tanh(float z) {
   const float c = 0.7978845608028654f;
   const float u = c * (z + 0.044715f * z * z * z);
-  return z / (1.0f + __expf(-2.0f * u));
+  return z * __builtin_amdgcn_rcpf(1.0f + __expf(-2.0f * u));
 }
 
 __device__ __forceinline__ int clamp_index(int j, int hi) { return j < 0 ? 0 : (j >= hi ? hi - 1 : j); }
+
+// Workgroups are handed to the 8 XCDs round-robin by linear id.  This maps the
+// linear id to a unit index so that each XCD runs one contiguous range of units
+// (in unit order): units that share data then share that XCD's L2.  Launch
+// 8 * ceil(units / 8) workgroups; ids mapped past `units` have no work.
+__device__ __forceinline__ int xcd_unit(int linear_id, int units) {
+  const int per = (units + 7) >> 3;
+  return (linear_id & 7) * per + (linear_id >> 3);
+}
+__host__ __device__ inline int xcd_grid(int units) { return ((units + 7) >> 3) << 3; }
 
 // Sum 16 per-lane values over the 32 lanes of each half-wave with one exchange
 // per halving: after the exchanges lane l holds the total of value

@@ -31,6 +31,9 @@ void timing_before(int kid, hipStream_t s);
 void timing_after(int kid, hipStream_t s);
 
 __host__ __device__ inline int64_t row_blocks(int64_t n) { return (n + kRowBlock - 1) / kRowBlock; }
+// Rows per block of the D tiles: k rounded up to the 64-wide reduction chunk
+// (the rows past k are zero, so phase 2 streams whole chunks).
+__host__ __device__ inline int padded_k(int k) { return (k + 63) / 64 * 64; }
 
 // MLP phase 1: gathered x W1[:,S] + GELU, then either the sparse epilogue
 // (D tiles, cache writeback) or the dense one (score, full cache write).

@@ -3,30 +3,37 @@
 // Phase 1 (mlp_gemm1): one workgroup per (128-row block b, tile of BN gathered
 // hidden units).  The tile's hidden units are rows of W1^T ([h][d], one
 // contiguous 2*d-byte row each), so gathering them is a set of coalesced row
-// reads; the x rows of block b are contiguous too.  Both operands stream through
-// double-buffered LDS tiles in K-chunks of 64 and feed the bf16 matrix cores
-// (32x32x16, fp32 accumulate).  Epilogue per element: + b1, GELU (tanh form),
-// round to bf16, then
+// reads; the x rows of block b are contiguous too.  Both operands stream
+// through a 3-stage LDS ring in K-chunks of 64, filled by direct global->LDS
+// loads two chunks ahead, and feed the bf16 matrix cores (32x32x16, fp32
+// accumulate).  Epilogue per element: + b1, GELU (tanh form), round to bf16, then
 //   sparse: D = a_new - a_cache (exact in fp32, rounded to bf16 as the next
-//           product's operand) -> D tiles; a_new -> cache (fused writeback) or
-//           a packed buffer;
-//   dense:  score[b][j] = sum over real rows |a_new - a_cache|; a_new -> cache.
+//           product's operand); a_new -> cache (fused writeback) or a packed
+//           buffer;
+//   dense:  D = a_new; score[b][j] = sum over real rows |a_new - a_cache|;
+//           a_new -> cache.
 // Phase 2 (mlp_gemm2): one workgroup per (block b, BN output columns); the
-// reduction runs over the block's k gathered hidden units: D tile rows
-// ([nb][k][128]) times the gathered W2 rows ([h][d], contiguous per unit).  Both
-// tiles sit in LDS as they come from memory ([unit][column]) and are read with
-// the transposing LDS read, so no shuffle is needed to put the reduction index
-// in registers.  y rows are read, added to and written once (no atomics: every
-// output element has exactly one writer, so results are deterministic).
+// reduction runs over the block's gathered hidden units: D tile rows
+// ([nb][kp][128], or the activation cache itself for the dense step) times the
+// gathered W2 rows ([h][d], contiguous per unit).  Both tiles are copied into
+// LDS as they lie in memory ([unit][column]) by direct global->LDS loads and
+// read back with the transposing LDS read, so no register staging is needed.
+// y rows are read, added to and written once (no atomics: every output element
+// has exactly one writer, so results are deterministic).
+//
+// Work order: units are numbered tile-major (all row blocks of one column tile
+// consecutively) and each XCD runs one contiguous range of them.  Row blocks
+// that run together then gather weight rows from the same range of hidden units
+// (index sets are ascending), which that XCD's L2 serves after the first fetch.
 #include "device_common.h"
 #include "internal.h"
 
 namespace chipmunk {
 namespace {
 
-constexpr int BM = 128;      // rows per block (one row block)
-constexpr int BK = 64;       // reduction chunk
-constexpr int LDA = BK + 8;  // padded K-contiguous row: 144 B (16-byte reads conflict-free)
+constexpr int BM = 128;   // rows per block (one row block)
+constexpr int BK = 64;    // reduction chunk
+constexpr int NS = 3;     // LDS ring stages: one consumed, two in flight
 
 template <int BN, bool DENSE>
 __global__ __launch_bounds__(256, 1) void mlp_gemm1(const uint16_t* __restrict__ x,
@@ -36,61 +43,59 @@ __global__ __launch_bounds__(256, 1) void mlp_gemm1(const uint16_t* __restrict__
                                                     uint16_t* __restrict__ a_cache,
                                                     uint16_t* __restrict__ dbuf,
                                                     uint16_t* __restrict__ a_packed,
-                                                    float* __restrict__ score, int64_t n, int d, int h, int k) {
-  constexpr int WN = BN / 2;                 // columns per wave (2x2 wave grid)
-  constexpr int NI = WN / 32;                // 32-wide column subtiles per wave
-  constexpr int MI = 2;                      // 32-row subtiles per wave (64 rows)
-  constexpr int A_CH = BM * BK / 8 / 256;    // 16-byte chunks per thread, x tile
-  constexpr int B_CH = BN * BK / 8 / 256;    // 16-byte chunks per thread, W1^T tile
+                                                    float* __restrict__ score, int64_t n, int d, int h, int k,
+                                                    int kp) {
+  constexpr int WN = BN / 2;          // columns per wave (2x2 wave grid)
+  constexpr int NI = WN / 32;         // 32-wide column subtiles per wave
+  constexpr int MI = 2;               // 32-row subtiles per wave (64 rows)
+  constexpr int A_INS = BM / 8 / 4;   // DMA instructions per wave per stage (8 rows each), x tile
+  constexpr int B_INS = BN / 8 / 4;   // same, W1^T tile
+  constexpr int L = A_INS + B_INS;    // DMA instructions per thread per stage
+  constexpr int A_BYTES = BM * 128;
+  constexpr int STAGE = (BM + BN) * 128;
 
-  __shared__ __align__(16) uint16_t sA[2][BM][LDA];
-  __shared__ __align__(16) uint16_t sB[2][BN][LDA];
+  __shared__ __align__(16) unsigned char smem[NS * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int b = blockIdx.y;
-  const int c0 = blockIdx.x * BN;
+  const int kcols = DENSE ? h : k;
+  const int nb = (int)row_blocks(n), ntiles = (kcols + BN - 1) / BN;
+  const int u = xcd_unit(blockIdx.x, ntiles * nb);
+  if (u >= ntiles * nb) return;
+  const int b = u % nb;
+  const int c0 = (u / nb) * BN;
   const int64_t r0 = (int64_t)b * BM;
   const int rows = (int)(n - r0 < BM ? n - r0 : BM);
-  const int kcols = DENSE ? h : k;
 
-  const uint16_t* a_src[A_CH];
-  bool a_ok[A_CH];
+  // Source of the 16-byte chunk this lane fills in each DMA instruction: row
+  // (instruction's first row + lane/8), physical chunk lane%8, logical chunk
+  // (lane%8) ^ swz8(row).  Rows past the data are clamped to a valid row: their
+  // products only reach output rows/columns the epilogue never stores.
+  const int lrow = lane >> 3, pch = lane & 7;
+  const uint16_t* asrc[A_INS];
 #pragma unroll
-  for (int i = 0; i < A_CH; ++i) {
-    const int c = tid + 256 * i, row = c >> 3, col8 = c & 7;
-    a_ok[i] = row < rows;
-    a_src[i] = x + (r0 + (a_ok[i] ? row : 0)) * (int64_t)d + col8 * 8;
+  for (int i = 0; i < A_INS; ++i) {
+    const int r = (wave * A_INS + i) * 8 + lrow;
+    const int rg = r < rows ? r : rows - 1;
+    asrc[i] = x + (r0 + rg) * (int64_t)d + ((pch ^ swz8(r)) << 3);
   }
-  const uint16_t* b_src[B_CH];
-  bool b_ok[B_CH];
+  const uint16_t* bsrc[B_INS];
 #pragma unroll
-  for (int i = 0; i < B_CH; ++i) {
-    const int c = tid + 256 * i, row = c >> 3, col8 = c & 7;
-    const int p = c0 + row;
-    b_ok[i] = p < kcols;
+  for (int i = 0; i < B_INS; ++i) {
+    const int r = (wave * B_INS + i) * 8 + lrow;
+    const int p = c0 + r;
     int j = 0;
-    if (b_ok[i]) j = DENSE ? p : clamp_index(idx[(int64_t)b * k + p], h);
-    b_src[i] = w1t + (int64_t)j * d + col8 * 8;
+    if (p < kcols) j = DENSE ? p : clamp_index(idx[(int64_t)b * k + p], h);
+    bsrc[i] = w1t + (int64_t)j * d + ((pch ^ swz8(r)) << 3);
   }
 
-  uint4 ra[A_CH], rb[B_CH];
-  const uint4 z4 = make_uint4(0, 0, 0, 0);
-#define G1_LOAD(kt_)                                                                          \
-  _Pragma("unroll") for (int i = 0; i < A_CH; ++i) {                                          \
-    if (a_ok[i]) ra[i] = *(const uint4*)(a_src[i] + (kt_) * BK); else ra[i] = z4;             \
-  }                                                                                           \
-  _Pragma("unroll") for (int i = 0; i < B_CH; ++i) {                                          \
-    if (b_ok[i]) rb[i] = *(const uint4*)(b_src[i] + (kt_) * BK); else rb[i] = z4;             \
-  }
-#define G1_STORE(buf_)                                                                        \
-  _Pragma("unroll") for (int i = 0; i < A_CH; ++i) {                                          \
-    const int c = tid + 256 * i;                                                              \
-    *(uint4*)&sA[buf_][c >> 3][(c & 7) * 8] = ra[i];                                          \
-  }                                                                                           \
-  _Pragma("unroll") for (int i = 0; i < B_CH; ++i) {                                          \
-    const int c = tid + 256 * i;                                                              \
-    *(uint4*)&sB[buf_][c >> 3][(c & 7) * 8] = rb[i];                                          \
+#define G1_ISSUE(kt_, buf_)                                                                 \
+  {                                                                                         \
+    unsigned char* st_ = smem + (buf_) * STAGE;                                             \
+    _Pragma("unroll") for (int i = 0; i < A_INS; ++i)                                       \
+        dma16(asrc[i] + (kt_) * BK, st_ + (wave * A_INS + i) * 1024);                       \
+    _Pragma("unroll") for (int i = 0; i < B_INS; ++i)                                       \
+        dma16(bsrc[i] + (kt_) * BK, st_ + A_BYTES + (wave * B_INS + i) * 1024);             \
   }
 
   f32x16_t acc[MI][NI];
@@ -101,95 +106,131 @@ __global__ __launch_bounds__(256, 1) void mlp_gemm1(const uint16_t* __restrict__
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
 
+  // Epilogue column ids and biases, fetched before the main loop so their
+  // latency hides under it.
+  int jcol[NI];
+  bool valid[NI];
+  float bias[NI];
+#pragma unroll
+  for (int ni = 0; ni < NI; ++ni) {
+    const int p = c0 + wn * WN + ni * 32 + (lane & 31);
+    valid[ni] = p < kcols;
+    jcol[ni] = valid[ni] ? (DENSE ? p : clamp_index(idx[(int64_t)b * k + p], h)) : 0;
+    bias[ni] = (valid[ni] && b1) ? b1[jcol[ni]] : 0.f;
+  }
+
+  // Operand reads: lane l reads row (base + l%32), logical chunk 2s + l/32.  Every
+  // row base is a multiple of 32, so the swizzle depends on the lane only.
+  const int sw = swz8(lane & 31);
   const int KT = d / BK;
-  G1_LOAD(0);
-  G1_STORE(0);
-  __syncthreads();
+  G1_ISSUE(0, 0);
+  if (KT > 1) G1_ISSUE(1, 1);
   for (int kt = 0; kt < KT; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < KT) {
-      G1_LOAD(kt + 1);
-    }
+    if (kt + 1 < KT)
+      wait_vmcnt<L>();
+    else
+      wait_vmcnt<0>();
+    barrier();
+    if (kt + 2 < KT) G1_ISSUE(kt + 2, (kt + 2) % NS);
+    const unsigned char* st = smem + (kt % NS) * STAGE;
 #pragma unroll
     for (int s = 0; s < BK / 16; ++s) {
+      const int coff = (((2 * s + (lane >> 5)) ^ sw) << 4);
       bf16x8_t af[MI], bfr[NI];
-      const int ko = s * 16 + (lane >> 5) * 8;
 #pragma unroll
-      for (int mi = 0; mi < MI; ++mi) af[mi] = *(const bf16x8_t*)&sA[buf][wm * 64 + mi * 32 + (lane & 31)][ko];
+      for (int mi = 0; mi < MI; ++mi)
+        af[mi] = *(const bf16x8_t*)(st + (wm * 64 + mi * 32 + (lane & 31)) * 128 + coff);
 #pragma unroll
-      for (int ni = 0; ni < NI; ++ni) bfr[ni] = *(const bf16x8_t*)&sB[buf][wn * WN + ni * 32 + (lane & 31)][ko];
+      for (int ni = 0; ni < NI; ++ni)
+        bfr[ni] = *(const bf16x8_t*)(st + A_BYTES + (wn * WN + ni * 32 + (lane & 31)) * 128 + coff);
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = mfma32(af[mi], bfr[ni], acc[mi][ni]);
     }
-    if (kt + 1 < KT) {
-      G1_STORE(buf ^ 1);
-    }
-    __syncthreads();
   }
-#undef G1_LOAD
-#undef G1_STORE
+#undef G1_ISSUE
 
   // ---- epilogue ----
-  float colsum[NI];
+  // a_new = bf16(GELU(acc + b1)) is staged in the (now idle) LDS ring as
+  // [tile column][128 rows], so that the cache columns (256 contiguous bytes
+  // each) are then read and written as whole 16-byte chunks by 16 consecutive
+  // lanes.  Chunk c (rows 8c..8c+7) of tile column t is stored at chunk
+  // c ^ (t % 16); the column's hidden-unit id follows the tile.
+  constexpr int CI = BN / 16;                // tile columns per thread in the coalesced phase
+  static_assert(BN * 256 + BN * 4 <= NS * STAGE, "staging tile exceeds the LDS ring");
+  unsigned char* stile = smem;
+  int* scol = (int*)(smem + BN * 256);
+  barrier();                                 // every wave is done reading the ring
 #pragma unroll
   for (int ni = 0; ni < NI; ++ni) {
-    colsum[ni] = 0.f;
-    const int jl = wn * WN + ni * 32 + (lane & 31);
-    const int p = c0 + jl;
-    const bool valid = p < kcols;
-    int j = 0;
-    if (valid) j = DENSE ? p : clamp_index(idx[(int64_t)b * k + p], h);
-    const float bias = (valid && b1) ? b1[j] : 0.f;
-    uint16_t* cache_col = a_cache + ((int64_t)b * h + j) * BM;
+    const int t = wn * WN + ni * 32 + (lane & 31);
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi) {
+    for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int m0 = wm * 64 + mi * 32 + g * 8 + (lane >> 5) * 4;
         float av[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float a = bf2f(f2bf(gelu_tanh(acc[mi][ni][g * 4 + e] + bias)));
-          av[e] = (m0 + e < rows) ? a : 0.f;
-        }
-        if (!valid) continue;
-        const uint2 old = *(const uint2*)(cache_col + m0);
-        const float o0 = bf2f(old.x & 0xffffu), o1 = bf2f(old.x >> 16);
-        const float o2 = bf2f(old.y & 0xffffu), o3 = bf2f(old.y >> 16);
-        const uint2 nw = make_uint2(pack2(av[0], av[1]), pack2(av[2], av[3]));
-        if (DENSE) {
-          colsum[ni] += (m0 + 0 < rows ? fabsf(av[0] - o0) : 0.f) + (m0 + 1 < rows ? fabsf(av[1] - o1) : 0.f) +
-                        (m0 + 2 < rows ? fabsf(av[2] - o2) : 0.f) + (m0 + 3 < rows ? fabsf(av[3] - o3) : 0.f);
-          *(uint2*)(cache_col + m0) = nw;
-        } else {
-          const uint2 dd = make_uint2(pack2(av[0] - o0, av[1] - o1), pack2(av[2] - o2, av[3] - o3));
-          *(uint2*)(dbuf + ((int64_t)b * k + p) * BM + m0) = dd;
-          if (a_packed)
-            *(uint2*)(a_packed + ((int64_t)b * k + p) * BM + m0) = nw;
-          else
-            *(uint2*)(cache_col + m0) = nw;
-        }
+        for (int e = 0; e < 4; ++e)
+          av[e] = (valid[ni] && m0 + e < rows) ? gelu_tanh(acc[mi][ni][g * 4 + e] + bias[ni]) : 0.f;
+        *(uint2*)(stile + t * 256 + (((m0 >> 3) ^ (t & 15)) << 4) + (m0 & 7) * 2) =
+            make_uint2(pack2(av[0], av[1]), pack2(av[2], av[3]));
       }
+    if (wm == 0 && lane < 32) scol[t] = jcol[ni];
+  }
+  __syncthreads();
+
+  const int ch = tid & 15, tc = tid >> 4;
+  uint4 oldv[CI];
+#pragma unroll
+  for (int i = 0; i < CI; ++i) {
+    const int t = tc + 16 * i;
+    if (c0 + t < kcols)
+      oldv[i] = *(const uint4*)(a_cache + ((int64_t)b * h + scol[t]) * BM + ch * 8);
+    else
+      oldv[i] = make_uint4(0, 0, 0, 0);
+  }
+  float colsum[CI];
+#pragma unroll
+  for (int i = 0; i < CI; ++i) {
+    const int t = tc + 16 * i, p = c0 + t;
+    const uint4 an = *(const uint4*)(stile + t * 256 + ((ch ^ tc) << 4));
+    uint32_t dw[4];
+    colsum[i] = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t a2 = word_of(an, w), o2 = word_of(oldv[i], w);
+      float dv[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const bool live = ch * 8 + w * 2 + e < rows;
+        dv[e] = live ? bf2f((a2 >> (16 * e)) & 0xffffu) - bf2f((o2 >> (16 * e)) & 0xffffu) : 0.f;
+        if (DENSE) colsum[i] += fabsf(dv[e]);
+      }
+      dw[w] = pack2(dv[0], dv[1]);
     }
+    if (p < kcols) {
+      if (DENSE || !a_packed)
+        *(uint4*)(a_cache + ((int64_t)b * h + scol[t]) * BM + ch * 8) = an;
+      else
+        *(uint4*)(a_packed + ((int64_t)b * k + p) * BM + ch * 8) = an;
+    }
+    // D rows past k (up to the padded count kp) are written as zero, so phase 2
+    // can stream whole 64-row chunks.
+    if (!DENSE && p < kp) *(uint4*)(dbuf + ((int64_t)b * kp + p) * BM + ch * 8) = make_uint4(dw[0], dw[1], dw[2], dw[3]);
   }
   if (DENSE) {
-    // Column L1 over the block's rows: lanes l and l^32 hold the two 4-row halves
-    // of each 8-row group; the wm=1 waves hold rows 64..127.
-    float* sred = (float*)&sA[0][0][0];
+    // Column L1 over the block's rows: the 16 lanes of a column hold 8 rows each.
 #pragma unroll
-    for (int ni = 0; ni < NI; ++ni) {
-      colsum[ni] += __shfl_xor(colsum[ni], 32);
-      if (wm == 1 && lane < 32) sred[wn * WN + ni * 32 + lane] = colsum[ni];
-    }
-    __syncthreads();
-    if (wm == 0 && lane < 32) {
-#pragma unroll
-      for (int ni = 0; ni < NI; ++ni) {
-        const int p = c0 + wn * WN + ni * 32 + lane;
-        if (p < kcols) score[(int64_t)b * h + p] = colsum[ni] + sred[wn * WN + ni * 32 + lane];
-      }
+    for (int i = 0; i < CI; ++i) {
+      float v = colsum[i];
+      v += __shfl_xor(v, 1);
+      v += __shfl_xor(v, 2);
+      v += __shfl_xor(v, 4);
+      v += __shfl_xor(v, 8);
+      const int p = c0 + tc + 16 * i;
+      if (ch == 0 && p < kcols) score[(int64_t)b * h + p] = v;
     }
   }
 }
@@ -199,56 +240,77 @@ __global__ __launch_bounds__(256, 1) void mlp_gemm2(const uint16_t* __restrict__
                                                     const uint16_t* __restrict__ w2,
                                                     const int32_t* __restrict__ idx,
                                                     const float* __restrict__ b2, float* __restrict__ y,
-                                                    int64_t n, int d, int h, int k, int kc) {
+                                                    int64_t n, int d, int h, int k, int kp) {
   constexpr int WN = BN / 2, NI = WN / 32, MI = 2;
-  constexpr int LDD = BM + 16;   // 288-byte rows for the transposing reads
-  constexpr int LDW = BN + 16;
-  constexpr int D_CH = BK * BM / 8 / 256;   // 4
-  constexpr int W_CH = BK * BN / 8 / 256;   // BN/32
-  constexpr int WROW = BN / 8;              // 16-byte chunks per W2 tile row
+  constexpr int D_ROWB = BM * 2;             // 256-byte D tile rows
+  constexpr int W_ROWB = BN * 2;             // W2 tile rows
+  constexpr int D_BYTES = BK * D_ROWB;       // 16 KB
+  constexpr int STAGE = D_BYTES + BK * W_ROWB;
+  constexpr int D_INS = D_BYTES / 1024 / 4;  // DMA instructions per wave per stage
+  constexpr int W_INS = BK * W_ROWB / 1024 / 4;
+  constexpr int D_RPI = 1024 / D_ROWB;       // rows per DMA instruction
+  constexpr int W_RPI = 1024 / W_ROWB;
 
-  __shared__ __align__(16) uint16_t sD[2][BK][LDD];
-  __shared__ __align__(16) uint16_t sW[2][BK][LDW];
+  __shared__ __align__(16) unsigned char smem[NS * STAGE];
+  // W2 row ids, ring of 8 chunks (chunk c in slot c % 8), filled by 4-byte
+  // direct loads six chunks ahead (sparse step only).
+  __shared__ __align__(16) int sIdx[8][BK];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int b = blockIdx.y;
-  const int n0 = blockIdx.x * BN;
+  const int nb = (int)row_blocks(n), ntn = d / BN;
+  const int u = xcd_unit(blockIdx.x, ntn * nb);
+  if (u >= ntn * nb) return;
+  const int b = u % nb;
+  const int n0 = (u / nb) * BN;
   const int64_t r0 = (int64_t)b * BM;
   const int rows = (int)(n - r0 < BM ? n - r0 : BM);
-  const int kk = DENSE ? h : k;
-  const uint16_t* sblk = src + (int64_t)b * kc * BM;
+  const int kk = DENSE ? h : k;             // real reduction length (rows kk .. kp of D are zero)
+  const uint16_t* sblk = src + (int64_t)b * kp * BM;
   const int32_t* sidx = DENSE ? nullptr : idx + (int64_t)b * k;
 
-  uint4 rd[D_CH], rw[W_CH];
-  const uint4 z4 = make_uint4(0, 0, 0, 0);
-#define G2_LOAD(kt_)                                                                          \
-  {                                                                                           \
-    const int j0 = (kt_) * BK;                                                                \
-    _Pragma("unroll") for (int i = 0; i < D_CH; ++i) {                                        \
-      const int c = tid + 256 * i, row = c >> 4, col = (c & 15) * 8;                          \
-      const int jr = j0 + row;                                                                \
-      if (jr < kk) rd[i] = *(const uint4*)(sblk + (int64_t)jr * BM + col); else rd[i] = z4;   \
-    }                                                                                         \
-    _Pragma("unroll") for (int i = 0; i < W_CH; ++i) {                                        \
-      const int c = tid + 256 * i, row = c / WROW, col = (c % WROW) * 8;                      \
-      const int jr = j0 + row;                                                                \
-      if (jr < kk) {                                                                          \
-        const int g = DENSE ? jr : clamp_index(sidx[jr], h);                                  \
-        rw[i] = *(const uint4*)(w2 + (int64_t)g * d + n0 + col);                              \
-      } else {                                                                                \
-        rw[i] = z4;                                                                           \
-      }                                                                                       \
-    }                                                                                         \
+  // Per-lane DMA geometry.  D: row (instruction's first row + lane/16), 32-byte
+  // pair ((lane%16)/2 ^ swzp(row)), half lane%2.  W2: row (instruction's first
+  // row + lane/(BN/8)), pair ((lane%(BN/8))/2 ^ swzp(row)), half lane%2.
+  const int d_lr = lane / (D_ROWB / 16), d_pc = lane % (D_ROWB / 16);
+  const int w_lr = lane / (W_ROWB / 16), w_pc = lane % (W_ROWB / 16);
+  int d_off[D_INS], w_row[W_INS], w_off[W_INS];
+#pragma unroll
+  for (int i = 0; i < D_INS; ++i) {
+    const int r = (wave * D_INS + i) * D_RPI + d_lr;
+    d_off[i] = r * BM + ((((d_pc >> 1) ^ swzp(r)) << 1) | (d_pc & 1)) * 8;
   }
-#define G2_STORE(buf_)                                                                        \
-  _Pragma("unroll") for (int i = 0; i < D_CH; ++i) {                                          \
-    const int c = tid + 256 * i;                                                              \
-    *(uint4*)&sD[buf_][c >> 4][(c & 15) * 8] = rd[i];                                         \
-  }                                                                                           \
-  _Pragma("unroll") for (int i = 0; i < W_CH; ++i) {                                          \
-    const int c = tid + 256 * i;                                                              \
-    *(uint4*)&sW[buf_][c / WROW][(c % WROW) * 8] = rw[i];                                     \
+#pragma unroll
+  for (int i = 0; i < W_INS; ++i) {
+    const int r = (wave * W_INS + i) * W_RPI + w_lr;
+    w_row[i] = r;
+    w_off[i] = ((((w_pc >> 1) ^ swzp(r)) << 1) | (w_pc & 1)) * 8;
+  }
+  // Ids of chunk t for this lane's W2 rows (identity for the dense step).
+  auto load_ids = [&](int t, int (&ids)[W_INS]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < W_INS; ++i) {
+      const int j = t * BK + w_row[i];
+      ids[i] = DENSE ? (j < kk ? j : 0) : clamp_index(sIdx[t & 7][w_row[i]], h);
+    }
+  };
+  // 4-byte direct load of chunk t's 64 ids into ring slot t % 8 (wave 0; lanes
+  // past k read id 0 of the block, whose D rows are zero).
+  auto id_dma = [&](int t) __attribute__((always_inline)) {
+    if (!DENSE && wave == 0) {
+      const int j = t * BK + lane;
+      dma4(sidx + (j < kk ? j : 0), &sIdx[t & 7][0]);
+    }
+  };
+
+#define G2_ISSUE(kt_, buf_, ids_)                                                           \
+  {                                                                                         \
+    unsigned char* st_ = smem + (buf_) * STAGE;                                             \
+    const uint16_t* dsrc_ = sblk + (int64_t)(kt_) * BK * BM;                                \
+    _Pragma("unroll") for (int i = 0; i < D_INS; ++i)                                       \
+        dma16(dsrc_ + d_off[i], st_ + (wave * D_INS + i) * 1024);                           \
+    _Pragma("unroll") for (int i = 0; i < W_INS; ++i)                                       \
+        dma16(w2 + (int64_t)ids_[i] * d + n0 + w_off[i], st_ + D_BYTES + (wave * W_INS + i) * 1024); \
   }
 
   f32x16_t acc[MI][NI];
@@ -259,36 +321,55 @@ __global__ __launch_bounds__(256, 1) void mlp_gemm2(const uint16_t* __restrict__
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
 
-  const int KT = (kk + BK - 1) / BK;
-  if (KT > 0) {
-    G2_LOAD(0);
-    G2_STORE(0);
-  }
+  // Pipeline.  Iteration kt: (a) wait for chunk kt's loads and barrier; (b) wave 0
+  // requests the ids of chunk kt+6; (c) chunk kt+2 is requested with ids read in
+  // the previous iteration; (d) the ids of chunk kt+3 are read from the ring;
+  // (e) chunk kt is multiplied.  Every global load in the loop is a direct-to-LDS
+  // load, so no register result is waited on inside it.  Wave 0 has one more
+  // load in flight per iteration (the id chunk, issued before the stage loads
+  // so that waiting for a stage also covers the ids issued with it).
+  const int KT = kp / BK;
+  constexpr int L = D_INS + W_INS;
+#pragma unroll
+  for (int t = 0; t < 6; ++t) id_dma(t);
+  wait_vmcnt<0>();
   __syncthreads();
+  int ids_a[W_INS], ids_b[W_INS];
+  load_ids(0, ids_a);
+  if (KT > 0) G2_ISSUE(0, 0, ids_a);
+  load_ids(1, ids_b);
+  if (KT > 1) G2_ISSUE(1, 1, ids_b);
+  load_ids(2, ids_a);
   for (int kt = 0; kt < KT; ++kt) {
-    const int buf = kt & 1;
     if (kt + 1 < KT) {
-      G2_LOAD(kt + 1);
+      if (wave == 0)
+        wait_vmcnt<L + 1>();
+      else
+        wait_vmcnt<L>();
+    } else {
+      wait_vmcnt<0>();
     }
+    barrier();
+    if (kt + 6 < KT) id_dma(kt + 6);
+    if (kt + 2 < KT) G2_ISSUE(kt + 2, (kt + 2) % NS, ids_a);
+    load_ids(kt + 3, ids_b);
+    const unsigned char* st = smem + (kt % NS) * STAGE;
 #pragma unroll
     for (int s = 0; s < BK / 16; ++s) {
       bf16x8_t af[MI], bfr[NI];
 #pragma unroll
-      for (int mi = 0; mi < MI; ++mi) af[mi] = tr_operand(&sD[buf][0][0], LDD, s * 16, wm * 64 + mi * 32, lane);
+      for (int mi = 0; mi < MI; ++mi) af[mi] = tr_operand_swz(st, D_ROWB, s * 16, wm * 64 + mi * 32, lane);
 #pragma unroll
-      for (int ni = 0; ni < NI; ++ni) bfr[ni] = tr_operand(&sW[buf][0][0], LDW, s * 16, wn * WN + ni * 32, lane);
+      for (int ni = 0; ni < NI; ++ni) bfr[ni] = tr_operand_swz(st + D_BYTES, W_ROWB, s * 16, wn * WN + ni * 32, lane);
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = mfma32(af[mi], bfr[ni], acc[mi][ni]);
     }
-    if (kt + 1 < KT) {
-      G2_STORE(buf ^ 1);
-    }
-    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < W_INS; ++i) ids_a[i] = ids_b[i];
   }
-#undef G2_LOAD
-#undef G2_STORE
+#undef G2_ISSUE
 
 #pragma unroll
   for (int ni = 0; ni < NI; ++ni) {
@@ -316,29 +397,30 @@ __global__ __launch_bounds__(256, 1) void mlp_gemm2(const uint16_t* __restrict__
 hipError_t launch_mlp_gemm1(bool dense, const uint16_t* x, const uint16_t* w1t, const float* b1,
                             const int32_t* idx, uint16_t* a_cache, uint16_t* dbuf, uint16_t* a_packed,
                             float* score, int64_t n, int d, int h, int k, hipStream_t s) {
-  const int64_t nb = row_blocks(n);
+  const int nb = (int)row_blocks(n);
   const int cols = dense ? h : k;
+  const int kp = padded_k(k);
   // 256-wide tiles when they waste little of the last tile, else 128-wide.
   const int t256 = (cols + 255) / 256, t128 = (cols + 127) / 128;
   const bool wide = t128 > 1 && (int64_t)t256 * 256 * 100 <= (int64_t)cols * 106;
   const int kid = dense ? K_MLP_GEMM1_DENSE : K_MLP_GEMM1_SPARSE;
   timing_before(kid, s);
   if (wide) {
-    dim3 grid(t256, (unsigned)nb);
+    const dim3 grid((unsigned)xcd_grid(t256 * nb));
     if (dense)
       hipLaunchKernelGGL((mlp_gemm1<256, true>), grid, dim3(256), 0, s, x, w1t, b1, idx, a_cache, dbuf, a_packed,
-                         score, n, d, h, k);
+                         score, n, d, h, k, kp);
     else
       hipLaunchKernelGGL((mlp_gemm1<256, false>), grid, dim3(256), 0, s, x, w1t, b1, idx, a_cache, dbuf,
-                         a_packed, score, n, d, h, k);
+                         a_packed, score, n, d, h, k, kp);
   } else {
-    dim3 grid(t128, (unsigned)nb);
+    const dim3 grid((unsigned)xcd_grid(t128 * nb));
     if (dense)
       hipLaunchKernelGGL((mlp_gemm1<128, true>), grid, dim3(256), 0, s, x, w1t, b1, idx, a_cache, dbuf, a_packed,
-                         score, n, d, h, k);
+                         score, n, d, h, k, kp);
     else
       hipLaunchKernelGGL((mlp_gemm1<128, false>), grid, dim3(256), 0, s, x, w1t, b1, idx, a_cache, dbuf,
-                         a_packed, score, n, d, h, k);
+                         a_packed, score, n, d, h, k, kp);
   }
   hipError_t e = hipGetLastError();
   timing_after(kid, s);
@@ -346,22 +428,22 @@ hipError_t launch_mlp_gemm1(bool dense, const uint16_t* x, const uint16_t* w1t, 
 }
 
 hipError_t launch_mlp_gemm2(bool dense, const uint16_t* src, const uint16_t* w2, const int32_t* idx,
-                            const float* b2, float* y, int64_t n, int d, int h, int k, int kc, hipStream_t s) {
-  const int64_t nb = row_blocks(n);
+                            const float* b2, float* y, int64_t n, int d, int h, int k, int kp, hipStream_t s) {
+  const int nb = (int)row_blocks(n);
   const int kid = dense ? K_MLP_GEMM2_DENSE : K_MLP_GEMM2_SPARSE;
   timing_before(kid, s);
   if (d % 256 == 0) {
-    dim3 grid(d / 256, (unsigned)nb);
+    const dim3 grid((unsigned)xcd_grid(d / 256 * nb));
     if (dense)
-      hipLaunchKernelGGL((mlp_gemm2<256, true>), grid, dim3(256), 0, s, src, w2, idx, b2, y, n, d, h, k, kc);
+      hipLaunchKernelGGL((mlp_gemm2<256, true>), grid, dim3(256), 0, s, src, w2, idx, b2, y, n, d, h, k, kp);
     else
-      hipLaunchKernelGGL((mlp_gemm2<256, false>), grid, dim3(256), 0, s, src, w2, idx, b2, y, n, d, h, k, kc);
+      hipLaunchKernelGGL((mlp_gemm2<256, false>), grid, dim3(256), 0, s, src, w2, idx, b2, y, n, d, h, k, kp);
   } else {
-    dim3 grid(d / 128, (unsigned)nb);
+    const dim3 grid((unsigned)xcd_grid(d / 128 * nb));
     if (dense)
-      hipLaunchKernelGGL((mlp_gemm2<128, true>), grid, dim3(256), 0, s, src, w2, idx, b2, y, n, d, h, k, kc);
+      hipLaunchKernelGGL((mlp_gemm2<128, true>), grid, dim3(256), 0, s, src, w2, idx, b2, y, n, d, h, k, kp);
     else
-      hipLaunchKernelGGL((mlp_gemm2<128, false>), grid, dim3(256), 0, s, src, w2, idx, b2, y, n, d, h, k, kc);
+      hipLaunchKernelGGL((mlp_gemm2<128, false>), grid, dim3(256), 0, s, src, w2, idx, b2, y, n, d, h, k, kp);
   }
   hipError_t e = hipGetLastError();
   timing_after(kid, s);

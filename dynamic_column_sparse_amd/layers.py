@@ -46,7 +46,7 @@ class MLPDelta:
         self.layer = lib.mlp_layer(n, d, h, w1t, w2, self.a_cache, self.score, b1, b2)
 
     def dense(self, x: torch.Tensor, stream=None):
-        lib.chipmunk_dense_step(lib.MLP, self.layer, x, None, None, self.y, stream=stream)
+        lib.chipmunk_dense_step(lib.MLP, self.layer, x, None, None, self.y, self.ws, stream=stream)
 
     def identify(self, stream=None):
         lib.chipmunk_identify_topk(self.score, self.nb, self.h, self.k, self.idx, stream=stream)

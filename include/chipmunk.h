@@ -18,7 +18,8 @@
  * the refresh-step row max, numerator and denominator.
  *
  * Conventions (all entry points)
- *  - Every tensor is a caller-owned HIP DEVICE pointer on the current device.
+ *  - Every tensor is a caller-owned HIP DEVICE pointer on the current device,
+ *    16-byte aligned except idx, score, b1, b2, m and den (4-byte aligned).
  *    bf16 tensors are passed as their raw 16-bit patterns (uint16_t).  The
  *    library allocates no device memory; scratch space is caller-provided and
  *    sized by chipmunk_workspace_bytes().
@@ -80,7 +81,7 @@ enum chipmunk_op {
 /* One MLP layer: y = gelu(x W1 + b1) W2 + b2, plus its caches.
  *   n      tokens (>= 1)
  *   d      model width, a multiple of 128
- *   h      hidden width (>= 1)
+ *   h      hidden width, a multiple of 64
  *   w1t    [h][d] bf16, row j = hidden unit j's input weights (an nn.Linear
  *          fc1.weight as stored); column j of W1 is row j here, so a gathered
  *          hidden unit is one contiguous row
@@ -168,7 +169,9 @@ int chipmunk_identify_topk(const float* score, int64_t rows, int64_t cols, int32
  * order, for chipmunk_cache_writeback) leaving the cache unchanged.
  * x [n][d] bf16, idx [nb][k] int32, y [n][d] fp32.  0 <= k <= h; k = 0 leaves
  * every buffer bit-unchanged.  ws must hold chipmunk_workspace_bytes(
- * CHIPMUNK_OP_SPARSE_MLP, n, d, h, k) bytes (the D tiles). */
+ * CHIPMUNK_OP_SPARSE_MLP, n, d, h, k) bytes: the D tiles, [nb][kp][128] bf16
+ * (same block-column-major order as the cache; kp = k rounded up to 64, rows
+ * past k are written as zero). */
 int chipmunk_sparse_mlp_delta(const chipmunk_mlp* layer, const uint16_t* x, const int32_t* idx,
                               int32_t k, float* y, uint16_t* a_new_packed, void* ws, size_t ws_bytes,
                               void* stream);
@@ -193,7 +196,9 @@ int chipmunk_sparse_attn_delta(const chipmunk_attn* layer, const uint16_t* q, co
 int chipmunk_cache_writeback(const chipmunk_mlp* layer, const uint16_t* a_new_packed, const int32_t* idx,
                              int32_t k, void* stream);
 
-/* Scratch bytes an op needs for these sizes (0 when none).  op: chipmunk_op. */
+/* Scratch bytes an op needs for these sizes (0 when none).  op: chipmunk_op.
+ * CHIPMUNK_OP_SPARSE_MLP: nb*kp*128*2 with kp = k rounded up to 64; the
+ * others: 0. */
 size_t chipmunk_workspace_bytes(int op, int64_t n, int32_t d, int32_t h, int32_t k);
 
 /* Thread-local text of the last failure on this thread ("" if none). */

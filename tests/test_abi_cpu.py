@@ -44,7 +44,7 @@ def test_version_names_workspace(L):
     assert L.chipmunk_abi_version() == 1
     names = L.kernel_names()
     assert "mlp_gemm1_sparse" in names and "attn_sparse" in names and "topk_rows" in names
-    assert L.chipmunk_workspace_bytes(L.OP_SPARSE_MLP, 4352, 3072, 12288, 3686) == 34 * 3686 * 128 * 2
+    assert L.chipmunk_workspace_bytes(L.OP_SPARSE_MLP, 4352, 3072, 12288, 3686) == 34 * 3712 * 128 * 2
     assert L.chipmunk_workspace_bytes(L.OP_SPARSE_MLP, 300, 128, 640, 0) == 0
     assert L.chipmunk_workspace_bytes(L.OP_DENSE_MLP, 300, 128, 640, 200) == 0
 
@@ -68,7 +68,7 @@ def _code(L, fn, *a, **kw):
 
 
 @pytest.mark.parametrize("case,code", [
-    (dict(n=0), 2), (dict(d=100), 2), (dict(d=64), 2), (dict(h=0), 2),
+    (dict(n=0), 2), (dict(d=100), 2), (dict(d=64), 2), (dict(h=0), 2), (dict(h=100), 2),
     (dict(w1t=None), 1), (dict(a_cache=None), 1), (dict(w2=FAKE + 8), 4),
 ])
 def test_sparse_mlp_rejects_bad_layer(L, case, code):
@@ -99,9 +99,10 @@ def test_sparse_mlp_argument_checks(L):
 def test_dense_step_checks(L):
     lay = _mlp(L)
     f = L.chipmunk_dense_step
-    assert _code(L, f, L.MLP, lay, FAKE, FAKE, None, FAKE, stream=0) == 2          # k given for an MLP
-    assert _code(L, f, L.MLP, lay, FAKE, None, None, None, stream=0) == 1          # out NULL
-    assert _code(L, f, L.MLP, _mlp(L, score=None), FAKE, None, None, FAKE, stream=0) == 1
+    big = 1 << 40
+    assert _code(L, f, L.MLP, lay, FAKE, FAKE, None, FAKE, FAKE, stream=0, ws_bytes=big) == 2   # k given for an MLP
+    assert _code(L, f, L.MLP, lay, FAKE, None, None, None, FAKE, stream=0, ws_bytes=big) == 1   # out NULL
+    assert _code(L, f, L.MLP, _mlp(L, score=None), FAKE, None, None, FAKE, FAKE, stream=0, ws_bytes=big) == 1
     assert _code(L, f, 7, lay, FAKE, None, None, FAKE, stream=0) == 2              # unknown kind
     att = L.attn_layer(300, 2, FAKE, FAKE, FAKE, FAKE, head_dim=64)
     assert _code(L, f, L.ATTN, att, FAKE, FAKE, FAKE, FAKE, stream=0) == 3         # head_dim 64
