@@ -67,6 +67,47 @@ def walk_block(seed: int, tag: int, step: int, head: int, block: int, rows: int,
     return x
 
 
+def _chunk_blocks(cols: int) -> int:
+    """Row blocks per generation job: about 2M floats, so a job's buffers stay small
+    while its draws are large enough to run outside the interpreter lock."""
+    return max(1, (1 << 21) // (ROW_BLOCK * cols))
+
+
+def _walk_rows(seed: int, t: int, head: int, n: int, cols: int, b0: int, b1: int, steps: int, emit) -> None:
+    """Advance the master walk of row blocks b0..b1-1 (one contiguous row range)
+    through steps 0..steps-1, calling ``emit(step, r0, r1, x)`` with the float32
+    walk after each step.  Same values as ``walk_block`` on every block."""
+    r0, r1 = b0 * ROW_BLOCK, min(n, b1 * ROW_BLOCK)
+    x = np.empty((r1 - r0, cols), np.float32)
+    eps = np.empty_like(x) if steps > 1 else None
+    for s in range(steps):
+        dst = x if s == 0 else eps
+        for b in range(b0, b1):
+            a, c = _block_rows(n, b)
+            stream(seed, t, s, head, b).standard_normal(out=dst[a - r0:c - r0], dtype=np.float32)
+        if s:
+            np.multiply(eps, DRIFT, out=eps)
+            np.add(x, eps, out=x)
+        emit(s, r0, r1, x)
+
+
+def _run_walks(seed: int, t: int, heads: int, n: int, cols: int, steps: int, emit) -> None:
+    nb = (n + ROW_BLOCK - 1) // ROW_BLOCK
+    ch = _chunk_blocks(cols)
+    jobs = [(h, b, min(nb, b + ch)) for h in range(heads) for b in range(0, nb, ch)]
+
+    def one(job):
+        h, b0, b1 = job
+        _walk_rows(seed, t, h, n, cols, b0, b1, steps, lambda s, r0, r1, x: emit(h, s, r0, r1, x))
+
+    if len(jobs) > 1:
+        with ThreadPoolExecutor(_threads()) as ex:
+            list(ex.map(one, jobs))
+    else:
+        for j in jobs:
+            one(j)
+
+
 def activations(seed: int, tag: str, step: int, n: int, cols: int, head: int = 0,
                 blocks=None) -> np.ndarray:
     """bf16 bits [rows, cols] of a drifting activation (X, or one head of Q/K/V).
@@ -74,76 +115,71 @@ def activations(seed: int, tag: str, step: int, n: int, cols: int, head: int = 0
     ``blocks``: iterable of 128-row block indices to generate (default: all).  The
     result stacks the requested blocks' rows in the given order.
     """
-    nb = (n + ROW_BLOCK - 1) // ROW_BLOCK
-    blocks = list(range(nb)) if blocks is None else list(blocks)
     t = TAG[tag]
+    if blocks is None:
+        out = np.empty((n, cols), np.uint16)
 
-    def one(b):
-        r0, r1 = _block_rows(n, b)
-        return f32_to_bf16_bits(walk_block(seed, t, step, head, b, r1 - r0, cols))
+        def emit(h, s, r0, r1, x):
+            if s == step:
+                out[r0:r1] = f32_to_bf16_bits(x)
 
-    if len(blocks) > 4:
+        nb = (n + ROW_BLOCK - 1) // ROW_BLOCK
+        ch = _chunk_blocks(cols)
+        jobs = [(b, min(nb, b + ch)) for b in range(0, nb, ch)]
+
+        def one(job):
+            _walk_rows(seed, t, head, n, cols, job[0], job[1], step + 1, lambda s, r0, r1, x: emit(head, s, r0, r1, x))
+
         with ThreadPoolExecutor(_threads()) as ex:
-            parts = list(ex.map(one, blocks))
-    else:
-        parts = [one(b) for b in blocks]
+            list(ex.map(one, jobs))
+        return out
+    parts = []
+    for b in blocks:
+        r0, r1 = _block_rows(n, b)
+        parts.append(f32_to_bf16_bits(walk_block(seed, t, step, head, b, r1 - r0, cols)))
     return np.concatenate(parts, axis=0) if parts else np.zeros((0, cols), np.uint16)
 
 
 def heads_activations(seed: int, tag: str, step: int, heads: int, n: int, dim: int = 128) -> np.ndarray:
     """bf16 bits [heads, n, dim] for Q, K or V."""
-    nb = (n + ROW_BLOCK - 1) // ROW_BLOCK
     out = np.empty((heads, n, dim), np.uint16)
-    t = TAG[tag]
 
-    def one(job):
-        h, b = job
-        r0, r1 = _block_rows(n, b)
-        out[h, r0:r1] = f32_to_bf16_bits(walk_block(seed, t, step, h, b, r1 - r0, dim))
+    def emit(h, s, r0, r1, x):
+        if s == step:
+            out[h, r0:r1] = f32_to_bf16_bits(x)
 
-    jobs = [(h, b) for h in range(heads) for b in range(nb)]
-    with ThreadPoolExecutor(_threads()) as ex:
-        list(ex.map(one, jobs))
+    _run_walks(seed, TAG[tag], heads, n, dim, step + 1, emit)
     return out
 
 
 def activation_walk(seed: int, tag: str, steps: int, n: int, cols: int, head: int = 0) -> list:
     """bf16 bits [n, cols] of a drifting activation at steps 0 .. steps-1, generated
     incrementally (same values as ``activations`` at each step)."""
-    nb = (n + ROW_BLOCK - 1) // ROW_BLOCK
     out = [np.empty((n, cols), np.uint16) for _ in range(steps)]
-    t = TAG[tag]
 
-    def one(b):
-        r0, r1 = _block_rows(n, b)
-        x = stream(seed, t, 0, head, b).standard_normal((r1 - r0, cols), dtype=np.float32)
-        out[0][r0:r1] = f32_to_bf16_bits(x)
-        for s in range(1, steps):
-            x = x + DRIFT * stream(seed, t, s, head, b).standard_normal((r1 - r0, cols), dtype=np.float32)
-            out[s][r0:r1] = f32_to_bf16_bits(x)
+    def emit(h, s, r0, r1, x):
+        out[s][r0:r1] = f32_to_bf16_bits(x)
+
+    nb = (n + ROW_BLOCK - 1) // ROW_BLOCK
+    ch = _chunk_blocks(cols)
+    jobs = [(b, min(nb, b + ch)) for b in range(0, nb, ch)]
+
+    def one(job):
+        _walk_rows(seed, TAG[tag], head, n, cols, job[0], job[1], steps, lambda s, r0, r1, x: emit(head, s, r0, r1, x))
 
     with ThreadPoolExecutor(_threads()) as ex:
-        list(ex.map(one, range(nb)))
+        list(ex.map(one, jobs))
     return out
 
 
 def heads_walk(seed: int, tag: str, steps: int, heads: int, n: int, dim: int = 128) -> list:
     """bf16 bits [heads, n, dim] of Q, K or V at steps 0 .. steps-1 (incremental)."""
-    nb = (n + ROW_BLOCK - 1) // ROW_BLOCK
     out = [np.empty((heads, n, dim), np.uint16) for _ in range(steps)]
-    t = TAG[tag]
 
-    def one(job):
-        h, b = job
-        r0, r1 = _block_rows(n, b)
-        x = stream(seed, t, 0, h, b).standard_normal((r1 - r0, dim), dtype=np.float32)
-        out[0][h, r0:r1] = f32_to_bf16_bits(x)
-        for s in range(1, steps):
-            x = x + DRIFT * stream(seed, t, s, h, b).standard_normal((r1 - r0, dim), dtype=np.float32)
-            out[s][h, r0:r1] = f32_to_bf16_bits(x)
+    def emit(h, s, r0, r1, x):
+        out[s][h, r0:r1] = f32_to_bf16_bits(x)
 
-    with ThreadPoolExecutor(_threads()) as ex:
-        list(ex.map(one, [(h, b) for h in range(heads) for b in range(nb)]))
+    _run_walks(seed, TAG[tag], heads, n, dim, steps, emit)
     return out
 
 

@@ -84,3 +84,19 @@ def test_incremental_walk_matches_per_step_generation():
     x = syn.walk_block(3, 1, 2, 0, 0, 128, 64)
     np.testing.assert_array_equal(syn.f32_to_bf16_bits(x).view(np.int16),
                                   torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy())
+
+
+def test_chunked_generation_matches_per_block_streams():
+    # Generation jobs cover several row blocks at once (5 blocks at 3072 columns);
+    # every block must still come from its own (tag, step, head, block) stream.
+    import synthetic as syn
+    from synthetic.gen import TAG, walk_block
+    n, cols = 1500, 3072                               # 12 blocks, last one 92 rows
+    ref = [np.concatenate([syn.f32_to_bf16_bits(walk_block(5, TAG["X"], t, 0, b, min(n, (b + 1) * 128) - b * 128, cols))
+                           for b in range(12)]) for t in range(3)]
+    w = syn.activation_walk(5, "X", 3, n, cols)
+    for t in range(3):
+        np.testing.assert_array_equal(w[t], ref[t])
+        np.testing.assert_array_equal(syn.activations(5, "X", t, n, cols), ref[t])
+    np.testing.assert_array_equal(syn.activations(5, "X", 2, n, cols, blocks=[11, 3]),
+                                  np.concatenate([ref[2][1408:], ref[2][384:512]]))
