@@ -97,6 +97,31 @@ __device__ __forceinline__ void dma4(const void* g, void* lds) {
       : "memory", "m0");
 }
 
+// Forms taking the LDS destination as a 32-bit LDS address that is already
+// wave-uniform (computed from the workgroup's LDS base, the loop counter and a
+// wave index made uniform with readfirstlane), so each load costs one M0 write.
+__device__ __forceinline__ uint32_t lds_addr(const void* lds) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)lds;
+}
+__device__ __forceinline__ void dma16_at(const void* g, uint32_t lds) {
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, off"
+      :
+      : "v"(g), "s"(lds)
+      : "memory", "m0");
+}
+__device__ __forceinline__ void dma4_at(const void* g, uint32_t lds) {
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %0, off"
+      :
+      : "v"(g), "s"(lds)
+      : "memory", "m0");
+}
+
 // Wait until at most N vector-memory instructions of this wave are in flight
 // (also waits for this wave's LDS instructions).
 template <int N>
@@ -113,6 +138,11 @@ __device__ __forceinline__ void barrier() { __builtin_amdgcn_s_barrier(); }
 // is stored at chunk c ^ swz8(r).  16-byte reads of one chunk by consecutive
 // rows then hit distinct banks in groups of 8 and of 16 lanes.
 __device__ __forceinline__ int swz8(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+// 64-byte rows (32 bf16 = 4 chunks of 16 bytes): chunk c of row r is stored at
+// chunk c ^ swz4(r).  Rows r..r+3 share one 256-byte bank window, so the XOR
+// term follows r/4: 16 consecutive rows reading the same logical chunk then
+// cover all 64 banks once.
+__device__ __forceinline__ int swz4(int r) { return (r >> 2) & 3; }
 
 // Tiles read with the transposing read ([k][col] rows): 32-byte column pairs
 // (q = col / 16) of row r are stored at pair q ^ swzp(r).  The 4 rows x 2 pairs
@@ -129,6 +159,22 @@ __device__ __forceinline__ bf16x8_t tr_operand_swz(const unsigned char* tile, in
   const int off = (((col >> 4) ^ swzp(kr)) << 5) + ((col & 15) << 1);
   i16x4_t lo = lds_read_tr16((const uint16_t*)(tile + kr * row_bytes + off));
   i16x4_t hi = lds_read_tr16((const uint16_t*)(tile + (kr + 8) * row_bytes + off));
+  typedef short i16x8_t __attribute__((ext_vector_type(8)));
+  i16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+// Same, in the natural reduction order of a K-contiguous operand: lane l gets
+// column cb + l%32 and rows k0 + (l/32)*8 .. +7 in order, so it pairs with an
+// operand read by plain 16-byte loads from a row-major tile.
+__device__ __forceinline__ bf16x8_t tr_operand_swz_nat(const unsigned char* tile, int row_bytes, int k0, int cb,
+                                                       int lane) {
+  const int G = lane >> 4, i = lane & 15;
+  const int col = cb + (G & 1) * 16 + (i & 3) * 4;
+  const int kr = k0 + (G >> 1) * 8 + (i >> 2);
+  const int off = (((col >> 4) ^ swzp(kr)) << 5) + ((col & 15) << 1);
+  i16x4_t lo = lds_read_tr16((const uint16_t*)(tile + kr * row_bytes + off));
+  i16x4_t hi = lds_read_tr16((const uint16_t*)(tile + (kr + 4) * row_bytes + off));
   typedef short i16x8_t __attribute__((ext_vector_type(8)));
   i16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   return __builtin_bit_cast(bf16x8_t, v);

@@ -36,7 +36,7 @@ constexpr int BK = 64;    // reduction chunk
 constexpr int NS = 3;     // LDS ring stages: one consumed, two in flight
 
 template <int BN, bool DENSE>
-__global__ __launch_bounds__(256, 1) void mlp_gemm1(const uint16_t* __restrict__ x,
+__global__ __launch_bounds__(256, 2) void mlp_gemm1(const uint16_t* __restrict__ x,
                                                     const uint16_t* __restrict__ w1t,
                                                     const float* __restrict__ b1,
                                                     const int32_t* __restrict__ idx,
@@ -48,15 +48,20 @@ __global__ __launch_bounds__(256, 1) void mlp_gemm1(const uint16_t* __restrict__
   constexpr int WN = BN / 2;          // columns per wave (2x2 wave grid)
   constexpr int NI = WN / 32;         // 32-wide column subtiles per wave
   constexpr int MI = 2;               // 32-row subtiles per wave (64 rows)
-  constexpr int A_INS = BM / 8 / 4;   // DMA instructions per wave per stage (8 rows each), x tile
-  constexpr int B_INS = BN / 8 / 4;   // same, W1^T tile
+  constexpr int BK = 32, NS = 3;      // 32-deep K-chunks, 3-stage ring: 72 KB, two workgroups per CU
+  constexpr int ROWB = BK * 2;        // LDS row: 64 bytes = 4 chunks of 16 bytes
+  constexpr int CPR = ROWB / 16, RPI = 1024 / ROWB;   // chunks per row, rows per direct load
+  constexpr int A_INS = BM / RPI / 4; // direct loads per wave per stage, x tile
+  constexpr int B_INS = BN / RPI / 4; // same, W1^T tile
   constexpr int L = A_INS + B_INS;    // DMA instructions per thread per stage
-  constexpr int A_BYTES = BM * 128;
-  constexpr int STAGE = (BM + BN) * 128;
+  constexpr int A_BYTES = BM * ROWB;
+  constexpr int STAGE = (BM + BN) * ROWB;
 
   __shared__ __align__(16) unsigned char smem[NS * STAGE];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, kept in SGPRs
+  const uint32_t smem_lds = lds_addr(smem);
   const int wm = wave >> 1, wn = wave & 1;
   const int kcols = DENSE ? h : k;
   const int nb = (int)row_blocks(n), ntiles = (kcols + BN - 1) / BN;
@@ -71,31 +76,31 @@ __global__ __launch_bounds__(256, 1) void mlp_gemm1(const uint16_t* __restrict__
   // (instruction's first row + lane/8), physical chunk lane%8, logical chunk
   // (lane%8) ^ swz8(row).  Rows past the data are clamped to a valid row: their
   // products only reach output rows/columns the epilogue never stores.
-  const int lrow = lane >> 3, pch = lane & 7;
+  const int lrow = lane / CPR, pch = lane % CPR;
   const uint16_t* asrc[A_INS];
 #pragma unroll
   for (int i = 0; i < A_INS; ++i) {
-    const int r = (wave * A_INS + i) * 8 + lrow;
+    const int r = (wave * A_INS + i) * RPI + lrow;
     const int rg = r < rows ? r : rows - 1;
-    asrc[i] = x + (r0 + rg) * (int64_t)d + ((pch ^ swz8(r)) << 3);
+    asrc[i] = x + (r0 + rg) * (int64_t)d + ((pch ^ swz4(r)) << 3);
   }
   const uint16_t* bsrc[B_INS];
 #pragma unroll
   for (int i = 0; i < B_INS; ++i) {
-    const int r = (wave * B_INS + i) * 8 + lrow;
+    const int r = (wave * B_INS + i) * RPI + lrow;
     const int p = c0 + r;
     int j = 0;
     if (p < kcols) j = DENSE ? p : clamp_index(idx[(int64_t)b * k + p], h);
-    bsrc[i] = w1t + (int64_t)j * d + ((pch ^ swz8(r)) << 3);
+    bsrc[i] = w1t + (int64_t)j * d + ((pch ^ swz4(r)) << 3);
   }
 
 #define G1_ISSUE(kt_, buf_)                                                                 \
   {                                                                                         \
-    unsigned char* st_ = smem + (buf_) * STAGE;                                             \
+    const uint32_t st_ = smem_lds + (buf_) * STAGE;                                         \
     _Pragma("unroll") for (int i = 0; i < A_INS; ++i)                                       \
-        dma16(asrc[i] + (kt_) * BK, st_ + (wave * A_INS + i) * 1024);                       \
+        dma16_at(asrc[i] + (kt_) * BK, st_ + (wave * A_INS + i) * 1024);                    \
     _Pragma("unroll") for (int i = 0; i < B_INS; ++i)                                       \
-        dma16(bsrc[i] + (kt_) * BK, st_ + A_BYTES + (wave * B_INS + i) * 1024);             \
+        dma16_at(bsrc[i] + (kt_) * BK, st_ + A_BYTES + (wave * B_INS + i) * 1024);          \
   }
 
   f32x16_t acc[MI][NI];
@@ -121,7 +126,7 @@ __global__ __launch_bounds__(256, 1) void mlp_gemm1(const uint16_t* __restrict__
 
   // Operand reads: lane l reads row (base + l%32), logical chunk 2s + l/32.  Every
   // row base is a multiple of 32, so the swizzle depends on the lane only.
-  const int sw = swz8(lane & 31);
+  const int sw = swz4(lane & 31);
   const int KT = d / BK;
   G1_ISSUE(0, 0);
   if (KT > 1) G1_ISSUE(1, 1);
@@ -133,21 +138,26 @@ __global__ __launch_bounds__(256, 1) void mlp_gemm1(const uint16_t* __restrict__
     barrier();
     if (kt + 2 < KT) G1_ISSUE(kt + 2, (kt + 2) % NS);
     const unsigned char* st = smem + (kt % NS) * STAGE;
+    // Operand fragments of K-substep s+1 are read while substep s multiplies.
+    bf16x8_t af[2][MI], bfr[2][NI];
+#define G1_FRAG(s_, q_)                                                                              \
+    {                                                                                                \
+      const int coff = (((2 * (s_) + (lane >> 5)) ^ sw) << 4);                                       \
+      _Pragma("unroll") for (int mi = 0; mi < MI; ++mi)                                              \
+        af[q_][mi] = *(const bf16x8_t*)(st + (wm * 64 + mi * 32 + (lane & 31)) * ROWB + coff);       \
+      _Pragma("unroll") for (int ni = 0; ni < NI; ++ni)                                              \
+        bfr[q_][ni] = *(const bf16x8_t*)(st + A_BYTES + (wn * WN + ni * 32 + (lane & 31)) * ROWB + coff); \
+    }
+    G1_FRAG(0, 0);
 #pragma unroll
     for (int s = 0; s < BK / 16; ++s) {
-      const int coff = (((2 * s + (lane >> 5)) ^ sw) << 4);
-      bf16x8_t af[MI], bfr[NI];
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
-        af[mi] = *(const bf16x8_t*)(st + (wm * 64 + mi * 32 + (lane & 31)) * 128 + coff);
-#pragma unroll
-      for (int ni = 0; ni < NI; ++ni)
-        bfr[ni] = *(const bf16x8_t*)(st + A_BYTES + (wn * WN + ni * 32 + (lane & 31)) * 128 + coff);
+      if (s + 1 < BK / 16) G1_FRAG(s + 1, (s + 1) & 1);
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = mfma32(af[mi], bfr[ni], acc[mi][ni]);
+        for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = mfma32(af[s & 1][mi], bfr[s & 1][ni], acc[mi][ni]);
     }
+#undef G1_FRAG
   }
 #undef G1_ISSUE
 
@@ -216,9 +226,36 @@ __global__ __launch_bounds__(256, 1) void mlp_gemm1(const uint16_t* __restrict__
       else
         *(uint4*)(a_packed + ((int64_t)b * k + p) * BM + ch * 8) = an;
     }
-    // D rows past k (up to the padded count kp) are written as zero, so phase 2
-    // can stream whole 64-row chunks.
-    if (!DENSE && p < kp) *(uint4*)(dbuf + ((int64_t)b * kp + p) * BM + ch * 8) = make_uint4(dw[0], dw[1], dw[2], dw[3]);
+    // D replaces a_new in the staging tile: this thread is the only reader and
+    // writer of this 16-byte slot.
+    if (!DENSE) *(uint4*)(stile + t * 256 + ((ch ^ tc) << 4)) = make_uint4(dw[0], dw[1], dw[2], dw[3]);
+  }
+  if (!DENSE) {
+    // D leaves row-major ([block][128 rows][kp]) so phase 2 reads it as a plain
+    // K-contiguous operand.  A 16-lane group transposes 8 units x 16 rows out of
+    // the [unit][row] tile with two transposing reads (units u..u+3, u+4..u+7):
+    // lane j points at unit row u + j/4, tokens 4(j%4)..+3 of its 16-row block,
+    // and receives the 4 units of token j.  Units k..kp of the tile are zero
+    // (their a_new and cached values are zero), so phase 2 can stream whole
+    // 32-unit chunks.
+    __syncthreads();
+    const int grp = lane >> 4, j = lane & 15;
+#pragma unroll 4
+    for (int it = 0; it < BN / 16; ++it) {
+      const int task = it * 16 + wave * 4 + grp;
+      const int u8 = task % (BN / 8), mb = task / (BN / 8);
+      const int p = c0 + u8 * 8;
+      const int mp = mb * 16 + 4 * (j & 3);
+      const int t0 = u8 * 8 + (j >> 2), t1 = t0 + 4;
+      const i16x4_t lo = lds_read_tr16((const uint16_t*)(stile + t0 * 256 + (((mp >> 3) ^ (t0 & 15)) << 4) + (mp & 7) * 2));
+      const i16x4_t hi = lds_read_tr16((const uint16_t*)(stile + t1 * 256 + (((mp >> 3) ^ (t1 & 15)) << 4) + (mp & 7) * 2));
+      if (p < kp) {
+        const int m = mb * 16 + j;
+        const uint4 v = make_uint4((uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16), (uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16),
+                                   (uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16), (uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16));
+        *(uint4*)(dbuf + ((int64_t)b * BM + m) * kp + p) = v;
+      }
+    }
   }
   if (DENSE) {
     // Column L1 over the block's rows: the 16 lanes of a column hold 8 rows each.
@@ -256,7 +293,9 @@ __global__ __launch_bounds__(256, 1) void mlp_gemm2(const uint16_t* __restrict__
   // direct loads six chunks ahead (sparse step only).
   __shared__ __align__(16) int sIdx[8][BK];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, kept in SGPRs
+  const uint32_t smem_lds = lds_addr(smem);
   const int wm = wave >> 1, wn = wave & 1;
   const int nb = (int)row_blocks(n), ntn = d / BN;
   const int u = xcd_unit(blockIdx.x, ntn * nb);
@@ -299,18 +338,18 @@ __global__ __launch_bounds__(256, 1) void mlp_gemm2(const uint16_t* __restrict__
   auto id_dma = [&](int t) __attribute__((always_inline)) {
     if (!DENSE && wave == 0) {
       const int j = t * BK + lane;
-      dma4(sidx + (j < kk ? j : 0), &sIdx[t & 7][0]);
+      dma4_at(sidx + (j < kk ? j : 0), lds_addr(&sIdx[t & 7][0]));
     }
   };
 
 #define G2_ISSUE(kt_, buf_, ids_)                                                           \
   {                                                                                         \
-    unsigned char* st_ = smem + (buf_) * STAGE;                                             \
+    const uint32_t st_ = smem_lds + (buf_) * STAGE;                                         \
     const uint16_t* dsrc_ = sblk + (int64_t)(kt_) * BK * BM;                                \
     _Pragma("unroll") for (int i = 0; i < D_INS; ++i)                                       \
-        dma16(dsrc_ + d_off[i], st_ + (wave * D_INS + i) * 1024);                           \
+        dma16_at(dsrc_ + d_off[i], st_ + (wave * D_INS + i) * 1024);                        \
     _Pragma("unroll") for (int i = 0; i < W_INS; ++i)                                       \
-        dma16(w2 + (int64_t)ids_[i] * d + n0 + w_off[i], st_ + D_BYTES + (wave * W_INS + i) * 1024); \
+        dma16_at(w2 + (int64_t)ids_[i] * d + n0 + w_off[i], st_ + D_BYTES + (wave * W_INS + i) * 1024); \
   }
 
   f32x16_t acc[MI][NI];
@@ -341,8 +380,11 @@ __global__ __launch_bounds__(256, 1) void mlp_gemm2(const uint16_t* __restrict__
   if (KT > 1) G2_ISSUE(1, 1, ids_b);
   load_ids(2, ids_a);
   for (int kt = 0; kt < KT; ++kt) {
+    // Outstanding loads of this wave, newest first: stage kt+1 (L) and, on wave
+    // 0 of the sparse step, the id load of chunk kt+5 if the previous
+    // iteration issued one.  Everything older (stage kt) must be complete.
     if (kt + 1 < KT) {
-      if (wave == 0)
+      if (!DENSE && wave == 0 && kt >= 1 && kt + 5 < KT)
         wait_vmcnt<L + 1>();
       else
         wait_vmcnt<L>();
@@ -354,13 +396,196 @@ __global__ __launch_bounds__(256, 1) void mlp_gemm2(const uint16_t* __restrict__
     if (kt + 2 < KT) G2_ISSUE(kt + 2, (kt + 2) % NS, ids_a);
     load_ids(kt + 3, ids_b);
     const unsigned char* st = smem + (kt % NS) * STAGE;
+    bf16x8_t af[2][MI], bfr[2][NI];
+#define G2_FRAG(s_, q_)                                                                              \
+    {                                                                                                \
+      _Pragma("unroll") for (int mi = 0; mi < MI; ++mi)                                              \
+        af[q_][mi] = tr_operand_swz(st, D_ROWB, (s_) * 16, wm * 64 + mi * 32, lane);                 \
+      _Pragma("unroll") for (int ni = 0; ni < NI; ++ni)                                              \
+        bfr[q_][ni] = tr_operand_swz(st + D_BYTES, W_ROWB, (s_) * 16, wn * WN + ni * 32, lane);       \
+    }
+    G2_FRAG(0, 0);
 #pragma unroll
     for (int s = 0; s < BK / 16; ++s) {
+      if (s + 1 < BK / 16) G2_FRAG(s + 1, (s + 1) & 1);
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = mfma32(af[s & 1][mi], bfr[s & 1][ni], acc[mi][ni]);
+    }
+#undef G2_FRAG
+#pragma unroll
+    for (int i = 0; i < W_INS; ++i) ids_a[i] = ids_b[i];
+  }
+#undef G2_ISSUE
+
+  // Epilogue in two phases (every old y value or bias loaded, then every sum
+  // stored): row offsets depend on d, so the compiler cannot reorder a store
+  // past a later load itself, and one-at-a-time read-modify-writes would each
+  // wait a full memory round trip.
+  float yold[NI][MI][16];
+#pragma unroll
+  for (int ni = 0; ni < NI; ++ni) {
+    const int col = n0 + wn * WN + ni * 32 + (lane & 31);
+    const float bias = (DENSE && b2) ? b2[col] : 0.f;
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = wm * 64 + mi * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        if (DENSE)
+          yold[ni][mi][r] = bias;
+        else
+          yold[ni][mi][r] = m < rows ? y[(r0 + m) * (int64_t)d + col] : 0.f;
+      }
+  }
+#pragma unroll
+  for (int ni = 0; ni < NI; ++ni) {
+    const int col = n0 + wn * WN + ni * 32 + (lane & 31);
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = wm * 64 + mi * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        if (m < rows) y[(r0 + m) * (int64_t)d + col] = yold[ni][mi][r] + acc[mi][ni][r];
+      }
+  }
+}
+
+// Sparse phase 2 over row-major D tiles ([block][128 rows][kp], written by the
+// sparse phase 1).  Four waves side by side (1x4): each wave owns all 128 rows
+// and BN/4 output columns, so per 16-deep K-substep it reads four D fragments
+// with plain 16-byte LDS reads and only BN/128 W2 fragments with the (slower)
+// transposing read.  32-deep K-chunks in a 3-stage ring (72 KB) leave room for
+// two workgroups per CU, which overlap each other's epilogue and barriers.
+template <int BN>
+__global__ __launch_bounds__(256, 2) void mlp_gemm2_rows(const uint16_t* __restrict__ dsrc,
+                                                         const uint16_t* __restrict__ w2,
+                                                         const int32_t* __restrict__ idx, float* __restrict__ y,
+                                                         int64_t n, int d, int h, int k, int kp) {
+  constexpr int BK = 32, NS = 3;
+  constexpr int WN = BN / 4, NI = WN / 32, MI = BM / 32;
+  constexpr int D_ROWB = BK * 2;             // 64-byte D rows (4 chunks)
+  constexpr int W_ROWB = BN * 2;             // W2 tile rows
+  constexpr int D_BYTES = BM * D_ROWB;       // 8 KB
+  constexpr int STAGE = D_BYTES + BK * W_ROWB;
+  constexpr int D_RPI = 1024 / D_ROWB;       // rows per direct load
+  constexpr int W_RPI = 1024 / W_ROWB;
+  constexpr int D_INS = BM / D_RPI / 4;      // direct loads per wave per stage
+  constexpr int W_INS = BK / W_RPI / 4;
+  constexpr int L = D_INS + W_INS;
+
+  __shared__ __align__(16) unsigned char smem[NS * STAGE];
+  // W2 row ids, ring of 8 chunks (chunk c in slot c % 8), filled by 4-byte
+  // direct loads six chunks ahead.
+  __shared__ __align__(16) int sIdx[8][BK];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t smem_lds = lds_addr(smem);
+  const int nb = (int)row_blocks(n), ntn = d / BN;
+  const int u = xcd_unit(blockIdx.x, ntn * nb);
+  if (u >= ntn * nb) return;
+  const int b = u % nb;
+  const int n0 = (u / nb) * BN;
+  const int64_t r0 = (int64_t)b * BM;
+  const int rows = (int)(n - r0 < BM ? n - r0 : BM);
+  const uint16_t* dblk = dsrc + (int64_t)b * BM * kp;
+  const int32_t* sidx = idx + (int64_t)b * k;
+
+  // D: row (instruction's first row + lane/4), physical chunk lane%4, logical
+  // chunk (lane%4) ^ swz4(row).  W2: row (instruction's first row +
+  // lane/(BN/8)), 32-byte pair ((lane%(BN/8))/2 ^ swzp(row)), half lane%2.
+  const int d_lr = lane >> 2, d_pc = lane & 3;
+  const int w_lr = lane / (W_ROWB / 16), w_pc = lane % (W_ROWB / 16);
+  const uint16_t* dsrc_l[D_INS];
+#pragma unroll
+  for (int i = 0; i < D_INS; ++i) {
+    const int r = (wave * D_INS + i) * D_RPI + d_lr;
+    dsrc_l[i] = dblk + (int64_t)r * kp + ((d_pc ^ swz4(r)) << 3);
+  }
+  int w_row[W_INS], w_off[W_INS];
+#pragma unroll
+  for (int i = 0; i < W_INS; ++i) {
+    const int r = (wave * W_INS + i) * W_RPI + w_lr;
+    w_row[i] = r;
+    w_off[i] = ((((w_pc >> 1) ^ swzp(r)) << 1) | (w_pc & 1)) * 8;
+  }
+  // Ids of chunk t for this lane's W2 rows.
+  auto load_ids = [&](int t, int (&ids)[W_INS]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < W_INS; ++i) ids[i] = clamp_index(sIdx[t & 7][w_row[i]], h);
+  };
+  // 4-byte direct load of chunk t's 32 ids into ring slot t % 8 (lanes 0..31 of
+  // wave 0; positions past k read id 0 of the block, whose D columns are zero).
+  auto id_dma = [&](int t) __attribute__((always_inline)) {
+    if (wave == 0 && lane < BK) {
+      const int j = t * BK + lane;
+      dma4_at(sidx + (j < k ? j : 0), lds_addr(&sIdx[t & 7][0]));
+    }
+  };
+
+#define G2R_ISSUE(kt_, buf_, ids_)                                                          \
+  {                                                                                         \
+    const uint32_t st_ = smem_lds + (buf_) * STAGE;                                         \
+    _Pragma("unroll") for (int i = 0; i < D_INS; ++i)                                       \
+        dma16_at(dsrc_l[i] + (kt_) * BK, st_ + (wave * D_INS + i) * 1024);                  \
+    _Pragma("unroll") for (int i = 0; i < W_INS; ++i)                                       \
+        dma16_at(w2 + (int64_t)ids_[i] * d + n0 + w_off[i], st_ + D_BYTES + (wave * W_INS + i) * 1024); \
+  }
+
+  f32x16_t acc[MI][NI];
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
+
+  const int KT = kp / BK;
+  // Prologue: ids of chunks 0..5, then stages 0 and 1.
+  if (wave == 0 && lane < BK) {
+#pragma unroll
+    for (int t = 0; t < 6; ++t)
+      if (t < KT) dma4_at(sidx + (t * BK + lane < k ? t * BK + lane : 0), lds_addr(&sIdx[t][0]));
+  }
+  wait_vmcnt<0>();
+  __syncthreads();
+  int ids_a[W_INS], ids_b[W_INS];
+  load_ids(0, ids_a);
+  G2R_ISSUE(0, 0, ids_a);
+  if (KT > 1) {
+    load_ids(1, ids_a);
+    G2R_ISSUE(1, 1, ids_a);
+  }
+  if (KT > 2) load_ids(2, ids_a);
+
+  const int sw = swz4(lane & 31);
+  for (int kt = 0; kt < KT; ++kt) {
+    // Outstanding loads of this wave, newest first: stage kt+1 (L) and, on wave
+    // 0, the id load of chunk kt+5 if the previous iteration issued one.
+    // Everything older (stage kt) must be complete.
+    if (kt + 1 < KT) {
+      if (wave == 0 && kt >= 1 && kt + 5 < KT)
+        wait_vmcnt<L + 1>();
+      else
+        wait_vmcnt<L>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    barrier();
+    if (kt + 6 < KT) id_dma(kt + 6);
+    if (kt + 2 < KT) G2R_ISSUE(kt + 2, (kt + 2) % NS, ids_a);
+    if (kt + 3 < KT) load_ids(kt + 3, ids_b);
+    const unsigned char* st = smem + (kt % NS) * STAGE;
+#pragma unroll
+    for (int s = 0; s < BK / 16; ++s) {
+      const int coff = (((2 * s + (lane >> 5)) ^ sw) << 4);
       bf16x8_t af[MI], bfr[NI];
 #pragma unroll
-      for (int mi = 0; mi < MI; ++mi) af[mi] = tr_operand_swz(st, D_ROWB, s * 16, wm * 64 + mi * 32, lane);
+      for (int ni = 0; ni < NI; ++ni) bfr[ni] = tr_operand_swz_nat(st + D_BYTES, W_ROWB, s * 16, wave * WN + ni * 32, lane);
 #pragma unroll
-      for (int ni = 0; ni < NI; ++ni) bfr[ni] = tr_operand_swz(st + D_BYTES, W_ROWB, s * 16, wn * WN + ni * 32, lane);
+      for (int mi = 0; mi < MI; ++mi) af[mi] = *(const bf16x8_t*)(st + (mi * 32 + (lane & 31)) * D_ROWB + coff);
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
@@ -369,26 +594,33 @@ __global__ __launch_bounds__(256, 1) void mlp_gemm2(const uint16_t* __restrict__
 #pragma unroll
     for (int i = 0; i < W_INS; ++i) ids_a[i] = ids_b[i];
   }
-#undef G2_ISSUE
+#undef G2R_ISSUE
 
+  // y += acc, one 32-column slice at a time: load all of its old values, then
+  // store all of its sums (row offsets depend on d, so the compiler cannot
+  // overlap one read-modify-write with the next by itself).  Row bases are
+  // wave-uniform; a lane adds one 32-bit offset (its 4-row half and column).
+  const int lane_off = (lane >> 5) * 4 * d + wave * WN + (lane & 31);
+  const int mhalf = (lane >> 5) * 4;
 #pragma unroll
   for (int ni = 0; ni < NI; ++ni) {
-    const int col = n0 + wn * WN + ni * 32 + (lane & 31);
-    const float bias = (DENSE && b2) ? b2[col] : 0.f;
+    float yold[MI][16];
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi) {
+    for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int m = wm * 64 + mi * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-        if (m < rows) {
-          float* yp = y + (r0 + m) * (int64_t)d + col;
-          if (DENSE)
-            *yp = acc[mi][ni][r] + bias;
-          else
-            *yp += acc[mi][ni][r];
-        }
+        const int R = mi * 32 + (r >> 2) * 8 + (r & 3);
+        const float* yrow = y + (r0 + R) * (int64_t)d + n0 + ni * 32;
+        yold[mi][r] = R + mhalf < rows ? yrow[lane_off] : 0.f;
       }
-    }
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int R = mi * 32 + (r >> 2) * 8 + (r & 3);
+        float* yrow = y + (r0 + R) * (int64_t)d + n0 + ni * 32;
+        if (R + mhalf < rows) yrow[lane_off] = yold[mi][r] + acc[mi][ni][r];
+      }
   }
 }
 
@@ -431,19 +663,19 @@ hipError_t launch_mlp_gemm2(bool dense, const uint16_t* src, const uint16_t* w2,
                             const float* b2, float* y, int64_t n, int d, int h, int k, int kp, hipStream_t s) {
   const int nb = (int)row_blocks(n);
   const int kid = dense ? K_MLP_GEMM2_DENSE : K_MLP_GEMM2_SPARSE;
+  const int bn = d % 256 == 0 ? 256 : 128;
+  const dim3 grid((unsigned)xcd_grid(d / bn * nb));
   timing_before(kid, s);
-  if (d % 256 == 0) {
-    const dim3 grid((unsigned)xcd_grid(d / 256 * nb));
-    if (dense)
+  if (dense) {
+    if (bn == 256)
       hipLaunchKernelGGL((mlp_gemm2<256, true>), grid, dim3(256), 0, s, src, w2, idx, b2, y, n, d, h, k, kp);
     else
-      hipLaunchKernelGGL((mlp_gemm2<256, false>), grid, dim3(256), 0, s, src, w2, idx, b2, y, n, d, h, k, kp);
-  } else {
-    const dim3 grid((unsigned)xcd_grid(d / 128 * nb));
-    if (dense)
       hipLaunchKernelGGL((mlp_gemm2<128, true>), grid, dim3(256), 0, s, src, w2, idx, b2, y, n, d, h, k, kp);
+  } else {
+    if (bn == 256)
+      hipLaunchKernelGGL((mlp_gemm2_rows<256>), grid, dim3(256), 0, s, src, w2, idx, y, n, d, h, k, kp);
     else
-      hipLaunchKernelGGL((mlp_gemm2<128, false>), grid, dim3(256), 0, s, src, w2, idx, b2, y, n, d, h, k, kp);
+      hipLaunchKernelGGL((mlp_gemm2_rows<128>), grid, dim3(256), 0, s, src, w2, idx, y, n, d, h, k, kp);
   }
   hipError_t e = hipGetLastError();
   timing_after(kid, s);

@@ -169,9 +169,9 @@ int chipmunk_identify_topk(const float* score, int64_t rows, int64_t cols, int32
  * order, for chipmunk_cache_writeback) leaving the cache unchanged.
  * x [n][d] bf16, idx [nb][k] int32, y [n][d] fp32.  0 <= k <= h; k = 0 leaves
  * every buffer bit-unchanged.  ws must hold chipmunk_workspace_bytes(
- * CHIPMUNK_OP_SPARSE_MLP, n, d, h, k) bytes: the D tiles, [nb][kp][128] bf16
- * (same block-column-major order as the cache; kp = k rounded up to 64, rows
- * past k are written as zero). */
+ * CHIPMUNK_OP_SPARSE_MLP, n, d, h, k) bytes: the D tiles, [nb][128][kp] bf16
+ * (row-major per block: token row, then the block's kept units in idx order;
+ * kp = k rounded up to 64, units past k are written as zero). */
 int chipmunk_sparse_mlp_delta(const chipmunk_mlp* layer, const uint16_t* x, const int32_t* idx,
                               int32_t k, float* y, uint16_t* a_new_packed, void* ws, size_t ws_bytes,
                               void* stream);
