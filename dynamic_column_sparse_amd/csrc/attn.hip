@@ -270,20 +270,36 @@ __global__ __launch_bounds__(256, 1) void attn_dense(const uint16_t* __restrict_
   if (lane < 32 && qok) den[hoff + r0 + qi] = sDen[qi];
 }
 
+// Sparse step / REFRESH over the gathered keys S of one (head, query block).
+// Gathered K and V rows (256 bytes each) move by direct global->LDS loads in
+// 32-key chunks through a 4-stage ring (64 KB, two workgroups per CU); their
+// key ids arrive in an 8-chunk LDS ring six chunks ahead, so no row load waits
+// on its id.  K rows store 16-byte chunk c at c ^ (row % 16) (plain 16-byte
+// operand reads, conflict-free); V rows store 32-byte column pairs at
+// pair ^ swzp(row) for the transposing reads.  The rest state (num, den) of the
+// workgroup's rows is loaded into registers before the key loop, in the
+// accumulator's layout, so the epilogue only stores.
 template <bool REFRESH>
-__global__ __launch_bounds__(256, 1) void attn_sparse(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+__global__ __launch_bounds__(256, 2) void attn_sparse(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                                       const uint16_t* __restrict__ v, const int32_t* __restrict__ idx,
                                                       const float* __restrict__ m, float* __restrict__ num,
                                                       float* __restrict__ den, float* __restrict__ o, int64_t n,
                                                       int heads, int kk, float scale) {
-  __shared__ __align__(16) uint16_t sK[2][KT][LDK];
-  __shared__ __align__(16) uint16_t sV[2][KT][LDV];
+  constexpr int SK = 32;                 // keys per chunk
+  constexpr int NSS = 4;                 // ring stages
+  constexpr int TILE = SK * 256;         // 8 KB per tensor per stage
+  constexpr int STAGE = 2 * TILE;
+  constexpr int INS = TILE / 1024 / 4;   // direct loads per wave per tensor per stage (2)
+  constexpr int L = 2 * INS;
+  __shared__ __align__(16) unsigned char smem[NSS * STAGE];
+  __shared__ __align__(16) int sIdx[8][SK];
   __shared__ float sDen[kRowBlock];
-  __shared__ int sIdx[3][KT];   // gathered key ids of the next three tiles
   const int nb = (int)row_blocks(n);
   int hh, b;
   head_block(heads, nb, hh, b);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t smem_lds = lds_addr(smem);
   const int64_t r0 = (int64_t)b * kRowBlock;
   const int rows = (int)(n - r0 < kRowBlock ? n - r0 : kRowBlock);
   const int64_t hoff = (int64_t)hh * n;
@@ -291,27 +307,54 @@ __global__ __launch_bounds__(256, 1) void attn_sparse(const uint16_t* __restrict
   const uint16_t* kh = k + hoff * 128;
   const uint16_t* vh = v + hoff * 128;
   const int32_t* S = idx + ((int64_t)hh * nb + b) * kk;
+  const int nn = (int)(n < 0x7fffffff ? n : 0x7fffffff);
   const int qi = wave * 32 + (lane & 31);
   const bool qok = qi < rows;
+
+  // Rest state in the accumulator layout: lane holds column ni*32 + lane%32 of
+  // rows wave*32 + acc_key(r, lane).
+  float nrest[4][16];
+#pragma unroll
+  for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int qr = wave * 32 + acc_key(r, lane);
+      nrest[ni][r] = qr < rows ? num[(hoff + r0 + qr) * 128 + ni * 32 + (lane & 31)] : 0.f;
+    }
   QFrag qf;
   load_q(qf, qh, r0 + qi, qok, lane);
   const float mrow = qok ? m[hoff + r0 + qi] : 0.f;
-  const int nn = (int)(n < 0x7fffffff ? n : 0x7fffffff);
 
-  uint4 rk[CH], rv[CH];
-  const uint4 z4 = make_uint4(0, 0, 0, 0);
-#define SP_LOAD(t_)                                                                           \
-  _Pragma("unroll") for (int i = 0; i < CH; ++i) {                                            \
-    const int c = tid + 256 * i, row = c >> 4, col = (c & 15) * 8;                            \
-    const int j = (t_) * KT + row;                                                            \
-    if (j < kk) {                                                                             \
-      const int64_t key = sIdx[(t_) % 3][row];                                                \
-      rk[i] = *(const uint4*)(kh + key * 128 + col);                                          \
-      rv[i] = *(const uint4*)(vh + key * 128 + col);                                          \
-    } else {                                                                                  \
-      rk[i] = z4;                                                                             \
-      rv[i] = z4;                                                                             \
-    }                                                                                         \
+  // Direct-load geometry: instruction i of a wave covers rows (wave*INS+i)*4 ..
+  // +3 of the tile; lane -> row lane/16, physical 16-byte chunk lane%16.
+  const int lr = lane >> 4, pc = lane & 15;
+  int krow[INS], koff[INS], voff[INS];
+#pragma unroll
+  for (int i = 0; i < INS; ++i) {
+    const int r = (wave * INS + i) * 4 + lr;
+    krow[i] = r;
+    koff[i] = (pc ^ (r & 15)) * 8;
+    voff[i] = ((((pc >> 1) ^ swzp(r)) << 1) | (pc & 1)) * 8;
+  }
+  auto load_ids = [&](int t, int (&ids)[INS]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < INS; ++i) ids[i] = clamp_index(sIdx[t & 7][krow[i]], nn);
+  };
+  // Chunk t's 32 key ids -> ring slot t % 8 (lanes 0..31 of wave 0; positions
+  // past kk read id 0, whose scores are masked to p = 0).
+  auto id_dma = [&](int t) __attribute__((always_inline)) {
+    if (wave == 0 && lane < SK) {
+      const int j = t * SK + lane;
+      dma4_at(S + (j < kk ? j : 0), lds_addr(&sIdx[t & 7][0]));
+    }
+  };
+#define AS_ISSUE(buf_, ids_)                                                                 \
+  {                                                                                          \
+    const uint32_t st_ = smem_lds + (buf_) * STAGE;                                          \
+    _Pragma("unroll") for (int i = 0; i < INS; ++i)                                          \
+        dma16_at(kh + (int64_t)ids_[i] * 128 + koff[i], st_ + (wave * INS + i) * 1024);      \
+    _Pragma("unroll") for (int i = 0; i < INS; ++i)                                          \
+        dma16_at(vh + (int64_t)ids_[i] * 128 + voff[i], st_ + TILE + (wave * INS + i) * 1024); \
   }
 
   f32x16_t acc[4];
@@ -320,80 +363,106 @@ __global__ __launch_bounds__(256, 1) void attn_sparse(const uint16_t* __restrict
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[ni][r] = 0.f;
   float dpart = 0.f;
-  const int ntiles = (kk + KT - 1) / KT;
-  // Index ring: slot t%3 holds the key ids of tile t, loaded two tiles ahead so
-  // no K/V row load waits on its index load.
-  auto key_of = [&](int t, int r) -> int {
-    const int j = t * KT + r;
-    return j < kk ? clamp_index(S[j], nn) : 0;
-  };
-  if (tid < KT) {
-    sIdx[0][tid] = key_of(0, tid);
-    sIdx[1][tid] = key_of(1, tid);
-    sIdx[2][tid] = key_of(2, tid);
-  }
-  __syncthreads();
-  if (ntiles > 0) {
-    SP_LOAD(0);
-    KV_STORE(0);
-  }
-  __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    int pre = 0;
-    if (t + 1 < ntiles) {
-      SP_LOAD(t + 1);
-    }
-    if (tid < KT) pre = key_of(t + 3, tid);
+  const int KT = (kk + SK - 1) / SK;
+
+  if (KT > 0) {
+    if (wave == 0 && lane < SK) {
 #pragma unroll
-    for (int kt2 = 0; kt2 < 2; ++kt2) {
-      const f32x16_t sacc = scores_t(&sK[buf][0][0], kt2 * 32, qf, lane);
+      for (int t = 0; t < 6; ++t)
+        if (t < KT) dma4_at(S + (t * SK + lane < kk ? t * SK + lane : 0), lds_addr(&sIdx[t][0]));
+    }
+    wait_vmcnt<0>();
+    __syncthreads();
+    int ids_a[INS], ids_b[INS];
+#pragma unroll
+    for (int t = 0; t < NSS - 1; ++t) {
+      if (t < KT) {
+        load_ids(t, ids_a);
+        AS_ISSUE(t, ids_a);
+      }
+    }
+    if (NSS - 1 < KT) load_ids(NSS - 1, ids_a);
+
+    const int ksw = lane & 15;   // K row (kb + lane%32) % 16 for kb a multiple of 32
+    for (int t = 0; t < KT; ++t) {
+      // Outstanding loads of this wave, newest first: stages t+1 .. t+NSS-2
+      // (L each) and, on wave 0, the id load issued by the previous iteration
+      // if there was one.  Stage t must be complete.
+      const int ahead = (KT - 1 - t) < (NSS - 2) ? (KT - 1 - t) : (NSS - 2);
+      const bool id_out = wave == 0 && t >= 1 && t + 5 < KT;
+      if (ahead == NSS - 2) {
+        if (id_out) wait_vmcnt<(NSS - 2) * L + 1>(); else wait_vmcnt<(NSS - 2) * L>();
+      } else if (ahead == 1) {
+        if (id_out) wait_vmcnt<L + 1>(); else wait_vmcnt<L>();
+      } else {
+        wait_vmcnt<0>();
+      }
+      barrier();
+      if (t + 6 < KT) id_dma(t + 6);
+      if (t + NSS - 1 < KT) AS_ISSUE((t + NSS - 1) % NSS, ids_a);
+      if (t + NSS < KT) load_ids(t + NSS, ids_b);
+      const unsigned char* st = smem + (t % NSS) * STAGE;
+      // s^T = K_chunk Q^T: lane holds query lane%32 and 16 keys (accumulator rows).
+      f32x16_t sacc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
+#pragma unroll
+      for (int s2 = 0; s2 < 8; ++s2) {
+        const bf16x8_t kf = *(const bf16x8_t*)(st + (lane & 31) * 256 + (((2 * s2 + (lane >> 5)) ^ ksw) << 4));
+        sacc = mfma32(kf, qf.f[s2], sacc);
+      }
       float p[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int j = t * KT + kt2 * 32 + acc_key(r, lane);
+        const int j = t * SK + acc_key(r, lane);
         p[r] = j < kk ? __expf(sacc[r] * scale - mrow) : 0.f;
         dpart += p[r];
       }
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
-        uint4 pk = make_uint4(pack2(p[hf * 8 + 0], p[hf * 8 + 1]), pack2(p[hf * 8 + 2], p[hf * 8 + 3]),
-                              pack2(p[hf * 8 + 4], p[hf * 8 + 5]), pack2(p[hf * 8 + 6], p[hf * 8 + 7]));
+        const uint4 pk = make_uint4(pack2(p[hf * 8 + 0], p[hf * 8 + 1]), pack2(p[hf * 8 + 2], p[hf * 8 + 3]),
+                                    pack2(p[hf * 8 + 4], p[hf * 8 + 5]), pack2(p[hf * 8 + 6], p[hf * 8 + 7]));
         const bf16x8_t pa = __builtin_bit_cast(bf16x8_t, pk);
 #pragma unroll
         for (int ni = 0; ni < 4; ++ni) {
-          const bf16x8_t vb = tr_operand(&sV[buf][0][0], LDV, kt2 * 32 + hf * 16, ni * 32, lane);
+          const bf16x8_t vb = tr_operand_swz(st + TILE, 256, hf * 16, ni * 32, lane);
           acc[ni] = mfma32(pa, vb, acc[ni]);
         }
       }
+#pragma unroll
+      for (int i = 0; i < INS; ++i) ids_a[i] = ids_b[i];
     }
-    if (t + 1 < ntiles) {
-      KV_STORE(buf ^ 1);
-    }
-    if (tid < KT) sIdx[t % 3][tid] = pre;
-    __syncthreads();
   }
-#undef SP_LOAD
+#undef AS_ISSUE
   dpart += __shfl_xor(dpart, 32);
   if (lane < 32) sDen[qi] = dpart;
   __syncthreads();
+  if (REFRESH) {
 #pragma unroll
-  for (int ni = 0; ni < 4; ++ni) {
-    const int c = ni * 32 + (lane & 31);
+    for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int qr = wave * 32 + acc_key(r, lane);
-      if (qr < rows) {
-        const int64_t row = hoff + r0 + qr;
-        const int64_t g = row * 128 + c;
-        if (REFRESH)
-          num[g] = num[g] - acc[ni][r];
-        else
-          o[g] = (num[g] + acc[ni][r]) / (den[row] + sDen[qr]);
+      for (int r = 0; r < 16; ++r) {
+        const int qr = wave * 32 + acc_key(r, lane);
+        if (qr < rows) num[(hoff + r0 + qr) * 128 + ni * 32 + (lane & 31)] = nrest[ni][r] - acc[ni][r];
       }
-    }
+    if (lane < 32 && qok) den[hoff + r0 + qi] = den[hoff + r0 + qi] - sDen[qi];
+  } else {
+    float dtot[4][4];   // den_rest + den_S of the lane's 16 rows (4 groups of 4)
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int qr = wave * 32 + acc_key(g * 4 + e, lane);
+        dtot[g][e] = qr < rows ? den[hoff + r0 + qr] + sDen[qr] : 1.f;
+      }
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int qr = wave * 32 + acc_key(r, lane);
+        if (qr < rows) o[(hoff + r0 + qr) * 128 + ni * 32 + (lane & 31)] = (nrest[ni][r] + acc[ni][r]) / dtot[r >> 2][r & 3];
+      }
   }
-  if (REFRESH && lane < 32 && qok) den[hoff + r0 + qi] = den[hoff + r0 + qi] - sDen[qi];
 }
 
 #undef KV_STORE
