@@ -273,12 +273,16 @@ __global__ __launch_bounds__(256, 1) void attn_dense(const uint16_t* __restrict_
 // Sparse step / REFRESH over the gathered keys S of one (head, query block).
 // Gathered K and V rows (256 bytes each) move by direct global->LDS loads in
 // 32-key chunks through a 4-stage ring (64 KB, two workgroups per CU); their
-// key ids arrive in an 8-chunk LDS ring six chunks ahead, so no row load waits
-// on its id.  K rows store 16-byte chunk c at c ^ (row % 16) (plain 16-byte
-// operand reads, conflict-free); V rows store 32-byte column pairs at
-// pair ^ swzp(row) for the transposing reads.  The rest state (num, den) of the
-// workgroup's rows is loaded into registers before the key loop, in the
-// accumulator's layout, so the epilogue only stores.
+// key ids arrive in an 8-chunk LDS ring far enough ahead that no row load
+// waits on its id.  K rows store 16-byte chunk c at c ^ (row % 16) (plain
+// 16-byte operand reads, no bank conflicts); V rows store 32-byte column pairs
+// at pair ^ swzp(row) for the transposing reads.  Only the id loads are waited
+// for before the first stages go out; Q, the row max and the rest denominator
+// follow the first stages, and the rest numerator (in the coalesced 16-byte
+// layout of the epilogue) follows the last stage, so none of them costs a
+// round trip of its own.  Every load between direct-load stages is issued
+// unconditionally, once per wave, so the per-wave load counts that the waits
+// rely on are exact.
 template <bool REFRESH>
 __global__ __launch_bounds__(256, 2) void attn_sparse(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                                       const uint16_t* __restrict__ v, const int32_t* __restrict__ idx,
@@ -291,9 +295,16 @@ __global__ __launch_bounds__(256, 2) void attn_sparse(const uint16_t* __restrict
   constexpr int STAGE = 2 * TILE;
   constexpr int INS = TILE / 1024 / 4;   // direct loads per wave per tensor per stage (2)
   constexpr int L = 2 * INS;
+  constexpr int DID = 2 * NSS - 1;       // id lookahead: chunk t+NSS's ids are older than stage t
+  constexpr int RID = 8;                 // id ring slots
+  constexpr int QL = 10;                 // Q (8), row max and rest denominator loads per wave
+  constexpr int PIECES = kRowBlock * 128 / 4 / 256;   // 16-byte rest/output pieces per thread (16)
+  constexpr int PRE = PIECES / 2;        // of which loaded early (register budget)
+  static_assert(RID >= DID - NSS + 1 && (RID & (RID - 1)) == 0, "id ring");
   __shared__ __align__(16) unsigned char smem[NSS * STAGE];
-  __shared__ __align__(16) int sIdx[8][SK];
+  __shared__ __align__(16) int sIdx[RID][SK];
   __shared__ float sDen[kRowBlock];
+  __shared__ float sDenRest[kRowBlock];
   const int nb = (int)row_blocks(n);
   int hh, b;
   head_block(heads, nb, hh, b);
@@ -310,42 +321,29 @@ __global__ __launch_bounds__(256, 2) void attn_sparse(const uint16_t* __restrict
   const int nn = (int)(n < 0x7fffffff ? n : 0x7fffffff);
   const int qi = wave * 32 + (lane & 31);
   const bool qok = qi < rows;
-
-  // Rest state in the accumulator layout: lane holds column ni*32 + lane%32 of
-  // rows wave*32 + acc_key(r, lane).
-  float nrest[4][16];
-#pragma unroll
-  for (int ni = 0; ni < 4; ++ni)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int qr = wave * 32 + acc_key(r, lane);
-      nrest[ni][r] = qr < rows ? num[(hoff + r0 + qr) * 128 + ni * 32 + (lane & 31)] : 0.f;
-    }
-  QFrag qf;
-  load_q(qf, qh, r0 + qi, qok, lane);
-  const float mrow = qok ? m[hoff + r0 + qi] : 0.f;
+  const int qc = qok ? qi : rows - 1;    // clamped row: loads stay unconditional
 
   // Direct-load geometry: instruction i of a wave covers rows (wave*INS+i)*4 ..
   // +3 of the tile; lane -> row lane/16, physical 16-byte chunk lane%16.
-  const int lr = lane >> 4, pc = lane & 15;
+  const int pc = lane & 15;
   int krow[INS], koff[INS], voff[INS];
 #pragma unroll
   for (int i = 0; i < INS; ++i) {
-    const int r = (wave * INS + i) * 4 + lr;
+    const int r = (wave * INS + i) * 4 + (lane >> 4);
     krow[i] = r;
     koff[i] = (pc ^ (r & 15)) * 8;
     voff[i] = ((((pc >> 1) ^ swzp(r)) << 1) | (pc & 1)) * 8;
   }
   auto load_ids = [&](int t, int (&ids)[INS]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < INS; ++i) ids[i] = clamp_index(sIdx[t & 7][krow[i]], nn);
+    for (int i = 0; i < INS; ++i) ids[i] = clamp_index(sIdx[t & (RID - 1)][krow[i]], nn);
   };
-  // Chunk t's 32 key ids -> ring slot t % 8 (lanes 0..31 of wave 0; positions
+  // Chunk t's 32 key ids -> ring slot t % RID (lanes 0..31 of wave 0; positions
   // past kk read id 0, whose scores are masked to p = 0).
   auto id_dma = [&](int t) __attribute__((always_inline)) {
     if (wave == 0 && lane < SK) {
       const int j = t * SK + lane;
-      dma4_at(S + (j < kk ? j : 0), lds_addr(&sIdx[t & 7][0]));
+      dma4_at(S + (j < kk ? j : 0), lds_addr(&sIdx[t & (RID - 1)][0]));
     }
   };
 #define AS_ISSUE(buf_, ids_)                                                                 \
@@ -356,6 +354,24 @@ __global__ __launch_bounds__(256, 2) void attn_sparse(const uint16_t* __restrict
     _Pragma("unroll") for (int i = 0; i < INS; ++i)                                          \
         dma16_at(vh + (int64_t)ids_[i] * 128 + voff[i], st_ + TILE + (wave * INS + i) * 1024); \
   }
+  float4 rest[PIECES];
+  auto load_rest = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int it = 0; it < PRE; ++it) {
+      const int e = it * 256 + tid, qr = e >> 5, c4 = e & 31;
+      const int qrc = qr < rows ? qr : rows - 1;
+      rest[it] = *(const float4*)(num + (hoff + r0 + qrc) * 128 + c4 * 4);
+    }
+  };
+  QFrag qf;
+  float mrow = 0.f, dr_pre = 1.f;
+  auto load_qmd = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int s2 = 0; s2 < 8; ++s2) qf.f[s2] = *(const bf16x8_t*)(qh + (r0 + qc) * 128 + s2 * 16 + (lane >> 5) * 8);
+    mrow = m[hoff + r0 + qc];
+    const int dq = (tid & (kRowBlock - 1)) < rows ? (tid & (kRowBlock - 1)) : rows - 1;
+    dr_pre = den[hoff + r0 + dq];
+  };
 
   f32x16_t acc[4];
 #pragma unroll
@@ -368,7 +384,7 @@ __global__ __launch_bounds__(256, 2) void attn_sparse(const uint16_t* __restrict
   if (KT > 0) {
     if (wave == 0 && lane < SK) {
 #pragma unroll
-      for (int t = 0; t < 6; ++t)
+      for (int t = 0; t < DID; ++t)
         if (t < KT) dma4_at(S + (t * SK + lane < kk ? t * SK + lane : 0), lds_addr(&sIdx[t][0]));
     }
     wait_vmcnt<0>();
@@ -382,40 +398,55 @@ __global__ __launch_bounds__(256, 2) void attn_sparse(const uint16_t* __restrict
       }
     }
     if (NSS - 1 < KT) load_ids(NSS - 1, ids_a);
+    load_qmd();
+    // The rest numerator follows the last stage: in the prologue when every
+    // stage is issued there, else at iteration t_r = KT - NSS.
+    const int t_r = KT - NSS;
+    if (t_r < 0) load_rest();
 
-    const int ksw = lane & 15;   // K row (kb + lane%32) % 16 for kb a multiple of 32
+    const int ksw = lane & 15;   // K row (lane % 32) % 16
     for (int t = 0; t < KT; ++t) {
-      // Outstanding loads of this wave, newest first: stages t+1 .. t+NSS-2
-      // (L each) and, on wave 0, the id load issued by the previous iteration
-      // if there was one.  Stage t must be complete.
+      // Loads of this wave newer than stage t: the stages after t already
+      // issued (L each); the Q/max/denominator loads if stage t came from the
+      // prologue; the rest numerator if it is already issued; and on wave 0
+      // the id loads of iterations t-NSS+2 .. t-1.  Waiting down to that count
+      // completes stage t and every older id load, including chunk t+NSS's
+      // (issued at iteration t+NSS-DID).
       const int ahead = (KT - 1 - t) < (NSS - 2) ? (KT - 1 - t) : (NSS - 2);
-      const bool id_out = wave == 0 && t >= 1 && t + 5 < KT;
-      if (ahead == NSS - 2) {
-        if (id_out) wait_vmcnt<(NSS - 2) * L + 1>(); else wait_vmcnt<(NSS - 2) * L>();
-      } else if (ahead == 1) {
-        if (id_out) wait_vmcnt<L + 1>(); else wait_vmcnt<L>();
-      } else {
-        wait_vmcnt<0>();
+      int newer = ahead * L + (t <= NSS - 2 ? QL : 0) + (t > t_r ? PRE : 0);
+      if (wave == 0) {
+        const int j0 = t - NSS + 2 > 0 ? t - NSS + 2 : 0;
+        const int j1 = (t - 1) < (KT - DID - 1) ? (t - 1) : (KT - DID - 1);
+        newer += j1 >= j0 ? j1 - j0 + 1 : 0;
       }
+      wait_vmcnt_upto<(NSS - 2) * L + QL + PRE + NSS - 2>(newer);
       barrier();
-      if (t + 6 < KT) id_dma(t + 6);
+      if (t + DID < KT) id_dma(t + DID);
       if (t + NSS - 1 < KT) AS_ISSUE((t + NSS - 1) % NSS, ids_a);
+      if (t == t_r) load_rest();
       if (t + NSS < KT) load_ids(t + NSS, ids_b);
       const unsigned char* st = smem + (t % NSS) * STAGE;
-      // s^T = K_chunk Q^T: lane holds query lane%32 and 16 keys (accumulator rows).
-      f32x16_t sacc;
+      // s^T = K_chunk Q^T in two interleaved chains: lane holds query lane%32
+      // and 16 keys (accumulator rows).
+      f32x16_t sacc, sacc2;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
+      for (int r = 0; r < 16; ++r) {
+        sacc[r] = 0.f;
+        sacc2[r] = 0.f;
+      }
 #pragma unroll
-      for (int s2 = 0; s2 < 8; ++s2) {
-        const bf16x8_t kf = *(const bf16x8_t*)(st + (lane & 31) * 256 + (((2 * s2 + (lane >> 5)) ^ ksw) << 4));
-        sacc = mfma32(kf, qf.f[s2], sacc);
+      for (int s2 = 0; s2 < 8; s2 += 2) {
+        const bf16x8_t kf0 = *(const bf16x8_t*)(st + (lane & 31) * 256 + (((2 * s2 + (lane >> 5)) ^ ksw) << 4));
+        const bf16x8_t kf1 = *(const bf16x8_t*)(st + (lane & 31) * 256 + (((2 * s2 + 2 + (lane >> 5)) ^ ksw) << 4));
+        sacc = mfma32(kf0, qf.f[s2], sacc);
+        sacc2 = mfma32(kf1, qf.f[s2 + 1], sacc2);
       }
       float p[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int j = t * SK + acc_key(r, lane);
-        p[r] = j < kk ? __expf(sacc[r] * scale - mrow) : 0.f;
+        const float e = __expf((sacc[r] + sacc2[r]) * scale - mrow);
+        p[r] = (j < kk && qok) ? e : 0.f;
         dpart += p[r];
       }
 #pragma unroll
@@ -432,37 +463,50 @@ __global__ __launch_bounds__(256, 2) void attn_sparse(const uint16_t* __restrict
 #pragma unroll
       for (int i = 0; i < INS; ++i) ids_a[i] = ids_b[i];
     }
+  } else {
+    load_qmd();
+    load_rest();
   }
 #undef AS_ISSUE
   dpart += __shfl_xor(dpart, 32);
-  if (lane < 32) sDen[qi] = dpart;
+  // Epilogue through the idle ring: the numerator part goes to LDS as fp32
+  // [128 rows][128 columns] (16-byte chunk c of row r at c ^ ((r / 4) % 2) * 8,
+  // so the two row groups of one store hit different banks), then every
+  // thread combines and stores whole 16-byte pieces.
   __syncthreads();
-  if (REFRESH) {
+  float* sacc_t = (float*)smem;
+  if (lane < 32) sDen[qi] = dpart;
+  if (tid < kRowBlock) sDenRest[tid] = dr_pre;
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni)
+  for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int qr = wave * 32 + acc_key(r, lane);
-        if (qr < rows) num[(hoff + r0 + qr) * 128 + ni * 32 + (lane & 31)] = nrest[ni][r] - acc[ni][r];
-      }
-    if (lane < 32 && qok) den[hoff + r0 + qi] = den[hoff + r0 + qi] - sDen[qi];
-  } else {
-    float dtot[4][4];   // den_rest + den_S of the lane's 16 rows (4 groups of 4)
+    for (int r = 0; r < 16; ++r) {
+      const int qr = wave * 32 + acc_key(r, lane);
+      const int cc = ni * 32 + (lane & 31);
+      sacc_t[qr * 128 + (((cc >> 2) ^ (((qr >> 2) & 1) << 3)) << 2) + (cc & 3)] = acc[ni][r];
+    }
 #pragma unroll
-    for (int g = 0; g < 4; ++g)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int qr = wave * 32 + acc_key(g * 4 + e, lane);
-        dtot[g][e] = qr < rows ? den[hoff + r0 + qr] + sDen[qr] : 1.f;
-      }
-#pragma unroll
-    for (int ni = 0; ni < 4; ++ni)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int qr = wave * 32 + acc_key(r, lane);
-        if (qr < rows) o[(hoff + r0 + qr) * 128 + ni * 32 + (lane & 31)] = (nrest[ni][r] + acc[ni][r]) / dtot[r >> 2][r & 3];
-      }
+  for (int it = PRE; it < PIECES; ++it) {
+    const int e = it * 256 + tid, qr = e >> 5, c4 = e & 31;
+    const int qrc = qr < rows ? qr : rows - 1;
+    rest[it] = *(const float4*)(num + (hoff + r0 + qrc) * 128 + c4 * 4);
   }
+  __syncthreads();
+#pragma unroll
+  for (int it = 0; it < PIECES; ++it) {
+    const int e = it * 256 + tid, qr = e >> 5, c4 = e & 31;
+    if (qr >= rows) continue;
+    const float4 a = *(const float4*)(sacc_t + qr * 128 + ((c4 ^ (((qr >> 2) & 1) << 3)) << 2));
+    const int64_t g = (hoff + r0 + qr) * 128 + c4 * 4;
+    if (REFRESH) {
+      *(float4*)(num + g) = make_float4(rest[it].x - a.x, rest[it].y - a.y, rest[it].z - a.z, rest[it].w - a.w);
+    } else {
+      const float dt = sDenRest[qr] + sDen[qr];
+      *(float4*)(o + g) = make_float4((rest[it].x + a.x) / dt, (rest[it].y + a.y) / dt, (rest[it].z + a.z) / dt,
+                                      (rest[it].w + a.w) / dt);
+    }
+  }
+  if (REFRESH && tid < rows) den[hoff + r0 + tid] = sDenRest[tid] - sDen[tid];
 }
 
 #undef KV_STORE

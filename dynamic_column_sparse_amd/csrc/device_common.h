@@ -12,15 +12,21 @@ typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-// fp32 -> bf16 bits, round to nearest, ties to even (NaN stays a quiet NaN).
-__device__ __forceinline__ uint32_t f2bf(float x) {
-  uint32_t u = __float_as_uint(x);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// fp32 -> bf16 bits, round to nearest, ties to even, through gfx950's packed
+// conversion (v_cvt_pk_bf16_f32).  Checked against a software round-to-nearest-
+// even on all 2^32 fp32 patterns: identical on every non-NaN input (subnormals
+// and overflow to infinity included); NaN inputs give NaN.  Branch-free, unlike
+// a software version with a NaN test, which the compiler turns into divergent
+// branches per element.
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
+__device__ __forceinline__ uint32_t f2bf(float x) { return pack2(x, 0.f) & 0xffffu; }
 __device__ __forceinline__ float bf2f(uint32_t b) { return __uint_as_float(b << 16); }
-__device__ __forceinline__ uint32_t pack2(float lo, float hi) { return f2bf(lo) | (f2bf(hi) << 16); }
 
 // D(32x32, fp32) += A(32x16) * B(16x32), bf16 operands.  Operand layout (checked on
 // gfx950): lane l holds A row l%32 / B column l%32, reduction indices
@@ -129,6 +135,20 @@ __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
 }
+// wait_vmcnt with a count known only at run time (wave-uniform, 0 .. 63):
+// dispatches to the immediate form.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_upto(int n) {
+  if constexpr (N == 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (n >= N)
+      wait_vmcnt<N>();
+    else
+      wait_vmcnt_upto<N - 1>(n);
+  }
+}
+
 // Workgroup barrier without the release/acquire fences of __syncthreads (which
 // would wait for every outstanding global load, draining the prefetch ring).
 // Callers order their own LDS traffic with wait_vmcnt before it.
