@@ -119,11 +119,180 @@ __global__ __launch_bounds__(kThreads) void topk_rows(const float* __restrict__ 
   }
 }
 
+// Register-resident variant for rows of up to kRegCols scores: 1024 threads,
+// thread t holds keys t + 1024 j (j < kRegKeys).
+//   1. Min and max of the row's keys: every key shares their common bit
+//      prefix, so the radix passes start at the first bit where they differ
+//      (positive scores of similar size share sign and exponent bits; starting
+//      at the top would send every key of the first passes to one bin).
+//   2. Radix select over the remaining bits, up to 8 per pass, with one
+//      256-bin histogram per wave (contention only inside a wave).
+//   3. Emit in index order: tie ranks, then output positions, each from one
+//      ballot per (batch j, wave) and a 16 x 16 prefix table.
+constexpr int kRegThreads = 1024;
+constexpr int kRegWaves = kRegThreads / 64;
+constexpr int kRegKeys = 16;
+constexpr int kRegCols = kRegThreads * kRegKeys;
+
+// Exclusive prefix sum over tab[0..255] in (batch, wave) order, in place;
+// returns the total.  Threads 0..255 take part; ends with a barrier.
+__device__ __forceinline__ uint32_t table_scan(uint32_t* tab, uint32_t* wsum, int tid) {
+  const int lane = tid & 63, wave = tid >> 6;
+  uint32_t v = 0, incl = 0;
+  if (tid < 256) {
+    v = tab[tid];
+    incl = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t t = __shfl_up(incl, o);
+      if (lane >= o) incl += t;
+    }
+    if (lane == 63) wsum[wave] = incl;
+  }
+  __syncthreads();
+  uint32_t total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+  if (tid < 256) {
+    for (int w = 0; w < wave; ++w) incl += wsum[w];
+    tab[tid] = incl - v;
+  }
+  __syncthreads();
+  return total;
+}
+
+__global__ __launch_bounds__(kRegThreads) void topk_rows_reg(const float* __restrict__ score, int cols, int k,
+                                                             int32_t* __restrict__ idx) {
+  __shared__ uint32_t hist[kRegWaves][256];
+  __shared__ uint32_t tab[kRegKeys * kRegWaves];
+  __shared__ uint32_t wsum[4];
+  __shared__ uint32_t red[2][kRegWaves];
+  __shared__ uint32_t sh_prefix, sh_remaining;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t row = blockIdx.x;
+  const float* srow = score + row * (int64_t)cols;
+  int32_t* orow = idx + row * (int64_t)k;
+
+  uint32_t key[kRegKeys];
+  uint32_t kmin = 0xffffffffu, kmax = 0u;
+#pragma unroll
+  for (int j = 0; j < kRegKeys; ++j) {
+    const int i = tid + kRegThreads * j;
+    key[j] = i < cols ? score_key(srow[i]) : 0u;
+    if (i < cols) {
+      kmin = min(kmin, key[j]);
+      kmax = max(kmax, key[j]);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o));
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o));
+  }
+  if (lane == 0) {
+    red[0][wave] = kmin;
+    red[1][wave] = kmax;
+  }
+  __syncthreads();
+  kmin = red[0][0];
+  kmax = red[1][0];
+#pragma unroll
+  for (int w = 1; w < kRegWaves; ++w) {
+    kmin = min(kmin, red[0][w]);
+    kmax = max(kmax, red[1][w]);
+  }
+  // Bits above `hi` are common to every key.
+  int hi = (kmin == kmax) ? -1 : 31 - __clz((int)(kmin ^ kmax));
+  uint32_t prefix = hi >= 31 ? 0u : (kmin & ~((2u << hi) - 1u));
+  if (hi < 0) prefix = kmin;
+  uint32_t remaining = (uint32_t)k;
+  while (hi >= 0) {
+    const int lo = hi >= 7 ? hi - 7 : 0;
+    const uint32_t above = hi >= 31 ? 0u : ~((2u << hi) - 1u);   // bits already fixed
+    for (int i = tid; i < kRegWaves * 256; i += kRegThreads) (&hist[0][0])[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kRegKeys; ++j) {
+      const int i = tid + kRegThreads * j;
+      if (i < cols && (key[j] & above) == prefix) atomicAdd(&hist[wave][(key[j] >> lo) & ((2u << (hi - lo)) - 1u)], 1u);
+    }
+    __syncthreads();
+    // Bin counts summed over the waves, scanned from the top bin down.
+    const int nbins = 2 << (hi - lo);
+    uint32_t hv = 0, incl = 0;
+    if (tid < 256) {
+      const int bin = nbins - 1 - tid;
+      if (bin >= 0) {
+#pragma unroll
+        for (int w = 0; w < kRegWaves; ++w) hv += hist[w][bin];
+      }
+      incl = hv;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t t = __shfl_up(incl, o);
+        if (lane >= o) incl += t;
+      }
+      if (lane == 63) wsum[wave] = incl;
+    }
+    __syncthreads();
+    if (tid < 256) {
+      for (int w = 0; w < wave; ++w) incl += wsum[w];
+      const uint32_t excl = incl - hv;
+      if (tid < nbins && excl < remaining && remaining <= incl) {
+        sh_prefix = prefix | ((uint32_t)(nbins - 1 - tid) << lo);
+        sh_remaining = remaining - excl;
+      }
+    }
+    __syncthreads();
+    prefix = sh_prefix;
+    remaining = sh_remaining;
+    hi = lo - 1;
+  }
+
+  const uint32_t T = prefix, need = remaining;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : ((~0ull) >> (64 - lane));
+  // Tie ranks: ties taken in index order, the first `need` of them.
+  uint64_t em[kRegKeys];
+#pragma unroll
+  for (int j = 0; j < kRegKeys; ++j) {
+    em[j] = __ballot(tid + kRegThreads * j < cols && key[j] == T);
+    if (lane == 0) tab[j * kRegWaves + wave] = (uint32_t)__popcll(em[j]);
+  }
+  __syncthreads();
+  table_scan(tab, wsum, tid);
+  uint32_t take_bits = 0;
+#pragma unroll
+  for (int j = 0; j < kRegKeys; ++j) {
+    const int i = tid + kRegThreads * j;
+    const bool valid = i < cols;
+    const bool eq = valid && key[j] == T;
+    const uint32_t eq_rank = tab[j * kRegWaves + wave] + (uint32_t)__popcll(em[j] & lt_mask);
+    if ((valid && key[j] > T) || (eq && eq_rank < need)) take_bits |= 1u << j;
+  }
+  __syncthreads();
+  // Output positions: taken indices in ascending order.
+#pragma unroll
+  for (int j = 0; j < kRegKeys; ++j) {
+    em[j] = __ballot((take_bits >> j) & 1u);
+    if (lane == 0) tab[j * kRegWaves + wave] = (uint32_t)__popcll(em[j]);
+  }
+  __syncthreads();
+  table_scan(tab, wsum, tid);
+#pragma unroll
+  for (int j = 0; j < kRegKeys; ++j) {
+    if ((take_bits >> j) & 1u) {
+      const uint32_t pos = tab[j * kRegWaves + wave] + (uint32_t)__popcll(em[j] & lt_mask);
+      if (pos < (uint32_t)k) orow[pos] = tid + kRegThreads * j;
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_topk(const float* score, int64_t rows, int64_t cols, int k, int32_t* idx, hipStream_t s) {
   timing_before(K_TOPK, s);
-  if (cols <= kLdsCap)
+  if (cols <= kRegCols)
+    hipLaunchKernelGGL(topk_rows_reg, dim3((unsigned)rows), dim3(kRegThreads), 0, s, score, (int)cols, k, idx);
+  else if (cols <= kLdsCap)
     hipLaunchKernelGGL((topk_rows<true>), dim3((unsigned)rows), dim3(kThreads), (size_t)cols * 4, s, score, cols, k,
                        idx);
   else
