@@ -240,6 +240,20 @@ __device__ __forceinline__ int xcd_unit(int linear_id, int units) {
 }
 __host__ __device__ inline int xcd_grid(int units) { return ((units + 7) >> 3) << 3; }
 
+// Unit -> (row block b, column tile t) with the column tiles in groups of `gt`:
+// inside a group, the gt tiles of one row block are consecutive units, then
+// those of the next block.  A contiguous range of units (one XCD's share) then
+// covers a few tiles of many blocks, so both the blocks' activation rows and the
+// tiles' weight rows are reused from that XCD's L2.
+__device__ __forceinline__ void grouped_tile(int u, int nb, int ntiles, int gt, int& b, int& t) {
+  const int per = nb * gt;
+  const int tg = u / per;
+  const int r = u - tg * per;
+  const int g = (ntiles - tg * gt) < gt ? (ntiles - tg * gt) : gt;
+  b = r / g;
+  t = tg * gt + r % g;
+}
+
 // Sum 16 per-lane values over the 32 lanes of each half-wave with one exchange
 // per halving: after the exchanges lane l holds the total of value
 // ((l >> 1) & 15) over its half-wave (lanes l and l^1 agree).

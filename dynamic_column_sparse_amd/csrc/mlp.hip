@@ -34,6 +34,10 @@ namespace {
 constexpr int BM = 128;   // rows per block (one row block)
 constexpr int BK = 64;    // reduction chunk
 constexpr int NS = 3;     // LDS ring stages: one consumed, two in flight
+#ifndef MLP_GROUP_TILES
+#define MLP_GROUP_TILES 2
+#endif
+constexpr int kGroupTiles = MLP_GROUP_TILES;   // column tiles of one row block run back to back
 
 template <int BN, bool DENSE>
 __global__ __launch_bounds__(256, 2) void mlp_gemm1(const uint16_t* __restrict__ x,
@@ -67,8 +71,9 @@ __global__ __launch_bounds__(256, 2) void mlp_gemm1(const uint16_t* __restrict__
   const int nb = (int)row_blocks(n), ntiles = (kcols + BN - 1) / BN;
   const int u = xcd_unit(blockIdx.x, ntiles * nb);
   if (u >= ntiles * nb) return;
-  const int b = u % nb;
-  const int c0 = (u / nb) * BN;
+  int b, tile;
+  grouped_tile(u, nb, ntiles, kGroupTiles, b, tile);
+  const int c0 = tile * BN;
   const int64_t r0 = (int64_t)b * BM;
   const int rows = (int)(n - r0 < BM ? n - r0 : BM);
 
@@ -486,8 +491,9 @@ __global__ __launch_bounds__(256, 2) void mlp_gemm2_rows(const uint16_t* __restr
   const int nb = (int)row_blocks(n), ntn = d / BN;
   const int u = xcd_unit(blockIdx.x, ntn * nb);
   if (u >= ntn * nb) return;
-  const int b = u % nb;
-  const int n0 = (u / nb) * BN;
+  int b, tile;
+  grouped_tile(u, nb, ntn, kGroupTiles, b, tile);
+  const int n0 = tile * BN;
   const int64_t r0 = (int64_t)b * BM;
   const int rows = (int)(n - r0 < BM ? n - r0 : BM);
   const uint16_t* dblk = dsrc + (int64_t)b * BM * kp;
