@@ -276,13 +276,12 @@ __global__ __launch_bounds__(256, 1) void attn_dense(const uint16_t* __restrict_
 // key ids arrive in an 8-chunk LDS ring far enough ahead that no row load
 // waits on its id.  K rows store 16-byte chunk c at c ^ (row % 16) (plain
 // 16-byte operand reads, no bank conflicts); V rows store 32-byte column pairs
-// at pair ^ swzp(row) for the transposing reads.  Only the id loads are waited
-// for before the first stages go out; Q, the row max and the rest denominator
-// follow the first stages, and the rest numerator (in the coalesced 16-byte
-// layout of the epilogue) follows the last stage, so none of them costs a
-// round trip of its own.  Every load between direct-load stages is issued
-// unconditionally, once per wave, so the per-wave load counts that the waits
-// rely on are exact.
+// at pair ^ swzp(row) for the transposing reads.  The score products of chunk
+// t+1 are issued before the exponentials and value products of chunk t, so the
+// matrix cores always have independent work.  The rest numerator (in the
+// coalesced 16-byte layout of the epilogue) is loaded behind the last stage.
+// Every load issued between direct-load stages is unconditional, once per
+// wave, so the per-wave load counts that the waits rely on are exact.
 template <bool REFRESH>
 __global__ __launch_bounds__(256, 2) void attn_sparse(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                                       const uint16_t* __restrict__ v, const int32_t* __restrict__ idx,
@@ -297,7 +296,6 @@ __global__ __launch_bounds__(256, 2) void attn_sparse(const uint16_t* __restrict
   constexpr int L = 2 * INS;
   constexpr int DID = 2 * NSS - 1;       // id lookahead: chunk t+NSS's ids are older than stage t
   constexpr int RID = 8;                 // id ring slots
-  constexpr int QL = 10;                 // Q (8), row max and rest denominator loads per wave
   constexpr int PIECES = kRowBlock * 128 / 4 / 256;   // 16-byte rest/output pieces per thread (16)
   constexpr int PRE = PIECES / 2;        // of which loaded early (register budget)
   static_assert(RID >= DID - NSS + 1 && (RID & (RID - 1)) == 0, "id ring");
@@ -389,6 +387,12 @@ __global__ __launch_bounds__(256, 2) void attn_sparse(const uint16_t* __restrict
     }
     wait_vmcnt<0>();
     __syncthreads();
+    // Q, the row max and the rest denominator go out before the first stages.
+    // Their first use (the scores of chunk 0) then waits for them once, before
+    // the key loop; issued after the stages, they would make the compiler's own
+    // waits inside the loop (which do not count the direct loads) drain the
+    // whole prefetch ring on every iteration.
+    load_qmd();
     int ids_a[INS], ids_b[INS];
 #pragma unroll
     for (int t = 0; t < NSS - 1; ++t) {
@@ -398,56 +402,85 @@ __global__ __launch_bounds__(256, 2) void attn_sparse(const uint16_t* __restrict
       }
     }
     if (NSS - 1 < KT) load_ids(NSS - 1, ids_a);
-    load_qmd();
     // The rest numerator follows the last stage: in the prologue when every
     // stage is issued there, else at iteration t_r = KT - NSS.
     const int t_r = KT - NSS;
     if (t_r < 0) load_rest();
 
     const int ksw = lane & 15;   // K row (lane % 32) % 16
-    for (int t = 0; t < KT; ++t) {
-      // Loads of this wave newer than stage t: the stages after t already
-      // issued (L each); the Q/max/denominator loads if stage t came from the
-      // prologue; the rest numerator if it is already issued; and on wave 0
-      // the id loads of iterations t-NSS+2 .. t-1.  Waiting down to that count
-      // completes stage t and every older id load, including chunk t+NSS's
-      // (issued at iteration t+NSS-DID).
-      const int ahead = (KT - 1 - t) < (NSS - 2) ? (KT - 1 - t) : (NSS - 2);
-      int newer = ahead * L + (t <= NSS - 2 ? QL : 0) + (t > t_r ? PRE : 0);
-      if (wave == 0) {
-        const int j0 = t - NSS + 2 > 0 ? t - NSS + 2 : 0;
-        const int j1 = (t - 1) < (KT - DID - 1) ? (t - 1) : (KT - DID - 1);
-        newer += j1 >= j0 ? j1 - j0 + 1 : 0;
+    // s^T = K_chunk Q^T for the chunk in stage slot `slot`: lane holds query
+    // lane%32 and 16 keys (accumulator rows).
+    auto scores = [&](int slot) __attribute__((always_inline)) {
+      const unsigned char* st = smem + slot * STAGE;
+      f32x16_t sc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sc[r] = 0.f;
+#pragma unroll
+      for (int s2 = 0; s2 < 8; ++s2) {
+        const bf16x8_t kf = *(const bf16x8_t*)(st + (lane & 31) * 256 + (((2 * s2 + (lane >> 5)) ^ ksw) << 4));
+        sc = mfma32(kf, qf.f[s2], sc);
       }
-      wait_vmcnt_upto<(NSS - 2) * L + QL + PRE + NSS - 2>(newer);
+      return sc;
+    };
+    // Stage 0 (issued in the prologue) must be complete; newer than it: the
+    // other prologue stages and the rest numerator if it went out in the
+    // prologue.
+    {
+      const int ahead = (KT - 1) < (NSS - 2) ? (KT - 1) : (NSS - 2);
+      wait_vmcnt_upto<(NSS - 2) * L + PRE>(ahead * L + (t_r < 0 ? PRE : 0));
       barrier();
-      if (t + DID < KT) id_dma(t + DID);
-      if (t + NSS - 1 < KT) AS_ISSUE((t + NSS - 1) % NSS, ids_a);
-      if (t == t_r) load_rest();
-      if (t + NSS < KT) load_ids(t + NSS, ids_b);
+    }
+    const float sl2 = scale * 1.4426950408889634f, ml2 = mrow * 1.4426950408889634f;
+    f32x16_t sacc = scores(0);
+    // Software pipeline: iteration t issues the score products of chunk t+1,
+    // then the exponentials and the P V products of chunk t, so the matrix
+    // cores have independent work while the exponentials run.
+    for (int t = 0; t < KT; ++t) {
+      if (t + 1 < KT) {
+        // Stage t+1 must be complete.  Newer than it: the stages after it
+        // already issued (L each), the rest numerator if already issued, and on
+        // wave 0 the
+        // id loads of iterations t-NSS+3 .. t-1 (stage t+1 went out at
+        // iteration t-NSS+2).  Chunk t+NSS's ids (issued at iteration
+        // t+NSS-DID) are older, so they are complete too.
+        const int issued_to = (t + NSS - 2) < (KT - 1) ? (t + NSS - 2) : (KT - 1);
+        const int ahead = issued_to - (t + 1);
+        int newer = ahead * L + (t > t_r ? PRE : 0);
+        if (wave == 0) {
+          const int j0 = t - NSS + 3 > 0 ? t - NSS + 3 : 0;
+          const int j1 = (t - 1) < (KT - DID - 1) ? (t - 1) : (KT - DID - 1);
+          newer += j1 >= j0 ? j1 - j0 + 1 : 0;
+        }
+        wait_vmcnt_upto<(NSS - 2) * L + PRE + NSS>(newer);
+        barrier();
+        // Slot of stage t+NSS-1 is stage t-1's: its keys were read at
+        // iteration t-2 and its values at t-1, before this barrier.
+        if (t + DID < KT) id_dma(t + DID);
+        if (t + NSS - 1 < KT) AS_ISSUE((t + NSS - 1) % NSS, ids_a);
+        if (t == t_r) load_rest();
+        if (t + NSS < KT) load_ids(t + NSS, ids_b);
+      }
+      f32x16_t snext;
+      if (t + 1 < KT) snext = scores((t + 1) % NSS);
       const unsigned char* st = smem + (t % NSS) * STAGE;
-      // s^T = K_chunk Q^T in two interleaved chains: lane holds query lane%32
-      // and 16 keys (accumulator rows).
-      f32x16_t sacc, sacc2;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        sacc[r] = 0.f;
-        sacc2[r] = 0.f;
-      }
-#pragma unroll
-      for (int s2 = 0; s2 < 8; s2 += 2) {
-        const bf16x8_t kf0 = *(const bf16x8_t*)(st + (lane & 31) * 256 + (((2 * s2 + (lane >> 5)) ^ ksw) << 4));
-        const bf16x8_t kf1 = *(const bf16x8_t*)(st + (lane & 31) * 256 + (((2 * s2 + 2 + (lane >> 5)) ^ ksw) << 4));
-        sacc = mfma32(kf0, qf.f[s2], sacc);
-        sacc2 = mfma32(kf1, qf.f[s2 + 1], sacc2);
-      }
+      // p = exp(s*scale - m) = 2^(s*scale*log2e - m*log2e): one FMA and one
+      // exp2 per element.  Only the last chunk can hold positions past kk.
+      // Query rows past the block end hold finite values (their loads are
+      // clamped) and are never stored, so they need no mask.
       float p[16];
+      if (t * SK + SK <= kk) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int j = t * SK + acc_key(r, lane);
-        const float e = __expf((sacc[r] + sacc2[r]) * scale - mrow);
-        p[r] = (j < kk && qok) ? e : 0.f;
-        dpart += p[r];
+        for (int r = 0; r < 16; ++r) {
+          p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], sl2, -ml2));
+          dpart += p[r];
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int j = t * SK + acc_key(r, lane);
+          p[r] = j < kk ? __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], sl2, -ml2)) : 0.f;
+          dpart += p[r];
+        }
       }
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
@@ -460,8 +493,11 @@ __global__ __launch_bounds__(256, 2) void attn_sparse(const uint16_t* __restrict
           acc[ni] = mfma32(pa, vb, acc[ni]);
         }
       }
+      if (t + 1 < KT) {
+        sacc = snext;
 #pragma unroll
-      for (int i = 0; i < INS; ++i) ids_a[i] = ids_b[i];
+        for (int i = 0; i < INS; ++i) ids_a[i] = ids_b[i];
+      }
     }
   } else {
     load_qmd();

@@ -135,18 +135,23 @@ __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
 }
-// wait_vmcnt with a count known only at run time (wave-uniform, 0 .. 63):
-// dispatches to the immediate form.
+// wait_vmcnt with a count known only at run time (wave-uniform, LO .. HI):
+// a binary search down to the immediate form.
+template <int LO, int HI>
+__device__ __forceinline__ void wait_vmcnt_range(int n) {
+  if constexpr (LO == HI) {
+    wait_vmcnt<LO>();
+  } else {
+    constexpr int MID = (LO + HI) / 2;
+    if (n <= MID)
+      wait_vmcnt_range<LO, MID>(n);
+    else
+      wait_vmcnt_range<MID + 1, HI>(n);
+  }
+}
 template <int N>
 __device__ __forceinline__ void wait_vmcnt_upto(int n) {
-  if constexpr (N == 0) {
-    wait_vmcnt<0>();
-  } else {
-    if (n >= N)
-      wait_vmcnt<N>();
-    else
-      wait_vmcnt_upto<N - 1>(n);
-  }
+  wait_vmcnt_range<0, N>(n);
 }
 
 // Workgroup barrier without the release/acquire fences of __syncthreads (which
