@@ -20,6 +20,8 @@
 // one XCD's L2, where that head's K and V rows are re-read.
 #include <math.h>
 
+#include <type_traits>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -433,42 +435,53 @@ __global__ __launch_bounds__(256, 2) void attn_sparse(const uint16_t* __restrict
     const float sl2 = scale * 1.4426950408889634f, ml2 = mrow * 1.4426950408889634f;
     f32x16_t sacc = scores(0);
     // Software pipeline: iteration t issues the score products of chunk t+1,
-    // then the exponentials and the P V products of chunk t, so the matrix
-    // cores have independent work while the exponentials run.
-    for (int t = 0; t < KT; ++t) {
-      if (t + 1 < KT) {
-        // Stage t+1 must be complete.  Newer than it: the stages after it
-        // already issued (L each), the rest numerator if already issued, and on
-        // wave 0 the
-        // id loads of iterations t-NSS+3 .. t-1 (stage t+1 went out at
-        // iteration t-NSS+2).  Chunk t+NSS's ids (issued at iteration
-        // t+NSS-DID) are older, so they are complete too.
-        const int issued_to = (t + NSS - 2) < (KT - 1) ? (t + NSS - 2) : (KT - 1);
-        const int ahead = issued_to - (t + 1);
-        int newer = ahead * L + (t > t_r ? PRE : 0);
-        if (wave == 0) {
-          const int j0 = t - NSS + 3 > 0 ? t - NSS + 3 : 0;
-          const int j1 = (t - 1) < (KT - DID - 1) ? (t - 1) : (KT - DID - 1);
-          newer += j1 >= j0 ? j1 - j0 + 1 : 0;
+    // then the exponentials and the value products of chunk t, so the matrix
+    // cores have independent work while the exponentials run.  Iterations with
+    // t + DID < KT are the steady state: every stage, id and score issue
+    // happens, the chunk is full, the rest numerator is not yet issued, and the
+    // loads newer than stage t+1 are one stage (L) plus, on wave 0 after the
+    // first iteration, one id load.  They run without run-time conditions.
+    auto body = [&](int t, auto STEADY) __attribute__((always_inline)) {
+      constexpr bool steady = decltype(STEADY)::value;
+      f32x16_t snext;
+      if (steady || t + 1 < KT) {
+        if (steady) {
+          if (wave == 0 && t >= 1)
+            wait_vmcnt<L + 1>();
+          else
+            wait_vmcnt<L>();
+        } else {
+          // Stage t+1 must be complete.  Newer than it: the stages after it
+          // already issued (L each), the rest numerator if already issued, and
+          // on wave 0 the id loads of iterations t-NSS+3 .. t-1 (stage t+1
+          // went out at iteration t-NSS+2).  Chunk t+NSS's ids (issued at
+          // iteration t+NSS-DID) are older, so they are complete too.
+          const int issued_to = (t + NSS - 2) < (KT - 1) ? (t + NSS - 2) : (KT - 1);
+          const int ahead = issued_to - (t + 1);
+          int newer = ahead * L + (t > t_r ? PRE : 0);
+          if (wave == 0) {
+            const int j0 = t - NSS + 3 > 0 ? t - NSS + 3 : 0;
+            const int j1 = (t - 1) < (KT - DID - 1) ? (t - 1) : (KT - DID - 1);
+            newer += j1 >= j0 ? j1 - j0 + 1 : 0;
+          }
+          wait_vmcnt_upto<(NSS - 2) * L + PRE + NSS>(newer);
         }
-        wait_vmcnt_upto<(NSS - 2) * L + PRE + NSS>(newer);
         barrier();
         // Slot of stage t+NSS-1 is stage t-1's: its keys were read at
         // iteration t-2 and its values at t-1, before this barrier.
-        if (t + DID < KT) id_dma(t + DID);
-        if (t + NSS - 1 < KT) AS_ISSUE((t + NSS - 1) % NSS, ids_a);
-        if (t == t_r) load_rest();
-        if (t + NSS < KT) load_ids(t + NSS, ids_b);
+        if (steady || t + DID < KT) id_dma(t + DID);
+        if (steady || t + NSS - 1 < KT) AS_ISSUE((t + NSS - 1) % NSS, ids_a);
+        if (!steady && t == t_r) load_rest();
+        if (steady || t + NSS < KT) load_ids(t + NSS, ids_b);
+        snext = scores((t + 1) % NSS);
       }
-      f32x16_t snext;
-      if (t + 1 < KT) snext = scores((t + 1) % NSS);
       const unsigned char* st = smem + (t % NSS) * STAGE;
       // p = exp(s*scale - m) = 2^(s*scale*log2e - m*log2e): one FMA and one
       // exp2 per element.  Only the last chunk can hold positions past kk.
       // Query rows past the block end hold finite values (their loads are
       // clamped) and are never stored, so they need no mask.
       float p[16];
-      if (t * SK + SK <= kk) {
+      if (steady || t * SK + SK <= kk) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], sl2, -ml2));
@@ -493,12 +506,15 @@ __global__ __launch_bounds__(256, 2) void attn_sparse(const uint16_t* __restrict
           acc[ni] = mfma32(pa, vb, acc[ni]);
         }
       }
-      if (t + 1 < KT) {
+      if (steady || t + 1 < KT) {
         sacc = snext;
 #pragma unroll
         for (int i = 0; i < INS; ++i) ids_a[i] = ids_b[i];
       }
-    }
+    };
+    int t = 0;
+    for (; t + DID < KT; ++t) body(t, std::true_type{});
+    for (; t < KT; ++t) body(t, std::false_type{});
   } else {
     load_qmd();
     load_rest();
