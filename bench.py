@@ -192,6 +192,9 @@ def main():
     ap.add_argument("--workload", default="flux", choices=sorted(WORKLOADS))
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay each sparse step as a captured HIP graph in the timed loop (eager launches are "
+                         "as fast on this path)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain copy of known size (for scaling HBM byte counters)")
     args = ap.parse_args()
@@ -252,13 +255,39 @@ def main():
     for i in range(args.warmup):
         sparse(1 + i % (T - 1))
     torch.cuda.synchronize()
+
+    # One HIP graph per step input: the step's kernels replay back to back
+    # without per-launch host work.  Capturing records the launches without
+    # running them, so the layer state is unchanged.
+    graphs = {}
+    if args.graph:
+        side = torch.cuda.Stream()
+        for t in range(1, T):
+            g = torch.cuda.CUDAGraph()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                with torch.cuda.graph(g, stream=side):
+                    sparse(t)
+            torch.cuda.current_stream().wait_stream(side)
+            graphs[t] = g
+        torch.cuda.synchronize()
+        for i in range(args.warmup):
+            graphs[1 + i % (T - 1)].replay()
+        torch.cuda.synchronize()
+
+    def run_step(t):
+        if graphs:
+            graphs[t].replay()
+        else:
+            sparse(t)
+
     log("warmup done")
 
     # The metric: K whole sparse steps, nothing recorded between kernels.
     torch.cuda.synchronize()
     ts = time.perf_counter()
     for i in range(args.steps):
-        sparse(1 + i % (T - 1))
+        run_step(1 + i % (T - 1))
     torch.cuda.synchronize()
     te = time.perf_counter()
     ms_per_step = (te - ts) * 1e3 / args.steps
@@ -324,7 +353,7 @@ def main():
                                 "hunyuan_attn": "HunyuanVideo-shaped attention delta"}[args.workload],
                    "tokens": w["n"], "d_model": w["d"], "d_hidden": w["h"], "mlp_keep": w["k"],
                    "heads": w["heads"], "head_dim": HEAD_DIM if w["heads"] else 0, "attn_keep": w["kk"],
-                   "row_block": 128},
+                   "row_block": 128, "launch": "hip graph per step" if args.graph else "eager"},
         "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "flop_per_step": fl,
         "roofline": roof,
