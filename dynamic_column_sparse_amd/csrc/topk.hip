@@ -127,8 +127,8 @@ __global__ __launch_bounds__(kThreads) void topk_rows(const float* __restrict__ 
 //      at the top would send every key of the first passes to one bin).
 //   2. Radix select over the remaining bits, up to 8 per pass, with one
 //      256-bin histogram per wave (contention only inside a wave).
-//   3. Emit in index order: tie ranks, then output positions, each from one
-//      ballot per (batch j, wave) and a 16 x 16 prefix table.
+//   3. Emit in index order from one ballot pair per (batch j, wave) and a
+//      single 16 x 16 prefix table of packed (above, equal) counts.
 constexpr int kRegThreads = 1024;
 constexpr int kRegWaves = kRegThreads / 64;
 constexpr int kRegKeys = 16;
@@ -250,37 +250,28 @@ __global__ __launch_bounds__(kRegThreads) void topk_rows_reg(const float* __rest
 
   const uint32_t T = prefix, need = remaining;
   const uint64_t lt_mask = (lane == 0) ? 0ull : ((~0ull) >> (64 - lane));
-  // Tie ranks: ties taken in index order, the first `need` of them.
-  uint64_t em[kRegKeys];
+  // One scan places every output: index i is taken if its key is above T, or
+  // equal to T with fewer than `need` equal keys before it; its position is
+  // (keys above T before i) + min(keys equal to T before i, need).  Both counts
+  // of each (batch, wave) travel packed in one word (each fits in 16 bits).
+  uint64_t gm[kRegKeys], em[kRegKeys];
 #pragma unroll
   for (int j = 0; j < kRegKeys; ++j) {
-    em[j] = __ballot(tid + kRegThreads * j < cols && key[j] == T);
-    if (lane == 0) tab[j * kRegWaves + wave] = (uint32_t)__popcll(em[j]);
-  }
-  __syncthreads();
-  table_scan(tab, wsum, tid);
-  uint32_t take_bits = 0;
-#pragma unroll
-  for (int j = 0; j < kRegKeys; ++j) {
-    const int i = tid + kRegThreads * j;
-    const bool valid = i < cols;
-    const bool eq = valid && key[j] == T;
-    const uint32_t eq_rank = tab[j * kRegWaves + wave] + (uint32_t)__popcll(em[j] & lt_mask);
-    if ((valid && key[j] > T) || (eq && eq_rank < need)) take_bits |= 1u << j;
-  }
-  __syncthreads();
-  // Output positions: taken indices in ascending order.
-#pragma unroll
-  for (int j = 0; j < kRegKeys; ++j) {
-    em[j] = __ballot((take_bits >> j) & 1u);
-    if (lane == 0) tab[j * kRegWaves + wave] = (uint32_t)__popcll(em[j]);
+    const bool valid = tid + kRegThreads * j < cols;
+    gm[j] = __ballot(valid && key[j] > T);
+    em[j] = __ballot(valid && key[j] == T);
+    if (lane == 0) tab[j * kRegWaves + wave] = (uint32_t)__popcll(gm[j]) | ((uint32_t)__popcll(em[j]) << 16);
   }
   __syncthreads();
   table_scan(tab, wsum, tid);
 #pragma unroll
   for (int j = 0; j < kRegKeys; ++j) {
-    if ((take_bits >> j) & 1u) {
-      const uint32_t pos = tab[j * kRegWaves + wave] + (uint32_t)__popcll(em[j] & lt_mask);
+    const uint32_t base = tab[j * kRegWaves + wave];
+    const uint32_t gt_before = (base & 0xffffu) + (uint32_t)__popcll(gm[j] & lt_mask);
+    const uint32_t eq_before = (base >> 16) + (uint32_t)__popcll(em[j] & lt_mask);
+    const bool gt = (gm[j] >> lane) & 1ull, eq = (em[j] >> lane) & 1ull;
+    if (gt || (eq && eq_before < need)) {
+      const uint32_t pos = gt_before + (eq_before < need ? eq_before : need);
       if (pos < (uint32_t)k) orow[pos] = tid + kRegThreads * j;
     }
   }
