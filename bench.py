@@ -4,7 +4,10 @@
 One step = one sparse diffusion step of a FLUX.1-dev-shaped DiT layer: identify
 the top-k MLP hidden units per 128-token block, the sparse MLP delta (gathered
 GEMM1 + GELU + delta + fused cache writeback, gathered GEMM2 into y) and the
-sparse attention delta over the top-k keys of every (head, query block).
+sparse attention delta over the top-k keys of every (head, query block).  The
+layer is taken as a parallel block (attention and MLP both read the block's
+input, as in FLUX's single-stream blocks), so by default the MLP's GEMM2 and
+the attention delta share one kernel grid (--separate: one call each).
 Inputs are seeded synthetic tensors of the real shapes (random-init weights,
 drifting activations), resident in HBM before the timed region.
 
@@ -61,6 +64,8 @@ def kernel_work(name, w):
         return 2.0 * n * k * d, "mfma"
     if name == "attn_sparse":
         return 4.0 * n * kk * HEAD_DIM * H, "mfma"
+    if name == "sparse_step_fused":
+        return 2.0 * n * k * d + 4.0 * n * kk * HEAD_DIM * H, "mfma"
     if name == "topk_rows":
         return float(nb * h * 4 + nb * k * 4), "hbm"
     return None, None
@@ -192,6 +197,8 @@ def main():
     ap.add_argument("--workload", default="flux", choices=sorted(WORKLOADS))
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--separate", action="store_true",
+                    help="run the MLP and attention deltas as separate calls instead of the shared-grid step")
     ap.add_argument("--graph", action="store_true",
                     help="replay each sparse step as a captured HIP graph in the timed loop (eager launches are "
                          "as fast on this path)")
@@ -211,7 +218,7 @@ def main():
 
     import synthetic as syn
     from dynamic_column_sparse_amd import lib
-    from dynamic_column_sparse_amd.layers import AttnDelta, MLPDelta
+    from dynamic_column_sparse_amd.layers import AttnDelta, MLPDelta, sparse_step
 
     w = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
@@ -245,7 +252,12 @@ def main():
         if att:
             att.step(*qkv[t], refresh=True)
 
+    fused = bool(mlp and att) and not args.separate
+
     def sparse(t):
+        if fused:
+            sparse_step(mlp, att, xs[t], *qkv[t])
+            return
         if mlp:
             mlp.step(xs[t], refresh=False)
         if att:
@@ -353,7 +365,8 @@ def main():
                                 "hunyuan_attn": "HunyuanVideo-shaped attention delta"}[args.workload],
                    "tokens": w["n"], "d_model": w["d"], "d_hidden": w["h"], "mlp_keep": w["k"],
                    "heads": w["heads"], "head_dim": HEAD_DIM if w["heads"] else 0, "attn_keep": w["kk"],
-                   "row_block": 128, "launch": "hip graph per step" if args.graph else "eager"},
+                   "row_block": 128, "launch": ("hip graph per step" if args.graph else "eager")
+                   + ("; MLP phase 2 and attention share one kernel" if fused else "")},
         "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "flop_per_step": fl,
         "roofline": roof,

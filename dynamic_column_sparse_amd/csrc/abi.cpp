@@ -37,6 +37,8 @@ int ok() {
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 constexpr int64_t kMaxGridY = 65535;
+// Workgroups of 256 threads in one launch (the grid's work-item count is 32-bit).
+constexpr int64_t kMaxGroups = (int64_t)UINT32_MAX / 256;
 
 int hip_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return ok();
@@ -69,8 +71,8 @@ int check_attn(const chipmunk_attn* L) {
     return fail(CHIPMUNK_E_UNSUPPORTED, "head_dim must be %d (got %d)", CHIPMUNK_HEAD_DIM, L->head_dim);
   if (!std::isfinite(L->scale)) return fail(CHIPMUNK_E_SHAPE, "scale must be finite");
   if (L->n > INT32_MAX) return fail(CHIPMUNK_E_SHAPE, "n must fit in int32");
-  if (chipmunk::row_blocks(L->n) * (int64_t)L->heads > INT32_MAX)
-    return fail(CHIPMUNK_E_SHAPE, "heads * row blocks exceeds the grid limit");
+  if (chipmunk::row_blocks(L->n) * (int64_t)L->heads > kMaxGroups)
+    return fail(CHIPMUNK_E_SHAPE, "heads * row blocks exceeds the grid limit (%lld workgroups)", (long long)kMaxGroups);
   if (!L->m || !L->num || !L->den) return fail(CHIPMUNK_E_NULLPTR, "layer m, num and den are required");
   if (!aligned(L->m, 4) || !aligned(L->den, 4) || !aligned(L->num, 16) || (L->score && !aligned(L->score, 4)))
     return fail(CHIPMUNK_E_ALIGN, "num must be 16-byte aligned; m, den, score 4-byte aligned");
@@ -86,6 +88,56 @@ int check_bf16_in(const void* p, const char* name) {
 // D tiles [nb][128][kp], row-major per block (kp = k rounded up to 64).
 size_t sparse_mlp_ws(int64_t n, int32_t k) {
   return (size_t)chipmunk::row_blocks(n) * (size_t)chipmunk::padded_k(k) * chipmunk::kRowBlock * sizeof(uint16_t);
+}
+
+// Arguments of the sparse MLP delta.
+int check_sparse_mlp(const chipmunk_mlp* L, const uint16_t* x, const int32_t* idx, int32_t k, const float* y,
+                     const uint16_t* a_new_packed, const void* ws, size_t ws_bytes) {
+  int rc = check_mlp(L, false);
+  if (rc) return rc;
+  if (k < 0 || k > L->h) return fail(CHIPMUNK_E_SHAPE, "k must be in [0, h] (k=%d, h=%d)", k, L->h);
+  if ((rc = check_bf16_in(x, "x"))) return rc;
+  if (!y) return fail(CHIPMUNK_E_NULLPTR, "y is NULL");
+  if (!aligned(y, 16)) return fail(CHIPMUNK_E_ALIGN, "y must be 16-byte aligned");
+  if (k > 0 && !idx) return fail(CHIPMUNK_E_NULLPTR, "idx is NULL");
+  if (idx && !aligned(idx, 4)) return fail(CHIPMUNK_E_ALIGN, "idx must be 4-byte aligned");
+  if (a_new_packed && !aligned(a_new_packed, 16)) return fail(CHIPMUNK_E_ALIGN, "a_new_packed must be 16-byte aligned");
+  const size_t need = sparse_mlp_ws(L->n, k);
+  if (k > 0 && (!ws || ws_bytes < need))
+    return fail(CHIPMUNK_E_WORKSPACE, "workspace of %zu bytes required (got %zu)", need, ws ? ws_bytes : (size_t)0);
+  if (ws && !aligned(ws, 16)) return fail(CHIPMUNK_E_ALIGN, "ws must be 16-byte aligned");
+  return CHIPMUNK_OK;
+}
+
+// Arguments of the sparse attention delta.
+int check_sparse_attn(const chipmunk_attn* L, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                      const int32_t* idx, int32_t kk, int mode, const float* o) {
+  int rc = check_attn(L);
+  if (rc) return rc;
+  if (mode != CHIPMUNK_ATTN_SPARSE && mode != CHIPMUNK_ATTN_REFRESH)
+    return fail(CHIPMUNK_E_SHAPE, "mode must be CHIPMUNK_ATTN_SPARSE or CHIPMUNK_ATTN_REFRESH (got %d)", mode);
+  if (kk < 0 || (int64_t)kk > L->n) return fail(CHIPMUNK_E_SHAPE, "kk must be in [0, n] (kk=%d)", kk);
+  if ((rc = check_bf16_in(q, "q")) || (rc = check_bf16_in(k, "k")) || (rc = check_bf16_in(v, "v"))) return rc;
+  if (kk > 0 && !idx) return fail(CHIPMUNK_E_NULLPTR, "idx is NULL");
+  if (idx && !aligned(idx, 4)) return fail(CHIPMUNK_E_ALIGN, "idx must be 4-byte aligned");
+  if (mode == CHIPMUNK_ATTN_SPARSE) {
+    if (!o) return fail(CHIPMUNK_E_NULLPTR, "o is NULL");
+    if (!aligned(o, 16)) return fail(CHIPMUNK_E_ALIGN, "o must be 16-byte aligned");
+  }
+  return CHIPMUNK_OK;
+}
+
+// A byte range [p, p + bytes) of one buffer named in an error message.
+struct Span {
+  const void* p;
+  size_t bytes;
+  const char* name;
+};
+
+bool overlap(const Span& a, const Span& b) {
+  if (!a.p || !b.p || !a.bytes || !b.bytes) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+  return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
 }
 
 
@@ -119,7 +171,7 @@ hipEvent_t take_event() {
 const char* kernel_name(int kid) {
   static const char* names[K_COUNT] = {"mlp_gemm1_sparse", "mlp_gemm1_dense", "mlp_gemm2_sparse", "mlp_gemm2_dense",
                                        "topk_rows",        "cache_writeback", "attn_stats",       "attn_dense",
-                                       "attn_sparse",      "attn_refresh"};
+                                       "attn_sparse",      "attn_refresh",     "sparse_step_fused"};
   return (kid >= 0 && kid < K_COUNT) ? names[kid] : "";
 }
 
@@ -260,19 +312,8 @@ extern "C" int chipmunk_identify_topk(const float* score, int64_t rows, int64_t 
 extern "C" int chipmunk_sparse_mlp_delta(const chipmunk_mlp* L, const uint16_t* x, const int32_t* idx, int32_t k,
                                          float* y, uint16_t* a_new_packed, void* ws, size_t ws_bytes, void* stream) {
   try {
-    int rc = check_mlp(L, false);
+    int rc = check_sparse_mlp(L, x, idx, k, y, a_new_packed, ws, ws_bytes);
     if (rc) return rc;
-    if (k < 0 || k > L->h) return fail(CHIPMUNK_E_SHAPE, "k must be in [0, h] (k=%d, h=%d)", k, L->h);
-    if ((rc = check_bf16_in(x, "x"))) return rc;
-    if (!y) return fail(CHIPMUNK_E_NULLPTR, "y is NULL");
-    if (!aligned(y, 16)) return fail(CHIPMUNK_E_ALIGN, "y must be 16-byte aligned");
-    if (k > 0 && !idx) return fail(CHIPMUNK_E_NULLPTR, "idx is NULL");
-    if (idx && !aligned(idx, 4)) return fail(CHIPMUNK_E_ALIGN, "idx must be 4-byte aligned");
-    if (a_new_packed && !aligned(a_new_packed, 16)) return fail(CHIPMUNK_E_ALIGN, "a_new_packed must be 16-byte aligned");
-    const size_t need = sparse_mlp_ws(L->n, k);
-    if (k > 0 && (!ws || ws_bytes < need))
-      return fail(CHIPMUNK_E_WORKSPACE, "workspace of %zu bytes required (got %zu)", need, ws ? ws_bytes : (size_t)0);
-    if (ws && !aligned(ws, 16)) return fail(CHIPMUNK_E_ALIGN, "ws must be 16-byte aligned");
     if (k == 0) return ok();
     hipStream_t s = static_cast<hipStream_t>(stream);
     uint16_t* dbuf = static_cast<uint16_t*>(ws);
@@ -290,24 +331,63 @@ extern "C" int chipmunk_sparse_attn_delta(const chipmunk_attn* L, const uint16_t
                                           const uint16_t* v, const int32_t* idx, int32_t kk, int mode, float* o,
                                           void* stream) {
   try {
-    int rc = check_attn(L);
+    int rc = check_sparse_attn(L, q, k, v, idx, kk, mode, o);
     if (rc) return rc;
-    if (mode != CHIPMUNK_ATTN_SPARSE && mode != CHIPMUNK_ATTN_REFRESH)
-      return fail(CHIPMUNK_E_SHAPE, "mode must be CHIPMUNK_ATTN_SPARSE or CHIPMUNK_ATTN_REFRESH (got %d)", mode);
-    if (kk < 0 || (int64_t)kk > L->n) return fail(CHIPMUNK_E_SHAPE, "kk must be in [0, n] (kk=%d)", kk);
-    if ((rc = check_bf16_in(q, "q")) || (rc = check_bf16_in(k, "k")) || (rc = check_bf16_in(v, "v"))) return rc;
-    if (kk > 0 && !idx) return fail(CHIPMUNK_E_NULLPTR, "idx is NULL");
-    if (idx && !aligned(idx, 4)) return fail(CHIPMUNK_E_ALIGN, "idx must be 4-byte aligned");
-    if (mode == CHIPMUNK_ATTN_SPARSE) {
-      if (!o) return fail(CHIPMUNK_E_NULLPTR, "o is NULL");
-      if (!aligned(o, 16)) return fail(CHIPMUNK_E_ALIGN, "o must be 16-byte aligned");
-    }
     if (mode == CHIPMUNK_ATTN_REFRESH && kk == 0) return ok();
     hipError_t e = chipmunk::launch_attn_sparse(mode == CHIPMUNK_ATTN_REFRESH, q, k, v, idx, L->m, L->num, L->den, o,
                                                 L->n, L->heads, kk, L->scale, static_cast<hipStream_t>(stream));
     return hip_status(e, "attention delta launch");
   } catch (...) {
     return fail(CHIPMUNK_E_INTERNAL, "internal error in chipmunk_sparse_attn_delta");
+  }
+}
+
+extern "C" int chipmunk_sparse_step(const chipmunk_mlp* M, const uint16_t* x, const int32_t* mlp_idx, int32_t k,
+                                    float* y, uint16_t* a_new_packed, void* ws, size_t ws_bytes,
+                                    const chipmunk_attn* A, const uint16_t* q, const uint16_t* kx, const uint16_t* v,
+                                    const int32_t* attn_idx, int32_t kk, float* o, void* stream) {
+  try {
+    int rc = check_sparse_mlp(M, x, mlp_idx, k, y, a_new_packed, ws, ws_bytes);
+    if (rc) return rc;
+    if ((rc = check_sparse_attn(A, q, kx, v, attn_idx, kk, CHIPMUNK_ATTN_SPARSE, o))) return rc;
+    // The two deltas run side by side in one grid: nothing one of them writes
+    // may share memory with anything the other touches.
+    const size_t nb = (size_t)chipmunk::row_blocks(M->n), nba = (size_t)chipmunk::row_blocks(A->n);
+    const size_t toks = (size_t)A->heads * (size_t)A->n, hd = CHIPMUNK_HEAD_DIM;
+    const size_t mk = k > 0 ? (size_t)k : 0, ak = kk > 0 ? (size_t)kk : 0;
+    const Span mlp_w[] = {{y, (size_t)M->n * M->d * 4, "y"},
+                          {M->a_cache, nb * M->h * 128 * 2, "mlp a_cache"},
+                          {a_new_packed, nb * mk * 128 * 2, "a_new_packed"},
+                          {ws, k > 0 ? sparse_mlp_ws(M->n, k) : 0, "ws"}};
+    const Span mlp_r[] = {{x, (size_t)M->n * M->d * 2, "x"},
+                          {M->w1t, (size_t)M->h * M->d * 2, "w1t"},
+                          {M->w2, (size_t)M->h * M->d * 2, "w2"},
+                          {M->b1, M->b1 ? (size_t)M->h * 4 : 0, "b1"},
+                          {mlp_idx, nb * mk * 4, "mlp idx"}};
+    const Span att_w[] = {{o, toks * hd * 4, "o"}};
+    const Span att_r[] = {{q, toks * hd * 2, "q"},          {kx, toks * hd * 2, "k"},
+                          {v, toks * hd * 2, "v"},          {attn_idx, (size_t)A->heads * nba * ak * 4, "attn idx"},
+                          {A->m, toks * 4, "m"},            {A->num, toks * hd * 4, "num"},
+                          {A->den, toks * 4, "den"}};
+    const int64_t groups = (k > 0 ? (int64_t)(M->d / 128) * (int64_t)nb + 8 : 0) + (int64_t)A->heads * (int64_t)nba;
+    if (groups > kMaxGroups)
+      return fail(CHIPMUNK_E_SHAPE, "the fused grid exceeds %lld workgroups", (long long)kMaxGroups);
+    for (const Span& w : mlp_w) {
+      for (const Span& r : att_w)
+        if (overlap(w, r)) return fail(CHIPMUNK_E_SHAPE, "%s overlaps %s", w.name, r.name);
+      for (const Span& r : att_r)
+        if (overlap(w, r)) return fail(CHIPMUNK_E_SHAPE, "%s overlaps %s", w.name, r.name);
+    }
+    for (const Span& w : att_w)
+      for (const Span& r : mlp_r)
+        if (overlap(w, r)) return fail(CHIPMUNK_E_SHAPE, "%s overlaps %s", w.name, r.name);
+    hipError_t e = chipmunk::launch_sparse_step(x, M->w1t, M->b1, mlp_idx, M->a_cache, static_cast<uint16_t*>(ws),
+                                                a_new_packed, M->w2, y, M->n, M->d, M->h, k, q, kx, v, attn_idx, A->m,
+                                                A->num, A->den, o, A->n, A->heads, kk, A->scale,
+                                                static_cast<hipStream_t>(stream));
+    return hip_status(e, "sparse step launch");
+  } catch (...) {
+    return fail(CHIPMUNK_E_INTERNAL, "internal error in chipmunk_sparse_step");
   }
 }
 

@@ -22,6 +22,7 @@ enum KernelId {
   K_ATTN_DENSE,
   K_ATTN_SPARSE,
   K_ATTN_REFRESH,
+  K_SPARSE_STEP_FUSED,
   K_COUNT
 };
 const char* kernel_name(int kid);
@@ -53,5 +54,13 @@ hipError_t launch_attn_dense(const uint16_t* q, const uint16_t* k, const uint16_
 hipError_t launch_attn_sparse(bool refresh, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                               const int32_t* idx, const float* m, float* num, float* den, float* o, int64_t n,
                               int heads, int kk, float scale, hipStream_t s);
+// Sparse MLP phase 1, then one kernel with the MLP phase-2 tiles first and the
+// sparse attention units after them (k = 0: attention units only).
+hipError_t launch_sparse_step(const uint16_t* x, const uint16_t* w1t, const float* b1, const int32_t* midx,
+                              uint16_t* a_cache, uint16_t* dbuf, uint16_t* a_packed, const uint16_t* w2, float* y,
+                              int64_t n, int d, int h, int k, const uint16_t* q, const uint16_t* kx,
+                              const uint16_t* v, const int32_t* aidx, const float* m, const float* num,
+                              const float* den, float* o, int64_t na, int heads, int kk, float scale,
+                              hipStream_t s);
 
 }  // namespace chipmunk

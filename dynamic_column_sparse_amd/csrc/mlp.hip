@@ -1,636 +1,7 @@
-// MLP kernels of the column-sparse delta (gfx950).
-//
-// Phase 1 (mlp_gemm1): one workgroup per (128-row block b, tile of BN gathered
-// hidden units).  The tile's hidden units are rows of W1^T ([h][d], one
-// contiguous 2*d-byte row each), so gathering them is a set of coalesced row
-// reads; the x rows of block b are contiguous too.  Both operands stream
-// through a 3-stage LDS ring in K-chunks of 64, filled by direct global->LDS
-// loads two chunks ahead, and feed the bf16 matrix cores (32x32x16, fp32
-// accumulate).  Epilogue per element: + b1, GELU (tanh form), round to bf16, then
-//   sparse: D = a_new - a_cache (exact in fp32, rounded to bf16 as the next
-//           product's operand); a_new -> cache (fused writeback) or a packed
-//           buffer;
-//   dense:  D = a_new; score[b][j] = sum over real rows |a_new - a_cache|;
-//           a_new -> cache.
-// Phase 2 (mlp_gemm2): one workgroup per (block b, BN output columns); the
-// reduction runs over the block's gathered hidden units: D tile rows
-// ([nb][kp][128], or the activation cache itself for the dense step) times the
-// gathered W2 rows ([h][d], contiguous per unit).  Both tiles are copied into
-// LDS as they lie in memory ([unit][column]) by direct global->LDS loads and
-// read back with the transposing LDS read, so no register staging is needed.
-// y rows are read, added to and written once (no atomics: every output element
-// has exactly one writer, so results are deterministic).
-//
-// Work order: units are numbered tile-major (all row blocks of one column tile
-// consecutively) and each XCD runs one contiguous range of them.  Row blocks
-// that run together then gather weight rows from the same range of hidden units
-// (index sets are ascending), which that XCD's L2 serves after the first fetch.
-#include "device_common.h"
-#include "internal.h"
+// Launchers of the MLP kernels (kernel code: mlp_kernels.h).
+#include "mlp_kernels.h"
 
 namespace chipmunk {
-namespace {
-
-constexpr int BM = 128;   // rows per block (one row block)
-constexpr int BK = 64;    // reduction chunk
-constexpr int NS = 3;     // LDS ring stages: one consumed, two in flight
-#ifndef MLP_GROUP_TILES
-#define MLP_GROUP_TILES 2
-#endif
-constexpr int kGroupTiles = MLP_GROUP_TILES;   // column tiles of one row block run back to back
-
-template <int BN, bool DENSE>
-__global__ __launch_bounds__(256, 2) void mlp_gemm1(const uint16_t* __restrict__ x,
-                                                    const uint16_t* __restrict__ w1t,
-                                                    const float* __restrict__ b1,
-                                                    const int32_t* __restrict__ idx,
-                                                    uint16_t* __restrict__ a_cache,
-                                                    uint16_t* __restrict__ dbuf,
-                                                    uint16_t* __restrict__ a_packed,
-                                                    float* __restrict__ score, int64_t n, int d, int h, int k,
-                                                    int kp) {
-  constexpr int WN = BN / 2;          // columns per wave (2x2 wave grid)
-  constexpr int NI = WN / 32;         // 32-wide column subtiles per wave
-  constexpr int MI = 2;               // 32-row subtiles per wave (64 rows)
-  constexpr int BK = 32, NS = 3;      // 32-deep K-chunks, 3-stage ring: 72 KB, two workgroups per CU
-  constexpr int ROWB = BK * 2;        // LDS row: 64 bytes = 4 chunks of 16 bytes
-  constexpr int CPR = ROWB / 16, RPI = 1024 / ROWB;   // chunks per row, rows per direct load
-  constexpr int A_INS = BM / RPI / 4; // direct loads per wave per stage, x tile
-  constexpr int B_INS = BN / RPI / 4; // same, W1^T tile
-  constexpr int L = A_INS + B_INS;    // DMA instructions per thread per stage
-  constexpr int A_BYTES = BM * ROWB;
-  constexpr int STAGE = (BM + BN) * ROWB;
-
-  __shared__ __align__(16) unsigned char smem[NS * STAGE];
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, kept in SGPRs
-  const uint32_t smem_lds = lds_addr(smem);
-  const int wm = wave >> 1, wn = wave & 1;
-  const int kcols = DENSE ? h : k;
-  const int nb = (int)row_blocks(n), ntiles = (kcols + BN - 1) / BN;
-  const int u = xcd_unit(blockIdx.x, ntiles * nb);
-  if (u >= ntiles * nb) return;
-  int b, tile;
-  grouped_tile(u, nb, ntiles, kGroupTiles, b, tile);
-  const int c0 = tile * BN;
-  const int64_t r0 = (int64_t)b * BM;
-  const int rows = (int)(n - r0 < BM ? n - r0 : BM);
-
-  // Source of the 16-byte chunk this lane fills in each DMA instruction: row
-  // (instruction's first row + lane/8), physical chunk lane%8, logical chunk
-  // (lane%8) ^ swz8(row).  Rows past the data are clamped to a valid row: their
-  // products only reach output rows/columns the epilogue never stores.
-  const int lrow = lane / CPR, pch = lane % CPR;
-  const uint16_t* asrc[A_INS];
-#pragma unroll
-  for (int i = 0; i < A_INS; ++i) {
-    const int r = (wave * A_INS + i) * RPI + lrow;
-    const int rg = r < rows ? r : rows - 1;
-    asrc[i] = x + (r0 + rg) * (int64_t)d + ((pch ^ swz4(r)) << 3);
-  }
-  const uint16_t* bsrc[B_INS];
-#pragma unroll
-  for (int i = 0; i < B_INS; ++i) {
-    const int r = (wave * B_INS + i) * RPI + lrow;
-    const int p = c0 + r;
-    int j = 0;
-    if (p < kcols) j = DENSE ? p : clamp_index(idx[(int64_t)b * k + p], h);
-    bsrc[i] = w1t + (int64_t)j * d + ((pch ^ swz4(r)) << 3);
-  }
-
-#define G1_ISSUE(kt_, buf_)                                                                 \
-  {                                                                                         \
-    const uint32_t st_ = smem_lds + (buf_) * STAGE;                                         \
-    _Pragma("unroll") for (int i = 0; i < A_INS; ++i)                                       \
-        dma16_at(asrc[i] + (kt_) * BK, st_ + (wave * A_INS + i) * 1024);                    \
-    _Pragma("unroll") for (int i = 0; i < B_INS; ++i)                                       \
-        dma16_at(bsrc[i] + (kt_) * BK, st_ + A_BYTES + (wave * B_INS + i) * 1024);          \
-  }
-
-  f32x16_t acc[MI][NI];
-#pragma unroll
-  for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < NI; ++ni)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
-
-  // Epilogue column ids and biases, fetched before the main loop so their
-  // latency hides under it.
-  int jcol[NI];
-  bool valid[NI];
-  float bias[NI];
-#pragma unroll
-  for (int ni = 0; ni < NI; ++ni) {
-    const int p = c0 + wn * WN + ni * 32 + (lane & 31);
-    valid[ni] = p < kcols;
-    jcol[ni] = valid[ni] ? (DENSE ? p : clamp_index(idx[(int64_t)b * k + p], h)) : 0;
-    bias[ni] = (valid[ni] && b1) ? b1[jcol[ni]] : 0.f;
-  }
-
-  // Operand reads: lane l reads row (base + l%32), logical chunk 2s + l/32.  Every
-  // row base is a multiple of 32, so the swizzle depends on the lane only.
-  const int sw = swz4(lane & 31);
-  const int KT = d / BK;
-  G1_ISSUE(0, 0);
-  if (KT > 1) G1_ISSUE(1, 1);
-  for (int kt = 0; kt < KT; ++kt) {
-    if (kt + 1 < KT)
-      wait_vmcnt<L>();
-    else
-      wait_vmcnt<0>();
-    barrier();
-    if (kt + 2 < KT) G1_ISSUE(kt + 2, (kt + 2) % NS);
-    const unsigned char* st = smem + (kt % NS) * STAGE;
-    // Operand fragments of K-substep s+1 are read while substep s multiplies.
-    bf16x8_t af[2][MI], bfr[2][NI];
-#define G1_FRAG(s_, q_)                                                                              \
-    {                                                                                                \
-      const int coff = (((2 * (s_) + (lane >> 5)) ^ sw) << 4);                                       \
-      _Pragma("unroll") for (int mi = 0; mi < MI; ++mi)                                              \
-        af[q_][mi] = *(const bf16x8_t*)(st + (wm * 64 + mi * 32 + (lane & 31)) * ROWB + coff);       \
-      _Pragma("unroll") for (int ni = 0; ni < NI; ++ni)                                              \
-        bfr[q_][ni] = *(const bf16x8_t*)(st + A_BYTES + (wn * WN + ni * 32 + (lane & 31)) * ROWB + coff); \
-    }
-    G1_FRAG(0, 0);
-#pragma unroll
-    for (int s = 0; s < BK / 16; ++s) {
-      if (s + 1 < BK / 16) G1_FRAG(s + 1, (s + 1) & 1);
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = mfma32(af[s & 1][mi], bfr[s & 1][ni], acc[mi][ni]);
-    }
-#undef G1_FRAG
-  }
-#undef G1_ISSUE
-
-  // ---- epilogue ----
-  // a_new = bf16(GELU(acc + b1)) is staged in the (now idle) LDS ring as
-  // [tile column][128 rows], so that the cache columns (256 contiguous bytes
-  // each) are then read and written as whole 16-byte chunks by 16 consecutive
-  // lanes.  Chunk c (rows 8c..8c+7) of tile column t is stored at chunk
-  // c ^ (t % 16); the column's hidden-unit id follows the tile.
-  constexpr int CI = BN / 16;                // tile columns per thread in the coalesced phase
-  static_assert(BN * 256 + BN * 4 <= NS * STAGE, "staging tile exceeds the LDS ring");
-  unsigned char* stile = smem;
-  int* scol = (int*)(smem + BN * 256);
-  barrier();                                 // every wave is done reading the ring
-#pragma unroll
-  for (int ni = 0; ni < NI; ++ni) {
-    const int t = wn * WN + ni * 32 + (lane & 31);
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int m0 = wm * 64 + mi * 32 + g * 8 + (lane >> 5) * 4;
-        float av[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          av[e] = (valid[ni] && m0 + e < rows) ? gelu_tanh(acc[mi][ni][g * 4 + e] + bias[ni]) : 0.f;
-        *(uint2*)(stile + t * 256 + (((m0 >> 3) ^ (t & 15)) << 4) + (m0 & 7) * 2) =
-            make_uint2(pack2(av[0], av[1]), pack2(av[2], av[3]));
-      }
-    if (wm == 0 && lane < 32) scol[t] = jcol[ni];
-  }
-  __syncthreads();
-
-  const int ch = tid & 15, tc = tid >> 4;
-  uint4 oldv[CI];
-#pragma unroll
-  for (int i = 0; i < CI; ++i) {
-    const int t = tc + 16 * i;
-    if (c0 + t < kcols)
-      oldv[i] = *(const uint4*)(a_cache + ((int64_t)b * h + scol[t]) * BM + ch * 8);
-    else
-      oldv[i] = make_uint4(0, 0, 0, 0);
-  }
-  float colsum[CI];
-#pragma unroll
-  for (int i = 0; i < CI; ++i) {
-    const int t = tc + 16 * i, p = c0 + t;
-    const uint4 an = *(const uint4*)(stile + t * 256 + ((ch ^ tc) << 4));
-    uint32_t dw[4];
-    colsum[i] = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const uint32_t a2 = word_of(an, w), o2 = word_of(oldv[i], w);
-      float dv[2];
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const bool live = ch * 8 + w * 2 + e < rows;
-        dv[e] = live ? bf2f((a2 >> (16 * e)) & 0xffffu) - bf2f((o2 >> (16 * e)) & 0xffffu) : 0.f;
-        if (DENSE) colsum[i] += fabsf(dv[e]);
-      }
-      dw[w] = pack2(dv[0], dv[1]);
-    }
-    if (p < kcols) {
-      if (DENSE || !a_packed)
-        *(uint4*)(a_cache + ((int64_t)b * h + scol[t]) * BM + ch * 8) = an;
-      else
-        *(uint4*)(a_packed + ((int64_t)b * k + p) * BM + ch * 8) = an;
-    }
-    // D replaces a_new in the staging tile: this thread is the only reader and
-    // writer of this 16-byte slot.
-    if (!DENSE) *(uint4*)(stile + t * 256 + ((ch ^ tc) << 4)) = make_uint4(dw[0], dw[1], dw[2], dw[3]);
-  }
-  if (!DENSE) {
-    // D leaves row-major ([block][128 rows][kp]) so phase 2 reads it as a plain
-    // K-contiguous operand.  A 16-lane group transposes 8 units x 16 rows out of
-    // the [unit][row] tile with two transposing reads (units u..u+3, u+4..u+7):
-    // lane j points at unit row u + j/4, tokens 4(j%4)..+3 of its 16-row block,
-    // and receives the 4 units of token j.  Units k..kp of the tile are zero
-    // (their a_new and cached values are zero), so phase 2 can stream whole
-    // 32-unit chunks.
-    __syncthreads();
-    const int grp = lane >> 4, j = lane & 15;
-#pragma unroll 4
-    for (int it = 0; it < BN / 16; ++it) {
-      const int task = it * 16 + wave * 4 + grp;
-      const int u8 = task % (BN / 8), mb = task / (BN / 8);
-      const int p = c0 + u8 * 8;
-      const int mp = mb * 16 + 4 * (j & 3);
-      const int t0 = u8 * 8 + (j >> 2), t1 = t0 + 4;
-      const i16x4_t lo = lds_read_tr16((const uint16_t*)(stile + t0 * 256 + (((mp >> 3) ^ (t0 & 15)) << 4) + (mp & 7) * 2));
-      const i16x4_t hi = lds_read_tr16((const uint16_t*)(stile + t1 * 256 + (((mp >> 3) ^ (t1 & 15)) << 4) + (mp & 7) * 2));
-      if (p < kp) {
-        const int m = mb * 16 + j;
-        const uint4 v = make_uint4((uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16), (uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16),
-                                   (uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16), (uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16));
-        *(uint4*)(dbuf + ((int64_t)b * BM + m) * kp + p) = v;
-      }
-    }
-  }
-  if (DENSE) {
-    // Column L1 over the block's rows: the 16 lanes of a column hold 8 rows each.
-#pragma unroll
-    for (int i = 0; i < CI; ++i) {
-      float v = colsum[i];
-      v += __shfl_xor(v, 1);
-      v += __shfl_xor(v, 2);
-      v += __shfl_xor(v, 4);
-      v += __shfl_xor(v, 8);
-      const int p = c0 + tc + 16 * i;
-      if (ch == 0 && p < kcols) score[(int64_t)b * h + p] = v;
-    }
-  }
-}
-
-template <int BN, bool DENSE>
-__global__ __launch_bounds__(256, 1) void mlp_gemm2(const uint16_t* __restrict__ src,
-                                                    const uint16_t* __restrict__ w2,
-                                                    const int32_t* __restrict__ idx,
-                                                    const float* __restrict__ b2, float* __restrict__ y,
-                                                    int64_t n, int d, int h, int k, int kp) {
-  constexpr int WN = BN / 2, NI = WN / 32, MI = 2;
-  constexpr int D_ROWB = BM * 2;             // 256-byte D tile rows
-  constexpr int W_ROWB = BN * 2;             // W2 tile rows
-  constexpr int D_BYTES = BK * D_ROWB;       // 16 KB
-  constexpr int STAGE = D_BYTES + BK * W_ROWB;
-  constexpr int D_INS = D_BYTES / 1024 / 4;  // DMA instructions per wave per stage
-  constexpr int W_INS = BK * W_ROWB / 1024 / 4;
-  constexpr int D_RPI = 1024 / D_ROWB;       // rows per DMA instruction
-  constexpr int W_RPI = 1024 / W_ROWB;
-
-  __shared__ __align__(16) unsigned char smem[NS * STAGE];
-  // W2 row ids, ring of 8 chunks (chunk c in slot c % 8), filled by 4-byte
-  // direct loads six chunks ahead (sparse step only).
-  __shared__ __align__(16) int sIdx[8][BK];
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, kept in SGPRs
-  const uint32_t smem_lds = lds_addr(smem);
-  const int wm = wave >> 1, wn = wave & 1;
-  const int nb = (int)row_blocks(n), ntn = d / BN;
-  const int u = xcd_unit(blockIdx.x, ntn * nb);
-  if (u >= ntn * nb) return;
-  const int b = u % nb;
-  const int n0 = (u / nb) * BN;
-  const int64_t r0 = (int64_t)b * BM;
-  const int rows = (int)(n - r0 < BM ? n - r0 : BM);
-  const int kk = DENSE ? h : k;             // real reduction length (rows kk .. kp of D are zero)
-  const uint16_t* sblk = src + (int64_t)b * kp * BM;
-  const int32_t* sidx = DENSE ? nullptr : idx + (int64_t)b * k;
-
-  // Per-lane DMA geometry.  D: row (instruction's first row + lane/16), 32-byte
-  // pair ((lane%16)/2 ^ swzp(row)), half lane%2.  W2: row (instruction's first
-  // row + lane/(BN/8)), pair ((lane%(BN/8))/2 ^ swzp(row)), half lane%2.
-  const int d_lr = lane / (D_ROWB / 16), d_pc = lane % (D_ROWB / 16);
-  const int w_lr = lane / (W_ROWB / 16), w_pc = lane % (W_ROWB / 16);
-  int d_off[D_INS], w_row[W_INS], w_off[W_INS];
-#pragma unroll
-  for (int i = 0; i < D_INS; ++i) {
-    const int r = (wave * D_INS + i) * D_RPI + d_lr;
-    d_off[i] = r * BM + ((((d_pc >> 1) ^ swzp(r)) << 1) | (d_pc & 1)) * 8;
-  }
-#pragma unroll
-  for (int i = 0; i < W_INS; ++i) {
-    const int r = (wave * W_INS + i) * W_RPI + w_lr;
-    w_row[i] = r;
-    w_off[i] = ((((w_pc >> 1) ^ swzp(r)) << 1) | (w_pc & 1)) * 8;
-  }
-  // Ids of chunk t for this lane's W2 rows (identity for the dense step).
-  auto load_ids = [&](int t, int (&ids)[W_INS]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < W_INS; ++i) {
-      const int j = t * BK + w_row[i];
-      ids[i] = DENSE ? (j < kk ? j : 0) : clamp_index(sIdx[t & 7][w_row[i]], h);
-    }
-  };
-  // 4-byte direct load of chunk t's 64 ids into ring slot t % 8 (wave 0; lanes
-  // past k read id 0 of the block, whose D rows are zero).
-  auto id_dma = [&](int t) __attribute__((always_inline)) {
-    if (!DENSE && wave == 0) {
-      const int j = t * BK + lane;
-      dma4_at(sidx + (j < kk ? j : 0), lds_addr(&sIdx[t & 7][0]));
-    }
-  };
-
-#define G2_ISSUE(kt_, buf_, ids_)                                                           \
-  {                                                                                         \
-    const uint32_t st_ = smem_lds + (buf_) * STAGE;                                         \
-    const uint16_t* dsrc_ = sblk + (int64_t)(kt_) * BK * BM;                                \
-    _Pragma("unroll") for (int i = 0; i < D_INS; ++i)                                       \
-        dma16_at(dsrc_ + d_off[i], st_ + (wave * D_INS + i) * 1024);                        \
-    _Pragma("unroll") for (int i = 0; i < W_INS; ++i)                                       \
-        dma16_at(w2 + (int64_t)ids_[i] * d + n0 + w_off[i], st_ + D_BYTES + (wave * W_INS + i) * 1024); \
-  }
-
-  f32x16_t acc[MI][NI];
-#pragma unroll
-  for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < NI; ++ni)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
-
-  // Pipeline.  Iteration kt: (a) wait for chunk kt's loads and barrier; (b) wave 0
-  // requests the ids of chunk kt+6; (c) chunk kt+2 is requested with ids read in
-  // the previous iteration; (d) the ids of chunk kt+3 are read from the ring;
-  // (e) chunk kt is multiplied.  Every global load in the loop is a direct-to-LDS
-  // load, so no register result is waited on inside it.  Wave 0 has one more
-  // load in flight per iteration (the id chunk, issued before the stage loads
-  // so that waiting for a stage also covers the ids issued with it).
-  const int KT = kp / BK;
-  constexpr int L = D_INS + W_INS;
-#pragma unroll
-  for (int t = 0; t < 6; ++t) id_dma(t);
-  wait_vmcnt<0>();
-  __syncthreads();
-  int ids_a[W_INS], ids_b[W_INS];
-  load_ids(0, ids_a);
-  if (KT > 0) G2_ISSUE(0, 0, ids_a);
-  load_ids(1, ids_b);
-  if (KT > 1) G2_ISSUE(1, 1, ids_b);
-  load_ids(2, ids_a);
-  for (int kt = 0; kt < KT; ++kt) {
-    // Outstanding loads of this wave, newest first: stage kt+1 (L) and, on wave
-    // 0 of the sparse step, the id load of chunk kt+5 if the previous
-    // iteration issued one.  Everything older (stage kt) must be complete.
-    if (kt + 1 < KT) {
-      if (!DENSE && wave == 0 && kt >= 1 && kt + 5 < KT)
-        wait_vmcnt<L + 1>();
-      else
-        wait_vmcnt<L>();
-    } else {
-      wait_vmcnt<0>();
-    }
-    barrier();
-    if (kt + 6 < KT) id_dma(kt + 6);
-    if (kt + 2 < KT) G2_ISSUE(kt + 2, (kt + 2) % NS, ids_a);
-    load_ids(kt + 3, ids_b);
-    const unsigned char* st = smem + (kt % NS) * STAGE;
-    bf16x8_t af[2][MI], bfr[2][NI];
-#define G2_FRAG(s_, q_)                                                                              \
-    {                                                                                                \
-      _Pragma("unroll") for (int mi = 0; mi < MI; ++mi)                                              \
-        af[q_][mi] = tr_operand_swz(st, D_ROWB, (s_) * 16, wm * 64 + mi * 32, lane);                 \
-      _Pragma("unroll") for (int ni = 0; ni < NI; ++ni)                                              \
-        bfr[q_][ni] = tr_operand_swz(st + D_BYTES, W_ROWB, (s_) * 16, wn * WN + ni * 32, lane);       \
-    }
-    G2_FRAG(0, 0);
-#pragma unroll
-    for (int s = 0; s < BK / 16; ++s) {
-      if (s + 1 < BK / 16) G2_FRAG(s + 1, (s + 1) & 1);
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = mfma32(af[s & 1][mi], bfr[s & 1][ni], acc[mi][ni]);
-    }
-#undef G2_FRAG
-#pragma unroll
-    for (int i = 0; i < W_INS; ++i) ids_a[i] = ids_b[i];
-  }
-#undef G2_ISSUE
-
-  // Epilogue in two phases (every old y value or bias loaded, then every sum
-  // stored): row offsets depend on d, so the compiler cannot reorder a store
-  // past a later load itself, and one-at-a-time read-modify-writes would each
-  // wait a full memory round trip.
-  float yold[NI][MI][16];
-#pragma unroll
-  for (int ni = 0; ni < NI; ++ni) {
-    const int col = n0 + wn * WN + ni * 32 + (lane & 31);
-    const float bias = (DENSE && b2) ? b2[col] : 0.f;
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = wm * 64 + mi * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-        if (DENSE)
-          yold[ni][mi][r] = bias;
-        else
-          yold[ni][mi][r] = m < rows ? y[(r0 + m) * (int64_t)d + col] : 0.f;
-      }
-  }
-#pragma unroll
-  for (int ni = 0; ni < NI; ++ni) {
-    const int col = n0 + wn * WN + ni * 32 + (lane & 31);
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = wm * 64 + mi * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-        if (m < rows) y[(r0 + m) * (int64_t)d + col] = yold[ni][mi][r] + acc[mi][ni][r];
-      }
-  }
-}
-
-// Sparse phase 2 over row-major D tiles ([block][128 rows][kp], written by the
-// sparse phase 1).  Four waves side by side (1x4): each wave owns all 128 rows
-// and BN/4 output columns, so per 16-deep K-substep it reads four D fragments
-// with plain 16-byte LDS reads and only BN/128 W2 fragments with the (slower)
-// transposing read.  32-deep K-chunks in a 3-stage ring (72 KB) leave room for
-// two workgroups per CU, which overlap each other's epilogue and barriers.
-template <int BN>
-__global__ __launch_bounds__(256, 2) void mlp_gemm2_rows(const uint16_t* __restrict__ dsrc,
-                                                         const uint16_t* __restrict__ w2,
-                                                         const int32_t* __restrict__ idx, float* __restrict__ y,
-                                                         int64_t n, int d, int h, int k, int kp) {
-  constexpr int BK = 32, NS = 3;
-  constexpr int WN = BN / 4, NI = WN / 32, MI = BM / 32;
-  constexpr int D_ROWB = BK * 2;             // 64-byte D rows (4 chunks)
-  constexpr int W_ROWB = BN * 2;             // W2 tile rows
-  constexpr int D_BYTES = BM * D_ROWB;       // 8 KB
-  constexpr int STAGE = D_BYTES + BK * W_ROWB;
-  constexpr int D_RPI = 1024 / D_ROWB;       // rows per direct load
-  constexpr int W_RPI = 1024 / W_ROWB;
-  constexpr int D_INS = BM / D_RPI / 4;      // direct loads per wave per stage
-  constexpr int W_INS = BK / W_RPI / 4;
-  constexpr int L = D_INS + W_INS;
-
-  __shared__ __align__(16) unsigned char smem[NS * STAGE];
-  // W2 row ids, ring of 8 chunks (chunk c in slot c % 8), filled by 4-byte
-  // direct loads six chunks ahead.
-  __shared__ __align__(16) int sIdx[8][BK];
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const uint32_t smem_lds = lds_addr(smem);
-  const int nb = (int)row_blocks(n), ntn = d / BN;
-  const int u = xcd_unit(blockIdx.x, ntn * nb);
-  if (u >= ntn * nb) return;
-  int b, tile;
-  grouped_tile(u, nb, ntn, kGroupTiles, b, tile);
-  const int n0 = tile * BN;
-  const int64_t r0 = (int64_t)b * BM;
-  const int rows = (int)(n - r0 < BM ? n - r0 : BM);
-  const uint16_t* dblk = dsrc + (int64_t)b * BM * kp;
-  const int32_t* sidx = idx + (int64_t)b * k;
-
-  // D: row (instruction's first row + lane/4), physical chunk lane%4, logical
-  // chunk (lane%4) ^ swz4(row).  W2: row (instruction's first row +
-  // lane/(BN/8)), 32-byte pair ((lane%(BN/8))/2 ^ swzp(row)), half lane%2.
-  const int d_lr = lane >> 2, d_pc = lane & 3;
-  const int w_lr = lane / (W_ROWB / 16), w_pc = lane % (W_ROWB / 16);
-  const uint16_t* dsrc_l[D_INS];
-#pragma unroll
-  for (int i = 0; i < D_INS; ++i) {
-    const int r = (wave * D_INS + i) * D_RPI + d_lr;
-    dsrc_l[i] = dblk + (int64_t)r * kp + ((d_pc ^ swz4(r)) << 3);
-  }
-  int w_row[W_INS], w_off[W_INS];
-#pragma unroll
-  for (int i = 0; i < W_INS; ++i) {
-    const int r = (wave * W_INS + i) * W_RPI + w_lr;
-    w_row[i] = r;
-    w_off[i] = ((((w_pc >> 1) ^ swzp(r)) << 1) | (w_pc & 1)) * 8;
-  }
-  // Ids of chunk t for this lane's W2 rows.
-  auto load_ids = [&](int t, int (&ids)[W_INS]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < W_INS; ++i) ids[i] = clamp_index(sIdx[t & 7][w_row[i]], h);
-  };
-  // 4-byte direct load of chunk t's 32 ids into ring slot t % 8 (lanes 0..31 of
-  // wave 0; positions past k read id 0 of the block, whose D columns are zero).
-  auto id_dma = [&](int t) __attribute__((always_inline)) {
-    if (wave == 0 && lane < BK) {
-      const int j = t * BK + lane;
-      dma4_at(sidx + (j < k ? j : 0), lds_addr(&sIdx[t & 7][0]));
-    }
-  };
-
-#define G2R_ISSUE(kt_, buf_, ids_)                                                          \
-  {                                                                                         \
-    const uint32_t st_ = smem_lds + (buf_) * STAGE;                                         \
-    _Pragma("unroll") for (int i = 0; i < D_INS; ++i)                                       \
-        dma16_at(dsrc_l[i] + (kt_) * BK, st_ + (wave * D_INS + i) * 1024);                  \
-    _Pragma("unroll") for (int i = 0; i < W_INS; ++i)                                       \
-        dma16_at(w2 + (int64_t)ids_[i] * d + n0 + w_off[i], st_ + D_BYTES + (wave * W_INS + i) * 1024); \
-  }
-
-  f32x16_t acc[MI][NI];
-#pragma unroll
-  for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < NI; ++ni)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
-
-  const int KT = kp / BK;
-  // Prologue: ids of chunks 0..5, then stages 0 and 1.
-  if (wave == 0 && lane < BK) {
-#pragma unroll
-    for (int t = 0; t < 6; ++t)
-      if (t < KT) dma4_at(sidx + (t * BK + lane < k ? t * BK + lane : 0), lds_addr(&sIdx[t][0]));
-  }
-  wait_vmcnt<0>();
-  __syncthreads();
-  int ids_a[W_INS], ids_b[W_INS];
-  load_ids(0, ids_a);
-  G2R_ISSUE(0, 0, ids_a);
-  if (KT > 1) {
-    load_ids(1, ids_a);
-    G2R_ISSUE(1, 1, ids_a);
-  }
-  if (KT > 2) load_ids(2, ids_a);
-
-  const int sw = swz4(lane & 31);
-  for (int kt = 0; kt < KT; ++kt) {
-    // Outstanding loads of this wave, newest first: stage kt+1 (L) and, on wave
-    // 0, the id load of chunk kt+5 if the previous iteration issued one.
-    // Everything older (stage kt) must be complete.
-    if (kt + 1 < KT) {
-      if (wave == 0 && kt >= 1 && kt + 5 < KT)
-        wait_vmcnt<L + 1>();
-      else
-        wait_vmcnt<L>();
-    } else {
-      wait_vmcnt<0>();
-    }
-    barrier();
-    if (kt + 6 < KT) id_dma(kt + 6);
-    if (kt + 2 < KT) G2R_ISSUE(kt + 2, (kt + 2) % NS, ids_a);
-    if (kt + 3 < KT) load_ids(kt + 3, ids_b);
-    const unsigned char* st = smem + (kt % NS) * STAGE;
-#pragma unroll
-    for (int s = 0; s < BK / 16; ++s) {
-      const int coff = (((2 * s + (lane >> 5)) ^ sw) << 4);
-      bf16x8_t af[MI], bfr[NI];
-#pragma unroll
-      for (int ni = 0; ni < NI; ++ni) bfr[ni] = tr_operand_swz_nat(st + D_BYTES, W_ROWB, s * 16, wave * WN + ni * 32, lane);
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi) af[mi] = *(const bf16x8_t*)(st + (mi * 32 + (lane & 31)) * D_ROWB + coff);
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = mfma32(af[mi], bfr[ni], acc[mi][ni]);
-    }
-#pragma unroll
-    for (int i = 0; i < W_INS; ++i) ids_a[i] = ids_b[i];
-  }
-#undef G2R_ISSUE
-
-  // y += acc, one 32-column slice at a time: load all of its old values, then
-  // store all of its sums (row offsets depend on d, so the compiler cannot
-  // overlap one read-modify-write with the next by itself).  Row bases are
-  // wave-uniform; a lane adds one 32-bit offset (its 4-row half and column).
-  const int lane_off = (lane >> 5) * 4 * d + wave * WN + (lane & 31);
-  const int mhalf = (lane >> 5) * 4;
-#pragma unroll
-  for (int ni = 0; ni < NI; ++ni) {
-    float yold[MI][16];
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int R = mi * 32 + (r >> 2) * 8 + (r & 3);
-        const float* yrow = y + (r0 + R) * (int64_t)d + n0 + ni * 32;
-        yold[mi][r] = R + mhalf < rows ? yrow[lane_off] : 0.f;
-      }
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int R = mi * 32 + (r >> 2) * 8 + (r & 3);
-        float* yrow = y + (r0 + R) * (int64_t)d + n0 + ni * 32;
-        if (R + mhalf < rows) yrow[lane_off] = yold[mi][r] + acc[mi][ni][r];
-      }
-  }
-}
-
-}  // namespace
 
 hipError_t launch_mlp_gemm1(bool dense, const uint16_t* x, const uint16_t* w1t, const float* b1,
                             const int32_t* idx, uint16_t* a_cache, uint16_t* dbuf, uint16_t* a_packed,

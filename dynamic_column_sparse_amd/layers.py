@@ -104,3 +104,13 @@ class AttnDelta:
             self.refresh_rest(q, k, v, stream=stream)
         else:
             self.sparse(q, k, v, stream=stream)
+
+
+def sparse_step(mlp: MLPDelta, att: AttnDelta, x, q, k, v, stream=None):
+    """One sparse step of a block whose attention and MLP deltas are independent
+    (both read the block's input): the MLP's top-k over its dense-step scores,
+    then both deltas through chipmunk_sparse_step.  Same results as
+    ``mlp.step(x, False)`` followed by ``att.step(q, k, v, False)``."""
+    mlp.identify(stream)
+    lib.chipmunk_sparse_step(mlp.layer, x, mlp.idx, mlp.k, mlp.y, None, mlp.ws, att.layer, q, k, v, att.idx,
+                             att.kk, att.o, stream=stream)

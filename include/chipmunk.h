@@ -190,6 +190,23 @@ int chipmunk_sparse_attn_delta(const chipmunk_attn* layer, const uint16_t* q, co
                                const uint16_t* v, const int32_t* idx, int32_t kk, int mode, float* o,
                                void* stream);
 
+/* Both sparse deltas of one step in two launches: chipmunk_sparse_mlp_delta on
+ * `mlp` and chipmunk_sparse_attn_delta(mode = CHIPMUNK_ATTN_SPARSE) on `attn`,
+ * with the arguments of those two calls and the same results, bit for bit.
+ * The MLP's sparse phase 1 runs first; one kernel then holds the MLP's phase-2
+ * tiles and the attention units side by side (the method computes each delta
+ * separately, see the two calls above; sharing one grid is a scheduling choice
+ * that keeps the chip full at the tails of both).  For deltas that do not
+ * depend on each other, e.g. a block that applies attention and MLP to the
+ * same input: no buffer written by one delta (y, a_cache, a_new_packed, ws;
+ * o) may overlap a buffer that the other reads or writes, and the call fails
+ * with CHIPMUNK_E_SHAPE when the ranges it can see overlap.  k = 0 skips the
+ * MLP part; kk = 0 writes o = num / den. */
+int chipmunk_sparse_step(const chipmunk_mlp* mlp, const uint16_t* x, const int32_t* mlp_idx, int32_t k,
+                         float* y, uint16_t* a_new_packed, void* ws, size_t ws_bytes,
+                         const chipmunk_attn* attn, const uint16_t* q, const uint16_t* kx, const uint16_t* v,
+                         const int32_t* attn_idx, int32_t kk, float* o, void* stream);
+
 /* Cache writeback (the separate form of the fused writeback above): copy the
  * packed new activations a_new_packed [nb][k][128] into a_cache[b][idx[b][p]]
  * for every block b and position p.  Contiguous 256-byte segments. */

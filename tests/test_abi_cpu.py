@@ -24,10 +24,10 @@ def _declared():
     return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]*?\b(chipmunk_\w+)\s*\(", text, re.M)))
 
 
-def test_header_declares_the_five_entry_points():
+def test_header_declares_the_entry_points():
     decl = _declared()
     for name in ("chipmunk_dense_step", "chipmunk_identify_topk", "chipmunk_sparse_mlp_delta",
-                 "chipmunk_sparse_attn_delta", "chipmunk_cache_writeback"):
+                 "chipmunk_sparse_attn_delta", "chipmunk_cache_writeback", "chipmunk_sparse_step"):
         assert name in decl
 
 
@@ -134,6 +134,31 @@ def test_topk_and_attn_checks(L):
     assert _code(L, w, _mlp(L), FAKE, FAKE, 700, stream=0) == 2
     assert _code(L, w, _mlp(L), None, FAKE, 10, stream=0) == 1
     assert _code(L, w, _mlp(L), FAKE, FAKE, 0, stream=0) == 0
+
+
+def test_sparse_step_checks(L):
+    # Every buffer at its own 4 GiB-spaced fake address, so only the pairs a
+    # case makes overlap do; each case fails validation before any launch.
+    base = {name: FAKE + i * (1 << 32) for i, name in enumerate(
+        ("w1t", "w2", "a_cache", "score", "x", "midx", "y", "ws", "m", "num", "den", "ascore", "q", "k", "v",
+         "aidx", "o"))}
+
+    def call(k=200, kk=100, **over):
+        a = {**base, **over}
+        lay = L.mlp_layer(300, 256, 640, a["w1t"], a["w2"], a["a_cache"], a["score"])
+        att = L.attn_layer(300, 2, a["m"], a["num"], a["den"], a["ascore"])
+        return _code(L, L.chipmunk_sparse_step, lay, a["x"], a["midx"], k, a["y"], None, a["ws"], att, a["q"],
+                     a["k"], a["v"], a["aidx"], kk, a["o"], stream=0, ws_bytes=1 << 30)
+
+    assert call(k=641) == 2                       # MLP argument checks apply
+    assert call(x=None) == 1
+    assert call(kk=301) == 2                      # attention argument checks apply
+    assert call(o=None) == 1
+    assert call(o=base["y"]) == 2                 # o is y
+    assert "overlaps" in L.chipmunk_last_error()
+    assert call(q=base["ws"] + 4096) == 2         # the MLP's workspace inside q
+    assert call(o=base["x"] + 16) == 2            # o over the MLP's input
+    assert call(num=base["a_cache"]) == 2         # the attention cache over the MLP cache
 
 
 def test_timer_api_without_launches(L):
