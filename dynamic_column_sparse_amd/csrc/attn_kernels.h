@@ -3,13 +3,15 @@
 //
 // Every kernel runs one workgroup (4 waves) per (head, 128-query block); wave w
 // owns queries 32w .. 32w+31 of the block and keeps their Q rows in registers
-// for the whole key loop.  Keys stream through double-buffered LDS tiles of 64
-// (K rows for the scores, V rows for the numerator).  Scores are computed
-// transposed, s^T = K_tile Q^T, so each lane holds one query and 16 keys: the
+// for the whole key loop.  Keys stream in 32-row chunks through a ring of LDS
+// stages filled by direct global->LDS loads.  Scores are computed transposed,
+// s^T = K_chunk Q^T, so each lane holds one query and 16 keys: the
 // exponentials then feed P V directly as the left operand, with V read through
 // the transposing LDS read in the same reduction order as the accumulator rows.
+// Exponentials are exp(scale s - m) = 2^(s * scale*log2e - m*log2e): one FMA
+// and one exp2 per element.
 //
-//   attn_stats  (refresh pass 1): online row max m and sum l over all keys.
+//   attn_stats  (refresh pass 1): row max m and row sum l over all keys.
 //   attn_dense  (refresh pass 2): p = exp(s - m), num = p V, den = sum p,
 //               o = num / den, and the key-mass score sum_i p_ij / l_i per key,
 //               reduced over the block's queries inside the workgroup.
@@ -29,11 +31,6 @@
 namespace chipmunk {
 namespace {
 
-constexpr int KT = 64;          // keys per tile
-constexpr int LDK = 128 + 8;    // 272-byte rows: 16-byte reads conflict-free
-constexpr int LDV = 128 + 16;   // 288-byte rows for the transposing reads
-constexpr int CH = KT * 128 / 8 / 256;  // 16-byte chunks per thread per tile (4)
-
 // Block -> (head, query block): all blocks of a head land on one XCD (workgroups
 // are dispatched to the 8 XCDs round-robin by linear id) when heads % 8 == 0.
 __device__ __forceinline__ void head_block(int heads, int nb, int& hh, int& b, int L) {
@@ -51,225 +48,442 @@ struct QFrag {
   bf16x8_t f[8];
 };
 
-__device__ __forceinline__ void load_q(QFrag& q, const uint16_t* qh, int64_t qrow, bool ok, int lane) {
-#pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    if (ok)
-      q.f[s] = *(const bf16x8_t*)(qh + qrow * 128 + s * 16 + (lane >> 5) * 8);
-    else
-      q.f[s] = __builtin_bit_cast(bf16x8_t, make_uint4(0, 0, 0, 0));
-  }
-}
-
-// s^T for 32 keys (tile rows kb .. kb+31) against the wave's 32 queries.
-__device__ __forceinline__ f32x16_t scores_t(const uint16_t* sk, int kb, const QFrag& q, int lane) {
-  f32x16_t acc;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-#pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    const bf16x8_t kf = *(const bf16x8_t*)(sk + (kb + (lane & 31)) * LDK + s * 16 + (lane >> 5) * 8);
-    acc = mfma32(kf, q.f[s], acc);
-  }
-  return acc;
-}
-
 // Tile key index of accumulator element r in lane `lane`, relative to the subtile.
 __device__ __forceinline__ int acc_key(int r, int lane) { return (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3); }
 
-__global__ __launch_bounds__(256, 1) void attn_stats(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-                                                     float* __restrict__ m_out, float* __restrict__ l_out, int64_t n,
-                                                     int heads, float scale) {
-  __shared__ __align__(16) uint16_t sK[2][KT][LDK];
-  const int nb = (int)row_blocks(n);
-  int hh, b;
-  head_block(heads, nb, hh, b, blockIdx.x);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t r0 = (int64_t)b * kRowBlock;
-  const int rows = (int)(n - r0 < kRowBlock ? n - r0 : kRowBlock);
-  const uint16_t* qh = q + (int64_t)hh * n * 128;
-  const uint16_t* kh = k + (int64_t)hh * n * 128;
-  const int qi = wave * 32 + (lane & 31);
-  QFrag qf;
-  load_q(qf, qh, r0 + qi, qi < rows, lane);
+// Geometry shared by the dense passes: 32-key chunks, K rows store 16-byte
+// chunk c at c ^ (row % 16) (plain 16-byte operand reads, no bank conflicts),
+// V rows store 32-byte column pairs at pair ^ swzp(row) for the transposing
+// reads.  Direct-load instruction i of a wave covers rows (wave*2+i)*4 .. +3
+// of a chunk; lane -> row lane/16, physical 16-byte chunk lane%16.
+constexpr int kSK = 32;                       // keys per chunk
+constexpr int kTile = kSK * 256;              // 8 KB per tensor per chunk
+constexpr int kIns = kTile / 1024 / 4;        // direct loads per wave per tensor per chunk (2)
 
-  uint4 rk[CH];
-  const uint4 z4 = make_uint4(0, 0, 0, 0);
-#define ST_LOAD(t_)                                                                           \
-  _Pragma("unroll") for (int i = 0; i < CH; ++i) {                                            \
-    const int c = tid + 256 * i, row = c >> 4, col = (c & 15) * 8;                            \
-    const int64_t key = (int64_t)(t_) * KT + row;                                             \
-    if (key < n) rk[i] = *(const uint4*)(kh + key * 128 + col); else rk[i] = z4;              \
+struct ChunkGeom {
+  int krow[kIns], koff[kIns], voff[kIns];
+  __device__ __forceinline__ explicit ChunkGeom(int wave, int lane) {
+    const int pc = lane & 15;
+#pragma unroll
+    for (int i = 0; i < kIns; ++i) {
+      const int r = (wave * kIns + i) * 4 + (lane >> 4);
+      krow[i] = r;
+      koff[i] = (pc ^ (r & 15)) * 8;
+      voff[i] = ((((pc >> 1) ^ swzp(r)) << 1) | (pc & 1)) * 8;
+    }
   }
-#define ST_STORE(buf_)                                                                        \
-  _Pragma("unroll") for (int i = 0; i < CH; ++i) {                                            \
-    const int c = tid + 256 * i;                                                              \
-    *(uint4*)&sK[buf_][c >> 4][(c & 15) * 8] = rk[i];                                         \
-  }
+};
 
-  float mr = -INFINITY, lr = 0.f;
-  const int ntiles = (int)((n + KT - 1) / KT);
-  ST_LOAD(0);
-  ST_STORE(0);
-  __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < ntiles) {
-      ST_LOAD(t + 1);
-    }
+// s^T = K_chunk Q^T for the chunk stored at `st`: lane holds query lane%32 and
+// the 16 keys acc_key(r, lane).
+__device__ __forceinline__ f32x16_t chunk_scores(const unsigned char* st, const QFrag& qf, int lane) {
+  const int ksw = lane & 15;   // K row (lane % 32) % 16
+  f32x16_t sc;
 #pragma unroll
-    for (int kt2 = 0; kt2 < 2; ++kt2) {
-      const f32x16_t sacc = scores_t(&sK[buf][0][0], kt2 * 32, qf, lane);
-      float sc[16], tmax = -INFINITY;
+  for (int r = 0; r < 16; ++r) sc[r] = 0.f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t key = (int64_t)t * KT + kt2 * 32 + acc_key(r, lane);
-        sc[r] = key < n ? sacc[r] * scale : -INFINITY;
-        tmax = fmaxf(tmax, sc[r]);
-      }
-      if (tmax > -INFINITY) {
-        const float mnew = fmaxf(mr, tmax);
-        float sum = 0.f;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sum += __expf(sc[r] - mnew);
-        lr = lr * __expf(mr - mnew) + sum;
-        mr = mnew;
-      }
-    }
-    if (t + 1 < ntiles) {
-      ST_STORE(buf ^ 1);
-    }
-    __syncthreads();
+  for (int s2 = 0; s2 < 8; ++s2) {
+    const bf16x8_t kf = *(const bf16x8_t*)(st + (lane & 31) * 256 + (((2 * s2 + (lane >> 5)) ^ ksw) << 4));
+    sc = mfma32(kf, qf.f[s2], sc);
   }
-#undef ST_LOAD
-#undef ST_STORE
-  const float m2 = __shfl_xor(mr, 32), l2 = __shfl_xor(lr, 32);
-  const float M = fmaxf(mr, m2);
-  const float L = (mr > -INFINITY ? lr * __expf(mr - M) : 0.f) + (m2 > -INFINITY ? l2 * __expf(m2 - M) : 0.f);
-  if (lane < 32 && qi < rows) {
-    m_out[(int64_t)hh * n + r0 + qi] = M;
-    l_out[(int64_t)hh * n + r0 + qi] = L;
+  return sc;
+}
+
+// Q fragments of query row `row` (a valid row: callers clamp), optionally with
+// every sign bit flipped (= the fragments of -Q).
+__device__ __forceinline__ void load_q_row(QFrag& qf, const uint16_t* qh, int64_t row, uint32_t flip, int lane) {
+#pragma unroll
+  for (int s2 = 0; s2 < 8; ++s2) {
+    uint4 u = *(const uint4*)(qh + row * 128 + s2 * 16 + (lane >> 5) * 8);
+    u.x ^= flip;
+    u.y ^= flip;
+    u.z ^= flip;
+    u.w ^= flip;
+    qf.f[s2] = __builtin_bit_cast(bf16x8_t, u);
   }
 }
 
-__global__ __launch_bounds__(256, 1) void attn_dense(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+// Refresh pass 1 for one (head, query block): m_i = max_j scale*s_ij and
+// l_i = sum_j exp(scale*s_ij - m_i) over all n keys.  Keys stream through a
+// 4-stage ring of 32-key chunks (32 KB; four workgroups per CU, so a
+// 24-head, 34-block layer runs in one round).  Full chunks load from a scalar
+// base and fixed lane offsets; the chunks past the last full one clamp their
+// rows to row n-1 (every load stays unconditional, so the per-wave load counts
+// behind the waits are exact) and mask them.  For a negative scale the kernel
+// runs on -Q with |scale|, so the running maximum is always a maximum of raw
+// scores: m = max_j(s'_ij) * |scale| exactly.
+constexpr int kStatsStages = 4;
+
+__global__ __launch_bounds__(256, 4) void attn_stats(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                                                     float* __restrict__ m_out, float* __restrict__ l_out, int64_t n,
+                                                     int heads, float scale) {
+  constexpr int NS = kStatsStages, L = kIns;
+  __shared__ __align__(16) unsigned char smem[NS * kTile];
+  const int nb = (int)row_blocks(n);
+  int hh, b;
+  head_block(heads, nb, hh, b, blockIdx.x);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t smem_lds = lds_addr(smem);
+  const int64_t r0 = (int64_t)b * kRowBlock;
+  const int rows = (int)(n - r0 < kRowBlock ? n - r0 : kRowBlock);
+  const int64_t hoff = (int64_t)hh * n;
+  const uint16_t* kh = k + hoff * 128;
+  const int nn = (int)n;
+  const int qi = wave * 32 + (lane & 31);
+  const int qc = qi < rows ? qi : rows - 1;
+  const float as = fabsf(scale), sl2 = as * 1.4426950408889634f;
+  const ChunkGeom geo(wave, lane);
+  const int KT = (nn + kSK - 1) / kSK, KF = nn / kSK;   // chunks, full chunks
+  uint32_t kofs[kIns];
+#pragma unroll
+  for (int i = 0; i < kIns; ++i) kofs[i] = geo.krow[i] * 256 + geo.koff[i] * 2;
+
+  auto issue = [&](int t) __attribute__((always_inline)) {
+    const uint32_t st = smem_lds + (t % NS) * kTile;
+#pragma unroll
+    for (int i = 0; i < kIns; ++i) {
+      const int key = t * kSK + geo.krow[i];
+      dma16_at(kh + (int64_t)(key < nn ? key : nn - 1) * 128 + geo.koff[i], st + (wave * kIns + i) * 1024);
+    }
+  };
+  auto issue_full = [&](int t) __attribute__((always_inline)) {
+    const uint32_t st = smem_lds + (t % NS) * kTile;
+    const unsigned char* base = (const unsigned char*)kh + (int64_t)t * kTile;
+#pragma unroll
+    for (int i = 0; i < kIns; ++i) dma16_sa(base, kofs[i], st + (wave * kIns + i) * 1024);
+  };
+
+  // Q goes out before the stages: its first use (chunk 0's scores, before the
+  // loop) then waits for it once.
+  QFrag qf;
+  load_q_row(qf, q + hoff * 128, r0 + qc, scale < 0.f ? 0x80008000u : 0u, lane);
+#pragma unroll
+  for (int t = 0; t < NS - 1; ++t)
+    if (t < KT) issue(t);
+  {
+    const int ahead = (KT - 1) < (NS - 2) ? (KT - 1) : (NS - 2);
+    wait_vmcnt_upto<(NS - 2) * L>(ahead * L);
+    barrier();
+  }
+  f32x16_t sa = chunk_scores(smem, qf, lane), sb;
+  float mr = -INFINITY, lr = 0.f;
+  // Iteration t issues chunk t+1's score products into `nxt`, then folds chunk
+  // t (in `cur`) into the running (m, l).  Steady iterations issue a full
+  // chunk (t + NS - 1 < KF); their own chunk is full too.
+  auto body = [&](int t, f32x16_t& cur, f32x16_t& nxt, auto STEADY) __attribute__((always_inline)) {
+    constexpr bool steady = decltype(STEADY)::value;
+    if (steady || t + 1 < KT) {
+      // Stage t+1 must be complete; newer than it are the stages issued up to
+      // min(t + NS - 2, KT - 1).
+      if (steady) {
+        wait_vmcnt<(NS - 3) * L>();
+      } else {
+        const int last = (t + NS - 2) < (KT - 1) ? (t + NS - 2) : (KT - 1);
+        wait_vmcnt_upto<(NS - 3) * L>((last - t - 1) * L);
+      }
+      barrier();
+      // Stage t+NS-1 reuses the slot of chunk t-1, read at iteration t-2.
+      if (steady)
+        issue_full(t + NS - 1);
+      else if (t + NS - 1 < KT)
+        issue(t + NS - 1);
+      nxt = chunk_scores(smem + ((t + 1) % NS) * kTile, qf, lane);
+    }
+    const bool full = steady || t * kSK + kSK <= nn;
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const bool ok = full || t * kSK + acc_key(r, lane) < nn;
+      mloc = ok ? fmaxf(mloc, cur[r]) : mloc;
+    }
+    const float mnew = fmaxf(mr, mloc);
+    const float ml2 = mnew * sl2;
+    float sum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const bool ok = full || t * kSK + acc_key(r, lane) < nn;
+      const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(cur[r], sl2, -ml2));
+      sum += ok ? e : 0.f;
+    }
+    // A lane whose keys so far are all masked (only when n < 32) keeps (-inf, 0).
+    const float resc = mr > -INFINITY ? __builtin_amdgcn_exp2f(__builtin_fmaf(mr, sl2, -ml2)) : 0.f;
+    if (steady || mnew > -INFINITY) {
+      lr = __builtin_fmaf(lr, resc, sum);
+      mr = mnew;
+    }
+  };
+  int t = 0;
+  for (; t + NS < KF; t += 2) {
+    body(t, sa, sb, std::true_type{});
+    body(t + 1, sb, sa, std::true_type{});
+  }
+  while (t < KT) {
+    body(t, sa, sb, std::false_type{});
+    if (++t >= KT) break;
+    body(t, sb, sa, std::false_type{});
+    ++t;
+  }
+
+  // Lanes l and l^32 hold the same query (different keys).
+  const float m2 = __shfl_xor(mr, 32), l2 = __shfl_xor(lr, 32);
+  const float M = fmaxf(mr, m2), M2 = M * sl2;
+  const float la = mr > -INFINITY ? lr * __builtin_amdgcn_exp2f(__builtin_fmaf(mr, sl2, -M2)) : 0.f;
+  const float lb = m2 > -INFINITY ? l2 * __builtin_amdgcn_exp2f(__builtin_fmaf(m2, sl2, -M2)) : 0.f;
+  if (lane < 32 && qi < rows) {
+    m_out[hoff + r0 + qi] = M * as;
+    l_out[hoff + r0 + qi] = la + lb;
+  }
+}
+
+// The p tile of one wave for the score products: [32 queries][32 keys] fp16,
+// 64-byte rows, 8-byte unit u of row r stored at unit u ^ ((r / 4) % 8): the 32
+// rows written at one unit then cover all 64 banks once, and the 4 rows x 4
+// units of one transposing read are distinct banks too.
+__device__ __forceinline__ int p_unit(int u, int r) { return u ^ ((r >> 2) & 7); }
+
+// Reads the p tile as the right operand of a 32x32x16 product with the QUERIES
+// as the reduction index: lane l gets key l%32 and queries k0 + (l/32)*8 .. +7
+// in order.
+__device__ __forceinline__ f16x8_t p_operand(const unsigned char* tile, int k0, int lane) {
+  const int G = lane >> 4, i = lane & 15;
+  const int u = (G & 1) * 4 + (i & 3);          // 8-byte unit of keys 4u .. 4u+3
+  const int kr = k0 + (G >> 1) * 8 + (i >> 2);  // query row; the second read is 4 rows on
+  i16x4_t lo = lds_read_tr16((const uint16_t*)(tile + kr * 64 + (p_unit(u, kr) << 3)));
+  i16x4_t hi = lds_read_tr16((const uint16_t*)(tile + (kr + 4) * 64 + (p_unit(u, kr + 4) << 3)));
+  typedef short i16x8_t __attribute__((ext_vector_type(8)));
+  i16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(f16x8_t, v);
+}
+
+// Refresh pass 2 for one (head, query block), given pass 1's m and l: with
+// p_ij = exp(scale*s_ij - m_i), num = p V (fp32 accumulate of bf16 p and V),
+// o = num / l, and the key-mass score score[h][b][j] = sum over the block's
+// queries of p_ij / l_i.  den keeps pass 1's l, which is sum_j p_ij.  K and V
+// move through a 4-stage ring of 32-key chunks (64 KB, two workgroups per CU);
+// the score products of chunk t+1 are issued before the exponentials and value
+// products of chunk t.  The score is a matrix product too: each wave writes
+// its p tile to LDS in fp16, reads it back transposed (queries as the
+// reduction index) and multiplies it by the row of its queries' 2^15/l in fp16
+// (1 <= l <= n keeps those normal up to n = 2^29; the 2^-15 is applied after
+// the fp32 sum, exactly).  fp16 rather than bf16 operands: the sums then carry
+// about 2^-12 relative error per term, small enough for the index sets even
+// when a block has few valid queries.  The four waves' partial sums meet in LDS and are stored for four chunks (128 keys) at a time
+// by wave 3.  Those stores are not counted in the waits (which then wait for a
+// little more than needed, never less).
+constexpr int kDenseStages = 4;
+constexpr int kScoreGroup = 4;   // chunks per score store
+
+__global__ __launch_bounds__(256, 2) void attn_dense(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                                      const uint16_t* __restrict__ v, const float* __restrict__ m,
                                                      float* __restrict__ den, float* __restrict__ num,
                                                      float* __restrict__ o, float* __restrict__ score, int64_t n,
                                                      int heads, float scale) {
-  __shared__ __align__(16) uint16_t sK[2][KT][LDK];
-  __shared__ __align__(16) uint16_t sV[2][KT][LDV];
-  __shared__ float sScore[4][KT];
-  __shared__ float sDen[kRowBlock];
+  constexpr int NS = kDenseStages, G = kScoreGroup;
+  constexpr int STAGE = 2 * kTile;
+  constexpr int L = 2 * kIns;
+  constexpr int PIECES = kRowBlock * 128 / 4 / 256;   // 16-byte output pieces per thread (16)
+  __shared__ __align__(16) unsigned char smem[NS * STAGE];
+  __shared__ __align__(16) unsigned char sP[4][32 * 64];
+  __shared__ float sSc[2][G][4][kSK];
+  __shared__ float sInv[kRowBlock];
+  __shared__ float sL[kRowBlock];
   const int nb = (int)row_blocks(n);
   int hh, b;
   head_block(heads, nb, hh, b, blockIdx.x);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t smem_lds = lds_addr(smem);
   const int64_t r0 = (int64_t)b * kRowBlock;
   const int rows = (int)(n - r0 < kRowBlock ? n - r0 : kRowBlock);
   const int64_t hoff = (int64_t)hh * n;
-  const uint16_t* qh = q + hoff * 128;
   const uint16_t* kh = k + hoff * 128;
   const uint16_t* vh = v + hoff * 128;
+  float* srow = score + ((int64_t)hh * nb + b) * n;
+  const int nn = (int)n;
   const int qi = wave * 32 + (lane & 31);
   const bool qok = qi < rows;
+  const int qc = qok ? qi : rows - 1;
+  const ChunkGeom geo(wave, lane);
+  const int KT = (nn + kSK - 1) / kSK, KF = nn / kSK;
+  uint32_t kofs[kIns], vofs[kIns];
+#pragma unroll
+  for (int i = 0; i < kIns; ++i) {
+    kofs[i] = geo.krow[i] * 256 + geo.koff[i] * 2;
+    vofs[i] = geo.krow[i] * 256 + geo.voff[i] * 2;
+  }
+
+  auto issue = [&](int t) __attribute__((always_inline)) {
+    const uint32_t st = smem_lds + (t % NS) * STAGE;
+    int key[kIns];
+#pragma unroll
+    for (int i = 0; i < kIns; ++i) {
+      const int j = t * kSK + geo.krow[i];
+      key[i] = j < nn ? j : nn - 1;
+    }
+#pragma unroll
+    for (int i = 0; i < kIns; ++i)
+      dma16_at(kh + (int64_t)key[i] * 128 + geo.koff[i], st + (wave * kIns + i) * 1024);
+#pragma unroll
+    for (int i = 0; i < kIns; ++i)
+      dma16_at(vh + (int64_t)key[i] * 128 + geo.voff[i], st + kTile + (wave * kIns + i) * 1024);
+  };
+  auto issue_full = [&](int t) __attribute__((always_inline)) {
+    const uint32_t st = smem_lds + (t % NS) * STAGE;
+    const unsigned char* kb = (const unsigned char*)kh + (int64_t)t * kTile;
+    const unsigned char* vb = (const unsigned char*)vh + (int64_t)t * kTile;
+#pragma unroll
+    for (int i = 0; i < kIns; ++i) dma16_sa(kb, kofs[i], st + (wave * kIns + i) * 1024);
+#pragma unroll
+    for (int i = 0; i < kIns; ++i) dma16_sa(vb, vofs[i], st + kTile + (wave * kIns + i) * 1024);
+  };
+  // Wave 3 stores the block's scores of chunks g*G .. g*G+G-1 (two keys per lane).
+  auto store_scores = [&](int g) __attribute__((always_inline)) {
+    if (wave == 3) {
+      const int c = lane >> 4, kc = (lane & 15) * 2;
+      const int j = (g * G + c) * kSK + kc;
+      const float (*ps)[kSK] = sSc[g & 1][c];
+      const float s0 = ps[0][kc] + ps[1][kc] + ps[2][kc] + ps[3][kc];
+      const float s1 = ps[0][kc + 1] + ps[1][kc + 1] + ps[2][kc + 1] + ps[3][kc + 1];
+      if (j < nn) srow[j] = s0;
+      if (j + 1 < nn) srow[j + 1] = s1;
+    }
+  };
+
   QFrag qf;
-  load_q(qf, qh, r0 + qi, qok, lane);
-  const float mrow = qok ? m[hoff + r0 + qi] : 0.f;
-  // den holds pass 1's row sums on entry; they normalise the key-mass scores.
-  const float invl = qok ? 1.f / den[hoff + r0 + qi] : 0.f;
-
-  uint4 rk[CH], rv[CH];
-  const uint4 z4 = make_uint4(0, 0, 0, 0);
-#define DN_LOAD(t_)                                                                           \
-  _Pragma("unroll") for (int i = 0; i < CH; ++i) {                                            \
-    const int c = tid + 256 * i, row = c >> 4, col = (c & 15) * 8;                            \
-    const int64_t key = (int64_t)(t_) * KT + row;                                             \
-    if (key < n) {                                                                            \
-      rk[i] = *(const uint4*)(kh + key * 128 + col);                                          \
-      rv[i] = *(const uint4*)(vh + key * 128 + col);                                          \
-    } else {                                                                                  \
-      rk[i] = z4;                                                                             \
-      rv[i] = z4;                                                                             \
-    }                                                                                         \
+  load_q_row(qf, q + hoff * 128, r0 + qc, 0u, lane);
+  const float mrow = m[hoff + r0 + qc];
+  const float lrow = den[hoff + r0 + qc];   // pass 1's l
+#pragma unroll
+  for (int t = 0; t < NS - 1; ++t)
+    if (t < KT) issue(t);
+  // Rows past the block end weigh nothing in the scores.
+  if (lane < 32) {
+    sInv[qi] = qok ? 1.f / lrow : 0.f;
+    sL[qi] = lrow;
   }
-#define KV_STORE(buf_)                                                                        \
-  _Pragma("unroll") for (int i = 0; i < CH; ++i) {                                            \
-    const int c = tid + 256 * i;                                                              \
-    *(uint4*)&sK[buf_][c >> 4][(c & 15) * 8] = rk[i];                                         \
-    *(uint4*)&sV[buf_][c >> 4][(c & 15) * 8] = rv[i];                                         \
+  {
+    const int ahead = (KT - 1) < (NS - 2) ? (KT - 1) : (NS - 2);
+    wait_vmcnt_upto<(NS - 2) * L>(ahead * L);
+    barrier();
   }
-
+  // Left operand of the score products: every row holds 2^15/l of the wave's
+  // queries, in the order p_operand delivers them.
+  f16x8_t wq[2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const float* w = sInv + wave * 32 + kb * 16 + (lane >> 5) * 8;
+    constexpr float S = 32768.f;
+    const uint4 pk = make_uint4(pack2h(w[0] * S, w[1] * S), pack2h(w[2] * S, w[3] * S),
+                                pack2h(w[4] * S, w[5] * S), pack2h(w[6] * S, w[7] * S));
+    wq[kb] = __builtin_bit_cast(f16x8_t, pk);
+  }
+  const float sl2 = scale * 1.4426950408889634f, ml2 = mrow * 1.4426950408889634f;
   f32x16_t acc[4];
 #pragma unroll
   for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[ni][r] = 0.f;
-  float dpart = 0.f;
-  const int ntiles = (int)((n + KT - 1) / KT);
-  DN_LOAD(0);
-  KV_STORE(0);
-  __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < ntiles) {
-      DN_LOAD(t + 1);
-    }
-#pragma unroll
-    for (int kt2 = 0; kt2 < 2; ++kt2) {
-      const f32x16_t sacc = scores_t(&sK[buf][0][0], kt2 * 32, qf, lane);
-      float p[16], w[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t key = (int64_t)t * KT + kt2 * 32 + acc_key(r, lane);
-        p[r] = key < n ? __expf(sacc[r] * scale - mrow) : 0.f;
-        dpart += p[r];
-        w[r] = p[r] * invl;
+  unsigned char* pw = sP[wave];
+  const int pq = lane & 31, ph = lane >> 5;
+  f32x16_t sa = chunk_scores(smem, qf, lane), sb;
+
+  auto body = [&](int t, f32x16_t& cur, f32x16_t& nxt, auto STEADY) __attribute__((always_inline)) {
+    constexpr bool steady = decltype(STEADY)::value;
+    if (steady || t + 1 < KT) {
+      if (steady) {
+        wait_vmcnt<(NS - 3) * L>();
+      } else {
+        const int last = (t + NS - 2) < (KT - 1) ? (t + NS - 2) : (KT - 1);
+        wait_vmcnt_upto<(NS - 3) * L>((last - t - 1) * L);
       }
-      const float tot = halfwave_transpose_sum16(w, lane);
-      if ((lane & 1) == 0) sScore[wave][kt2 * 32 + acc_key((lane >> 1) & 15, lane)] = tot;
+      barrier();
+      // Every wave's partial scores of chunks t-G .. t-1 are in LDS.
+      if (t % G == 0 && t >= G) store_scores(t / G - 1);
+      // Stage t+NS-1 reuses the slot of chunk t-1: its keys were read at
+      // iteration t-2 and its values at t-1, before this barrier.
+      if (steady)
+        issue_full(t + NS - 1);
+      else if (t + NS - 1 < KT)
+        issue(t + NS - 1);
+      nxt = chunk_scores(smem + ((t + 1) % NS) * STAGE, qf, lane);
+    }
+    const unsigned char* st = smem + (t % NS) * STAGE;
+    const bool full = steady || t * kSK + kSK <= nn;
+    float p[16];
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        bf16x8_t pa;
-        uint4 pk = make_uint4(pack2(p[hf * 8 + 0], p[hf * 8 + 1]), pack2(p[hf * 8 + 2], p[hf * 8 + 3]),
-                              pack2(p[hf * 8 + 4], p[hf * 8 + 5]), pack2(p[hf * 8 + 6], p[hf * 8 + 7]));
-        pa = __builtin_bit_cast(bf16x8_t, pk);
+    for (int r = 0; r < 16; ++r) {
+      const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(cur[r], sl2, -ml2));
+      p[r] = (full || t * kSK + acc_key(r, lane) < nn) ? e : 0.f;
+    }
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni) {
-          const bf16x8_t vb = tr_operand(&sV[buf][0][0], LDV, kt2 * 32 + hf * 16, ni * 32, lane);
-          acc[ni] = mfma32(pa, vb, acc[ni]);
-        }
+    for (int hf = 0; hf < 2; ++hf) {
+      const uint4 pk = make_uint4(pack2(p[hf * 8 + 0], p[hf * 8 + 1]), pack2(p[hf * 8 + 2], p[hf * 8 + 3]),
+                                  pack2(p[hf * 8 + 4], p[hf * 8 + 5]), pack2(p[hf * 8 + 6], p[hf * 8 + 7]));
+      // This lane's keys 8*(2hf) + 4*ph .. +3 and 8*(2hf+1) + 4*ph .. +3 of query
+      // pq, in fp16 for the score products.
+      *(uint2*)(pw + pq * 64 + (p_unit(4 * hf + ph, pq) << 3)) =
+          make_uint2(pack2h(p[hf * 8 + 0], p[hf * 8 + 1]), pack2h(p[hf * 8 + 2], p[hf * 8 + 3]));
+      *(uint2*)(pw + pq * 64 + (p_unit(4 * hf + 2 + ph, pq) << 3)) =
+          make_uint2(pack2h(p[hf * 8 + 4], p[hf * 8 + 5]), pack2h(p[hf * 8 + 6], p[hf * 8 + 7]));
+      const bf16x8_t pa = __builtin_bit_cast(bf16x8_t, pk);
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni) {
+        const bf16x8_t vb = tr_operand_swz(st + kTile, 256, hf * 16, ni * 32, lane);
+        acc[ni] = mfma32(pa, vb, acc[ni]);
       }
     }
-    __syncthreads();
-    if (tid < KT) {
-      const int64_t key = (int64_t)t * KT + tid;
-      if (key < n)
-        score[((int64_t)hh * nb + b) * n + key] = sScore[0][tid] + sScore[1][tid] + sScore[2][tid] + sScore[3][tid];
-    }
-    if (t + 1 < ntiles) {
-      KV_STORE(buf ^ 1);
-    }
-    __syncthreads();
+    f32x16_t sc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sc[r] = 0.f;
+    sc = mfma32h(wq[0], p_operand(pw, 0, lane), sc);
+    sc = mfma32h(wq[1], p_operand(pw, 16, lane), sc);
+    if (lane < 32) sSc[(t / G) & 1][t % G][wave][lane] = sc[0] * (1.f / 32768.f);
+  };
+  int t = 0;
+  for (; t + NS < KF; t += 2) {
+    body(t, sa, sb, std::true_type{});
+    body(t + 1, sb, sa, std::true_type{});
   }
-#undef DN_LOAD
-  dpart += __shfl_xor(dpart, 32);
-  if (lane < 32) sDen[qi] = dpart;
+  while (t < KT) {
+    body(t, sa, sb, std::false_type{});
+    if (++t >= KT) break;
+    body(t, sb, sa, std::false_type{});
+    ++t;
+  }
+
+  // Epilogue through the idle ring: the numerator goes to LDS as fp32 [128
+  // rows][128 columns] (16-byte chunk c of row r at c ^ ((r / 4) % 2) * 8), then
+  // every thread stores whole 16-byte pieces of num and o.
   __syncthreads();
+  // Score groups not yet stored: the last one, and the one before it when the
+  // loop's final iteration (which has no barrier) was due to store it.
+  {
+    const int glast = (KT - 1) / G;
+    if ((KT - 1) % G == 0 && glast >= 1) store_scores(glast - 1);
+    store_scores(glast);
+  }
+  float* sacc_t = (float*)smem;
 #pragma unroll
-  for (int ni = 0; ni < 4; ++ni) {
-    const int c = ni * 32 + (lane & 31);
+  for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int qr = wave * 32 + acc_key(r, lane);
-      if (qr < rows) {
-        const int64_t g = (hoff + r0 + qr) * 128 + c;
-        num[g] = acc[ni][r];
-        o[g] = acc[ni][r] / sDen[qr];
-      }
+      const int cc = ni * 32 + (lane & 31);
+      sacc_t[qr * 128 + (((cc >> 2) ^ (((qr >> 2) & 1) << 3)) << 2) + (cc & 3)] = acc[ni][r];
     }
+  __syncthreads();
+#pragma unroll
+  for (int it = 0; it < PIECES; ++it) {
+    const int e = it * 256 + tid, qr = e >> 5, c4 = e & 31;
+    if (qr >= rows) continue;
+    const float4 a = *(const float4*)(sacc_t + qr * 128 + ((c4 ^ (((qr >> 2) & 1) << 3)) << 2));
+    const int64_t g = (hoff + r0 + qr) * 128 + c4 * 4;
+    // o = num / den with den = l, divided as the sparse step divides.
+    const float dl = sL[qr];
+    *(float4*)(num + g) = a;
+    *(float4*)(o + g) = make_float4(a.x / dl, a.y / dl, a.z / dl, a.w / dl);
   }
-  if (lane < 32 && qok) den[hoff + r0 + qi] = sDen[qi];
 }
 
 // Sparse step / REFRESH over the gathered keys S of one (head, query block).
@@ -580,8 +794,6 @@ __global__ __launch_bounds__(256, 2) void attn_sparse(const uint16_t* __restrict
   __shared__ float sDenRest[kRowBlock];
   attn_sparse_body<REFRESH>(blockIdx.x, smem, sIdx, sDen, sDenRest, q, k, v, idx, m, num, den, o, n, heads, kk, scale);
 }
-
-#undef KV_STORE
 
 }  // namespace
 }  // namespace chipmunk

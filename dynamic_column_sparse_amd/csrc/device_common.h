@@ -1,4 +1,4 @@
-// Device helpers shared by the gfx950 kernels: bf16 packing, the bf16 matrix-core
+// Device helpers shared by the gfx950 kernels: bf16/fp16 packing, the matrix-core
 // instructions, the transposing LDS read and wave-level reductions.
 #pragma once
 
@@ -14,6 +14,8 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 
 // fp32 -> bf16 bits, round to nearest, ties to even, through gfx950's packed
 // conversion (v_cvt_pk_bf16_f32).  Checked against a software round-to-nearest-
@@ -26,6 +28,11 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 __device__ __forceinline__ uint32_t f2bf(float x) { return pack2(x, 0.f) & 0xffffu; }
+// fp32 pair -> fp16 bits (v_cvt_pk_f16_f32, round to nearest even).
+__device__ __forceinline__ uint32_t pack2h(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
+}
 __device__ __forceinline__ float bf2f(uint32_t b) { return __uint_as_float(b << 16); }
 
 // D(32x32, fp32) += A(32x16) * B(16x32), bf16 operands.  Operand layout (checked on
@@ -34,6 +41,10 @@ __device__ __forceinline__ float bf2f(uint32_t b) { return __uint_as_float(b << 
 // column l%32.
 __device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+// The same product with fp16 operands (same register layout).
+__device__ __forceinline__ f32x16_t mfma32h(f16x8_t a, f16x8_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
 // Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
@@ -116,6 +127,17 @@ __device__ __forceinline__ void dma16_at(const void* g, uint32_t lds) {
       "global_load_lds_dwordx4 %0, off"
       :
       : "v"(g), "s"(lds)
+      : "memory", "m0");
+}
+// Form with a wave-uniform 64-bit base in SGPRs and a per-lane 32-bit byte
+// offset: advancing the base costs scalar work only.
+__device__ __forceinline__ void dma16_sa(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(voff), "s"(base), "s"(lds)
       : "memory", "m0");
 }
 __device__ __forceinline__ void dma4_at(const void* g, uint32_t lds) {

@@ -165,12 +165,17 @@ def _qkv(H, n, step, seed=0):
     return [syn.heads_activations(seed, t, step, H, n) for t in "QKV"]
 
 
-@pytest.mark.parametrize("n,H,kk", [(300, 2, 100), (256, 8, 64), (200, 1, 200)])
-def test_attention_refresh_and_sparse_match_oracle(L, n, H, kk):
-    print(f"attention parity n={n} H={H} kk={kk}", flush=True)
+@pytest.mark.parametrize("n,H,kk,sc", [
+    (300, 2, 100, SCALE), (256, 8, 64, SCALE), (200, 1, 200, SCALE),
+    (33, 3, 5, SCALE),          # one full 32-key chunk and a 1-key tail
+    (1, 1, 1, SCALE),           # a single token
+    (300, 2, 100, -0.5 * SCALE),  # negative scale: the row max is the minimum raw score
+])
+def test_attention_refresh_and_sparse_match_oracle(L, n, H, kk, sc):
+    print(f"attention parity n={n} H={H} kk={kk} scale={sc}", flush=True)
     from dynamic_column_sparse_amd.layers import AttnDelta
     b0, b1_ = _qkv(H, n, 0), _qkv(H, n, 1)
-    att = AttnDelta(n, H, kk, "cuda")
+    att = AttnDelta(n, H, kk, "cuda", scale=sc)
     g0 = [up_bf16(a) for a in b0]
     g1 = [up_bf16(a) for a in b1_]
     att.dense(*g0)
@@ -180,7 +185,7 @@ def test_attention_refresh_and_sparse_match_oracle(L, n, H, kk):
     refs = []
     for hh in range(H):
         q0, k0, v0 = (oracle.from_bf16_bits(a[hh]) for a in b0)
-        m, den, num, o, score = oracle.attn_dense(q0, k0, v0, SCALE)
+        m, den, num, o, score = oracle.attn_dense(q0, k0, v0, sc)
         np.testing.assert_allclose(m_g[hh], m, rtol=1e-5, atol=1e-5)
         assert oracle.rel_frobenius(den_g[hh], den) < 1e-3
         assert oracle.rel_frobenius(num_g[hh], num) < TOL
@@ -198,10 +203,10 @@ def test_attention_refresh_and_sparse_match_oracle(L, n, H, kk):
         q0, k0, v0 = (oracle.from_bf16_bits(a[hh]) for a in b0)
         q1, k1, v1 = (oracle.from_bf16_bits(a[hh]) for a in b1_)
         sidx = idx[hh * nb:(hh + 1) * nb]
-        nr, dr = oracle.attn_rest(q0, k0, v0, refs[hh][0], sidx, SCALE)
+        nr, dr = oracle.attn_rest(q0, k0, v0, refs[hh][0], sidx, sc)
         assert oracle.rel_frobenius(den_g[hh], dr) < 1e-3
         assert oracle.rel_frobenius(num_g[hh], nr) < TOL
-        o1 = oracle.attn_sparse(q1, k1, v1, refs[hh][0], nr, dr, sidx, SCALE)
+        o1 = oracle.attn_sparse(q1, k1, v1, refs[hh][0], nr, dr, sidx, sc)
         assert oracle.rel_frobenius(o_g[hh], o1) < TOL
 
 
