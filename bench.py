@@ -35,6 +35,9 @@ WORKLOADS = {
     # FLUX.1-dev at 1280x768: 3840 image + 512 text tokens, d 3072, h 12288;
     # MLP 70% sparse (keep 3686 of 12288), attention 83.5% sparse (keep 718 of 4352 keys).
     "flux": dict(n=4352, d=3072, h=12288, k=3686, heads=24, kk=718, steps=10),
+    # FLUX.1-dev at 2304x1280: 144x80 = 11520 image + 512 text tokens, the same
+    # sparsities (keep 3686 of 12288 hidden units, 16.5% = 1985 of 12032 keys).
+    "flux_2304": dict(n=12032, d=3072, h=12288, k=3686, heads=24, kk=1985, steps=10),
     "tiny": dict(n=256, d=128, h=512, k=128, heads=0, kk=0, steps=2),
     # HunyuanVideo 720x1280x129: 33x45x80 latent patches, 93% sparse.
     "hunyuan_mlp": dict(n=118800, d=3072, h=12288, k=860, heads=0, kk=0, steps=3),
@@ -361,6 +364,7 @@ def main():
         "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic (seeded Gaussian weights and drifting activations, real shapes)",
         "config": {"workload": {"flux": "FLUX.1-dev-shaped sparse step (MLP + attention delta)",
+                                "flux_2304": "FLUX.1-dev-shaped sparse step at 2304x1280 (MLP + attention delta)",
                                 "tiny": "tiny MLP delta", "hunyuan_mlp": "HunyuanVideo-shaped MLP delta",
                                 "hunyuan_attn": "HunyuanVideo-shaped attention delta"}[args.workload],
                    "tokens": w["n"], "d_model": w["d"], "d_hidden": w["h"], "mlp_keep": w["k"],

@@ -6,8 +6,8 @@
     tile widths (d a multiple of 256, and not), head counts with and without
     the XCD head mapping (heads % 8), k = 0, kk = 0, and an attention layer
     whose token count differs from the MLP's.
-  * Against the oracle at the FLUX.1-dev shape, in the launch configuration the
-    benchmark times: sampled row blocks (MLP) and (head, query block) slices
+  * Against the oracle at the FLUX.1-dev shapes (1280x768 and 2304x1280), in
+    the launch configuration the benchmark times: sampled row blocks (MLP) and (head, query block) slices
     (attention), each recomputed on its own (exact, as every block depends only
     on its own rows and the shared weights or keys).  Bars as for the separate
     calls: rel. Frobenius <= 2e-2 on outputs, 1e-3 on the cache.
@@ -90,19 +90,22 @@ def test_fused_step_refuses_overlap(gpu_lib):
     assert torch.equal(mlp.y, y_before)
 
 
-def test_flux_fused_step_against_oracle(gpu_lib):
-    # FLUX.1-dev shape (4352 tokens; MLP d 3072, h 12288, keep 3686 per block;
-    # 24 heads x 128, keep 718 keys per query block): refresh at step 0, then
-    # three sparse steps through the shared-grid call.
+@pytest.mark.parametrize("n,kk", [
+    (4352, 718),     # FLUX.1-dev at 1280x768: 3840 image + 512 text tokens, keep 16.5% of keys
+    (12032, 1985),   # FLUX.1-dev at 2304x1280: 11520 image + 512 text tokens, same sparsity
+])
+def test_flux_fused_step_against_oracle(gpu_lib, n, kk):
+    # MLP d 3072, h 12288, keep 3686 per block; 24 heads x 128: refresh at step
+    # 0, then three sparse steps through the shared-grid call.
     from dynamic_column_sparse_amd.layers import AttnDelta, MLPDelta, sparse_step
-    n, d, h, k, H, kk, steps, seed = 4352, 3072, 12288, 3686, 24, 718, 4, 0
+    d, h, k, H, steps, seed = 3072, 12288, 3686, 24, 4, 0
     nb = (n + RB - 1) // RB
     blocks = _sample_blocks(nb, 3, seed + 11, n)
     rows = _rows_of(blocks, n)
     rows_t = torch.from_numpy(rows).cuda()
     g = np.random.default_rng(21)
     slices = [(int(g.integers(H)), int(g.integers(nb))) for _ in range(3)] + [(H - 1, nb - 1)]
-    print(f"flux fused step: blocks {blocks}, slices {slices}", flush=True)
+    print(f"flux fused step n={n} kk={kk}: blocks {blocks}, slices {slices}", flush=True)
 
     w1t_b, w2_b = syn.mlp_weights(seed, d, h)
     mlp = MLPDelta(up_bf16(w1t_b), up_bf16(w2_b), n, k)
