@@ -7,9 +7,10 @@
     the XCD head mapping (heads % 8), k = 0, kk = 0, and an attention layer
     whose token count differs from the MLP's.
   * Against the oracle at the FLUX.1-dev shapes (1280x768 and 2304x1280), in
-    the launch configuration the benchmark times: sampled row blocks (MLP) and (head, query block) slices
-    (attention), each recomputed on its own (exact, as every block depends only
-    on its own rows and the shared weights or keys).  Bars as for the separate
+    the launch configuration the benchmark times: sampled row blocks (MLP) and
+    (head, query block) slices (attention), each recomputed on its own (exact,
+    as every block depends only on its own rows and the shared weights or
+    keys).  Bars as for the separate
     calls: rel. Frobenius <= 2e-2 on outputs, 1e-3 on the cache.
   * Overlapping buffers are refused before anything is launched.
 """
