@@ -202,6 +202,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--separate", action="store_true",
                     help="run the MLP and attention deltas as separate calls instead of the shared-grid step")
+    ap.add_argument("--mlp-rescore", action="store_true",
+                    help="every sparse step rescores the MLP units it recomputed, so S can change each step")
     ap.add_argument("--graph", action="store_true",
                     help="replay each sparse step as a captured HIP graph in the timed loop (eager launches are "
                          "as fast on this path)")
@@ -238,7 +240,7 @@ def main():
         inputs["w1t"], inputs["w2"] = syn.mlp_weights(0, w["d"], w["h"])
         inputs["x"] = syn.activation_walk(0, "X", T, w["n"], w["d"])
         xs = [up(x) for x in inputs["x"]]
-        mlp = MLPDelta(up(inputs["w1t"]), up(inputs["w2"]), w["n"], w["k"])
+        mlp = MLPDelta(up(inputs["w1t"]), up(inputs["w2"]), w["n"], w["k"], rescore=args.mlp_rescore)
     if w["kk"]:
         walks = [syn.heads_walk(0, t, T, w["heads"], w["n"]) for t in "QKV"]
         inputs["qkv"] = [[walks[i][s] for i in range(3)] for s in range(T)]
@@ -370,7 +372,8 @@ def main():
                    "tokens": w["n"], "d_model": w["d"], "d_hidden": w["h"], "mlp_keep": w["k"],
                    "heads": w["heads"], "head_dim": HEAD_DIM if w["heads"] else 0, "attn_keep": w["kk"],
                    "row_block": 128, "launch": ("hip graph per step" if args.graph else "eager")
-                   + ("; MLP phase 2 and attention share one kernel" if fused else "")},
+                   + ("; MLP phase 2 and attention share one kernel" if fused else ""),
+                   "mlp_set": "rescored every step" if args.mlp_rescore else "fixed between refreshes"},
         "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "flop_per_step": fl,
         "roofline": roof,

@@ -56,6 +56,9 @@ int check_mlp(const chipmunk_mlp* L, bool need_score) {
                 (long long)kMaxGridY);
   if (!L->w1t || !L->w2 || !L->a_cache) return fail(CHIPMUNK_E_NULLPTR, "layer w1t, w2 and a_cache are required");
   if (need_score && !L->score) return fail(CHIPMUNK_E_NULLPTR, "layer score is required by the dense step");
+  if (L->flags & ~CHIPMUNK_MLP_RESCORE) return fail(CHIPMUNK_E_SHAPE, "unknown layer flags 0x%x", L->flags);
+  if ((L->flags & CHIPMUNK_MLP_RESCORE) && !L->score)
+    return fail(CHIPMUNK_E_NULLPTR, "layer score is required by CHIPMUNK_MLP_RESCORE");
   if (!aligned(L->w1t, 16) || !aligned(L->w2, 16) || !aligned(L->a_cache, 16))
     return fail(CHIPMUNK_E_ALIGN, "w1t, w2 and a_cache must be 16-byte aligned");
   if ((L->b1 && !aligned(L->b1, 4)) || (L->b2 && !aligned(L->b2, 4)) || (L->score && !aligned(L->score, 4)))
@@ -89,6 +92,9 @@ int check_bf16_in(const void* p, const char* name) {
 size_t sparse_mlp_ws(int64_t n, int32_t k) {
   return (size_t)chipmunk::row_blocks(n) * (size_t)chipmunk::padded_k(k) * chipmunk::kRowBlock * sizeof(uint16_t);
 }
+
+// Scores the sparse delta rewrites (NULL: S stays fixed until the next dense step).
+float* rescore_target(const chipmunk_mlp* L) { return (L->flags & CHIPMUNK_MLP_RESCORE) ? L->score : nullptr; }
 
 // Arguments of the sparse MLP delta.
 int check_sparse_mlp(const chipmunk_mlp* L, const uint16_t* x, const int32_t* idx, int32_t k, const float* y,
@@ -317,8 +323,8 @@ extern "C" int chipmunk_sparse_mlp_delta(const chipmunk_mlp* L, const uint16_t* 
     if (k == 0) return ok();
     hipStream_t s = static_cast<hipStream_t>(stream);
     uint16_t* dbuf = static_cast<uint16_t*>(ws);
-    hipError_t e = chipmunk::launch_mlp_gemm1(false, x, L->w1t, L->b1, idx, L->a_cache, dbuf, a_new_packed, nullptr,
-                                              L->n, L->d, L->h, k, s);
+    hipError_t e = chipmunk::launch_mlp_gemm1(false, x, L->w1t, L->b1, idx, L->a_cache, dbuf, a_new_packed,
+                                              rescore_target(L), L->n, L->d, L->h, k, s);
     if (e != hipSuccess) return hip_status(e, "mlp_gemm1 (sparse) launch");
     e = chipmunk::launch_mlp_gemm2(false, dbuf, L->w2, idx, nullptr, y, L->n, L->d, L->h, k, chipmunk::padded_k(k), s);
     return hip_status(e, "mlp_gemm2 (sparse) launch");
@@ -358,7 +364,8 @@ extern "C" int chipmunk_sparse_step(const chipmunk_mlp* M, const uint16_t* x, co
     const Span mlp_w[] = {{y, (size_t)M->n * M->d * 4, "y"},
                           {M->a_cache, nb * M->h * 128 * 2, "mlp a_cache"},
                           {a_new_packed, nb * mk * 128 * 2, "a_new_packed"},
-                          {ws, k > 0 ? sparse_mlp_ws(M->n, k) : 0, "ws"}};
+                          {ws, k > 0 ? sparse_mlp_ws(M->n, k) : 0, "ws"},
+                          {rescore_target(M), rescore_target(M) ? nb * M->h * 4 : 0, "mlp score"}};
     const Span mlp_r[] = {{x, (size_t)M->n * M->d * 2, "x"},
                           {M->w1t, (size_t)M->h * M->d * 2, "w1t"},
                           {M->w2, (size_t)M->h * M->d * 2, "w2"},
@@ -382,9 +389,9 @@ extern "C" int chipmunk_sparse_step(const chipmunk_mlp* M, const uint16_t* x, co
       for (const Span& r : mlp_r)
         if (overlap(w, r)) return fail(CHIPMUNK_E_SHAPE, "%s overlaps %s", w.name, r.name);
     hipError_t e = chipmunk::launch_sparse_step(x, M->w1t, M->b1, mlp_idx, M->a_cache, static_cast<uint16_t*>(ws),
-                                                a_new_packed, M->w2, y, M->n, M->d, M->h, k, q, kx, v, attn_idx, A->m,
-                                                A->num, A->den, o, A->n, A->heads, kk, A->scale,
-                                                static_cast<hipStream_t>(stream));
+                                                a_new_packed, rescore_target(M), M->w2, y, M->n, M->d, M->h, k, q,
+                                                kx, v, attn_idx, A->m, A->num, A->den, o, A->n, A->heads, kk,
+                                                A->scale, static_cast<hipStream_t>(stream));
     return hip_status(e, "sparse step launch");
   } catch (...) {
     return fail(CHIPMUNK_E_INTERNAL, "internal error in chipmunk_sparse_step");

@@ -37,7 +37,8 @@ __host__ __device__ inline int64_t row_blocks(int64_t n) { return (n + kRowBlock
 __host__ __device__ inline int padded_k(int k) { return (k + 63) / 64 * 64; }
 
 // MLP phase 1: gathered x W1[:,S] + GELU, then either the sparse epilogue
-// (D tiles, cache writeback) or the dense one (score, full cache write).
+// (D tiles, cache writeback; with a score array, also S's column L1 of D) or
+// the dense one (score, full cache write).
 hipError_t launch_mlp_gemm1(bool dense, const uint16_t* x, const uint16_t* w1t, const float* b1,
                             const int32_t* idx, uint16_t* a_cache, uint16_t* dbuf, uint16_t* a_packed,
                             float* score, int64_t n, int d, int h, int k, hipStream_t s);
@@ -57,7 +58,8 @@ hipError_t launch_attn_sparse(bool refresh, const uint16_t* q, const uint16_t* k
 // Sparse MLP phase 1, then one kernel with the MLP phase-2 tiles first and the
 // sparse attention units after them (k = 0: attention units only).
 hipError_t launch_sparse_step(const uint16_t* x, const uint16_t* w1t, const float* b1, const int32_t* midx,
-                              uint16_t* a_cache, uint16_t* dbuf, uint16_t* a_packed, const uint16_t* w2, float* y,
+                              uint16_t* a_cache, uint16_t* dbuf, uint16_t* a_packed, float* mscore,
+                              const uint16_t* w2, float* y,
                               int64_t n, int d, int h, int k, const uint16_t* q, const uint16_t* kx,
                               const uint16_t* v, const int32_t* aidx, const float* m, const float* num,
                               const float* den, float* o, int64_t na, int heads, int kk, float scale,

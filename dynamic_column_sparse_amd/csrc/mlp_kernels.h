@@ -207,6 +207,9 @@ __global__ __launch_bounds__(256, 2) void mlp_gemm1(const uint16_t* __restrict__
     else
       oldv[i] = make_uint4(0, 0, 0, 0);
   }
+  // Column L1 of D over the block's real rows: the dense step's score; on a
+  // sparse step, the rescore of the recomputed units when a score array is given.
+  const bool rescore = !DENSE && score != nullptr;
   float colsum[CI];
 #pragma unroll
   for (int i = 0; i < CI; ++i) {
@@ -222,7 +225,7 @@ __global__ __launch_bounds__(256, 2) void mlp_gemm1(const uint16_t* __restrict__
       for (int e = 0; e < 2; ++e) {
         const bool live = ch * 8 + w * 2 + e < rows;
         dv[e] = live ? bf2f((a2 >> (16 * e)) & 0xffffu) - bf2f((o2 >> (16 * e)) & 0xffffu) : 0.f;
-        if (DENSE) colsum[i] += fabsf(dv[e]);
+        if (DENSE || rescore) colsum[i] += fabsf(dv[e]);
       }
       dw[w] = pack2(dv[0], dv[1]);
     }
@@ -235,6 +238,19 @@ __global__ __launch_bounds__(256, 2) void mlp_gemm1(const uint16_t* __restrict__
     // D replaces a_new in the staging tile: this thread is the only reader and
     // writer of this 16-byte slot.
     if (!DENSE) *(uint4*)(stile + t * 256 + ((ch ^ tc) << 4)) = make_uint4(dw[0], dw[1], dw[2], dw[3]);
+  }
+  if (DENSE || rescore) {
+    // The 16 lanes of a column hold 8 rows each.
+#pragma unroll
+    for (int i = 0; i < CI; ++i) {
+      float v = colsum[i];
+      v += __shfl_xor(v, 1);
+      v += __shfl_xor(v, 2);
+      v += __shfl_xor(v, 4);
+      v += __shfl_xor(v, 8);
+      const int t = tc + 16 * i, p = c0 + t;
+      if (ch == 0 && p < kcols) score[(int64_t)b * h + (DENSE ? p : scol[t])] = v;
+    }
   }
   if (!DENSE) {
     // D leaves row-major ([block][128 rows][kp]) so phase 2 reads it as a plain
@@ -261,19 +277,6 @@ __global__ __launch_bounds__(256, 2) void mlp_gemm1(const uint16_t* __restrict__
                                    (uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16), (uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16));
         *(uint4*)(dbuf + ((int64_t)b * BM + m) * kp + p) = v;
       }
-    }
-  }
-  if (DENSE) {
-    // Column L1 over the block's rows: the 16 lanes of a column hold 8 rows each.
-#pragma unroll
-    for (int i = 0; i < CI; ++i) {
-      float v = colsum[i];
-      v += __shfl_xor(v, 1);
-      v += __shfl_xor(v, 2);
-      v += __shfl_xor(v, 4);
-      v += __shfl_xor(v, 8);
-      const int p = c0 + tc + 16 * i;
-      if (ch == 0 && p < kcols) score[(int64_t)b * h + p] = v;
     }
   }
 }

@@ -28,9 +28,11 @@ def row_blocks(n: int) -> int:
 
 
 class MLPDelta:
-    """One MLP layer: w1t [h,d], w2 [h,d] bf16 device tensors; k kept columns per block."""
+    """One MLP layer: w1t [h,d], w2 [h,d] bf16 device tensors; k kept columns per block.
+    rescore=True: every sparse step rescores the units it recomputed, so the set
+    S can change from step to step (CHIPMUNK_MLP_RESCORE)."""
 
-    def __init__(self, w1t: torch.Tensor, w2: torch.Tensor, n: int, k: int, b1=None, b2=None):
+    def __init__(self, w1t: torch.Tensor, w2: torch.Tensor, n: int, k: int, b1=None, b2=None, rescore=False):
         h, d = w1t.shape
         assert w2.shape == (h, d) and w1t.dtype == torch.bfloat16 and w2.dtype == torch.bfloat16
         dev = w1t.device
@@ -43,7 +45,8 @@ class MLPDelta:
         self.idx = torch.zeros(self.nb, max(k, 1), dtype=torch.int32, device=dev)
         ws = lib.chipmunk_workspace_bytes(lib.OP_SPARSE_MLP, n, d, h, k)
         self.ws = torch.empty(max(ws, 16), dtype=torch.uint8, device=dev)
-        self.layer = lib.mlp_layer(n, d, h, w1t, w2, self.a_cache, self.score, b1, b2)
+        self.layer = lib.mlp_layer(n, d, h, w1t, w2, self.a_cache, self.score, b1, b2,
+                                   lib.MLP_RESCORE if rescore else 0)
 
     def dense(self, x: torch.Tensor, stream=None):
         lib.chipmunk_dense_step(lib.MLP, self.layer, x, None, None, self.y, self.ws, stream=stream)

@@ -19,6 +19,7 @@ ROW_BLOCK = 128
 HEAD_DIM = 128
 MLP, ATTN = 0, 1
 ATTN_SPARSE, ATTN_REFRESH = 0, 1
+MLP_RESCORE = 1   # chipmunk_mlp.flags: sparse steps rescore their recomputed units
 OP_DENSE_MLP, OP_SPARSE_MLP, OP_TOPK, OP_DENSE_ATTN, OP_SPARSE_ATTN = 0, 1, 2, 3, 4
 
 STATUS = {0: "CHIPMUNK_OK", 1: "CHIPMUNK_E_NULLPTR", 2: "CHIPMUNK_E_SHAPE", 3: "CHIPMUNK_E_UNSUPPORTED",
@@ -41,7 +42,8 @@ class MLPLayer(ctypes.Structure):
     """``chipmunk_mlp``: sizes and device pointers of one MLP layer."""
     _fields_ = [("n", ctypes.c_int64), ("d", ctypes.c_int32), ("h", ctypes.c_int32),
                 ("w1t", ctypes.c_void_p), ("b1", ctypes.c_void_p), ("w2", ctypes.c_void_p),
-                ("b2", ctypes.c_void_p), ("a_cache", ctypes.c_void_p), ("score", ctypes.c_void_p)]
+                ("b2", ctypes.c_void_p), ("a_cache", ctypes.c_void_p), ("score", ctypes.c_void_p),
+                ("flags", ctypes.c_uint32)]
 
 
 class AttnLayer(ctypes.Structure):
@@ -129,8 +131,8 @@ def chipmunk_workspace_bytes(op: int, n: int, d: int, h: int, k: int) -> int:
     return int(_lib.chipmunk_workspace_bytes(op, n, d, h, k))
 
 
-def mlp_layer(n, d, h, w1t, w2, a_cache, score=None, b1=None, b2=None) -> MLPLayer:
-    return MLPLayer(n, d, h, _ptr(w1t), _ptr(b1), _ptr(w2), _ptr(b2), _ptr(a_cache), _ptr(score))
+def mlp_layer(n, d, h, w1t, w2, a_cache, score=None, b1=None, b2=None, flags=0) -> MLPLayer:
+    return MLPLayer(n, d, h, _ptr(w1t), _ptr(b1), _ptr(w2), _ptr(b2), _ptr(a_cache), _ptr(score), flags)
 
 
 def attn_layer(n, heads, m, num, den, score=None, scale=None, head_dim=HEAD_DIM) -> AttnLayer:

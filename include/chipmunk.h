@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define CHIPMUNK_ABI_VERSION 1
+#define CHIPMUNK_ABI_VERSION 2
 #define CHIPMUNK_ROW_BLOCK 128
 #define CHIPMUNK_HEAD_DIM 128
 
@@ -93,6 +93,15 @@ enum chipmunk_op {
  *   a_cache [nb][h][128] bf16 activation cache, block-column-major: hidden unit
  *          j of block b is 128 contiguous values (256 bytes), one per row
  *   score  [nb][h] fp32 per-block column scores written by the dense step
+ *          (and, with CHIPMUNK_MLP_RESCORE, by every sparse step for its S)
+ *   flags  0, or CHIPMUNK_MLP_RESCORE: the sparse delta also sets score[b][j]
+ *          for each recomputed unit j of S_b to this step's column L1 over the
+ *          block's rows, sum_i |a_S[i,j] - a_cache[i,j]| (the dense step's
+ *          score formula, applied to the units the step recomputed), so the
+ *          next identification can choose a different S (the Chipmunk post
+ *          chooses which vectors to recompute dynamically, in each step;
+ *          Activation Deltas section).  Units outside S_b keep their scores.
+ *          Requires score.  0 keeps S fixed until the next dense step.
  */
 typedef struct chipmunk_mlp {
   int64_t n;
@@ -104,7 +113,10 @@ typedef struct chipmunk_mlp {
   const float* b2;
   uint16_t* a_cache;
   float* score;
+  uint32_t flags;
 } chipmunk_mlp;
+
+#define CHIPMUNK_MLP_RESCORE 1u
 
 /* One attention layer's cache (all heads).
  *   n        tokens (queries = keys, >= 1)

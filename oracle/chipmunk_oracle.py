@@ -43,6 +43,8 @@ design notes of this repository):
   R8 D is the exact difference of the stored bf16 values (no rounding of D here).
   R9 a partial last row block is scored over its real rows only.
   R10 sparse attention steps keep the refresh-step row max (no re-normalisation).
+  R12 optional per-step rescoring of the MLP: a sparse step sets the score of each
+      unit it recomputed to that step's column L1 of D; other units keep theirs.
 
 Parity pins for every function live in ``tests/test_oracle_*.py``.
 """
@@ -168,7 +170,7 @@ def mlp_dense(x, w1t, b1, w2, b2, a_old):
     return a_new, y, score
 
 
-def mlp_sparse(x, w1t, b1, w2, a, y, idx):
+def mlp_sparse(x, w1t, b1, w2, a, y, idx, score=None):
     """One sparse MLP step (Chipmunk post, Activation Deltas section: only the
     chosen output vectors are swapped for new ones, the others are kept).
 
@@ -180,6 +182,12 @@ def mlp_sparse(x, w1t, b1, w2, a, y, idx):
       y_b  += D w2[S]                               swap old vectors for new ones
       a[b rows, S] = a_S                            cache writeback
     Returns new copies (a, y); the inputs are not modified.
+
+    With ``score`` [nb,h] given (the per-step rescoring variant, reading R12:
+    the post chooses the recomputed vectors in each step), also returns a new
+    score in which score[b, S] = sum over the block's real rows of |D| -- the
+    dense step's score formula (R1) applied to this step's recomputed units --
+    and every other entry is unchanged: (a, y, score).
     """
     x = np.asarray(x, np.float64)
     w1t = np.asarray(w1t, np.float64)
@@ -187,6 +195,7 @@ def mlp_sparse(x, w1t, b1, w2, a, y, idx):
     a = np.array(a, dtype=np.float64, copy=True)
     y = np.array(y, dtype=np.float64, copy=True)
     idx = np.asarray(idx)
+    sc = None if score is None else np.array(score, dtype=np.float64, copy=True)
     n = x.shape[0]
     for b, r0, r1 in _blocks(n):
         s = idx[b]
@@ -199,6 +208,10 @@ def mlp_sparse(x, w1t, b1, w2, a, y, idx):
         d = a_s - a[r0:r1][:, s]
         y[r0:r1] += d @ w2[s]
         a[r0:r1, s] = a_s
+        if sc is not None:
+            sc[b, s] = np.abs(d).sum(axis=0)
+    if sc is not None:
+        return a, y, sc
     return a, y
 
 

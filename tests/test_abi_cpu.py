@@ -41,7 +41,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_names_workspace(L):
-    assert L.chipmunk_abi_version() == 1
+    assert L.chipmunk_abi_version() == 2
     names = L.kernel_names()
     assert "mlp_gemm1_sparse" in names and "attn_sparse" in names and "topk_rows" in names
     assert L.chipmunk_workspace_bytes(L.OP_SPARSE_MLP, 4352, 3072, 12288, 3686) == 34 * 3712 * 128 * 2
@@ -70,6 +70,8 @@ def _code(L, fn, *a, **kw):
 @pytest.mark.parametrize("case,code", [
     (dict(n=0), 2), (dict(d=100), 2), (dict(d=64), 2), (dict(h=0), 2), (dict(h=100), 2),
     (dict(w1t=None), 1), (dict(a_cache=None), 1), (dict(w2=FAKE + 8), 4),
+    (dict(flags=2), 2),                      # unknown flag bit
+    (dict(flags=1, score=None), 1),          # rescoring needs the score array
 ])
 def test_sparse_mlp_rejects_bad_layer(L, case, code):
     lay = _mlp(L, **case)

@@ -10,8 +10,8 @@
     the launch configuration the benchmark times: sampled row blocks (MLP) and
     (head, query block) slices (attention), each recomputed on its own (exact,
     as every block depends only on its own rows and the shared weights or
-    keys).  Bars as for the separate
-    calls: rel. Frobenius <= 2e-2 on outputs, 1e-3 on the cache.
+    keys).  Bars as for the separate calls: rel. Frobenius <= 2e-2 on outputs,
+    1e-3 on the cache.
   * Overlapping buffers are refused before anything is launched.
 """
 import numpy as np

@@ -148,3 +148,52 @@ def test_drifting_input_sparse_close_to_dense(seed):
     _, y1 = mlp_sparse(xs[1], w1t, b1, w2, a0, y0, idx)
     _, y1d, _ = mlp_dense(xs[1], w1t, b1, w2, b2, a0)
     assert rel_frobenius(y1, y1d) < 0.05
+
+
+# --------------------------------------------- per-step rescoring (R12) ---
+def test_rescore_equals_dense_score_on_recomputed_units():
+    # The rescore of a recomputed unit is the dense step's score formula (R1)
+    # for that step: mlp_dense(X1, a_old = A0) gives sum_i |A1 - A0| for every
+    # unit; a sparse step from A0 must reproduce it exactly on S_b and keep the
+    # previous scores elsewhere.  Random S per block (ragged tail block).
+    xs, w1t, b1, w2, b2 = _setup(n=300, d=64, h=192)
+    a0, y0, sc0 = mlp_dense(xs[0], w1t, b1, w2, b2, np.zeros((300, 192)))
+    _, _, sc_dense1 = mlp_dense(xs[1], w1t, b1, w2, b2, a0)
+    g = np.random.default_rng(3)
+    idx = np.stack([np.sort(g.choice(192, size=50, replace=False)) for _ in range(3)]).astype(np.int32)
+    a1, y1, sc1 = mlp_sparse(xs[1], w1t, b1, w2, a0, y0, idx, score=sc0)
+    a1n, y1n = mlp_sparse(xs[1], w1t, b1, w2, a0, y0, idx)
+    np.testing.assert_array_equal(a1, a1n)          # rescoring changes no other output
+    np.testing.assert_array_equal(y1, y1n)
+    for b in range(3):
+        inside = np.zeros(192, bool)
+        inside[idx[b]] = True
+        np.testing.assert_allclose(sc1[b, inside], sc_dense1[b, inside], rtol=1e-12, atol=0)
+        np.testing.assert_array_equal(sc1[b, ~inside], sc0[b, ~inside])
+
+
+def test_rescore_brute_force_tiny():
+    n, d, h = 130, 8, 6
+    xs, w1t, b1, w2, b2 = _setup(n, d, h, seed=5)
+    a0 = bf16_round(np.random.default_rng(2).standard_normal((n, h)))
+    y0 = np.zeros((n, d))
+    sc0 = np.full((2, h), 7.0)
+    idx = np.array([[1, 4], [0, 5]], np.int32)
+    _, _, sc = mlp_sparse(xs[1], w1t, b1, w2, a0, y0, idx, score=sc0)
+    for b, (r0, r1) in enumerate([(0, 128), (128, 130)]):
+        for j in range(h):
+            if j in idx[b]:
+                z = [sum(xs[1][i, c] * w1t[j, c] for c in range(d)) + b1[j] for i in range(r0, r1)]
+                a_new = [bf16_round(np.array(0.5 * v * (1 + np.tanh(np.sqrt(2 / np.pi) * (v + 0.044715 * v ** 3)))))
+                         for v in z]
+                want = sum(abs(float(a_new[i - r0]) - a0[i, j]) for i in range(r0, r1))
+                assert abs(sc[b, j] - want) <= 1e-9 * max(1.0, want)
+            else:
+                assert sc[b, j] == 7.0
+
+
+def test_rescore_empty_set_keeps_scores():
+    xs, w1t, b1, w2, b2 = _setup()
+    a0, y0, sc0 = mlp_dense(xs[0], w1t, b1, w2, b2, np.zeros((300, 192)))
+    _, _, sc = mlp_sparse(xs[1], w1t, b1, w2, a0, y0, np.zeros((3, 0), np.int32), score=sc0)
+    np.testing.assert_array_equal(sc, sc0)
