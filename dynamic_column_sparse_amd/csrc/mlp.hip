@@ -3,6 +3,13 @@
 
 namespace chipmunk {
 
+#ifndef MLP_WIDE_WASTE_PCT
+#define MLP_WIDE_WASTE_PCT 25
+#endif
+// Largest share of computed-but-unused columns (percent) accepted for 256-wide
+// phase-1 tiles.
+constexpr int kWideWastePct = MLP_WIDE_WASTE_PCT;
+
 hipError_t launch_mlp_gemm1(bool dense, const uint16_t* x, const uint16_t* w1t, const float* b1,
                             const int32_t* idx, uint16_t* a_cache, uint16_t* dbuf, uint16_t* a_packed,
                             float* score, int64_t n, int d, int h, int k, hipStream_t s) {
@@ -11,7 +18,7 @@ hipError_t launch_mlp_gemm1(bool dense, const uint16_t* x, const uint16_t* w1t, 
   const int kp = padded_k(k);
   // 256-wide tiles when they waste little of the last tile, else 128-wide.
   const int t256 = (cols + 255) / 256, t128 = (cols + 127) / 128;
-  const bool wide = t128 > 1 && (int64_t)t256 * 256 * 100 <= (int64_t)cols * 106;
+  const bool wide = t128 > 1 && (int64_t)t256 * 256 * 100 <= (int64_t)cols * (100 + kWideWastePct);
   const int kid = dense ? K_MLP_GEMM1_DENSE : K_MLP_GEMM1_SPARSE;
   timing_before(kid, s);
   if (wide) {

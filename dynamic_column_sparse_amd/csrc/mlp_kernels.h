@@ -553,15 +553,10 @@ __device__ __forceinline__ void gemm2_rows_body(int lin, unsigned char* smem, in
   }
 
   f32x16_t acc[MI][NI];
-#pragma unroll
-  for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < NI; ++ni)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
-
   const int KT = kp / BK;
-  // Prologue: ids of chunks 0..5, then stages 0 and 1.
+  // Prologue: ids of chunks 0..5, then stages 0 and 1, then the tile's old y
+  // into the accumulators (so the sums start from y and the epilogue only
+  // stores; the y loads' latency overlaps the first stages).
   if (wave == 0 && lane < BK) {
 #pragma unroll
     for (int t = 0; t < 6; ++t)
@@ -577,12 +572,31 @@ __device__ __forceinline__ void gemm2_rows_body(int lin, unsigned char* smem, in
     G2R_ISSUE(1, 1, ids_a);
   }
   if (KT > 2) load_ids(2, ids_a);
+  // Row bases are wave-uniform; a lane adds one 32-bit offset (its 4-row half
+  // and column).  Rows past the block end start at 0 and are never stored.
+  const int lane_off = (lane >> 5) * 4 * d + wave * WN + (lane & 31);
+  const int mhalf = (lane >> 5) * 4;
+  const bool full = rows == BM;   // wave-uniform: only a ragged last block clamps
+#pragma unroll
+  for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int R = mi * 32 + (r >> 2) * 8 + (r & 3);
+        if (full) {
+          acc[mi][ni][r] = y[(r0 + R) * (int64_t)d + n0 + ni * 32 + lane_off];
+        } else {
+          const int rr = R + mhalf < rows ? R + mhalf : rows - 1;
+          acc[mi][ni][r] = y[(r0 + rr) * (int64_t)d + n0 + ni * 32 + wave * WN + (lane & 31)];
+        }
+      }
 
   const int sw = swz4(lane & 31);
   for (int kt = 0; kt < KT; ++kt) {
     // Outstanding loads of this wave, newest first: stage kt+1 (L) and, on wave
     // 0, the id load of chunk kt+5 if the previous iteration issued one.
-    // Everything older (stage kt) must be complete.
+    // Everything older (stage kt, and y) must be complete.
     if (kt + 1 < KT) {
       if (wave == 0 && kt >= 1 && kt + 5 < KT)
         wait_vmcnt<L + 1>();
@@ -614,32 +628,17 @@ __device__ __forceinline__ void gemm2_rows_body(int lin, unsigned char* smem, in
   }
 #undef G2R_ISSUE
 
-  // y += acc, one 32-column slice at a time: load all of its old values, then
-  // store all of its sums (row offsets depend on d, so the compiler cannot
-  // overlap one read-modify-write with the next by itself).  Row bases are
-  // wave-uniform; a lane adds one 32-bit offset (its 4-row half and column).
-  const int lane_off = (lane >> 5) * 4 * d + wave * WN + (lane & 31);
-  const int mhalf = (lane >> 5) * 4;
+  // y = acc (which started from the old y).
 #pragma unroll
-  for (int ni = 0; ni < NI; ++ni) {
-    float yold[MI][16];
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int R = mi * 32 + (r >> 2) * 8 + (r & 3);
-        const float* yrow = y + (r0 + R) * (int64_t)d + n0 + ni * 32;
-        yold[mi][r] = R + mhalf < rows ? yrow[lane_off] : 0.f;
-      }
+  for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int R = mi * 32 + (r >> 2) * 8 + (r & 3);
         float* yrow = y + (r0 + R) * (int64_t)d + n0 + ni * 32;
-        if (R + mhalf < rows) yrow[lane_off] = yold[mi][r] + acc[mi][ni][r];
+        if (full || R + mhalf < rows) yrow[lane_off] = acc[mi][ni][r];
       }
-  }
 }
 
 template <int BN>
