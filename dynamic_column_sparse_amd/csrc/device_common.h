@@ -249,10 +249,15 @@ __device__ __forceinline__ void transpose8x8_bf16(const uint4 (&in)[8], uint4 (&
 // evaluated as z / (1 + exp(-2u)) (the same function: 0.5 (1 + tanh u) is the
 // logistic function of 2u), with the hardware reciprocal (about 1 ulp; the
 // result is rounded to bf16 next).  exp(-2u) overflowing to +inf gives z * 0.
+//
+// The exponent -2u, in base 2, is z * (a + b z^2) with a = -2c log2(e) and
+// b = -2c * 0.044715 * log2(e) (c = sqrt(2/pi)): one FMA and two products
+// before the hardware exp2, and no branches.
 __device__ __forceinline__ float gelu_tanh(float z) {
-  const float c = 0.7978845608028654f;
-  const float u = c * (z + 0.044715f * z * z * z);
-  return z * __builtin_amdgcn_rcpf(1.0f + __expf(-2.0f * u));
+  constexpr float a = -2.0f * 0.7978845608028654f * 1.4426950408889634f;
+  constexpr float b = a * 0.044715f;
+  const float t = z * __builtin_fmaf(b, z * z, a);
+  return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(t));
 }
 
 __device__ __forceinline__ int clamp_index(int j, int hi) { return j < 0 ? 0 : (j >= hi ? hi - 1 : j); }

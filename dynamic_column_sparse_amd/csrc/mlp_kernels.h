@@ -186,10 +186,14 @@ __global__ __launch_bounds__(256, 2) void mlp_gemm1(const uint16_t* __restrict__
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int m0 = wm * 64 + mi * 32 + g * 8 + (lane >> 5) * 4;
+        // Evaluated for every element, then selected: a branch per element
+        // would cost more than the arithmetic.
         float av[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          av[e] = (valid[ni] && m0 + e < rows) ? gelu_tanh(acc[mi][ni][g * 4 + e] + bias[ni]) : 0.f;
+        for (int e = 0; e < 4; ++e) {
+          const float gv = gelu_tanh(acc[mi][ni][g * 4 + e] + bias[ni]);
+          av[e] = (valid[ni] && m0 + e < rows) ? gv : 0.f;
+        }
         *(uint2*)(stile + t * 256 + (((m0 >> 3) ^ (t & 15)) << 4) + (m0 & 7) * 2) =
             make_uint2(pack2(av[0], av[1]), pack2(av[2], av[3]));
       }
