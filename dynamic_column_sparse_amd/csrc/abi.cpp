@@ -73,7 +73,8 @@ int check_attn(const chipmunk_attn* L) {
   if (L->head_dim != CHIPMUNK_HEAD_DIM)
     return fail(CHIPMUNK_E_UNSUPPORTED, "head_dim must be %d (got %d)", CHIPMUNK_HEAD_DIM, L->head_dim);
   if (!std::isfinite(L->scale)) return fail(CHIPMUNK_E_SHAPE, "scale must be finite");
-  if (L->n > INT32_MAX) return fail(CHIPMUNK_E_SHAPE, "n must fit in int32");
+  if (L->n >= (int64_t)1 << 24)
+    return fail(CHIPMUNK_E_SHAPE, "n must be below 2^24 (32-bit byte offsets of gathered K/V rows)");
   if (chipmunk::row_blocks(L->n) * (int64_t)L->heads > kMaxGroups)
     return fail(CHIPMUNK_E_SHAPE, "heads * row blocks exceeds the grid limit (%lld workgroups)", (long long)kMaxGroups);
   if (!L->m || !L->num || !L->den) return fail(CHIPMUNK_E_NULLPTR, "layer m, num and den are required");

@@ -567,13 +567,15 @@ __device__ __forceinline__ void attn_sparse_body(int lin, unsigned char* smem, i
       dma4_at(S + (j < kk ? j : 0), lds_addr(&sIdx[t & (RID - 1)][0]));
     }
   };
+  // Gathered rows load from the head's K / V base (wave-uniform, in SGPRs) plus
+  // a 32-bit byte offset id * 256 + the lane's chunk (n < 2^24 keeps it exact).
 #define AS_ISSUE(buf_, ids_)                                                                 \
   {                                                                                          \
     const uint32_t st_ = smem_lds + (buf_) * STAGE;                                          \
     _Pragma("unroll") for (int i = 0; i < INS; ++i)                                          \
-        dma16_at(kh + (int64_t)ids_[i] * 128 + koff[i], st_ + (wave * INS + i) * 1024);      \
+        dma16_sa(kh, (uint32_t)ids_[i] * 256u + (uint32_t)koff[i] * 2u, st_ + (wave * INS + i) * 1024); \
     _Pragma("unroll") for (int i = 0; i < INS; ++i)                                          \
-        dma16_at(vh + (int64_t)ids_[i] * 128 + voff[i], st_ + TILE + (wave * INS + i) * 1024); \
+        dma16_sa(vh, (uint32_t)ids_[i] * 256u + (uint32_t)voff[i] * 2u, st_ + TILE + (wave * INS + i) * 1024); \
   }
   float4 rest[PIECES];
   auto load_rest = [&]() __attribute__((always_inline)) {

@@ -119,7 +119,7 @@ typedef struct chipmunk_mlp {
 #define CHIPMUNK_MLP_RESCORE 1u
 
 /* One attention layer's cache (all heads).
- *   n        tokens (queries = keys, >= 1)
+ *   n        tokens (queries = keys, 1 <= n < 2^24)
  *   heads    number of heads (>= 1)
  *   head_dim must be 128
  *   scale    softmax scale (usually 1/sqrt(head_dim))

@@ -132,6 +132,8 @@ def test_topk_and_attn_checks(L):
     assert _code(L, s, att, FAKE, FAKE, FAKE, None, 10, L.ATTN_SPARSE, FAKE, stream=0) == 1
     assert _code(L, s, att, FAKE, FAKE, FAKE, None, 0, L.ATTN_REFRESH, None, stream=0) == 0
     assert _code(L, s, L.attn_layer(300, 0, FAKE, FAKE, FAKE), FAKE, FAKE, FAKE, FAKE, 1, 0, FAKE, stream=0) == 2
+    # gathered K/V rows use 32-bit byte offsets within a head: n < 2^24
+    assert _code(L, s, L.attn_layer(1 << 24, 1, FAKE, FAKE, FAKE), FAKE, FAKE, FAKE, FAKE, 1, 0, FAKE, stream=0) == 2
     w = L.chipmunk_cache_writeback
     assert _code(L, w, _mlp(L), FAKE, FAKE, 700, stream=0) == 2
     assert _code(L, w, _mlp(L), None, FAKE, 10, stream=0) == 1
