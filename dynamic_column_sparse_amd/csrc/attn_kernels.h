@@ -11,10 +11,11 @@
 // Exponentials are exp(scale s - m) = 2^(s * scale*log2e - m*log2e): one FMA
 // and one exp2 per element.
 //
-//   attn_stats  (refresh pass 1): row max m and row sum l over all keys.
-//   attn_dense  (refresh pass 2): p = exp(s - m), num = p V, den = sum p,
-//               o = num / den, and the key-mass score sum_i p_ij / l_i per key,
-//               reduced over the block's queries inside the workgroup.
+//   attn_stats  (refresh pass 1): row max m and row sum l over all keys
+//               (l is the refresh's den = sum_j p_ij).
+//   attn_dense  (refresh pass 2): p = exp(s - m), num = p V, o = num / l, and
+//               the key-mass score sum_i p_ij / l_i per key, reduced over the
+//               block's queries on the matrix cores.
 //   attn_sparse (sparse step / REFRESH): the same loop over the gathered keys
 //               S only, with the cached m; SPARSE writes
 //               o = (num + num_S) / (den + den_S); REFRESH subtracts the S part
