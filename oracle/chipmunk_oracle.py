@@ -45,6 +45,11 @@ design notes of this repository):
   R10 sparse attention steps keep the refresh-step row max (no re-normalisation).
   R12 optional per-step rescoring of the MLP: a sparse step sets the score of each
       unit it recomputed to that step's column L1 of D; other units keep theirs.
+  R13 optional per-step re-identification of attention: the cache keeps the total
+      numerator and denominator of the dense step; a sparse step takes the chosen
+      keys' share as computed from the previous step's q, k, v out of them and puts
+      the share from this step's q, k, v in, and sets those keys' scores to this
+      step's probability mass over the denominator held at the start of the step.
 
 Parity pins for every function live in ``tests/test_oracle_*.py``.
 """
@@ -286,6 +291,41 @@ def attn_sparse(q, k, v, m, num_rest, den_rest, idx, scale: float):
         p = np.exp(scale * (q[r0:r1] @ k[s].T) - m[r0:r1, None])
         o[r0:r1] = (num_rest[r0:r1] + p @ v[s]) / (den_rest[r0:r1] + p.sum(axis=1))[:, None]
     return o
+
+
+def attn_reident(q_prev, k_prev, v_prev, q, k, v, m, num, den, score, idx, scale: float):
+    """One sparse attention step that lets S change from step to step (reading
+    R13; Chipmunk post, Activation Deltas section: the subset of vectors to
+    recompute is chosen anew in each step, and a step swaps the chosen vectors of
+    the earlier step for this step's).
+
+    The cache (num, den) holds totals over all keys, as the dense step leaves them.
+    For each block b with S = idx[b], and the row max m kept from the refresh:
+      p_old = exp(scale q_prev_b k_prev[S]^T - m_b)      (the previous step's share)
+      p_new = exp(scale q_b k[S]^T - m_b)                (this step's share)
+      num_b <- num_b - p_old v_prev[S] + p_new v[S]
+      den_b <- den_b - sum_j p_old + sum_j p_new
+      o_b    = num_b / den_b
+      score[b, S] <- sum over the block's rows of p_new / den_b (den before the step)
+    Scores of keys outside S are kept.  Returns (o, num, den, score), new arrays.
+    """
+    f = lambda a: np.asarray(a, np.float64)
+    q_prev, k_prev, v_prev, q, k, v, m = map(f, (q_prev, k_prev, v_prev, q, k, v, m))
+    num = f(num).copy()
+    den = f(den).copy()
+    score = f(score).copy()
+    nq = q.shape[0]
+    o = np.zeros((nq, v.shape[1]))
+    for b, r0, r1 in _blocks(nq):
+        s = np.asarray(idx[b])
+        mb = m[r0:r1, None]
+        p_old = np.exp(scale * (q_prev[r0:r1] @ k_prev[s].T) - mb)
+        p_new = np.exp(scale * (q[r0:r1] @ k[s].T) - mb)
+        score[b, s] = (p_new / den[r0:r1, None]).sum(axis=0)
+        num[r0:r1] += p_new @ v[s] - p_old @ v_prev[s]
+        den[r0:r1] += p_new.sum(axis=1) - p_old.sum(axis=1)
+        o[r0:r1] = num[r0:r1] / den[r0:r1, None]
+    return o, num, den, score
 
 
 def rel_frobenius(a, b) -> float:
