@@ -53,11 +53,13 @@ def flops_mlp(w):
     return 4.0 * w["n"] * w["d"] * w["k"]
 
 
-def flops_attn(w):
-    return 4.0 * w["n"] * w["kk"] * HEAD_DIM * w["heads"]
+def flops_attn(w, reident=False):
+    # With per-step re-identification the delta computes two shares of the
+    # chosen keys (the previous step's, taken out, and this step's, put in).
+    return (8.0 if reident else 4.0) * w["n"] * w["kk"] * HEAD_DIM * w["heads"]
 
 
-def kernel_work(name, w):
+def kernel_work(name, w, reident=False):
     """(amount, bound) of algorithmic work in ONE launch of kernel `name`."""
     n, d, h, k, H, kk = w["n"], w["d"], w["h"], w["k"], w["heads"], w["kk"]
     nb = (n + 127) // 128
@@ -67,10 +69,15 @@ def kernel_work(name, w):
         return 2.0 * n * k * d, "mfma"
     if name == "attn_sparse":
         return 4.0 * n * kk * HEAD_DIM * H, "mfma"
+    if name == "attn_reident":
+        return 8.0 * n * kk * HEAD_DIM * H, "mfma"
     if name == "sparse_step_fused":
         return 2.0 * n * k * d + 4.0 * n * kk * HEAD_DIM * H, "mfma"
     if name == "topk_rows":
-        return float(nb * h * 4 + nb * k * 4), "hbm"
+        # score rows read + index rows written, averaged over the step's
+        # launches: the MLP's, and the attention's when it re-identifies
+        parts = ([nb * h * 4 + nb * k * 4] if k else []) + ([H * nb * n * 4 + H * nb * kk * 4] if reident else [])
+        return (float(sum(parts)) / len(parts), "hbm") if parts else (None, None)
     return None, None
 
 
@@ -129,7 +136,7 @@ def blas_threads():
     return len(os.sched_getaffinity(0))
 
 
-def cpu_baseline(w, inputs, budget_s):
+def cpu_baseline(w, inputs, budget_s, reident=False):
     """The CPU oracle, as it stands, on a bounded sample of the same sparse step.
     MLP: whole 128-row blocks until half the budget is used; attention: whole
     (head, query block) pairs of the first heads until the rest is used.  The
@@ -167,10 +174,15 @@ def cpu_baseline(w, inputs, budget_s):
             for b in range(nb):
                 r0, r1 = b * 128, min(n, b * 128 + 128)
                 m, den, num, o, sc = oracle.attn_dense(q0[r0:r1], k0, v0, scale)
-                idx = oracle.identify_topk(sc.astype(np.float32), kk)
-                nr, dr = oracle.attn_rest(q0[r0:r1], k0, v0, m, idx, scale)
-                t0 = time.perf_counter()
-                oracle.attn_sparse(q1[r0:r1], k1, v1, m, nr, dr, idx, scale)
+                if reident:
+                    t0 = time.perf_counter()
+                    idx = oracle.identify_topk(sc.astype(np.float32), kk)
+                    oracle.attn_reident(q0[r0:r1], k0, v0, q1[r0:r1], k1, v1, m, num, den, sc, idx, scale)
+                else:
+                    idx = oracle.identify_topk(sc.astype(np.float32), kk)
+                    nr, dr = oracle.attn_rest(q0[r0:r1], k0, v0, m, idx, scale)
+                    t0 = time.perf_counter()
+                    oracle.attn_sparse(q1[r0:r1], k1, v1, m, nr, dr, idx, scale)
                 t_att += time.perf_counter() - t0
                 n_att += 1
                 if t_att > budget_s / 2:
@@ -184,7 +196,7 @@ def cpu_baseline(w, inputs, budget_s):
         t_full += t_mlp / n_mlp * ((w["n"] + 127) // 128)
     if n_att:
         t_full += t_att / n_att * (w["heads"] * ((w["n"] + 127) // 128))
-    fl = flops_mlp(w) + flops_attn(w)
+    fl = flops_mlp(w) + flops_attn(w, reident)
     return {"value": round(fl / t_full / 1e12, 6), "unit": "TFLOP/s", "cores": blas_threads(),
             "kind": "oracle",
             "sample": "; ".join(desc) + f" of one sparse step, fp64 NumPy, scaled to the full step "
@@ -204,6 +216,9 @@ def main():
                     help="run the MLP and attention deltas as separate calls instead of the shared-grid step")
     ap.add_argument("--mlp-rescore", action="store_true",
                     help="every sparse step rescores the MLP units it recomputed, so S can change each step")
+    ap.add_argument("--attn-reident", action="store_true",
+                    help="attention identifies its keys anew every step (the cache keeps totals; each step swaps "
+                         "the chosen keys' previous-step share for this step's)")
     ap.add_argument("--graph", action="store_true",
                     help="replay each sparse step as a captured HIP graph in the timed loop (eager launches are "
                          "as fast on this path)")
@@ -245,7 +260,7 @@ def main():
         walks = [syn.heads_walk(0, t, T, w["heads"], w["n"]) for t in "QKV"]
         inputs["qkv"] = [[walks[i][s] for i in range(3)] for s in range(T)]
         qkv = [[up(a) for a in step] for step in inputs["qkv"]]
-        att = AttnDelta(w["n"], w["heads"], w["kk"], dev)
+        att = AttnDelta(w["n"], w["heads"], w["kk"], dev, reident=args.attn_reident)
     torch.cuda.synchronize()
     log(f"inputs ready ({time.time() - t0:.1f} s): workload {args.workload} {w}")
 
@@ -257,7 +272,7 @@ def main():
         if att:
             att.step(*qkv[t], refresh=True)
 
-    fused = bool(mlp and att) and not args.separate
+    fused = bool(mlp and att) and not args.separate and not args.attn_reident
 
     def sparse(t):
         if fused:
@@ -332,12 +347,12 @@ def main():
     torch.cuda.synchronize()
     refresh_ms = (time.perf_counter() - tr) * 1e3 / reps
 
-    fl = flops_mlp(w) + flops_attn(w)
+    fl = flops_mlp(w) + flops_attn(w, args.attn_reident)
     tflops = fl / (ms_per_step * 1e-3) / 1e12
 
     table = {}
     for name, r in kern.items():
-        amount, bound = kernel_work(name, w)
+        amount, bound = kernel_work(name, w, args.attn_reident)
         ent = {"avg_us": round(r["avg_us"], 3), "launches": r["launches"],
                "share": round(r["ms_total"] / max(1e-12, sum(v["ms_total"] for v in kern.values())), 4)}
         if amount is not None:
@@ -347,8 +362,9 @@ def main():
             else:
                 ent.update(achieved=round(ach / 1e9, 1), unit="GB/s", frac=round(ach / 1e9 / PEAK_HBM_GBS, 4))
         table[name] = ent
-    dom = max((n for n in kern if kernel_work(n, w)[0] is not None), key=lambda n: kern[n]["ms_total"])
-    amount, bound = kernel_work(dom, w)
+    dom = max((n for n in kern if kernel_work(n, w, args.attn_reident)[0] is not None),
+              key=lambda n: kern[n]["ms_total"])
+    amount, bound = kernel_work(dom, w, args.attn_reident)
     avg_s = kern[dom]["avg_us"] * 1e-6
     if bound == "mfma":
         roof = {"bound": "mfma", "achieved": round(amount / avg_s / 1e12, 2), "peak": PEAK_BF16_TFLOPS,
@@ -373,7 +389,8 @@ def main():
                    "heads": w["heads"], "head_dim": HEAD_DIM if w["heads"] else 0, "attn_keep": w["kk"],
                    "row_block": 128, "launch": ("hip graph per step" if args.graph else "eager")
                    + ("; MLP phase 2 and attention share one kernel" if fused else ""),
-                   "mlp_set": "rescored every step" if args.mlp_rescore else "fixed between refreshes"},
+                   "mlp_set": "rescored every step" if args.mlp_rescore else "fixed between refreshes",
+                   "attn_set": "re-identified every step" if args.attn_reident else "fixed between refreshes"},
         "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "flop_per_step": fl,
         "roofline": roof,
@@ -386,7 +403,7 @@ def main():
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         cb = cpu_baseline(w, {**inputs, "x": inputs.get("x", [None, None])[:2],
-                              "qkv": inputs.get("qkv", [None, None])[:2]}, args.cpu_budget)
+                              "qkv": inputs.get("qkv", [None, None])[:2]}, args.cpu_budget, args.attn_reident)
         out["cpu_baseline"] = cb
     print(json.dumps(out), flush=True)
 

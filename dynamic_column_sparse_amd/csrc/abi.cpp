@@ -178,7 +178,8 @@ hipEvent_t take_event() {
 const char* kernel_name(int kid) {
   static const char* names[K_COUNT] = {"mlp_gemm1_sparse", "mlp_gemm1_dense", "mlp_gemm2_sparse", "mlp_gemm2_dense",
                                        "topk_rows",        "cache_writeback", "attn_stats",       "attn_dense",
-                                       "attn_sparse",      "attn_refresh",     "sparse_step_fused"};
+                                       "attn_sparse",      "attn_refresh",     "sparse_step_fused",
+                                       "attn_reident"};
   return (kid >= 0 && kid < K_COUNT) ? names[kid] : "";
 }
 
@@ -346,6 +347,44 @@ extern "C" int chipmunk_sparse_attn_delta(const chipmunk_attn* L, const uint16_t
     return hip_status(e, "attention delta launch");
   } catch (...) {
     return fail(CHIPMUNK_E_INTERNAL, "internal error in chipmunk_sparse_attn_delta");
+  }
+}
+
+extern "C" int chipmunk_sparse_attn_reident(const chipmunk_attn* L, const uint16_t* q_prev, const uint16_t* k_prev,
+                                            const uint16_t* v_prev, const uint16_t* q, const uint16_t* k,
+                                            const uint16_t* v, const int32_t* idx, int32_t kk, float* o,
+                                            void* stream) {
+  try {
+    int rc = check_sparse_attn(L, q, k, v, idx, kk, CHIPMUNK_ATTN_SPARSE, o);
+    if (rc) return rc;
+    if ((rc = check_bf16_in(q_prev, "q_prev")) || (rc = check_bf16_in(k_prev, "k_prev")) ||
+        (rc = check_bf16_in(v_prev, "v_prev")))
+      return rc;
+    if (!L->score) return fail(CHIPMUNK_E_NULLPTR, "layer score is required (the step rescores its keys)");
+    // The kernel updates num, den and score in place and writes o while it
+    // reads the inputs: no written buffer may share memory with another
+    // buffer of the call.
+    const size_t toks = (size_t)L->heads * (size_t)L->n, hd = CHIPMUNK_HEAD_DIM;
+    const size_t nba = (size_t)chipmunk::row_blocks(L->n), ak = kk > 0 ? (size_t)kk : 0;
+    const Span wr[] = {{o, toks * hd * 4, "o"},
+                       {L->num, toks * hd * 4, "num"},
+                       {L->den, toks * 4, "den"},
+                       {L->score, (size_t)L->heads * nba * (size_t)L->n * 4, "score"}};
+    const Span rd[] = {{q_prev, toks * hd * 2, "q_prev"}, {k_prev, toks * hd * 2, "k_prev"},
+                       {v_prev, toks * hd * 2, "v_prev"}, {q, toks * hd * 2, "q"},
+                       {k, toks * hd * 2, "k"},           {v, toks * hd * 2, "v"},
+                       {idx, (size_t)L->heads * nba * ak * 4, "idx"}, {L->m, toks * 4, "m"}};
+    for (size_t i = 0; i < sizeof wr / sizeof wr[0]; ++i) {
+      for (size_t j = i + 1; j < sizeof wr / sizeof wr[0]; ++j)
+        if (overlap(wr[i], wr[j])) return fail(CHIPMUNK_E_SHAPE, "%s overlaps %s", wr[i].name, wr[j].name);
+      for (const Span& r : rd)
+        if (overlap(wr[i], r)) return fail(CHIPMUNK_E_SHAPE, "%s overlaps %s", wr[i].name, r.name);
+    }
+    hipError_t e = chipmunk::launch_attn_reident(q_prev, k_prev, v_prev, q, k, v, idx, L->m, L->num, L->den, L->score,
+                                                 o, L->n, L->heads, kk, L->scale, static_cast<hipStream_t>(stream));
+    return hip_status(e, "re-identifying attention delta launch");
+  } catch (...) {
+    return fail(CHIPMUNK_E_INTERNAL, "internal error in chipmunk_sparse_attn_reident");
   }
 }
 

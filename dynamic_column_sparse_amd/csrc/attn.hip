@@ -35,4 +35,18 @@ hipError_t launch_attn_sparse(bool refresh, const uint16_t* q, const uint16_t* k
   return e;
 }
 
+hipError_t launch_attn_reident(const uint16_t* q_prev, const uint16_t* k_prev, const uint16_t* v_prev,
+                               const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* idx,
+                               const float* m, float* num, float* den, float* score, float* o, int64_t n, int heads,
+                               int kk, float scale, hipStream_t s) {
+  const int64_t nb = row_blocks(n);
+  const dim3 grid((unsigned)(nb * heads));
+  timing_before(K_ATTN_REIDENT, s);
+  hipLaunchKernelGGL(attn_reident, grid, dim3(256), 0, s, q_prev, k_prev, v_prev, q, k, v, idx, m, num, den, score, o,
+                     n, heads, kk, scale);
+  hipError_t e = hipGetLastError();
+  timing_after(K_ATTN_REIDENT, s);
+  return e;
+}
+
 }  // namespace chipmunk

@@ -798,5 +798,319 @@ __global__ __launch_bounds__(256, 2) void attn_sparse(const uint16_t* __restrict
   attn_sparse_body<REFRESH>(blockIdx.x, smem, sIdx, sDen, sDenRest, q, k, v, idx, m, num, den, o, n, heads, kk, scale);
 }
 
+// Sparse step with per-step re-identification, for one (head, query block).
+// The cache holds totals over all keys (as the dense step leaves them), and S
+// may differ from the previous step's.  For the gathered keys S, the share
+// computed from the previous step's q, k, v is taken out of num and den and
+// this step's share is put in; then o = num / den, and each key of S gets the
+// score sum over the block's queries of p_ij / den_i, with den as it stood
+// when the step began.  The keys of S pass through the ring twice, as one
+// sequence of 2 * ceil(kk / 32) chunks: first the previous step's rows (their
+// p enter the sums with a minus sign), then this step's.  Both passes
+// accumulate into the same numerator and denominator registers, and the ring,
+// id ring and load accounting are those of the sparse step over the doubled
+// sequence (every chunk loads its own copy of its 32 ids; the id ring has 16
+// slots so that a chunk's ids outlive its score store).  One Q fragment set
+// is live at a time: the current step's Q rows replace the previous step's
+// right after the scores of the last old chunk are issued (a compiler-visible
+// load there drains the ring once per workgroup).  The scores of new chunk c
+// are a matrix product of this step's p tile (fp16, written to LDS and read
+// back transposed) with 2^14 / den (fp16); the four waves' partial sums meet
+// in LDS and wave 3 stores them one chunk later, after a barrier (those
+// stores are not counted in the waits, which then wait a little longer than
+// needed, never less).
+constexpr int kReidIdSlots = 16;
+
+__device__ __forceinline__ void load_q_frag(QFrag& qf, const uint16_t* row, int lane) {
+#pragma unroll
+  for (int s2 = 0; s2 < 8; ++s2) qf.f[s2] = *(const bf16x8_t*)(row + s2 * 16 + (lane >> 5) * 8);
+}
+
+__global__ __launch_bounds__(256, 2) void attn_reident(
+    const uint16_t* __restrict__ q_prev, const uint16_t* __restrict__ k_prev, const uint16_t* __restrict__ v_prev,
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const int32_t* __restrict__ idx, const float* __restrict__ m, float* __restrict__ num, float* __restrict__ den,
+    float* __restrict__ score, float* __restrict__ o, int64_t n, int heads, int kk, float scale) {
+  constexpr int SK = kSK;
+  constexpr int NSS = 4;
+  constexpr int STAGE = 2 * kTile;
+  constexpr int INS = kIns;
+  constexpr int L = 2 * INS;
+  constexpr int DID = 2 * NSS - 1;
+  constexpr int RID = kReidIdSlots;
+  constexpr int PIECES = kRowBlock * 128 / 4 / 256;
+  constexpr float kW = 16384.f;   // score weights 2^14 / den: normal fp16 for den in [2^-2, 2^28]
+  static_assert((RID & (RID - 1)) == 0 && RID >= DID + 2, "id ring: a new chunk's slot lives until its score store");
+  __shared__ __align__(16) unsigned char smem[NSS * STAGE];
+  __shared__ __align__(16) int sIdx[RID][SK];
+  __shared__ __align__(16) unsigned char sP[4][32 * 64];
+  __shared__ float sSc[2][4][SK];
+  __shared__ float sInv[kRowBlock];
+  __shared__ float sDen[kRowBlock];
+  __shared__ float sDenOld[kRowBlock];
+  const int nb = (int)row_blocks(n);
+  int hh, b;
+  head_block(heads, nb, hh, b, blockIdx.x);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t smem_lds = lds_addr(smem);
+  const int64_t r0 = (int64_t)b * kRowBlock;
+  const int rows = (int)(n - r0 < kRowBlock ? n - r0 : kRowBlock);
+  const int64_t hoff = (int64_t)hh * n;
+  const uint16_t* khp = k_prev + hoff * 128;
+  const uint16_t* vhp = v_prev + hoff * 128;
+  const uint16_t* khn = k + hoff * 128;
+  const uint16_t* vhn = v + hoff * 128;
+  const int32_t* S = idx + ((int64_t)hh * nb + b) * kk;
+  float* srow = score + ((int64_t)hh * nb + b) * n;
+  const int nn = (int)n;
+  const int qi = wave * 32 + (lane & 31);
+  const bool qok = qi < rows;
+  const int qc = qok ? qi : rows - 1;   // clamped row: loads stay unconditional
+  const ChunkGeom geo(wave, lane);
+  const int KR = (kk + SK - 1) / SK;     // chunks of S
+  const int KT = 2 * KR;                 // chunks of the sequence: KR old, then KR new
+
+  auto load_ids = [&](int t, int (&ids)[INS]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < INS; ++i) ids[i] = clamp_index(sIdx[t & (RID - 1)][geo.krow[i]], nn);
+  };
+  // Sequence chunk t's 32 key ids (chunk t mod KR of S) -> ring slot t % RID;
+  // positions past kk read id 0, whose p are masked to 0.
+  auto id_dma = [&](int t) __attribute__((always_inline)) {
+    if (wave == 0 && lane < SK) {
+      const int j = (t < KR ? t : t - KR) * SK + lane;
+      dma4_at(S + (j < kk ? j : 0), lds_addr(&sIdx[t & (RID - 1)][0]));
+    }
+  };
+  // Rows of sequence chunk t from the wave-uniform K / V bases of its step plus
+  // 32-bit byte offsets id * 256 + the lane's chunk (n < 2^24 keeps them exact).
+#define AR_ISSUE(t_, ids_, new_)                                                                       \
+  {                                                                                                    \
+    const uint32_t st_ = smem_lds + ((t_) % NSS) * STAGE;                                              \
+    const uint16_t* kb_ = (new_) ? khn : khp;                                                          \
+    const uint16_t* vb_ = (new_) ? vhn : vhp;                                                          \
+    _Pragma("unroll") for (int i = 0; i < INS; ++i)                                                    \
+        dma16_sa(kb_, (uint32_t)ids_[i] * 256u + (uint32_t)geo.koff[i] * 2u, st_ + (wave * INS + i) * 1024); \
+    _Pragma("unroll") for (int i = 0; i < INS; ++i)                                                    \
+        dma16_sa(vb_, (uint32_t)ids_[i] * 256u + (uint32_t)geo.voff[i] * 2u,                           \
+                 st_ + kTile + (wave * INS + i) * 1024);                                               \
+  }
+  // Wave 3 stores the scores of new chunk c (lanes 0..31: one key each); its
+  // ids are in the slot of sequence chunk KR + c.
+  auto store_scores = [&](int c) __attribute__((always_inline)) {
+    if (wave == 3 && lane < SK) {
+      const int j = c * SK + lane;
+      if (j < kk) {
+        const float (*ps)[SK] = sSc[c & 1];
+        srow[clamp_index(sIdx[(KR + c) & (RID - 1)][lane], nn)] = ps[0][lane] + ps[1][lane] + ps[2][lane] + ps[3][lane];
+      }
+    }
+  };
+
+  QFrag qf;
+  const float mrow = m[hoff + r0 + qc];
+  const float drow = den[hoff + r0 + qc];
+  f32x16_t acc[4];
+#pragma unroll
+  for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[ni][r] = 0.f;
+  float dpart = 0.f;
+
+  if (KT > 0) {
+    if (wave == 0 && lane < SK) {
+#pragma unroll
+      for (int t = 0; t < DID; ++t)
+        if (t < KT) {
+          const int j = (t < KR ? t : t - KR) * SK + lane;
+          dma4_at(S + (j < kk ? j : 0), lds_addr(&sIdx[t][0]));
+        }
+    }
+    wait_vmcnt<0>();
+    __syncthreads();
+    // The previous step's Q rows go out before the first stages (their first
+    // use, before the loop, then waits for them once).
+    load_q_frag(qf, q_prev + (hoff + r0 + qc) * 128, lane);
+    int ids_a[INS], ids_b[INS];
+#pragma unroll
+    for (int t = 0; t < NSS - 1; ++t) {
+      if (t < KT) {
+        load_ids(t, ids_a);
+        AR_ISSUE(t, ids_a, t >= KR);
+      }
+    }
+    if (NSS - 1 < KT) load_ids(NSS - 1, ids_a);
+    {
+      const int ahead = (KT - 1) < (NSS - 2) ? (KT - 1) : (NSS - 2);
+      wait_vmcnt_upto<(NSS - 2) * L>(ahead * L);
+      barrier();
+    }
+    // Score weights of this wave's queries (rows past the block end weigh 0),
+    // in the order p_operand delivers the queries; written and read back by
+    // the same wave.
+    if (lane < 32) sInv[qi] = qok ? 1.f / drow : 0.f;
+    f16x8_t wq[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const float* w = sInv + wave * 32 + kb * 16 + (lane >> 5) * 8;
+      const uint4 pk = make_uint4(pack2h(w[0] * kW, w[1] * kW), pack2h(w[2] * kW, w[3] * kW),
+                                  pack2h(w[4] * kW, w[5] * kW), pack2h(w[6] * kW, w[7] * kW));
+      wq[kb] = __builtin_bit_cast(f16x8_t, pk);
+    }
+    const float sl2 = scale * 1.4426950408889634f, ml2 = mrow * 1.4426950408889634f;
+    f32x16_t sacc = chunk_scores(smem, qf, lane);
+    // With a single old chunk, this step's Q rows are due for chunk 1 already.
+    if (KR == 1) load_q_frag(qf, q + (hoff + r0 + qc) * 128, lane);
+    unsigned char* pw = sP[wave];
+    const int pq = lane & 31, ph = lane >> 5;
+
+    // Iteration t: scores of chunk t+1, then the exponentials and value
+    // products of chunk t.  NEW: chunk t is one of this step's.  STEADY: every
+    // stage, id and score issue happens, chunk t is full, and chunks t+1 and
+    // t+NSS-1 belong to the same step as chunk t.
+    auto body = [&](int t, auto NEW, auto STEADY) __attribute__((always_inline)) {
+      constexpr bool steady = decltype(STEADY)::value;
+      constexpr bool cur_new = decltype(NEW)::value;
+      const int c = cur_new ? t - KR : t;   // chunk of S
+      f32x16_t snext;
+      if (steady || t + 1 < KT) {
+        if (steady) {
+          if (wave == 0 && t >= 1)
+            wait_vmcnt<L + 1>();
+          else
+            wait_vmcnt<L>();
+        } else {
+          // Stage t+1 must be complete.  Newer than it: the stages after it
+          // already issued, and on wave 0 the id loads of iterations
+          // t-NSS+3 .. t-1.
+          const int issued_to = (t + NSS - 2) < (KT - 1) ? (t + NSS - 2) : (KT - 1);
+          int newer = (issued_to - (t + 1)) * L;
+          if (wave == 0) {
+            const int j0 = t - NSS + 3 > 0 ? t - NSS + 3 : 0;
+            const int j1 = (t - 1) < (KT - DID - 1) ? (t - 1) : (KT - DID - 1);
+            newer += j1 >= j0 ? j1 - j0 + 1 : 0;
+          }
+          wait_vmcnt_upto<(NSS - 2) * L + NSS>(newer);
+        }
+        barrier();
+        // Every wave's partial scores of new chunk c-1 are in LDS.
+        if (cur_new && c >= 1) store_scores(c - 1);
+        if (steady || t + DID < KT) id_dma(t + DID);
+        if (steady) {
+          AR_ISSUE(t + NSS - 1, ids_a, cur_new);
+        } else if (t + NSS - 1 < KT) {
+          AR_ISSUE(t + NSS - 1, ids_a, t + NSS - 1 >= KR);
+        }
+        if (steady || t + NSS < KT) load_ids(t + NSS, ids_b);
+        snext = chunk_scores(smem + ((t + 1) % NSS) * STAGE, qf, lane);
+        // After the scores of the last old chunk: this step's Q rows.
+        if (!cur_new && !steady && t + 2 == KR) load_q_frag(qf, q + (hoff + r0 + qc) * 128, lane);
+      }
+      const unsigned char* st = smem + (t % NSS) * STAGE;
+      float p[16];
+      if (steady || c * SK + SK <= kk) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], sl2, -ml2));
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int j = c * SK + acc_key(r, lane);
+          p[r] = j < kk ? __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], sl2, -ml2)) : 0.f;
+        }
+      }
+      float psum = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) psum += p[r];
+      dpart += cur_new ? psum : -psum;
+      constexpr float sg = cur_new ? 1.f : -1.f;
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const uint4 pk = make_uint4(pack2(sg * p[hf * 8 + 0], sg * p[hf * 8 + 1]),
+                                    pack2(sg * p[hf * 8 + 2], sg * p[hf * 8 + 3]),
+                                    pack2(sg * p[hf * 8 + 4], sg * p[hf * 8 + 5]),
+                                    pack2(sg * p[hf * 8 + 6], sg * p[hf * 8 + 7]));
+        if (cur_new) {
+          // This lane's keys 8*(2hf) + 4*ph .. +3 and 8*(2hf+1) + 4*ph .. +3 of
+          // query pq, in fp16 for the score products.
+          *(uint2*)(pw + pq * 64 + (p_unit(4 * hf + ph, pq) << 3)) =
+              make_uint2(pack2h(p[hf * 8 + 0], p[hf * 8 + 1]), pack2h(p[hf * 8 + 2], p[hf * 8 + 3]));
+          *(uint2*)(pw + pq * 64 + (p_unit(4 * hf + 2 + ph, pq) << 3)) =
+              make_uint2(pack2h(p[hf * 8 + 4], p[hf * 8 + 5]), pack2h(p[hf * 8 + 6], p[hf * 8 + 7]));
+        }
+        const bf16x8_t pa = __builtin_bit_cast(bf16x8_t, pk);
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) {
+          const bf16x8_t vb = tr_operand_swz(st + kTile, 256, hf * 16, ni * 32, lane);
+          acc[ni] = mfma32(pa, vb, acc[ni]);
+        }
+      }
+      if (cur_new) {
+        f32x16_t sc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sc[r] = 0.f;
+        sc = mfma32h(wq[0], p_operand(pw, 0, lane), sc);
+        sc = mfma32h(wq[1], p_operand(pw, 16, lane), sc);
+        if (lane < 32) sSc[c & 1][wave][lane] = sc[0] * (1.f / kW);
+      }
+      if (steady || t + 1 < KT) {
+        sacc = snext;
+#pragma unroll
+        for (int i = 0; i < INS; ++i) ids_a[i] = ids_b[i];
+      }
+    };
+    int t = 0;
+    // Old chunks: steady while chunks t .. t+NSS-1 are all old (then chunk t is
+    // not the last old one, so it is full, and t + DID < KT).
+    for (; t + NSS - 1 < KR; ++t) body(t, std::false_type{}, std::true_type{});
+    for (; t < KR; ++t) body(t, std::false_type{}, std::false_type{});
+    for (; t + DID < KT; ++t) body(t, std::true_type{}, std::true_type{});
+    for (; t < KT; ++t) body(t, std::true_type{}, std::false_type{});
+  }
+#undef AR_ISSUE
+  dpart += __shfl_xor(dpart, 32);
+  // Epilogue through the idle ring, as in the sparse step: the numerator change
+  // goes to LDS as fp32 [128 rows][128 columns], then every thread updates
+  // whole 16-byte pieces of num and stores o.
+  __syncthreads();
+  // Score stores not yet done: the last new chunk's, and the one before it,
+  // due at the final iteration (which has no barrier).
+  if (KR >= 2) store_scores(KR - 2);
+  if (KR >= 1) store_scores(KR - 1);
+  float* sacc_t = (float*)smem;
+  if (lane < 32) {
+    sDen[qi] = dpart;
+    sDenOld[qi] = drow;
+  }
+#pragma unroll
+  for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int qr = wave * 32 + acc_key(r, lane);
+      const int cc = ni * 32 + (lane & 31);
+      sacc_t[qr * 128 + (((cc >> 2) ^ (((qr >> 2) & 1) << 3)) << 2) + (cc & 3)] = acc[ni][r];
+    }
+  float4 rest[PIECES];
+#pragma unroll
+  for (int it = 0; it < PIECES; ++it) {
+    const int e = it * 256 + tid, qr = e >> 5, c4 = e & 31;
+    const int qrc = qr < rows ? qr : rows - 1;
+    rest[it] = *(const float4*)(num + (hoff + r0 + qrc) * 128 + c4 * 4);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int it = 0; it < PIECES; ++it) {
+    const int e = it * 256 + tid, qr = e >> 5, c4 = e & 31;
+    if (qr >= rows) continue;
+    const float4 a = *(const float4*)(sacc_t + qr * 128 + ((c4 ^ (((qr >> 2) & 1) << 3)) << 2));
+    const int64_t g = (hoff + r0 + qr) * 128 + c4 * 4;
+    const float4 nw = make_float4(rest[it].x + a.x, rest[it].y + a.y, rest[it].z + a.z, rest[it].w + a.w);
+    const float dt = sDenOld[qr] + sDen[qr];
+    *(float4*)(num + g) = nw;
+    *(float4*)(o + g) = make_float4(nw.x / dt, nw.y / dt, nw.z / dt, nw.w / dt);
+  }
+  if (tid < rows) den[hoff + r0 + tid] = sDenOld[tid] + sDen[tid];
+}
+
 }  // namespace
 }  // namespace chipmunk

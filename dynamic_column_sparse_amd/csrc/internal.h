@@ -23,6 +23,7 @@ enum KernelId {
   K_ATTN_SPARSE,
   K_ATTN_REFRESH,
   K_SPARSE_STEP_FUSED,
+  K_ATTN_REIDENT,
   K_COUNT
 };
 const char* kernel_name(int kid);
@@ -55,6 +56,11 @@ hipError_t launch_attn_dense(const uint16_t* q, const uint16_t* k, const uint16_
 hipError_t launch_attn_sparse(bool refresh, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                               const int32_t* idx, const float* m, float* num, float* den, float* o, int64_t n,
                               int heads, int kk, float scale, hipStream_t s);
+// Sparse attention step with per-step re-identification (num, den hold totals).
+hipError_t launch_attn_reident(const uint16_t* q_prev, const uint16_t* k_prev, const uint16_t* v_prev,
+                               const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* idx,
+                               const float* m, float* num, float* den, float* score, float* o, int64_t n, int heads,
+                               int kk, float scale, hipStream_t s);
 // Sparse MLP phase 1, then one kernel with the MLP phase-2 tiles first and the
 // sparse attention units after them (k = 0: attention units only).
 hipError_t launch_sparse_step(const uint16_t* x, const uint16_t* w1t, const float* b1, const int32_t* midx,

@@ -11,6 +11,10 @@ their coefficients, then recompute a chosen subset each step):
   attention  refresh: dense step (m, num, den, o, key-mass scores), identify the
              top-k keys per query block, then REFRESH (num, den keep only the
              part outside S); sparse: the sparse delta writes o.
+             With reident=True: the refresh is the dense step alone (num, den
+             keep totals); each sparse step identifies S from the latest
+             scores, then swaps S's previous-step share for this step's and
+             rescores S (chipmunk_sparse_attn_reident).
 """
 from __future__ import annotations
 
@@ -71,10 +75,15 @@ class MLPDelta:
 
 
 class AttnDelta:
-    """One attention layer (all heads), head_dim 128; kk kept keys per query block."""
+    """One attention layer (all heads), head_dim 128; kk kept keys per query block.
+    reident=True: S is identified anew at every sparse step; the layer then
+    keeps references to the previous step's q, k, v, which the caller must
+    leave unmodified until the next step."""
 
-    def __init__(self, n: int, heads: int, kk: int, device, scale=None):
+    def __init__(self, n: int, heads: int, kk: int, device, scale=None, reident=False):
         self.n, self.heads, self.kk = n, heads, kk
+        self.reident = reident
+        self.prev = None
         self.nb = row_blocks(n)
         self.scale = 1.0 / math.sqrt(lib.HEAD_DIM) if scale is None else scale
         f32 = dict(dtype=torch.float32, device=device)
@@ -100,8 +109,21 @@ class AttnDelta:
         lib.chipmunk_sparse_attn_delta(self.layer, q, k, v, self.idx if idx is None else idx, self.kk,
                                        lib.ATTN_SPARSE, self.o, stream=stream)
 
+    def reident_sparse(self, q, k, v, idx=None, stream=None):
+        qp, kp, vp = self.prev
+        lib.chipmunk_sparse_attn_reident(self.layer, qp, kp, vp, q, k, v, self.idx if idx is None else idx,
+                                         self.kk, self.o, stream=stream)
+        self.prev = (q, k, v)
+
     def step(self, q, k, v, refresh: bool, stream=None):
-        if refresh:
+        if self.reident:
+            if refresh:
+                self.dense(q, k, v, stream)
+                self.prev = (q, k, v)
+            else:
+                self.identify(stream)
+                self.reident_sparse(q, k, v, stream=stream)
+        elif refresh:
             self.dense(q, k, v, stream)
             self.identify(stream)
             self.refresh_rest(q, k, v, stream=stream)

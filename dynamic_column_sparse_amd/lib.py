@@ -26,7 +26,8 @@ STATUS = {0: "CHIPMUNK_OK", 1: "CHIPMUNK_E_NULLPTR", 2: "CHIPMUNK_E_SHAPE", 3: "
           4: "CHIPMUNK_E_ALIGN", 5: "CHIPMUNK_E_WORKSPACE", 6: "CHIPMUNK_E_HIP", 7: "CHIPMUNK_E_INTERNAL"}
 
 EXPORTS = ("chipmunk_dense_step", "chipmunk_identify_topk", "chipmunk_sparse_mlp_delta",
-           "chipmunk_sparse_attn_delta", "chipmunk_sparse_step", "chipmunk_cache_writeback",
+           "chipmunk_sparse_attn_delta", "chipmunk_sparse_attn_reident", "chipmunk_sparse_step",
+           "chipmunk_cache_writeback",
            "chipmunk_workspace_bytes",
            "chipmunk_last_error", "chipmunk_abi_version", "chipmunk_timing_enable", "chipmunk_timing_read",
            "chipmunk_kernel_count", "chipmunk_kernel_name")
@@ -64,6 +65,7 @@ def _load() -> ctypes.CDLL:
         "chipmunk_identify_topk": (ctypes.c_int, [vp, i64, i64, i32, vp, vp, sz, vp]),
         "chipmunk_sparse_mlp_delta": (ctypes.c_int, [vp, vp, vp, i32, vp, vp, vp, sz, vp]),
         "chipmunk_sparse_attn_delta": (ctypes.c_int, [vp, vp, vp, vp, vp, i32, ctypes.c_int, vp, vp]),
+        "chipmunk_sparse_attn_reident": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp]),
         "chipmunk_sparse_step": (ctypes.c_int, [vp, vp, vp, i32, vp, vp, vp, sz,
                                                  vp, vp, vp, vp, vp, i32, vp, vp]),
         "chipmunk_cache_writeback": (ctypes.c_int, [vp, vp, vp, i32, vp]),
@@ -161,6 +163,11 @@ def chipmunk_sparse_mlp_delta(layer: MLPLayer, x, idx, k: int, y, a_new_packed=N
 def chipmunk_sparse_attn_delta(layer: AttnLayer, q, k, v, idx, kk: int, mode: int, o=None, stream=None):
     _check(_lib.chipmunk_sparse_attn_delta(ctypes.byref(layer), _ptr(q), _ptr(k), _ptr(v), _ptr(idx), kk, mode,
                                            _ptr(o), _stream(stream)))
+
+
+def chipmunk_sparse_attn_reident(layer: AttnLayer, q_prev, k_prev, v_prev, q, k, v, idx, kk: int, o, stream=None):
+    _check(_lib.chipmunk_sparse_attn_reident(ctypes.byref(layer), _ptr(q_prev), _ptr(k_prev), _ptr(v_prev), _ptr(q),
+                                             _ptr(k), _ptr(v), _ptr(idx), kk, _ptr(o), _stream(stream)))
 
 
 def chipmunk_sparse_step(mlp: MLPLayer, x, mlp_idx, k: int, y, a_new_packed, ws, attn: AttnLayer, q, kx, v,

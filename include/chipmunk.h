@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define CHIPMUNK_ABI_VERSION 2
+#define CHIPMUNK_ABI_VERSION 3
 #define CHIPMUNK_ROW_BLOCK 128
 #define CHIPMUNK_HEAD_DIM 128
 
@@ -201,6 +201,32 @@ int chipmunk_sparse_mlp_delta(const chipmunk_mlp* layer, const uint16_t* x, cons
 int chipmunk_sparse_attn_delta(const chipmunk_attn* layer, const uint16_t* q, const uint16_t* k,
                                const uint16_t* v, const int32_t* idx, int32_t kk, int mode, float* o,
                                void* stream);
+
+/* Sparse attention step with per-step re-identification (Chipmunk post,
+ * Activation Deltas section: the vectors to recompute are chosen anew in each
+ * step, and a step swaps the earlier step's chosen vectors for its own).  Here
+ * num and den hold TOTALS over all keys, as chipmunk_dense_step(CHIPMUNK_ATTN)
+ * leaves them (no REFRESH call), and S = idx[h*nb + b] may change from step to
+ * step (typically chipmunk_identify_topk on the layer's scores, run before each
+ * step).  Per head h and query block b, with the refresh row max m:
+ *   p_old = exp(scale q_prev_b K_prev[S]^T - m)   (the previous step's share)
+ *   p_new = exp(scale q_b K[S]^T - m)             (this step's share)
+ *   num <- num - p_old V_prev[S] + p_new V[S],  den <- den - sum p_old + sum p_new
+ *   o    = num / den
+ *   score[h][b][j] <- sum over the block's rows of p_new / den_before, j in S
+ *                     (den_before: den when the call starts); other scores kept.
+ * The bf16 products use p rounded to bf16 (p_old negated exactly); den sums
+ * the fp32 p; the scores are fp32 sums of fp16 p times fp16 2^14 / den_before
+ * (den_before must lie in [2^-2, 2^28], which holds while the row max is
+ * close to the refresh's).  q_prev, k_prev, v_prev are the previous step's
+ * inputs (the dense step's for the first sparse step); they may be the same
+ * buffers as q, k, v.  layer->score is required.  No buffer the call writes
+ * (o, num, den, score) may overlap another buffer of the call:
+ * CHIPMUNK_E_SHAPE.  kk = 0 writes o = num / den and leaves num, den and score
+ * as they are.  Shapes, alignment and kk as for chipmunk_sparse_attn_delta. */
+int chipmunk_sparse_attn_reident(const chipmunk_attn* layer, const uint16_t* q_prev, const uint16_t* k_prev,
+                                 const uint16_t* v_prev, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                 const int32_t* idx, int32_t kk, float* o, void* stream);
 
 /* Both sparse deltas of one step in two launches: chipmunk_sparse_mlp_delta on
  * `mlp` and chipmunk_sparse_attn_delta(mode = CHIPMUNK_ATTN_SPARSE) on `attn`,

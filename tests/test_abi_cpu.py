@@ -27,7 +27,8 @@ def _declared():
 def test_header_declares_the_entry_points():
     decl = _declared()
     for name in ("chipmunk_dense_step", "chipmunk_identify_topk", "chipmunk_sparse_mlp_delta",
-                 "chipmunk_sparse_attn_delta", "chipmunk_cache_writeback", "chipmunk_sparse_step"):
+                 "chipmunk_sparse_attn_delta", "chipmunk_cache_writeback", "chipmunk_sparse_step",
+                 "chipmunk_sparse_attn_reident"):
         assert name in decl
 
 
@@ -41,9 +42,10 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_names_workspace(L):
-    assert L.chipmunk_abi_version() == 2
+    assert L.chipmunk_abi_version() == 3
     names = L.kernel_names()
     assert "mlp_gemm1_sparse" in names and "attn_sparse" in names and "topk_rows" in names
+    assert "attn_reident" in names
     assert L.chipmunk_workspace_bytes(L.OP_SPARSE_MLP, 4352, 3072, 12288, 3686) == 34 * 3712 * 128 * 2
     assert L.chipmunk_workspace_bytes(L.OP_SPARSE_MLP, 300, 128, 640, 0) == 0
     assert L.chipmunk_workspace_bytes(L.OP_DENSE_MLP, 300, 128, 640, 200) == 0
@@ -163,6 +165,29 @@ def test_sparse_step_checks(L):
     assert call(q=base["ws"] + 4096) == 2         # the MLP's workspace inside q
     assert call(o=base["x"] + 16) == 2            # o over the MLP's input
     assert call(num=base["a_cache"]) == 2         # the attention cache over the MLP cache
+
+
+def test_reident_checks(L):
+    base = {name: FAKE + i * (1 << 32) for i, name in enumerate(
+        ("m", "num", "den", "score", "qp", "kp", "vp", "q", "k", "v", "idx", "o"))}
+
+    def call(kk=100, n=300, heads=2, **over):
+        a = {**base, **over}
+        att = L.attn_layer(n, heads, a["m"], a["num"], a["den"], a["score"])
+        return _code(L, L.chipmunk_sparse_attn_reident, att, a["qp"], a["kp"], a["vp"], a["q"], a["k"], a["v"],
+                     a["idx"], kk, a["o"], stream=0)
+
+    assert call(kk=301) == 2 and call(kk=-1) == 2
+    assert call(o=None) == 1 and call(qp=None) == 1 and call(vp=None) == 1 and call(idx=None) == 1
+    assert call(score=None) == 1                  # the step rescores its keys
+    assert call(kp=base["kp"] + 2) == 4           # misaligned
+    assert call(o=base["num"]) == 2               # written buffers must not overlap
+    assert "overlaps" in L.chipmunk_last_error()
+    assert call(num=base["k"] + 256) == 2         # nor overlap an input
+    assert call(score=base["den"] + 4) == 2
+    assert call(n=1 << 24) == 2                   # 32-bit gathered row offsets
+    # the previous step's inputs may be the current ones (read-only)
+    assert call(qp=base["q"], kp=base["k"], vp=base["v"], kk=-1) == 2   # still fails on kk alone
 
 
 def test_timer_api_without_launches(L):

@@ -1,0 +1,141 @@
+"""chipmunk_sparse_attn_reident: attention sparse steps that identify their keys
+anew at every step (reading R13: the cache keeps totals; a step swaps the chosen
+keys' previous-step share for this step's and rescores them).
+
+Per step, against the oracle (attn_dense for the refresh, attn_reident for each
+sparse step), with the GPU's own index sets so both sides stay in lockstep:
+  * the index sets equal the oracle's top-k of the GPU's fp32 score bits;
+  * o and num within rel. Frobenius 2e-2, den within 1e-3;
+  * the rescored keys' scores within 2e-3 (fp16 products, fp32 sums) and every
+    other score bit-unchanged.
+Shapes cover ragged blocks, S shorter than one, two or three 32-key chunks and
+long enough for the steady loop, kk = n, kk = 0, head counts with and without
+the XCD head mapping, and the FLUX.1-dev shape on sampled (head, query block)
+slices in the launch configuration the benchmark times.  Unchanged inputs must
+leave the cache as it is (to fp32 rounding), and repeated runs are bit-identical.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic as syn
+from tests.gpu_helpers import up_bf16
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-2
+SCALE = 1.0 / np.sqrt(128.0)
+RB = 128
+
+
+def _check_scores(g_after, g_before, ref, sidx, where):
+    """Row-wise: keys in S match the oracle; the others keep their bits."""
+    for r in range(g_after.shape[0]):
+        s = sidx[r]
+        np.testing.assert_allclose(g_after[r, s], ref[r, s], rtol=2e-3, atol=1e-6, err_msg=f"{where} row {r}")
+        keep = np.ones(g_after.shape[1], bool)
+        keep[s] = False
+        np.testing.assert_array_equal(g_after[r, keep].view(np.int32), g_before[r, keep].view(np.int32),
+                                      err_msg=f"{where} row {r}: a score outside S changed")
+
+
+def _run(n, H, kk, steps, slices, seed):
+    """Refresh at step 0, then `steps` re-identifying sparse steps; the oracle
+    follows every (head, block) slice in `slices` (None: every slice)."""
+    from dynamic_column_sparse_amd.layers import AttnDelta
+    nb = (n + RB - 1) // RB
+    if slices is None:
+        slices = [(hh, b) for hh in range(H) for b in range(nb)]
+    walks = [syn.heads_walk(seed, tag, steps + 1, H, n) for tag in "QKV"]
+    att = AttnDelta(n, H, kk, "cuda", reident=True)
+    gq = [[up_bf16(w[t]) for w in walks] for t in range(steps + 1)]
+    att.step(*gq[0], refresh=True)
+    torch.cuda.synchronize()
+    state = {}
+    for (hh, b) in slices:
+        r0, r1 = b * RB, min(n, (b + 1) * RB)
+        q = oracle.from_bf16_bits(walks[0][0][hh, r0:r1])
+        kx, vx = (oracle.from_bf16_bits(w[0][hh]) for w in walks[1:])
+        m, den, num, o, score = oracle.attn_dense(q, kx, vx, SCALE)
+        assert oracle.rel_frobenius(att.o[hh, r0:r1].cpu().numpy(), o) < TOL
+        state[(hh, b)] = (m, num, den, score)
+    sets = []
+    for t in range(1, steps + 1):
+        before = att.score.cpu().numpy()
+        att.step(*gq[t], refresh=False)
+        torch.cuda.synchronize()
+        g_idx = att.idx.cpu().numpy()[:, :kk]
+        sets.append(g_idx.copy())
+        np.testing.assert_array_equal(g_idx, oracle.identify_topk(before.reshape(H * nb, n), kk))
+        after = att.score.cpu().numpy()
+        o_g, num_g, den_g = att.o.cpu().numpy(), att.num.cpu().numpy(), att.den.cpu().numpy()
+        worst = 0.0
+        for (hh, b) in slices:
+            r0, r1 = b * RB, min(n, (b + 1) * RB)
+            qp, q = (oracle.from_bf16_bits(walks[0][s][hh, r0:r1]) for s in (t - 1, t))
+            kp, kx = (oracle.from_bf16_bits(walks[1][s][hh]) for s in (t - 1, t))
+            vp, vx = (oracle.from_bf16_bits(walks[2][s][hh]) for s in (t - 1, t))
+            m, num, den, score = state[(hh, b)]
+            sidx = g_idx[hh * nb + b][None]
+            o, num, den, score = oracle.attn_reident(qp, kp, vp, q, kx, vx, m, num, den, score, sidx, SCALE)
+            state[(hh, b)] = (m, num, den, score)
+            where = f"step {t} head {hh} block {b}"
+            e = oracle.rel_frobenius(o_g[hh, r0:r1], o)
+            worst = max(worst, e)
+            assert e < TOL, f"{where}: o {e:.2e}"
+            assert oracle.rel_frobenius(num_g[hh, r0:r1], num) < TOL, f"{where}: num"
+            assert oracle.rel_frobenius(den_g[hh, r0:r1], den) < 1e-3, f"{where}: den"
+            _check_scores(after[hh, b][None], before[hh, b][None], score, sidx, where)
+        print(f"  step {t}: {len(slices)} slices ok, worst o rel-F {worst:.2e}", flush=True)
+    return sets
+
+
+@pytest.mark.parametrize("n,H,kk", [
+    (300, 2, 100),     # ragged last block; 4 chunks of S (one steady old iteration)
+    (600, 3, 200),     # 7 chunks
+    (1000, 8, 300),    # XCD head mapping, 10 chunks
+    (129, 1, 129),     # every key (o is dense attention on each step's inputs)
+    (33, 1, 5),        # one partial chunk
+    (200, 2, 40),      # two chunks
+    (256, 2, 96),      # three full chunks
+    (300, 2, 0),       # kk = 0: o = num / den, cache and scores unchanged
+])
+def test_reident_steps_match_oracle(gpu_lib, n, H, kk):
+    print(f"re-identifying attention n={n} H={H} kk={kk}", flush=True)
+    sets = _run(n, H, kk, steps=3, slices=None, seed=9)
+    if 0 < kk < n // 2 and H * ((n + RB - 1) // RB) >= 6:
+        # the point of the mode: the chosen keys move between steps
+        assert any(not np.array_equal(a, b) for a, b in zip(sets, sets[1:])), "S never changed"
+
+
+def test_reident_flux_sampled(gpu_lib):
+    # FLUX.1-dev shape: 4352 tokens, 24 heads x 128, keep 718 keys per query
+    # block; refresh, then three re-identifying sparse steps.
+    g = np.random.default_rng(23)
+    slices = [(int(g.integers(24)), int(g.integers(34))) for _ in range(3)] + [(23, 33)]
+    print(f"re-identifying attention, FLUX shape, slices {slices}", flush=True)
+    _run(4352, 24, 718, steps=3, slices=slices, seed=0)
+
+
+def test_reident_unchanged_inputs_keep_cache_and_is_deterministic(gpu_lib):
+    from dynamic_column_sparse_amd.layers import AttnDelta
+    n, H, kk = 700, 3, 150
+    print(f"re-identifying attention on unchanged inputs n={n} H={H} kk={kk}", flush=True)
+    qkv = [up_bf16(a) for a in (syn.heads_activations(5, t, 0, H, n) for t in "QKV")]
+    runs = []
+    for _ in range(2):
+        att = AttnDelta(n, H, kk, "cuda", reident=True)
+        att.step(*qkv, refresh=True)
+        torch.cuda.synchronize()
+        o0, num0, den0, sc0 = att.o.clone(), att.num.clone(), att.den.clone(), att.score.clone()
+        att.step(*qkv, refresh=False)      # previous inputs = these inputs
+        torch.cuda.synchronize()
+        assert oracle.rel_frobenius(att.num.cpu().numpy(), num0.cpu().numpy()) < 1e-5
+        assert oracle.rel_frobenius(att.den.cpu().numpy(), den0.cpu().numpy()) < 1e-6
+        assert oracle.rel_frobenius(att.o.cpu().numpy(), o0.cpu().numpy()) < 1e-5
+        # S's new scores are the refresh's own (the same p and den), to the
+        # precision of the fp16 score products
+        np.testing.assert_allclose(att.score.cpu().numpy(), sc0.cpu().numpy(), rtol=2e-3, atol=1e-6)
+        runs.append([x.clone() for x in (att.o, att.num, att.den, att.score, att.idx)])
+    for a, b in zip(*runs):
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32))
