@@ -50,6 +50,11 @@ design notes of this repository):
       keys' share as computed from the previous step's q, k, v out of them and puts
       the share from this step's q, k, v in, and sets those keys' scores to this
       step's probability mass over the denominator held at the start of the step.
+  R14 optional fp8 variant of the MLP's first product: x and W1^T become e4m3 codes
+      row by row, each row with the smallest power-of-two scale that brings its
+      largest magnitude within 448, rounded to nearest even; the product (dense and
+      sparse) takes those values, and everything after it is unchanged.  The fp8
+      MLP is mlp_dense / mlp_sparse applied to fp8_rows(x) and fp8_rows(w1t).
 
 Parity pins for every function live in ``tests/test_oracle_*.py``.
 """
@@ -90,6 +95,86 @@ def from_bf16_bits(b) -> np.ndarray:
     u = np.asarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
     with np.errstate(invalid="ignore"):
         return u.view(np.float32).astype(np.float64)
+
+
+# --------------------------------------------------------------------------- #
+# FP8 operands (the fp8 variant of the MLP's first product)
+# --------------------------------------------------------------------------- #
+E4M3_MAX = 448.0
+
+
+def fp8_e4m3_round(v) -> np.ndarray:
+    """Nearest OCP fp8 e4m3 ("fn": 4 exponent bits with bias 7, 3 mantissa bits,
+    no infinities, largest finite value 448) value of each element, ties to the
+    even code, as float64.  Normal values are 2**(E-7) (1 + m/8) for E in 1..15;
+    below 2**-6 the spacing is 2**-9 (subnormals).  Inputs must satisfy
+    |v| <= 448 (the quantizer scales rows into that range)."""
+    v = np.asarray(v, dtype=np.float64)
+    assert np.all(np.abs(v) <= E4M3_MAX), "value outside the e4m3 range"
+    a = np.abs(v)
+    _, ex = np.frexp(a)                          # a = mant * 2**ex, 0.5 <= mant < 1: binade 2**(ex-1)
+    # quantum: 2**(ex-1-3) in a normal binade, 2**-9 below 2**-6
+    q = np.where(a >= 2.0 ** -6, np.ldexp(1.0, ex - 4), 2.0 ** -9)
+    r = np.rint(a / q) * q                       # np.rint: half to even (even quotient = even code)
+    return np.copysign(r, v)
+
+
+def fp8_e4m3_decode(codes) -> np.ndarray:
+    """float64 values of e4m3 codes (0x7f / 0xff are NaN)."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    s = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 15
+    m = c & 7
+    mag = np.where(e == 0, np.ldexp(m.astype(np.float64), -9), np.ldexp(1.0 + m / 8.0, e - 7))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return s * mag
+
+
+def fp8_e4m3_encode(v) -> np.ndarray:
+    """e4m3 codes (uint8) of fp8_e4m3_round(v); -0 keeps its sign bit."""
+    r = fp8_e4m3_round(v)
+    a = np.abs(r)
+    mant, ex = np.frexp(a)
+    normal = a >= 2.0 ** -6
+    eb = np.where(normal, ex - 1 + 7, 0)
+    m = np.where(normal, np.rint((2.0 * mant - 1.0) * 8), np.rint(a * 2.0 ** 9)).astype(np.int64)
+    sign = np.signbit(r).astype(np.int64) << 7
+    return (sign | (eb.astype(np.int64) << 3) | m).astype(np.uint8)
+
+
+def fp8_row_exponent(amax) -> np.ndarray:
+    """Per-row scale exponent e: the smallest integer with amax * 2**-e <= 448,
+    at least -126; e = 0 for an all-zero row.  With amax = mant * 2**ex
+    (0.5 <= mant < 1) and 448 = 0.875 * 2**9 that is ex - 9, plus one when
+    mant > 0.875."""
+    amax = np.asarray(amax, dtype=np.float64)
+    assert np.all(np.isfinite(amax)) and np.all(amax >= 0)
+    mant, ex = np.frexp(amax)
+    e = ex.astype(np.int64) - 9 + (mant > 0.875)
+    e = np.maximum(e, -126)
+    return np.where(amax > 0, e, 0)
+
+
+def quantize_fp8_rows(a):
+    """Row-wise fp8 quantization: each row gets the power-of-two scale 2**e of
+    fp8_row_exponent(max |row|) and its elements become e4m3 codes of
+    a * 2**-e (exact scaling, then round to nearest even).  Returns (codes uint8
+    [rows, cols], scale bytes uint8 [rows] = 127 + e, the E8M0 encoding of 2**e)."""
+    a = np.asarray(a, dtype=np.float64)
+    e = fp8_row_exponent(np.abs(a).max(axis=1) if a.shape[1] else np.zeros(a.shape[0]))
+    codes = fp8_e4m3_encode(np.ldexp(a, -e[:, None]))
+    return codes, (e + 127).astype(np.uint8)
+
+
+def dequantize_fp8_rows(codes, scale_bytes) -> np.ndarray:
+    """float64 values code * 2**(scale byte - 127), row by row."""
+    e = np.asarray(scale_bytes, dtype=np.int64) - 127
+    return np.ldexp(fp8_e4m3_decode(codes), e[:, None])
+
+
+def fp8_rows(a) -> np.ndarray:
+    """The values an fp8 operand carries: dequantize_fp8_rows(quantize_fp8_rows(a))."""
+    return dequantize_fp8_rows(*quantize_fp8_rows(a))
 
 
 # --------------------------------------------------------------------------- #
