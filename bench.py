@@ -28,6 +28,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak (published)
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 matrix peak (published)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E bandwidth (published)
 HEAD_DIM = 128
 
@@ -59,12 +60,15 @@ def flops_attn(w, reident=False):
     return (8.0 if reident else 4.0) * w["n"] * w["kk"] * HEAD_DIM * w["heads"]
 
 
-def kernel_work(name, w, reident=False):
-    """(amount, bound) of algorithmic work in ONE launch of kernel `name`."""
+def kernel_work(name, w, reident=False, fp8=False):
+    """(amount, bound) of algorithmic work in ONE launch of kernel `name`
+    (bound "mfma": bf16 matrix cores; "mfma_fp8": fp8 matrix cores)."""
     n, d, h, k, H, kk = w["n"], w["d"], w["h"], w["k"], w["heads"], w["kk"]
     nb = (n + 127) // 128
     if name == "mlp_gemm1_sparse":
-        return 2.0 * n * d * k, "mfma"
+        return 2.0 * n * d * k, ("mfma_fp8" if fp8 else "mfma")
+    if name == "quantize_fp8":
+        return float(n * d * 2 + n * d + n), "hbm"
     if name == "mlp_gemm2_sparse":
         return 2.0 * n * k * d, "mfma"
     if name == "attn_sparse":
@@ -216,6 +220,9 @@ def main():
                     help="run the MLP and attention deltas as separate calls instead of the shared-grid step")
     ap.add_argument("--mlp-rescore", action="store_true",
                     help="every sparse step rescores the MLP units it recomputed, so S can change each step")
+    ap.add_argument("--fp8", action="store_true",
+                    help="the MLP's first product (dense and sparse) on fp8 e4m3 operands with per-row "
+                         "power-of-two scales; x is quantized every step")
     ap.add_argument("--attn-reident", action="store_true",
                     help="attention identifies its keys anew every step (the cache keeps totals; each step swaps "
                          "the chosen keys' previous-step share for this step's)")
@@ -255,7 +262,8 @@ def main():
         inputs["w1t"], inputs["w2"] = syn.mlp_weights(0, w["d"], w["h"])
         inputs["x"] = syn.activation_walk(0, "X", T, w["n"], w["d"])
         xs = [up(x) for x in inputs["x"]]
-        mlp = MLPDelta(up(inputs["w1t"]), up(inputs["w2"]), w["n"], w["k"], rescore=args.mlp_rescore)
+        mlp = MLPDelta(up(inputs["w1t"]), up(inputs["w2"]), w["n"], w["k"], rescore=args.mlp_rescore,
+                       fp8=args.fp8)
     if w["kk"]:
         walks = [syn.heads_walk(0, t, T, w["heads"], w["n"]) for t in "QKV"]
         inputs["qkv"] = [[walks[i][s] for i in range(3)] for s in range(T)]
@@ -352,23 +360,27 @@ def main():
 
     table = {}
     for name, r in kern.items():
-        amount, bound = kernel_work(name, w, args.attn_reident)
+        amount, bound = kernel_work(name, w, args.attn_reident, args.fp8)
         ent = {"avg_us": round(r["avg_us"], 3), "launches": r["launches"],
                "share": round(r["ms_total"] / max(1e-12, sum(v["ms_total"] for v in kern.values())), 4)}
         if amount is not None:
             ach = amount / (r["avg_us"] * 1e-6)
-            if bound == "mfma":
-                ent.update(achieved=round(ach / 1e12, 2), unit="TFLOP/s", frac=round(ach / 1e12 / PEAK_BF16_TFLOPS, 4))
+            if bound in ("mfma", "mfma_fp8"):
+                peak = PEAK_FP8_TFLOPS if bound == "mfma_fp8" else PEAK_BF16_TFLOPS
+                ent.update(achieved=round(ach / 1e12, 2), unit="TFLOP/s", frac=round(ach / 1e12 / peak, 4))
+                if bound == "mfma_fp8":
+                    ent["peak"] = PEAK_FP8_TFLOPS
             else:
                 ent.update(achieved=round(ach / 1e9, 1), unit="GB/s", frac=round(ach / 1e9 / PEAK_HBM_GBS, 4))
         table[name] = ent
-    dom = max((n for n in kern if kernel_work(n, w, args.attn_reident)[0] is not None),
+    dom = max((n for n in kern if kernel_work(n, w, args.attn_reident, args.fp8)[0] is not None),
               key=lambda n: kern[n]["ms_total"])
-    amount, bound = kernel_work(dom, w, args.attn_reident)
+    amount, bound = kernel_work(dom, w, args.attn_reident, args.fp8)
     avg_s = kern[dom]["avg_us"] * 1e-6
-    if bound == "mfma":
-        roof = {"bound": "mfma", "achieved": round(amount / avg_s / 1e12, 2), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(amount / avg_s / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    if bound in ("mfma", "mfma_fp8"):
+        peak = PEAK_FP8_TFLOPS if bound == "mfma_fp8" else PEAK_BF16_TFLOPS
+        roof = {"bound": "mfma", "achieved": round(amount / avg_s / 1e12, 2), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(amount / avg_s / 1e12 / peak, 4)}
     else:
         roof = {"bound": "hbm", "achieved": round(amount / avg_s / 1e9, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(amount / avg_s / 1e9 / PEAK_HBM_GBS, 4)}
@@ -380,7 +392,7 @@ def main():
         "metric": "ms/step and effective TFLOP/s (% bf16 MFMA peak) for sparse MLP/attn delta",
         "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16", "data": "synthetic (seeded Gaussian weights and drifting activations, real shapes)",
+        "dtype": "bf16, fp8 e4m3 in the MLP's first product" if args.fp8 else "bf16", "data": "synthetic (seeded Gaussian weights and drifting activations, real shapes)",
         "config": {"workload": {"flux": "FLUX.1-dev-shaped sparse step (MLP + attention delta)",
                                 "flux_2304": "FLUX.1-dev-shaped sparse step at 2304x1280 (MLP + attention delta)",
                                 "tiny": "tiny MLP delta", "hunyuan_mlp": "HunyuanVideo-shaped MLP delta",
@@ -390,7 +402,8 @@ def main():
                    "row_block": 128, "launch": ("hip graph per step" if args.graph else "eager")
                    + ("; MLP phase 2 and attention share one kernel" if fused else ""),
                    "mlp_set": "rescored every step" if args.mlp_rescore else "fixed between refreshes",
-                   "attn_set": "re-identified every step" if args.attn_reident else "fixed between refreshes"},
+                   "attn_set": "re-identified every step" if args.attn_reident else "fixed between refreshes",
+                   "mlp_first_product": "fp8 e4m3, per-row power-of-two scales" if args.fp8 else "bf16"},
         "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "flop_per_step": fl,
         "roofline": roof,

@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libchipmunk.so")
 
-SOURCES = ["abi.cpp", "mlp.hip", "topk.hip", "attn.hip", "writeback.hip", "step.hip"]
+SOURCES = ["abi.cpp", "mlp.hip", "topk.hip", "attn.hip", "writeback.hip", "step.hip", "quant.hip"]
 ARCH = "gfx950"
 
 

@@ -54,13 +54,19 @@ int check_mlp(const chipmunk_mlp* L, bool need_score) {
   if (chipmunk::row_blocks(L->n) > kMaxGridY)
     return fail(CHIPMUNK_E_SHAPE, "n too large: %lld row blocks exceed %lld", (long long)chipmunk::row_blocks(L->n),
                 (long long)kMaxGridY);
-  if (!L->w1t || !L->w2 || !L->a_cache) return fail(CHIPMUNK_E_NULLPTR, "layer w1t, w2 and a_cache are required");
+  if (L->flags & ~(CHIPMUNK_MLP_RESCORE | CHIPMUNK_MLP_FP8))
+    return fail(CHIPMUNK_E_SHAPE, "unknown layer flags 0x%x", L->flags);
+  const bool fp8 = (L->flags & CHIPMUNK_MLP_FP8) != 0;
+  if ((!fp8 && !L->w1t) || !L->w2 || !L->a_cache)
+    return fail(CHIPMUNK_E_NULLPTR, "layer w1t (unless FP8), w2 and a_cache are required");
+  if (fp8 && (!L->w1t_f8 || !L->w1t_scale))
+    return fail(CHIPMUNK_E_NULLPTR, "layer w1t_f8 and w1t_scale are required by CHIPMUNK_MLP_FP8");
   if (need_score && !L->score) return fail(CHIPMUNK_E_NULLPTR, "layer score is required by the dense step");
-  if (L->flags & ~CHIPMUNK_MLP_RESCORE) return fail(CHIPMUNK_E_SHAPE, "unknown layer flags 0x%x", L->flags);
   if ((L->flags & CHIPMUNK_MLP_RESCORE) && !L->score)
     return fail(CHIPMUNK_E_NULLPTR, "layer score is required by CHIPMUNK_MLP_RESCORE");
-  if (!aligned(L->w1t, 16) || !aligned(L->w2, 16) || !aligned(L->a_cache, 16))
-    return fail(CHIPMUNK_E_ALIGN, "w1t, w2 and a_cache must be 16-byte aligned");
+  if ((L->w1t && !aligned(L->w1t, 16)) || !aligned(L->w2, 16) || !aligned(L->a_cache, 16) ||
+      (fp8 && !aligned(L->w1t_f8, 16)))
+    return fail(CHIPMUNK_E_ALIGN, "w1t, w1t_f8, w2 and a_cache must be 16-byte aligned");
   if ((L->b1 && !aligned(L->b1, 4)) || (L->b2 && !aligned(L->b2, 4)) || (L->score && !aligned(L->score, 4)))
     return fail(CHIPMUNK_E_ALIGN, "b1, b2 and score must be 4-byte aligned");
   return CHIPMUNK_OK;
@@ -93,6 +99,25 @@ int check_bf16_in(const void* p, const char* name) {
 size_t sparse_mlp_ws(int64_t n, int32_t k) {
   return (size_t)chipmunk::row_blocks(n) * (size_t)chipmunk::padded_k(k) * chipmunk::kRowBlock * sizeof(uint16_t);
 }
+// fp8 copy of x: [n][d] e4m3 codes, then n scale bytes, rounded up to 16.
+size_t fp8_x_ws(int64_t n, int32_t d) { return ((size_t)n * (size_t)d + (size_t)n + 15) / 16 * 16; }
+bool is_fp8(const chipmunk_mlp* L) { return (L->flags & CHIPMUNK_MLP_FP8) != 0; }
+// Workspace of the sparse MLP delta of layer L at keep count k.
+size_t layer_sparse_ws(const chipmunk_mlp* L, int32_t k) {
+  return sparse_mlp_ws(L->n, k) + (is_fp8(L) ? fp8_x_ws(L->n, L->d) : 0);
+}
+// Quantizes x into ws + off (fp8 layers) and returns the operands of the first
+// product; nullptr for bf16 layers.
+hipError_t prepare_fp8(const chipmunk_mlp* L, const uint16_t* x, void* ws, size_t off, chipmunk::Fp8Rows* f8,
+                       const chipmunk::Fp8Rows** out, hipStream_t s) {
+  *out = nullptr;
+  if (!is_fp8(L)) return hipSuccess;
+  uint8_t* xq = static_cast<uint8_t*>(ws) + off;
+  uint8_t* xsc = xq + (size_t)L->n * (size_t)L->d;
+  *f8 = {xq, xsc, L->w1t_f8, L->w1t_scale};
+  *out = f8;
+  return chipmunk::launch_quantize_fp8(x, L->n, L->d, xq, xsc, s);
+}
 
 // Scores the sparse delta rewrites (NULL: S stays fixed until the next dense step).
 float* rescore_target(const chipmunk_mlp* L) { return (L->flags & CHIPMUNK_MLP_RESCORE) ? L->score : nullptr; }
@@ -109,7 +134,7 @@ int check_sparse_mlp(const chipmunk_mlp* L, const uint16_t* x, const int32_t* id
   if (k > 0 && !idx) return fail(CHIPMUNK_E_NULLPTR, "idx is NULL");
   if (idx && !aligned(idx, 4)) return fail(CHIPMUNK_E_ALIGN, "idx must be 4-byte aligned");
   if (a_new_packed && !aligned(a_new_packed, 16)) return fail(CHIPMUNK_E_ALIGN, "a_new_packed must be 16-byte aligned");
-  const size_t need = sparse_mlp_ws(L->n, k);
+  const size_t need = layer_sparse_ws(L, k);
   if (k > 0 && (!ws || ws_bytes < need))
     return fail(CHIPMUNK_E_WORKSPACE, "workspace of %zu bytes required (got %zu)", need, ws ? ws_bytes : (size_t)0);
   if (ws && !aligned(ws, 16)) return fail(CHIPMUNK_E_ALIGN, "ws must be 16-byte aligned");
@@ -179,7 +204,7 @@ const char* kernel_name(int kid) {
   static const char* names[K_COUNT] = {"mlp_gemm1_sparse", "mlp_gemm1_dense", "mlp_gemm2_sparse", "mlp_gemm2_dense",
                                        "topk_rows",        "cache_writeback", "attn_stats",       "attn_dense",
                                        "attn_sparse",      "attn_refresh",     "sparse_step_fused",
-                                       "attn_reident"};
+                                       "attn_reident",     "quantize_fp8"};
   return (kid >= 0 && kid < K_COUNT) ? names[kid] : "";
 }
 
@@ -253,6 +278,10 @@ extern "C" size_t chipmunk_workspace_bytes(int op, int64_t n, int32_t d, int32_t
   switch (op) {
     case CHIPMUNK_OP_SPARSE_MLP:
       return sparse_mlp_ws(n, k);
+    case CHIPMUNK_OP_SPARSE_MLP_FP8:
+      return d > 0 ? sparse_mlp_ws(n, k) + fp8_x_ws(n, d) : 0;
+    case CHIPMUNK_OP_DENSE_MLP_FP8:
+      return d > 0 ? fp8_x_ws(n, d) : 0;
     default:
       return 0;
   }
@@ -271,12 +300,20 @@ extern "C" int chipmunk_dense_step(int kind, const void* layer, const uint16_t* 
       if (k || v) return fail(CHIPMUNK_E_SHAPE, "k and v must be NULL for an MLP layer");
       if (!out) return fail(CHIPMUNK_E_NULLPTR, "out (y) is NULL");
       if (!aligned(out, 16)) return fail(CHIPMUNK_E_ALIGN, "out (y) must be 16-byte aligned");
-      (void)ws;
-      (void)ws_bytes;
+      if (is_fp8(L)) {
+        const size_t need = fp8_x_ws(L->n, L->d);
+        if (!ws || ws_bytes < need)
+          return fail(CHIPMUNK_E_WORKSPACE, "workspace of %zu bytes required (got %zu)", need, ws ? ws_bytes : (size_t)0);
+        if (!aligned(ws, 16)) return fail(CHIPMUNK_E_ALIGN, "ws must be 16-byte aligned");
+      }
+      chipmunk::Fp8Rows f8buf;
+      const chipmunk::Fp8Rows* f8 = nullptr;
+      hipError_t e = prepare_fp8(L, x_or_q, ws, 0, &f8buf, &f8, s);
+      if (e != hipSuccess) return hip_status(e, "quantize_fp8 launch");
       // The second product reads the freshly written activation cache directly
       // ([nb][h][128] is the [unit][row] layout it streams).
-      hipError_t e = chipmunk::launch_mlp_gemm1(true, x_or_q, L->w1t, L->b1, nullptr, L->a_cache, nullptr, nullptr,
-                                                L->score, L->n, L->d, L->h, L->h, s);
+      e = chipmunk::launch_mlp_gemm1(true, x_or_q, L->w1t, L->b1, nullptr, L->a_cache, nullptr, nullptr, L->score,
+                                     L->n, L->d, L->h, L->h, s, f8);
       if (e != hipSuccess) return hip_status(e, "mlp_gemm1 (dense) launch");
       e = chipmunk::launch_mlp_gemm2(true, L->a_cache, L->w2, nullptr, L->b2, out, L->n, L->d, L->h, L->h, L->h, s);
       return hip_status(e, "mlp_gemm2 (dense) launch");
@@ -325,8 +362,12 @@ extern "C" int chipmunk_sparse_mlp_delta(const chipmunk_mlp* L, const uint16_t* 
     if (k == 0) return ok();
     hipStream_t s = static_cast<hipStream_t>(stream);
     uint16_t* dbuf = static_cast<uint16_t*>(ws);
-    hipError_t e = chipmunk::launch_mlp_gemm1(false, x, L->w1t, L->b1, idx, L->a_cache, dbuf, a_new_packed,
-                                              rescore_target(L), L->n, L->d, L->h, k, s);
+    chipmunk::Fp8Rows f8buf;
+    const chipmunk::Fp8Rows* f8 = nullptr;
+    hipError_t e = prepare_fp8(L, x, ws, sparse_mlp_ws(L->n, k), &f8buf, &f8, s);
+    if (e != hipSuccess) return hip_status(e, "quantize_fp8 launch");
+    e = chipmunk::launch_mlp_gemm1(false, x, L->w1t, L->b1, idx, L->a_cache, dbuf, a_new_packed, rescore_target(L),
+                                   L->n, L->d, L->h, k, s, f8);
     if (e != hipSuccess) return hip_status(e, "mlp_gemm1 (sparse) launch");
     e = chipmunk::launch_mlp_gemm2(false, dbuf, L->w2, idx, nullptr, y, L->n, L->d, L->h, k, chipmunk::padded_k(k), s);
     return hip_status(e, "mlp_gemm2 (sparse) launch");
@@ -404,10 +445,12 @@ extern "C" int chipmunk_sparse_step(const chipmunk_mlp* M, const uint16_t* x, co
     const Span mlp_w[] = {{y, (size_t)M->n * M->d * 4, "y"},
                           {M->a_cache, nb * M->h * 128 * 2, "mlp a_cache"},
                           {a_new_packed, nb * mk * 128 * 2, "a_new_packed"},
-                          {ws, k > 0 ? sparse_mlp_ws(M->n, k) : 0, "ws"},
+                          {ws, k > 0 ? layer_sparse_ws(M, k) : 0, "ws"},
                           {rescore_target(M), rescore_target(M) ? nb * M->h * 4 : 0, "mlp score"}};
     const Span mlp_r[] = {{x, (size_t)M->n * M->d * 2, "x"},
                           {M->w1t, (size_t)M->h * M->d * 2, "w1t"},
+                          {is_fp8(M) ? M->w1t_f8 : nullptr, (size_t)M->h * M->d, "w1t_f8"},
+                          {is_fp8(M) ? M->w1t_scale : nullptr, (size_t)M->h, "w1t_scale"},
                           {M->w2, (size_t)M->h * M->d * 2, "w2"},
                           {M->b1, M->b1 ? (size_t)M->h * 4 : 0, "b1"},
                           {mlp_idx, nb * mk * 4, "mlp idx"}};
@@ -428,13 +471,40 @@ extern "C" int chipmunk_sparse_step(const chipmunk_mlp* M, const uint16_t* x, co
     for (const Span& w : att_w)
       for (const Span& r : mlp_r)
         if (overlap(w, r)) return fail(CHIPMUNK_E_SHAPE, "%s overlaps %s", w.name, r.name);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    chipmunk::Fp8Rows f8buf;
+    const chipmunk::Fp8Rows* f8 = nullptr;
+    if (k > 0) {
+      hipError_t e = prepare_fp8(M, x, ws, sparse_mlp_ws(M->n, k), &f8buf, &f8, s);
+      if (e != hipSuccess) return hip_status(e, "quantize_fp8 launch");
+    }
     hipError_t e = chipmunk::launch_sparse_step(x, M->w1t, M->b1, mlp_idx, M->a_cache, static_cast<uint16_t*>(ws),
                                                 a_new_packed, rescore_target(M), M->w2, y, M->n, M->d, M->h, k, q,
                                                 kx, v, attn_idx, A->m, A->num, A->den, o, A->n, A->heads, kk,
-                                                A->scale, static_cast<hipStream_t>(stream));
+                                                A->scale, s, f8);
     return hip_status(e, "sparse step launch");
   } catch (...) {
     return fail(CHIPMUNK_E_INTERNAL, "internal error in chipmunk_sparse_step");
+  }
+}
+
+extern "C" int chipmunk_quantize_fp8(const uint16_t* src, int64_t rows, int32_t cols, uint8_t* dst, uint8_t* scale,
+                                     void* stream) {
+  try {
+    if (rows < 0) return fail(CHIPMUNK_E_SHAPE, "rows must be >= 0");
+    if (cols < 8 || cols % 8 != 0) return fail(CHIPMUNK_E_SHAPE, "cols must be a positive multiple of 8 (got %d)", cols);
+    if ((rows + 3) / 4 > (int64_t)UINT32_MAX) return fail(CHIPMUNK_E_SHAPE, "rows exceeds the grid limit");
+    if (!src || !dst || !scale) return fail(CHIPMUNK_E_NULLPTR, "src, dst and scale are required");
+    if (!aligned(src, 16) || !aligned(dst, 16)) return fail(CHIPMUNK_E_ALIGN, "src and dst must be 16-byte aligned");
+    const Span in{src, (size_t)rows * (size_t)cols * 2, "src"};
+    const Span o1{dst, (size_t)rows * (size_t)cols, "dst"}, o2{scale, (size_t)rows, "scale"};
+    if (overlap(in, o1) || overlap(in, o2) || overlap(o1, o2))
+      return fail(CHIPMUNK_E_SHAPE, "src, dst and scale must not overlap");
+    if (rows == 0) return ok();
+    return hip_status(chipmunk::launch_quantize_fp8(src, rows, cols, dst, scale, static_cast<hipStream_t>(stream)),
+                      "quantize_fp8 launch");
+  } catch (...) {
+    return fail(CHIPMUNK_E_INTERNAL, "internal error in chipmunk_quantize_fp8");
   }
 }
 

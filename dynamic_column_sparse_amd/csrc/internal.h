@@ -24,6 +24,7 @@ enum KernelId {
   K_ATTN_REFRESH,
   K_SPARSE_STEP_FUSED,
   K_ATTN_REIDENT,
+  K_QUANTIZE_FP8,
   K_COUNT
 };
 const char* kernel_name(int kid);
@@ -37,12 +38,25 @@ __host__ __device__ inline int64_t row_blocks(int64_t n) { return (n + kRowBlock
 // (the rows past k are zero, so phase 2 streams whole chunks).
 __host__ __device__ inline int padded_k(int k) { return (k + 63) / 64 * 64; }
 
+// fp8 operands of the MLP's first product: e4m3 codes of x [n][d] and W1^T
+// [h][d] with one E8M0 scale byte per row.
+struct Fp8Rows {
+  const uint8_t* x;
+  const uint8_t* x_scale;
+  const uint8_t* w;
+  const uint8_t* w_scale;
+};
 // MLP phase 1: gathered x W1[:,S] + GELU, then either the sparse epilogue
 // (D tiles, cache writeback; with a score array, also S's column L1 of D) or
-// the dense one (score, full cache write).
+// the dense one (score, full cache write).  f8 non-NULL: the product runs on
+// the fp8 operands instead of x and w1t.
 hipError_t launch_mlp_gemm1(bool dense, const uint16_t* x, const uint16_t* w1t, const float* b1,
                             const int32_t* idx, uint16_t* a_cache, uint16_t* dbuf, uint16_t* a_packed,
-                            float* score, int64_t n, int d, int h, int k, hipStream_t s);
+                            float* score, int64_t n, int d, int h, int k, hipStream_t s,
+                            const Fp8Rows* f8 = nullptr);
+// Row-wise fp8 quantization of a bf16 [rows][cols] matrix (cols % 8 == 0).
+hipError_t launch_quantize_fp8(const uint16_t* src, int64_t rows, int cols, uint8_t* dst, uint8_t* scale,
+                               hipStream_t s);
 // MLP phase 2: y (+)= src[b] W2[S] where src is [nb][kc][128] (D tiles, or the cache).
 hipError_t launch_mlp_gemm2(bool dense, const uint16_t* src, const uint16_t* w2, const int32_t* idx,
                             const float* b2, float* y, int64_t n, int d, int h, int k, int kc,
@@ -69,6 +83,6 @@ hipError_t launch_sparse_step(const uint16_t* x, const uint16_t* w1t, const floa
                               int64_t n, int d, int h, int k, const uint16_t* q, const uint16_t* kx,
                               const uint16_t* v, const int32_t* aidx, const float* m, const float* num,
                               const float* den, float* o, int64_t na, int heads, int kk, float scale,
-                              hipStream_t s);
+                              hipStream_t s, const Fp8Rows* f8 = nullptr);
 
 }  // namespace chipmunk

@@ -12,7 +12,7 @@ constexpr int kWideWastePct = MLP_WIDE_WASTE_PCT;
 
 hipError_t launch_mlp_gemm1(bool dense, const uint16_t* x, const uint16_t* w1t, const float* b1,
                             const int32_t* idx, uint16_t* a_cache, uint16_t* dbuf, uint16_t* a_packed,
-                            float* score, int64_t n, int d, int h, int k, hipStream_t s) {
+                            float* score, int64_t n, int d, int h, int k, hipStream_t s, const Fp8Rows* f8) {
   const int nb = (int)row_blocks(n);
   const int cols = dense ? h : k;
   const int kp = padded_k(k);
@@ -20,24 +20,35 @@ hipError_t launch_mlp_gemm1(bool dense, const uint16_t* x, const uint16_t* w1t, 
   const int t256 = (cols + 255) / 256, t128 = (cols + 127) / 128;
   const bool wide = t128 > 1 && (int64_t)t256 * 256 * 100 <= (int64_t)cols * (100 + kWideWastePct);
   const int kid = dense ? K_MLP_GEMM1_DENSE : K_MLP_GEMM1_SPARSE;
+  const void* xa = f8 ? (const void*)f8->x : (const void*)x;
+  const void* wa = f8 ? (const void*)f8->w : (const void*)w1t;
+  const uint8_t* xs = f8 ? f8->x_scale : nullptr;
+  const uint8_t* ws = f8 ? f8->w_scale : nullptr;
+  const dim3 grid((unsigned)xcd_grid((wide ? t256 : t128) * nb));
+#define G1_LAUNCH(BN_, DENSE_, F8_)                                                                               \
+  hipLaunchKernelGGL((mlp_gemm1<BN_, DENSE_, F8_>), grid, dim3(256), 0, s, xa, wa, xs, ws, b1, idx, a_cache, dbuf, \
+                     a_packed, score, n, d, h, k, kp)
+#define G1_LAUNCH_F8(BN_, DENSE_) \
+  {                               \
+    if (f8)                       \
+      G1_LAUNCH(BN_, DENSE_, true);  \
+    else                          \
+      G1_LAUNCH(BN_, DENSE_, false); \
+  }
   timing_before(kid, s);
   if (wide) {
-    const dim3 grid((unsigned)xcd_grid(t256 * nb));
     if (dense)
-      hipLaunchKernelGGL((mlp_gemm1<256, true>), grid, dim3(256), 0, s, x, w1t, b1, idx, a_cache, dbuf, a_packed,
-                         score, n, d, h, k, kp);
+      G1_LAUNCH_F8(256, true)
     else
-      hipLaunchKernelGGL((mlp_gemm1<256, false>), grid, dim3(256), 0, s, x, w1t, b1, idx, a_cache, dbuf,
-                         a_packed, score, n, d, h, k, kp);
+      G1_LAUNCH_F8(256, false)
   } else {
-    const dim3 grid((unsigned)xcd_grid(t128 * nb));
     if (dense)
-      hipLaunchKernelGGL((mlp_gemm1<128, true>), grid, dim3(256), 0, s, x, w1t, b1, idx, a_cache, dbuf, a_packed,
-                         score, n, d, h, k, kp);
+      G1_LAUNCH_F8(128, true)
     else
-      hipLaunchKernelGGL((mlp_gemm1<128, false>), grid, dim3(256), 0, s, x, w1t, b1, idx, a_cache, dbuf,
-                         a_packed, score, n, d, h, k, kp);
+      G1_LAUNCH_F8(128, false)
   }
+#undef G1_LAUNCH_F8
+#undef G1_LAUNCH
   hipError_t e = hipGetLastError();
   timing_after(kid, s);
   return e;

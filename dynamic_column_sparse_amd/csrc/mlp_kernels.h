@@ -40,9 +40,19 @@ constexpr int NS = 3;     // LDS ring stages: one consumed, two in flight
 #endif
 constexpr int kGroupTiles = MLP_GROUP_TILES;   // column tiles of one row block run back to back
 
-template <int BN, bool DENSE>
-__global__ __launch_bounds__(256, 2) void mlp_gemm1(const uint16_t* __restrict__ x,
-                                                    const uint16_t* __restrict__ w1t,
+// F8: x and W1^T are e4m3 codes (one byte per element) with one E8M0 scale
+// byte per row (xs for the token rows, ws1 for the hidden units); each 64-byte
+// row piece of a chunk is then 64 reduction steps instead of 32, and one
+// scaled fp8 product (32x32x64) replaces the two bf16 ones.  Lane l's operand
+// bytes are the same two 16-byte LDS pieces (K bytes 16g.. and 32+16g.., g =
+// l/32) that feed the two bf16 substeps.  The row scales are fixed for a
+// tile, so each lane keeps its row's and its column's scale byte in a
+// register for the whole loop; the products come out scaled.
+template <int BN, bool DENSE, bool F8>
+__global__ __launch_bounds__(256, 2) void mlp_gemm1(const void* __restrict__ xv,
+                                                    const void* __restrict__ wv,
+                                                    const uint8_t* __restrict__ xs,
+                                                    const uint8_t* __restrict__ ws1,
                                                     const float* __restrict__ b1,
                                                     const int32_t* __restrict__ idx,
                                                     uint16_t* __restrict__ a_cache,
@@ -53,8 +63,8 @@ __global__ __launch_bounds__(256, 2) void mlp_gemm1(const uint16_t* __restrict__
   constexpr int WN = BN / 2;          // columns per wave (2x2 wave grid)
   constexpr int NI = WN / 32;         // 32-wide column subtiles per wave
   constexpr int MI = 2;               // 32-row subtiles per wave (64 rows)
-  constexpr int BK = 32, NS = 3;      // 32-deep K-chunks, 3-stage ring: 72 KB, two workgroups per CU
-  constexpr int ROWB = BK * 2;        // LDS row: 64 bytes = 4 chunks of 16 bytes
+  constexpr int BK = 32, NS = 3;      // 32-deep (bf16) K-chunks, 3-stage ring: 72 KB, two workgroups per CU
+  constexpr int ROWB = 64;            // LDS row: 64 bytes = 4 chunks of 16 bytes (32 bf16 or 64 fp8)
   constexpr int CPR = ROWB / 16, RPI = 1024 / ROWB;   // chunks per row, rows per direct load
   constexpr int A_INS = BM / RPI / 4; // direct loads per wave per stage, x tile
   constexpr int B_INS = BN / RPI / 4; // same, W1^T tile
@@ -82,31 +92,34 @@ __global__ __launch_bounds__(256, 2) void mlp_gemm1(const uint16_t* __restrict__
   // (instruction's first row + lane/8), physical chunk lane%8, logical chunk
   // (lane%8) ^ swz8(row).  Rows past the data are clamped to a valid row: their
   // products only reach output rows/columns the epilogue never stores.
+  const int64_t RB = F8 ? (int64_t)d : 2 * (int64_t)d;   // bytes per x / W1^T row
+  const unsigned char* x = (const unsigned char*)xv;
+  const unsigned char* w1t = (const unsigned char*)wv;
   const int lrow = lane / CPR, pch = lane % CPR;
-  const uint16_t* asrc[A_INS];
+  const unsigned char* asrc[A_INS];
 #pragma unroll
   for (int i = 0; i < A_INS; ++i) {
     const int r = (wave * A_INS + i) * RPI + lrow;
     const int rg = r < rows ? r : rows - 1;
-    asrc[i] = x + (r0 + rg) * (int64_t)d + ((pch ^ swz4(r)) << 3);
+    asrc[i] = x + (r0 + rg) * RB + ((pch ^ swz4(r)) << 4);
   }
-  const uint16_t* bsrc[B_INS];
+  const unsigned char* bsrc[B_INS];
 #pragma unroll
   for (int i = 0; i < B_INS; ++i) {
     const int r = (wave * B_INS + i) * RPI + lrow;
     const int p = c0 + r;
     int j = 0;
     if (p < kcols) j = DENSE ? p : clamp_index(idx[(int64_t)b * k + p], h);
-    bsrc[i] = w1t + (int64_t)j * d + ((pch ^ swz4(r)) << 3);
+    bsrc[i] = w1t + (int64_t)j * RB + ((pch ^ swz4(r)) << 4);
   }
 
 #define G1_ISSUE(kt_, buf_)                                                                 \
   {                                                                                         \
     const uint32_t st_ = smem_lds + (buf_) * STAGE;                                         \
     _Pragma("unroll") for (int i = 0; i < A_INS; ++i)                                       \
-        dma16_at(asrc[i] + (kt_) * BK, st_ + (wave * A_INS + i) * 1024);                    \
+        dma16_at(asrc[i] + (kt_) * ROWB, st_ + (wave * A_INS + i) * 1024);                  \
     _Pragma("unroll") for (int i = 0; i < B_INS; ++i)                                       \
-        dma16_at(bsrc[i] + (kt_) * BK, st_ + A_BYTES + (wave * B_INS + i) * 1024);          \
+        dma16_at(bsrc[i] + (kt_) * ROWB, st_ + A_BYTES + (wave * B_INS + i) * 1024);        \
   }
 
   f32x16_t acc[MI][NI];
@@ -130,10 +143,24 @@ __global__ __launch_bounds__(256, 2) void mlp_gemm1(const uint16_t* __restrict__
     bias[ni] = (valid[ni] && b1) ? b1[jcol[ni]] : 0.f;
   }
 
+  // fp8: the scale bytes of this lane's rows (one per 32-row subtile) and
+  // columns (one per 32-column subtile), the same for both 32-deep halves of a
+  // product (lanes l and l+32 carry the same row / column).
+  int sa[MI], sb[NI];
+  if (F8) {
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+      const int r = wm * 64 + mi * 32 + (lane & 31);
+      sa[mi] = xs[r0 + (r < rows ? r : rows - 1)];
+    }
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) sb[ni] = ws1[jcol[ni]];
+  }
+
   // Operand reads: lane l reads row (base + l%32), logical chunk 2s + l/32.  Every
   // row base is a multiple of 32, so the swizzle depends on the lane only.
   const int sw = swz4(lane & 31);
-  const int KT = d / BK;
+  const int KT = (int)(RB / ROWB);
   G1_ISSUE(0, 0);
   if (KT > 1) G1_ISSUE(1, 1);
   for (int kt = 0; kt < KT; ++kt) {
@@ -155,13 +182,33 @@ __global__ __launch_bounds__(256, 2) void mlp_gemm1(const uint16_t* __restrict__
         bfr[q_][ni] = *(const bf16x8_t*)(st + A_BYTES + (wn * WN + ni * 32 + (lane & 31)) * ROWB + coff); \
     }
     G1_FRAG(0, 0);
+    if constexpr (F8) {
+      // Both 16-byte halves form one 64-deep fp8 operand.
+      G1_FRAG(1, 1);
+      typedef int i32x4_t __attribute__((ext_vector_type(4)));
+      typedef int i32x8_t __attribute__((ext_vector_type(8)));
+      auto cat = [](bf16x8_t lo, bf16x8_t hi) __attribute__((always_inline)) {
+        const i32x4_t a = __builtin_bit_cast(i32x4_t, lo), c = __builtin_bit_cast(i32x4_t, hi);
+        const i32x8_t r = {a[0], a[1], a[2], a[3], c[0], c[1], c[2], c[3]};
+        return r;
+      };
 #pragma unroll
-    for (int s = 0; s < BK / 16; ++s) {
-      if (s + 1 < BK / 16) G1_FRAG(s + 1, (s + 1) & 1);
+      for (int mi = 0; mi < MI; ++mi) {
+        const i32x8_t a8 = cat(af[0][mi], af[1][mi]);
 #pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
+        for (int ni = 0; ni < NI; ++ni)
+          acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, cat(bfr[0][ni], bfr[1][ni]), acc[mi][ni],
+                                                                        0, 0, 0, sa[mi], 0, sb[ni]);
+      }
+    } else {
 #pragma unroll
-        for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = mfma32(af[s & 1][mi], bfr[s & 1][ni], acc[mi][ni]);
+      for (int s = 0; s < BK / 16; ++s) {
+        if (s + 1 < BK / 16) G1_FRAG(s + 1, (s + 1) & 1);
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+          for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = mfma32(af[s & 1][mi], bfr[s & 1][ni], acc[mi][ni]);
+      }
     }
 #undef G1_FRAG
   }

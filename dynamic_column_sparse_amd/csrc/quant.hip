@@ -1,0 +1,73 @@
+// Row-wise fp8 quantization for the fp8 variant of the MLP's first product
+// (gfx950).  Each row of a bf16 matrix becomes OCP e4m3 codes with one
+// power-of-two scale 2^e per row: e is the smallest integer (at least -126)
+// with max|row| * 2^-e <= 448, e = 0 for an all-zero row, and each element is
+// rounded to nearest even after the exact scaling by 2^-e (v_cvt_pk_fp8_f32;
+// scaled values never exceed 448, so no code is NaN).  The scale is stored as
+// its E8M0 byte 127 + e, the form the scaled matrix-core instructions take.
+//
+// One wave per row, four rows per workgroup: the row maximum is a wave
+// reduction (no LDS, no barrier), then the row is read again (from cache) and
+// converted 8 elements at a time (16-byte loads, 8-byte stores).
+#include "device_common.h"
+#include "internal.h"
+
+namespace chipmunk {
+namespace {
+
+__global__ __launch_bounds__(256) void quantize_fp8_rows(const uint16_t* __restrict__ src, int64_t rows, int cols,
+                                                         uint8_t* __restrict__ dst, uint8_t* __restrict__ scale) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const uint16_t* s = src + row * cols;
+  uint8_t* o = dst + row * cols;
+  const int units = cols >> 3;
+  // |x| as bf16 bits (sign cleared) orders like the values (finite inputs).
+  uint32_t mx = 0;
+  for (int u = lane; u < units; u += 64) {
+    const uint4 v = *(const uint4*)(s + u * 8);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mx = max(mx, max(w[i] & 0x7fffu, (w[i] >> 16) & 0x7fffu));
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, off));
+  // amax = 2^(E-127) (1 + f/2^23) as fp32; with 448 = 1.75 * 2^8 the smallest
+  // fitting exponent is E - 135, plus one when 1 + f/2^23 > 1.75.
+  const uint32_t ab = mx << 16;
+  const int E = (int)(ab >> 23), f = (int)(ab & 0x7fffff);
+  int e = 0;
+  if (mx != 0) e = E == 0 ? -126 : max(E - 135 + (f > 0x600000 ? 1 : 0), -126);
+  if (lane == 0) scale[row] = (uint8_t)(127 + e);
+  const float mul = __uint_as_float((uint32_t)(127 - e) << 23);   // 2^-e, exact
+  for (int u = lane; u < units; u += 64) {
+    const uint4 v = *(const uint4*)(s + u * 8);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    float x[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = bf2f(w[i] & 0xffffu) * mul;
+      x[2 * i + 1] = bf2f(w[i] >> 16) * mul;
+    }
+    int lo = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
+    lo = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], lo, true);
+    int hi = __builtin_amdgcn_cvt_pk_fp8_f32(x[4], x[5], 0, false);
+    hi = __builtin_amdgcn_cvt_pk_fp8_f32(x[6], x[7], hi, true);
+    *(uint2*)(o + u * 8) = make_uint2((uint32_t)lo, (uint32_t)hi);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_quantize_fp8(const uint16_t* src, int64_t rows, int cols, uint8_t* dst, uint8_t* scale,
+                               hipStream_t s) {
+  const dim3 grid((unsigned)((rows + 3) / 4));
+  timing_before(K_QUANTIZE_FP8, s);
+  hipLaunchKernelGGL(quantize_fp8_rows, grid, dim3(256), 0, s, src, rows, cols, dst, scale);
+  hipError_t e = hipGetLastError();
+  timing_after(K_QUANTIZE_FP8, s);
+  return e;
+}
+
+}  // namespace chipmunk

@@ -51,12 +51,12 @@ hipError_t launch_sparse_step(const uint16_t* x, const uint16_t* w1t, const floa
                               const uint16_t* w2, float* y, int64_t n, int d, int h, int k, const uint16_t* q,
                               const uint16_t* kx, const uint16_t* v, const int32_t* aidx, const float* m,
                               const float* num, const float* den, float* o, int64_t na, int heads, int kk,
-                              float scale, hipStream_t s) {
+                              float scale, hipStream_t s, const Fp8Rows* f8) {
   const int kp = padded_k(k);
   int g2 = 0;
   const int bn = d % 256 == 0 ? 256 : 128;
   if (k > 0) {
-    hipError_t e = launch_mlp_gemm1(false, x, w1t, b1, midx, a_cache, dbuf, a_packed, mscore, n, d, h, k, s);
+    hipError_t e = launch_mlp_gemm1(false, x, w1t, b1, midx, a_cache, dbuf, a_packed, mscore, n, d, h, k, s, f8);
     if (e != hipSuccess) return e;
     g2 = xcd_grid(d / bn * (int)row_blocks(n));
   }

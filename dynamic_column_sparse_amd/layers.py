@@ -34,9 +34,12 @@ def row_blocks(n: int) -> int:
 class MLPDelta:
     """One MLP layer: w1t [h,d], w2 [h,d] bf16 device tensors; k kept columns per block.
     rescore=True: every sparse step rescores the units it recomputed, so the set
-    S can change from step to step (CHIPMUNK_MLP_RESCORE)."""
+    S can change from step to step (CHIPMUNK_MLP_RESCORE).
+    fp8=True: the first product runs on fp8 operands (CHIPMUNK_MLP_FP8); W1^T is
+    quantized once here, x by every call."""
 
-    def __init__(self, w1t: torch.Tensor, w2: torch.Tensor, n: int, k: int, b1=None, b2=None, rescore=False):
+    def __init__(self, w1t: torch.Tensor, w2: torch.Tensor, n: int, k: int, b1=None, b2=None, rescore=False,
+                 fp8=False):
         h, d = w1t.shape
         assert w2.shape == (h, d) and w1t.dtype == torch.bfloat16 and w2.dtype == torch.bfloat16
         dev = w1t.device
@@ -47,10 +50,19 @@ class MLPDelta:
         self.score = torch.zeros(self.nb, h, dtype=torch.float32, device=dev)
         self.y = torch.zeros(n, d, dtype=torch.float32, device=dev)
         self.idx = torch.zeros(self.nb, max(k, 1), dtype=torch.int32, device=dev)
-        ws = lib.chipmunk_workspace_bytes(lib.OP_SPARSE_MLP, n, d, h, k)
+        self.w1t_f8 = self.w1t_scale = None
+        if fp8:
+            self.w1t_f8 = torch.empty(h, d, dtype=torch.uint8, device=dev)
+            self.w1t_scale = torch.empty(h, dtype=torch.uint8, device=dev)
+            lib.chipmunk_quantize_fp8(w1t, h, d, self.w1t_f8, self.w1t_scale)
+            ws = max(lib.chipmunk_workspace_bytes(lib.OP_SPARSE_MLP_FP8, n, d, h, k),
+                     lib.chipmunk_workspace_bytes(lib.OP_DENSE_MLP_FP8, n, d, h, 0))
+        else:
+            ws = lib.chipmunk_workspace_bytes(lib.OP_SPARSE_MLP, n, d, h, k)
         self.ws = torch.empty(max(ws, 16), dtype=torch.uint8, device=dev)
-        self.layer = lib.mlp_layer(n, d, h, w1t, w2, self.a_cache, self.score, b1, b2,
-                                   lib.MLP_RESCORE if rescore else 0)
+        flags = (lib.MLP_RESCORE if rescore else 0) | (lib.MLP_FP8 if fp8 else 0)
+        self.layer = lib.mlp_layer(n, d, h, w1t, w2, self.a_cache, self.score, b1, b2, flags, self.w1t_f8,
+                                   self.w1t_scale)
 
     def dense(self, x: torch.Tensor, stream=None):
         lib.chipmunk_dense_step(lib.MLP, self.layer, x, None, None, self.y, self.ws, stream=stream)

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define CHIPMUNK_ABI_VERSION 3
+#define CHIPMUNK_ABI_VERSION 4
 #define CHIPMUNK_ROW_BLOCK 128
 #define CHIPMUNK_HEAD_DIM 128
 
@@ -75,7 +75,9 @@ enum chipmunk_op {
   CHIPMUNK_OP_SPARSE_MLP = 1,
   CHIPMUNK_OP_TOPK = 2,
   CHIPMUNK_OP_DENSE_ATTN = 3,
-  CHIPMUNK_OP_SPARSE_ATTN = 4
+  CHIPMUNK_OP_SPARSE_ATTN = 4,
+  CHIPMUNK_OP_DENSE_MLP_FP8 = 5, /* the dense MLP step of a CHIPMUNK_MLP_FP8 layer */
+  CHIPMUNK_OP_SPARSE_MLP_FP8 = 6 /* the sparse MLP delta of a CHIPMUNK_MLP_FP8 layer */
 };
 
 /* One MLP layer: y = gelu(x W1 + b1) W2 + b2, plus its caches.
@@ -102,6 +104,17 @@ enum chipmunk_op {
  *          chooses which vectors to recompute dynamically, in each step;
  *          Activation Deltas section).  Units outside S_b keep their scores.
  *          Requires score.  0 keeps S fixed until the next dense step.
+ *          CHIPMUNK_MLP_FP8 (may be combined with RESCORE): the first product
+ *          (dense and sparse) runs on fp8 operands -- the Chipmunk post
+ *          sparsifies an FP8 FLUX model (Results section).  Each call
+ *          quantizes x into its workspace row by row (chipmunk_quantize_fp8's
+ *          encoding) and reads W1^T from w1t_f8 / w1t_scale, which the caller
+ *          fills once with chipmunk_quantize_fp8(w1t).  The matrix cores take
+ *          the e4m3 codes with the row scales as E8M0 scale operands and
+ *          accumulate in fp32; everything after the product (b1, GELU, bf16
+ *          cache, D, the second product) is unchanged.  w1t may then be NULL.
+ *   w1t_f8    [h][d] e4m3 codes of W1^T (FP8 layers only; 16-byte aligned)
+ *   w1t_scale [h] E8M0 scale bytes of those rows (FP8 layers only)
  */
 typedef struct chipmunk_mlp {
   int64_t n;
@@ -114,9 +127,12 @@ typedef struct chipmunk_mlp {
   uint16_t* a_cache;
   float* score;
   uint32_t flags;
+  const uint8_t* w1t_f8;
+  const uint8_t* w1t_scale;
 } chipmunk_mlp;
 
 #define CHIPMUNK_MLP_RESCORE 1u
+#define CHIPMUNK_MLP_FP8 2u
 
 /* One attention layer's cache (all heads).
  *   n        tokens (queries = keys, 1 <= n < 2^24)
@@ -148,7 +164,9 @@ typedef struct chipmunk_attn {
  *   k and v must be NULL; out = the output cache y [n][d] fp32.  Computes
  *   z = x W1 + b1, a = bf16(gelu_tanh(z)) (fp32 math, round to nearest even),
  *   score[b][j] = sum over block b's real rows of |a - a_cache_old| (fp32),
- *   then a_cache <- a and y = a W2 + b2 (fp32 accumulate).  ws may be NULL.
+ *   then a_cache <- a and y = a W2 + b2 (fp32 accumulate).  ws may be NULL,
+ *   except for a CHIPMUNK_MLP_FP8 layer: chipmunk_workspace_bytes(
+ *   CHIPMUNK_OP_DENSE_MLP_FP8, n, d, h, 0) bytes, 16-byte aligned.
  * kind = CHIPMUNK_ATTN: layer is a const chipmunk_attn*; x_or_q, k, v =
  *   q, k, v [heads][n][128] bf16; out = o [heads][n][128] fp32.  Per head, with
  *   s = scale q k^T: m = rowmax(s), den = sum_j exp(s - m), num = exp(s - m) v,
@@ -183,7 +201,9 @@ int chipmunk_identify_topk(const float* score, int64_t rows, int64_t cols, int32
  * every buffer bit-unchanged.  ws must hold chipmunk_workspace_bytes(
  * CHIPMUNK_OP_SPARSE_MLP, n, d, h, k) bytes: the D tiles, [nb][128][kp] bf16
  * (row-major per block: token row, then the block's kept units in idx order;
- * kp = k rounded up to 64, units past k are written as zero). */
+ * kp = k rounded up to 64, units past k are written as zero); for a
+ * CHIPMUNK_MLP_FP8 layer, chipmunk_workspace_bytes(CHIPMUNK_OP_SPARSE_MLP_FP8,
+ * n, d, h, k) bytes: the D tiles, then the fp8 copy of x. */
 int chipmunk_sparse_mlp_delta(const chipmunk_mlp* layer, const uint16_t* x, const int32_t* idx,
                               int32_t k, float* y, uint16_t* a_new_packed, void* ws, size_t ws_bytes,
                               void* stream);
@@ -251,9 +271,22 @@ int chipmunk_sparse_step(const chipmunk_mlp* mlp, const uint16_t* x, const int32
 int chipmunk_cache_writeback(const chipmunk_mlp* layer, const uint16_t* a_new_packed, const int32_t* idx,
                              int32_t k, void* stream);
 
+/* Row-wise fp8 quantization (the operand encoding of CHIPMUNK_MLP_FP8): for
+ * each row of src [rows][cols] bf16, e = the smallest integer >= -126 with
+ * max|row| * 2^-e <= 448 (e = 0 for an all-zero row); dst[r][c] = the OCP e4m3
+ * code of src[r][c] * 2^-e rounded to nearest even (the scaling is exact and
+ * the result never exceeds 448); scale[r] = 127 + e, the E8M0 byte of 2^e.
+ * Inputs must be finite.  cols a positive multiple of 8; src and dst 16-byte
+ * aligned, scale any alignment; dst and scale must not overlap src.  rows = 0
+ * enqueues nothing.  Bit-exact (integer work after an exact scaling). */
+int chipmunk_quantize_fp8(const uint16_t* src, int64_t rows, int32_t cols, uint8_t* dst, uint8_t* scale,
+                          void* stream);
+
 /* Scratch bytes an op needs for these sizes (0 when none).  op: chipmunk_op.
- * CHIPMUNK_OP_SPARSE_MLP: nb*kp*128*2 with kp = k rounded up to 64; the
- * others: 0. */
+ * CHIPMUNK_OP_SPARSE_MLP: nb*kp*128*2 with kp = k rounded up to 64 (the D
+ * tiles); CHIPMUNK_OP_SPARSE_MLP_FP8: that plus the fp8 copy of x, n*d codes
+ * and n scale bytes rounded up to 16; CHIPMUNK_OP_DENSE_MLP_FP8: the fp8 copy
+ * of x alone; the others: 0. */
 size_t chipmunk_workspace_bytes(int op, int64_t n, int32_t d, int32_t h, int32_t k);
 
 /* Thread-local text of the last failure on this thread ("" if none). */

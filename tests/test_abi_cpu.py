@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_names_workspace(L):
-    assert L.chipmunk_abi_version() == 3
+    assert L.chipmunk_abi_version() == 4
     names = L.kernel_names()
     assert "mlp_gemm1_sparse" in names and "attn_sparse" in names and "topk_rows" in names
     assert "attn_reident" in names
@@ -72,8 +72,12 @@ def _code(L, fn, *a, **kw):
 @pytest.mark.parametrize("case,code", [
     (dict(n=0), 2), (dict(d=100), 2), (dict(d=64), 2), (dict(h=0), 2), (dict(h=100), 2),
     (dict(w1t=None), 1), (dict(a_cache=None), 1), (dict(w2=FAKE + 8), 4),
-    (dict(flags=2), 2),                      # unknown flag bit
+    (dict(flags=4), 2),                      # unknown flag bit
     (dict(flags=1, score=None), 1),          # rescoring needs the score array
+    (dict(flags=2), 1),                      # fp8 needs w1t_f8 and w1t_scale
+    (dict(flags=2, w1t_f8=FAKE, w1t_scale=None), 1),
+    (dict(flags=2, w1t_f8=FAKE + 8, w1t_scale=FAKE), 4),
+    (dict(w1t=None), 1),                     # a bf16 layer needs w1t
 ])
 def test_sparse_mlp_rejects_bad_layer(L, case, code):
     lay = _mlp(L, **case)
@@ -188,6 +192,30 @@ def test_reident_checks(L):
     assert call(n=1 << 24) == 2                   # 32-bit gathered row offsets
     # the previous step's inputs may be the current ones (read-only)
     assert call(qp=base["q"], kp=base["k"], vp=base["v"], kk=-1) == 2   # still fails on kk alone
+
+
+def test_fp8_checks(L):
+    q = L.chipmunk_quantize_fp8
+    assert _code(L, q, FAKE, 4, 12, FAKE + (1 << 32), FAKE + (2 << 32), stream=0) == 2      # cols % 8
+    assert _code(L, q, FAKE, 4, 0, FAKE + (1 << 32), FAKE + (2 << 32), stream=0) == 2
+    assert _code(L, q, FAKE, -1, 16, FAKE + (1 << 32), FAKE + (2 << 32), stream=0) == 2
+    assert _code(L, q, None, 4, 16, FAKE + (1 << 32), FAKE + (2 << 32), stream=0) == 1
+    assert _code(L, q, FAKE, 4, 16, FAKE + (1 << 32), None, stream=0) == 1
+    assert _code(L, q, FAKE + 8, 4, 16, FAKE + (1 << 32), FAKE + (2 << 32), stream=0) == 4
+    assert _code(L, q, FAKE, 4, 16, FAKE + 64, FAKE + (2 << 32), stream=0) == 2          # dst inside src
+    assert _code(L, q, FAKE, 0, 16, FAKE + (1 << 32), FAKE + (2 << 32), stream=0) == 0    # no rows: no-op
+    # workspace sizes of an fp8 layer: the D tiles, then x's codes and scales
+    base = L.chipmunk_workspace_bytes(L.OP_SPARSE_MLP, 4352, 3072, 12288, 3686)
+    xq = (4352 * 3072 + 4352 + 15) // 16 * 16
+    assert L.chipmunk_workspace_bytes(L.OP_SPARSE_MLP_FP8, 4352, 3072, 12288, 3686) == base + xq
+    assert L.chipmunk_workspace_bytes(L.OP_DENSE_MLP_FP8, 4352, 3072, 12288, 0) == xq
+    # an fp8 layer's sparse delta wants the larger workspace; its dense step one too
+    lay = _mlp(L, flags=2, w1t_f8=FAKE + (3 << 32), w1t_scale=FAKE + (4 << 32))
+    small = L.chipmunk_workspace_bytes(L.OP_SPARSE_MLP, 300, 256, 640, 10)
+    rc = L.raw().chipmunk_sparse_mlp_delta(ctypes.byref(lay), FAKE, FAKE, 10, FAKE, None, FAKE, small, None)
+    assert rc == 5
+    rc = L.raw().chipmunk_dense_step(0, ctypes.byref(lay), FAKE, None, None, FAKE, None, 0, None)
+    assert rc == 5
 
 
 def test_timer_api_without_launches(L):

@@ -1,0 +1,168 @@
+"""The fp8 variant of the MLP's first product (reading R14: x and W1^T as e4m3
+codes with one power-of-two scale per row; everything after the product as in
+the bf16 path).
+
+  * chipmunk_quantize_fp8 against the oracle's quantizer: codes and scale bytes
+    bit-exact, on activation-like rows and on edge rows (all zero, -0, tiny,
+    huge, bf16 subnormals, a row maximum exactly at 448 and just past it, a wide
+    range inside one row), and on the layer's W1^T.
+  * fp8 layers against the oracle run on the quantize-dequantized operands: the
+    dense step (a within 1e-3, y within 2e-2, scores within 1e-3) and two
+    sparse steps on the GPU's own index sets
+    (which equal the oracle's top-k of the GPU's score bits): y and the step's
+    change of y within 2e-2, the cache within 1e-3.  The workspace copy of x is
+    checked bit for bit as well.
+  * The FLUX.1-dev shape through the shared-grid step call, on sampled row
+    blocks, in the launch configuration the benchmark times.
+
+The fp8 matrix cores sum the products of one instruction in groups of 8
+consecutive reduction steps, and within a group a product below about 2^-13 of
+the group's largest is dropped (measured on gfx950 with a single-instruction
+probe: of 63 products at 2^-14 .. 2^-18 beside one product of 1, exactly the 7
+in the large product's group are lost).  The first product therefore carries a
+relative error of about 1e-4 where the bf16 path carries about 1e-7, and about
+1% of the bf16-rounded activations land one unit from the oracle's (instead of
+a few in 10^4): the activation check bounds that share at 3% and the relative
+error at 1e-3; outputs keep the 2e-2 bar.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic as syn
+from tests.gpu_helpers import bits_of, cache_to_rows, up_bf16, up_f32
+from tests.test_gpu_fullsize import RB, _cache_rows, _rows_of, _sample_blocks
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-2
+
+
+def _quantize_gpu(lib, bits):
+    rows, cols = bits.shape
+    src = up_bf16(bits)
+    dst = torch.full((rows, cols), 0xAA, dtype=torch.uint8, device="cuda")
+    sc = torch.full((rows,), 0xAA, dtype=torch.uint8, device="cuda")
+    lib.chipmunk_quantize_fp8(src, rows, cols, dst, sc)
+    torch.cuda.synchronize()
+    return dst.cpu().numpy(), sc.cpu().numpy()
+
+
+def _edge_rows(cols):
+    g = np.random.default_rng(4)
+    r = [np.zeros(cols), -np.zeros(cols),
+         g.standard_normal(cols) * 1e-30, g.standard_normal(cols) * 1e30,
+         g.standard_normal(cols) * 1e-39,                       # bf16 subnormals
+         np.concatenate([[448.0, -3.0], g.uniform(-448, 448, cols - 2)]),
+         np.concatenate([[-450.0], g.uniform(-1, 1, cols - 1)]),  # just past 448: the next exponent
+         g.standard_normal(cols) * np.exp(g.uniform(-14, 8, cols)),
+         np.where(g.random(cols) < 0.5, 0.0, g.standard_normal(cols))]
+    return oracle.bf16_bits(np.stack(r))
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 8), (9, 24), (300, 3072), (4352, 3072)])
+def test_quantize_bit_exact(gpu_lib, rows, cols):
+    print(f"quantize fp8 rows={rows} cols={cols}", flush=True)
+    bits = syn.activations(2, "X", 0, rows, cols)
+    if rows >= 9:
+        bits = np.concatenate([_edge_rows(cols), bits[9:]])
+    codes, sc = _quantize_gpu(gpu_lib, bits)
+    rc, rs = oracle.quantize_fp8_rows(oracle.from_bf16_bits(bits))
+    np.testing.assert_array_equal(sc, rs)
+    np.testing.assert_array_equal(codes, rc)
+
+
+def _inputs(n, d, h, seed, steps):
+    w1t_b, w2_b = syn.mlp_weights(seed, d, h)
+    g = np.random.default_rng(seed + 100)
+    b1 = (g.standard_normal(h) * 0.1).astype(np.float32)
+    xs = [syn.activations(seed, "X", t, n, d) for t in range(steps)]
+    return w1t_b, w2_b, b1, xs
+
+
+@pytest.mark.parametrize("n,d,h,k", [(300, 256, 640, 200), (256, 128, 512, 128), (130, 384, 1024, 1000)])
+def test_fp8_mlp_matches_oracle(gpu_lib, n, d, h, k):
+    from dynamic_column_sparse_amd.layers import MLPDelta
+    print(f"fp8 mlp parity n={n} d={d} h={h} k={k}", flush=True)
+    w1t_b, w2_b, b1, xs = _inputs(n, d, h, 1, 3)
+    lay = MLPDelta(up_bf16(w1t_b), up_bf16(w2_b), n, k, up_f32(b1), None, fp8=True)
+    w1t, w2 = oracle.from_bf16_bits(w1t_b), oracle.from_bf16_bits(w2_b)
+    wc, ws = oracle.quantize_fp8_rows(w1t)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(lay.w1t_f8.cpu().numpy(), wc)
+    np.testing.assert_array_equal(lay.w1t_scale.cpu().numpy(), ws)
+    w1q = oracle.dequantize_fp8_rows(wc, ws)
+
+    lay.dense(up_bf16(xs[0]))
+    torch.cuda.synchronize()
+    x0 = oracle.from_bf16_bits(xs[0])
+    xc, xsc = oracle.quantize_fp8_rows(x0)
+    wsb = lay.ws.cpu().numpy()                         # dense step: the fp8 copy of x at offset 0
+    np.testing.assert_array_equal(wsb[:n * d].reshape(n, d), xc)
+    np.testing.assert_array_equal(wsb[n * d:n * d + n], xsc)
+    a, y, sc = oracle.mlp_dense(oracle.fp8_rows(x0), w1q, b1, w2, None, np.zeros((n, h)))
+    a_gpu = cache_to_rows(lay.a_cache, n)
+    assert np.mean(a_gpu != a) < 3e-2
+    assert oracle.rel_frobenius(a_gpu, a) < 1e-3
+    assert oracle.rel_frobenius(lay.y.cpu().numpy(), y) < TOL
+    assert oracle.rel_frobenius(lay.score.cpu().numpy(), sc) < 1e-3
+
+    for t in (1, 2):
+        y_before = lay.y.cpu().numpy()
+        lay.identify()
+        torch.cuda.synchronize()
+        g_idx = lay.idx.cpu().numpy()[:, :k]
+        np.testing.assert_array_equal(g_idx, oracle.identify_topk(lay.score.cpu().numpy(), k))
+        lay.sparse(up_bf16(xs[t]))
+        torch.cuda.synchronize()
+        a, y1 = oracle.mlp_sparse(oracle.fp8_rows(oracle.from_bf16_bits(xs[t])), w1q, b1, w2, a, y, g_idx)
+        y_gpu = lay.y.cpu().numpy()
+        e = oracle.rel_frobenius(y_gpu, y1)
+        assert e < TOL, f"step {t}: y {e:.2e}"
+        assert oracle.rel_frobenius(y_gpu - y_before, y1 - y) < TOL, f"step {t}: dy"
+        assert oracle.rel_frobenius(cache_to_rows(lay.a_cache, n), a) < 1e-3, f"step {t}: cache"
+        y = y1
+        print(f"  step {t}: y rel-F {e:.2e}", flush=True)
+
+
+def test_fp8_flux_fused_step_sampled(gpu_lib):
+    # FLUX.1-dev MLP (4352 tokens, d 3072, h 12288, keep 3686) with an fp8 first
+    # product, through chipmunk_sparse_step beside the FLUX attention delta:
+    # refresh, then two sparse steps; three sampled row blocks plus the last.
+    from dynamic_column_sparse_amd.layers import AttnDelta, MLPDelta, sparse_step
+    n, d, h, k, H, kk, seed, steps = 4352, 3072, 12288, 3686, 24, 718, 0, 3
+    nb = (n + RB - 1) // RB
+    blocks = _sample_blocks(nb, 3, seed + 13, n)
+    rows = _rows_of(blocks, n)
+    rows_t = torch.from_numpy(rows).cuda()
+    print(f"fp8 flux fused step: blocks {blocks}", flush=True)
+    w1t_b, w2_b = syn.mlp_weights(seed, d, h)
+    mlp = MLPDelta(up_bf16(w1t_b), up_bf16(w2_b), n, k, fp8=True)
+    w1q = oracle.fp8_rows(oracle.from_bf16_bits(w1t_b))
+    w2 = oracle.from_bf16_bits(w2_b)
+    del w1t_b, w2_b
+    att = AttnDelta(n, H, kk, "cuda")
+    xs = syn.activation_walk(seed, "X", steps, n, d)
+    walks = [syn.heads_walk(seed, tag, steps, H, n) for tag in "QKV"]
+    a_s = y_s = None
+    for t in range(steps):
+        x_g = up_bf16(xs[t])
+        qkv = [up_bf16(w[t]) for w in walks]
+        x_s = oracle.fp8_rows(oracle.from_bf16_bits(xs[t][rows]))
+        if t == 0:
+            mlp.step(x_g, refresh=True)
+            att.step(*qkv, refresh=True)
+            torch.cuda.synchronize()
+            a_s, y_s, _ = oracle.mlp_dense(x_s, w1q, None, w2, None, np.zeros((len(rows), h)))
+            assert oracle.rel_frobenius(mlp.y[rows_t].cpu().numpy(), y_s) < TOL, "dense y"
+            continue
+        sparse_step(mlp, att, x_g, *qkv)
+        torch.cuda.synchronize()
+        g_idx = mlp.idx[torch.tensor(blocks, device="cuda")].cpu().numpy()
+        g_score = mlp.score[torch.tensor(blocks, device="cuda")].cpu().numpy()
+        np.testing.assert_array_equal(g_idx, oracle.identify_topk(g_score, k))
+        a_s, y_s = oracle.mlp_sparse(x_s, w1q, None, w2, a_s, y_s, g_idx)
+        e = oracle.rel_frobenius(mlp.y[rows_t].cpu().numpy(), y_s)
+        assert e < TOL, f"step {t}: y {e:.2e}"
+        assert oracle.rel_frobenius(_cache_rows(mlp.a_cache, blocks, n), a_s) < 1e-3, f"step {t}: cache"
+        print(f"  step {t}: y rel-F {e:.2e}", flush=True)
