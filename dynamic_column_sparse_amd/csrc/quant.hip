@@ -7,14 +7,42 @@
 // its E8M0 byte 127 + e, the form the scaled matrix-core instructions take.
 //
 // One wave per row, four rows per workgroup: the row maximum is a wave
-// reduction (no LDS, no barrier), then the row is read again (from cache) and
-// converted 8 elements at a time (16-byte loads, 8-byte stores).
+// reduction (no LDS, no barrier).  Rows of up to kCachedUnits * 64 * 8 values
+// stay in registers between the maximum and the conversion (one read of the
+// row; all of a lane's 16-byte loads are in flight together); longer rows are
+// read twice.  Conversion goes 8 elements at a time (8-byte stores).
 #include "device_common.h"
 #include "internal.h"
 
 namespace chipmunk {
 namespace {
 
+constexpr int kCachedUnits = 8;   // 16-byte units per lane kept in registers (rows up to 4096)
+
+__device__ __forceinline__ uint32_t abs_max8(const uint4& v) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t mx = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) mx = max(mx, max(w[i] & 0x7fffu, (w[i] >> 16) & 0x7fffu));
+  return mx;
+}
+
+__device__ __forceinline__ uint2 to_fp8x8(const uint4& v, float mul) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  float x[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = bf2f(w[i] & 0xffffu) * mul;
+    x[2 * i + 1] = bf2f(w[i] >> 16) * mul;
+  }
+  int lo = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
+  lo = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], lo, true);
+  int hi = __builtin_amdgcn_cvt_pk_fp8_f32(x[4], x[5], 0, false);
+  hi = __builtin_amdgcn_cvt_pk_fp8_f32(x[6], x[7], hi, true);
+  return make_uint2((uint32_t)lo, (uint32_t)hi);
+}
+
+template <bool CACHED>
 __global__ __launch_bounds__(256) void quantize_fp8_rows(const uint16_t* __restrict__ src, int64_t rows, int cols,
                                                          uint8_t* __restrict__ dst, uint8_t* __restrict__ scale) {
   const int lane = threadIdx.x & 63;
@@ -25,11 +53,17 @@ __global__ __launch_bounds__(256) void quantize_fp8_rows(const uint16_t* __restr
   const int units = cols >> 3;
   // |x| as bf16 bits (sign cleared) orders like the values (finite inputs).
   uint32_t mx = 0;
-  for (int u = lane; u < units; u += 64) {
-    const uint4 v = *(const uint4*)(s + u * 8);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint4 keep[CACHED ? kCachedUnits : 1];
+  if (CACHED) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) mx = max(mx, max(w[i] & 0x7fffu, (w[i] >> 16) & 0x7fffu));
+    for (int i = 0; i < kCachedUnits; ++i) {
+      const int u = lane + 64 * i;
+      keep[i] = u < units ? *(const uint4*)(s + u * 8) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < kCachedUnits; ++i) mx = max(mx, abs_max8(keep[i]));
+  } else {
+    for (int u = lane; u < units; u += 64) mx = max(mx, abs_max8(*(const uint4*)(s + u * 8)));
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, off));
@@ -41,20 +75,14 @@ __global__ __launch_bounds__(256) void quantize_fp8_rows(const uint16_t* __restr
   if (mx != 0) e = E == 0 ? -126 : max(E - 135 + (f > 0x600000 ? 1 : 0), -126);
   if (lane == 0) scale[row] = (uint8_t)(127 + e);
   const float mul = __uint_as_float((uint32_t)(127 - e) << 23);   // 2^-e, exact
-  for (int u = lane; u < units; u += 64) {
-    const uint4 v = *(const uint4*)(s + u * 8);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    float x[8];
+  if (CACHED) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x[2 * i] = bf2f(w[i] & 0xffffu) * mul;
-      x[2 * i + 1] = bf2f(w[i] >> 16) * mul;
+    for (int i = 0; i < kCachedUnits; ++i) {
+      const int u = lane + 64 * i;
+      if (u < units) *(uint2*)(o + u * 8) = to_fp8x8(keep[i], mul);
     }
-    int lo = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
-    lo = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], lo, true);
-    int hi = __builtin_amdgcn_cvt_pk_fp8_f32(x[4], x[5], 0, false);
-    hi = __builtin_amdgcn_cvt_pk_fp8_f32(x[6], x[7], hi, true);
-    *(uint2*)(o + u * 8) = make_uint2((uint32_t)lo, (uint32_t)hi);
+  } else {
+    for (int u = lane; u < units; u += 64) *(uint2*)(o + u * 8) = to_fp8x8(*(const uint4*)(s + u * 8), mul);
   }
 }
 
@@ -64,7 +92,10 @@ hipError_t launch_quantize_fp8(const uint16_t* src, int64_t rows, int cols, uint
                                hipStream_t s) {
   const dim3 grid((unsigned)((rows + 3) / 4));
   timing_before(K_QUANTIZE_FP8, s);
-  hipLaunchKernelGGL(quantize_fp8_rows, grid, dim3(256), 0, s, src, rows, cols, dst, scale);
+  if (cols <= kCachedUnits * 64 * 8)
+    hipLaunchKernelGGL(quantize_fp8_rows<true>, grid, dim3(256), 0, s, src, rows, cols, dst, scale);
+  else
+    hipLaunchKernelGGL(quantize_fp8_rows<false>, grid, dim3(256), 0, s, src, rows, cols, dst, scale);
   hipError_t e = hipGetLastError();
   timing_after(K_QUANTIZE_FP8, s);
   return e;

@@ -60,7 +60,8 @@ def _edge_rows(cols):
     return oracle.bf16_bits(np.stack(r))
 
 
-@pytest.mark.parametrize("rows,cols", [(1, 8), (9, 24), (300, 3072), (4352, 3072)])
+@pytest.mark.parametrize("rows,cols", [(1, 8), (9, 24), (300, 3072), (4352, 3072),
+                                       (11, 4104), (20, 12288)])   # rows read twice past 4096 columns
 def test_quantize_bit_exact(gpu_lib, rows, cols):
     print(f"quantize fp8 rows={rows} cols={cols}", flush=True)
     bits = syn.activations(2, "X", 0, rows, cols)
