@@ -55,6 +55,11 @@ design notes of this repository):
       largest magnitude within 448, rounded to nearest even; the product (dense and
       sparse) takes those values, and everything after it is unchanged.  The fp8
       MLP is mlp_dense / mlp_sparse applied to fp8_rows(x) and fp8_rows(w1t).
+  R15 optional fp8 second product of the sparse delta (with R14): D, rounded to
+      bf16 as the bf16 path stores it, becomes e4m3 codes per (row, 32 consecutive
+      units of S) block, and W2 per column (output feature); each block and column
+      takes its own smallest fitting power-of-two scale.  The dense step's second
+      product stays bf16.  mlp_sparse(..., w2=fp8_cols(w2), d_fp8=True).
 
 Parity pins for every function live in ``tests/test_oracle_*.py``.
 """
@@ -177,6 +182,32 @@ def fp8_rows(a) -> np.ndarray:
     return dequantize_fp8_rows(*quantize_fp8_rows(a))
 
 
+def quantize_fp8_blocks(a, block: int = 32):
+    """Each row cut into consecutive blocks of `block` elements (the last one
+    padded with zeros), every block quantized as one row of quantize_fp8_rows.
+    Returns (codes [rows, cols] uint8, scale bytes [rows, ceil(cols/block)])."""
+    a = np.asarray(a, dtype=np.float64)
+    rows, cols = a.shape
+    nblk = (cols + block - 1) // block
+    padded = np.zeros((rows, nblk * block))
+    padded[:, :cols] = a
+    codes, sb = quantize_fp8_rows(padded.reshape(rows * nblk, block))
+    return codes.reshape(rows, nblk * block)[:, :cols], sb.reshape(rows, nblk)
+
+
+def fp8_blocks(a, block: int = 32) -> np.ndarray:
+    """The values of quantize_fp8_blocks(a, block), dequantized."""
+    codes, sb = quantize_fp8_blocks(a, block)
+    rows, cols = codes.shape
+    e = np.repeat(sb.astype(np.int64) - 127, block, axis=1)[:, :cols]
+    return np.ldexp(fp8_e4m3_decode(codes), e)
+
+
+def fp8_cols(a) -> np.ndarray:
+    """Column-wise fp8 values: each column with its own power-of-two scale."""
+    return fp8_rows(np.asarray(a, dtype=np.float64).T).T
+
+
 # --------------------------------------------------------------------------- #
 # Non-linearity
 # --------------------------------------------------------------------------- #
@@ -260,7 +291,7 @@ def mlp_dense(x, w1t, b1, w2, b2, a_old):
     return a_new, y, score
 
 
-def mlp_sparse(x, w1t, b1, w2, a, y, idx, score=None):
+def mlp_sparse(x, w1t, b1, w2, a, y, idx, score=None, d_fp8=False):
     """One sparse MLP step (Chipmunk post, Activation Deltas section: only the
     chosen output vectors are swapped for new ones, the others are kept).
 
@@ -278,6 +309,11 @@ def mlp_sparse(x, w1t, b1, w2, a, y, idx, score=None):
     score in which score[b, S] = sum over the block's real rows of |D| -- the
     dense step's score formula (R1) applied to this step's recomputed units --
     and every other entry is unchanged: (a, y, score).
+
+    With ``d_fp8`` (the fp8 second product, reading R15) the product takes D
+    rounded to bf16 (as the bf16 path stores it) and then to e4m3 codes per
+    (row, 32 consecutive units of S) block, fp8_blocks(bf16(D)); pass w2 as the
+    values the fp8 operand carries, fp8_cols(w2).
     """
     x = np.asarray(x, np.float64)
     w1t = np.asarray(w1t, np.float64)
@@ -296,7 +332,7 @@ def mlp_sparse(x, w1t, b1, w2, a, y, idx, score=None):
             z = z + np.asarray(b1, np.float64)[s][None, :]
         a_s = bf16_round(gelu_tanh(z))
         d = a_s - a[r0:r1][:, s]
-        y[r0:r1] += d @ w2[s]
+        y[r0:r1] += (fp8_blocks(bf16_round(d), 32) if d_fp8 else d) @ w2[s]
         a[r0:r1, s] = a_s
         if sc is not None:
             sc[b, s] = np.abs(d).sum(axis=0)
