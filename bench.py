@@ -60,17 +60,20 @@ def flops_attn(w, reident=False):
     return (8.0 if reident else 4.0) * w["n"] * w["kk"] * HEAD_DIM * w["heads"]
 
 
-def kernel_work(name, w, reident=False, fp8=False):
+def kernel_work(name, w, reident=False, fp8=False, fp8_w2=False):
     """(amount, bound) of algorithmic work in ONE launch of kernel `name`
-    (bound "mfma": bf16 matrix cores; "mfma_fp8": fp8 matrix cores)."""
+    (bound "mfma": bf16 matrix cores; "mfma_fp8": fp8 matrix cores; a
+    ("mfma_mix", fp8 flops) bound: part of the flops on fp8 matrix cores)."""
     n, d, h, k, H, kk = w["n"], w["d"], w["h"], w["k"], w["heads"], w["kk"]
     nb = (n + 127) // 128
     if name == "mlp_gemm1_sparse":
         return 2.0 * n * d * k, ("mfma_fp8" if fp8 else "mfma")
+    if name == "mlp_gemm2_sparse":
+        return 2.0 * n * k * d, ("mfma_fp8" if fp8_w2 else "mfma")
+    if name == "sparse_step_fused" and fp8_w2:
+        return 2.0 * n * k * d + 4.0 * n * kk * HEAD_DIM * H, ("mfma_mix", 2.0 * n * k * d)
     if name == "quantize_fp8":
         return float(n * d * 2 + n * d + n), "hbm"
-    if name == "mlp_gemm2_sparse":
-        return 2.0 * n * k * d, "mfma"
     if name == "attn_sparse":
         return 4.0 * n * kk * HEAD_DIM * H, "mfma"
     if name == "attn_reident":
@@ -83,6 +86,18 @@ def kernel_work(name, w, reident=False, fp8=False):
         parts = ([nb * h * 4 + nb * k * 4] if k else []) + ([H * nb * n * 4 + H * nb * kk * 4] if reident else [])
         return (float(sum(parts)) / len(parts), "hbm") if parts else (None, None)
     return None, None
+
+
+def peak_for(bound, amount):
+    """Matrix-core peak (TFLOP/s) for a kernel's bound: bf16, fp8, or a mix in
+    which the fp8 flops run at the fp8 peak and the rest at the bf16 peak (the
+    peak is then the total flops over the shortest time for both parts)."""
+    if bound == "mfma_fp8":
+        return PEAK_FP8_TFLOPS
+    if isinstance(bound, tuple):
+        f8 = bound[1]
+        return amount / (f8 / PEAK_FP8_TFLOPS + (amount - f8) / PEAK_BF16_TFLOPS)
+    return PEAK_BF16_TFLOPS
 
 
 def source_digest():
@@ -223,6 +238,9 @@ def main():
     ap.add_argument("--fp8", action="store_true",
                     help="the MLP's first product (dense and sparse) on fp8 e4m3 operands with per-row "
                          "power-of-two scales; x is quantized every step")
+    ap.add_argument("--fp8-w2", action="store_true",
+                    help="the sparse MLP delta's second product on fp8 operands (D per row and 32 units, W2 per "
+                         "column)")
     ap.add_argument("--attn-reident", action="store_true",
                     help="attention identifies its keys anew every step (the cache keeps totals; each step swaps "
                          "the chosen keys' previous-step share for this step's)")
@@ -263,7 +281,7 @@ def main():
         inputs["x"] = syn.activation_walk(0, "X", T, w["n"], w["d"])
         xs = [up(x) for x in inputs["x"]]
         mlp = MLPDelta(up(inputs["w1t"]), up(inputs["w2"]), w["n"], w["k"], rescore=args.mlp_rescore,
-                       fp8=args.fp8)
+                       fp8=args.fp8, fp8_w2=args.fp8_w2)
     if w["kk"]:
         walks = [syn.heads_walk(0, t, T, w["heads"], w["n"]) for t in "QKV"]
         inputs["qkv"] = [[walks[i][s] for i in range(3)] for s in range(T)]
@@ -360,25 +378,25 @@ def main():
 
     table = {}
     for name, r in kern.items():
-        amount, bound = kernel_work(name, w, args.attn_reident, args.fp8)
+        amount, bound = kernel_work(name, w, args.attn_reident, args.fp8, args.fp8_w2)
         ent = {"avg_us": round(r["avg_us"], 3), "launches": r["launches"],
                "share": round(r["ms_total"] / max(1e-12, sum(v["ms_total"] for v in kern.values())), 4)}
         if amount is not None:
             ach = amount / (r["avg_us"] * 1e-6)
-            if bound in ("mfma", "mfma_fp8"):
-                peak = PEAK_FP8_TFLOPS if bound == "mfma_fp8" else PEAK_BF16_TFLOPS
+            if bound in ("mfma", "mfma_fp8") or isinstance(bound, tuple):
+                peak = peak_for(bound, amount)
                 ent.update(achieved=round(ach / 1e12, 2), unit="TFLOP/s", frac=round(ach / 1e12 / peak, 4))
-                if bound == "mfma_fp8":
-                    ent["peak"] = PEAK_FP8_TFLOPS
+                if bound != "mfma":
+                    ent["peak"] = round(peak, 1)
             else:
                 ent.update(achieved=round(ach / 1e9, 1), unit="GB/s", frac=round(ach / 1e9 / PEAK_HBM_GBS, 4))
         table[name] = ent
-    dom = max((n for n in kern if kernel_work(n, w, args.attn_reident, args.fp8)[0] is not None),
+    dom = max((n for n in kern if kernel_work(n, w, args.attn_reident, args.fp8, args.fp8_w2)[0] is not None),
               key=lambda n: kern[n]["ms_total"])
-    amount, bound = kernel_work(dom, w, args.attn_reident, args.fp8)
+    amount, bound = kernel_work(dom, w, args.attn_reident, args.fp8, args.fp8_w2)
     avg_s = kern[dom]["avg_us"] * 1e-6
-    if bound in ("mfma", "mfma_fp8"):
-        peak = PEAK_FP8_TFLOPS if bound == "mfma_fp8" else PEAK_BF16_TFLOPS
+    if bound in ("mfma", "mfma_fp8") or isinstance(bound, tuple):
+        peak = round(peak_for(bound, amount), 1)
         roof = {"bound": "mfma", "achieved": round(amount / avg_s / 1e12, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(amount / avg_s / 1e12 / peak, 4)}
     else:
@@ -392,7 +410,9 @@ def main():
         "metric": "ms/step and effective TFLOP/s (% bf16 MFMA peak) for sparse MLP/attn delta",
         "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16, fp8 e4m3 in the MLP's first product" if args.fp8 else "bf16", "data": "synthetic (seeded Gaussian weights and drifting activations, real shapes)",
+        "dtype": ("bf16, fp8 e4m3 in the MLP's " + " and ".join(
+            p for p, on in (("first product", args.fp8), ("second product", args.fp8_w2)) if on))
+        if (args.fp8 or args.fp8_w2) else "bf16", "data": "synthetic (seeded Gaussian weights and drifting activations, real shapes)",
         "config": {"workload": {"flux": "FLUX.1-dev-shaped sparse step (MLP + attention delta)",
                                 "flux_2304": "FLUX.1-dev-shaped sparse step at 2304x1280 (MLP + attention delta)",
                                 "tiny": "tiny MLP delta", "hunyuan_mlp": "HunyuanVideo-shaped MLP delta",
@@ -403,7 +423,9 @@ def main():
                    + ("; MLP phase 2 and attention share one kernel" if fused else ""),
                    "mlp_set": "rescored every step" if args.mlp_rescore else "fixed between refreshes",
                    "attn_set": "re-identified every step" if args.attn_reident else "fixed between refreshes",
-                   "mlp_first_product": "fp8 e4m3, per-row power-of-two scales" if args.fp8 else "bf16"},
+                   "mlp_first_product": "fp8 e4m3, per-row power-of-two scales" if args.fp8 else "bf16",
+                   "mlp_second_product": "fp8 e4m3, D per (row, 32 units), W2 per column" if args.fp8_w2
+                   else "bf16"},
         "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "flop_per_step": fl,
         "roofline": roof,

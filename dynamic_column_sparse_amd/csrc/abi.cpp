@@ -54,8 +54,12 @@ int check_mlp(const chipmunk_mlp* L, bool need_score) {
   if (chipmunk::row_blocks(L->n) > kMaxGridY)
     return fail(CHIPMUNK_E_SHAPE, "n too large: %lld row blocks exceed %lld", (long long)chipmunk::row_blocks(L->n),
                 (long long)kMaxGridY);
-  if (L->flags & ~(CHIPMUNK_MLP_RESCORE | CHIPMUNK_MLP_FP8))
+  if (L->flags & ~(CHIPMUNK_MLP_RESCORE | CHIPMUNK_MLP_FP8 | CHIPMUNK_MLP_FP8_W2))
     return fail(CHIPMUNK_E_SHAPE, "unknown layer flags 0x%x", L->flags);
+  const bool fp8w = (L->flags & CHIPMUNK_MLP_FP8_W2) != 0;
+  if (fp8w && (!L->w2_f8 || !L->w2_scale))
+    return fail(CHIPMUNK_E_NULLPTR, "layer w2_f8 and w2_scale are required by CHIPMUNK_MLP_FP8_W2");
+  if (fp8w && !aligned(L->w2_f8, 16)) return fail(CHIPMUNK_E_ALIGN, "w2_f8 must be 16-byte aligned");
   const bool fp8 = (L->flags & CHIPMUNK_MLP_FP8) != 0;
   if ((!fp8 && !L->w1t) || !L->w2 || !L->a_cache)
     return fail(CHIPMUNK_E_NULLPTR, "layer w1t (unless FP8), w2 and a_cache are required");
@@ -102,6 +106,12 @@ size_t sparse_mlp_ws(int64_t n, int32_t k) {
 // fp8 copy of x: [n][d] e4m3 codes, then n scale bytes, rounded up to 16.
 size_t fp8_x_ws(int64_t n, int32_t d) { return ((size_t)n * (size_t)d + (size_t)n + 15) / 16 * 16; }
 bool is_fp8(const chipmunk_mlp* L) { return (L->flags & CHIPMUNK_MLP_FP8) != 0; }
+// Operands of the fp8 second product, or nullptr.
+const chipmunk::Fp8Cols* fp8_second(const chipmunk_mlp* L, chipmunk::Fp8Cols* buf) {
+  if (!(L->flags & CHIPMUNK_MLP_FP8_W2)) return nullptr;
+  *buf = {L->w2_f8, L->w2_scale};
+  return buf;
+}
 // Workspace of the sparse MLP delta of layer L at keep count k.
 size_t layer_sparse_ws(const chipmunk_mlp* L, int32_t k) {
   return sparse_mlp_ws(L->n, k) + (is_fp8(L) ? fp8_x_ws(L->n, L->d) : 0);
@@ -366,10 +376,13 @@ extern "C" int chipmunk_sparse_mlp_delta(const chipmunk_mlp* L, const uint16_t* 
     const chipmunk::Fp8Rows* f8 = nullptr;
     hipError_t e = prepare_fp8(L, x, ws, sparse_mlp_ws(L->n, k), &f8buf, &f8, s);
     if (e != hipSuccess) return hip_status(e, "quantize_fp8 launch");
+    chipmunk::Fp8Cols f8wbuf;
+    const chipmunk::Fp8Cols* f8w = fp8_second(L, &f8wbuf);
     e = chipmunk::launch_mlp_gemm1(false, x, L->w1t, L->b1, idx, L->a_cache, dbuf, a_new_packed, rescore_target(L),
-                                   L->n, L->d, L->h, k, s, f8);
+                                   L->n, L->d, L->h, k, s, f8, f8w != nullptr);
     if (e != hipSuccess) return hip_status(e, "mlp_gemm1 (sparse) launch");
-    e = chipmunk::launch_mlp_gemm2(false, dbuf, L->w2, idx, nullptr, y, L->n, L->d, L->h, k, chipmunk::padded_k(k), s);
+    e = chipmunk::launch_mlp_gemm2(false, dbuf, L->w2, idx, nullptr, y, L->n, L->d, L->h, k, chipmunk::padded_k(k), s,
+                                   f8w);
     return hip_status(e, "mlp_gemm2 (sparse) launch");
   } catch (...) {
     return fail(CHIPMUNK_E_INTERNAL, "internal error in chipmunk_sparse_mlp_delta");
@@ -451,6 +464,8 @@ extern "C" int chipmunk_sparse_step(const chipmunk_mlp* M, const uint16_t* x, co
                           {M->w1t, (size_t)M->h * M->d * 2, "w1t"},
                           {is_fp8(M) ? M->w1t_f8 : nullptr, (size_t)M->h * M->d, "w1t_f8"},
                           {is_fp8(M) ? M->w1t_scale : nullptr, (size_t)M->h, "w1t_scale"},
+                          {(M->flags & CHIPMUNK_MLP_FP8_W2) ? M->w2_f8 : nullptr, (size_t)M->h * M->d, "w2_f8"},
+                          {(M->flags & CHIPMUNK_MLP_FP8_W2) ? M->w2_scale : nullptr, (size_t)M->d, "w2_scale"},
                           {M->w2, (size_t)M->h * M->d * 2, "w2"},
                           {M->b1, M->b1 ? (size_t)M->h * 4 : 0, "b1"},
                           {mlp_idx, nb * mk * 4, "mlp idx"}};
@@ -478,10 +493,12 @@ extern "C" int chipmunk_sparse_step(const chipmunk_mlp* M, const uint16_t* x, co
       hipError_t e = prepare_fp8(M, x, ws, sparse_mlp_ws(M->n, k), &f8buf, &f8, s);
       if (e != hipSuccess) return hip_status(e, "quantize_fp8 launch");
     }
+    chipmunk::Fp8Cols f8wbuf;
+    const chipmunk::Fp8Cols* f8w = fp8_second(M, &f8wbuf);
     hipError_t e = chipmunk::launch_sparse_step(x, M->w1t, M->b1, mlp_idx, M->a_cache, static_cast<uint16_t*>(ws),
                                                 a_new_packed, rescore_target(M), M->w2, y, M->n, M->d, M->h, k, q,
                                                 kx, v, attn_idx, A->m, A->num, A->den, o, A->n, A->heads, kk,
-                                                A->scale, s, f8);
+                                                A->scale, s, f8, f8w);
     return hip_status(e, "sparse step launch");
   } catch (...) {
     return fail(CHIPMUNK_E_INTERNAL, "internal error in chipmunk_sparse_step");
@@ -505,6 +522,26 @@ extern "C" int chipmunk_quantize_fp8(const uint16_t* src, int64_t rows, int32_t 
                       "quantize_fp8 launch");
   } catch (...) {
     return fail(CHIPMUNK_E_INTERNAL, "internal error in chipmunk_quantize_fp8");
+  }
+}
+
+extern "C" int chipmunk_quantize_fp8_cols(const uint16_t* src, int64_t rows, int32_t cols, uint8_t* dst,
+                                          uint8_t* scale, void* stream) {
+  try {
+    if (rows < 0) return fail(CHIPMUNK_E_SHAPE, "rows must be >= 0");
+    if (cols < 8 || cols % 8 != 0) return fail(CHIPMUNK_E_SHAPE, "cols must be a positive multiple of 8 (got %d)", cols);
+    if (!src || !dst || !scale) return fail(CHIPMUNK_E_NULLPTR, "src, dst and scale are required");
+    if (!aligned(src, 16) || !aligned(dst, 16)) return fail(CHIPMUNK_E_ALIGN, "src and dst must be 16-byte aligned");
+    const Span in{src, (size_t)rows * (size_t)cols * 2, "src"};
+    const Span o1{dst, (size_t)rows * (size_t)cols, "dst"}, o2{scale, (size_t)cols, "scale"};
+    if (overlap(in, o1) || overlap(in, o2) || overlap(o1, o2))
+      return fail(CHIPMUNK_E_SHAPE, "src, dst and scale must not overlap");
+    if (rows == 0) return ok();
+    return hip_status(
+        chipmunk::launch_quantize_fp8_cols(src, rows, cols, dst, scale, static_cast<hipStream_t>(stream)),
+        "quantize_fp8_cols launch");
+  } catch (...) {
+    return fail(CHIPMUNK_E_INTERNAL, "internal error in chipmunk_quantize_fp8_cols");
   }
 }
 

@@ -260,6 +260,43 @@ __device__ __forceinline__ float gelu_tanh(float z) {
   return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(t));
 }
 
+// fp8 (OCP e4m3) power-of-two scale of a set of values whose largest |bf16|
+// bit pattern (sign cleared) is mx: the smallest e >= -126 with
+// max * 2^-e <= 448 (e = 0 when mx = 0).  With the maximum as fp32
+// 2^(E-127) (1 + f/2^23) and 448 = 1.75 * 2^8: e = E - 135, plus one when
+// 1 + f/2^23 > 1.75.
+__device__ __forceinline__ int fp8_exponent(uint32_t mx) {
+  if (mx == 0) return 0;
+  const uint32_t ab = mx << 16;
+  const int E = (int)(ab >> 23), f = (int)(ab & 0x7fffff);
+  return E == 0 ? -126 : max(E - 135 + (f > 0x600000 ? 1 : 0), -126);
+}
+// Largest |bf16| bit pattern among the 8 values of v (sign bits cleared).
+__device__ __forceinline__ uint32_t abs_max_bf16x8(const uint4& v) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t mx = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) mx = max(mx, max(w[i] & 0x7fffu, (w[i] >> 16) & 0x7fffu));
+  return mx;
+}
+// 8 bf16 values times 2^-e (exact) as e4m3 codes, rounded to nearest even
+// (v_cvt_pk_fp8_f32); the caller's scale keeps every product within 448.
+__device__ __forceinline__ uint2 bf16x8_to_fp8(const uint4& v, int e) {
+  const float mul = __uint_as_float((uint32_t)(127 - e) << 23);   // 2^-e
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  float x[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = bf2f(w[i] & 0xffffu) * mul;
+    x[2 * i + 1] = bf2f(w[i] >> 16) * mul;
+  }
+  int lo = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
+  lo = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], lo, true);
+  int hi = __builtin_amdgcn_cvt_pk_fp8_f32(x[4], x[5], 0, false);
+  hi = __builtin_amdgcn_cvt_pk_fp8_f32(x[6], x[7], hi, true);
+  return make_uint2((uint32_t)lo, (uint32_t)hi);
+}
+
 __device__ __forceinline__ int clamp_index(int j, int hi) { return j < 0 ? 0 : (j >= hi ? hi - 1 : j); }
 
 // Workgroups are handed to the 8 XCDs round-robin by linear id.  This maps the

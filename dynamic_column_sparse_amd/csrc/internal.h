@@ -46,21 +46,32 @@ struct Fp8Rows {
   const uint8_t* w;
   const uint8_t* w_scale;
 };
+// fp8 W2 of the fp8 second product: e4m3 codes [h][d] with one E8M0 scale
+// byte per column (output feature).
+struct Fp8Cols {
+  const uint8_t* w;
+  const uint8_t* w_scale;
+};
 // MLP phase 1: gathered x W1[:,S] + GELU, then either the sparse epilogue
 // (D tiles, cache writeback; with a score array, also S's column L1 of D) or
 // the dense one (score, full cache write).  f8 non-NULL: the product runs on
-// the fp8 operands instead of x and w1t.
+// the fp8 operands instead of x and w1t; fp8_d (sparse): D leaves as fp8
+// codes with (row, 32-unit) scales for the fp8 second product.
 hipError_t launch_mlp_gemm1(bool dense, const uint16_t* x, const uint16_t* w1t, const float* b1,
                             const int32_t* idx, uint16_t* a_cache, uint16_t* dbuf, uint16_t* a_packed,
                             float* score, int64_t n, int d, int h, int k, hipStream_t s,
-                            const Fp8Rows* f8 = nullptr);
+                            const Fp8Rows* f8 = nullptr, bool fp8_d = false);
 // Row-wise fp8 quantization of a bf16 [rows][cols] matrix (cols % 8 == 0).
 hipError_t launch_quantize_fp8(const uint16_t* src, int64_t rows, int cols, uint8_t* dst, uint8_t* scale,
                                hipStream_t s);
+// Column-wise: scale[c] for each column (cols % 8 == 0).
+hipError_t launch_quantize_fp8_cols(const uint16_t* src, int64_t rows, int cols, uint8_t* dst, uint8_t* scale,
+                                    hipStream_t s);
 // MLP phase 2: y (+)= src[b] W2[S] where src is [nb][kc][128] (D tiles, or the cache).
+// f8w (sparse only): src holds phase 1's fp8 D and the product runs on f8w.
 hipError_t launch_mlp_gemm2(bool dense, const uint16_t* src, const uint16_t* w2, const int32_t* idx,
                             const float* b2, float* y, int64_t n, int d, int h, int k, int kc,
-                            hipStream_t s);
+                            hipStream_t s, const Fp8Cols* f8w = nullptr);
 hipError_t launch_writeback(const uint16_t* packed, const int32_t* idx, uint16_t* a_cache, int64_t n, int h,
                             int k, hipStream_t s);
 hipError_t launch_topk(const float* score, int64_t rows, int64_t cols, int k, int32_t* idx, hipStream_t s);
@@ -83,6 +94,6 @@ hipError_t launch_sparse_step(const uint16_t* x, const uint16_t* w1t, const floa
                               int64_t n, int d, int h, int k, const uint16_t* q, const uint16_t* kx,
                               const uint16_t* v, const int32_t* aidx, const float* m, const float* num,
                               const float* den, float* o, int64_t na, int heads, int kk, float scale,
-                              hipStream_t s, const Fp8Rows* f8 = nullptr);
+                              hipStream_t s, const Fp8Rows* f8 = nullptr, const Fp8Cols* f8w = nullptr);
 
 }  // namespace chipmunk

@@ -12,7 +12,8 @@ constexpr int kWideWastePct = MLP_WIDE_WASTE_PCT;
 
 hipError_t launch_mlp_gemm1(bool dense, const uint16_t* x, const uint16_t* w1t, const float* b1,
                             const int32_t* idx, uint16_t* a_cache, uint16_t* dbuf, uint16_t* a_packed,
-                            float* score, int64_t n, int d, int h, int k, hipStream_t s, const Fp8Rows* f8) {
+                            float* score, int64_t n, int d, int h, int k, hipStream_t s, const Fp8Rows* f8,
+                            bool fp8_d) {
   const int nb = (int)row_blocks(n);
   const int cols = dense ? h : k;
   const int kp = padded_k(k);
@@ -25,15 +26,22 @@ hipError_t launch_mlp_gemm1(bool dense, const uint16_t* x, const uint16_t* w1t, 
   const uint8_t* xs = f8 ? f8->x_scale : nullptr;
   const uint8_t* ws = f8 ? f8->w_scale : nullptr;
   const dim3 grid((unsigned)xcd_grid((wide ? t256 : t128) * nb));
-#define G1_LAUNCH(BN_, DENSE_, F8_)                                                                               \
-  hipLaunchKernelGGL((mlp_gemm1<BN_, DENSE_, F8_>), grid, dim3(256), 0, s, xa, wa, xs, ws, b1, idx, a_cache, dbuf, \
-                     a_packed, score, n, d, h, k, kp)
-#define G1_LAUNCH_F8(BN_, DENSE_) \
-  {                               \
-    if (f8)                       \
-      G1_LAUNCH(BN_, DENSE_, true);  \
-    else                          \
-      G1_LAUNCH(BN_, DENSE_, false); \
+#define G1_LAUNCH(BN_, DENSE_, F8_, FD_)                                                                    \
+  hipLaunchKernelGGL((mlp_gemm1<BN_, DENSE_, F8_, FD_>), grid, dim3(256), 0, s, xa, wa, xs, ws, b1, idx, a_cache, \
+                     dbuf, a_packed, score, n, d, h, k, kp)
+  // (the dense step writes no D, so it has no fp8-D form)
+#define G1_LAUNCH_F8(BN_, DENSE_)                 \
+  {                                               \
+    if (!DENSE_ && fp8_d) {                       \
+      if (f8)                                     \
+        G1_LAUNCH(BN_, false, true, true);        \
+      else                                        \
+        G1_LAUNCH(BN_, false, false, true);       \
+    } else if (f8) {                              \
+      G1_LAUNCH(BN_, DENSE_, true, false);        \
+    } else {                                      \
+      G1_LAUNCH(BN_, DENSE_, false, false);       \
+    }                                             \
   }
   timing_before(kid, s);
   if (wide) {
@@ -55,7 +63,8 @@ hipError_t launch_mlp_gemm1(bool dense, const uint16_t* x, const uint16_t* w1t, 
 }
 
 hipError_t launch_mlp_gemm2(bool dense, const uint16_t* src, const uint16_t* w2, const int32_t* idx,
-                            const float* b2, float* y, int64_t n, int d, int h, int k, int kp, hipStream_t s) {
+                            const float* b2, float* y, int64_t n, int d, int h, int k, int kp, hipStream_t s,
+                            const Fp8Cols* f8w) {
   const int nb = (int)row_blocks(n);
   const int kid = dense ? K_MLP_GEMM2_DENSE : K_MLP_GEMM2_SPARSE;
   const int bn = d % 256 == 0 ? 256 : 128;
@@ -66,6 +75,14 @@ hipError_t launch_mlp_gemm2(bool dense, const uint16_t* src, const uint16_t* w2,
       hipLaunchKernelGGL((mlp_gemm2<256, true>), grid, dim3(256), 0, s, src, w2, idx, b2, y, n, d, h, k, kp);
     else
       hipLaunchKernelGGL((mlp_gemm2<128, true>), grid, dim3(256), 0, s, src, w2, idx, b2, y, n, d, h, k, kp);
+  } else if (f8w) {
+    const unsigned char* d8 = (const unsigned char*)src;
+    if (bn == 256)
+      hipLaunchKernelGGL((mlp_gemm2_rows_f8<256>), grid, dim3(256), 0, s, d8, f8w->w, f8w->w_scale, idx, y, n, d, h,
+                         k, kp);
+    else
+      hipLaunchKernelGGL((mlp_gemm2_rows_f8<128>), grid, dim3(256), 0, s, d8, f8w->w, f8w->w_scale, idx, y, n, d, h,
+                         k, kp);
   } else {
     if (bn == 256)
       hipLaunchKernelGGL((mlp_gemm2_rows<256>), grid, dim3(256), 0, s, src, w2, idx, y, n, d, h, k, kp);

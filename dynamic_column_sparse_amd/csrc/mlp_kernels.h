@@ -48,7 +48,13 @@ constexpr int kGroupTiles = MLP_GROUP_TILES;   // column tiles of one row block 
 // l/32) that feed the two bf16 substeps.  The row scales are fixed for a
 // tile, so each lane keeps its row's and its column's scale byte in a
 // register for the whole loop; the products come out scaled.
-template <int BN, bool DENSE, bool F8>
+//
+// FD (sparse only): D leaves as e4m3 codes for the fp8 second product instead
+// of bf16: dbuf holds [nb][128][kp] codes, followed by one E8M0 scale byte per
+// (row, 32 consecutive units), stored per 64-unit chunk as [nb][kp/64][128][2]
+// so that the second product streams a chunk's scales with its codes.  D is
+// first rounded to bf16, as the bf16 path stores it.
+template <int BN, bool DENSE, bool F8, bool FD>
 __global__ __launch_bounds__(256, 2) void mlp_gemm1(const void* __restrict__ xv,
                                                     const void* __restrict__ wv,
                                                     const uint8_t* __restrict__ xs,
@@ -322,11 +328,28 @@ __global__ __launch_bounds__(256, 2) void mlp_gemm1(const void* __restrict__ xv,
       const int t0 = u8 * 8 + (j >> 2), t1 = t0 + 4;
       const i16x4_t lo = lds_read_tr16((const uint16_t*)(stile + t0 * 256 + (((mp >> 3) ^ (t0 & 15)) << 4) + (mp & 7) * 2));
       const i16x4_t hi = lds_read_tr16((const uint16_t*)(stile + t1 * 256 + (((mp >> 3) ^ (t1 & 15)) << 4) + (mp & 7) * 2));
-      if (p < kp) {
-        const int m = mb * 16 + j;
-        const uint4 v = make_uint4((uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16), (uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16),
-                                   (uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16), (uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16));
-        *(uint4*)(dbuf + ((int64_t)b * BM + m) * kp + p) = v;
+      const int m = mb * 16 + j;
+      const uint4 v = make_uint4((uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16), (uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16),
+                                 (uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16), (uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16));
+      if constexpr (FD) {
+        // The wave's four 16-lane groups hold units u8 = 4w'..4w'+3 (32
+        // consecutive units, one scale block) of the same 16 rows: lanes j,
+        // j+16, j+32, j+48 share row m, and two exchanges give the block's
+        // maximum.  A block is wholly below kp or wholly past it (kp % 64 == 0).
+        uint32_t mx = abs_max_bf16x8(v);
+        mx = max(mx, (uint32_t)__shfl_xor((int)mx, 16));
+        mx = max(mx, (uint32_t)__shfl_xor((int)mx, 32));
+        const int e = fp8_exponent(mx);
+        if (p < kp) {
+          unsigned char* d8 = (unsigned char*)dbuf;
+          *(uint2*)(d8 + ((int64_t)b * BM + m) * kp + p) = bf16x8_to_fp8(v, e);
+          if (grp == 0) {
+            unsigned char* dsc = d8 + (int64_t)nb * BM * kp;
+            dsc[(((int64_t)b * (kp / 64) + p / 64) * BM + m) * 2 + ((p >> 5) & 1)] = (unsigned char)(127 + e);
+          }
+        }
+      } else {
+        if (p < kp) *(uint4*)(dbuf + ((int64_t)b * BM + m) * kp + p) = v;
       }
     }
   }
@@ -690,6 +713,225 @@ __device__ __forceinline__ void gemm2_rows_body(int lin, unsigned char* smem, in
         float* yrow = y + (r0 + R) * (int64_t)d + n0 + ni * 32;
         if (full || R + mhalf < rows) yrow[lane_off] = acc[mi][ni][r];
       }
+}
+
+// Sparse phase 2 on fp8 operands (the fp8 second product): D as e4m3 codes
+// with a scale byte per (row, 32 units) (written by phase 1, see FD above) and
+// the gathered W2 rows as e4m3 codes with one scale per output column.  The
+// ring and its accounting are those of gemm2_rows_body with 64-unit chunks:
+// a stage holds D's 128 rows x 64 bytes, 64 gathered W2 rows x BN bytes and
+// the chunk's 256 D scale bytes (one 4-byte direct load of 16 lanes per
+// wave, so every wave issues the same number of loads per stage).  W2 rows
+// store 16-byte chunk c at c ^ (row % 8); each fp8 B operand is four 8-bit
+// transposing reads (ds_read_b64_tr_b8: within 16 lanes, lane i receives byte
+// i % 8 of the vectors that lanes 2e + i/8 read, e = 0..7), lane pair 2e, 2e+1
+// pointing at row k0 + e, columns c .. c+7 and c+8 .. c+15, so that lane i
+// gets column c + i of rows k0 .. k0+7.  Four runs of 8 rows (K bytes 16g..,
+// 16g+8.., 32+16g.., 40+16g.. for g = lane/32) make the operand layout of
+// v_mfma_scale_f32_32x32x64_f8f6f4.  The D scales are read per product from
+// the stage (a byte per lane: row lane%32, block lane/32); the W2 column
+// scales stay in registers.
+template <int BN>
+struct Gemm2RowsF8Lds {
+  static constexpr int kStage = BM * 64 + 64 * BN + 256;
+  static constexpr int kRing = 3 * kStage;
+  static constexpr int kIds = 8 * 64;
+};
+
+__device__ __forceinline__ uint2 lds_read_tr8(const unsigned char* p) {
+  typedef int v2i_t __attribute__((ext_vector_type(2)));
+  typedef __attribute__((address_space(3))) v2i_t lds_v2i;
+  const v2i_t r = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(p));
+  return make_uint2((uint32_t)r[0], (uint32_t)r[1]);
+}
+
+template <int BN>
+__device__ __forceinline__ void gemm2_rows_body_f8(int lin, unsigned char* smem, int (*sIdx)[64],
+                                                   const unsigned char* __restrict__ dsrc,
+                                                   const unsigned char* __restrict__ w2,
+                                                   const uint8_t* __restrict__ w2s, const int32_t* __restrict__ idx,
+                                                   float* __restrict__ y, int64_t n, int d, int h, int k, int kp) {
+  constexpr int BK = 64, NS = 3;
+  constexpr int WN = BN / 4, NI = WN / 32, MI = BM / 32;
+  constexpr int D_ROWB = 64;                 // 64 units of a D row
+  constexpr int W_ROWB = BN;                 // a W2 row of the tile
+  constexpr int D_BYTES = BM * D_ROWB;       // 8 KB
+  constexpr int W_BYTES = BK * W_ROWB;
+  constexpr int STAGE = D_BYTES + W_BYTES + 256;
+  constexpr int D_RPI = 1024 / D_ROWB;
+  constexpr int W_RPI = 1024 / W_ROWB;
+  constexpr int D_INS = BM / D_RPI / 4;
+  constexpr int W_INS = BK / W_RPI / 4;
+  constexpr int L = D_INS + W_INS + 1;       // + the scale bytes
+  constexpr int WCH = BN / 16;               // 16-byte chunks per W2 tile row
+  static_assert(NS * STAGE == Gemm2RowsF8Lds<BN>::kRing, "LDS layout");
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t smem_lds = lds_addr(smem);
+  const int nb = (int)row_blocks(n), ntn = d / BN;
+  const int u = xcd_unit(lin, ntn * nb);
+  if (u >= ntn * nb) return;
+  int b, tile;
+  grouped_tile(u, nb, ntn, kGroupTiles, b, tile);
+  const int n0 = tile * BN;
+  const int64_t r0 = (int64_t)b * BM;
+  const int rows = (int)(n - r0 < BM ? n - r0 : BM);
+  const int KT = kp / BK;
+  const unsigned char* dblk = dsrc + (int64_t)b * BM * kp;
+  const unsigned char* sblk = dsrc + (int64_t)nb * BM * kp + (int64_t)b * KT * 256;   // chunk scales
+  const int32_t* sidx = idx + (int64_t)b * k;
+
+  // D: row (instruction's first row + lane/4), physical chunk lane%4, logical
+  // chunk (lane%4) ^ swz4(row).  W2: row (instruction's first row + lane/WCH),
+  // physical chunk lane%WCH, logical chunk (lane%WCH) ^ (row % 8).
+  const int d_lr = lane >> 2, d_pc = lane & 3;
+  const int w_lr = lane / WCH, w_pc = lane % WCH;
+  const unsigned char* dsrc_l[D_INS];
+#pragma unroll
+  for (int i = 0; i < D_INS; ++i) {
+    const int r = (wave * D_INS + i) * D_RPI + d_lr;
+    dsrc_l[i] = dblk + (int64_t)r * kp + ((d_pc ^ swz4(r)) << 4);
+  }
+  int w_row[W_INS], w_off[W_INS];
+#pragma unroll
+  for (int i = 0; i < W_INS; ++i) {
+    const int r = (wave * W_INS + i) * W_RPI + w_lr;
+    w_row[i] = r;
+    w_off[i] = n0 + ((w_pc ^ (r & 7)) << 4);
+  }
+  auto load_ids = [&](int t, int (&ids)[W_INS]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < W_INS; ++i) ids[i] = clamp_index(sIdx[t & 7][w_row[i]], h);
+  };
+  auto id_dma = [&](int t) __attribute__((always_inline)) {
+    if (wave == 0) {
+      const int j = t * BK + lane;
+      dma4_at(sidx + (j < k ? j : 0), lds_addr(&sIdx[t & 7][0]));
+    }
+  };
+#define G2F_ISSUE(kt_, buf_, ids_)                                                                  \
+  {                                                                                                 \
+    const uint32_t st_ = smem_lds + (buf_) * STAGE;                                                 \
+    _Pragma("unroll") for (int i = 0; i < D_INS; ++i)                                               \
+        dma16_at(dsrc_l[i] + (kt_) * BK, st_ + (wave * D_INS + i) * 1024);                          \
+    _Pragma("unroll") for (int i = 0; i < W_INS; ++i)                                               \
+        dma16_at(w2 + (int64_t)ids_[i] * d + w_off[i], st_ + D_BYTES + (wave * W_INS + i) * 1024);  \
+    if (lane < 16) dma4_at(sblk + (kt_) * 256 + wave * 64 + lane * 4, st_ + D_BYTES + W_BYTES + wave * 64); \
+  }
+
+  f32x16_t acc[MI][NI];
+  if (wave == 0) {
+#pragma unroll
+    for (int t = 0; t < 6; ++t)
+      if (t < KT) dma4_at(sidx + (t * BK + lane < k ? t * BK + lane : 0), lds_addr(&sIdx[t][0]));
+  }
+  wait_vmcnt<0>();
+  __syncthreads();
+  int ids_a[W_INS], ids_b[W_INS];
+  load_ids(0, ids_a);
+  G2F_ISSUE(0, 0, ids_a);
+  if (KT > 1) {
+    load_ids(1, ids_a);
+    G2F_ISSUE(1, 1, ids_a);
+  }
+  if (KT > 2) load_ids(2, ids_a);
+  // W2 column scales of this lane's output columns, then the tile's old y.
+  int sb[NI];
+#pragma unroll
+  for (int ni = 0; ni < NI; ++ni) sb[ni] = w2s[n0 + wave * WN + ni * 32 + (lane & 31)];
+  const int lane_off = (lane >> 5) * 4 * d + wave * WN + (lane & 31);
+  const int mhalf = (lane >> 5) * 4;
+  const bool full = rows == BM;
+#pragma unroll
+  for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int R = mi * 32 + (r >> 2) * 8 + (r & 3);
+        if (full) {
+          acc[mi][ni][r] = y[(r0 + R) * (int64_t)d + n0 + ni * 32 + lane_off];
+        } else {
+          const int rr = R + mhalf < rows ? R + mhalf : rows - 1;
+          acc[mi][ni][r] = y[(r0 + rr) * (int64_t)d + n0 + ni * 32 + wave * WN + (lane & 31)];
+        }
+      }
+
+  typedef int i32x4_t __attribute__((ext_vector_type(4)));
+  typedef int i32x8_t __attribute__((ext_vector_type(8)));
+  const int sw = swz4(lane & 31);
+  const int g = lane >> 5;
+  // transposing-read geometry: lane pair (2e, 2e+1) of a 16-lane group reads
+  // row e of a run, bytes (lane%2)*8 of the group's 16-column chunk
+  const int tj = lane & 15, trow = tj >> 1, thalf = (tj & 1) * 8;
+  for (int kt = 0; kt < KT; ++kt) {
+    if (kt + 1 < KT) {
+      if (wave == 0 && kt >= 1 && kt + 5 < KT)
+        wait_vmcnt<L + 1>();
+      else
+        wait_vmcnt<L>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    barrier();
+    if (kt + 6 < KT) id_dma(kt + 6);
+    if (kt + 2 < KT) G2F_ISSUE(kt + 2, (kt + 2) % NS, ids_a);
+    if (kt + 3 < KT) load_ids(kt + 3, ids_b);
+    const unsigned char* st = smem + (kt % NS) * STAGE;
+    const unsigned char* sw2 = st + D_BYTES;
+    const unsigned char* ssc = st + D_BYTES + W_BYTES;
+    i32x8_t bop[NI];
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) {
+      const int cchunk = (wave * WN + ni * 32 + (lane & 16)) >> 4;   // the group's 16-column chunk
+      uint2 q[4];
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int krow = (rr >> 1) * 32 + (rr & 1) * 8 + g * 16 + trow;
+        q[rr] = lds_read_tr8(sw2 + krow * W_ROWB + ((cchunk ^ (krow & 7)) << 4) + thalf);
+      }
+      const i32x8_t v = {(int)q[0].x, (int)q[0].y, (int)q[1].x, (int)q[1].y,
+                         (int)q[2].x, (int)q[2].y, (int)q[3].x, (int)q[3].y};
+      bop[ni] = v;
+    }
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+      const unsigned char* arow = st + (mi * 32 + (lane & 31)) * D_ROWB;
+      const i32x4_t lo = *(const i32x4_t*)(arow + ((g ^ sw) << 4));
+      const i32x4_t hi = *(const i32x4_t*)(arow + (((2 + g) ^ sw) << 4));
+      const i32x8_t aop = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      const int sa = ssc[(mi * 32 + (lane & 31)) * 2 + g];
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni)
+        acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aop, bop[ni], acc[mi][ni], 0, 0, 0, sa, 0, sb[ni]);
+    }
+#pragma unroll
+    for (int i = 0; i < W_INS; ++i) ids_a[i] = ids_b[i];
+  }
+#undef G2F_ISSUE
+
+#pragma unroll
+  for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int R = mi * 32 + (r >> 2) * 8 + (r & 3);
+        float* yrow = y + (r0 + R) * (int64_t)d + n0 + ni * 32;
+        if (full || R + mhalf < rows) yrow[lane_off] = acc[mi][ni][r];
+      }
+}
+
+template <int BN>
+__global__ __launch_bounds__(256, 2) void mlp_gemm2_rows_f8(const unsigned char* __restrict__ dsrc,
+                                                            const unsigned char* __restrict__ w2,
+                                                            const uint8_t* __restrict__ w2s,
+                                                            const int32_t* __restrict__ idx, float* __restrict__ y,
+                                                            int64_t n, int d, int h, int k, int kp) {
+  __shared__ __align__(16) unsigned char smem[Gemm2RowsF8Lds<BN>::kRing];
+  __shared__ __align__(16) int sIdx[8][64];
+  gemm2_rows_body_f8<BN>(blockIdx.x, smem, sIdx, dsrc, w2, w2s, idx, y, n, d, h, k, kp);
 }
 
 template <int BN>

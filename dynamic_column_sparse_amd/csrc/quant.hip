@@ -19,29 +19,6 @@ namespace {
 
 constexpr int kCachedUnits = 8;   // 16-byte units per lane kept in registers (rows up to 4096)
 
-__device__ __forceinline__ uint32_t abs_max8(const uint4& v) {
-  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-  uint32_t mx = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) mx = max(mx, max(w[i] & 0x7fffu, (w[i] >> 16) & 0x7fffu));
-  return mx;
-}
-
-__device__ __forceinline__ uint2 to_fp8x8(const uint4& v, float mul) {
-  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-  float x[8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    x[2 * i] = bf2f(w[i] & 0xffffu) * mul;
-    x[2 * i + 1] = bf2f(w[i] >> 16) * mul;
-  }
-  int lo = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
-  lo = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], lo, true);
-  int hi = __builtin_amdgcn_cvt_pk_fp8_f32(x[4], x[5], 0, false);
-  hi = __builtin_amdgcn_cvt_pk_fp8_f32(x[6], x[7], hi, true);
-  return make_uint2((uint32_t)lo, (uint32_t)hi);
-}
-
 template <bool CACHED>
 __global__ __launch_bounds__(256) void quantize_fp8_rows(const uint16_t* __restrict__ src, int64_t rows, int cols,
                                                          uint8_t* __restrict__ dst, uint8_t* __restrict__ scale) {
@@ -61,32 +38,96 @@ __global__ __launch_bounds__(256) void quantize_fp8_rows(const uint16_t* __restr
       keep[i] = u < units ? *(const uint4*)(s + u * 8) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
-    for (int i = 0; i < kCachedUnits; ++i) mx = max(mx, abs_max8(keep[i]));
+    for (int i = 0; i < kCachedUnits; ++i) mx = max(mx, abs_max_bf16x8(keep[i]));
   } else {
-    for (int u = lane; u < units; u += 64) mx = max(mx, abs_max8(*(const uint4*)(s + u * 8)));
+    for (int u = lane; u < units; u += 64) mx = max(mx, abs_max_bf16x8(*(const uint4*)(s + u * 8)));
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, off));
-  // amax = 2^(E-127) (1 + f/2^23) as fp32; with 448 = 1.75 * 2^8 the smallest
-  // fitting exponent is E - 135, plus one when 1 + f/2^23 > 1.75.
-  const uint32_t ab = mx << 16;
-  const int E = (int)(ab >> 23), f = (int)(ab & 0x7fffff);
-  int e = 0;
-  if (mx != 0) e = E == 0 ? -126 : max(E - 135 + (f > 0x600000 ? 1 : 0), -126);
+  const int e = fp8_exponent(mx);
   if (lane == 0) scale[row] = (uint8_t)(127 + e);
-  const float mul = __uint_as_float((uint32_t)(127 - e) << 23);   // 2^-e, exact
   if (CACHED) {
 #pragma unroll
     for (int i = 0; i < kCachedUnits; ++i) {
       const int u = lane + 64 * i;
-      if (u < units) *(uint2*)(o + u * 8) = to_fp8x8(keep[i], mul);
+      if (u < units) *(uint2*)(o + u * 8) = bf16x8_to_fp8(keep[i], e);
     }
   } else {
-    for (int u = lane; u < units; u += 64) *(uint2*)(o + u * 8) = to_fp8x8(*(const uint4*)(s + u * 8), mul);
+    for (int u = lane; u < units; u += 64) *(uint2*)(o + u * 8) = bf16x8_to_fp8(*(const uint4*)(s + u * 8), e);
+  }
+}
+
+// Column-wise variant (the output features of W2 for the fp8 second product):
+// every column gets its own power-of-two scale, the same rule as a row above.
+// One workgroup per strip of 128 columns: thread (row group rg = t/16, column
+// group cg = t%16) takes 8 columns (16-byte loads) of rows rg, rg+16, ...; the
+// 16 partial maxima of a column meet in LDS, then each thread converts its
+// rows again with its columns' scales.  Used once per layer at set-up.
+__global__ __launch_bounds__(256) void quantize_fp8_cols(const uint16_t* __restrict__ src, int64_t rows, int cols,
+                                                         uint8_t* __restrict__ dst, uint8_t* __restrict__ scale) {
+  __shared__ uint32_t smax[16][128 + 1];
+  __shared__ int sexp[128];
+  const int t = threadIdx.x, cg = t & 15, rg = t >> 4;
+  const int c0 = blockIdx.x * 128 + cg * 8;
+  const bool live = c0 < cols;   // cols % 8 == 0: a column group is wholly in or out
+  uint32_t mx[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) mx[e] = 0;
+  if (live) {
+    for (int64_t r = rg; r < rows; r += 16) {
+      const uint4 v = *(const uint4*)(src + r * cols + c0);
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        mx[2 * i] = max(mx[2 * i], w[i] & 0x7fffu);
+        mx[2 * i + 1] = max(mx[2 * i + 1], (w[i] >> 16) & 0x7fffu);
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) smax[rg][cg * 8 + e] = mx[e];
+  __syncthreads();
+  if (t < 128) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int g = 0; g < 16; ++g) m = max(m, smax[g][t]);
+    const int e = fp8_exponent(m);
+    sexp[t] = e;
+    if (blockIdx.x * 128 + t < cols) scale[blockIdx.x * 128 + t] = (uint8_t)(127 + e);
+  }
+  __syncthreads();
+  if (!live) return;
+  float mul[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) mul[e] = __uint_as_float((uint32_t)(127 - sexp[cg * 8 + e]) << 23);
+  for (int64_t r = rg; r < rows; r += 16) {
+    const uint4 v = *(const uint4*)(src + r * cols + c0);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    float x[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = bf2f(w[i] & 0xffffu) * mul[2 * i];
+      x[2 * i + 1] = bf2f(w[i] >> 16) * mul[2 * i + 1];
+    }
+    int lo = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
+    lo = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], lo, true);
+    int hi = __builtin_amdgcn_cvt_pk_fp8_f32(x[4], x[5], 0, false);
+    hi = __builtin_amdgcn_cvt_pk_fp8_f32(x[6], x[7], hi, true);
+    *(uint2*)(dst + r * cols + c0) = make_uint2((uint32_t)lo, (uint32_t)hi);
   }
 }
 
 }  // namespace
+
+hipError_t launch_quantize_fp8_cols(const uint16_t* src, int64_t rows, int cols, uint8_t* dst, uint8_t* scale,
+                                    hipStream_t s) {
+  const dim3 grid((unsigned)((cols + 127) / 128));
+  timing_before(K_QUANTIZE_FP8, s);
+  hipLaunchKernelGGL(quantize_fp8_cols, grid, dim3(256), 0, s, src, rows, cols, dst, scale);
+  hipError_t e = hipGetLastError();
+  timing_after(K_QUANTIZE_FP8, s);
+  return e;
+}
 
 hipError_t launch_quantize_fp8(const uint16_t* src, int64_t rows, int cols, uint8_t* dst, uint8_t* scale,
                                hipStream_t s) {

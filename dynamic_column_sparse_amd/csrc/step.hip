@@ -22,26 +22,34 @@ constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
 // blockIdx.x < g2: phase-2 unit blockIdx.x of xcd_grid(ntn * nb) units.
 // Otherwise: attention unit blockIdx.x - g2.  g2 is a multiple of 8, so both
-// bodies keep their own unit -> XCD mapping (unit id mod 8).
-template <int BN>
+// bodies keep their own unit -> XCD mapping (unit id mod 8).  F8W: the phase-2
+// tiles run the fp8 second product (fp8 D from phase 1, fp8 W2 rows).
+template <int BN, bool F8W>
 __global__ __launch_bounds__(256, 2) void sparse_step_fused(
-    int g2, const uint16_t* __restrict__ dsrc, const uint16_t* __restrict__ w2, const int32_t* __restrict__ midx,
-    float* __restrict__ y, int64_t n, int d, int h, int k, int kp, const uint16_t* __restrict__ q,
-    const uint16_t* __restrict__ kx, const uint16_t* __restrict__ v, const int32_t* __restrict__ aidx,
-    const float* __restrict__ m, const float* __restrict__ num, const float* __restrict__ den,
-    float* __restrict__ o, int64_t na, int heads, int kk, float scale) {
-  __shared__ __align__(16) unsigned char smem[cmax(Gemm2RowsLds<BN>::kRing, AttnSparseLds::kRing)];
-  __shared__ __align__(16) int sIdx[8][32];
+    int g2, const uint16_t* __restrict__ dsrc, const uint16_t* __restrict__ w2, const uint8_t* __restrict__ w2f8,
+    const uint8_t* __restrict__ w2s, const int32_t* __restrict__ midx, float* __restrict__ y, int64_t n, int d, int h,
+    int k, int kp, const uint16_t* __restrict__ q, const uint16_t* __restrict__ kx, const uint16_t* __restrict__ v,
+    const int32_t* __restrict__ aidx, const float* __restrict__ m, const float* __restrict__ num,
+    const float* __restrict__ den, float* __restrict__ o, int64_t na, int heads, int kk, float scale) {
+  constexpr int kG2Ring = F8W ? Gemm2RowsF8Lds<BN>::kRing : Gemm2RowsLds<BN>::kRing;
+  constexpr int kG2Ids = F8W ? Gemm2RowsF8Lds<BN>::kIds : Gemm2RowsLds<BN>::kIds;
+  __shared__ __align__(16) unsigned char smem[cmax(kG2Ring, AttnSparseLds::kRing)];
+  __shared__ __align__(16) int sIdx[cmax(kG2Ids, AttnSparseLds::kIds)];
   __shared__ float sDen[kRowBlock];
   __shared__ float sDenRest[kRowBlock];
-  static_assert(Gemm2RowsLds<BN>::kIds == 8 * 32 && AttnSparseLds::kIds == 8 * 32, "id ring size");
+  static_assert(AttnSparseLds::kIds == 8 * 32, "id ring size");
   const int bid = blockIdx.x;
-  if (bid < g2)
-    gemm2_rows_body<BN>(bid, smem, sIdx, dsrc, w2, midx, y, n, d, h, k, kp);
-  else
+  if (bid < g2) {
+    if constexpr (F8W)
+      gemm2_rows_body_f8<BN>(bid, smem, reinterpret_cast<int(*)[64]>(sIdx), (const unsigned char*)dsrc, w2f8, w2s,
+                             midx, y, n, d, h, k, kp);
+    else
+      gemm2_rows_body<BN>(bid, smem, reinterpret_cast<int(*)[32]>(sIdx), dsrc, w2, midx, y, n, d, h, k, kp);
+  } else {
     // The sparse (non-refresh) body only reads num and den.
-    attn_sparse_body<false>(bid - g2, smem, sIdx, sDen, sDenRest, q, kx, v, aidx, m, const_cast<float*>(num),
-                            const_cast<float*>(den), o, na, heads, kk, scale);
+    attn_sparse_body<false>(bid - g2, smem, reinterpret_cast<int(*)[32]>(sIdx), sDen, sDenRest, q, kx, v, aidx, m,
+                            const_cast<float*>(num), const_cast<float*>(den), o, na, heads, kk, scale);
+  }
 }
 
 }  // namespace
@@ -51,24 +59,36 @@ hipError_t launch_sparse_step(const uint16_t* x, const uint16_t* w1t, const floa
                               const uint16_t* w2, float* y, int64_t n, int d, int h, int k, const uint16_t* q,
                               const uint16_t* kx, const uint16_t* v, const int32_t* aidx, const float* m,
                               const float* num, const float* den, float* o, int64_t na, int heads, int kk,
-                              float scale, hipStream_t s, const Fp8Rows* f8) {
+                              float scale, hipStream_t s, const Fp8Rows* f8, const Fp8Cols* f8w) {
   const int kp = padded_k(k);
   int g2 = 0;
   const int bn = d % 256 == 0 ? 256 : 128;
   if (k > 0) {
-    hipError_t e = launch_mlp_gemm1(false, x, w1t, b1, midx, a_cache, dbuf, a_packed, mscore, n, d, h, k, s, f8);
+    hipError_t e =
+        launch_mlp_gemm1(false, x, w1t, b1, midx, a_cache, dbuf, a_packed, mscore, n, d, h, k, s, f8, f8w != nullptr);
     if (e != hipSuccess) return e;
     g2 = xcd_grid(d / bn * (int)row_blocks(n));
   }
   const int ga = (int)(row_blocks(na) * heads);
   const dim3 grid((unsigned)(g2 + ga));
   timing_before(K_SPARSE_STEP_FUSED, s);
-  if (bn == 256)
-    hipLaunchKernelGGL((sparse_step_fused<256>), grid, dim3(256), 0, s, g2, dbuf, w2, midx, y, n, d, h, k, kp, q, kx,
-                       v, aidx, m, num, den, o, na, heads, kk, scale);
-  else
-    hipLaunchKernelGGL((sparse_step_fused<128>), grid, dim3(256), 0, s, g2, dbuf, w2, midx, y, n, d, h, k, kp, q, kx,
-                       v, aidx, m, num, den, o, na, heads, kk, scale);
+  const uint8_t* w2f8 = f8w ? f8w->w : nullptr;
+  const uint8_t* w2s = f8w ? f8w->w_scale : nullptr;
+#define FUSED_LAUNCH(BN_, F8W_)                                                                                      \
+  hipLaunchKernelGGL((sparse_step_fused<BN_, F8W_>), grid, dim3(256), 0, s, g2, dbuf, w2, w2f8, w2s, midx, y, n, d, h, \
+                     k, kp, q, kx, v, aidx, m, num, den, o, na, heads, kk, scale)
+  if (bn == 256) {
+    if (f8w)
+      FUSED_LAUNCH(256, true);
+    else
+      FUSED_LAUNCH(256, false);
+  } else {
+    if (f8w)
+      FUSED_LAUNCH(128, true);
+    else
+      FUSED_LAUNCH(128, false);
+  }
+#undef FUSED_LAUNCH
   hipError_t e = hipGetLastError();
   timing_after(K_SPARSE_STEP_FUSED, s);
   return e;

@@ -36,10 +36,12 @@ class MLPDelta:
     rescore=True: every sparse step rescores the units it recomputed, so the set
     S can change from step to step (CHIPMUNK_MLP_RESCORE).
     fp8=True: the first product runs on fp8 operands (CHIPMUNK_MLP_FP8); W1^T is
-    quantized once here, x by every call."""
+    quantized once here, x by every call.  fp8_w2=True: the sparse delta's
+    second product runs on fp8 operands too (CHIPMUNK_MLP_FP8_W2); W2 is
+    quantized once here, column by column."""
 
     def __init__(self, w1t: torch.Tensor, w2: torch.Tensor, n: int, k: int, b1=None, b2=None, rescore=False,
-                 fp8=False):
+                 fp8=False, fp8_w2=False):
         h, d = w1t.shape
         assert w2.shape == (h, d) and w1t.dtype == torch.bfloat16 and w2.dtype == torch.bfloat16
         dev = w1t.device
@@ -60,9 +62,15 @@ class MLPDelta:
         else:
             ws = lib.chipmunk_workspace_bytes(lib.OP_SPARSE_MLP, n, d, h, k)
         self.ws = torch.empty(max(ws, 16), dtype=torch.uint8, device=dev)
-        flags = (lib.MLP_RESCORE if rescore else 0) | (lib.MLP_FP8 if fp8 else 0)
+        self.w2_f8 = self.w2_scale = None
+        if fp8_w2:
+            self.w2_f8 = torch.empty(h, d, dtype=torch.uint8, device=dev)
+            self.w2_scale = torch.empty(d, dtype=torch.uint8, device=dev)
+            lib.chipmunk_quantize_fp8_cols(w2, h, d, self.w2_f8, self.w2_scale)
+        flags = ((lib.MLP_RESCORE if rescore else 0) | (lib.MLP_FP8 if fp8 else 0)
+                 | (lib.MLP_FP8_W2 if fp8_w2 else 0))
         self.layer = lib.mlp_layer(n, d, h, w1t, w2, self.a_cache, self.score, b1, b2, flags, self.w1t_f8,
-                                   self.w1t_scale)
+                                   self.w1t_scale, self.w2_f8, self.w2_scale)
 
     def dense(self, x: torch.Tensor, stream=None):
         lib.chipmunk_dense_step(lib.MLP, self.layer, x, None, None, self.y, self.ws, stream=stream)

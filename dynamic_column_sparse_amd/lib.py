@@ -21,6 +21,7 @@ MLP, ATTN = 0, 1
 ATTN_SPARSE, ATTN_REFRESH = 0, 1
 MLP_RESCORE = 1   # chipmunk_mlp.flags: sparse steps rescore their recomputed units
 MLP_FP8 = 2       # chipmunk_mlp.flags: the first product runs on fp8 operands
+MLP_FP8_W2 = 4    # chipmunk_mlp.flags: the sparse delta's second product runs on fp8 operands
 OP_DENSE_MLP, OP_SPARSE_MLP, OP_TOPK, OP_DENSE_ATTN, OP_SPARSE_ATTN = 0, 1, 2, 3, 4
 OP_DENSE_MLP_FP8, OP_SPARSE_MLP_FP8 = 5, 6
 
@@ -30,6 +31,7 @@ STATUS = {0: "CHIPMUNK_OK", 1: "CHIPMUNK_E_NULLPTR", 2: "CHIPMUNK_E_SHAPE", 3: "
 EXPORTS = ("chipmunk_dense_step", "chipmunk_identify_topk", "chipmunk_sparse_mlp_delta",
            "chipmunk_sparse_attn_delta", "chipmunk_sparse_attn_reident", "chipmunk_sparse_step",
            "chipmunk_cache_writeback", "chipmunk_quantize_fp8",
+           "chipmunk_quantize_fp8_cols",
            "chipmunk_workspace_bytes",
            "chipmunk_last_error", "chipmunk_abi_version", "chipmunk_timing_enable", "chipmunk_timing_read",
            "chipmunk_kernel_count", "chipmunk_kernel_name")
@@ -46,7 +48,8 @@ class MLPLayer(ctypes.Structure):
     _fields_ = [("n", ctypes.c_int64), ("d", ctypes.c_int32), ("h", ctypes.c_int32),
                 ("w1t", ctypes.c_void_p), ("b1", ctypes.c_void_p), ("w2", ctypes.c_void_p),
                 ("b2", ctypes.c_void_p), ("a_cache", ctypes.c_void_p), ("score", ctypes.c_void_p),
-                ("flags", ctypes.c_uint32), ("w1t_f8", ctypes.c_void_p), ("w1t_scale", ctypes.c_void_p)]
+                ("flags", ctypes.c_uint32), ("w1t_f8", ctypes.c_void_p), ("w1t_scale", ctypes.c_void_p),
+                ("w2_f8", ctypes.c_void_p), ("w2_scale", ctypes.c_void_p)]
 
 
 class AttnLayer(ctypes.Structure):
@@ -72,6 +75,7 @@ def _load() -> ctypes.CDLL:
                                                  vp, vp, vp, vp, vp, i32, vp, vp]),
         "chipmunk_cache_writeback": (ctypes.c_int, [vp, vp, vp, i32, vp]),
         "chipmunk_quantize_fp8": (ctypes.c_int, [vp, i64, i32, vp, vp, vp]),
+        "chipmunk_quantize_fp8_cols": (ctypes.c_int, [vp, i64, i32, vp, vp, vp]),
         "chipmunk_workspace_bytes": (sz, [ctypes.c_int, i64, i32, i32, i32]),
         "chipmunk_last_error": (ctypes.c_char_p, []),
         "chipmunk_abi_version": (ctypes.c_int, []),
@@ -137,9 +141,9 @@ def chipmunk_workspace_bytes(op: int, n: int, d: int, h: int, k: int) -> int:
 
 
 def mlp_layer(n, d, h, w1t, w2, a_cache, score=None, b1=None, b2=None, flags=0, w1t_f8=None,
-              w1t_scale=None) -> MLPLayer:
+              w1t_scale=None, w2_f8=None, w2_scale=None) -> MLPLayer:
     return MLPLayer(n, d, h, _ptr(w1t), _ptr(b1), _ptr(w2), _ptr(b2), _ptr(a_cache), _ptr(score), flags,
-                    _ptr(w1t_f8), _ptr(w1t_scale))
+                    _ptr(w1t_f8), _ptr(w1t_scale), _ptr(w2_f8), _ptr(w2_scale))
 
 
 def attn_layer(n, heads, m, num, den, score=None, scale=None, head_dim=HEAD_DIM) -> AttnLayer:
@@ -185,6 +189,10 @@ def chipmunk_sparse_step(mlp: MLPLayer, x, mlp_idx, k: int, y, a_new_packed, ws,
 
 def chipmunk_quantize_fp8(src, rows: int, cols: int, dst, scale, stream=None):
     _check(_lib.chipmunk_quantize_fp8(_ptr(src), rows, cols, _ptr(dst), _ptr(scale), _stream(stream)))
+
+
+def chipmunk_quantize_fp8_cols(src, rows: int, cols: int, dst, scale, stream=None):
+    _check(_lib.chipmunk_quantize_fp8_cols(_ptr(src), rows, cols, _ptr(dst), _ptr(scale), _stream(stream)))
 
 
 def chipmunk_cache_writeback(layer: MLPLayer, a_new_packed, idx, k: int, stream=None):

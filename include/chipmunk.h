@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define CHIPMUNK_ABI_VERSION 4
+#define CHIPMUNK_ABI_VERSION 5
 #define CHIPMUNK_ROW_BLOCK 128
 #define CHIPMUNK_HEAD_DIM 128
 
@@ -113,8 +113,19 @@ enum chipmunk_op {
  *          the e4m3 codes with the row scales as E8M0 scale operands and
  *          accumulate in fp32; everything after the product (b1, GELU, bf16
  *          cache, D, the second product) is unchanged.  w1t may then be NULL.
+ *          CHIPMUNK_MLP_FP8_W2 (may be combined with the others): the
+ *          second product of the sparse delta runs on fp8 operands too.  The
+ *          first product's epilogue rounds D to bf16 (as always) and then to
+ *          e4m3 codes with one E8M0 scale per (row, 32 consecutive units of
+ *          S_b), chipmunk_quantize_fp8's rule applied to each such block; W2
+ *          comes from w2_f8 / w2_scale, which the caller fills once with
+ *          chipmunk_quantize_fp8_cols(w2) (one scale per output column).  The
+ *          dense step's second product stays bf16 (it reads w2).  The
+ *          workspace is the same as without the flag.
  *   w1t_f8    [h][d] e4m3 codes of W1^T (FP8 layers only; 16-byte aligned)
  *   w1t_scale [h] E8M0 scale bytes of those rows (FP8 layers only)
+ *   w2_f8     [h][d] e4m3 codes of W2 (FP8_W2 layers only; 16-byte aligned)
+ *   w2_scale  [d] E8M0 scale bytes of W2's columns (FP8_W2 layers only)
  */
 typedef struct chipmunk_mlp {
   int64_t n;
@@ -129,10 +140,13 @@ typedef struct chipmunk_mlp {
   uint32_t flags;
   const uint8_t* w1t_f8;
   const uint8_t* w1t_scale;
+  const uint8_t* w2_f8;
+  const uint8_t* w2_scale;
 } chipmunk_mlp;
 
 #define CHIPMUNK_MLP_RESCORE 1u
 #define CHIPMUNK_MLP_FP8 2u
+#define CHIPMUNK_MLP_FP8_W2 4u
 
 /* One attention layer's cache (all heads).
  *   n        tokens (queries = keys, 1 <= n < 2^24)
@@ -281,6 +295,13 @@ int chipmunk_cache_writeback(const chipmunk_mlp* layer, const uint16_t* a_new_pa
  * enqueues nothing.  Bit-exact (integer work after an exact scaling). */
 int chipmunk_quantize_fp8(const uint16_t* src, int64_t rows, int32_t cols, uint8_t* dst, uint8_t* scale,
                           void* stream);
+
+/* Column-wise form (the encoding of w2_f8 / w2_scale): the same rule with one
+ * scale per column, scale[c] = 127 + e_c for e_c from max over rows of
+ * |src[r][c]|.  Same arguments and conditions as chipmunk_quantize_fp8
+ * (scale has cols bytes). */
+int chipmunk_quantize_fp8_cols(const uint16_t* src, int64_t rows, int32_t cols, uint8_t* dst, uint8_t* scale,
+                               void* stream);
 
 /* Scratch bytes an op needs for these sizes (0 when none).  op: chipmunk_op.
  * CHIPMUNK_OP_SPARSE_MLP: nb*kp*128*2 with kp = k rounded up to 64 (the D

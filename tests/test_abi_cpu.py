@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_names_workspace(L):
-    assert L.chipmunk_abi_version() == 4
+    assert L.chipmunk_abi_version() == 5
     names = L.kernel_names()
     assert "mlp_gemm1_sparse" in names and "attn_sparse" in names and "topk_rows" in names
     assert "attn_reident" in names
@@ -72,7 +72,9 @@ def _code(L, fn, *a, **kw):
 @pytest.mark.parametrize("case,code", [
     (dict(n=0), 2), (dict(d=100), 2), (dict(d=64), 2), (dict(h=0), 2), (dict(h=100), 2),
     (dict(w1t=None), 1), (dict(a_cache=None), 1), (dict(w2=FAKE + 8), 4),
-    (dict(flags=4), 2),                      # unknown flag bit
+    (dict(flags=8), 2),                      # unknown flag bit
+    (dict(flags=4), 1),                      # fp8 second product needs w2_f8 and w2_scale
+    (dict(flags=4, w2_f8=FAKE + 4, w2_scale=FAKE), 4),
     (dict(flags=1, score=None), 1),          # rescoring needs the score array
     (dict(flags=2), 1),                      # fp8 needs w1t_f8 and w1t_scale
     (dict(flags=2, w1t_f8=FAKE, w1t_scale=None), 1),
@@ -204,6 +206,11 @@ def test_fp8_checks(L):
     assert _code(L, q, FAKE + 8, 4, 16, FAKE + (1 << 32), FAKE + (2 << 32), stream=0) == 4
     assert _code(L, q, FAKE, 4, 16, FAKE + 64, FAKE + (2 << 32), stream=0) == 2          # dst inside src
     assert _code(L, q, FAKE, 0, 16, FAKE + (1 << 32), FAKE + (2 << 32), stream=0) == 0    # no rows: no-op
+    qc = L.chipmunk_quantize_fp8_cols
+    assert _code(L, qc, FAKE, 4, 12, FAKE + (1 << 32), FAKE + (2 << 32), stream=0) == 2
+    assert _code(L, qc, FAKE, 4, 16, None, FAKE + (2 << 32), stream=0) == 1
+    assert _code(L, qc, FAKE, 4, 16, FAKE + (1 << 32), FAKE + 100, stream=0) == 2       # scale inside src
+    assert _code(L, qc, FAKE, 0, 16, FAKE + (1 << 32), FAKE + (2 << 32), stream=0) == 0
     # workspace sizes of an fp8 layer: the D tiles, then x's codes and scales
     base = L.chipmunk_workspace_bytes(L.OP_SPARSE_MLP, 4352, 3072, 12288, 3686)
     xq = (4352 * 3072 + 4352 + 15) // 16 * 16

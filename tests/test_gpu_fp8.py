@@ -167,3 +167,129 @@ def test_fp8_flux_fused_step_sampled(gpu_lib):
         assert e < TOL, f"step {t}: y {e:.2e}"
         assert oracle.rel_frobenius(_cache_rows(mlp.a_cache, blocks, n), a_s) < 1e-3, f"step {t}: cache"
         print(f"  step {t}: y rel-F {e:.2e}", flush=True)
+
+
+# ---- the fp8 second product (reading R15) -----------------------------------
+@pytest.mark.parametrize("rows,cols", [(1, 8), (37, 24), (640, 256), (12288, 3072)])
+def test_quantize_cols_bit_exact(gpu_lib, rows, cols):
+    print(f"quantize fp8 columns rows={rows} cols={cols}", flush=True)
+    if rows == 12288:
+        bits = syn.mlp_weights(0, cols, rows)[1]                  # W2 of the FLUX.1-dev MLP, [h][d]
+    else:
+        g = np.random.default_rng(rows)
+        a = g.standard_normal((rows, cols)) * np.exp(g.uniform(-10, 10, (1, cols)))
+        a[:, 0] = 0.0                                             # an all-zero column
+        if rows > 1:
+            a[0, -1] = 448.0 * 2.0 ** 3                           # a column maximum exactly at 448 * 2^3
+        bits = oracle.bf16_bits(a)
+    src = up_bf16(bits)
+    dst = torch.full((rows, cols), 0xAA, dtype=torch.uint8, device="cuda")
+    sc = torch.full((cols,), 0xAA, dtype=torch.uint8, device="cuda")
+    gpu_lib.chipmunk_quantize_fp8_cols(src, rows, cols, dst, sc)
+    torch.cuda.synchronize()
+    rc, rs = oracle.quantize_fp8_rows(oracle.from_bf16_bits(bits).T)
+    np.testing.assert_array_equal(sc.cpu().numpy(), rs)
+    np.testing.assert_array_equal(dst.cpu().numpy(), rc.T)
+
+
+def _fp8_d_from_ws(lay, n, kp):
+    """(codes [nb,128,kp], scale bytes [nb,128,kp/32]) of the fp8 D the first
+    product left in the workspace ([nb][128][kp] codes, then per 64-unit chunk
+    [nb][kp/64][128][2] scale bytes)."""
+    nb = lay.nb
+    ws = lay.ws.cpu().numpy()
+    codes = ws[:nb * 128 * kp].reshape(nb, 128, kp)
+    sc = ws[nb * 128 * kp:nb * 128 * kp + nb * (kp // 64) * 256].reshape(nb, kp // 64, 128, 2)
+    return codes, sc.transpose(0, 2, 1, 3).reshape(nb, 128, kp // 32)
+
+
+@pytest.mark.parametrize("n,d,h,k,first", [(300, 256, 640, 200, False), (300, 256, 640, 200, True),
+                                           (256, 128, 512, 128, True), (130, 384, 1024, 1000, False)])
+def test_fp8_second_product_matches_oracle(gpu_lib, n, d, h, k, first):
+    from dynamic_column_sparse_amd.layers import MLPDelta
+    print(f"fp8 second product n={n} d={d} h={h} k={k} fp8 first product={first}", flush=True)
+    w1t_b, w2_b, b1, xs = _inputs(n, d, h, 2, 3)
+    lay = MLPDelta(up_bf16(w1t_b), up_bf16(w2_b), n, k, up_f32(b1), None, fp8=first, fp8_w2=True)
+    w1t, w2 = oracle.from_bf16_bits(w1t_b), oracle.from_bf16_bits(w2_b)
+    torch.cuda.synchronize()
+    wc, ws = oracle.quantize_fp8_rows(w2.T)
+    np.testing.assert_array_equal(lay.w2_f8.cpu().numpy(), wc.T)
+    np.testing.assert_array_equal(lay.w2_scale.cpu().numpy(), ws)
+    w1o = oracle.fp8_rows(w1t) if first else w1t
+    xop = (lambda v: oracle.fp8_rows(v)) if first else (lambda v: v)
+    w2q = oracle.fp8_cols(w2)
+
+    lay.dense(up_bf16(xs[0]))                          # the dense step's second product stays bf16
+    torch.cuda.synchronize()
+    a, y, _ = oracle.mlp_dense(xop(oracle.from_bf16_bits(xs[0])), w1o, b1, w2, None, np.zeros((n, h)))
+    assert oracle.rel_frobenius(lay.y.cpu().numpy(), y) < TOL
+    kp = (k + 63) // 64 * 64
+    for t in (1, 2):
+        y_before = lay.y.cpu().numpy()
+        a_before = cache_to_rows(lay.a_cache, n)
+        lay.identify()
+        torch.cuda.synchronize()
+        g_idx = lay.idx.cpu().numpy()[:, :k]
+        np.testing.assert_array_equal(g_idx, oracle.identify_topk(lay.score.cpu().numpy(), k))
+        lay.sparse(up_bf16(xs[t]))
+        torch.cuda.synchronize()
+        # the fp8 D in the workspace: codes and scales of the GPU's own D,
+        # bf16(a_new - a_old) from its cache, bit for bit
+        a_after = cache_to_rows(lay.a_cache, n)
+        codes, scb = _fp8_d_from_ws(lay, n, kp)
+        for b in range(lay.nb):
+            r0, r1 = b * 128, min(n, (b + 1) * 128)
+            dd = np.zeros((128, kp))
+            dd[:r1 - r0, :k] = oracle.bf16_round(a_after[r0:r1][:, g_idx[b]] - a_before[r0:r1][:, g_idx[b]])
+            rc, rs = oracle.quantize_fp8_blocks(dd, 32)
+            np.testing.assert_array_equal(codes[b], rc, err_msg=f"step {t} block {b}: D codes")
+            np.testing.assert_array_equal(scb[b], rs, err_msg=f"step {t} block {b}: D scales")
+        a, y1 = oracle.mlp_sparse(xop(oracle.from_bf16_bits(xs[t])), w1o, b1, w2q, a, y, g_idx, d_fp8=True)
+        y_gpu = lay.y.cpu().numpy()
+        e = oracle.rel_frobenius(y_gpu, y1)
+        assert e < TOL, f"step {t}: y {e:.2e}"
+        assert oracle.rel_frobenius(y_gpu - y_before, y1 - y) < TOL, f"step {t}: dy"
+        assert oracle.rel_frobenius(a_after, a) < 1e-3, f"step {t}: cache"
+        y = y1
+        print(f"  step {t}: y rel-F {e:.2e}, dy rel-F {oracle.rel_frobenius(y_gpu - y_before, y1 - y_before):.2e}",
+              flush=True)
+
+
+def test_fp8_both_products_flux_fused_step_sampled(gpu_lib):
+    # The FLUX.1-dev MLP with both products in fp8, through chipmunk_sparse_step
+    # beside the FLUX attention delta; sampled row blocks plus the last.
+    from dynamic_column_sparse_amd.layers import AttnDelta, MLPDelta, sparse_step
+    n, d, h, k, H, kk, seed, steps = 4352, 3072, 12288, 3686, 24, 718, 0, 3
+    nb = (n + RB - 1) // RB
+    blocks = _sample_blocks(nb, 3, seed + 17, n)
+    rows = _rows_of(blocks, n)
+    rows_t = torch.from_numpy(rows).cuda()
+    print(f"fp8 (both products) flux fused step: blocks {blocks}", flush=True)
+    w1t_b, w2_b = syn.mlp_weights(seed, d, h)
+    mlp = MLPDelta(up_bf16(w1t_b), up_bf16(w2_b), n, k, fp8=True, fp8_w2=True)
+    w1q = oracle.fp8_rows(oracle.from_bf16_bits(w1t_b))
+    w2 = oracle.from_bf16_bits(w2_b)
+    w2q = oracle.fp8_cols(w2)
+    del w1t_b, w2_b
+    att = AttnDelta(n, H, kk, "cuda")
+    xs = syn.activation_walk(seed, "X", steps, n, d)
+    walks = [syn.heads_walk(seed, tag, steps, H, n) for tag in "QKV"]
+    a_s = y_s = None
+    for t in range(steps):
+        x_g = up_bf16(xs[t])
+        qkv = [up_bf16(w[t]) for w in walks]
+        x_s = oracle.fp8_rows(oracle.from_bf16_bits(xs[t][rows]))
+        if t == 0:
+            mlp.step(x_g, refresh=True)
+            att.step(*qkv, refresh=True)
+            torch.cuda.synchronize()
+            a_s, y_s, _ = oracle.mlp_dense(x_s, w1q, None, w2, None, np.zeros((len(rows), h)))
+            continue
+        sparse_step(mlp, att, x_g, *qkv)
+        torch.cuda.synchronize()
+        g_idx = mlp.idx[torch.tensor(blocks, device="cuda")].cpu().numpy()
+        a_s, y_s = oracle.mlp_sparse(x_s, w1q, None, w2q, a_s, y_s, g_idx, d_fp8=True)
+        e = oracle.rel_frobenius(mlp.y[rows_t].cpu().numpy(), y_s)
+        assert e < TOL, f"step {t}: y {e:.2e}"
+        assert oracle.rel_frobenius(_cache_rows(mlp.a_cache, blocks, n), a_s) < 1e-3, f"step {t}: cache"
+        print(f"  step {t}: y rel-F {e:.2e}", flush=True)
