@@ -1,24 +1,18 @@
 // Sparsity identification: exact top-k per score row (gfx950).
 //
-// One workgroup (512 threads, 8 waves) per row.  Scores become monotone 32-bit
-// keys (NaN -> 0, the lowest; -0 -> +0; sign-magnitude -> offset binary), so the
-// choice is integer work and matches any exact reference bit for bit.
-//   1. Radix select, 8 bits per pass from the top: an LDS histogram of the
-//      candidates that still match the prefix finds the k-th largest key T and
-//      how many keys equal to T must still be taken (ties go to the lower index).
-//   2. One pass in index order emits key > T plus the first `need` keys == T,
-//      using wave ballots for the in-order ranks, so the output is ascending.
-// Rows of up to kLdsCap scores are staged in LDS once; longer rows (attention
-// at long sequence lengths) are re-read from global memory on each pass.
+// Scores become monotone 32-bit keys (NaN -> 0, the lowest; -0 -> +0;
+// sign-magnitude -> offset binary), so the choice is integer work and matches
+// any exact reference bit for bit.  The k-th largest key T and the number of
+// keys equal to T still to take (ties go to the lower index) come from radix
+// passes over LDS histograms; a final pass in index order emits key > T and the
+// first `need` keys == T, so the output is ascending.  Rows of up to 16384
+// scores stay in registers (one workgroup of 1024 threads); longer rows are
+// read three times by a 512-thread workgroup (see topk_rows_long).
 #include "device_common.h"
 #include "internal.h"
 
 namespace chipmunk {
 namespace {
-
-constexpr int kThreads = 512;
-constexpr int kWaves = kThreads / 64;
-constexpr int kLdsCap = 15360;  // 60 KB of keys
 
 __device__ __forceinline__ uint32_t score_key(float f) {
   uint32_t u = __float_as_uint(f);
@@ -27,95 +21,230 @@ __device__ __forceinline__ uint32_t score_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-template <bool IN_LDS>
-__global__ __launch_bounds__(kThreads) void topk_rows(const float* __restrict__ score, int64_t cols, int k,
-                                                      int32_t* __restrict__ idx) {
-  extern __shared__ uint32_t skey[];
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t wtot[kWaves];
-  __shared__ uint32_t wtot2[kWaves];
-  __shared__ uint32_t sh_prefix, sh_remaining;
+// Rows longer than the register variant holds (attention rows at long sequence
+// lengths), one workgroup of 512 threads per row, three reads of the row:
+//   1. an 8192-bin histogram of the keys' top 13 bits finds the bin B that
+//      holds the k-th largest key, the count above it and how many of the
+//      bin's keys are still needed;
+//   2. the keys of bin B (their low 19 bits) are gathered into LDS (wave-
+//      aggregated slots), and radix passes of 10 and 9 bits over them give the
+//      exact k-th key T and how many keys equal to T are taken (ties to the
+//      lower index); a bin larger than the LDS buffer is resolved with the
+//      same two passes over the row in global memory instead;
+//   3. one pass in index order emits key > T and the first `need` keys == T,
+//      each thread taking 16 consecutive scores per iteration (the next 16 are
+//      loaded before this iteration's scan), with a block scan of packed
+//      (above, equal) counts for the output positions.
+// Loads are 16-byte when the row is 16-byte aligned (cols % 4 == 0).  LDS is
+// 32 KB of bins and 47 KB of candidates, so two workgroups share a CU.
+constexpr int kLongThreads = 512;
+constexpr int kLongWaves = kLongThreads / 64;
+constexpr int kTopBits = 13;
+constexpr int kTopBins = 1 << kTopBits;
+constexpr int kLowBits = 32 - kTopBits;   // 19: resolved as 10 + 9
+constexpr int kCandCap = 12000;   // candidate keys (47 KB)
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// Exclusive block scan (in thread order) of one 32-bit value per thread;
+// returns the exclusive prefix and sets `total`.  Ends with a barrier (wsum
+// may be reused after it).
+__device__ __forceinline__ uint32_t block_scan_excl(uint32_t v, uint32_t* wsum, uint32_t& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t t = __shfl_up(incl, o);
+    if (lane >= o) incl += t;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  uint32_t before = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kLongWaves; ++w) {
+    const uint32_t x = wsum[w];
+    before += w < wave ? x : 0u;
+    tot += x;
+  }
+  total = tot;
+  __syncthreads();
+  return before + incl - v;
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(kLongThreads) void topk_rows_long(const float* __restrict__ score, int64_t cols, int k,
+                                                               int32_t* __restrict__ idx) {
+  __shared__ uint32_t hist[kTopBins];
+  __shared__ uint32_t cand[kCandCap];
+  __shared__ uint32_t wsum[kLongWaves];
+  __shared__ uint32_t sh_bin, sh_above, sh_fill;
+  const int tid = threadIdx.x, lane = tid & 63;
   const int64_t row = blockIdx.x;
   const float* srow = score + row * cols;
   int32_t* orow = idx + row * (int64_t)k;
-
-  if (IN_LDS) {
-    for (int64_t i = tid; i < cols; i += kThreads) skey[i] = score_key(srow[i]);
-  }
-  __syncthreads();
-  auto key_at = [&](int64_t i) -> uint32_t { return IN_LDS ? skey[i] : score_key(srow[i]); };
-
-  uint32_t prefix = 0, mask = 0, remaining = (uint32_t)k;
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    for (int i = tid; i < 256; i += kThreads) hist[i] = 0;
-    __syncthreads();
-    for (int64_t i = tid; i < cols; i += kThreads) {
-      const uint32_t key = key_at(i);
-      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
-    }
-    __syncthreads();
-    // Inclusive scan of the counts from the top digit down (threads 0..255).
-    uint32_t hv = 0, incl = 0;
-    if (tid < 256) {
-      hv = hist[255 - tid];
-      incl = hv;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t t = __shfl_up(incl, o);
-        if (lane >= o) incl += t;
-      }
-      if (lane == 63) wtot[wave] = incl;
-    }
-    __syncthreads();
-    if (tid < 256) {
-      for (int w = 0; w < wave; ++w) incl += wtot[w];
-      const uint32_t excl = incl - hv;
-      if (excl < remaining && remaining <= incl) {
-        sh_prefix = prefix | ((uint32_t)(255 - tid) << shift);
-        sh_remaining = remaining - excl;
-      }
-    }
-    __syncthreads();
-    prefix = sh_prefix;
-    remaining = sh_remaining;
-    mask |= 255u << shift;
-  }
-
-  const uint32_t T = prefix, need = remaining;
-  uint32_t taken = 0, eq_seen = 0;
+  const int64_t nvec = VEC ? cols / 4 : 0;
   const uint64_t lt_mask = (lane == 0) ? 0ull : ((~0ull) >> (64 - lane));
-  for (int64_t base = 0; base < cols && taken < (uint32_t)k; base += kThreads) {
-    const int64_t i = base + tid;
-    const bool in = i < cols;
-    const uint32_t key = in ? key_at(i) : 0u;
-    const bool gt = in && key > T;
-    const bool eq = in && key == T;
-    const uint64_t em = __ballot(eq);
-    if (lane == 0) wtot[wave] = (uint32_t)__popcll(em);
-    __syncthreads();
-    uint32_t eq_before = eq_seen, eq_chunk = 0;
-    for (int w = 0; w < kWaves; ++w) {
-      if (w < wave) eq_before += wtot[w];
-      eq_chunk += wtot[w];
+
+  // f(key, valid) for every score of the row (any order), four 16-byte loads
+  // per thread in flight before any of them is used; every lane of a wave
+  // runs the same calls (invalid ones with valid = false), so f may use
+  // wave-wide operations.
+  auto for_each = [&](auto&& f) __attribute__((always_inline)) {
+    if (VEC) {
+      for (int64_t v0 = 0; v0 < nvec; v0 += 4 * kLongThreads) {
+        float4 x[4];
+        bool ok[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int64_t v = v0 + u * kLongThreads + tid;
+          ok[u] = v < nvec;
+          x[u] = ok[u] ? *(const float4*)(srow + 4 * v) : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          f(score_key(x[u].x), ok[u]);
+          f(score_key(x[u].y), ok[u]);
+          f(score_key(x[u].z), ok[u]);
+          f(score_key(x[u].w), ok[u]);
+        }
+      }
     }
-    const uint32_t eq_rank = eq_before + (uint32_t)__popcll(em & lt_mask);
-    const bool take = gt || (eq && eq_rank < need);
-    const uint64_t tm = __ballot(take);
-    if (lane == 0) wtot2[wave] = (uint32_t)__popcll(tm);
-    __syncthreads();
-    uint32_t t_before = taken, t_chunk = 0;
-    for (int w = 0; w < kWaves; ++w) {
-      if (w < wave) t_before += wtot2[w];
-      t_chunk += wtot2[w];
+    for (int64_t i0 = 4 * nvec; i0 < cols; i0 += kLongThreads) {
+      const int64_t i = i0 + tid;
+      const bool ok = i < cols;
+      f(ok ? score_key(srow[i]) : 0u, ok);
     }
-    const uint32_t pos = t_before + (uint32_t)__popcll(tm & lt_mask);
-    if (take && pos < (uint32_t)k) orow[pos] = (int32_t)i;
-    taken += t_chunk;
-    eq_seen += eq_chunk;
+  };
+  // Bin of the kth largest among `nbins` (8192, 1024 or 512) counts in hist,
+  // from the top bin down: sets sh_bin and sh_above (the count in higher bins).
+  auto select_bin = [&](int nbins, uint32_t kth) __attribute__((always_inline)) {
+    const int per = nbins / kLongThreads;    // 16, 2 or 1 bins per thread, highest first
+    uint32_t c[16], tot = 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      c[j] = j < per ? hist[nbins - 1 - tid * per - j] : 0u;
+      tot += c[j];
+    }
+    uint32_t all;
+    const uint32_t excl = block_scan_excl(tot, wsum, all);
+    uint32_t run = excl;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if (j < per && run < kth && kth <= run + c[j]) {
+        sh_bin = (uint32_t)(nbins - 1 - tid * per - j);
+        sh_above = run;
+      }
+      run += c[j];
+    }
     __syncthreads();
+  };
+
+  // ---- 1. top 13 bits
+  for (int i = tid; i < kTopBins; i += kLongThreads) hist[i] = 0u;
+  if (tid == 0) sh_fill = 0u;
+  __syncthreads();
+  for_each([&](uint32_t key, bool ok) {
+    if (ok) atomicAdd(&hist[key >> kLowBits], 1u);
+  });
+  __syncthreads();
+  select_bin(kTopBins, (uint32_t)k);
+  const uint32_t B = sh_bin;
+  uint32_t remaining = (uint32_t)k - sh_above;      // still needed from bin B
+  const uint32_t candN = hist[B];
+  const bool in_lds = candN <= (uint32_t)kCandCap;
+  __syncthreads();
+
+  // ---- 2. the keys of bin B
+  if (in_lds) {
+    // wave-aggregated slots: one LDS atomic per wave and ballot
+    auto keep = [&](uint32_t key, bool hit) __attribute__((always_inline)) {
+      const uint64_t m = __ballot(hit);
+      if (m == 0) return;
+      const int first = __builtin_ctzll(m);
+      uint32_t base = 0;
+      if (lane == first) base = atomicAdd(&sh_fill, (uint32_t)__popcll(m));
+      base = __shfl(base, first);
+      if (hit) cand[base + __popcll(m & lt_mask)] = key & ((1u << kLowBits) - 1u);
+    };
+    for_each([&](uint32_t key, bool ok) { keep(key, ok && (key >> kLowBits) == B); });
+    __syncthreads();
+  }
+  // low 19 bits: passes of 10 and 9 bits over bin B's keys (in LDS, or the row)
+  uint32_t prefix = B << kLowBits;
+  for (int pass = 0; pass < 2; ++pass) {
+    const int shift = pass == 0 ? 9 : 0;
+    const int nbins = pass == 0 ? 1024 : 512;
+    const uint32_t mask = pass == 0 ? ~((1u << kLowBits) - 1u) : ~((1u << 9) - 1u);
+    for (int i = tid; i < nbins; i += kLongThreads) hist[i] = 0u;
+    __syncthreads();
+    if (in_lds) {
+      for (uint32_t c = tid; c < candN; c += kLongThreads) {
+        const uint32_t key = cand[c] | (B << kLowBits);
+        if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & (uint32_t)(nbins - 1)], 1u);
+      }
+    } else {
+      for_each([&](uint32_t key, bool ok) {
+        if (ok && (key & mask) == prefix) atomicAdd(&hist[(key >> shift) & (uint32_t)(nbins - 1)], 1u);
+      });
+    }
+    __syncthreads();
+    select_bin(nbins, remaining);
+    prefix |= sh_bin << shift;
+    remaining -= sh_above;
+  }
+  const uint32_t T = prefix, need = remaining;
+
+  // ---- 3. emit in index order: thread t takes scores base + 16t .. base + 16t + 15
+  constexpr int EPT = 16;
+  auto load_run = [&](int64_t i0, uint32_t (&key)[EPT]) __attribute__((always_inline)) {
+    if (VEC && i0 + EPT <= cols) {
+#pragma unroll
+      for (int q = 0; q < EPT / 4; ++q) {
+        const float4 x = *(const float4*)(srow + i0 + 4 * q);
+        key[4 * q] = score_key(x.x);
+        key[4 * q + 1] = score_key(x.y);
+        key[4 * q + 2] = score_key(x.z);
+        key[4 * q + 3] = score_key(x.w);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) key[e] = i0 + e < cols ? score_key(srow[i0 + e]) : 0u;
+    }
+  };
+  uint32_t gt_total = 0, eq_total = 0;
+  uint32_t cur[EPT], nxt[EPT];
+  load_run(EPT * (int64_t)tid, cur);
+  for (int64_t base = 0; base < cols; base += EPT * kLongThreads) {
+    if (gt_total + (eq_total < need ? eq_total : need) >= (uint32_t)k) break;   // uniform
+    const int64_t i0 = base + EPT * tid;
+    if (base + EPT * kLongThreads < cols) load_run(i0 + EPT * kLongThreads, nxt);
+    uint32_t cg = 0, ce = 0;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      const bool in = i0 + e < cols;
+      cg += (in && cur[e] > T) ? 1u : 0u;
+      ce += (in && cur[e] == T) ? 1u : 0u;
+    }
+    uint32_t chunk;
+    const uint32_t excl = block_scan_excl(cg | (ce << 16), wsum, chunk);
+    uint32_t gt_before = gt_total + (excl & 0xffffu), eq_before = eq_total + (excl >> 16);
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      const bool in = i0 + e < cols;
+      if (in && cur[e] > T) {
+        const uint32_t pos = gt_before + (eq_before < need ? eq_before : need);
+        if (pos < (uint32_t)k) orow[pos] = (int32_t)(i0 + e);
+        ++gt_before;
+      } else if (in && cur[e] == T) {
+        if (eq_before < need) {
+          const uint32_t pos = gt_before + eq_before;
+          if (pos < (uint32_t)k) orow[pos] = (int32_t)(i0 + e);
+        }
+        ++eq_before;
+      }
+    }
+    gt_total += chunk & 0xffffu;
+    eq_total += chunk >> 16;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) cur[e] = nxt[e];
   }
 }
 
@@ -283,11 +412,10 @@ hipError_t launch_topk(const float* score, int64_t rows, int64_t cols, int k, in
   timing_before(K_TOPK, s);
   if (cols <= kRegCols)
     hipLaunchKernelGGL(topk_rows_reg, dim3((unsigned)rows), dim3(kRegThreads), 0, s, score, (int)cols, k, idx);
-  else if (cols <= kLdsCap)
-    hipLaunchKernelGGL((topk_rows<true>), dim3((unsigned)rows), dim3(kThreads), (size_t)cols * 4, s, score, cols, k,
-                       idx);
+  else if (cols % 4 == 0 && ((uintptr_t)score & 15) == 0)
+    hipLaunchKernelGGL((topk_rows_long<true>), dim3((unsigned)rows), dim3(kLongThreads), 0, s, score, cols, k, idx);
   else
-    hipLaunchKernelGGL((topk_rows<false>), dim3((unsigned)rows), dim3(kThreads), 0, s, score, cols, k, idx);
+    hipLaunchKernelGGL((topk_rows_long<false>), dim3((unsigned)rows), dim3(kLongThreads), 0, s, score, cols, k, idx);
   hipError_t e = hipGetLastError();
   timing_after(K_TOPK, s);
   return e;

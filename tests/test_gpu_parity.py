@@ -27,6 +27,9 @@ def L(gpu_lib):
 @pytest.mark.parametrize("rows,cols,k", [
     (5, 1, 1), (7, 7, 3), (9, 100, 1), (9, 100, 50), (9, 100, 99), (9, 100, 100),
     (4, 4352, 718), (3, 12288, 3686), (3, 12288, 860), (2, 20000, 1400), (1, 118800, 8316),
+    (3, 20001, 777),     # long rows not a multiple of 4: 4-byte loads
+    (2, 16385, 16385),   # every column of a long row
+    (2, 40000, 1),
 ])
 def test_topk_bit_exact(L, kind, rows, cols, k):
     print(f"topk kind={kind} rows={rows} cols={cols} k={k}", flush=True)
