@@ -248,8 +248,10 @@ __global__ __launch_bounds__(kLongThreads) void topk_rows_long(const float* __re
   }
 }
 
-// Register-resident variant for rows of up to kRegCols scores: 1024 threads,
-// thread t holds keys t + 1024 j (j < kRegKeys).
+// Register-resident variant for rows of up to kRegCols scores: THREADS
+// threads (256, 512 or 1024: the smallest that holds the row, so short rows
+// leave no idle lanes and more rows share a CU), thread t holds keys
+// t + THREADS j (j < kRegKeys).
 //   1. Min and max of the row's keys: every key shares their common bit
 //      prefix, so the radix passes start at the first bit where they differ
 //      (positive scores of similar size share sign and exponent bits; starting
@@ -257,18 +259,18 @@ __global__ __launch_bounds__(kLongThreads) void topk_rows_long(const float* __re
 //   2. Radix select over the remaining bits, up to 8 per pass, with one
 //      256-bin histogram per wave (contention only inside a wave).
 //   3. Emit in index order from one ballot pair per (batch j, wave) and a
-//      single 16 x 16 prefix table of packed (above, equal) counts.
-constexpr int kRegThreads = 1024;
-constexpr int kRegWaves = kRegThreads / 64;
+//      single 16 x waves prefix table of packed (above, equal) counts.
 constexpr int kRegKeys = 16;
-constexpr int kRegCols = kRegThreads * kRegKeys;
+constexpr int kRegCols = 1024 * kRegKeys;
 
-// Exclusive prefix sum over tab[0..255] in (batch, wave) order, in place;
-// returns the total.  Threads 0..255 take part; ends with a barrier.
+// Exclusive prefix sum over tab[0..N-1] (N = 64, 128 or 256) in (batch, wave)
+// order, in place; returns the total.  Threads 0..N-1 take part; ends with a
+// barrier.
+template <int N>
 __device__ __forceinline__ uint32_t table_scan(uint32_t* tab, uint32_t* wsum, int tid) {
   const int lane = tid & 63, wave = tid >> 6;
   uint32_t v = 0, incl = 0;
-  if (tid < 256) {
+  if (tid < N) {
     v = tab[tid];
     incl = v;
 #pragma unroll
@@ -279,8 +281,10 @@ __device__ __forceinline__ uint32_t table_scan(uint32_t* tab, uint32_t* wsum, in
     if (lane == 63) wsum[wave] = incl;
   }
   __syncthreads();
-  uint32_t total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
-  if (tid < 256) {
+  uint32_t total = 0;
+#pragma unroll
+  for (int w = 0; w < N / 64; ++w) total += wsum[w];
+  if (tid < N) {
     for (int w = 0; w < wave; ++w) incl += wsum[w];
     tab[tid] = incl - v;
   }
@@ -288,8 +292,11 @@ __device__ __forceinline__ uint32_t table_scan(uint32_t* tab, uint32_t* wsum, in
   return total;
 }
 
-__global__ __launch_bounds__(kRegThreads) void topk_rows_reg(const float* __restrict__ score, int cols, int k,
-                                                             int32_t* __restrict__ idx) {
+template <int THREADS>
+__global__ __launch_bounds__(THREADS) void topk_rows_reg(const float* __restrict__ score, int cols, int k,
+                                                        int32_t* __restrict__ idx) {
+  constexpr int kRegThreads = THREADS;
+  constexpr int kRegWaves = THREADS / 64;
   __shared__ uint32_t hist[kRegWaves][256];
   __shared__ uint32_t tab[kRegKeys * kRegWaves];
   __shared__ uint32_t wsum[4];
@@ -392,7 +399,7 @@ __global__ __launch_bounds__(kRegThreads) void topk_rows_reg(const float* __rest
     if (lane == 0) tab[j * kRegWaves + wave] = (uint32_t)__popcll(gm[j]) | ((uint32_t)__popcll(em[j]) << 16);
   }
   __syncthreads();
-  table_scan(tab, wsum, tid);
+  table_scan<kRegKeys * kRegWaves>(tab, wsum, tid);
 #pragma unroll
   for (int j = 0; j < kRegKeys; ++j) {
     const uint32_t base = tab[j * kRegWaves + wave];
@@ -410,8 +417,12 @@ __global__ __launch_bounds__(kRegThreads) void topk_rows_reg(const float* __rest
 
 hipError_t launch_topk(const float* score, int64_t rows, int64_t cols, int k, int32_t* idx, hipStream_t s) {
   timing_before(K_TOPK, s);
-  if (cols <= kRegCols)
-    hipLaunchKernelGGL(topk_rows_reg, dim3((unsigned)rows), dim3(kRegThreads), 0, s, score, (int)cols, k, idx);
+  if (cols <= 256 * kRegKeys)
+    hipLaunchKernelGGL(topk_rows_reg<256>, dim3((unsigned)rows), dim3(256), 0, s, score, (int)cols, k, idx);
+  else if (cols <= 512 * kRegKeys)
+    hipLaunchKernelGGL(topk_rows_reg<512>, dim3((unsigned)rows), dim3(512), 0, s, score, (int)cols, k, idx);
+  else if (cols <= kRegCols)
+    hipLaunchKernelGGL(topk_rows_reg<1024>, dim3((unsigned)rows), dim3(1024), 0, s, score, (int)cols, k, idx);
   else if (cols % 4 == 0 && ((uintptr_t)score & 15) == 0)
     hipLaunchKernelGGL((topk_rows_long<true>), dim3((unsigned)rows), dim3(kLongThreads), 0, s, score, cols, k, idx);
   else
