@@ -155,9 +155,11 @@ def blas_threads():
     return len(os.sched_getaffinity(0))
 
 
-def cpu_baseline(w, inputs, budget_s, reident=False):
-    """The CPU oracle, as it stands, on a bounded sample of the same sparse step.
-    MLP: whole 128-row blocks until half the budget is used; attention: whole
+def cpu_baseline(w, inputs, budget_s, reident=False, fp8=False, fp8_w2=False):
+    """The CPU oracle, as it stands, on a bounded sample of the same sparse step
+    (in the fp8 modes, on the fp8 operands: the weights' fp8 values are taken
+    once, outside the timed part, as the layer takes them at set-up).  MLP:
+    whole 128-row blocks until half the budget is used; attention: whole
     (head, query block) pairs of the first heads until the rest is used.  The
     time per block / pair scales to the full step."""
     import oracle
@@ -168,15 +170,20 @@ def cpu_baseline(w, inputs, budget_s, reident=False):
         n, h, k = w["n"], w["h"], w["k"]
         w1t = oracle.from_bf16_bits(inputs["w1t"])
         w2 = oracle.from_bf16_bits(inputs["w2"])
+        if fp8:
+            w1t = oracle.fp8_rows(w1t)
+        w2_sparse = oracle.fp8_cols(w2) if fp8_w2 else w2
         nb = (n + 127) // 128
         x0 = oracle.from_bf16_bits(inputs["x"][0])
         x1 = oracle.from_bf16_bits(inputs["x"][1])
         for b in range(nb):
             r0, r1 = b * 128, min(n, b * 128 + 128)
-            a0, y0, sc = oracle.mlp_dense(x0[r0:r1], w1t, None, w2, None, np.zeros((r1 - r0, h)))
+            xd = oracle.fp8_rows(x0[r0:r1]) if fp8 else x0[r0:r1]
+            a0, y0, sc = oracle.mlp_dense(xd, w1t, None, w2, None, np.zeros((r1 - r0, h)))
             t0 = time.perf_counter()
             idx = oracle.identify_topk(sc.astype(np.float32), k)
-            oracle.mlp_sparse(x1[r0:r1], w1t, None, w2, a0, y0, idx)
+            xs1 = oracle.fp8_rows(x1[r0:r1]) if fp8 else x1[r0:r1]
+            oracle.mlp_sparse(xs1, w1t, None, w2_sparse, a0, y0, idx, d_fp8=fp8_w2)
             t_mlp += time.perf_counter() - t0
             n_mlp += 1
             if t_mlp > budget_s / 2:
@@ -438,7 +445,8 @@ def main():
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         cb = cpu_baseline(w, {**inputs, "x": inputs.get("x", [None, None])[:2],
-                              "qkv": inputs.get("qkv", [None, None])[:2]}, args.cpu_budget, args.attn_reident)
+                              "qkv": inputs.get("qkv", [None, None])[:2]}, args.cpu_budget, args.attn_reident,
+                          args.fp8, args.fp8_w2)
         out["cpu_baseline"] = cb
     print(json.dumps(out), flush=True)
 
