@@ -5,7 +5,8 @@
     several sparse steps.  The shapes cover ragged row blocks, both phase-2
     tile widths (d a multiple of 256, and not), head counts with and without
     the XCD head mapping (heads % 8), k = 0, kk = 0, and an attention layer
-    whose token count differs from the MLP's.
+    whose token count differs from the MLP's; layers with bf16 products, both
+    products on fp8, and the fp8 second product with per-step rescoring.
   * Against the oracle at the FLUX.1-dev shapes (1280x768 and 2304x1280), in
     the launch configuration the benchmark times: sampled row blocks (MLP) and
     (head, query block) slices (attention), each recomputed on its own (exact,
@@ -32,14 +33,14 @@ def _bits(t):
     return t.view(torch.int32) if t.dtype == torch.float32 else t.view(torch.int16)
 
 
-def _pair(n, d, h, k, na, H, kk, seed, steps):
+def _pair(n, d, h, k, na, H, kk, seed, steps, **mlp_kw):
     from dynamic_column_sparse_amd.layers import AttnDelta, MLPDelta
     w1t_b, w2_b = syn.mlp_weights(seed, d, h)
     xs = [up_bf16(x) for x in syn.activation_walk(seed, "X", steps, n, d)]
     qkv = [[up_bf16(a) for a in st] for st in zip(*[syn.heads_walk(seed, t, steps, H, na) for t in "QKV"])]
     layers = []
     for _ in range(2):
-        mlp = MLPDelta(up_bf16(w1t_b), up_bf16(w2_b), n, k)
+        mlp = MLPDelta(up_bf16(w1t_b), up_bf16(w2_b), n, k, **mlp_kw)
         att = AttnDelta(na, H, kk, "cuda")
         mlp.step(xs[0], refresh=True)
         att.step(*qkv[0], refresh=True)
@@ -47,18 +48,22 @@ def _pair(n, d, h, k, na, H, kk, seed, steps):
     return layers, xs, qkv
 
 
-@pytest.mark.parametrize("n,d,h,k,na,H,kk", [
-    (300, 256, 640, 200, 300, 2, 100),      # ragged, 256-wide phase-2 tiles, 2 heads
-    (1000, 384, 1024, 130, 1000, 8, 300),   # 128-wide tiles (d % 256 != 0), XCD head mapping
-    (300, 256, 640, 0, 517, 3, 64),         # k = 0: attention units only; other token count
-    (517, 256, 512, 64, 300, 8, 0),         # kk = 0: o = num / den beside the MLP tiles
-    (129, 128, 64, 64, 129, 1, 129),        # one unit each side, every column / key kept
+@pytest.mark.parametrize("n,d,h,k,na,H,kk,mode", [
+    (300, 256, 640, 200, 300, 2, 100, "bf16"),      # ragged, 256-wide phase-2 tiles, 2 heads
+    (1000, 384, 1024, 130, 1000, 8, 300, "bf16"),   # 128-wide tiles (d % 256 != 0), XCD head mapping
+    (300, 256, 640, 0, 517, 3, 64, "bf16"),         # k = 0: attention units only; other token count
+    (517, 256, 512, 64, 300, 8, 0, "bf16"),         # kk = 0: o = num / den beside the MLP tiles
+    (129, 128, 64, 64, 129, 1, 129, "bf16"),        # one unit each side, every column / key kept
+    (300, 256, 640, 200, 300, 2, 100, "fp8"),       # both MLP products on fp8 operands
+    (1000, 384, 1024, 130, 1000, 8, 300, "fp8"),    # the same with 128-wide phase-2 tiles
+    (517, 256, 512, 64, 300, 8, 0, "fp8w2"),        # fp8 second product only, rescoring on
 ])
-def test_fused_step_matches_separate_calls(gpu_lib, n, d, h, k, na, H, kk):
+def test_fused_step_matches_separate_calls(gpu_lib, n, d, h, k, na, H, kk, mode):
     from dynamic_column_sparse_amd.layers import sparse_step
-    print(f"fused step vs separate calls n={n} d={d} h={h} k={k} na={na} H={H} kk={kk}", flush=True)
+    print(f"fused step vs separate calls n={n} d={d} h={h} k={k} na={na} H={H} kk={kk} {mode}", flush=True)
     steps = 4
-    ((m_s, a_s), (m_f, a_f)), xs, qkv = _pair(n, d, h, k, na, H, kk, 5, steps)
+    kw = {"bf16": {}, "fp8": dict(fp8=True, fp8_w2=True), "fp8w2": dict(fp8_w2=True, rescore=True)}[mode]
+    ((m_s, a_s), (m_f, a_f)), xs, qkv = _pair(n, d, h, k, na, H, kk, 5, steps, **kw)
     torch.cuda.synchronize()
     for t in range(1, steps):
         m_s.step(xs[t], refresh=False)
