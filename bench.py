@@ -70,6 +70,10 @@ def kernel_work(name, w, reident=False, fp8=False, fp8_w2=False):
         return 2.0 * n * d * k, ("mfma_fp8" if fp8 else "mfma")
     if name == "mlp_gemm2_sparse":
         return 2.0 * n * k * d, ("mfma_fp8" if fp8_w2 else "mfma")
+    if name == "sparse_step_reident_fused":
+        f8 = 2.0 * n * k * d
+        total = f8 + 8.0 * n * kk * HEAD_DIM * H
+        return total, (("mfma_mix", f8) if fp8_w2 else "mfma")
     if name == "sparse_step_fused" and fp8_w2:
         return 2.0 * n * k * d + 4.0 * n * kk * HEAD_DIM * H, ("mfma_mix", 2.0 * n * k * d)
     if name == "quantize_fp8":
@@ -305,7 +309,7 @@ def main():
         if att:
             att.step(*qkv[t], refresh=True)
 
-    fused = bool(mlp and att) and not args.separate and not args.attn_reident
+    fused = bool(mlp and att) and not args.separate
 
     def sparse(t):
         if fused:

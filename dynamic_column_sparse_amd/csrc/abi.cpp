@@ -182,6 +182,37 @@ bool overlap(const Span& a, const Span& b) {
   return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
 }
 
+// Arguments of the re-identifying attention step, including that no buffer it
+// writes (o, num, den, score: updated in place while the inputs are read)
+// shares memory with another buffer of the call.
+int check_reident(const chipmunk_attn* L, const uint16_t* q_prev, const uint16_t* k_prev, const uint16_t* v_prev,
+                  const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* idx, int32_t kk,
+                  const float* o) {
+  int rc = check_sparse_attn(L, q, k, v, idx, kk, CHIPMUNK_ATTN_SPARSE, o);
+  if (rc) return rc;
+  if ((rc = check_bf16_in(q_prev, "q_prev")) || (rc = check_bf16_in(k_prev, "k_prev")) ||
+      (rc = check_bf16_in(v_prev, "v_prev")))
+    return rc;
+  if (!L->score) return fail(CHIPMUNK_E_NULLPTR, "layer score is required (the step rescores its keys)");
+  const size_t toks = (size_t)L->heads * (size_t)L->n, hd = CHIPMUNK_HEAD_DIM;
+  const size_t nba = (size_t)chipmunk::row_blocks(L->n), ak = kk > 0 ? (size_t)kk : 0;
+  const Span wr[] = {{o, toks * hd * 4, "o"},
+                     {L->num, toks * hd * 4, "num"},
+                     {L->den, toks * 4, "den"},
+                     {L->score, (size_t)L->heads * nba * (size_t)L->n * 4, "score"}};
+  const Span rd[] = {{q_prev, toks * hd * 2, "q_prev"}, {k_prev, toks * hd * 2, "k_prev"},
+                     {v_prev, toks * hd * 2, "v_prev"}, {q, toks * hd * 2, "q"},
+                     {k, toks * hd * 2, "k"},           {v, toks * hd * 2, "v"},
+                     {idx, (size_t)L->heads * nba * ak * 4, "idx"}, {L->m, toks * 4, "m"}};
+  for (size_t i = 0; i < sizeof wr / sizeof wr[0]; ++i) {
+    for (size_t j = i + 1; j < sizeof wr / sizeof wr[0]; ++j)
+      if (overlap(wr[i], wr[j])) return fail(CHIPMUNK_E_SHAPE, "%s overlaps %s", wr[i].name, wr[j].name);
+    for (const Span& r : rd)
+      if (overlap(wr[i], r)) return fail(CHIPMUNK_E_SHAPE, "%s overlaps %s", wr[i].name, r.name);
+  }
+  return CHIPMUNK_OK;
+}
+
 
 }  // namespace
 
@@ -214,7 +245,7 @@ const char* kernel_name(int kid) {
   static const char* names[K_COUNT] = {"mlp_gemm1_sparse", "mlp_gemm1_dense", "mlp_gemm2_sparse", "mlp_gemm2_dense",
                                        "topk_rows",        "cache_writeback", "attn_stats",       "attn_dense",
                                        "attn_sparse",      "attn_refresh",     "sparse_step_fused",
-                                       "attn_reident",     "quantize_fp8"};
+                                       "attn_reident",     "quantize_fp8",     "sparse_step_reident_fused"};
   return (kid >= 0 && kid < K_COUNT) ? names[kid] : "";
 }
 
@@ -409,31 +440,8 @@ extern "C" int chipmunk_sparse_attn_reident(const chipmunk_attn* L, const uint16
                                             const uint16_t* v, const int32_t* idx, int32_t kk, float* o,
                                             void* stream) {
   try {
-    int rc = check_sparse_attn(L, q, k, v, idx, kk, CHIPMUNK_ATTN_SPARSE, o);
+    int rc = check_reident(L, q_prev, k_prev, v_prev, q, k, v, idx, kk, o);
     if (rc) return rc;
-    if ((rc = check_bf16_in(q_prev, "q_prev")) || (rc = check_bf16_in(k_prev, "k_prev")) ||
-        (rc = check_bf16_in(v_prev, "v_prev")))
-      return rc;
-    if (!L->score) return fail(CHIPMUNK_E_NULLPTR, "layer score is required (the step rescores its keys)");
-    // The kernel updates num, den and score in place and writes o while it
-    // reads the inputs: no written buffer may share memory with another
-    // buffer of the call.
-    const size_t toks = (size_t)L->heads * (size_t)L->n, hd = CHIPMUNK_HEAD_DIM;
-    const size_t nba = (size_t)chipmunk::row_blocks(L->n), ak = kk > 0 ? (size_t)kk : 0;
-    const Span wr[] = {{o, toks * hd * 4, "o"},
-                       {L->num, toks * hd * 4, "num"},
-                       {L->den, toks * 4, "den"},
-                       {L->score, (size_t)L->heads * nba * (size_t)L->n * 4, "score"}};
-    const Span rd[] = {{q_prev, toks * hd * 2, "q_prev"}, {k_prev, toks * hd * 2, "k_prev"},
-                       {v_prev, toks * hd * 2, "v_prev"}, {q, toks * hd * 2, "q"},
-                       {k, toks * hd * 2, "k"},           {v, toks * hd * 2, "v"},
-                       {idx, (size_t)L->heads * nba * ak * 4, "idx"}, {L->m, toks * 4, "m"}};
-    for (size_t i = 0; i < sizeof wr / sizeof wr[0]; ++i) {
-      for (size_t j = i + 1; j < sizeof wr / sizeof wr[0]; ++j)
-        if (overlap(wr[i], wr[j])) return fail(CHIPMUNK_E_SHAPE, "%s overlaps %s", wr[i].name, wr[j].name);
-      for (const Span& r : rd)
-        if (overlap(wr[i], r)) return fail(CHIPMUNK_E_SHAPE, "%s overlaps %s", wr[i].name, r.name);
-    }
     hipError_t e = chipmunk::launch_attn_reident(q_prev, k_prev, v_prev, q, k, v, idx, L->m, L->num, L->den, L->score,
                                                  o, L->n, L->heads, kk, L->scale, static_cast<hipStream_t>(stream));
     return hip_status(e, "re-identifying attention delta launch");
@@ -441,6 +449,45 @@ extern "C" int chipmunk_sparse_attn_reident(const chipmunk_attn* L, const uint16
     return fail(CHIPMUNK_E_INTERNAL, "internal error in chipmunk_sparse_attn_reident");
   }
 }
+
+namespace {
+// Both deltas in one grid: nothing one of them writes may share memory with
+// anything the other reads or writes.  att_w / att_r: the attention side's
+// written and read buffers.
+template <size_t NW, size_t NR>
+int check_step_overlap(const chipmunk_mlp* M, const uint16_t* x, const int32_t* mlp_idx, int32_t k, const float* y,
+                       const uint16_t* a_new_packed, const void* ws, const Span (&att_w)[NW], const Span (&att_r)[NR],
+                       int64_t attn_groups) {
+  const size_t nb = (size_t)chipmunk::row_blocks(M->n);
+  const size_t mk = k > 0 ? (size_t)k : 0;
+  const Span mlp_w[] = {{y, (size_t)M->n * M->d * 4, "y"},
+                        {M->a_cache, nb * M->h * 128 * 2, "mlp a_cache"},
+                        {a_new_packed, nb * mk * 128 * 2, "a_new_packed"},
+                        {ws, k > 0 ? layer_sparse_ws(M, k) : 0, "ws"},
+                        {rescore_target(M), rescore_target(M) ? nb * M->h * 4 : 0, "mlp score"}};
+  const Span mlp_r[] = {{x, (size_t)M->n * M->d * 2, "x"},
+                        {M->w1t, (size_t)M->h * M->d * 2, "w1t"},
+                        {is_fp8(M) ? M->w1t_f8 : nullptr, (size_t)M->h * M->d, "w1t_f8"},
+                        {is_fp8(M) ? M->w1t_scale : nullptr, (size_t)M->h, "w1t_scale"},
+                        {(M->flags & CHIPMUNK_MLP_FP8_W2) ? M->w2_f8 : nullptr, (size_t)M->h * M->d, "w2_f8"},
+                        {(M->flags & CHIPMUNK_MLP_FP8_W2) ? M->w2_scale : nullptr, (size_t)M->d, "w2_scale"},
+                        {M->w2, (size_t)M->h * M->d * 2, "w2"},
+                        {M->b1, M->b1 ? (size_t)M->h * 4 : 0, "b1"},
+                        {mlp_idx, nb * mk * 4, "mlp idx"}};
+  const int64_t groups = (k > 0 ? (int64_t)(M->d / 128) * (int64_t)nb + 8 : 0) + attn_groups;
+  if (groups > kMaxGroups) return fail(CHIPMUNK_E_SHAPE, "the fused grid exceeds %lld workgroups", (long long)kMaxGroups);
+  for (const Span& w : mlp_w) {
+    for (const Span& r : att_w)
+      if (overlap(w, r)) return fail(CHIPMUNK_E_SHAPE, "%s overlaps %s", w.name, r.name);
+    for (const Span& r : att_r)
+      if (overlap(w, r)) return fail(CHIPMUNK_E_SHAPE, "%s overlaps %s", w.name, r.name);
+  }
+  for (const Span& w : att_w)
+    for (const Span& r : mlp_r)
+      if (overlap(w, r)) return fail(CHIPMUNK_E_SHAPE, "%s overlaps %s", w.name, r.name);
+  return CHIPMUNK_OK;
+}
+}  // namespace
 
 extern "C" int chipmunk_sparse_step(const chipmunk_mlp* M, const uint16_t* x, const int32_t* mlp_idx, int32_t k,
                                     float* y, uint16_t* a_new_packed, void* ws, size_t ws_bytes,
@@ -450,42 +497,17 @@ extern "C" int chipmunk_sparse_step(const chipmunk_mlp* M, const uint16_t* x, co
     int rc = check_sparse_mlp(M, x, mlp_idx, k, y, a_new_packed, ws, ws_bytes);
     if (rc) return rc;
     if ((rc = check_sparse_attn(A, q, kx, v, attn_idx, kk, CHIPMUNK_ATTN_SPARSE, o))) return rc;
-    // The two deltas run side by side in one grid: nothing one of them writes
-    // may share memory with anything the other touches.
-    const size_t nb = (size_t)chipmunk::row_blocks(M->n), nba = (size_t)chipmunk::row_blocks(A->n);
+    const size_t nba = (size_t)chipmunk::row_blocks(A->n);
     const size_t toks = (size_t)A->heads * (size_t)A->n, hd = CHIPMUNK_HEAD_DIM;
-    const size_t mk = k > 0 ? (size_t)k : 0, ak = kk > 0 ? (size_t)kk : 0;
-    const Span mlp_w[] = {{y, (size_t)M->n * M->d * 4, "y"},
-                          {M->a_cache, nb * M->h * 128 * 2, "mlp a_cache"},
-                          {a_new_packed, nb * mk * 128 * 2, "a_new_packed"},
-                          {ws, k > 0 ? layer_sparse_ws(M, k) : 0, "ws"},
-                          {rescore_target(M), rescore_target(M) ? nb * M->h * 4 : 0, "mlp score"}};
-    const Span mlp_r[] = {{x, (size_t)M->n * M->d * 2, "x"},
-                          {M->w1t, (size_t)M->h * M->d * 2, "w1t"},
-                          {is_fp8(M) ? M->w1t_f8 : nullptr, (size_t)M->h * M->d, "w1t_f8"},
-                          {is_fp8(M) ? M->w1t_scale : nullptr, (size_t)M->h, "w1t_scale"},
-                          {(M->flags & CHIPMUNK_MLP_FP8_W2) ? M->w2_f8 : nullptr, (size_t)M->h * M->d, "w2_f8"},
-                          {(M->flags & CHIPMUNK_MLP_FP8_W2) ? M->w2_scale : nullptr, (size_t)M->d, "w2_scale"},
-                          {M->w2, (size_t)M->h * M->d * 2, "w2"},
-                          {M->b1, M->b1 ? (size_t)M->h * 4 : 0, "b1"},
-                          {mlp_idx, nb * mk * 4, "mlp idx"}};
+    const size_t ak = kk > 0 ? (size_t)kk : 0;
     const Span att_w[] = {{o, toks * hd * 4, "o"}};
     const Span att_r[] = {{q, toks * hd * 2, "q"},          {kx, toks * hd * 2, "k"},
                           {v, toks * hd * 2, "v"},          {attn_idx, (size_t)A->heads * nba * ak * 4, "attn idx"},
                           {A->m, toks * 4, "m"},            {A->num, toks * hd * 4, "num"},
                           {A->den, toks * 4, "den"}};
-    const int64_t groups = (k > 0 ? (int64_t)(M->d / 128) * (int64_t)nb + 8 : 0) + (int64_t)A->heads * (int64_t)nba;
-    if (groups > kMaxGroups)
-      return fail(CHIPMUNK_E_SHAPE, "the fused grid exceeds %lld workgroups", (long long)kMaxGroups);
-    for (const Span& w : mlp_w) {
-      for (const Span& r : att_w)
-        if (overlap(w, r)) return fail(CHIPMUNK_E_SHAPE, "%s overlaps %s", w.name, r.name);
-      for (const Span& r : att_r)
-        if (overlap(w, r)) return fail(CHIPMUNK_E_SHAPE, "%s overlaps %s", w.name, r.name);
-    }
-    for (const Span& w : att_w)
-      for (const Span& r : mlp_r)
-        if (overlap(w, r)) return fail(CHIPMUNK_E_SHAPE, "%s overlaps %s", w.name, r.name);
+    if ((rc = check_step_overlap(M, x, mlp_idx, k, y, a_new_packed, ws, att_w, att_r,
+                                 (int64_t)A->heads * (int64_t)nba)))
+      return rc;
     hipStream_t s = static_cast<hipStream_t>(stream);
     chipmunk::Fp8Rows f8buf;
     const chipmunk::Fp8Rows* f8 = nullptr;
@@ -502,6 +524,49 @@ extern "C" int chipmunk_sparse_step(const chipmunk_mlp* M, const uint16_t* x, co
     return hip_status(e, "sparse step launch");
   } catch (...) {
     return fail(CHIPMUNK_E_INTERNAL, "internal error in chipmunk_sparse_step");
+  }
+}
+
+extern "C" int chipmunk_sparse_step_reident(const chipmunk_mlp* M, const uint16_t* x, const int32_t* mlp_idx,
+                                            int32_t k, float* y, uint16_t* a_new_packed, void* ws, size_t ws_bytes,
+                                            const chipmunk_attn* A, const uint16_t* q_prev, const uint16_t* k_prev,
+                                            const uint16_t* v_prev, const uint16_t* q, const uint16_t* kx,
+                                            const uint16_t* v, const int32_t* attn_idx, int32_t kk, float* o,
+                                            void* stream) {
+  try {
+    int rc = check_sparse_mlp(M, x, mlp_idx, k, y, a_new_packed, ws, ws_bytes);
+    if (rc) return rc;
+    if ((rc = check_reident(A, q_prev, k_prev, v_prev, q, kx, v, attn_idx, kk, o))) return rc;
+    const size_t nba = (size_t)chipmunk::row_blocks(A->n);
+    const size_t toks = (size_t)A->heads * (size_t)A->n, hd = CHIPMUNK_HEAD_DIM;
+    const size_t ak = kk > 0 ? (size_t)kk : 0;
+    const Span att_w[] = {{o, toks * hd * 4, "o"},
+                          {A->num, toks * hd * 4, "num"},
+                          {A->den, toks * 4, "den"},
+                          {A->score, (size_t)A->heads * nba * (size_t)A->n * 4, "attn score"}};
+    const Span att_r[] = {{q_prev, toks * hd * 2, "q_prev"}, {k_prev, toks * hd * 2, "k_prev"},
+                          {v_prev, toks * hd * 2, "v_prev"}, {q, toks * hd * 2, "q"},
+                          {kx, toks * hd * 2, "k"},          {v, toks * hd * 2, "v"},
+                          {attn_idx, (size_t)A->heads * nba * ak * 4, "attn idx"}, {A->m, toks * 4, "m"}};
+    if ((rc = check_step_overlap(M, x, mlp_idx, k, y, a_new_packed, ws, att_w, att_r,
+                                 (int64_t)A->heads * (int64_t)nba)))
+      return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    chipmunk::Fp8Rows f8buf;
+    const chipmunk::Fp8Rows* f8 = nullptr;
+    if (k > 0) {
+      hipError_t e = prepare_fp8(M, x, ws, sparse_mlp_ws(M->n, k), &f8buf, &f8, s);
+      if (e != hipSuccess) return hip_status(e, "quantize_fp8 launch");
+    }
+    chipmunk::Fp8Cols f8wbuf;
+    const chipmunk::Fp8Cols* f8w = fp8_second(M, &f8wbuf);
+    hipError_t e = chipmunk::launch_sparse_step_reident(
+        x, M->w1t, M->b1, mlp_idx, M->a_cache, static_cast<uint16_t*>(ws), a_new_packed, rescore_target(M), M->w2, y,
+        M->n, M->d, M->h, k, q_prev, k_prev, v_prev, q, kx, v, attn_idx, A->m, A->num, A->den, A->score, o, A->n,
+        A->heads, kk, A->scale, s, f8, f8w);
+    return hip_status(e, "re-identifying sparse step launch");
+  } catch (...) {
+    return fail(CHIPMUNK_E_INTERNAL, "internal error in chipmunk_sparse_step_reident");
   }
 }
 

@@ -826,11 +826,23 @@ __device__ __forceinline__ void load_q_frag(QFrag& qf, const uint16_t* row, int 
   for (int s2 = 0; s2 < 8; ++s2) qf.f[s2] = *(const bf16x8_t*)(row + s2 * 16 + (lane >> 5) * 8);
 }
 
-__global__ __launch_bounds__(256, 2) void attn_reident(
-    const uint16_t* __restrict__ q_prev, const uint16_t* __restrict__ k_prev, const uint16_t* __restrict__ v_prev,
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const int32_t* __restrict__ idx, const float* __restrict__ m, float* __restrict__ num, float* __restrict__ den,
-    float* __restrict__ score, float* __restrict__ o, int64_t n, int heads, int kk, float scale) {
+// LDS of one attn_reident workgroup (a struct, so that a shared-grid kernel can
+// overlay it with another body's LDS).
+struct AttnReidentLds {
+  unsigned char ring[4 * 2 * kTile];      // 4 stages of 32 K rows + 32 V rows
+  int ids[kReidIdSlots][kSK];
+  unsigned char p[4][32 * 64];            // each wave's fp16 p tile
+  float sc[2][4][kSK];                    // partial scores of two chunks
+  float inv[kRowBlock], den[kRowBlock], den_old[kRowBlock];
+};
+
+// Body of the re-identifying step for workgroup `lin` of its grid.
+__device__ __forceinline__ void attn_reident_body(
+    int lin, AttnReidentLds& lds, const uint16_t* __restrict__ q_prev, const uint16_t* __restrict__ k_prev,
+    const uint16_t* __restrict__ v_prev, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const int32_t* __restrict__ idx, const float* __restrict__ m,
+    float* __restrict__ num, float* __restrict__ den, float* __restrict__ score, float* __restrict__ o, int64_t n,
+    int heads, int kk, float scale) {
   constexpr int SK = kSK;
   constexpr int NSS = 4;
   constexpr int STAGE = 2 * kTile;
@@ -841,16 +853,17 @@ __global__ __launch_bounds__(256, 2) void attn_reident(
   constexpr int PIECES = kRowBlock * 128 / 4 / 256;
   constexpr float kW = 16384.f;   // score weights 2^14 / den: normal fp16 for den in [2^-2, 2^28]
   static_assert((RID & (RID - 1)) == 0 && RID >= DID + 2, "id ring: a new chunk's slot lives until its score store");
-  __shared__ __align__(16) unsigned char smem[NSS * STAGE];
-  __shared__ __align__(16) int sIdx[RID][SK];
-  __shared__ __align__(16) unsigned char sP[4][32 * 64];
-  __shared__ float sSc[2][4][SK];
-  __shared__ float sInv[kRowBlock];
-  __shared__ float sDen[kRowBlock];
-  __shared__ float sDenOld[kRowBlock];
+  static_assert(sizeof(lds.ring) == NSS * STAGE, "LDS layout");
+  unsigned char* smem = lds.ring;
+  int (*sIdx)[SK] = lds.ids;
+  unsigned char (*sP)[32 * 64] = lds.p;
+  float (*sSc)[4][SK] = lds.sc;
+  float* sInv = lds.inv;
+  float* sDen = lds.den;
+  float* sDenOld = lds.den_old;
   const int nb = (int)row_blocks(n);
   int hh, b;
-  head_block(heads, nb, hh, b, blockIdx.x);
+  head_block(heads, nb, hh, b, lin);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint32_t smem_lds = lds_addr(smem);
@@ -1110,6 +1123,16 @@ __global__ __launch_bounds__(256, 2) void attn_reident(
     *(float4*)(o + g) = make_float4(nw.x / dt, nw.y / dt, nw.z / dt, nw.w / dt);
   }
   if (tid < rows) den[hoff + r0 + tid] = sDenOld[tid] + sDen[tid];
+}
+
+__global__ __launch_bounds__(256, 2) void attn_reident(
+    const uint16_t* __restrict__ q_prev, const uint16_t* __restrict__ k_prev, const uint16_t* __restrict__ v_prev,
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const int32_t* __restrict__ idx, const float* __restrict__ m, float* __restrict__ num, float* __restrict__ den,
+    float* __restrict__ score, float* __restrict__ o, int64_t n, int heads, int kk, float scale) {
+  __shared__ __align__(16) AttnReidentLds lds;
+  attn_reident_body(blockIdx.x, lds, q_prev, k_prev, v_prev, q, k, v, idx, m, num, den, score, o, n, heads, kk,
+                    scale);
 }
 
 }  // namespace

@@ -25,6 +25,7 @@ enum KernelId {
   K_SPARSE_STEP_FUSED,
   K_ATTN_REIDENT,
   K_QUANTIZE_FP8,
+  K_SPARSE_STEP_REIDENT_FUSED,
   K_COUNT
 };
 const char* kernel_name(int kid);
@@ -95,5 +96,15 @@ hipError_t launch_sparse_step(const uint16_t* x, const uint16_t* w1t, const floa
                               const uint16_t* v, const int32_t* aidx, const float* m, const float* num,
                               const float* den, float* o, int64_t na, int heads, int kk, float scale,
                               hipStream_t s, const Fp8Rows* f8 = nullptr, const Fp8Cols* f8w = nullptr);
+
+// The same with the re-identifying attention step in the shared grid.
+hipError_t launch_sparse_step_reident(const uint16_t* x, const uint16_t* w1t, const float* b1, const int32_t* midx,
+                                      uint16_t* a_cache, uint16_t* dbuf, uint16_t* a_packed, float* mscore,
+                                      const uint16_t* w2, float* y, int64_t n, int d, int h, int k,
+                                      const uint16_t* q_prev, const uint16_t* k_prev, const uint16_t* v_prev,
+                                      const uint16_t* q, const uint16_t* kx, const uint16_t* v, const int32_t* aidx,
+                                      const float* m, float* num, float* den, float* ascore, float* o, int64_t na,
+                                      int heads, int kk, float scale, hipStream_t s, const Fp8Rows* f8,
+                                      const Fp8Cols* f8w);
 
 }  // namespace chipmunk

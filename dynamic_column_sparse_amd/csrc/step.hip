@@ -1,6 +1,7 @@
 // The sparse step of one transformer block as two launches: the MLP's sparse
 // phase 1, then ONE kernel whose first workgroups run the MLP's phase-2 tiles
-// and whose remaining workgroups run the attention delta.
+// and whose remaining workgroups run the attention delta (the fixed-set step,
+// or the step that re-identifies its keys every step).
 //
 // The attention delta and the MLP delta of a step read different inputs and
 // write different outputs, so nothing orders them.  Run one after the other,
@@ -52,7 +53,89 @@ __global__ __launch_bounds__(256, 2) void sparse_step_fused(
   }
 }
 
+// LDS of a phase-2 tile (ring and id ring), for the overlay below.
+template <int BN, bool F8W>
+struct Gemm2TileLds {
+  unsigned char ring[F8W ? Gemm2RowsF8Lds<BN>::kRing : Gemm2RowsLds<BN>::kRing];
+  int ids[F8W ? Gemm2RowsF8Lds<BN>::kIds : Gemm2RowsLds<BN>::kIds];
+};
+template <int BN, bool F8W>
+union ReidentStepLds {
+  Gemm2TileLds<BN, F8W> g2;
+  AttnReidentLds at;
+};
+
+// The same shared grid with the re-identifying attention step (num, den hold
+// totals; the previous step's q, k, v give the share taken out) in place of
+// the fixed-set one.  The two bodies' LDS overlay each other.
+template <int BN, bool F8W>
+__global__ __launch_bounds__(256, 2) void sparse_step_reident_fused(
+    int g2, const uint16_t* __restrict__ dsrc, const uint16_t* __restrict__ w2, const uint8_t* __restrict__ w2f8,
+    const uint8_t* __restrict__ w2s, const int32_t* __restrict__ midx, float* __restrict__ y, int64_t n, int d, int h,
+    int k, int kp, const uint16_t* __restrict__ q_prev, const uint16_t* __restrict__ k_prev,
+    const uint16_t* __restrict__ v_prev, const uint16_t* __restrict__ q, const uint16_t* __restrict__ kx,
+    const uint16_t* __restrict__ v, const int32_t* __restrict__ aidx, const float* __restrict__ m,
+    float* __restrict__ num, float* __restrict__ den, float* __restrict__ ascore, float* __restrict__ o, int64_t na,
+    int heads, int kk, float scale) {
+  __shared__ __align__(16) ReidentStepLds<BN, F8W> lds;
+  const int bid = blockIdx.x;
+  if (bid < g2) {
+    if constexpr (F8W)
+      gemm2_rows_body_f8<BN>(bid, lds.g2.ring, reinterpret_cast<int(*)[64]>(lds.g2.ids),
+                             (const unsigned char*)dsrc, w2f8, w2s, midx, y, n, d, h, k, kp);
+    else
+      gemm2_rows_body<BN>(bid, lds.g2.ring, reinterpret_cast<int(*)[32]>(lds.g2.ids), dsrc, w2, midx, y, n, d, h, k,
+                          kp);
+  } else {
+    attn_reident_body(bid - g2, lds.at, q_prev, k_prev, v_prev, q, kx, v, aidx, m, num, den, ascore, o, na, heads,
+                      kk, scale);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_sparse_step_reident(const uint16_t* x, const uint16_t* w1t, const float* b1, const int32_t* midx,
+                                      uint16_t* a_cache, uint16_t* dbuf, uint16_t* a_packed, float* mscore,
+                                      const uint16_t* w2, float* y, int64_t n, int d, int h, int k,
+                                      const uint16_t* q_prev, const uint16_t* k_prev, const uint16_t* v_prev,
+                                      const uint16_t* q, const uint16_t* kx, const uint16_t* v, const int32_t* aidx,
+                                      const float* m, float* num, float* den, float* ascore, float* o, int64_t na,
+                                      int heads, int kk, float scale, hipStream_t s, const Fp8Rows* f8,
+                                      const Fp8Cols* f8w) {
+  const int kp = padded_k(k);
+  int g2 = 0;
+  const int bn = d % 256 == 0 ? 256 : 128;
+  if (k > 0) {
+    hipError_t e =
+        launch_mlp_gemm1(false, x, w1t, b1, midx, a_cache, dbuf, a_packed, mscore, n, d, h, k, s, f8, f8w != nullptr);
+    if (e != hipSuccess) return e;
+    g2 = xcd_grid(d / bn * (int)row_blocks(n));
+  }
+  const int ga = (int)(row_blocks(na) * heads);
+  const dim3 grid((unsigned)(g2 + ga));
+  timing_before(K_SPARSE_STEP_REIDENT_FUSED, s);
+  const uint8_t* w2f8 = f8w ? f8w->w : nullptr;
+  const uint8_t* w2s = f8w ? f8w->w_scale : nullptr;
+#define REID_LAUNCH(BN_, F8W_)                                                                                       \
+  hipLaunchKernelGGL((sparse_step_reident_fused<BN_, F8W_>), grid, dim3(256), 0, s, g2, dbuf, w2, w2f8, w2s, midx, y, \
+                     n, d, h, k, kp, q_prev, k_prev, v_prev, q, kx, v, aidx, m, num, den, ascore, o, na, heads, kk,  \
+                     scale)
+  if (bn == 256) {
+    if (f8w)
+      REID_LAUNCH(256, true);
+    else
+      REID_LAUNCH(256, false);
+  } else {
+    if (f8w)
+      REID_LAUNCH(128, true);
+    else
+      REID_LAUNCH(128, false);
+  }
+#undef REID_LAUNCH
+  hipError_t e = hipGetLastError();
+  timing_after(K_SPARSE_STEP_REIDENT_FUSED, s);
+  return e;
+}
 
 hipError_t launch_sparse_step(const uint16_t* x, const uint16_t* w1t, const float* b1, const int32_t* midx,
                               uint16_t* a_cache, uint16_t* dbuf, uint16_t* a_packed, float* mscore,

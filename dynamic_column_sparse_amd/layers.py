@@ -153,9 +153,17 @@ class AttnDelta:
 
 def sparse_step(mlp: MLPDelta, att: AttnDelta, x, q, k, v, stream=None):
     """One sparse step of a block whose attention and MLP deltas are independent
-    (both read the block's input): the MLP's top-k over its dense-step scores,
-    then both deltas through chipmunk_sparse_step.  Same results as
+    (both read the block's input): the MLP's top-k over its scores (and the
+    attention's, when it re-identifies every step), then both deltas through
+    chipmunk_sparse_step (or chipmunk_sparse_step_reident).  Same results as
     ``mlp.step(x, False)`` followed by ``att.step(q, k, v, False)``."""
     mlp.identify(stream)
-    lib.chipmunk_sparse_step(mlp.layer, x, mlp.idx, mlp.k, mlp.y, None, mlp.ws, att.layer, q, k, v, att.idx,
-                             att.kk, att.o, stream=stream)
+    if att.reident:
+        att.identify(stream)
+        qp, kp, vp = att.prev
+        lib.chipmunk_sparse_step_reident(mlp.layer, x, mlp.idx, mlp.k, mlp.y, None, mlp.ws, att.layer, qp, kp, vp,
+                                         q, k, v, att.idx, att.kk, att.o, stream=stream)
+        att.prev = (q, k, v)
+    else:
+        lib.chipmunk_sparse_step(mlp.layer, x, mlp.idx, mlp.k, mlp.y, None, mlp.ws, att.layer, q, k, v, att.idx,
+                                 att.kk, att.o, stream=stream)

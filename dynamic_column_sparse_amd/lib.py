@@ -30,6 +30,7 @@ STATUS = {0: "CHIPMUNK_OK", 1: "CHIPMUNK_E_NULLPTR", 2: "CHIPMUNK_E_SHAPE", 3: "
 
 EXPORTS = ("chipmunk_dense_step", "chipmunk_identify_topk", "chipmunk_sparse_mlp_delta",
            "chipmunk_sparse_attn_delta", "chipmunk_sparse_attn_reident", "chipmunk_sparse_step",
+           "chipmunk_sparse_step_reident",
            "chipmunk_cache_writeback", "chipmunk_quantize_fp8",
            "chipmunk_quantize_fp8_cols",
            "chipmunk_workspace_bytes",
@@ -73,6 +74,8 @@ def _load() -> ctypes.CDLL:
         "chipmunk_sparse_attn_reident": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp]),
         "chipmunk_sparse_step": (ctypes.c_int, [vp, vp, vp, i32, vp, vp, vp, sz,
                                                  vp, vp, vp, vp, vp, i32, vp, vp]),
+        "chipmunk_sparse_step_reident": (ctypes.c_int, [vp, vp, vp, i32, vp, vp, vp, sz,
+                                                         vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp]),
         "chipmunk_cache_writeback": (ctypes.c_int, [vp, vp, vp, i32, vp]),
         "chipmunk_quantize_fp8": (ctypes.c_int, [vp, i64, i32, vp, vp, vp]),
         "chipmunk_quantize_fp8_cols": (ctypes.c_int, [vp, i64, i32, vp, vp, vp]),
@@ -185,6 +188,15 @@ def chipmunk_sparse_step(mlp: MLPLayer, x, mlp_idx, k: int, y, a_new_packed, ws,
     _check(_lib.chipmunk_sparse_step(ctypes.byref(mlp), _ptr(x), _ptr(mlp_idx), k, _ptr(y), _ptr(a_new_packed),
                                      _ptr(ws), nbytes, ctypes.byref(attn), _ptr(q), _ptr(kx), _ptr(v),
                                      _ptr(attn_idx), kk, _ptr(o), _stream(stream)))
+
+
+def chipmunk_sparse_step_reident(mlp: MLPLayer, x, mlp_idx, k: int, y, a_new_packed, ws, attn: AttnLayer, q_prev,
+                                 k_prev, v_prev, q, kx, v, attn_idx, kk: int, o, stream=None, ws_bytes=None):
+    nbytes = _nbytes(ws, ws_bytes)
+    _check(_lib.chipmunk_sparse_step_reident(ctypes.byref(mlp), _ptr(x), _ptr(mlp_idx), k, _ptr(y),
+                                             _ptr(a_new_packed), _ptr(ws), nbytes, ctypes.byref(attn), _ptr(q_prev),
+                                             _ptr(k_prev), _ptr(v_prev), _ptr(q), _ptr(kx), _ptr(v), _ptr(attn_idx),
+                                             kk, _ptr(o), _stream(stream)))
 
 
 def chipmunk_quantize_fp8(src, rows: int, cols: int, dst, scale, stream=None):

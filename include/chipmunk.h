@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define CHIPMUNK_ABI_VERSION 5
+#define CHIPMUNK_ABI_VERSION 6
 #define CHIPMUNK_ROW_BLOCK 128
 #define CHIPMUNK_HEAD_DIM 128
 
@@ -278,6 +278,20 @@ int chipmunk_sparse_step(const chipmunk_mlp* mlp, const uint16_t* x, const int32
                          float* y, uint16_t* a_new_packed, void* ws, size_t ws_bytes,
                          const chipmunk_attn* attn, const uint16_t* q, const uint16_t* kx, const uint16_t* v,
                          const int32_t* attn_idx, int32_t kk, float* o, void* stream);
+
+/* chipmunk_sparse_step with the re-identifying attention step: the MLP delta
+ * of chipmunk_sparse_mlp_delta and chipmunk_sparse_attn_reident on `attn`,
+ * with the arguments of those two calls and the same results, bit for bit,
+ * in two launches (the MLP's phase 1, then one grid with the MLP's phase-2
+ * tiles and the attention units).  The same independence rule as
+ * chipmunk_sparse_step: no buffer either delta writes (y, a_cache,
+ * a_new_packed, ws, the MLP score when rescoring; o, num, den, the attention
+ * score) may overlap a buffer the other reads or writes (CHIPMUNK_E_SHAPE). */
+int chipmunk_sparse_step_reident(const chipmunk_mlp* mlp, const uint16_t* x, const int32_t* mlp_idx, int32_t k,
+                                 float* y, uint16_t* a_new_packed, void* ws, size_t ws_bytes,
+                                 const chipmunk_attn* attn, const uint16_t* q_prev, const uint16_t* k_prev,
+                                 const uint16_t* v_prev, const uint16_t* q, const uint16_t* kx, const uint16_t* v,
+                                 const int32_t* attn_idx, int32_t kk, float* o, void* stream);
 
 /* Cache writeback (the separate form of the fused writeback above): copy the
  * packed new activations a_new_packed [nb][k][128] into a_cache[b][idx[b][p]]

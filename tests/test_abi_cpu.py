@@ -28,7 +28,7 @@ def test_header_declares_the_entry_points():
     decl = _declared()
     for name in ("chipmunk_dense_step", "chipmunk_identify_topk", "chipmunk_sparse_mlp_delta",
                  "chipmunk_sparse_attn_delta", "chipmunk_cache_writeback", "chipmunk_sparse_step",
-                 "chipmunk_sparse_attn_reident"):
+                 "chipmunk_sparse_attn_reident", "chipmunk_sparse_step_reident"):
         assert name in decl
 
 
@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_names_workspace(L):
-    assert L.chipmunk_abi_version() == 5
+    assert L.chipmunk_abi_version() == 6
     names = L.kernel_names()
     assert "mlp_gemm1_sparse" in names and "attn_sparse" in names and "topk_rows" in names
     assert "attn_reident" in names
@@ -223,6 +223,29 @@ def test_fp8_checks(L):
     assert rc == 5
     rc = L.raw().chipmunk_dense_step(0, ctypes.byref(lay), FAKE, None, None, FAKE, None, 0, None)
     assert rc == 5
+
+
+def test_reident_step_checks(L):
+    base = {name: FAKE + i * (1 << 32) for i, name in enumerate(
+        ("w1t", "w2", "a_cache", "score", "x", "midx", "y", "ws", "m", "num", "den", "ascore", "qp", "kp", "vp",
+         "q", "k", "v", "aidx", "o"))}
+
+    def call(k=200, kk=100, **over):
+        a = {**base, **over}
+        lay = L.mlp_layer(300, 256, 640, a["w1t"], a["w2"], a["a_cache"], a["score"])
+        att = L.attn_layer(300, 2, a["m"], a["num"], a["den"], a["ascore"])
+        return _code(L, L.chipmunk_sparse_step_reident, lay, a["x"], a["midx"], k, a["y"], None, a["ws"], att,
+                     a["qp"], a["kp"], a["vp"], a["q"], a["k"], a["v"], a["aidx"], kk, a["o"], stream=0,
+                     ws_bytes=1 << 30)
+
+    assert call(k=641) == 2 and call(kk=301) == 2
+    assert call(ascore=None) == 1                 # the attention step rescores its keys
+    assert call(qp=None) == 1
+    assert call(num=base["y"]) == 2               # the attention cache over the MLP output
+    assert "overlaps" in L.chipmunk_last_error()
+    assert call(ascore=base["ws"] + 64) == 2      # the attention scores inside the MLP workspace
+    assert call(o=base["num"]) == 2               # two attention outputs on one buffer
+    assert call(qp=base["a_cache"]) == 2          # the MLP writes what the attention reads
 
 
 def test_timer_api_without_launches(L):

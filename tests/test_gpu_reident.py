@@ -139,3 +139,42 @@ def test_reident_unchanged_inputs_keep_cache_and_is_deterministic(gpu_lib):
         runs.append([x.clone() for x in (att.o, att.num, att.den, att.score, att.idx)])
     for a, b in zip(*runs):
         assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
+@pytest.mark.parametrize("n,d,h,k,na,H,kk,mode", [
+    (300, 256, 640, 200, 300, 2, 100, "bf16"),      # ragged, 256-wide phase-2 tiles
+    (1000, 384, 1024, 130, 700, 8, 150, "bf16"),    # 128-wide tiles, XCD head mapping, other token count
+    (300, 256, 640, 0, 300, 3, 70, "bf16"),         # k = 0: attention units only
+    (517, 256, 512, 64, 300, 2, 0, "bf16"),         # kk = 0 beside the MLP tiles
+    (300, 256, 640, 200, 300, 2, 100, "fp8"),       # both MLP products on fp8
+])
+def test_reident_shared_grid_matches_separate_calls(gpu_lib, n, d, h, k, na, H, kk, mode):
+    # chipmunk_sparse_step_reident equals chipmunk_sparse_mlp_delta followed by
+    # chipmunk_sparse_attn_reident, bit for bit, over several steps in which
+    # both index sets are identified anew.
+    from dynamic_column_sparse_amd.layers import AttnDelta, MLPDelta, sparse_step
+    print(f"re-identifying shared grid vs separate n={n} d={d} h={h} k={k} na={na} H={H} kk={kk} {mode}", flush=True)
+    steps = 4
+    w1t_b, w2_b = syn.mlp_weights(4, d, h)
+    xs = [up_bf16(x) for x in syn.activation_walk(4, "X", steps, n, d)]
+    qkv = [[up_bf16(a) for a in st] for st in zip(*[syn.heads_walk(4, t, steps, H, na) for t in "QKV"])]
+    kw = dict(fp8=True, fp8_w2=True) if mode == "fp8" else {}
+    pairs = []
+    for _ in range(2):
+        mlp = MLPDelta(up_bf16(w1t_b), up_bf16(w2_b), n, k, **kw)
+        att = AttnDelta(na, H, kk, "cuda", reident=True)
+        mlp.step(xs[0], refresh=True)
+        att.step(*qkv[0], refresh=True)
+        pairs.append((mlp, att))
+    (m_s, a_s), (m_f, a_f) = pairs
+    torch.cuda.synchronize()
+    bits = lambda t: t.view(torch.int32) if t.dtype in (torch.float32, torch.int32) else t.view(torch.int16)
+    for t in range(1, steps):
+        m_s.step(xs[t], refresh=False)
+        a_s.step(*qkv[t], refresh=False)
+        sparse_step(m_f, a_f, xs[t], *qkv[t])
+        torch.cuda.synchronize()
+        for name, a, b in (("y", m_s.y, m_f.y), ("a_cache", m_s.a_cache, m_f.a_cache), ("mlp idx", m_s.idx, m_f.idx),
+                           ("o", a_s.o, a_f.o), ("num", a_s.num, a_f.num), ("den", a_s.den, a_f.den),
+                           ("attn score", a_s.score, a_f.score), ("attn idx", a_s.idx, a_f.idx)):
+            assert torch.equal(bits(a), bits(b)), f"step {t}: {name}"
