@@ -20,8 +20,14 @@ def _bits(t):
     return t.view(torch.int32) if t.dtype == torch.float32 else t.view(torch.int16)
 
 
-def test_sparse_step_graph_replay_matches_eager(gpu_lib):
+@pytest.mark.parametrize("mode", ["bf16", "fp8", "reident"])
+def test_sparse_step_graph_replay_matches_eager(gpu_lib, mode):
+    # bf16: the default layers; fp8: both MLP products on fp8 (the quantize
+    # kernel of x runs inside the graph); reident: attention identifying its
+    # keys every step (the previous step's q, k, v are baked into each captured
+    # step, so the eager side is given the same ones).
     from dynamic_column_sparse_amd.layers import AttnDelta, MLPDelta
+    print(f"graph replay {mode}", flush=True)
     n, d, h, k, H, kk = 300, 256, 640, 200, 2, 100
     w1t_b, w2_b = syn.mlp_weights(1, d, h)
     xs = [up_bf16(x) for x in syn.activation_walk(1, "X", 4, n, d)]
@@ -29,8 +35,8 @@ def test_sparse_step_graph_replay_matches_eager(gpu_lib):
 
     layers = []
     for _ in range(2):
-        mlp = MLPDelta(up_bf16(w1t_b), up_bf16(w2_b), n, k)
-        att = AttnDelta(n, H, kk, "cuda")
+        mlp = MLPDelta(up_bf16(w1t_b), up_bf16(w2_b), n, k, **(dict(fp8=True, fp8_w2=True) if mode == "fp8" else {}))
+        att = AttnDelta(n, H, kk, "cuda", reident=mode == "reident")
         mlp.step(xs[0], refresh=True)
         att.step(*qkv[0], refresh=True)
         layers.append((mlp, att))
@@ -38,6 +44,8 @@ def test_sparse_step_graph_replay_matches_eager(gpu_lib):
     (m_e, a_e), (m_g, a_g) = layers
 
     def step(mlp, att, t):
+        if att.reident:
+            att.prev = tuple(qkv[t - 1])
         mlp.step(xs[t], refresh=False)
         att.step(*qkv[t], refresh=False)
 
@@ -63,7 +71,8 @@ def test_sparse_step_graph_replay_matches_eager(gpu_lib):
             scratch.add_(1.0)                      # unrelated eager work between replays
             graphs[t].replay()
             torch.cuda.synchronize()
-            for a, b in ((m_e.y, m_g.y), (m_e.a_cache, m_g.a_cache), (m_e.idx, m_g.idx), (a_e.o, a_g.o)):
+            for a, b in ((m_e.y, m_g.y), (m_e.a_cache, m_g.a_cache), (m_e.idx, m_g.idx), (a_e.o, a_g.o),
+                         (a_e.num, a_g.num), (a_e.score, a_g.score), (a_e.idx, a_g.idx)):
                 assert torch.equal(_bits(a) if a.dtype != torch.int32 else a, _bits(b) if b.dtype != torch.int32 else b), \
                     f"replay {rep} step {t}"
     assert float(scratch[0]) == 9.0
