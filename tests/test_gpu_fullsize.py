@@ -53,18 +53,25 @@ def _cache_rows(a_cache, blocks, n):
 
 
 # -------------------------------------------------------------------- MLP ---
-def _mlp_loop(L, n, d, h, k, steps, dense_every, nsample, seed=0):
+def _mlp_loop(L, n, d, h, k, steps, dense_every, nsample, seed=0, fp8=False):
+    # fp8: both products on fp8 operands; the oracle runs on the values those
+    # operands carry (fp8_rows of x and W1^T; fp8_cols of W2 and fp8 blocks of
+    # D in the sparse steps).
     from dynamic_column_sparse_amd.layers import MLPDelta
     nb = (n + RB - 1) // RB
     blocks = _sample_blocks(nb, nsample, seed + 11, n)
     rows = _rows_of(blocks, n)
     rows_t = torch.from_numpy(rows).cuda()
-    print(f"mlp full size n={n} d={d} h={h} k={k} steps={steps} sampled blocks={len(blocks)}", flush=True)
+    print(f"mlp full size n={n} d={d} h={h} k={k} steps={steps} sampled blocks={len(blocks)} fp8={fp8}", flush=True)
 
     w1t_b, w2_b = syn.mlp_weights(seed, d, h)
-    lay = MLPDelta(up_bf16(w1t_b), up_bf16(w2_b), n, k)
+    lay = MLPDelta(up_bf16(w1t_b), up_bf16(w2_b), n, k, **(dict(fp8=True, fp8_w2=True) if fp8 else {}))
     w1t, w2 = oracle.from_bf16_bits(w1t_b), oracle.from_bf16_bits(w2_b)
     del w1t_b, w2_b
+    w2_sparse = w2
+    if fp8:
+        w1t = oracle.fp8_rows(w1t)
+        w2_sparse = oracle.fp8_cols(w2)
     xs = syn.activation_walk(seed, "X", steps, n, d)
 
     a_s = np.zeros((len(rows), h))
@@ -73,6 +80,8 @@ def _mlp_loop(L, n, d, h, k, steps, dense_every, nsample, seed=0):
     for t in range(steps):
         x_g = up_bf16(xs[t])
         x_s = oracle.from_bf16_bits(xs[t][rows])
+        if fp8:
+            x_s = oracle.fp8_rows(x_s)
         if t % dense_every == 0:
             lay.dense(x_g)
             torch.cuda.synchronize()
@@ -93,7 +102,7 @@ def _mlp_loop(L, n, d, h, k, steps, dense_every, nsample, seed=0):
         np.testing.assert_array_equal(g_idx, oracle.identify_topk(g_score, k))
         jac = idx_sets_valid(g_idx, oracle.identify_topk(sc_s.astype(np.float32), k), sc_s.astype(np.float32))
         y_old = y_s
-        a_s, y_s = oracle.mlp_sparse(x_s, w1t, None, w2, a_s, y_s, g_idx)
+        a_s, y_s = oracle.mlp_sparse(x_s, w1t, None, w2_sparse, a_s, y_s, g_idx, d_fp8=fp8)
         y_g = lay.y[rows_t].cpu().numpy()
         e_y = oracle.rel_frobenius(y_g, y_s)
         e_dy = oracle.rel_frobenius(y_g - y_prev, y_s - y_old)
@@ -113,6 +122,12 @@ def test_hunyuan_mlp_sampled(gpu_lib):
     # the first three steps of the loop (dense, then sparse); the oracle follows
     # 32 seeded blocks (4096 rows) plus the 16-row tail block.
     _mlp_loop(gpu_lib, 118800, 3072, 12288, 860, steps=3, dense_every=10, nsample=32)
+
+
+def test_hunyuan_mlp_fp8_sampled(gpu_lib):
+    # The same shape with both products on fp8 operands (16 seeded blocks and
+    # the 16-row tail block).
+    _mlp_loop(gpu_lib, 118800, 3072, 12288, 860, steps=3, dense_every=10, nsample=16, fp8=True)
 
 
 # -------------------------------------------------------------- attention ---
