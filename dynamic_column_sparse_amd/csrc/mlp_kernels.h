@@ -40,6 +40,7 @@ constexpr int NS = 3;     // LDS ring stages: one consumed, two in flight
 #endif
 constexpr int kGroupTiles = MLP_GROUP_TILES;   // column tiles of one row block run back to back
 
+
 // F8: x and W1^T are e4m3 codes (one byte per element) with one E8M0 scale
 // byte per row (xs for the token rows, ws1 for the hidden units); each 64-byte
 // row piece of a chunk is then 64 reduction steps instead of 32, and one
@@ -355,16 +356,19 @@ __global__ __launch_bounds__(256, 2) void mlp_gemm1(const void* __restrict__ xv,
   }
 }
 
+// 32-deep chunks: a 72 KB ring, so two workgroups share a CU (with 64-deep
+// chunks and one workgroup per CU the refresh took 7-9% longer).
 template <int BN, bool DENSE>
-__global__ __launch_bounds__(256, 1) void mlp_gemm2(const uint16_t* __restrict__ src,
+__global__ __launch_bounds__(256, 2) void mlp_gemm2(const uint16_t* __restrict__ src,
                                                     const uint16_t* __restrict__ w2,
                                                     const int32_t* __restrict__ idx,
                                                     const float* __restrict__ b2, float* __restrict__ y,
                                                     int64_t n, int d, int h, int k, int kp) {
+  constexpr int BK = 32;
   constexpr int WN = BN / 2, NI = WN / 32, MI = 2;
   constexpr int D_ROWB = BM * 2;             // 256-byte D tile rows
   constexpr int W_ROWB = BN * 2;             // W2 tile rows
-  constexpr int D_BYTES = BK * D_ROWB;       // 16 KB
+  constexpr int D_BYTES = BK * D_ROWB;       // 8 KB
   constexpr int STAGE = D_BYTES + BK * W_ROWB;
   constexpr int D_INS = D_BYTES / 1024 / 4;  // DMA instructions per wave per stage
   constexpr int W_INS = BK * W_ROWB / 1024 / 4;
