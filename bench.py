@@ -84,9 +84,6 @@ def kernel_work(name, w, reident=False, fp8=False, fp8_w2=False):
         return 8.0 * n * kk * HEAD_DIM * H, "mfma"
     if name == "sparse_step_fused":
         return 2.0 * n * k * d + 4.0 * n * kk * HEAD_DIM * H, "mfma"
-    if name == "sparse_step_whole":
-        # the whole step: both MLP products and the attention delta
-        return 4.0 * n * k * d + 4.0 * n * kk * HEAD_DIM * H, "mfma"
     if name == "topk_rows":
         # score rows read + index rows written, averaged over the step's
         # launches: the MLP's, and the attention's when it re-identifies
@@ -258,9 +255,6 @@ def main():
     ap.add_argument("--attn-reident", action="store_true",
                     help="attention identifies its keys anew every step (the cache keeps totals; each step swaps "
                          "the chosen keys' previous-step share for this step's)")
-    ap.add_argument("--whole", action="store_true",
-                    help="run each sparse step as one launch (chipmunk_sparse_step_whole: the MLP's "
-                         "identification, both of its products and the attention delta as work items of one grid)")
     ap.add_argument("--graph", action="store_true",
                     help="replay each sparse step as a captured HIP graph in the timed loop (eager launches are "
                          "as fast on this path)")
@@ -319,7 +313,7 @@ def main():
 
     def sparse(t):
         if fused:
-            sparse_step(mlp, att, xs[t], *qkv[t], whole=args.whole)
+            sparse_step(mlp, att, xs[t], *qkv[t])
             return
         if mlp:
             mlp.step(xs[t], refresh=False)
@@ -437,8 +431,7 @@ def main():
                    "tokens": w["n"], "d_model": w["d"], "d_hidden": w["h"], "mlp_keep": w["k"],
                    "heads": w["heads"], "head_dim": HEAD_DIM if w["heads"] else 0, "attn_keep": w["kk"],
                    "row_block": 128, "launch": ("hip graph per step" if args.graph else "eager")
-                   + (("; identification, both MLP products and attention in one kernel" if args.whole
-                       else "; MLP phase 2 and attention share one kernel") if fused else ""),
+                   + ("; MLP phase 2 and attention share one kernel" if fused else ""),
                    "mlp_set": "rescored every step" if args.mlp_rescore else "fixed between refreshes",
                    "attn_set": "re-identified every step" if args.attn_reident else "fixed between refreshes",
                    "mlp_first_product": "fp8 e4m3, per-row power-of-two scales" if args.fp8 else "bf16",

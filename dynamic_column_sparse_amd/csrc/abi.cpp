@@ -106,12 +106,6 @@ size_t sparse_mlp_ws(int64_t n, int32_t k) {
 // fp8 copy of x: [n][d] e4m3 codes, then n scale bytes, rounded up to 16.
 size_t fp8_x_ws(int64_t n, int32_t d) { return ((size_t)n * (size_t)d + (size_t)n + 15) / 16 * 16; }
 bool is_fp8(const chipmunk_mlp* L) { return (L->flags & CHIPMUNK_MLP_FP8) != 0; }
-// Whole-step workspace: the D tiles, then the padded copy of the index rows
-// ([nb][padded_ids(k)] int32).
-size_t whole_step_ws(int64_t n, int32_t k) {
-  if (k <= 0) return 0;
-  return sparse_mlp_ws(n, k) + (size_t)chipmunk::row_blocks(n) * (size_t)chipmunk::padded_ids(k) * sizeof(int32_t);
-}
 // Operands of the fp8 second product, or nullptr.
 const chipmunk::Fp8Cols* fp8_second(const chipmunk_mlp* L, chipmunk::Fp8Cols* buf) {
   if (!(L->flags & CHIPMUNK_MLP_FP8_W2)) return nullptr;
@@ -251,8 +245,7 @@ const char* kernel_name(int kid) {
   static const char* names[K_COUNT] = {"mlp_gemm1_sparse", "mlp_gemm1_dense", "mlp_gemm2_sparse", "mlp_gemm2_dense",
                                        "topk_rows",        "cache_writeback", "attn_stats",       "attn_dense",
                                        "attn_sparse",      "attn_refresh",     "sparse_step_fused",
-                                       "attn_reident",     "quantize_fp8",     "sparse_step_reident_fused",
-                                       "sparse_step_whole"};
+                                       "attn_reident",     "quantize_fp8",     "sparse_step_reident_fused"};
   return (kid >= 0 && kid < K_COUNT) ? names[kid] : "";
 }
 
@@ -330,10 +323,6 @@ extern "C" size_t chipmunk_workspace_bytes(int op, int64_t n, int32_t d, int32_t
       return d > 0 ? sparse_mlp_ws(n, k) + fp8_x_ws(n, d) : 0;
     case CHIPMUNK_OP_DENSE_MLP_FP8:
       return d > 0 ? fp8_x_ws(n, d) : 0;
-    case CHIPMUNK_OP_SPARSE_STEP_WHOLE:
-      return whole_step_ws(n, k);
-    case CHIPMUNK_OP_STEP_SYNC:
-      return (size_t)chipmunk::whole_sync_words(n) * sizeof(uint32_t);
     default:
       return 0;
   }
@@ -578,74 +567,6 @@ extern "C" int chipmunk_sparse_step_reident(const chipmunk_mlp* M, const uint16_
     return hip_status(e, "re-identifying sparse step launch");
   } catch (...) {
     return fail(CHIPMUNK_E_INTERNAL, "internal error in chipmunk_sparse_step_reident");
-  }
-}
-
-
-extern "C" int chipmunk_sparse_step_whole(const chipmunk_mlp* M, const uint16_t* x, int32_t k, int32_t* mlp_idx,
-                                          float* y, void* ws, size_t ws_bytes, uint32_t* sync,
-                                          const chipmunk_attn* A, const uint16_t* q, const uint16_t* kx,
-                                          const uint16_t* v, const int32_t* attn_idx, int32_t kk, float* o,
-                                          void* stream) {
-  try {
-    // (the workspace size is checked below against this entry's own layout)
-    int rc = check_sparse_mlp(M, x, mlp_idx, k, y, nullptr, ws, ws ? SIZE_MAX : 0);
-    if (rc) return rc;
-    if (M->flags != 0)
-      return fail(CHIPMUNK_E_UNSUPPORTED, "chipmunk_sparse_step_whole runs bf16 layers without rescoring (flags 0x%x)",
-                  M->flags);
-    if (!M->score) return fail(CHIPMUNK_E_NULLPTR, "layer score is required (the step identifies its units)");
-    if (M->h > chipmunk::kWholeMaxH)
-      return fail(CHIPMUNK_E_UNSUPPORTED, "chipmunk_sparse_step_whole identifies rows of at most %d scores (h=%d)",
-                  chipmunk::kWholeMaxH, M->h);
-    if ((rc = check_sparse_attn(A, q, kx, v, attn_idx, kk, CHIPMUNK_ATTN_SPARSE, o))) return rc;
-    const size_t need = whole_step_ws(M->n, k);
-    if (k > 0 && (!ws || ws_bytes < need))
-      return fail(CHIPMUNK_E_WORKSPACE, "workspace of %zu bytes required (got %zu)", need, ws ? ws_bytes : (size_t)0);
-    if (ws && !aligned(ws, 16)) return fail(CHIPMUNK_E_ALIGN, "ws must be 16-byte aligned");
-    if (!sync) return fail(CHIPMUNK_E_NULLPTR, "sync is NULL");
-    if (!aligned(sync, 4)) return fail(CHIPMUNK_E_ALIGN, "sync must be 4-byte aligned");
-    const int64_t nb = chipmunk::row_blocks(M->n), nba = chipmunk::row_blocks(A->n);
-    const int64_t groups = 8 * ((nb + 7) / 8 + (A->heads * nba + 7) / 8 + (nb * ((k + 127) / 128) + 7) / 8 +
-                                (nb * (M->d / 128) + 7) / 8);
-    if (groups > kMaxGroups) return fail(CHIPMUNK_E_SHAPE, "the step's grid exceeds %lld workgroups", (long long)kMaxGroups);
-    // Nothing the step writes may share memory with anything else it touches.
-    const size_t toks = (size_t)A->heads * (size_t)A->n, hd = CHIPMUNK_HEAD_DIM;
-    const size_t mk = k > 0 ? (size_t)k : 0, ak = kk > 0 ? (size_t)kk : 0;
-    const size_t unb = (size_t)nb;
-    const Span wr[] = {{y, (size_t)M->n * M->d * 4, "y"},
-                       {M->a_cache, unb * M->h * 128 * 2, "mlp a_cache"},
-                       {ws, k > 0 ? need : 0, "ws"},
-                       {mlp_idx, unb * mk * 4, "mlp idx"},
-                       {sync, (size_t)chipmunk::whole_sync_words(M->n) * 4, "sync"},
-                       {o, toks * hd * 4, "o"}};
-    const Span rd[] = {{x, (size_t)M->n * M->d * 2, "x"},
-                       {M->w1t, (size_t)M->h * M->d * 2, "w1t"},
-                       {M->w2, (size_t)M->h * M->d * 2, "w2"},
-                       {M->b1, M->b1 ? (size_t)M->h * 4 : 0, "b1"},
-                       {M->score, unb * M->h * 4, "mlp score"},
-                       {q, toks * hd * 2, "q"},
-                       {kx, toks * hd * 2, "k"},
-                       {v, toks * hd * 2, "v"},
-                       {attn_idx, (size_t)A->heads * (size_t)nba * ak * 4, "attn idx"},
-                       {A->m, toks * 4, "m"},
-                       {A->num, toks * hd * 4, "num"},
-                       {A->den, toks * 4, "den"}};
-    for (size_t i = 0; i < sizeof wr / sizeof wr[0]; ++i) {
-      for (size_t j = i + 1; j < sizeof wr / sizeof wr[0]; ++j)
-        if (overlap(wr[i], wr[j])) return fail(CHIPMUNK_E_SHAPE, "%s overlaps %s", wr[i].name, wr[j].name);
-      for (const Span& r : rd)
-        if (overlap(wr[i], r)) return fail(CHIPMUNK_E_SHAPE, "%s overlaps %s", wr[i].name, r.name);
-    }
-    int32_t* midx_pad =
-        k > 0 ? reinterpret_cast<int32_t*>(static_cast<unsigned char*>(ws) + sparse_mlp_ws(M->n, k)) : nullptr;
-    hipError_t e = chipmunk::launch_sparse_step_whole(
-        M->score, mlp_idx, midx_pad, x, M->w1t, M->b1, M->a_cache, static_cast<uint16_t*>(ws), M->w2, y, M->n, M->d,
-        M->h, k, q, kx, v, attn_idx, A->m, A->num, A->den, o, A->n, A->heads, kk, A->scale, sync,
-        static_cast<hipStream_t>(stream));
-    return hip_status(e, "whole sparse step launch");
-  } catch (...) {
-    return fail(CHIPMUNK_E_INTERNAL, "internal error in chipmunk_sparse_step_whole");
   }
 }
 

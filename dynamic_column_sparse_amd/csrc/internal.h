@@ -26,7 +26,6 @@ enum KernelId {
   K_ATTN_REIDENT,
   K_QUANTIZE_FP8,
   K_SPARSE_STEP_REIDENT_FUSED,
-  K_SPARSE_STEP_WHOLE,
   K_COUNT
 };
 const char* kernel_name(int kid);
@@ -39,21 +38,6 @@ __host__ __device__ inline int64_t row_blocks(int64_t n) { return (n + kRowBlock
 // Rows per block of the D tiles: k rounded up to the 64-wide reduction chunk
 // (the rows past k are zero, so phase 2 streams whole chunks).
 __host__ __device__ inline int padded_k(int k) { return (k + 63) / 64 * 64; }
-// Row stride of the whole-step kernel's own copy of the MLP index rows: k
-// rounded up to 32 ids, so that every block's row starts a 128-byte line.
-__host__ __device__ inline int padded_ids(int k) { return (k + 31) / 32 * 32; }
-
-// Sync block of the whole-step kernel (32-bit words): exit count, status
-// (sticky; bit 0: a dependency wait gave up), one claim counter per XCD, then
-// per row block an "identified" flag and a "phase-1 tiles done" count.
-constexpr int kSyncExit = 0;
-constexpr int kSyncStatus = 1;
-constexpr int kSyncClaim = 8;     // 8 words
-constexpr int kSyncFlags = 16;    // 2 * nb words
-__host__ __device__ inline int64_t whole_sync_words(int64_t n) { return kSyncFlags + 2 * row_blocks(n); }
-// Longest score row the whole-step kernel identifies (256 threads x 64 keys).
-constexpr int kWholeTopkKeys = 64;
-constexpr int kWholeMaxH = 256 * kWholeTopkKeys;
 
 // fp8 operands of the MLP's first product: e4m3 codes of x [n][d] and W1^T
 // [h][d] with one E8M0 scale byte per row.
@@ -103,8 +87,6 @@ hipError_t launch_attn_reident(const uint16_t* q_prev, const uint16_t* k_prev, c
                                const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* idx,
                                const float* m, float* num, float* den, float* score, float* o, int64_t n, int heads,
                                int kk, float scale, hipStream_t s);
-// Whether phase 1 over `cols` gathered units runs 256-wide tiles (else 128).
-bool mlp_gemm1_wide(int cols);
 // Sparse MLP phase 1, then one kernel with the MLP phase-2 tiles first and the
 // sparse attention units after them (k = 0: attention units only).
 hipError_t launch_sparse_step(const uint16_t* x, const uint16_t* w1t, const float* b1, const int32_t* midx,
@@ -124,16 +106,5 @@ hipError_t launch_sparse_step_reident(const uint16_t* x, const uint16_t* w1t, co
                                       const float* m, float* num, float* den, float* ascore, float* o, int64_t na,
                                       int heads, int kk, float scale, hipStream_t s, const Fp8Rows* f8,
                                       const Fp8Cols* f8w);
-
-// The whole sparse step in one launch: identification of the MLP's index rows
-// (midx [nb][k] and the kernel's padded copy midx_pad [nb][padded_ids(k)]),
-// its phase 1 and phase 2, and the fixed-set sparse attention delta.  sync:
-// whole_sync_words(n) words, zero on entry except the status word, left so.
-hipError_t launch_sparse_step_whole(const float* mscore, int32_t* midx, int32_t* midx_pad, const uint16_t* x,
-                                    const uint16_t* w1t, const float* b1, uint16_t* a_cache, uint16_t* dbuf,
-                                    const uint16_t* w2, float* y, int64_t n, int d, int h, int k, const uint16_t* q,
-                                    const uint16_t* kx, const uint16_t* v, const int32_t* aidx, const float* m,
-                                    const float* num, const float* den, float* o, int64_t na, int heads, int kk,
-                                    float scale, uint32_t* sync, hipStream_t s);
 
 }  // namespace chipmunk

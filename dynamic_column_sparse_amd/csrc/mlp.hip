@@ -10,12 +10,6 @@ namespace chipmunk {
 // phase-1 tiles.
 constexpr int kWideWastePct = MLP_WIDE_WASTE_PCT;
 
-// 256-wide tiles when they waste little of the last tile, else 128-wide.
-bool mlp_gemm1_wide(int cols) {
-  const int t256 = (cols + 255) / 256, t128 = (cols + 127) / 128;
-  return t128 > 1 && (int64_t)t256 * 256 * 100 <= (int64_t)cols * (100 + kWideWastePct);
-}
-
 hipError_t launch_mlp_gemm1(bool dense, const uint16_t* x, const uint16_t* w1t, const float* b1,
                             const int32_t* idx, uint16_t* a_cache, uint16_t* dbuf, uint16_t* a_packed,
                             float* score, int64_t n, int d, int h, int k, hipStream_t s, const Fp8Rows* f8,
@@ -23,8 +17,9 @@ hipError_t launch_mlp_gemm1(bool dense, const uint16_t* x, const uint16_t* w1t, 
   const int nb = (int)row_blocks(n);
   const int cols = dense ? h : k;
   const int kp = padded_k(k);
-  const bool wide = mlp_gemm1_wide(cols);
+  // 256-wide tiles when they waste little of the last tile, else 128-wide.
   const int t256 = (cols + 255) / 256, t128 = (cols + 127) / 128;
+  const bool wide = t128 > 1 && (int64_t)t256 * 256 * 100 <= (int64_t)cols * (100 + kWideWastePct);
   const int kid = dense ? K_MLP_GEMM1_DENSE : K_MLP_GEMM1_SPARSE;
   const void* xa = f8 ? (const void*)f8->x : (const void*)x;
   const void* wa = f8 ? (const void*)f8->w : (const void*)w1t;

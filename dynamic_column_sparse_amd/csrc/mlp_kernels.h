@@ -55,23 +55,18 @@ constexpr int kGroupTiles = MLP_GROUP_TILES;   // column tiles of one row block 
 // (row, 32 consecutive units), stored per 64-unit chunk as [nb][kp/64][128][2]
 // so that the second product streams a chunk's scales with its codes.  D is
 // first rounded to bf16, as the bf16 path stores it.
-// LDS ring of one phase-1 workgroup (three stages of 32-deep bf16 chunks).
-template <int BN>
-struct Gemm1Lds {
-  static constexpr int kRing = 3 * (BM + BN) * 64;
-};
-
-// Body of phase 1 for workgroup `lin` of a grid of xcd_grid(tiles * nb)
-// workgroups; `smem` is the caller's 16-byte aligned LDS ring and `ild` the
-// row stride of idx (k for the caller's [nb][k] index array).
 template <int BN, bool DENSE, bool F8, bool FD>
-__device__ __forceinline__ void gemm1_body(int lin, unsigned char* smem, const void* __restrict__ xv,
-                                           const void* __restrict__ wv, const uint8_t* __restrict__ xs,
-                                           const uint8_t* __restrict__ ws1, const float* __restrict__ b1,
-                                           const int32_t* __restrict__ idx, uint16_t* __restrict__ a_cache,
-                                           uint16_t* __restrict__ dbuf, uint16_t* __restrict__ a_packed,
-                                           float* __restrict__ score, int64_t n, int d, int h, int k, int kp,
-                                           int64_t ild) {
+__global__ __launch_bounds__(256, 2) void mlp_gemm1(const void* __restrict__ xv,
+                                                    const void* __restrict__ wv,
+                                                    const uint8_t* __restrict__ xs,
+                                                    const uint8_t* __restrict__ ws1,
+                                                    const float* __restrict__ b1,
+                                                    const int32_t* __restrict__ idx,
+                                                    uint16_t* __restrict__ a_cache,
+                                                    uint16_t* __restrict__ dbuf,
+                                                    uint16_t* __restrict__ a_packed,
+                                                    float* __restrict__ score, int64_t n, int d, int h, int k,
+                                                    int kp) {
   constexpr int WN = BN / 2;          // columns per wave (2x2 wave grid)
   constexpr int NI = WN / 32;         // 32-wide column subtiles per wave
   constexpr int MI = 2;               // 32-row subtiles per wave (64 rows)
@@ -84,7 +79,7 @@ __device__ __forceinline__ void gemm1_body(int lin, unsigned char* smem, const v
   constexpr int A_BYTES = BM * ROWB;
   constexpr int STAGE = (BM + BN) * ROWB;
 
-  static_assert(NS * STAGE == Gemm1Lds<BN>::kRing, "LDS layout");
+  __shared__ __align__(16) unsigned char smem[NS * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, kept in SGPRs
@@ -92,7 +87,7 @@ __device__ __forceinline__ void gemm1_body(int lin, unsigned char* smem, const v
   const int wm = wave >> 1, wn = wave & 1;
   const int kcols = DENSE ? h : k;
   const int nb = (int)row_blocks(n), ntiles = (kcols + BN - 1) / BN;
-  const int u = xcd_unit(lin, ntiles * nb);
+  const int u = xcd_unit(blockIdx.x, ntiles * nb);
   if (u >= ntiles * nb) return;
   int b, tile;
   grouped_tile(u, nb, ntiles, kGroupTiles, b, tile);
@@ -121,7 +116,7 @@ __device__ __forceinline__ void gemm1_body(int lin, unsigned char* smem, const v
     const int r = (wave * B_INS + i) * RPI + lrow;
     const int p = c0 + r;
     int j = 0;
-    if (p < kcols) j = DENSE ? p : clamp_index(idx[(int64_t)b * ild + p], h);
+    if (p < kcols) j = DENSE ? p : clamp_index(idx[(int64_t)b * k + p], h);
     bsrc[i] = w1t + (int64_t)j * RB + ((pch ^ swz4(r)) << 4);
   }
 
@@ -151,7 +146,7 @@ __device__ __forceinline__ void gemm1_body(int lin, unsigned char* smem, const v
   for (int ni = 0; ni < NI; ++ni) {
     const int p = c0 + wn * WN + ni * 32 + (lane & 31);
     valid[ni] = p < kcols;
-    jcol[ni] = valid[ni] ? (DENSE ? p : clamp_index(idx[(int64_t)b * ild + p], h)) : 0;
+    jcol[ni] = valid[ni] ? (DENSE ? p : clamp_index(idx[(int64_t)b * k + p], h)) : 0;
     bias[ni] = (valid[ni] && b1) ? b1[jcol[ni]] : 0.f;
   }
 
@@ -361,18 +356,6 @@ __device__ __forceinline__ void gemm1_body(int lin, unsigned char* smem, const v
   }
 }
 
-template <int BN, bool DENSE, bool F8, bool FD>
-__global__ __launch_bounds__(256, 2) void mlp_gemm1(const void* __restrict__ xv, const void* __restrict__ wv,
-                                                    const uint8_t* __restrict__ xs, const uint8_t* __restrict__ ws1,
-                                                    const float* __restrict__ b1, const int32_t* __restrict__ idx,
-                                                    uint16_t* __restrict__ a_cache, uint16_t* __restrict__ dbuf,
-                                                    uint16_t* __restrict__ a_packed, float* __restrict__ score,
-                                                    int64_t n, int d, int h, int k, int kp) {
-  __shared__ __align__(16) unsigned char smem[Gemm1Lds<BN>::kRing];
-  gemm1_body<BN, DENSE, F8, FD>(blockIdx.x, smem, xv, wv, xs, ws1, b1, idx, a_cache, dbuf, a_packed, score, n, d, h,
-                                k, kp, k);
-}
-
 // 32-deep chunks: a 72 KB ring, so two workgroups share a CU (with 64-deep
 // chunks and one workgroup per CU the refresh took 7-9% longer).
 template <int BN, bool DENSE>
@@ -570,13 +553,12 @@ struct Gemm2RowsLds {
 };
 
 // Body of the sparse phase 2 for workgroup `lin` of its grid; `smem` (ring,
-// 16-byte aligned) and `sIdx` (8 x 32 ids) are LDS provided by the caller;
-// `ild` is the row stride of idx (k for the caller's [nb][k] index array).
+// 16-byte aligned) and `sIdx` (8 x 32 ids) are LDS provided by the caller.
 template <int BN>
 __device__ __forceinline__ void gemm2_rows_body(int lin, unsigned char* smem, int (*sIdx)[32],
                                                 const uint16_t* __restrict__ dsrc, const uint16_t* __restrict__ w2,
                                                 const int32_t* __restrict__ idx, float* __restrict__ y, int64_t n,
-                                                int d, int h, int k, int kp, int64_t ild) {
+                                                int d, int h, int k, int kp) {
   constexpr int BK = 32, NS = 3;
   constexpr int WN = BN / 4, NI = WN / 32, MI = BM / 32;
   constexpr int D_ROWB = BK * 2;             // 64-byte D rows (4 chunks)
@@ -605,7 +587,7 @@ __device__ __forceinline__ void gemm2_rows_body(int lin, unsigned char* smem, in
   const int64_t r0 = (int64_t)b * BM;
   const int rows = (int)(n - r0 < BM ? n - r0 : BM);
   const uint16_t* dblk = dsrc + (int64_t)b * BM * kp;
-  const int32_t* sidx = idx + (int64_t)b * ild;
+  const int32_t* sidx = idx + (int64_t)b * k;
 
   // D: row (instruction's first row + lane/4), physical chunk lane%4, logical
   // chunk (lane%4) ^ swz4(row).  W2: row (instruction's first row +
@@ -963,7 +945,7 @@ __global__ __launch_bounds__(256, 2) void mlp_gemm2_rows(const uint16_t* __restr
                                                          int64_t n, int d, int h, int k, int kp) {
   __shared__ __align__(16) unsigned char smem[Gemm2RowsLds<BN>::kRing];
   __shared__ __align__(16) int sIdx[8][32];
-  gemm2_rows_body<BN>(blockIdx.x, smem, sIdx, dsrc, w2, idx, y, n, d, h, k, kp, k);
+  gemm2_rows_body<BN>(blockIdx.x, smem, sIdx, dsrc, w2, idx, y, n, d, h, k, kp);
 }
 
 }  // namespace

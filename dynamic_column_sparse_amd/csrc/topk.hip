@@ -8,10 +8,18 @@
 // first `need` keys == T, so the output is ascending.  Rows of up to 16384
 // scores stay in registers (one workgroup of 1024 threads); longer rows are
 // read three times by a 512-thread workgroup (see topk_rows_long).
-#include "topk_kernels.h"
+#include "device_common.h"
+#include "internal.h"
 
 namespace chipmunk {
 namespace {
+
+__device__ __forceinline__ uint32_t score_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0u;  // NaN ranks lowest
+  if (u == 0x80000000u) u = 0u;                     // -0 == +0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
 
 // Rows longer than the register variant holds (attention rows at long sequence
 // lengths), one workgroup of 512 threads per row, three reads of the row:
@@ -240,11 +248,169 @@ __global__ __launch_bounds__(kLongThreads) void topk_rows_long(const float* __re
   }
 }
 
+// Register-resident variant for rows of up to kRegCols scores: THREADS
+// threads (256, 512 or 1024: the smallest that holds the row, so short rows
+// leave no idle lanes and more rows share a CU), thread t holds keys
+// t + THREADS j (j < kRegKeys).
+//   1. Min and max of the row's keys: every key shares their common bit
+//      prefix, so the radix passes start at the first bit where they differ
+//      (positive scores of similar size share sign and exponent bits; starting
+//      at the top would send every key of the first passes to one bin).
+//   2. Radix select over the remaining bits, up to 8 per pass, with one
+//      256-bin histogram per wave (contention only inside a wave).
+//   3. Emit in index order from one ballot pair per (batch j, wave) and a
+//      single 16 x waves prefix table of packed (above, equal) counts.
+constexpr int kRegKeys = 16;
+constexpr int kRegCols = 1024 * kRegKeys;
+
+// Exclusive prefix sum over tab[0..N-1] (N = 64, 128 or 256) in (batch, wave)
+// order, in place; returns the total.  Threads 0..N-1 take part; ends with a
+// barrier.
+template <int N>
+__device__ __forceinline__ uint32_t table_scan(uint32_t* tab, uint32_t* wsum, int tid) {
+  const int lane = tid & 63, wave = tid >> 6;
+  uint32_t v = 0, incl = 0;
+  if (tid < N) {
+    v = tab[tid];
+    incl = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t t = __shfl_up(incl, o);
+      if (lane >= o) incl += t;
+    }
+    if (lane == 63) wsum[wave] = incl;
+  }
+  __syncthreads();
+  uint32_t total = 0;
+#pragma unroll
+  for (int w = 0; w < N / 64; ++w) total += wsum[w];
+  if (tid < N) {
+    for (int w = 0; w < wave; ++w) incl += wsum[w];
+    tab[tid] = incl - v;
+  }
+  __syncthreads();
+  return total;
+}
+
 template <int THREADS>
 __global__ __launch_bounds__(THREADS) void topk_rows_reg(const float* __restrict__ score, int cols, int k,
                                                         int32_t* __restrict__ idx) {
-  __shared__ TopkRegLds<THREADS, kRegKeys> lds;
-  topk_reg_body<THREADS, kRegKeys>((int64_t)blockIdx.x, lds, score, cols, k, idx, nullptr, 0);
+  constexpr int kRegThreads = THREADS;
+  constexpr int kRegWaves = THREADS / 64;
+  __shared__ uint32_t hist[kRegWaves][256];
+  __shared__ uint32_t tab[kRegKeys * kRegWaves];
+  __shared__ uint32_t wsum[4];
+  __shared__ uint32_t red[2][kRegWaves];
+  __shared__ uint32_t sh_prefix, sh_remaining;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t row = blockIdx.x;
+  const float* srow = score + row * (int64_t)cols;
+  int32_t* orow = idx + row * (int64_t)k;
+
+  uint32_t key[kRegKeys];
+  uint32_t kmin = 0xffffffffu, kmax = 0u;
+#pragma unroll
+  for (int j = 0; j < kRegKeys; ++j) {
+    const int i = tid + kRegThreads * j;
+    key[j] = i < cols ? score_key(srow[i]) : 0u;
+    if (i < cols) {
+      kmin = min(kmin, key[j]);
+      kmax = max(kmax, key[j]);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o));
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o));
+  }
+  if (lane == 0) {
+    red[0][wave] = kmin;
+    red[1][wave] = kmax;
+  }
+  __syncthreads();
+  kmin = red[0][0];
+  kmax = red[1][0];
+#pragma unroll
+  for (int w = 1; w < kRegWaves; ++w) {
+    kmin = min(kmin, red[0][w]);
+    kmax = max(kmax, red[1][w]);
+  }
+  // Bits above `hi` are common to every key.
+  int hi = (kmin == kmax) ? -1 : 31 - __clz((int)(kmin ^ kmax));
+  uint32_t prefix = hi >= 31 ? 0u : (kmin & ~((2u << hi) - 1u));
+  if (hi < 0) prefix = kmin;
+  uint32_t remaining = (uint32_t)k;
+  while (hi >= 0) {
+    const int lo = hi >= 7 ? hi - 7 : 0;
+    const uint32_t above = hi >= 31 ? 0u : ~((2u << hi) - 1u);   // bits already fixed
+    for (int i = tid; i < kRegWaves * 256; i += kRegThreads) (&hist[0][0])[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kRegKeys; ++j) {
+      const int i = tid + kRegThreads * j;
+      if (i < cols && (key[j] & above) == prefix) atomicAdd(&hist[wave][(key[j] >> lo) & ((2u << (hi - lo)) - 1u)], 1u);
+    }
+    __syncthreads();
+    // Bin counts summed over the waves, scanned from the top bin down.
+    const int nbins = 2 << (hi - lo);
+    uint32_t hv = 0, incl = 0;
+    if (tid < 256) {
+      const int bin = nbins - 1 - tid;
+      if (bin >= 0) {
+#pragma unroll
+        for (int w = 0; w < kRegWaves; ++w) hv += hist[w][bin];
+      }
+      incl = hv;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t t = __shfl_up(incl, o);
+        if (lane >= o) incl += t;
+      }
+      if (lane == 63) wsum[wave] = incl;
+    }
+    __syncthreads();
+    if (tid < 256) {
+      for (int w = 0; w < wave; ++w) incl += wsum[w];
+      const uint32_t excl = incl - hv;
+      if (tid < nbins && excl < remaining && remaining <= incl) {
+        sh_prefix = prefix | ((uint32_t)(nbins - 1 - tid) << lo);
+        sh_remaining = remaining - excl;
+      }
+    }
+    __syncthreads();
+    prefix = sh_prefix;
+    remaining = sh_remaining;
+    hi = lo - 1;
+  }
+
+  const uint32_t T = prefix, need = remaining;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : ((~0ull) >> (64 - lane));
+  // One scan places every output: index i is taken if its key is above T, or
+  // equal to T with fewer than `need` equal keys before it; its position is
+  // (keys above T before i) + min(keys equal to T before i, need).  Both counts
+  // of each (batch, wave) travel packed in one word (each fits in 16 bits).
+  uint64_t gm[kRegKeys], em[kRegKeys];
+#pragma unroll
+  for (int j = 0; j < kRegKeys; ++j) {
+    const bool valid = tid + kRegThreads * j < cols;
+    gm[j] = __ballot(valid && key[j] > T);
+    em[j] = __ballot(valid && key[j] == T);
+    if (lane == 0) tab[j * kRegWaves + wave] = (uint32_t)__popcll(gm[j]) | ((uint32_t)__popcll(em[j]) << 16);
+  }
+  __syncthreads();
+  table_scan<kRegKeys * kRegWaves>(tab, wsum, tid);
+#pragma unroll
+  for (int j = 0; j < kRegKeys; ++j) {
+    const uint32_t base = tab[j * kRegWaves + wave];
+    const uint32_t gt_before = (base & 0xffffu) + (uint32_t)__popcll(gm[j] & lt_mask);
+    const uint32_t eq_before = (base >> 16) + (uint32_t)__popcll(em[j] & lt_mask);
+    const bool gt = (gm[j] >> lane) & 1ull, eq = (em[j] >> lane) & 1ull;
+    if (gt || (eq && eq_before < need)) {
+      const uint32_t pos = gt_before + (eq_before < need ? eq_before : need);
+      if (pos < (uint32_t)k) orow[pos] = tid + kRegThreads * j;
+    }
+  }
 }
 
 }  // namespace

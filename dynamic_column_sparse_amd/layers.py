@@ -60,13 +60,8 @@ class MLPDelta:
             ws = max(lib.chipmunk_workspace_bytes(lib.OP_SPARSE_MLP_FP8, n, d, h, k),
                      lib.chipmunk_workspace_bytes(lib.OP_DENSE_MLP_FP8, n, d, h, 0))
         else:
-            # (the whole-step entry's workspace holds the sparse delta's and more)
-            ws = max(lib.chipmunk_workspace_bytes(lib.OP_SPARSE_MLP, n, d, h, k),
-                     lib.chipmunk_workspace_bytes(lib.OP_SPARSE_STEP_WHOLE, n, d, h, k))
+            ws = lib.chipmunk_workspace_bytes(lib.OP_SPARSE_MLP, n, d, h, k)
         self.ws = torch.empty(max(ws, 16), dtype=torch.uint8, device=dev)
-        # Sync block of chipmunk_sparse_step_whole: zero once, left zero by every call.
-        self.sync = torch.zeros(lib.chipmunk_workspace_bytes(lib.OP_STEP_SYNC, n, d, h, k) // 4, dtype=torch.int32,
-                                device=dev)
         self.w2_f8 = self.w2_scale = None
         if fp8_w2:
             self.w2_f8 = torch.empty(h, d, dtype=torch.uint8, device=dev)
@@ -156,18 +151,12 @@ class AttnDelta:
             self.sparse(q, k, v, stream=stream)
 
 
-def sparse_step(mlp: MLPDelta, att: AttnDelta, x, q, k, v, stream=None, whole=False):
+def sparse_step(mlp: MLPDelta, att: AttnDelta, x, q, k, v, stream=None):
     """One sparse step of a block whose attention and MLP deltas are independent
     (both read the block's input): the MLP's top-k over its scores (and the
     attention's, when it re-identifies every step), then both deltas through
-    chipmunk_sparse_step (or chipmunk_sparse_step_reident).  whole=True (bf16
-    MLP layers without rescoring, fixed-set attention): identification and both
-    deltas in one launch, chipmunk_sparse_step_whole.  Same results as
+    chipmunk_sparse_step (or chipmunk_sparse_step_reident).  Same results as
     ``mlp.step(x, False)`` followed by ``att.step(q, k, v, False)``."""
-    if whole:
-        lib.chipmunk_sparse_step_whole(mlp.layer, x, mlp.k, mlp.idx, mlp.y, mlp.ws, mlp.sync, att.layer, q, k, v,
-                                       att.idx, att.kk, att.o, stream=stream)
-        return
     mlp.identify(stream)
     if att.reident:
         att.identify(stream)

@@ -24,15 +24,13 @@ MLP_FP8 = 2       # chipmunk_mlp.flags: the first product runs on fp8 operands
 MLP_FP8_W2 = 4    # chipmunk_mlp.flags: the sparse delta's second product runs on fp8 operands
 OP_DENSE_MLP, OP_SPARSE_MLP, OP_TOPK, OP_DENSE_ATTN, OP_SPARSE_ATTN = 0, 1, 2, 3, 4
 OP_DENSE_MLP_FP8, OP_SPARSE_MLP_FP8 = 5, 6
-OP_SPARSE_STEP_WHOLE, OP_STEP_SYNC = 7, 8
-SYNC_STATUS_WORD = 1   # sticky status word of chipmunk_sparse_step_whole's sync block
 
 STATUS = {0: "CHIPMUNK_OK", 1: "CHIPMUNK_E_NULLPTR", 2: "CHIPMUNK_E_SHAPE", 3: "CHIPMUNK_E_UNSUPPORTED",
           4: "CHIPMUNK_E_ALIGN", 5: "CHIPMUNK_E_WORKSPACE", 6: "CHIPMUNK_E_HIP", 7: "CHIPMUNK_E_INTERNAL"}
 
 EXPORTS = ("chipmunk_dense_step", "chipmunk_identify_topk", "chipmunk_sparse_mlp_delta",
            "chipmunk_sparse_attn_delta", "chipmunk_sparse_attn_reident", "chipmunk_sparse_step",
-           "chipmunk_sparse_step_reident", "chipmunk_sparse_step_whole",
+           "chipmunk_sparse_step_reident",
            "chipmunk_cache_writeback", "chipmunk_quantize_fp8",
            "chipmunk_quantize_fp8_cols",
            "chipmunk_workspace_bytes",
@@ -78,8 +76,6 @@ def _load() -> ctypes.CDLL:
                                                  vp, vp, vp, vp, vp, i32, vp, vp]),
         "chipmunk_sparse_step_reident": (ctypes.c_int, [vp, vp, vp, i32, vp, vp, vp, sz,
                                                          vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp]),
-        "chipmunk_sparse_step_whole": (ctypes.c_int, [vp, vp, i32, vp, vp, vp, sz, vp,
-                                                       vp, vp, vp, vp, vp, i32, vp, vp]),
         "chipmunk_cache_writeback": (ctypes.c_int, [vp, vp, vp, i32, vp]),
         "chipmunk_quantize_fp8": (ctypes.c_int, [vp, i64, i32, vp, vp, vp]),
         "chipmunk_quantize_fp8_cols": (ctypes.c_int, [vp, i64, i32, vp, vp, vp]),
@@ -192,14 +188,6 @@ def chipmunk_sparse_step(mlp: MLPLayer, x, mlp_idx, k: int, y, a_new_packed, ws,
     _check(_lib.chipmunk_sparse_step(ctypes.byref(mlp), _ptr(x), _ptr(mlp_idx), k, _ptr(y), _ptr(a_new_packed),
                                      _ptr(ws), nbytes, ctypes.byref(attn), _ptr(q), _ptr(kx), _ptr(v),
                                      _ptr(attn_idx), kk, _ptr(o), _stream(stream)))
-
-
-def chipmunk_sparse_step_whole(mlp: MLPLayer, x, k: int, mlp_idx, y, ws, sync, attn: AttnLayer, q, kx, v,
-                               attn_idx, kk: int, o, stream=None, ws_bytes=None):
-    nbytes = _nbytes(ws, ws_bytes)
-    _check(_lib.chipmunk_sparse_step_whole(ctypes.byref(mlp), _ptr(x), k, _ptr(mlp_idx), _ptr(y), _ptr(ws), nbytes,
-                                           _ptr(sync), ctypes.byref(attn), _ptr(q), _ptr(kx), _ptr(v),
-                                           _ptr(attn_idx), kk, _ptr(o), _stream(stream)))
 
 
 def chipmunk_sparse_step_reident(mlp: MLPLayer, x, mlp_idx, k: int, y, a_new_packed, ws, attn: AttnLayer, q_prev,

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define CHIPMUNK_ABI_VERSION 7
+#define CHIPMUNK_ABI_VERSION 6
 #define CHIPMUNK_ROW_BLOCK 128
 #define CHIPMUNK_HEAD_DIM 128
 
@@ -77,9 +77,7 @@ enum chipmunk_op {
   CHIPMUNK_OP_DENSE_ATTN = 3,
   CHIPMUNK_OP_SPARSE_ATTN = 4,
   CHIPMUNK_OP_DENSE_MLP_FP8 = 5, /* the dense MLP step of a CHIPMUNK_MLP_FP8 layer */
-  CHIPMUNK_OP_SPARSE_MLP_FP8 = 6, /* the sparse MLP delta of a CHIPMUNK_MLP_FP8 layer */
-  CHIPMUNK_OP_SPARSE_STEP_WHOLE = 7, /* the workspace of chipmunk_sparse_step_whole */
-  CHIPMUNK_OP_STEP_SYNC = 8          /* the sync block of chipmunk_sparse_step_whole */
+  CHIPMUNK_OP_SPARSE_MLP_FP8 = 6 /* the sparse MLP delta of a CHIPMUNK_MLP_FP8 layer */
 };
 
 /* One MLP layer: y = gelu(x W1 + b1) W2 + b2, plus its caches.
@@ -295,40 +293,6 @@ int chipmunk_sparse_step_reident(const chipmunk_mlp* mlp, const uint16_t* x, con
                                  const uint16_t* v_prev, const uint16_t* q, const uint16_t* kx, const uint16_t* v,
                                  const int32_t* attn_idx, int32_t kk, float* o, void* stream);
 
-/* One whole sparse step in ONE launch: the MLP's identification
- * (chipmunk_identify_topk of layer->score, nb rows of h scores, k kept, into
- * mlp_idx [nb][k]), then chipmunk_sparse_mlp_delta with those indices and the
- * fused cache writeback, and chipmunk_sparse_attn_delta(mode =
- * CHIPMUNK_ATTN_SPARSE) on `attn`; the same results, bit for bit, as those
- * calls (or chipmunk_identify_topk followed by chipmunk_sparse_step).  The
- * method (Chipmunk post, Activation Deltas section) picks each block's units,
- * recomputes them and writes the cache back; this entry only schedules those
- * steps as work items of one grid, where an item starts
- * once the items it reads have published their output, so the attention
- * units run while the MLP is identified and the chip never drains between
- * the steps.
- *   mlp       bf16 layer (flags 0) with score; h <= 16384
- *   k         kept hidden units per block, 0 <= k <= h (0: attention only,
- *             mlp_idx untouched)
- *   mlp_idx   [nb][k] int32 output (ascending per row)
- *   y, x, q, kx, v, attn_idx, kk, o: as for chipmunk_sparse_step
- *   ws        >= chipmunk_workspace_bytes(CHIPMUNK_OP_SPARSE_STEP_WHOLE, n, d,
- *             h, k) bytes, 16-byte aligned (D tiles, then the kernel's own
- *             copy of the index rows)
- *   sync      >= chipmunk_workspace_bytes(CHIPMUNK_OP_STEP_SYNC, n, d, h, k)
- *             bytes of device memory, 4-byte aligned, caller-owned: zero it
- *             once before the first call; every call leaves it zero again
- *             except word 1, a sticky status (nonzero: a wait between work
- *             items gave up after about a second and the results of that
- *             call are not valid).  Calls that share a sync block, or a
- *             workspace, must not run at the same time.
- * No buffer the call writes (y, a_cache, ws, mlp_idx, sync, o) may overlap
- * another buffer of the call (CHIPMUNK_E_SHAPE).  Other flags: E_UNSUPPORTED. */
-int chipmunk_sparse_step_whole(const chipmunk_mlp* mlp, const uint16_t* x, int32_t k, int32_t* mlp_idx, float* y,
-                               void* ws, size_t ws_bytes, uint32_t* sync, const chipmunk_attn* attn,
-                               const uint16_t* q, const uint16_t* kx, const uint16_t* v, const int32_t* attn_idx,
-                               int32_t kk, float* o, void* stream);
-
 /* Cache writeback (the separate form of the fused writeback above): copy the
  * packed new activations a_new_packed [nb][k][128] into a_cache[b][idx[b][p]]
  * for every block b and position p.  Contiguous 256-byte segments. */
@@ -357,9 +321,7 @@ int chipmunk_quantize_fp8_cols(const uint16_t* src, int64_t rows, int32_t cols, 
  * CHIPMUNK_OP_SPARSE_MLP: nb*kp*128*2 with kp = k rounded up to 64 (the D
  * tiles); CHIPMUNK_OP_SPARSE_MLP_FP8: that plus the fp8 copy of x, n*d codes
  * and n scale bytes rounded up to 16; CHIPMUNK_OP_DENSE_MLP_FP8: the fp8 copy
- * of x alone; CHIPMUNK_OP_SPARSE_STEP_WHOLE: the D tiles plus nb*k32*4 with
- * k32 = k rounded up to 32 (0 when k = 0); CHIPMUNK_OP_STEP_SYNC: (16 + 2*nb)*4;
- * the others: 0. */
+ * of x alone; the others: 0. */
 size_t chipmunk_workspace_bytes(int op, int64_t n, int32_t d, int32_t h, int32_t k);
 
 /* Thread-local text of the last failure on this thread ("" if none). */

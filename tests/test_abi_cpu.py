@@ -28,7 +28,7 @@ def test_header_declares_the_entry_points():
     decl = _declared()
     for name in ("chipmunk_dense_step", "chipmunk_identify_topk", "chipmunk_sparse_mlp_delta",
                  "chipmunk_sparse_attn_delta", "chipmunk_cache_writeback", "chipmunk_sparse_step",
-                 "chipmunk_sparse_attn_reident", "chipmunk_sparse_step_reident", "chipmunk_sparse_step_whole"):
+                 "chipmunk_sparse_attn_reident", "chipmunk_sparse_step_reident"):
         assert name in decl
 
 
@@ -42,16 +42,10 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_names_workspace(L):
-    assert L.chipmunk_abi_version() == 7
+    assert L.chipmunk_abi_version() == 6
     names = L.kernel_names()
     assert "mlp_gemm1_sparse" in names and "attn_sparse" in names and "topk_rows" in names
-    assert "attn_reident" in names and "sparse_step_whole" in names
-    # whole step: D tiles, then the index rows padded to 32 ids; sync: 16 words + 2 per row block
-    assert L.chipmunk_workspace_bytes(L.OP_SPARSE_STEP_WHOLE, 4352, 3072, 12288, 3686) == \
-        34 * 3712 * 128 * 2 + 34 * 3712 * 4
-    assert L.chipmunk_workspace_bytes(L.OP_SPARSE_STEP_WHOLE, 300, 256, 640, 200) == 3 * 256 * 128 * 2 + 3 * 224 * 4
-    assert L.chipmunk_workspace_bytes(L.OP_SPARSE_STEP_WHOLE, 300, 256, 640, 0) == 0
-    assert L.chipmunk_workspace_bytes(L.OP_STEP_SYNC, 118800, 3072, 12288, 860) == (16 + 2 * 929) * 4
+    assert "attn_reident" in names
     assert L.chipmunk_workspace_bytes(L.OP_SPARSE_MLP, 4352, 3072, 12288, 3686) == 34 * 3712 * 128 * 2
     assert L.chipmunk_workspace_bytes(L.OP_SPARSE_MLP, 300, 128, 640, 0) == 0
     assert L.chipmunk_workspace_bytes(L.OP_DENSE_MLP, 300, 128, 640, 200) == 0
@@ -252,37 +246,6 @@ def test_reident_step_checks(L):
     assert call(ascore=base["ws"] + 64) == 2      # the attention scores inside the MLP workspace
     assert call(o=base["num"]) == 2               # two attention outputs on one buffer
     assert call(qp=base["a_cache"]) == 2          # the MLP writes what the attention reads
-
-
-def test_whole_step_checks(L):
-    base = {name: FAKE + i * (1 << 32) for i, name in enumerate(
-        ("w1t", "w2", "a_cache", "score", "x", "midx", "y", "ws", "sync", "m", "num", "den", "ascore", "q", "k",
-         "v", "aidx", "o"))}
-
-    def call(k=200, kk=100, h=640, flags=0, ws_bytes=1 << 30, **over):
-        a = {**base, **over}
-        lay = L.mlp_layer(300, 256, h, a["w1t"], a["w2"], a["a_cache"], a["score"], flags=flags,
-                          w1t_f8=FAKE, w1t_scale=FAKE, w2_f8=FAKE, w2_scale=FAKE)
-        att = L.attn_layer(300, 2, a["m"], a["num"], a["den"], a["ascore"])
-        return _code(L, L.chipmunk_sparse_step_whole, lay, a["x"], k, a["midx"], a["y"], a["ws"], a["sync"], att,
-                     a["q"], a["k"], a["v"], a["aidx"], kk, a["o"], stream=0, ws_bytes=ws_bytes)
-
-    assert call(k=641) == 2 and call(kk=301) == 2 and call(x=None) == 1 and call(o=None) == 1
-    assert call(midx=None) == 1                   # the identified rows are an output
-    assert call(score=None) == 1                  # identification reads the layer's scores
-    assert call(sync=None) == 1
-    assert call(sync=base["sync"] + 2) == 4
-    for flags in (1, 2, 4):                       # rescoring and fp8 layers take the other entries
-        assert call(flags=flags) == 3
-    assert call(h=16384 + 64, k=200) == 3         # identification rows of at most 16384 scores
-    need = L.chipmunk_workspace_bytes(L.OP_SPARSE_STEP_WHOLE, 300, 256, 640, 200)
-    assert call(ws_bytes=need - 4) == 5
-    assert call(ws=None) == 5
-    assert call(midx=base["y"] + 64) == 2         # the index output over y
-    assert "overlaps" in L.chipmunk_last_error()
-    assert call(sync=base["ws"] + 256) == 2       # the sync block inside the workspace
-    assert call(midx=base["score"]) == 2          # the index output over the scores it reads
-    assert call(o=base["num"]) == 2               # the attention output over its cache
 
 
 def test_timer_api_without_launches(L):
