@@ -250,16 +250,22 @@ __global__ __launch_bounds__(kLongThreads) void topk_rows_long(const float* __re
 
 // Register-resident variant for rows of up to kRegCols scores: THREADS
 // threads (256, 512 or 1024: the smallest that holds the row, so short rows
-// leave no idle lanes and more rows share a CU), thread t holds keys
-// t + THREADS j (j < kRegKeys).
+// leave no idle lanes and more rows share a CU), each holding kRegKeys keys.
+// Scalar layout: thread t holds keys t + THREADS j (j < kRegKeys).  VEC layout
+// (rows of a multiple of 4 scores, 16-byte aligned): key j of thread t is
+// score 4 (t + THREADS (j / 4)) + j % 4, read as one 16-byte load per group of
+// four (a quarter of the load instructions).
 //   1. Min and max of the row's keys: every key shares their common bit
 //      prefix, so the radix passes start at the first bit where they differ
 //      (positive scores of similar size share sign and exponent bits; starting
 //      at the top would send every key of the first passes to one bin).
 //   2. Radix select over the remaining bits, up to 8 per pass, with one
 //      256-bin histogram per wave (contention only inside a wave).
-//   3. Emit in index order from one ballot pair per (batch j, wave) and a
-//      single 16 x waves prefix table of packed (above, equal) counts.
+//   3. Emit in index order from ballots per (batch, wave) and a single
+//      prefix table of packed (above, equal) counts per (batch, wave); a
+//      batch is one key per thread (scalar) or one group of four (VEC), and
+//      either way the batches, then the waves, then the lanes run in index
+//      order.
 constexpr int kRegKeys = 16;
 constexpr int kRegCols = 1024 * kRegKeys;
 
@@ -292,15 +298,16 @@ __device__ __forceinline__ uint32_t table_scan(uint32_t* tab, uint32_t* wsum, in
   return total;
 }
 
-template <int THREADS>
+template <int THREADS, bool VEC>
 __global__ __launch_bounds__(THREADS) void topk_rows_reg(const float* __restrict__ score, int cols, int k,
                                                         int32_t* __restrict__ idx) {
-  constexpr int kRegThreads = THREADS;
-  constexpr int kRegWaves = THREADS / 64;
-  __shared__ uint32_t hist[kRegWaves][256];
-  __shared__ uint32_t tab[kRegKeys * kRegWaves];
+  constexpr int kWaves = THREADS / 64;
+  constexpr int kBatches = VEC ? kRegKeys / 4 : kRegKeys;   // prefix-table rows
+  constexpr int kPer = VEC ? 4 : 1;                          // keys per batch and thread
+  __shared__ uint32_t hist[kWaves][256];
+  __shared__ uint32_t tab[kBatches * kWaves];
   __shared__ uint32_t wsum[4];
-  __shared__ uint32_t red[2][kRegWaves];
+  __shared__ uint32_t red[2][kWaves];
   __shared__ uint32_t sh_prefix, sh_remaining;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -308,15 +315,31 @@ __global__ __launch_bounds__(THREADS) void topk_rows_reg(const float* __restrict
   const float* srow = score + row * (int64_t)cols;
   int32_t* orow = idx + row * (int64_t)k;
 
+  // Key j of this thread is score index i0(j / kPer) + j % kPer, valid when
+  // its batch is inside the row (VEC: cols % 4 == 0, so a group is whole).
+  auto i0 = [&](int bt) __attribute__((always_inline)) { return kPer * (tid + THREADS * bt); };
   uint32_t key[kRegKeys];
+  bool ok[kBatches];
   uint32_t kmin = 0xffffffffu, kmax = 0u;
 #pragma unroll
-  for (int j = 0; j < kRegKeys; ++j) {
-    const int i = tid + kRegThreads * j;
-    key[j] = i < cols ? score_key(srow[i]) : 0u;
-    if (i < cols) {
-      kmin = min(kmin, key[j]);
-      kmax = max(kmax, key[j]);
+  for (int bt = 0; bt < kBatches; ++bt) {
+    ok[bt] = i0(bt) < cols;
+    if constexpr (VEC) {
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (ok[bt]) v = reinterpret_cast<const float4*>(srow)[tid + THREADS * bt];
+      key[4 * bt] = score_key(v.x);
+      key[4 * bt + 1] = score_key(v.y);
+      key[4 * bt + 2] = score_key(v.z);
+      key[4 * bt + 3] = score_key(v.w);
+    } else {
+      key[bt] = ok[bt] ? score_key(srow[i0(bt)]) : 0u;
+    }
+    if (ok[bt]) {
+#pragma unroll
+      for (int e = 0; e < kPer; ++e) {
+        kmin = min(kmin, key[kPer * bt + e]);
+        kmax = max(kmax, key[kPer * bt + e]);
+      }
     }
   }
 #pragma unroll
@@ -332,7 +355,7 @@ __global__ __launch_bounds__(THREADS) void topk_rows_reg(const float* __restrict
   kmin = red[0][0];
   kmax = red[1][0];
 #pragma unroll
-  for (int w = 1; w < kRegWaves; ++w) {
+  for (int w = 1; w < kWaves; ++w) {
     kmin = min(kmin, red[0][w]);
     kmax = max(kmax, red[1][w]);
   }
@@ -344,12 +367,12 @@ __global__ __launch_bounds__(THREADS) void topk_rows_reg(const float* __restrict
   while (hi >= 0) {
     const int lo = hi >= 7 ? hi - 7 : 0;
     const uint32_t above = hi >= 31 ? 0u : ~((2u << hi) - 1u);   // bits already fixed
-    for (int i = tid; i < kRegWaves * 256; i += kRegThreads) (&hist[0][0])[i] = 0u;
+    for (int i = tid; i < kWaves * 256; i += THREADS) (&hist[0][0])[i] = 0u;
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < kRegKeys; ++j) {
-      const int i = tid + kRegThreads * j;
-      if (i < cols && (key[j] & above) == prefix) atomicAdd(&hist[wave][(key[j] >> lo) & ((2u << (hi - lo)) - 1u)], 1u);
+      if (ok[j / kPer] && (key[j] & above) == prefix)
+        atomicAdd(&hist[wave][(key[j] >> lo) & ((2u << (hi - lo)) - 1u)], 1u);
     }
     __syncthreads();
     // Bin counts summed over the waves, scanned from the top bin down.
@@ -359,7 +382,7 @@ __global__ __launch_bounds__(THREADS) void topk_rows_reg(const float* __restrict
       const int bin = nbins - 1 - tid;
       if (bin >= 0) {
 #pragma unroll
-        for (int w = 0; w < kRegWaves; ++w) hv += hist[w][bin];
+        for (int w = 0; w < kWaves; ++w) hv += hist[w][bin];
       }
       incl = hv;
 #pragma unroll
@@ -386,29 +409,49 @@ __global__ __launch_bounds__(THREADS) void topk_rows_reg(const float* __restrict
 
   const uint32_t T = prefix, need = remaining;
   const uint64_t lt_mask = (lane == 0) ? 0ull : ((~0ull) >> (64 - lane));
-  // One scan places every output: index i is taken if its key is above T, or
-  // equal to T with fewer than `need` equal keys before it; its position is
-  // (keys above T before i) + min(keys equal to T before i, need).  Both counts
-  // of each (batch, wave) travel packed in one word (each fits in 16 bits).
+  // Index i is taken if its key is above T, or equal to T with fewer than
+  // `need` equal keys before it; its position is (keys above T before i) +
+  // min(keys equal to T before i, need).  Both counts of each (batch, wave)
+  // travel packed in one word (each fits in 16 bits).
   uint64_t gm[kRegKeys], em[kRegKeys];
 #pragma unroll
-  for (int j = 0; j < kRegKeys; ++j) {
-    const bool valid = tid + kRegThreads * j < cols;
-    gm[j] = __ballot(valid && key[j] > T);
-    em[j] = __ballot(valid && key[j] == T);
-    if (lane == 0) tab[j * kRegWaves + wave] = (uint32_t)__popcll(gm[j]) | ((uint32_t)__popcll(em[j]) << 16);
+  for (int bt = 0; bt < kBatches; ++bt) {
+    uint32_t cg = 0, ce = 0;
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      const int j = kPer * bt + e;
+      gm[j] = __ballot(ok[bt] && key[j] > T);
+      em[j] = __ballot(ok[bt] && key[j] == T);
+      cg += (uint32_t)__popcll(gm[j]);
+      ce += (uint32_t)__popcll(em[j]);
+    }
+    if (lane == 0) tab[bt * kWaves + wave] = cg | (ce << 16);
   }
   __syncthreads();
-  table_scan<kRegKeys * kRegWaves>(tab, wsum, tid);
+  table_scan<kBatches * kWaves>(tab, wsum, tid);
 #pragma unroll
-  for (int j = 0; j < kRegKeys; ++j) {
-    const uint32_t base = tab[j * kRegWaves + wave];
-    const uint32_t gt_before = (base & 0xffffu) + (uint32_t)__popcll(gm[j] & lt_mask);
-    const uint32_t eq_before = (base >> 16) + (uint32_t)__popcll(em[j] & lt_mask);
-    const bool gt = (gm[j] >> lane) & 1ull, eq = (em[j] >> lane) & 1ull;
-    if (gt || (eq && eq_before < need)) {
-      const uint32_t pos = gt_before + (eq_before < need ? eq_before : need);
-      if (pos < (uint32_t)k) orow[pos] = tid + kRegThreads * j;
+  for (int bt = 0; bt < kBatches; ++bt) {
+    const uint32_t base = tab[bt * kWaves + wave];
+    // Keys of this batch before this thread's: those of the lower lanes (all
+    // kPer of each), then this thread's own, one at a time.
+    uint32_t g = base & 0xffffu, q = base >> 16;
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      g += (uint32_t)__popcll(gm[kPer * bt + e] & lt_mask);
+      q += (uint32_t)__popcll(em[kPer * bt + e] & lt_mask);
+    }
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      const int j = kPer * bt + e;
+      const bool gt = (gm[j] >> lane) & 1ull, eq = (em[j] >> lane) & 1ull;
+      if (gt) {
+        const uint32_t pos = g + (q < need ? q : need);
+        if (pos < (uint32_t)k) orow[pos] = i0(bt) + e;
+        ++g;
+      } else if (eq) {
+        if (q < need && g + q < (uint32_t)k) orow[g + q] = i0(bt) + e;
+        ++q;
+      }
     }
   }
 }
@@ -417,16 +460,26 @@ __global__ __launch_bounds__(THREADS) void topk_rows_reg(const float* __restrict
 
 hipError_t launch_topk(const float* score, int64_t rows, int64_t cols, int k, int32_t* idx, hipStream_t s) {
   timing_before(K_TOPK, s);
+  // 16-byte loads when every row starts 16-byte aligned.
+  const bool vec = cols % 4 == 0 && ((uintptr_t)score & 15) == 0;
+#define REG_LAUNCH(T_)                                                                                         \
+  {                                                                                                            \
+    if (vec)                                                                                                   \
+      hipLaunchKernelGGL((topk_rows_reg<T_, true>), dim3((unsigned)rows), dim3(T_), 0, s, score, (int)cols, k, idx); \
+    else                                                                                                       \
+      hipLaunchKernelGGL((topk_rows_reg<T_, false>), dim3((unsigned)rows), dim3(T_), 0, s, score, (int)cols, k, idx); \
+  }
   if (cols <= 256 * kRegKeys)
-    hipLaunchKernelGGL(topk_rows_reg<256>, dim3((unsigned)rows), dim3(256), 0, s, score, (int)cols, k, idx);
+    REG_LAUNCH(256)
   else if (cols <= 512 * kRegKeys)
-    hipLaunchKernelGGL(topk_rows_reg<512>, dim3((unsigned)rows), dim3(512), 0, s, score, (int)cols, k, idx);
+    REG_LAUNCH(512)
   else if (cols <= kRegCols)
-    hipLaunchKernelGGL(topk_rows_reg<1024>, dim3((unsigned)rows), dim3(1024), 0, s, score, (int)cols, k, idx);
-  else if (cols % 4 == 0 && ((uintptr_t)score & 15) == 0)
+    REG_LAUNCH(1024)
+  else if (vec)
     hipLaunchKernelGGL((topk_rows_long<true>), dim3((unsigned)rows), dim3(kLongThreads), 0, s, score, cols, k, idx);
   else
     hipLaunchKernelGGL((topk_rows_long<false>), dim3((unsigned)rows), dim3(kLongThreads), 0, s, score, cols, k, idx);
+#undef REG_LAUNCH
   hipError_t e = hipGetLastError();
   timing_after(K_TOPK, s);
   return e;

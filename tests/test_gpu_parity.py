@@ -27,6 +27,8 @@ def L(gpu_lib):
 @pytest.mark.parametrize("rows,cols,k", [
     (5, 1, 1), (7, 7, 3), (9, 100, 1), (9, 100, 50), (9, 100, 99), (9, 100, 100),
     (4, 4352, 718), (3, 12288, 3686), (3, 12288, 860), (2, 20000, 1400), (1, 118800, 8316),
+    (3, 16384, 5000),    # the longest register-held row (16 keys per thread, 16-byte loads)
+    (3, 16380, 4000),    # 16-byte loads with the last group of the row out of range
     (3, 20001, 777),     # long rows not a multiple of 4: 4-byte loads
     (2, 16385, 16385),   # every column of a long row
     (2, 40000, 1),
@@ -36,6 +38,22 @@ def test_topk_bit_exact(L, kind, rows, cols, k):
     s = syn.scores(7, rows, cols, kind)
     idx = torch.full((rows, k), -1, dtype=torch.int32, device="cuda")
     L.chipmunk_identify_topk(up_f32(s), rows, cols, k, idx)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(idx.cpu().numpy(), oracle.identify_topk(s, k))
+
+
+@pytest.mark.parametrize("rows,cols,k", [(3, 12288, 3686), (9, 100, 50), (4, 4352, 718)])
+def test_topk_unaligned_rows_take_scalar_loads(L, rows, cols, k):
+    # Scores starting 4 bytes past a 16-byte boundary: the register variant
+    # reads them one float at a time; same result.
+    print(f"topk unaligned rows={rows} cols={cols} k={k}", flush=True)
+    s = syn.scores(11, rows, cols, "normal")
+    buf = torch.zeros(rows * cols + 4, dtype=torch.float32, device="cuda")
+    view = buf[1:1 + rows * cols]
+    view.copy_(up_f32(s).reshape(-1))
+    assert view.data_ptr() % 16 == 4
+    idx = torch.full((rows, k), -1, dtype=torch.int32, device="cuda")
+    L.chipmunk_identify_topk(view, rows, cols, k, idx)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(idx.cpu().numpy(), oracle.identify_topk(s, k))
 
