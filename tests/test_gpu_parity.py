@@ -32,6 +32,8 @@ def L(gpu_lib):
     (3, 20001, 777),     # long rows not a multiple of 4: 4-byte loads
     (2, 16385, 16385),   # every column of a long row
     (2, 40000, 1),
+    (2, 30000, 15000),   # long rows, both index lists in LDS (two reads)
+    (2, 30000, 19000),   # long rows whose lists overflow LDS (three reads)
 ])
 def test_topk_bit_exact(L, kind, rows, cols, k):
     print(f"topk kind={kind} rows={rows} cols={cols} k={k}", flush=True)
