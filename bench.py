@@ -1,22 +1,33 @@
 #!/usr/bin/env python3
 """Benchmark of the column-sparse delta hot path on one MI355X.
 
-One step = one sparse diffusion step of a FLUX.1-dev-shaped DiT layer: identify
-the top-k MLP hidden units per 128-token block, the sparse MLP delta (gathered
-GEMM1 + GELU + delta + fused cache writeback, gathered GEMM2 into y) and the
-sparse attention delta over the top-k keys of every (head, query block).  The
-layer is taken as a parallel block (attention and MLP both read the block's
-input, as in FLUX's single-stream blocks), so by default the MLP's GEMM2 and
-the attention delta share one kernel grid (--separate: one call each).
+One step = one sparse diffusion step of a DiT block: identify the top-k MLP
+hidden units per 128-token block, the sparse MLP delta (gathered GEMM1 + GELU +
+delta + fused cache writeback, gathered GEMM2 into y) and the sparse attention
+delta over the top-k keys of every (head, query block).  The block is taken as
+a parallel block (attention and MLP both read the block's input), so by default
+the MLP's GEMM2 and the attention delta share one kernel grid (--separate: one
+call each).
+
+Default workload: HunyuanVideo 720x1280x129 (118 800 tokens: 33x45x80 latent
+patches), MLP d 3072 / h 12288 keeping 860 hidden units per block (93% sparse),
+attention 24 heads x 128 keeping 8316 keys per query block (93% sparse).  The
+metric times K sparse steps back to back; then one whole 50-step loop runs with
+its own schedule (MLP refresh every 10 steps; attention refresh at t mod 9 = 0,
+6 of 50) and is timed step by step.  `--workload flux` runs the FLUX.1-dev
+1280x768 shape (4352 tokens, keep 3686 units and 718 keys; 10-step loop with a
+refresh at step 0).
+
 Inputs are seeded synthetic tensors of the real shapes (random-init weights,
-drifting activations), resident in HBM before the timed region.
+drifting activations).  A few distinct diffusion steps of inputs are generated
+and kept in HBM; the loops cycle through them.  Everything is resident before
+a timed region starts.
 
 Prints one JSON line (last line of stdout).  Progress goes to stderr.
 """
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -31,18 +42,41 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak (published)
 PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 matrix peak (published)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E bandwidth (published)
 HEAD_DIM = 128
+RB = 128
 
+# loop: steps of the sampler loop; mlp_every / attn_every: a layer refreshes at
+# the steps t with t % every == 0; inputs: distinct diffusion steps of inputs
+# kept in HBM (loop step t uses input t % inputs); mlp_sample / attn_sample:
+# the oracle sample of cpu_baseline (row blocks; (head, query block) pairs),
+# None = whole units until the time budget is used.
 WORKLOADS = {
-    # FLUX.1-dev at 1280x768: 3840 image + 512 text tokens, d 3072, h 12288;
-    # MLP 70% sparse (keep 3686 of 12288), attention 83.5% sparse (keep 718 of 4352 keys).
-    "flux": dict(n=4352, d=3072, h=12288, k=3686, heads=24, kk=718, steps=10),
+    # HunyuanVideo 720x1280x129: 33x45x80 latent patches, 93% sparse on the
+    # sparse steps; MLP refresh every 10 steps, attention 6 dense of 50.
+    "hunyuan": dict(n=118800, d=3072, h=12288, k=860, heads=24, kk=8316, loop=50, mlp_every=10, attn_every=9,
+                    inputs=10, mlp_sample=32, attn_sample=4),
+    "hunyuan_mlp": dict(n=118800, d=3072, h=12288, k=860, heads=0, kk=0, loop=50, mlp_every=10, attn_every=9,
+                        inputs=10, mlp_sample=32, attn_sample=0),
+    "hunyuan_attn": dict(n=118800, d=0, h=0, k=0, heads=24, kk=8316, loop=50, mlp_every=10, attn_every=9,
+                         inputs=10, mlp_sample=0, attn_sample=4),
+    # FLUX.1-dev at 1280x768: 3840 image + 512 text tokens; MLP 70% sparse (keep
+    # 3686 of 12288), attention 83.5% sparse (keep 718 of 4352 keys); 10 steps,
+    # refresh at step 0.
+    "flux": dict(n=4352, d=3072, h=12288, k=3686, heads=24, kk=718, loop=10, mlp_every=10, attn_every=10,
+                 inputs=10, mlp_sample=None, attn_sample=None),
     # FLUX.1-dev at 2304x1280: 144x80 = 11520 image + 512 text tokens, the same
     # sparsities (keep 3686 of 12288 hidden units, 16.5% = 1985 of 12032 keys).
-    "flux_2304": dict(n=12032, d=3072, h=12288, k=3686, heads=24, kk=1985, steps=10),
-    "tiny": dict(n=256, d=128, h=512, k=128, heads=0, kk=0, steps=2),
-    # HunyuanVideo 720x1280x129: 33x45x80 latent patches, 93% sparse.
-    "hunyuan_mlp": dict(n=118800, d=3072, h=12288, k=860, heads=0, kk=0, steps=3),
-    "hunyuan_attn": dict(n=118800, d=0, h=0, k=0, heads=24, kk=8316, steps=2),
+    "flux_2304": dict(n=12032, d=3072, h=12288, k=3686, heads=24, kk=1985, loop=10, mlp_every=10, attn_every=10,
+                      inputs=10, mlp_sample=None, attn_sample=None),
+    "tiny": dict(n=256, d=128, h=512, k=128, heads=0, kk=0, loop=2, mlp_every=2, attn_every=2, inputs=2,
+                 mlp_sample=None, attn_sample=0),
+}
+WORKLOAD_NAMES = {
+    "hunyuan": "HunyuanVideo-shaped sparse step (MLP + attention delta)",
+    "hunyuan_mlp": "HunyuanVideo-shaped MLP delta",
+    "hunyuan_attn": "HunyuanVideo-shaped attention delta",
+    "flux": "FLUX.1-dev-shaped sparse step (MLP + attention delta)",
+    "flux_2304": "FLUX.1-dev-shaped sparse step at 2304x1280 (MLP + attention delta)",
+    "tiny": "tiny MLP delta",
 }
 
 
@@ -65,7 +99,7 @@ def kernel_work(name, w, reident=False, fp8=False, fp8_w2=False):
     (bound "mfma": bf16 matrix cores; "mfma_fp8": fp8 matrix cores; a
     ("mfma_mix", fp8 flops) bound: part of the flops on fp8 matrix cores)."""
     n, d, h, k, H, kk = w["n"], w["d"], w["h"], w["k"], w["heads"], w["kk"]
-    nb = (n + 127) // 128
+    nb = (n + RB - 1) // RB
     if name == "mlp_gemm1_sparse":
         return 2.0 * n * d * k, ("mfma_fp8" if fp8 else "mfma")
     if name == "mlp_gemm2_sparse":
@@ -105,12 +139,8 @@ def peak_for(bound, amount):
 
 
 def source_digest():
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "dynamic_column_sparse_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
-    return h.hexdigest()[:16]
+    from dynamic_column_sparse_amd.digest import source_digest as sd
+    return sd()
 
 
 def traffic_for(kernel, workload):
@@ -148,90 +178,136 @@ def copy_calibration(mib=256, reps=5):
                                            "kernel": "elementwise add (torch)"}}), flush=True)
 
 
-def blas_threads():
+def blas_info():
+    """(threads, description) of the BLAS the oracle's NumPy runs on."""
     try:
         from threadpoolctl import threadpool_info
-        th = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
-        if th:
-            return int(max(th))
+        for i in threadpool_info():
+            if i.get("user_api") == "blas":
+                desc = f"{i.get('internal_api')} {i.get('version')} ({i.get('architecture')}, " \
+                       f"{i.get('threading_layer')})"
+                return int(i.get("num_threads", 1)), desc
     except Exception:
         pass
-    return len(os.sched_getaffinity(0))
+    return len(os.sched_getaffinity(0)), "unknown"
 
 
-def cpu_baseline(w, inputs, budget_s, reident=False, fp8=False, fp8_w2=False):
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def pct(vals, q):
+    return float(np.percentile(np.asarray(vals), q)) if len(vals) else None
+
+
+def stats_ms(vals):
+    if not vals:
+        return None
+    return {"count": len(vals), "median": round(pct(vals, 50), 4), "p10": round(pct(vals, 10), 4),
+            "p90": round(pct(vals, 90), 4), "mean": round(float(np.mean(vals)), 4)}
+
+
+def cpu_baseline(w, host, budget_s, reident=False, fp8=False, fp8_w2=False):
     """The CPU oracle, as it stands, on a bounded sample of the same sparse step
     (in the fp8 modes, on the fp8 operands: the weights' fp8 values are taken
-    once, outside the timed part, as the layer takes them at set-up).  MLP:
-    whole 128-row blocks until half the budget is used; attention: whole
-    (head, query block) pairs of the first heads until the rest is used.  The
-    time per block / pair scales to the full step."""
+    once, outside the timed part, as the layer takes them at set-up).  The
+    refresh state of each sampled unit is built outside the timed part; the
+    timed part is the step: identification and the delta (MLP, per row block),
+    or the delta alone (attention, whose identification belongs to the
+    refresh).  MLP: the workload's seeded row blocks, or whole blocks in order
+    until half the budget is used; attention: the workload's seeded (head,
+    query block) pairs, or pairs in order until the rest is used.  The time per
+    block / pair scales to the full step."""
     import oracle
     t_mlp = t_att = 0.0
     n_mlp = n_att = 0
     desc = []
+    n = w["n"]
+    nb = (n + RB - 1) // RB
+    g = np.random.default_rng(1234)
     if w["k"]:
-        n, h, k = w["n"], w["h"], w["k"]
-        w1t = oracle.from_bf16_bits(inputs["w1t"])
-        w2 = oracle.from_bf16_bits(inputs["w2"])
+        h, k = w["h"], w["k"]
+        w1t = oracle.from_bf16_bits(host["w1t"])
+        w2 = oracle.from_bf16_bits(host["w2"])
         if fp8:
             w1t = oracle.fp8_rows(w1t)
         w2_sparse = oracle.fp8_cols(w2) if fp8_w2 else w2
-        nb = (n + 127) // 128
-        x0 = oracle.from_bf16_bits(inputs["x"][0])
-        x1 = oracle.from_bf16_bits(inputs["x"][1])
-        for b in range(nb):
-            r0, r1 = b * 128, min(n, b * 128 + 128)
-            xd = oracle.fp8_rows(x0[r0:r1]) if fp8 else x0[r0:r1]
+        x0 = host["x"][0]
+        x1 = host["x"][1]
+        blocks = list(range(nb)) if not w["mlp_sample"] else sorted(
+            g.choice(nb, size=min(nb, w["mlp_sample"]), replace=False).tolist())
+        for b in blocks:
+            r0, r1 = b * RB, min(n, b * RB + RB)
+            xd = oracle.from_bf16_bits(x0[r0:r1])
+            xd = oracle.fp8_rows(xd) if fp8 else xd
             a0, y0, sc = oracle.mlp_dense(xd, w1t, None, w2, None, np.zeros((r1 - r0, h)))
+            xs1 = oracle.from_bf16_bits(x1[r0:r1])
             t0 = time.perf_counter()
             idx = oracle.identify_topk(sc.astype(np.float32), k)
-            xs1 = oracle.fp8_rows(x1[r0:r1]) if fp8 else x1[r0:r1]
+            xs1 = oracle.fp8_rows(xs1) if fp8 else xs1
             oracle.mlp_sparse(xs1, w1t, None, w2_sparse, a0, y0, idx, d_fp8=fp8_w2)
             t_mlp += time.perf_counter() - t0
             n_mlp += 1
-            if t_mlp > budget_s / 2:
+            if not w["mlp_sample"] and t_mlp > budget_s / 2:
                 break
-        desc.append(f"MLP {n_mlp}/{nb} row blocks")
+        desc.append(f"MLP {n_mlp}/{nb} row blocks" + (" (seeded sample)" if w["mlp_sample"] else ""))
     if w["kk"]:
-        n, H, kk = w["n"], w["heads"], w["kk"]
-        nb = (n + 127) // 128
+        H, kk = w["heads"], w["kk"]
         scale = 1.0 / np.sqrt(HEAD_DIM)
-        done = False
-        for hh in range(H):
-            q0, k0, v0 = (oracle.from_bf16_bits(a[hh]) for a in inputs["qkv"][0])
-            q1, k1, v1 = (oracle.from_bf16_bits(a[hh]) for a in inputs["qkv"][1])
-            for b in range(nb):
-                r0, r1 = b * 128, min(n, b * 128 + 128)
-                m, den, num, o, sc = oracle.attn_dense(q0[r0:r1], k0, v0, scale)
-                if reident:
-                    t0 = time.perf_counter()
-                    idx = oracle.identify_topk(sc.astype(np.float32), kk)
-                    oracle.attn_reident(q0[r0:r1], k0, v0, q1[r0:r1], k1, v1, m, num, den, sc, idx, scale)
-                else:
-                    idx = oracle.identify_topk(sc.astype(np.float32), kk)
-                    nr, dr = oracle.attn_rest(q0[r0:r1], k0, v0, m, idx, scale)
-                    t0 = time.perf_counter()
-                    oracle.attn_sparse(q1[r0:r1], k1, v1, m, nr, dr, idx, scale)
-                t_att += time.perf_counter() - t0
-                n_att += 1
-                if t_att > budget_s / 2:
-                    done = True
-                    break
-            if done:
+        if w["attn_sample"]:
+            side = int(round(np.sqrt(w["attn_sample"])))
+            heads = sorted(g.choice(H, size=side, replace=False).tolist())
+            qblocks = sorted(g.choice(nb, size=side, replace=False).tolist())
+            pairs = [(hh, b) for hh in heads for b in qblocks]
+        else:
+            pairs = [(hh, b) for hh in range(H) for b in range(nb)]
+        cur = None
+        for hh, b in pairs:
+            if cur != hh:
+                k0, v0 = (oracle.from_bf16_bits(a[hh]) for a in host["qkv"][0][1:])
+                k1, v1 = (oracle.from_bf16_bits(a[hh]) for a in host["qkv"][1][1:])
+                cur = hh
+            r0, r1 = b * RB, min(n, b * RB + RB)
+            q0 = oracle.from_bf16_bits(host["qkv"][0][0][hh, r0:r1])
+            q1 = oracle.from_bf16_bits(host["qkv"][1][0][hh, r0:r1])
+            m, den, num, o, sc = oracle.attn_dense(q0, k0, v0, scale)
+            if reident:
+                t0 = time.perf_counter()
+                idx = oracle.identify_topk(sc.astype(np.float32), kk)
+                oracle.attn_reident(q0, k0, v0, q1, k1, v1, m, num, den, sc, idx, scale)
+            else:
+                idx = oracle.identify_topk(sc.astype(np.float32), kk)
+                nr, dr = oracle.attn_rest(q0, k0, v0, m, idx, scale)
+                t0 = time.perf_counter()
+                oracle.attn_sparse(q1, k1, v1, m, nr, dr, idx, scale)
+            t_att += time.perf_counter() - t0
+            n_att += 1
+            if not w["attn_sample"] and t_att > budget_s / 2:
                 break
-        desc.append(f"attention {n_att}/{H * nb} (head, query block) pairs")
+        desc.append(f"attention {n_att}/{H * nb} (head, query block) pairs"
+                    + (" (seeded 2 heads x 2 query blocks)" if w["attn_sample"] else ""))
     t_full = 0.0
     if n_mlp:
-        t_full += t_mlp / n_mlp * ((w["n"] + 127) // 128)
+        t_full += t_mlp / n_mlp * nb
     if n_att:
-        t_full += t_att / n_att * (w["heads"] * ((w["n"] + 127) // 128))
+        t_full += t_att / n_att * (w["heads"] * nb)
+    extrapolated = (n_mlp and n_mlp < nb) or (n_att and n_att < w["heads"] * nb)
     fl = flops_mlp(w) + flops_attn(w, reident)
-    return {"value": round(fl / t_full / 1e12, 6), "unit": "TFLOP/s", "cores": blas_threads(),
+    threads, blas = blas_info()
+    return {"value": round(fl / t_full / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
             "kind": "oracle",
             "sample": "; ".join(desc) + f" of one sparse step, fp64 NumPy, scaled to the full step "
-                      f"({t_full * 1e3:.0f} ms/step extrapolated; sampled {t_mlp + t_att:.1f} s)",
-            "ms_per_step": round(t_full * 1e3, 3)}
+                      f"({t_full * 1e3:.0f} ms/step{' extrapolated' if extrapolated else ''}; "
+                      f"sampled {t_mlp + t_att:.2f} s)",
+            "ms_per_step": round(t_full * 1e3, 3), "extrapolated": bool(extrapolated),
+            "cpu_model": cpu_model(), "blas": blas}
 
 
 def main():
@@ -239,9 +315,12 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="flux", choices=sorted(WORKLOADS))
-    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
+    ap.add_argument("--workload", default="hunyuan", choices=sorted(WORKLOADS))
+    ap.add_argument("--cpu-budget", type=float, default=12.0,
+                    help="seconds of oracle time for cpu_baseline (workloads without a fixed sample)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-loop", action="store_true", help="skip the whole-loop timing (profiler runs)")
+    ap.add_argument("--inputs", type=int, default=0, help="distinct input steps kept in HBM (0: the workload's)")
     ap.add_argument("--separate", action="store_true",
                     help="run the MLP and attention deltas as separate calls instead of the shared-grid step")
     ap.add_argument("--mlp-rescore", action="store_true",
@@ -278,51 +357,62 @@ def main():
 
     w = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
-    T = w["steps"]
+    T = w["loop"]
+    D = max(2, min(T, args.inputs or w["inputs"]))
+    log(f"library sources {lib.chipmunk_source_digest()}")
 
     def up(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
 
     t0 = time.time()
-    inputs = {}
+    host = {}
     mlp = att = None
-    xs = qkv = []
+    xs, qkv = [], []
     if w["k"]:
-        inputs["w1t"], inputs["w2"] = syn.mlp_weights(0, w["d"], w["h"])
-        inputs["x"] = syn.activation_walk(0, "X", T, w["n"], w["d"])
-        xs = [up(x) for x in inputs["x"]]
-        mlp = MLPDelta(up(inputs["w1t"]), up(inputs["w2"]), w["n"], w["k"], rescore=args.mlp_rescore,
+        host["w1t"], host["w2"] = syn.mlp_weights(0, w["d"], w["h"])
+        mlp = MLPDelta(up(host["w1t"]), up(host["w2"]), w["n"], w["k"], rescore=args.mlp_rescore,
                        fp8=args.fp8, fp8_w2=args.fp8_w2)
+        walk = syn.Walk(0, "X", 1, w["n"], w["d"])
+        host["x"] = []
+        for s in range(D):
+            xb = walk.advance()[0]
+            xs.append(up(xb))
+            if s < 2:
+                host["x"].append(xb)
+        del walk
     if w["kk"]:
-        walks = [syn.heads_walk(0, t, T, w["heads"], w["n"]) for t in "QKV"]
-        inputs["qkv"] = [[walks[i][s] for i in range(3)] for s in range(T)]
-        qkv = [[up(a) for a in step] for step in inputs["qkv"]]
+        walks = [syn.Walk(0, t, w["heads"], w["n"], HEAD_DIM) for t in "QKV"]
+        host["qkv"] = []
+        for s in range(D):
+            st = [wk.advance() for wk in walks]
+            qkv.append([up(a) for a in st])
+            if s < 2:
+                host["qkv"].append(st)
+        del walks
         att = AttnDelta(w["n"], w["heads"], w["kk"], dev, reident=args.attn_reident)
     torch.cuda.synchronize()
-    log(f"inputs ready ({time.time() - t0:.1f} s): workload {args.workload} {w}")
-
-    stream = torch.cuda.current_stream()
-
-    def refresh(t):
-        if mlp:
-            mlp.step(xs[t], refresh=True)
-        if att:
-            att.step(*qkv[t], refresh=True)
+    log(f"inputs ready ({time.time() - t0:.1f} s): workload {args.workload} {w}, {D} distinct input steps")
 
     fused = bool(mlp and att) and not args.separate
 
-    def sparse(t):
-        if fused:
-            sparse_step(mlp, att, xs[t], *qkv[t])
+    def step(t_in, mlp_dense, attn_dense):
+        if fused and not mlp_dense and not attn_dense:
+            sparse_step(mlp, att, xs[t_in], *qkv[t_in])
             return
         if mlp:
-            mlp.step(xs[t], refresh=False)
+            mlp.step(xs[t_in], refresh=mlp_dense)
         if att:
-            att.step(*qkv[t], refresh=False)
+            att.step(*qkv[t_in], refresh=attn_dense)
 
-    refresh(0)
+    def sparse(t_in):
+        step(t_in, False, False)
+
+    def metric_input(i):
+        return 1 + i % (D - 1)
+
+    step(0, True, True)
     for i in range(args.warmup):
-        sparse(1 + i % (T - 1))
+        sparse(metric_input(i))
     torch.cuda.synchronize()
 
     # One HIP graph per step input: the step's kernels replay back to back
@@ -331,7 +421,7 @@ def main():
     graphs = {}
     if args.graph:
         side = torch.cuda.Stream()
-        for t in range(1, T):
+        for t in range(1, D):
             g = torch.cuda.CUDAGraph()
             side.wait_stream(torch.cuda.current_stream())
             with torch.cuda.stream(side):
@@ -341,14 +431,14 @@ def main():
             graphs[t] = g
         torch.cuda.synchronize()
         for i in range(args.warmup):
-            graphs[1 + i % (T - 1)].replay()
+            graphs[metric_input(i)].replay()
         torch.cuda.synchronize()
 
-    def run_step(t):
+    def run_sparse(t_in):
         if graphs:
-            graphs[t].replay()
+            graphs[t_in].replay()
         else:
-            sparse(t)
+            sparse(t_in)
 
     log("warmup done")
 
@@ -356,15 +446,27 @@ def main():
     torch.cuda.synchronize()
     ts = time.perf_counter()
     for i in range(args.steps):
-        run_step(1 + i % (T - 1))
+        run_sparse(metric_input(i))
     torch.cuda.synchronize()
     te = time.perf_counter()
     ms_per_step = (te - ts) * 1e3 / args.steps
+    log(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step")
+
+    # The spread: the same K steps with an event pair around each step.
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for i in range(args.steps):
+        evs[i][0].record(stream)
+        run_sparse(metric_input(i))
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    step_ms = [a.elapsed_time(b) for a, b in evs]
+
     # Per-kernel durations: the same steps again, with HIP events recorded by the
     # library around every launch, on the stream the kernel runs on.
     lib.chipmunk_timing_enable(True)
     for i in range(args.steps):
-        sparse(1 + i % (T - 1))
+        sparse(metric_input(i))
     torch.cuda.synchronize()
     lib.chipmunk_timing_enable(False)
     names = lib.kernel_names()
@@ -373,16 +475,34 @@ def main():
         tot, cnt = lib.chipmunk_timing_read(kid)
         if cnt:
             kern[name] = {"ms_total": tot, "launches": cnt, "avg_us": tot / cnt * 1e3}
-    log(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step")
 
-    # dense refresh step, for the loop total (not part of the sparse-step metric)
-    torch.cuda.synchronize()
-    tr = time.perf_counter()
-    reps = 2
-    for _ in range(reps):
-        refresh(0)
-    torch.cuda.synchronize()
-    refresh_ms = (time.perf_counter() - tr) * 1e3 / reps
+    # The sampler loop as the workload schedules it, timed step by step: a
+    # refresh of each layer where its schedule puts one, sparse steps elsewhere.
+    loop = None
+    if not args.no_loop:
+        torch.cuda.synchronize()
+        levs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(T)]
+        kinds = []
+        tl = time.perf_counter()
+        for t in range(T):
+            md = bool(mlp) and t % w["mlp_every"] == 0
+            ad = bool(att) and t % w["attn_every"] == 0
+            kinds.append("sparse" if not (md or ad) else "dense")
+            levs[t][0].record(stream)
+            step(t % D, md, ad)
+            levs[t][1].record(stream)
+        torch.cuda.synchronize()
+        total_ms = (time.perf_counter() - tl) * 1e3
+        lms = [a.elapsed_time(b) for a, b in levs]
+        sp = [v for v, kd in zip(lms, kinds) if kd == "sparse"]
+        dn = [v for v, kd in zip(lms, kinds) if kd == "dense"]
+        loop = {"steps": T, "total_ms": round(total_ms, 3),
+                "mlp_refresh_at": f"t % {w['mlp_every']} == 0" if mlp else None,
+                "attn_refresh_at": f"t % {w['attn_every']} == 0" if att else None,
+                "steps_with_a_refresh": len(dn), "sparse_steps": len(sp),
+                "sparse_step_ms": stats_ms(sp), "refresh_step_ms": stats_ms(dn),
+                "distinct_inputs": D}
+        log(f"loop of {T} steps: {total_ms:.1f} ms ({len(dn)} with a refresh)")
 
     fl = flops_mlp(w) + flops_attn(w, args.attn_reident)
     tflops = fl / (ms_per_step * 1e-3) / 1e12
@@ -423,14 +543,12 @@ def main():
         "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": ("bf16, fp8 e4m3 in the MLP's " + " and ".join(
             p for p, on in (("first product", args.fp8), ("second product", args.fp8_w2)) if on))
-        if (args.fp8 or args.fp8_w2) else "bf16", "data": "synthetic (seeded Gaussian weights and drifting activations, real shapes)",
-        "config": {"workload": {"flux": "FLUX.1-dev-shaped sparse step (MLP + attention delta)",
-                                "flux_2304": "FLUX.1-dev-shaped sparse step at 2304x1280 (MLP + attention delta)",
-                                "tiny": "tiny MLP delta", "hunyuan_mlp": "HunyuanVideo-shaped MLP delta",
-                                "hunyuan_attn": "HunyuanVideo-shaped attention delta"}[args.workload],
+        if (args.fp8 or args.fp8_w2) else "bf16",
+        "data": "synthetic (seeded Gaussian weights and drifting activations, real shapes)",
+        "config": {"workload": WORKLOAD_NAMES[args.workload],
                    "tokens": w["n"], "d_model": w["d"], "d_hidden": w["h"], "mlp_keep": w["k"],
                    "heads": w["heads"], "head_dim": HEAD_DIM if w["heads"] else 0, "attn_keep": w["kk"],
-                   "row_block": 128, "launch": ("hip graph per step" if args.graph else "eager")
+                   "row_block": RB, "launch": ("hip graph per step" if args.graph else "eager")
                    + ("; MLP phase 2 and attention share one kernel" if fused else ""),
                    "mlp_set": "rescored every step" if args.mlp_rescore else "fixed between refreshes",
                    "attn_set": "re-identified every step" if args.attn_reident else "fixed between refreshes",
@@ -439,19 +557,15 @@ def main():
                    else "bf16"},
         "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "flop_per_step": fl,
+        "step_ms": stats_ms(step_ms),
         "roofline": roof,
         "kernels": table,
-        "refresh_ms": round(refresh_ms, 4),
-        "loop_ms": {"steps": T, "dense": 1, "sparse": T - 1,
-                    "total": round(refresh_ms + (T - 1) * ms_per_step, 4)},
+        "loop": loop,
         "source_digest": source_digest(),
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
-        cb = cpu_baseline(w, {**inputs, "x": inputs.get("x", [None, None])[:2],
-                              "qkv": inputs.get("qkv", [None, None])[:2]}, args.cpu_budget, args.attn_reident,
-                          args.fp8, args.fp8_w2)
-        out["cpu_baseline"] = cb
+        out["cpu_baseline"] = cpu_baseline(w, host, args.cpu_budget, args.attn_reident, args.fp8, args.fp8_w2)
     print(json.dumps(out), flush=True)
 
 

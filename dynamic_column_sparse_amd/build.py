@@ -2,7 +2,8 @@
 
 Each source compiles to an object under ``_build/`` (in parallel), then one
 shared-library link.  Every call rebuilds everything, so the result always
-matches the sources.
+matches the sources; the sources' digest is compiled in
+(``chipmunk_source_digest()``) and checked when the library is loaded.
 """
 from __future__ import annotations
 
@@ -22,6 +23,16 @@ SOURCES = ["abi.cpp", "mlp.hip", "topk.hip", "attn.hip", "writeback.hip", "step.
 ARCH = "gfx950"
 
 
+def _digest() -> str:
+    # Loaded by path so that `python build.py` works without the package import
+    # (which would load the library being rebuilt).
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("_chipmunk_digest", os.path.join(HERE, "digest.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod.source_digest()
+
+
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
@@ -38,9 +49,9 @@ def common_flags() -> list:
     ]
 
 
-def _compile(src: str) -> str:
+def _compile(src: str, digest: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *common_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *common_flags(), f'-DCHIPMUNK_SOURCE_DIGEST="{digest}"', "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".hip"):
         cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -51,8 +62,9 @@ def _compile(src: str) -> str:
 
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
+    digest = _digest()
     with ThreadPoolExecutor(min(len(SOURCES), 8)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+        objs = list(ex.map(lambda src: _compile(src, digest), SOURCES))
     tmp = LIB + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -60,7 +72,7 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"link failed:\n{r.stderr[-6000:]}")
     os.replace(tmp, LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} (sources {digest})")
     return LIB
 
 

@@ -312,6 +312,12 @@ extern "C" const char* chipmunk_kernel_name(int kid) { return chipmunk::kernel_n
 extern "C" const char* chipmunk_last_error(void) { return g_err.c_str(); }
 extern "C" int chipmunk_abi_version(void) { return CHIPMUNK_ABI_VERSION; }
 
+// Set by the build from the digest of the sources it compiled.
+#ifndef CHIPMUNK_SOURCE_DIGEST
+#define CHIPMUNK_SOURCE_DIGEST "unknown"
+#endif
+extern "C" const char* chipmunk_source_digest(void) { return CHIPMUNK_SOURCE_DIGEST; }
+
 extern "C" size_t chipmunk_workspace_bytes(int op, int64_t n, int32_t d, int32_t h, int32_t k) {
   (void)d;
   (void)h;

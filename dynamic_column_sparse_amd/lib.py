@@ -12,9 +12,12 @@ import os
 
 import torch
 
+from .digest import source_digest
+
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libchipmunk.so")
 
+ABI_VERSION = 7
 ROW_BLOCK = 128
 HEAD_DIM = 128
 MLP, ATTN = 0, 1
@@ -34,7 +37,7 @@ EXPORTS = ("chipmunk_dense_step", "chipmunk_identify_topk", "chipmunk_sparse_mlp
            "chipmunk_cache_writeback", "chipmunk_quantize_fp8",
            "chipmunk_quantize_fp8_cols",
            "chipmunk_workspace_bytes",
-           "chipmunk_last_error", "chipmunk_abi_version", "chipmunk_timing_enable", "chipmunk_timing_read",
+           "chipmunk_last_error", "chipmunk_abi_version", "chipmunk_source_digest", "chipmunk_timing_enable", "chipmunk_timing_read",
            "chipmunk_kernel_count", "chipmunk_kernel_name")
 
 
@@ -82,6 +85,7 @@ def _load() -> ctypes.CDLL:
         "chipmunk_workspace_bytes": (sz, [ctypes.c_int, i64, i32, i32, i32]),
         "chipmunk_last_error": (ctypes.c_char_p, []),
         "chipmunk_abi_version": (ctypes.c_int, []),
+        "chipmunk_source_digest": (ctypes.c_char_p, []),
         "chipmunk_timing_enable": (ctypes.c_int, [ctypes.c_int]),
         "chipmunk_timing_read": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_double),
                                                 ctypes.POINTER(ctypes.c_int64)]),
@@ -91,6 +95,15 @@ def _load() -> ctypes.CDLL:
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
         f.restype, f.argtypes = res, args
+    # The library must be the build of the sources beside it: same ABI version,
+    # same source digest.  A stale binary is refused, never run.
+    ver = lib.chipmunk_abi_version()
+    built = (lib.chipmunk_source_digest() or b"").decode()
+    here = source_digest()
+    if ver != ABI_VERSION or built != here:
+        raise ImportError(f"{LIB_PATH} does not match the sources in this tree (ABI {ver}, sources {built}; "
+                          f"expected ABI {ABI_VERSION}, sources {here}); rebuild it with "
+                          "__graft_entry__.build() (python -m dynamic_column_sparse_amd.build)")
     return lib
 
 
@@ -137,6 +150,10 @@ def chipmunk_last_error() -> str:
 
 def chipmunk_abi_version() -> int:
     return _lib.chipmunk_abi_version()
+
+
+def chipmunk_source_digest() -> str:
+    return (_lib.chipmunk_source_digest() or b"").decode()
 
 
 def chipmunk_workspace_bytes(op: int, n: int, d: int, h: int, k: int) -> int:

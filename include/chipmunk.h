@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define CHIPMUNK_ABI_VERSION 6
+#define CHIPMUNK_ABI_VERSION 7
 #define CHIPMUNK_ROW_BLOCK 128
 #define CHIPMUNK_HEAD_DIM 128
 
@@ -329,6 +329,13 @@ const char* chipmunk_last_error(void);
 
 /* CHIPMUNK_ABI_VERSION of the loaded library. */
 int chipmunk_abi_version(void);
+
+/* Digest of the sources the library was built from: the first 16 hex digits
+ * of SHA-256 over every file of the library's source and include folders, as
+ * the package's build step computes it ("unknown" for a build that did not
+ * pass one).  The Python binding refuses a library whose digest differs from
+ * the sources beside it.  Static string, never freed. */
+const char* chipmunk_source_digest(void);
 
 /* Optional per-kernel timer.  While enabled, every kernel the library launches
  * is bracketed by a pair of HIP events on its own stream.  chipmunk_timing_read

@@ -183,6 +183,44 @@ def heads_walk(seed: int, tag: str, steps: int, heads: int, n: int, dim: int = 1
     return out
 
 
+class Walk:
+    """The master walk of one drifting tensor ([heads, n, cols]), advanced one
+    diffusion step at a time: ``advance()`` returns the bf16 bits of the next
+    step.  Same values as ``heads_walk`` / ``activation_walk`` at every step,
+    holding one float32 copy of the walk instead of every step's bits."""
+
+    def __init__(self, seed: int, tag: str, heads: int, n: int, cols: int):
+        self.seed, self.tag, self.heads, self.n, self.cols = seed, TAG[tag], heads, n, cols
+        self.x = np.empty((heads, n, cols), np.float32)
+        self.t = -1
+
+    def advance(self) -> np.ndarray:
+        """bf16 bits [heads, n, cols] of step t + 1 (step 0 on the first call)."""
+        self.t += 1
+        s, n, cols = self.t, self.n, self.cols
+        nb = (n + ROW_BLOCK - 1) // ROW_BLOCK
+        ch = _chunk_blocks(cols)
+        jobs = [(h, b, min(nb, b + ch)) for h in range(self.heads) for b in range(0, nb, ch)]
+        out = np.empty((self.heads, n, cols), np.uint16)
+
+        def one(job):
+            h, b0, b1 = job
+            r0, r1 = b0 * ROW_BLOCK, min(n, b1 * ROW_BLOCK)
+            x = self.x[h, r0:r1]
+            dst = x if s == 0 else np.empty_like(x)
+            for b in range(b0, b1):
+                a, c = _block_rows(n, b)
+                stream(self.seed, self.tag, s, h, b).standard_normal(out=dst[a - r0:c - r0], dtype=np.float32)
+            if s:
+                np.multiply(dst, DRIFT, out=dst)
+                np.add(x, dst, out=x)
+            out[h, r0:r1] = f32_to_bf16_bits(x)
+
+        with ThreadPoolExecutor(_threads()) as ex:
+            list(ex.map(one, jobs))
+        return out
+
+
 def weight(seed: int, tag: str, rows: int, cols: int, fan_in: int) -> np.ndarray:
     """bf16 bits [rows, cols] of N(0,1) * 1/sqrt(fan_in) (standard deviation 1/sqrt(fan_in))."""
     nb = (rows + ROW_BLOCK - 1) // ROW_BLOCK

@@ -57,3 +57,42 @@ def idx_sets_valid(gpu_idx: np.ndarray, ref_idx: np.ndarray, ref_score: np.ndarr
             assert abs(ref_score[r][c] - tau) <= rtol * max(abs(tau), 1e-30), (r, c, ref_score[r][c], tau)
         jac.append(len(a & b) / len(a | b))
     return float(np.mean(jac)) if jac else 1.0
+
+
+def block_sizes(blocks, n: int) -> list:
+    """Row counts of the sampled row blocks (the last block of n may be partial)."""
+    return [min(n, (b + 1) * ROW_BLOCK) - b * ROW_BLOCK for b in blocks]
+
+
+def worst_block_error(g: np.ndarray, ref: np.ndarray, sizes, col_group: int = 0):
+    """Largest relative Frobenius error over the row blocks of stacked rows
+    (``sizes`` rows each, in order) and, with ``col_group``, over every (row
+    block, group of col_group columns) tile of them: one bar per tile, so a
+    wrong tile or a wrong short tail block is not averaged away by the rest.
+    Returns (error, row block position, column group)."""
+    import oracle
+    worst = (0.0, -1, -1)
+    r0 = 0
+    for i, s in enumerate(sizes):
+        gb, rb = g[r0:r0 + s], ref[r0:r0 + s]
+        r0 += s
+        e = oracle.rel_frobenius(gb, rb)
+        if e > worst[0]:
+            worst = (e, i, -1)
+        if col_group:
+            for c in range(0, rb.shape[1], col_group):
+                e = oracle.rel_frobenius(gb[:, c:c + col_group], rb[:, c:c + col_group])
+                if e > worst[0]:
+                    worst = (e, i, c // col_group)
+    return worst
+
+
+def attn_s_only(lib, att, q, k, v, idx=None):
+    """The sparse attention call on a copy of the layer whose rest caches (num,
+    den) are zero: o = num_S / den_S over the chosen keys alone.  The layer's
+    own caches are left as they were."""
+    num, den = torch.zeros_like(att.num), torch.zeros_like(att.den)
+    o = torch.empty_like(att.o)
+    layer = lib.attn_layer(att.n, att.heads, att.m, num, den, att.score, att.scale)
+    lib.chipmunk_sparse_attn_delta(layer, q, k, v, att.idx if idx is None else idx, att.kk, lib.ATTN_SPARSE, o)
+    return o

@@ -6,6 +6,8 @@ import re
 
 import pytest
 
+from dynamic_column_sparse_amd.digest import source_digest
+
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "chipmunk.h")
 LIBSO = os.path.join(ROOT, "dynamic_column_sparse_amd", "libchipmunk.so")
@@ -42,7 +44,8 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_names_workspace(L):
-    assert L.chipmunk_abi_version() == 6
+    assert L.chipmunk_abi_version() == L.ABI_VERSION == 7
+    assert L.chipmunk_source_digest() == source_digest()
     names = L.kernel_names()
     assert "mlp_gemm1_sparse" in names and "attn_sparse" in names and "topk_rows" in names
     assert "attn_reident" in names
@@ -268,3 +271,13 @@ def test_product_path_does_not_import_oracle():
         if f.endswith(".py"):
             text = open(os.path.join(ROOT, "oracle", f)).read()
             assert not re.search(r"^\s*(from|import)\s+(dynamic_column_sparse_amd|synthetic)\b", text, re.M), f
+
+
+def test_binding_refuses_a_library_built_from_other_sources(L, monkeypatch):
+    # The loaded library carries the digest of the sources it was built from;
+    # the binding compares it with the sources in the tree and refuses a stale
+    # build instead of running it.
+    assert L.chipmunk_source_digest() == source_digest()
+    monkeypatch.setattr(L, "source_digest", lambda: "0123456789abcdef")
+    with pytest.raises(ImportError, match="does not match the sources"):
+        L._load()

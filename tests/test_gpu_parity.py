@@ -10,7 +10,8 @@ import torch
 
 import oracle
 import synthetic as syn
-from tests.gpu_helpers import (bf16_values, bits_of, cache_to_rows, idx_sets_valid, up_bf16, up_f32)
+from tests.gpu_helpers import (attn_s_only, bf16_values, bits_of, cache_to_rows, idx_sets_valid, up_bf16, up_f32,
+                               worst_block_error)
 
 pytestmark = pytest.mark.gpu
 TOL = 2e-2
@@ -193,6 +194,11 @@ def _qkv(H, n, step, seed=0):
     (33, 3, 5, SCALE),          # one full 32-key chunk and a 1-key tail
     (1, 1, 1, SCALE),           # a single token
     (300, 2, 100, -0.5 * SCALE),  # negative scale: the row max is the minimum raw score
+    # more than 256 keys: the 8-slot key-id ring wraps, and the steady-state
+    # loop (at least 8 chunks) runs
+    (1000, 2, 300, SCALE),
+    (600, 2, 600, SCALE),       # every key of the layer, 19 chunks (last one partial)
+    (2000, 8, 718, SCALE),      # the FLUX keep count, 8 heads (XCD head mapping)
 ])
 def test_attention_refresh_and_sparse_match_oracle(L, n, H, kk, sc):
     print(f"attention parity n={n} H={H} kk={kk} scale={sc}", flush=True)
@@ -217,20 +223,32 @@ def test_attention_refresh_and_sparse_match_oracle(L, n, H, kk, sc):
         refs.append((m, score))
     # refresh with the oracle's index sets, then a sparse step on drifted inputs
     idx = np.concatenate([oracle.identify_topk(refs[hh][1].astype(np.float32), kk) for hh in range(H)], axis=0)
-    att.refresh_rest(*g0, idx=torch.from_numpy(idx).cuda())
-    att.sparse(*g1, idx=torch.from_numpy(idx).cuda())
+    idx_g = torch.from_numpy(idx).cuda()
+    att.refresh_rest(*g0, idx=idx_g)
+    att.sparse(*g1, idx=idx_g)
+    o_s_g = attn_s_only(L, att, *g1, idx=idx_g).cpu().numpy()
     torch.cuda.synchronize()
     nb = (n + 127) // 128
-    num_g, den_g, o_g = att.num.cpu().numpy(), att.den.cpu().numpy(), att.o.cpu().numpy()
+    sizes = [min(n, (b + 1) * 128) - b * 128 for b in range(nb)]
+    num_r, den_r, o_g = att.num.cpu().numpy(), att.den.cpu().numpy(), att.o.cpu().numpy()
     for hh in range(H):
         q0, k0, v0 = (oracle.from_bf16_bits(a[hh]) for a in b0)
         q1, k1, v1 = (oracle.from_bf16_bits(a[hh]) for a in b1_)
         sidx = idx[hh * nb:(hh + 1) * nb]
-        nr, dr = oracle.attn_rest(q0, k0, v0, refs[hh][0], sidx, sc)
-        assert oracle.rel_frobenius(den_g[hh], dr) < 1e-3
-        assert oracle.rel_frobenius(num_g[hh], nr) < TOL
-        o1 = oracle.attn_sparse(q1, k1, v1, refs[hh][0], nr, dr, sidx, sc)
-        assert oracle.rel_frobenius(o_g[hh], o1) < TOL
+        m = refs[hh][0]
+        _, den, num, _, _ = oracle.attn_dense(q0, k0, v0, sc)
+        nr, dr = oracle.attn_rest(q0, k0, v0, m, sidx, sc)
+        # bars per query block: the rest state, the part REFRESH took out (the
+        # chosen keys alone), the sparse output, and the output over S alone
+        z = np.zeros_like(nr)
+        o1 = oracle.attn_sparse(q1, k1, v1, m, nr, dr, sidx, sc)
+        o_s = oracle.attn_sparse(q1, k1, v1, m, z, np.zeros_like(dr), sidx, sc)
+        for name, g, r, tol in (("den_rest", den_r[hh][:, None], dr[:, None], 1e-3), ("num_rest", num_r[hh], nr, TOL),
+                                ("den_S", (den_g[hh] - den_r[hh])[:, None], (den - dr)[:, None], 1e-3),
+                                ("num_S", num_g[hh] - num_r[hh], num - nr, TOL),
+                                ("o", o_g[hh], o1, TOL), ("o over S alone", o_s_g[hh], o_s, TOL)):
+            e, i, _ = worst_block_error(g, r, sizes)
+            assert e < tol, f"head {hh} block {i}: {name} rel-F {e:.2e}"
 
 
 def test_attention_free_running_and_deterministic(L):

@@ -11,8 +11,10 @@
     the launch configuration the benchmark times: sampled row blocks (MLP) and
     (head, query block) slices (attention), each recomputed on its own (exact,
     as every block depends only on its own rows and the shared weights or
-    keys).  Bars as for the separate calls: rel. Frobenius <= 2e-2 on outputs,
-    1e-3 on the cache.
+    keys).  Bars as for the separate calls: rel. Frobenius <= 2e-2 on y and on
+    its change per step, per sampled row block and per (block, 256 columns)
+    tile; on o per slice and on o over the chosen keys alone; 1e-3 on the
+    cache.
   * Overlapping buffers are refused before anything is launched.
 """
 import numpy as np
@@ -21,7 +23,7 @@ import torch
 
 import oracle
 import synthetic as syn
-from tests.gpu_helpers import up_bf16
+from tests.gpu_helpers import attn_s_only, block_sizes, up_bf16, worst_block_error
 from tests.test_gpu_fullsize import RB, SCALE, TOL, _cache_rows, _rows_of, _sample_blocks
 
 pytestmark = pytest.mark.gpu
@@ -144,15 +146,23 @@ def test_flux_fused_step_against_oracle(gpu_lib, n, kk):
                 nr, dr = oracle.attn_rest(q, kx, vx, m, g_idx, SCALE)
                 state[(hh, b)] = (m, nr, dr, g_idx)
             continue
+        y_prev = mlp.y[rows_t].cpu().numpy()
         sparse_step(mlp, att, x_g, *qkv_g)
+        o_s_only = attn_s_only(gpu_lib, att, *qkv_g)
         torch.cuda.synchronize()
         del qkv_g
         g_idx = mlp.idx[torch.tensor(blocks, device="cuda")].cpu().numpy()
         g_score = mlp.score[torch.tensor(blocks, device="cuda")].cpu().numpy()
         np.testing.assert_array_equal(g_idx, oracle.identify_topk(g_score, k))
+        y_old = y_s
         a_s, y_s = oracle.mlp_sparse(x_s, w1t, None, w2, a_s, y_s, g_idx)
-        e_y = oracle.rel_frobenius(mlp.y[rows_t].cpu().numpy(), y_s)
-        assert e_y < TOL, f"step {t}: y {e_y:.2e}"
+        y_g = mlp.y[rows_t].cpu().numpy()
+        # bars per sampled row block and per (block, 256 columns) tile, on y and
+        # on the step's change of y
+        e_y, i, c = worst_block_error(y_g, y_s, block_sizes(blocks, n), 256)
+        assert e_y < TOL, f"step {t}: y {e_y:.2e} in block {blocks[i]} column group {c}"
+        e_dy, i, c = worst_block_error(y_g - y_prev, y_s - y_old, block_sizes(blocks, n), 256)
+        assert e_dy < TOL, f"step {t}: delta of y {e_dy:.2e} in block {blocks[i]} column group {c}"
         assert oracle.rel_frobenius(_cache_rows(mlp.a_cache, blocks, n), a_s) < 1e-3, f"step {t}: cache"
         for (hh, b) in slices:
             r0, r1 = b * RB, min(n, (b + 1) * RB)
@@ -163,4 +173,8 @@ def test_flux_fused_step_against_oracle(gpu_lib, n, kk):
             o1 = oracle.attn_sparse(q, kx, vx, m, nr, dr, s_idx, SCALE)
             e = oracle.rel_frobenius(att.o[hh, r0:r1].cpu().numpy(), o1)
             assert e < TOL, f"step {t} head {hh} block {b}: o {e:.2e}"
-        print(f"  step {t}: MLP rel-F {e_y:.2e}, attention slices ok", flush=True)
+            o_s = oracle.attn_sparse(q, kx, vx, m, np.zeros_like(nr), np.zeros_like(dr), s_idx, SCALE)
+            e_s = oracle.rel_frobenius(o_s_only[hh, r0:r1].cpu().numpy(), o_s)
+            assert e_s < TOL, f"step {t} head {hh} block {b}: o over S alone {e_s:.2e}"
+        print(f"  step {t}: MLP worst block/tile rel-F y {e_y:.2e}, delta {e_dy:.2e}; attention slices ok",
+              flush=True)

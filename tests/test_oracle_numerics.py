@@ -100,3 +100,57 @@ def test_chunked_generation_matches_per_block_streams():
         np.testing.assert_array_equal(syn.activations(5, "X", t, n, cols), ref[t])
     np.testing.assert_array_equal(syn.activations(5, "X", 2, n, cols, blocks=[11, 3]),
                                   np.concatenate([ref[2][1408:], ref[2][384:512]]))
+
+
+# ------------------------------------------------------ the parity checker ---
+def test_rel_frobenius_hand_values():
+    # ||a - b||_F / ||b||_F, worked by hand.  The reference is the second
+    # argument: swapping the arguments changes the result.
+    from oracle import rel_frobenius
+    b = np.array([[3.0, 0.0], [0.0, 4.0]])              # ||b||_F = 5
+    assert rel_frobenius(b, b) == 0.0
+    assert rel_frobenius(2 * b, b) == 1.0               # ||b|| / ||b||
+    assert rel_frobenius(np.zeros_like(b), b) == 1.0    # a dropped output is a 100% error
+    assert rel_frobenius(b + np.array([[0.0, 0.5], [0.0, 0.0]]), b) == 0.1
+    assert rel_frobenius(b, 2 * b) == 0.5               # ||b|| / ||2b||, not ||b|| / ||b||
+    assert rel_frobenius(np.array([1.0, 2.0]), np.array([1.0, 0.0])) == 2.0
+    # zero reference: the absolute norm of the difference
+    assert rel_frobenius(np.zeros(3), np.zeros(3)) == 0.0
+    assert rel_frobenius(np.array([0.0, 3.0, 4.0]), np.zeros(3)) == 5.0
+
+
+def test_rel_frobenius_matches_linalg_norms():
+    # Against numpy's own norms on random arrays of several ranks, float32
+    # inputs included (the checker works in float64).
+    from oracle import rel_frobenius
+    g = np.random.default_rng(5)
+    for shape in [(7,), (33, 17), (4, 5, 6)]:
+        b = g.standard_normal(shape)
+        a = b + 1e-3 * g.standard_normal(shape)
+        ref = np.sqrt(np.sum((a - b) ** 2)) / np.sqrt(np.sum(b ** 2))
+        assert abs(rel_frobenius(a, b) - ref) <= 1e-12 * ref
+        a32, b32 = a.astype(np.float32), b.astype(np.float32)
+        ref32 = (np.linalg.norm((a32.astype(np.float64) - b32.astype(np.float64)).ravel())
+                 / np.linalg.norm(b32.astype(np.float64).ravel()))
+        assert abs(rel_frobenius(a32, b32) - ref32) <= 1e-12 * ref32
+    # one wrong column of 3072 columns: about 1/sqrt(3072) of the whole, so a
+    # single norm over a tensor dilutes a localized error (the GPU tests also
+    # apply their bars per block and per column group)
+    b = g.standard_normal((128, 3072))
+    a = b.copy()
+    a[:, 5] = 0.0
+    assert 0.015 < rel_frobenius(a, b) < 0.022
+
+
+def test_stepwise_walk_matches_whole_walks():
+    # The step-at-a-time walker gives the same bits as the whole-walk
+    # generators, for several heads, a ragged last block and wide rows.
+    import synthetic as syn
+    w = syn.Walk(3, "K", 2, 300, 128)
+    hw = syn.heads_walk(3, "K", 4, 2, 300)
+    for t in range(4):
+        np.testing.assert_array_equal(w.advance(), hw[t])
+    wx = syn.Walk(5, "X", 1, 1500, 3072)
+    aw = syn.activation_walk(5, "X", 3, 1500, 3072)
+    for t in range(3):
+        np.testing.assert_array_equal(wx.advance()[0], aw[t])
