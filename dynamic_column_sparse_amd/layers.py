@@ -72,6 +72,28 @@ class MLPDelta:
         self.layer = lib.mlp_layer(n, d, h, w1t, w2, self.a_cache, self.score, b1, b2, flags, self.w1t_f8,
                                    self.w1t_scale, self.w2_f8, self.w2_scale)
 
+    STATE = ("a_cache", "score", "y", "idx")
+
+    def state_dict(self) -> dict:
+        """The layer's cached state (activation cache, scores, output cache and
+        the current index sets) as host tensors, for a checkpoint."""
+        return {name: getattr(self, name).detach().cpu() for name in self.STATE}
+
+    def load_state_dict(self, state: dict):
+        """Restore a state_dict() of a layer of the same shape, in place (the C
+        layer keeps pointing at the same buffers)."""
+        for name in self.STATE:
+            dst = getattr(self, name)
+            src = state[name]
+            assert src.shape == dst.shape and src.dtype == dst.dtype, name
+            dst.copy_(src)
+
+    def reset(self):
+        """Back to the state of a new layer: zero caches, so the next dense
+        step scores its activations against zero, as the first one does."""
+        for name in self.STATE:
+            getattr(self, name).zero_()
+
     def dense(self, x: torch.Tensor, stream=None):
         lib.chipmunk_dense_step(lib.MLP, self.layer, x, None, None, self.y, self.ws, stream=stream)
 
@@ -114,6 +136,27 @@ class AttnDelta:
         self.o = torch.zeros(heads, n, lib.HEAD_DIM, **f32)
         self.idx = torch.zeros(heads * self.nb, max(kk, 1), dtype=torch.int32, device=device)
         self.layer = lib.attn_layer(n, heads, self.m, self.num, self.den, self.score, self.scale)
+
+    STATE = ("m", "den", "num", "score", "o", "idx")
+
+    def state_dict(self) -> dict:
+        """The layer's cached state (row max, numerator, denominator, key-mass
+        scores, output and index sets) as host tensors, for a checkpoint.  A
+        re-identifying layer also needs the previous step's q, k, v, which the
+        caller owns."""
+        return {name: getattr(self, name).detach().cpu() for name in self.STATE}
+
+    def load_state_dict(self, state: dict):
+        for name in self.STATE:
+            dst = getattr(self, name)
+            src = state[name]
+            assert src.shape == dst.shape and src.dtype == dst.dtype, name
+            dst.copy_(src)
+
+    def reset(self):
+        for name in self.STATE:
+            getattr(self, name).zero_()
+        self.prev = None
 
     def dense(self, q, k, v, stream=None):
         lib.chipmunk_dense_step(lib.ATTN, self.layer, q, k, v, self.o, stream=stream)

@@ -127,7 +127,8 @@ def _mlp_loop(L, n, d, h, k, steps, dense_every, nsample, seed=0, fp8=False):
         g_idx = lay.idx[bt].cpu().numpy()
         g_score = lay.score[bt].cpu().numpy()
         np.testing.assert_array_equal(g_idx, oracle.identify_topk(g_score, k))
-        jac = idx_sets_valid(g_idx, oracle.identify_topk(sc_s.astype(np.float32), k), sc_s.astype(np.float32))
+        jac = idx_sets_valid(g_idx, oracle.identify_topk(sc_s.astype(np.float32), k), sc_s.astype(np.float32),
+                             gpu_score=g_score)
         y_old = y_s
         a_s, y_s = oracle.mlp_sparse(x_s, w1t, None, w2_sparse, a_s, y_s, g_idx, d_fp8=fp8)
         y_g = lay.y[rows_t].cpu().numpy()
@@ -204,7 +205,8 @@ def _attn_loop(L, n, H, kk, steps, dense_at, slices, seed=0):
                 assert oracle.rel_frobenius(g_score, score) < 1e-3, f"step {t}: score"
                 g_idx = att.idx[hh * nb + b].cpu().numpy()[None]
                 np.testing.assert_array_equal(g_idx, oracle.identify_topk(g_score, kk))
-                jac = idx_sets_valid(g_idx, oracle.identify_topk(score.astype(np.float32), kk), score.astype(np.float32))
+                jac = idx_sets_valid(g_idx, oracle.identify_topk(score.astype(np.float32), kk), score.astype(np.float32),
+                                     gpu_score=g_score)
                 nr, dr = oracle.attn_rest(q, kx, vx, m, g_idx, SCALE)
                 num_g, den_g = att.num[hh, r0:r1].cpu().numpy(), att.den[hh, r0:r1].cpu().numpy()
                 assert oracle.rel_frobenius(num_g, nr) < TOL, f"step {t}: num_rest"
