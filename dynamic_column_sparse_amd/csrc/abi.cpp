@@ -15,6 +15,8 @@
 
 #include "internal.h"
 
+static_assert(CHIPMUNK_NOALLOC_SCRATCH_BYTES == chipmunk::kNoAllocScratchBytes, "scratch array size");
+
 namespace {
 
 thread_local std::string g_err;
@@ -423,6 +425,33 @@ extern "C" int chipmunk_sparse_mlp_delta(const chipmunk_mlp* L, const uint16_t* 
     return hip_status(e, "mlp_gemm2 (sparse) launch");
   } catch (...) {
     return fail(CHIPMUNK_E_INTERNAL, "internal error in chipmunk_sparse_mlp_delta");
+  }
+}
+
+extern "C" int chipmunk_sparse_mlp_delta_noalloc(const chipmunk_mlp* L, const uint16_t* x, const int32_t* idx,
+                                                 int32_t k, float* y, uint16_t* a_new_packed, void* stream) {
+  try {
+    // Every argument is checked before any HIP call, the scratch size against
+    // the library's array; only then is the array's device address taken.
+    int rc = check_mlp(L, false);
+    if (rc) return rc;
+    if (k < 0 || k > L->h) return fail(CHIPMUNK_E_SHAPE, "k must be in [0, h] (k=%d, h=%d)", k, L->h);
+    const size_t need = layer_sparse_ws(L, k);
+    if (need > chipmunk::kNoAllocScratchBytes)
+      return fail(CHIPMUNK_E_WORKSPACE,
+                  "this call needs %zu bytes of scratch, above the %zu-byte array of the allocation-free entry "
+                  "point; call chipmunk_sparse_mlp_delta with a workspace instead",
+                  need, chipmunk::kNoAllocScratchBytes);
+    // A stand-in workspace (aligned, never dereferenced) for the shared checks.
+    void* const stand_in = reinterpret_cast<void*>(static_cast<uintptr_t>(256));
+    if ((rc = check_sparse_mlp(L, x, idx, k, y, a_new_packed, stand_in, chipmunk::kNoAllocScratchBytes))) return rc;
+    if (k == 0) return ok();
+    void* ws = nullptr;
+    hipError_t e = chipmunk::noalloc_scratch(&ws);
+    if (e != hipSuccess) return hip_status(e, "scratch array address");
+    return chipmunk_sparse_mlp_delta(L, x, idx, k, y, a_new_packed, ws, chipmunk::kNoAllocScratchBytes, stream);
+  } catch (...) {
+    return fail(CHIPMUNK_E_INTERNAL, "internal error in chipmunk_sparse_mlp_delta_noalloc");
   }
 }
 

@@ -30,6 +30,13 @@ enum KernelId {
 };
 const char* kernel_name(int kid);
 
+// Size of the library-owned scratch array of the allocation-free entry point
+// (CHIPMUNK_NOALLOC_SCRATCH_BYTES).
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+// Device address of that array on the current device (looked up once per
+// device, then cached).  Allocates nothing.
+hipError_t noalloc_scratch(void** out);
+
 // Timer hooks (no-ops unless chipmunk_timing_enable(1)).
 void timing_before(int kid, hipStream_t s);
 void timing_after(int kid, hipStream_t s);

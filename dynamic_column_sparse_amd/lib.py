@@ -18,6 +18,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libchipmunk.so")
 
 ABI_VERSION = 7
+NOALLOC_SCRATCH_BYTES = 64 << 20   # CHIPMUNK_NOALLOC_SCRATCH_BYTES
 ROW_BLOCK = 128
 HEAD_DIM = 128
 MLP, ATTN = 0, 1
@@ -33,7 +34,7 @@ STATUS = {0: "CHIPMUNK_OK", 1: "CHIPMUNK_E_NULLPTR", 2: "CHIPMUNK_E_SHAPE", 3: "
 
 EXPORTS = ("chipmunk_dense_step", "chipmunk_identify_topk", "chipmunk_sparse_mlp_delta",
            "chipmunk_sparse_attn_delta", "chipmunk_sparse_attn_reident", "chipmunk_sparse_step",
-           "chipmunk_sparse_step_reident",
+           "chipmunk_sparse_step_reident", "chipmunk_sparse_mlp_delta_noalloc",
            "chipmunk_cache_writeback", "chipmunk_quantize_fp8",
            "chipmunk_quantize_fp8_cols",
            "chipmunk_workspace_bytes",
@@ -73,6 +74,7 @@ def _load() -> ctypes.CDLL:
         "chipmunk_dense_step": (ctypes.c_int, [ctypes.c_int, vp, vp, vp, vp, vp, vp, sz, vp]),
         "chipmunk_identify_topk": (ctypes.c_int, [vp, i64, i64, i32, vp, vp, sz, vp]),
         "chipmunk_sparse_mlp_delta": (ctypes.c_int, [vp, vp, vp, i32, vp, vp, vp, sz, vp]),
+        "chipmunk_sparse_mlp_delta_noalloc": (ctypes.c_int, [vp, vp, vp, i32, vp, vp, vp]),
         "chipmunk_sparse_attn_delta": (ctypes.c_int, [vp, vp, vp, vp, vp, i32, ctypes.c_int, vp, vp]),
         "chipmunk_sparse_attn_reident": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp]),
         "chipmunk_sparse_step": (ctypes.c_int, [vp, vp, vp, i32, vp, vp, vp, sz,
@@ -187,6 +189,11 @@ def chipmunk_sparse_mlp_delta(layer: MLPLayer, x, idx, k: int, y, a_new_packed=N
     nbytes = _nbytes(ws, ws_bytes)
     _check(_lib.chipmunk_sparse_mlp_delta(ctypes.byref(layer), _ptr(x), _ptr(idx), k, _ptr(y), _ptr(a_new_packed),
                                           _ptr(ws), nbytes, _stream(stream)))
+
+
+def chipmunk_sparse_mlp_delta_noalloc(layer: MLPLayer, x, idx, k: int, y, a_new_packed=None, stream=None):
+    _check(_lib.chipmunk_sparse_mlp_delta_noalloc(ctypes.byref(layer), _ptr(x), _ptr(idx), k, _ptr(y),
+                                                  _ptr(a_new_packed), _stream(stream)))
 
 
 def chipmunk_sparse_attn_delta(layer: AttnLayer, q, k, v, idx, kk: int, mode: int, o=None, stream=None):

@@ -222,6 +222,24 @@ int chipmunk_sparse_mlp_delta(const chipmunk_mlp* layer, const uint16_t* x, cons
                               int32_t k, float* y, uint16_t* a_new_packed, void* ws, size_t ws_bytes,
                               void* stream);
 
+/* chipmunk_sparse_mlp_delta for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments and results as chipmunk_sparse_mlp_delta (bit
+ * for bit: the same kernels), without ws: the workspace is a scratch array
+ * inside the library, CHIPMUNK_NOALLOC_SCRATCH_BYTES (64 MiB) of device
+ * memory that every GPU the library runs on holds from module load until the
+ * process ends.  Calls whose workspace (chipmunk_workspace_bytes of
+ * CHIPMUNK_OP_SPARSE_MLP, or of CHIPMUNK_OP_SPARSE_MLP_FP8 for an FP8 layer)
+ * exceeds it fail with CHIPMUNK_E_WORKSPACE before anything is enqueued (the
+ * FLUX.1-dev 1280x768 shape, 4352 tokens at k = 3686, needs 32.3 MB).  The
+ * call allocates nothing.  Every call on one GPU shares that GPU's array:
+ * calls that may overlap in time on one GPU (other streams, other threads)
+ * race on it and must be ordered by the caller.  Nothing in the array needs
+ * to start at zero (each call writes every byte it later reads). */
+#define CHIPMUNK_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int chipmunk_sparse_mlp_delta_noalloc(const chipmunk_mlp* layer, const uint16_t* x, const int32_t* idx, int32_t k,
+                                      float* y, uint16_t* a_new_packed, void* stream);
+
 /* Sparse attention delta (Chipmunk post, Activation Deltas section): per head h
  * and query block b with S = idx[h*nb + b] (kk keys), gather K[S], V[S] into
  * on-chip tiles, p = exp(scale q_b K[S]^T - m) with the refresh row max m,

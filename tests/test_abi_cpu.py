@@ -281,3 +281,22 @@ def test_binding_refuses_a_library_built_from_other_sources(L, monkeypatch):
     monkeypatch.setattr(L, "source_digest", lambda: "0123456789abcdef")
     with pytest.raises(ImportError, match="does not match the sources"):
         L._load()
+
+
+def test_noalloc_entry_checks_before_any_hip_call(L):
+    # The allocation-free form of the sparse MLP delta validates every argument,
+    # and its scratch size against the library's 64 MiB array, before touching
+    # the GPU (these calls run without one).
+    f = L.chipmunk_sparse_mlp_delta_noalloc
+    assert L.NOALLOC_SCRATCH_BYTES == 64 << 20
+    # the HunyuanVideo shape needs 929 * 896 * 256 bytes of D tiles: refused
+    big = _mlp(L, n=118800, d=3072, h=12288)
+    assert L.chipmunk_workspace_bytes(L.OP_SPARSE_MLP, 118800, 3072, 12288, 860) > L.NOALLOC_SCRATCH_BYTES
+    assert _code(L, f, big, FAKE, FAKE, 860, FAKE, None, stream=0) == 5
+    assert "allocation-free" in L.chipmunk_last_error()
+    lay = _mlp(L)
+    assert _code(L, f, lay, FAKE, FAKE, 641, FAKE, None, stream=0) == 2       # k > h
+    assert _code(L, f, lay, None, FAKE, 10, FAKE, None, stream=0) == 1        # x NULL
+    assert _code(L, f, lay, FAKE, FAKE, 10, FAKE + 4, None, stream=0) == 4    # y misaligned
+    assert _code(L, f, _mlp(L, a_cache=None), FAKE, FAKE, 10, FAKE, None, stream=0) == 1
+    assert _code(L, f, lay, FAKE, None, 0, FAKE, None, stream=0) == 0         # k = 0: no-op, nothing enqueued
