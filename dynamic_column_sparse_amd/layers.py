@@ -15,6 +15,10 @@ their coefficients, then recompute a chosen subset each step):
              keep totals); each sparse step identifies S from the latest
              scores, then swaps S's previous-step share for this step's and
              rescores S (chipmunk_sparse_attn_reident).
+  cached     (step caching, stacked on the deltas in the post's Results
+             section): nothing is recomputed and nothing is launched; the
+             layer's output buffer keeps the latest computed output and every
+             cache keeps its value.
 """
 from __future__ import annotations
 
@@ -192,6 +196,28 @@ class AttnDelta:
             self.refresh_rest(q, k, v, stream=stream)
         else:
             self.sparse(q, k, v, stream=stream)
+
+
+DENSE, SPARSE, CACHED = "dense", "sparse", "cached"
+
+
+def schedule_step(kind: str, mlp: MLPDelta = None, att: AttnDelta = None, x=None, q=None, k=None, v=None,
+                  fused: bool = True, stream=None):
+    """One step of a sampler loop for a block's MLP and / or attention layer:
+    kind DENSE (refresh), SPARSE (the delta; through the shared-grid call when
+    both layers are given and fused) or CACHED (step caching: nothing runs, the
+    output buffers keep the latest computed outputs)."""
+    if kind == CACHED:
+        return
+    if kind not in (DENSE, SPARSE):
+        raise ValueError(kind)
+    if kind == SPARSE and fused and mlp is not None and att is not None:
+        sparse_step(mlp, att, x, q, k, v, stream=stream)
+        return
+    if mlp is not None:
+        mlp.step(x, refresh=kind == DENSE, stream=stream)
+    if att is not None:
+        att.step(q, k, v, refresh=kind == DENSE, stream=stream)
 
 
 def sparse_step(mlp: MLPDelta, att: AttnDelta, x, q, k, v, stream=None):

@@ -55,6 +55,10 @@ design notes of this repository):
       largest magnitude within 448, rounded to nearest even; the product (dense and
       sparse) takes those values, and everything after it is unchanged.  The fp8
       MLP is mlp_dense / mlp_sparse applied to fp8_rows(x) and fp8_rows(w1t).
+  R16 step caching: a cached step recomputes nothing for the layer -- its output
+      is the output cache as the latest computed step left it, and every cache
+      keeps its value (the delta over an empty set of vectors, for the whole
+      layer).  Which steps are cached is the schedule's choice.
   R15 optional fp8 second product of the sparse delta (with R14): D, rounded to
       bf16 as the bf16 path stores it, becomes e4m3 codes per (row, 32 consecutive
       units of S) block, and W2 per column (output feature); each block and column
@@ -447,6 +451,68 @@ def attn_reident(q_prev, k_prev, v_prev, q, k, v, m, num, den, score, idx, scale
         den[r0:r1] += p_new.sum(axis=1) - p_old.sum(axis=1)
         o[r0:r1] = num[r0:r1] / den[r0:r1, None]
     return o, num, den, score
+
+
+# --------------------------------------------------------------------------- #
+# Step caching (reading R16): schedules of dense, sparse and cached steps
+# --------------------------------------------------------------------------- #
+DENSE, SPARSE, CACHED = "dense", "sparse", "cached"
+
+
+def mlp_schedule(xs, w1t, b1, w2, b2, k: int, schedule):
+    """The MLP over a sampler loop.  schedule[t] is DENSE (mlp_dense, the
+    cache starting at zero), SPARSE (top-k of the latest dense step's scores,
+    then mlp_sparse on xs[t]) or CACHED (nothing is recomputed: the output of
+    step t is the output cache left by the latest computed step, and the
+    activation cache is kept).  The Chipmunk post stacks step caching on the
+    deltas (Results section) without describing it; reading R16 takes a cached
+    step as the delta over the empty set for the whole layer.  Returns the
+    output of every step (list of [n,d])."""
+    n, h = np.asarray(xs[0]).shape[0], np.asarray(w1t).shape[0]
+    a = np.zeros((n, h))
+    y = score = None
+    out = []
+    for t, kind in enumerate(schedule):
+        if kind == DENSE:
+            a, y, score = mlp_dense(xs[t], w1t, b1, w2, b2, a)
+        elif kind == SPARSE:
+            if y is None:
+                raise ValueError("a sparse step needs an earlier dense step")
+            a, y = mlp_sparse(xs[t], w1t, b1, w2, a, y, identify_topk(score.astype(np.float32), k))
+        elif kind == CACHED:
+            if y is None:
+                raise ValueError("a cached step needs an earlier computed step")
+        else:
+            raise ValueError(kind)
+        out.append(y.copy())
+    return out
+
+
+def attn_schedule(qs, ks, vs, scale: float, kk: int, schedule):
+    """One attention head over a sampler loop: DENSE (attn_dense, top-kk of its
+    key-mass scores per query block, the rest state of attn_rest), SPARSE
+    (attn_sparse with the latest refresh's sets and rest state) or CACHED (the
+    output of step t is the latest computed output; nothing is recomputed and
+    the caches keep their values, reading R16).  Returns the output of every
+    step (list of [nq,hd])."""
+    o = m = nr = dr = idx = None
+    out = []
+    for t, kind in enumerate(schedule):
+        if kind == DENSE:
+            m, _, _, o, score = attn_dense(qs[t], ks[t], vs[t], scale)
+            idx = identify_topk(score.astype(np.float32), kk)
+            nr, dr = attn_rest(qs[t], ks[t], vs[t], m, idx, scale)
+        elif kind == SPARSE:
+            if m is None:
+                raise ValueError("a sparse step needs an earlier dense step")
+            o = attn_sparse(qs[t], ks[t], vs[t], m, nr, dr, idx, scale)
+        elif kind == CACHED:
+            if o is None:
+                raise ValueError("a cached step needs an earlier computed step")
+        else:
+            raise ValueError(kind)
+        out.append(o.copy())
+    return out
 
 
 def rel_frobenius(a, b) -> float:
