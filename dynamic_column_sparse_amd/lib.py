@@ -15,7 +15,9 @@ import torch
 from .digest import source_digest
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libchipmunk.so")
+# CHIPMUNK_LIBRARY names another build of the same sources (the host-sanitized
+# build of the test suite); it is held to the same ABI and source-digest check.
+LIB_PATH = os.environ.get("CHIPMUNK_LIBRARY") or os.path.join(_HERE, "libchipmunk.so")
 
 ABI_VERSION = 7
 NOALLOC_SCRATCH_BYTES = 64 << 20   # CHIPMUNK_NOALLOC_SCRATCH_BYTES
