@@ -1,10 +1,12 @@
 #!/usr/bin/env python3
 """Benchmark of the column-sparse delta hot path on one MI355X.
 
-One step = one sparse diffusion step of a DiT block: identify the top-k MLP
-hidden units per 128-token block, the sparse MLP delta (gathered GEMM1 + GELU +
-delta + fused cache writeback, gathered GEMM2 into y) and the sparse attention
-delta over the top-k keys of every (head, query block).  The block is taken as
+One step = one sparse diffusion step of a DiT block: the sparse MLP delta over
+the top-k hidden units of each 128-token block (gathered GEMM1 + GELU + delta +
+fused cache writeback, gathered GEMM2 into y) and the sparse attention delta
+over the top-k keys of every (head, query block).  Both index sets are found at
+the refresh, from the refresh's scores; with --mlp-rescore the MLP's scores
+change every step, and each step identifies its units first.  The block is taken as
 a parallel block (attention and MLP both read the block's input), so by default
 the MLP's GEMM2 and the attention delta share one kernel grid (--separate: one
 call each).
@@ -178,6 +180,58 @@ def copy_calibration(mib=256, reps=5):
                                            "kernel": "elementwise add (torch)"}}), flush=True)
 
 
+def window_sweep(workload, reps=5):
+    """The sparse attention delta of the workload's shape on index sets drawn
+    from the first W keys of each head, for a few W: the same kernel, the same
+    flops and instruction stream, only the span of key rows the gathers touch
+    changes (W keys x 512 bytes of K and V per head).  Prints one JSON line per
+    W and a summary line.  Inputs are seeded Gaussian q, k, v; the index sets
+    are uniform random subsets of [0, W), ascending."""
+    import torch
+    from dynamic_column_sparse_amd.layers import AttnDelta
+    w = WORKLOADS[workload]
+    n, H, kk = w["n"], w["heads"], w["kk"]
+    if not kk:
+        sys.exit(f"--window-sweep needs a workload with attention; {workload} has none")
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0)
+    q, k, v = (torch.randn(H, n, HEAD_DIM, generator=gen, device=dev).to(torch.bfloat16) for _ in range(3))
+    att = AttnDelta(n, H, kk, dev)
+    att.m.fill_(4.0)
+    att.den.fill_(10.0)
+    rows = H * att.nb
+    windows = sorted({min(n, kk * f) for f in (1, 2, 4, 8)} | {n})
+    flops = flops_attn(w)
+    out = []
+    for W in windows:
+        for r0 in range(0, rows, 256):
+            r1 = min(rows, r0 + 256)
+            sc = torch.rand(r1 - r0, W, generator=gen, device=dev)
+            att.idx[r0:r1] = sc.topk(kk, dim=1).indices.sort(dim=1).values.int()
+        del sc
+        for _ in range(2):
+            att.sparse(q, k, v)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            att.sparse(q, k, v)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        gathered = rows * kk * 2 * HEAD_DIM * 2
+        rec = {"window_keys": W, "window_mib_per_head": round(W * 2 * HEAD_DIM * 2 / 2 ** 20, 1),
+               "ms": round(ms, 3), "tflops": round(flops / ms / 1e9, 1),
+               "gathered_gb": round(gathered / 1e9, 2), "gathered_tb_per_s": round(gathered / ms / 1e9, 2),
+               "launches": reps + 2}
+        out.append(rec)
+        print(json.dumps({"window_sweep": rec}), flush=True)
+    print(json.dumps({"window_sweep_summary": {"workload": WORKLOAD_NAMES[workload], "heads": H, "tokens": n, "keys_kept": kk,
+                                               "windows": [r["window_keys"] for r in out],
+                                               "ms": [r["ms"] for r in out]}}), flush=True)
+
+
 def blas_info():
     """(threads, description) of the BLAS the oracle's NumPy runs on."""
     try:
@@ -214,14 +268,14 @@ def stats_ms(vals):
             "p90": round(pct(vals, 90), 4), "mean": round(float(np.mean(vals)), 4)}
 
 
-def cpu_baseline(w, host, budget_s, reident=False, fp8=False, fp8_w2=False):
+def cpu_baseline(w, host, budget_s, reident=False, fp8=False, fp8_w2=False, rescore=False):
     """The CPU oracle, as it stands, on a bounded sample of the same sparse step
     (in the fp8 modes, on the fp8 operands: the weights' fp8 values are taken
     once, outside the timed part, as the layer takes them at set-up).  The
     refresh state of each sampled unit is built outside the timed part; the
-    timed part is the step: identification and the delta (MLP, per row block),
-    or the delta alone (attention, whose identification belongs to the
-    refresh).  MLP: the workload's seeded row blocks, or whole blocks in order
+    timed part is the step: the delta, per MLP row block and per attention
+    (head, query block), whose index sets belong to the refresh (the MLP's
+    identification is timed with the step when it rescores every step).  MLP: the workload's seeded row blocks, or whole blocks in order
     until half the budget is used; attention: the workload's seeded (head,
     query block) pairs, or pairs in order until the rest is used.  A fixed
     sample is timed repeatedly until half the budget is used.  The time per
@@ -250,12 +304,14 @@ def cpu_baseline(w, host, budget_s, reident=False, fp8=False, fp8_w2=False):
             xd = oracle.from_bf16_bits(x0[r0:r1])
             xd = oracle.fp8_rows(xd) if fp8 else xd
             a0, y0, sc = oracle.mlp_dense(xd, w1t, None, w2, None, np.zeros((r1 - r0, h)))
-            return oracle.from_bf16_bits(x1[r0:r1]), a0, y0, sc
+            idx = None if rescore else oracle.identify_topk(sc.astype(np.float32), k)
+            return oracle.from_bf16_bits(x1[r0:r1]), a0, y0, sc, idx
 
         def run(st):
-            xs1, a0, y0, sc = st
+            xs1, a0, y0, sc, idx = st
             t0 = time.perf_counter()
-            idx = oracle.identify_topk(sc.astype(np.float32), k)
+            if rescore:
+                idx = oracle.identify_topk(sc.astype(np.float32), k)
             xs1 = oracle.fp8_rows(xs1) if fp8 else xs1
             oracle.mlp_sparse(xs1, w1t, None, w2_sparse, a0, y0, idx, d_fp8=fp8_w2)
             return time.perf_counter() - t0
@@ -382,6 +438,9 @@ def main():
                          "nothing and keep their outputs); 0 = off")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain copy of known size (for scaling HBM byte counters)")
+    ap.add_argument("--window-sweep", action="store_true",
+                    help="only time the workload's sparse attention delta on index sets drawn from the first W keys "
+                         "of each head, for several W (how the span of gathered rows sets the kernel's time)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
@@ -390,6 +449,9 @@ def main():
 
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.window_sweep:
+        window_sweep(args.workload)
         return
 
     import torch
@@ -616,7 +678,8 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
-        out["cpu_baseline"] = cpu_baseline(w, host, args.cpu_budget, args.attn_reident, args.fp8, args.fp8_w2)
+        out["cpu_baseline"] = cpu_baseline(w, host, args.cpu_budget, args.attn_reident, args.fp8, args.fp8_w2,
+                                          args.mlp_rescore)
     print(json.dumps(out), flush=True)
 
 

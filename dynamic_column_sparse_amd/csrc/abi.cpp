@@ -256,16 +256,24 @@ void timing_before(int kid, hipStream_t s) {
   std::lock_guard<std::mutex> g(g_tmu);
   if (!g_ton) return;
   g_open = take_event();
-  if (g_open) hipEventRecord(g_open, s);
+  // A start event that could not be recorded is dropped (back to the pool):
+  // that launch is then simply not timed.
+  if (g_open && hipEventRecord(g_open, s) != hipSuccess) {
+    g_pool.push_back(g_open);
+    g_open = nullptr;
+  }
 }
 
 void timing_after(int kid, hipStream_t s) {
   std::lock_guard<std::mutex> g(g_tmu);
   if (!g_ton || !g_open) return;
   hipEvent_t e = take_event();
-  if (!e) return;
-  hipEventRecord(e, s);
-  g_recs.push_back({kid, g_open, e});
+  if (e && hipEventRecord(e, s) == hipSuccess) {
+    g_recs.push_back({kid, g_open, e});
+  } else {
+    if (e) g_pool.push_back(e);
+    g_pool.push_back(g_open);
+  }
   g_open = nullptr;
 }
 }  // namespace chipmunk
@@ -274,12 +282,24 @@ extern "C" int chipmunk_timing_enable(int on) {
   using namespace chipmunk;
   std::lock_guard<std::mutex> g(g_tmu);
   if (on) {
+    // Records of the previous window are discarded; their events return to the
+    // pool once complete.  A failed wait leaves the events out of the pool
+    // (they may still be pending) and is reported.
+    hipError_t first = hipSuccess;
     for (auto& r : g_recs) {
-      hipEventSynchronize(r.b);
-      g_pool.push_back(r.a);
-      g_pool.push_back(r.b);
+      const hipError_t e = hipEventSynchronize(r.b);
+      if (e == hipSuccess) {
+        g_pool.push_back(r.a);
+        g_pool.push_back(r.b);
+      } else if (first == hipSuccess) {
+        first = e;
+      }
     }
     g_recs.clear();
+    if (first != hipSuccess) {
+      g_ton = false;
+      return hip_status(first, "hipEventSynchronize");
+    }
   }
   g_ton = on != 0;
   return ok();

@@ -6,8 +6,11 @@ Schedule per layer and diffusion step (the Chipmunk post, section "Activation
 Deltas Across Diffusion Steps are Very Sparse": cache the value vectors and
 their coefficients, then recompute a chosen subset each step):
   MLP        refresh: dense step (fills the activation cache, output cache and
-             per-block column scores); sparse: identify top-k from the scores,
-             then the sparse delta with fused cache writeback.
+             per-block column scores), then identify the top-k columns per
+             block; sparse: the sparse delta with fused cache writeback.  The
+             scores change only at a refresh, so the index sets are found once
+             there; with rescore=True the sparse delta updates the scores of
+             the units it recomputed, and each sparse step identifies first.
   attention  refresh: dense step (m, num, den, o, key-mass scores), identify the
              top-k keys per query block, then REFRESH (num, den keep only the
              part outside S); sparse: the sparse delta writes o.
@@ -73,8 +76,11 @@ class MLPDelta:
             lib.chipmunk_quantize_fp8_cols(w2, h, d, self.w2_f8, self.w2_scale)
         flags = ((lib.MLP_RESCORE if rescore else 0) | (lib.MLP_FP8 if fp8 else 0)
                  | (lib.MLP_FP8_W2 if fp8_w2 else 0))
+        self.rescore = rescore
         self.layer = lib.mlp_layer(n, d, h, w1t, w2, self.a_cache, self.score, b1, b2, flags, self.w1t_f8,
                                    self.w1t_scale, self.w2_f8, self.w2_scale)
+        # index sets of the (zero) scores, so that idx always holds valid sets
+        self.identify()
 
     STATE = ("a_cache", "score", "y", "idx")
 
@@ -97,6 +103,7 @@ class MLPDelta:
         step scores its activations against zero, as the first one does."""
         for name in self.STATE:
             getattr(self, name).zero_()
+        self.identify()
 
     def dense(self, x: torch.Tensor, stream=None):
         lib.chipmunk_dense_step(lib.MLP, self.layer, x, None, None, self.y, self.ws, stream=stream)
@@ -115,8 +122,11 @@ class MLPDelta:
     def step(self, x: torch.Tensor, refresh: bool, stream=None):
         if refresh:
             self.dense(x, stream)
+            if not self.rescore:
+                self.identify(stream)
         else:
-            self.identify(stream)
+            if self.rescore:
+                self.identify(stream)
             self.sparse(x, stream=stream)
 
 
@@ -222,11 +232,12 @@ def schedule_step(kind: str, mlp: MLPDelta = None, att: AttnDelta = None, x=None
 
 def sparse_step(mlp: MLPDelta, att: AttnDelta, x, q, k, v, stream=None):
     """One sparse step of a block whose attention and MLP deltas are independent
-    (both read the block's input): the MLP's top-k over its scores (and the
-    attention's, when it re-identifies every step), then both deltas through
-    chipmunk_sparse_step (or chipmunk_sparse_step_reident).  Same results as
-    ``mlp.step(x, False)`` followed by ``att.step(q, k, v, False)``."""
-    mlp.identify(stream)
+    (both read the block's input): the top-k of a layer that re-identifies
+    every step (MLP rescoring, re-identifying attention), then both deltas
+    through chipmunk_sparse_step (or chipmunk_sparse_step_reident).  Same
+    results as ``mlp.step(x, False)`` followed by ``att.step(q, k, v, False)``."""
+    if mlp.rescore:
+        mlp.identify(stream)
     if att.reident:
         att.identify(stream)
         qp, kp, vp = att.prev
