@@ -96,7 +96,7 @@ def flops_attn(w, reident=False):
     return (8.0 if reident else 4.0) * w["n"] * w["kk"] * HEAD_DIM * w["heads"]
 
 
-def kernel_work(name, w, reident=False, fp8=False, fp8_w2=False):
+def kernel_work(name, w, reident=False, fp8=False, fp8_w2=False, rescore=False):
     """(amount, bound) of algorithmic work in ONE launch of kernel `name`
     (bound "mfma": bf16 matrix cores; "mfma_fp8": fp8 matrix cores; a
     ("mfma_mix", fp8 flops) bound: part of the flops on fp8 matrix cores)."""
@@ -122,8 +122,10 @@ def kernel_work(name, w, reident=False, fp8=False, fp8_w2=False):
         return 2.0 * n * k * d + 4.0 * n * kk * HEAD_DIM * H, "mfma"
     if name == "topk_rows":
         # score rows read + index rows written, averaged over the step's
-        # launches: the MLP's, and the attention's when it re-identifies
-        parts = ([nb * h * 4 + nb * k * 4] if k else []) + ([H * nb * n * 4 + H * nb * kk * 4] if reident else [])
+        # launches: the MLP's when it rescores every step, and the
+        # attention's when it re-identifies (otherwise both run at the refresh)
+        parts = (([nb * h * 4 + nb * k * 4] if k and rescore else []) +
+                 ([H * nb * n * 4 + H * nb * kk * 4] if reident else []))
         return (float(sum(parts)) / len(parts), "hbm") if parts else (None, None)
     return None, None
 
@@ -622,7 +624,7 @@ def main():
 
     table = {}
     for name, r in kern.items():
-        amount, bound = kernel_work(name, w, args.attn_reident, args.fp8, args.fp8_w2)
+        amount, bound = kernel_work(name, w, args.attn_reident, args.fp8, args.fp8_w2, args.mlp_rescore)
         ent = {"avg_us": round(r["avg_us"], 3), "launches": r["launches"],
                "share": round(r["ms_total"] / max(1e-12, sum(v["ms_total"] for v in kern.values())), 4)}
         if amount is not None:
@@ -635,9 +637,9 @@ def main():
             else:
                 ent.update(achieved=round(ach / 1e9, 1), unit="GB/s", frac=round(ach / 1e9 / PEAK_HBM_GBS, 4))
         table[name] = ent
-    dom = max((n for n in kern if kernel_work(n, w, args.attn_reident, args.fp8, args.fp8_w2)[0] is not None),
+    dom = max((n for n in kern if kernel_work(n, w, args.attn_reident, args.fp8, args.fp8_w2, args.mlp_rescore)[0] is not None),
               key=lambda n: kern[n]["ms_total"])
-    amount, bound = kernel_work(dom, w, args.attn_reident, args.fp8, args.fp8_w2)
+    amount, bound = kernel_work(dom, w, args.attn_reident, args.fp8, args.fp8_w2, args.mlp_rescore)
     avg_s = kern[dom]["avg_us"] * 1e-6
     if bound in ("mfma", "mfma_fp8") or isinstance(bound, tuple):
         peak = round(peak_for(bound, amount), 1)
