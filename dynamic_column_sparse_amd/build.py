@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libchipmunk.so")
 
-SOURCES = ["abi.cpp", "mlp.hip", "topk.hip", "attn.hip", "writeback.hip", "step.hip", "quant.hip", "noalloc.hip"]
+SOURCES = ["abi.cpp", "mlp.hip", "topk.hip", "attn.hip", "writeback.hip", "step.hip", "quant.hip", "noalloc.hip", "check.hip"]
 ARCH = "gfx950"
 
 

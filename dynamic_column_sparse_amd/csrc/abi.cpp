@@ -423,6 +423,25 @@ extern "C" int chipmunk_identify_topk(const float* score, int64_t rows, int64_t 
   }
 }
 
+extern "C" int chipmunk_check_index_sets(const int32_t* idx, int64_t rows, int32_t k, int64_t cols, int64_t* result,
+                                         void* stream) {
+  try {
+    if (rows < 0) return fail(CHIPMUNK_E_SHAPE, "rows must be >= 0");
+    if (cols < 1) return fail(CHIPMUNK_E_SHAPE, "cols must be >= 1");
+    if (k < 0 || k > cols) return fail(CHIPMUNK_E_SHAPE, "k must be in [0, cols] (k=%d, cols=%lld)", k, (long long)cols);
+    // four rows per workgroup of the check kernel
+    if ((rows + 3) / 4 > INT32_MAX) return fail(CHIPMUNK_E_SHAPE, "rows exceeds the grid limit");
+    if (!result) return fail(CHIPMUNK_E_NULLPTR, "result is required");
+    if (rows > 0 && k > 0 && !idx) return fail(CHIPMUNK_E_NULLPTR, "idx is required");
+    if (!aligned(result, 8)) return fail(CHIPMUNK_E_ALIGN, "result must be 8-byte aligned");
+    if (idx && !aligned(idx, 4)) return fail(CHIPMUNK_E_ALIGN, "idx must be 4-byte aligned");
+    return hip_status(chipmunk::launch_check_index_sets(idx, rows, k, cols, result, static_cast<hipStream_t>(stream)),
+                      "index-set check launch");
+  } catch (...) {
+    return fail(CHIPMUNK_E_INTERNAL, "internal error in chipmunk_check_index_sets");
+  }
+}
+
 extern "C" int chipmunk_sparse_mlp_delta(const chipmunk_mlp* L, const uint16_t* x, const int32_t* idx, int32_t k,
                                          float* y, uint16_t* a_new_packed, void* ws, size_t ws_bytes, void* stream) {
   try {

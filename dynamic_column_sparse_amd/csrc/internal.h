@@ -83,6 +83,10 @@ hipError_t launch_mlp_gemm2(bool dense, const uint16_t* src, const uint16_t* w2,
 hipError_t launch_writeback(const uint16_t* packed, const int32_t* idx, uint16_t* a_cache, int64_t n, int h,
                             int k, hipStream_t s);
 hipError_t launch_topk(const float* score, int64_t rows, int64_t cols, int k, int32_t* idx, hipStream_t s);
+// Index-set check: result[0] = rows breaking the contract, result[1] = the
+// smallest such row (rows if none).
+hipError_t launch_check_index_sets(const int32_t* idx, int64_t rows, int k, int64_t cols, int64_t* result,
+                                   hipStream_t s);
 hipError_t launch_attn_dense(const uint16_t* q, const uint16_t* k, const uint16_t* v, float* m, float* num,
                              float* den, float* o, float* score, int64_t n, int heads, float scale,
                              hipStream_t s);

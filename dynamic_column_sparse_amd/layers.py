@@ -38,6 +38,18 @@ def row_blocks(n: int) -> int:
     return (n + ROW_BLOCK - 1) // ROW_BLOCK
 
 
+def check_index_sets(idx: torch.Tensor, cols: int, what: str = "index sets"):
+    """Raise ValueError unless every row of idx [rows][k] (int32, on the
+    device) is strictly ascending with values in [0, cols): the contract the
+    kernels assume (they clamp bad values rather than fault).  Synchronizes."""
+    rows, k = idx.shape
+    res = torch.empty(2, dtype=torch.int64, device=idx.device)
+    lib.chipmunk_check_index_sets(idx, rows, k, cols, res)
+    bad, first = res.tolist()
+    if bad:
+        raise ValueError(f"{what}: {bad} of {rows} rows are not ascending sets of [0, {cols}) (first: row {first})")
+
+
 class MLPDelta:
     """One MLP layer: w1t [h,d], w2 [h,d] bf16 device tensors; k kept columns per block.
     rescore=True: every sparse step rescores the units it recomputed, so the set
@@ -91,12 +103,16 @@ class MLPDelta:
 
     def load_state_dict(self, state: dict):
         """Restore a state_dict() of a layer of the same shape, in place (the C
-        layer keeps pointing at the same buffers)."""
+        layer keeps pointing at the same buffers).  The index sets are checked
+        on the device (ValueError if a row is not an ascending set of hidden
+        units)."""
         for name in self.STATE:
             dst = getattr(self, name)
             src = state[name]
             assert src.shape == dst.shape and src.dtype == dst.dtype, name
             dst.copy_(src)
+        if self.k:
+            check_index_sets(self.idx, self.h, "MLP index sets")
 
     def reset(self):
         """Back to the state of a new layer: zero caches, so the next dense
@@ -161,11 +177,15 @@ class AttnDelta:
         return {name: getattr(self, name).detach().cpu() for name in self.STATE}
 
     def load_state_dict(self, state: dict):
+        """As MLPDelta.load_state_dict; the index sets are checked against the
+        key range."""
         for name in self.STATE:
             dst = getattr(self, name)
             src = state[name]
             assert src.shape == dst.shape and src.dtype == dst.dtype, name
             dst.copy_(src)
+        if self.kk:
+            check_index_sets(self.idx, self.n, "attention index sets")
 
     def reset(self):
         for name in self.STATE:

@@ -19,7 +19,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 # build of the test suite); it is held to the same ABI and source-digest check.
 LIB_PATH = os.environ.get("CHIPMUNK_LIBRARY") or os.path.join(_HERE, "libchipmunk.so")
 
-ABI_VERSION = 7
+ABI_VERSION = 8
 NOALLOC_SCRATCH_BYTES = 64 << 20   # CHIPMUNK_NOALLOC_SCRATCH_BYTES
 ROW_BLOCK = 128
 HEAD_DIM = 128
@@ -34,7 +34,7 @@ OP_DENSE_MLP_FP8, OP_SPARSE_MLP_FP8 = 5, 6
 STATUS = {0: "CHIPMUNK_OK", 1: "CHIPMUNK_E_NULLPTR", 2: "CHIPMUNK_E_SHAPE", 3: "CHIPMUNK_E_UNSUPPORTED",
           4: "CHIPMUNK_E_ALIGN", 5: "CHIPMUNK_E_WORKSPACE", 6: "CHIPMUNK_E_HIP", 7: "CHIPMUNK_E_INTERNAL"}
 
-EXPORTS = ("chipmunk_dense_step", "chipmunk_identify_topk", "chipmunk_sparse_mlp_delta",
+EXPORTS = ("chipmunk_dense_step", "chipmunk_identify_topk", "chipmunk_check_index_sets", "chipmunk_sparse_mlp_delta",
            "chipmunk_sparse_attn_delta", "chipmunk_sparse_attn_reident", "chipmunk_sparse_step",
            "chipmunk_sparse_step_reident", "chipmunk_sparse_mlp_delta_noalloc",
            "chipmunk_cache_writeback", "chipmunk_quantize_fp8",
@@ -75,6 +75,7 @@ def _load() -> ctypes.CDLL:
     sig = {
         "chipmunk_dense_step": (ctypes.c_int, [ctypes.c_int, vp, vp, vp, vp, vp, vp, sz, vp]),
         "chipmunk_identify_topk": (ctypes.c_int, [vp, i64, i64, i32, vp, vp, sz, vp]),
+        "chipmunk_check_index_sets": (ctypes.c_int, [vp, i64, i32, i64, vp, vp]),
         "chipmunk_sparse_mlp_delta": (ctypes.c_int, [vp, vp, vp, i32, vp, vp, vp, sz, vp]),
         "chipmunk_sparse_mlp_delta_noalloc": (ctypes.c_int, [vp, vp, vp, i32, vp, vp, vp]),
         "chipmunk_sparse_attn_delta": (ctypes.c_int, [vp, vp, vp, vp, vp, i32, ctypes.c_int, vp, vp]),
@@ -180,6 +181,14 @@ def chipmunk_dense_step(kind: int, layer, x_or_q, k=None, v=None, out=None, ws=N
     nbytes = _nbytes(ws, ws_bytes)
     _check(_lib.chipmunk_dense_step(kind, ctypes.byref(layer), _ptr(x_or_q), _ptr(k), _ptr(v), _ptr(out),
                                     _ptr(ws), nbytes, _stream(stream)))
+
+
+def chipmunk_check_index_sets(idx, rows: int, k: int, cols: int, result, stream=None):
+    """Enqueue the device check of index sets idx [rows][k] against the
+    contract (values in [0, cols), rows strictly ascending); result is an int64
+    device tensor of 2 that receives (rows breaking it, smallest such row or
+    `rows`)."""
+    _check(_lib.chipmunk_check_index_sets(_ptr(idx), rows, k, cols, _ptr(result), _stream(stream)))
 
 
 def chipmunk_identify_topk(score, rows: int, cols: int, k: int, idx, ws=None, stream=None, ws_bytes=None):

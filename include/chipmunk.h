@@ -35,8 +35,11 @@
  *    outputs, and are kept at zero in the activation cache.
  *  - Index sets (`idx`): int32 [rows][k], each row ascending and unique, every
  *    value in [0, cols).  Kernels clamp out-of-range values into range (so a
- *    bad index cannot fault) but the result is then meaningless.
- *  - Offsets are 64-bit throughout.  Calls are re-entrant; the only shared
+ *    bad index cannot fault) but the result is then meaningless;
+ *    chipmunk_check_index_sets() checks sets a caller built itself.
+ *  - Offsets are 64-bit, except the gathered K/V rows of the attention
+ *    kernels, addressed by 32-bit byte offsets from each head's base: the
+ *    attention calls require n < 2^24.  Calls are re-entrant; the only shared
  *    mutable state is the optional kernel timer (chipmunk_timing_*), which
  *    takes a lock.
  *  - Two calls that write the same buffers must be ordered by the caller
@@ -52,7 +55,7 @@
 extern "C" {
 #endif
 
-#define CHIPMUNK_ABI_VERSION 7
+#define CHIPMUNK_ABI_VERSION 8
 #define CHIPMUNK_ROW_BLOCK 128
 #define CHIPMUNK_HEAD_DIM 128
 
@@ -201,6 +204,18 @@ int chipmunk_dense_step(int kind, const void* layer, const uint16_t* x_or_q, con
  * ws may be NULL. */
 int chipmunk_identify_topk(const float* score, int64_t rows, int64_t cols, int32_t k, int32_t* idx,
                            void* ws, size_t ws_bytes, void* stream);
+
+/* Checks index sets against the contract above, on the device: for each of
+ * `rows` rows of idx [rows][k] (row stride k), whether every value is in
+ * [0, cols) and the row is strictly ascending (so its values are unique).
+ * Writes result[0] = the number of rows that break the contract and
+ * result[1] = the smallest such row (`rows` if none), as int64 in device
+ * memory the caller owns (8-byte aligned); the call allocates nothing.  For
+ * callers that build index sets themselves (the kernels clamp bad values,
+ * which hides the mistake).  0 <= k <= cols; rows = 0 or k = 0 writes
+ * {0, rows}.  Enqueues two small kernels on `stream`. */
+int chipmunk_check_index_sets(const int32_t* idx, int64_t rows, int32_t k, int64_t cols, int64_t* result,
+                              void* stream);
 
 /* Sparse MLP delta step (Chipmunk post, Activation Deltas section): per block b
  * with S = idx[b] (k hidden units), gather the rows W1^T[S], W2[S] and the cache

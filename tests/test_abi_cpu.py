@@ -44,7 +44,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_names_workspace(L):
-    assert L.chipmunk_abi_version() == L.ABI_VERSION == 7
+    assert L.chipmunk_abi_version() == L.ABI_VERSION == 8
     assert L.chipmunk_source_digest() == source_digest()
     names = L.kernel_names()
     assert "mlp_gemm1_sparse" in names and "attn_sparse" in names and "topk_rows" in names
@@ -149,6 +149,19 @@ def test_topk_and_attn_checks(L):
     assert _code(L, w, _mlp(L), FAKE, FAKE, 700, stream=0) == 2
     assert _code(L, w, _mlp(L), None, FAKE, 10, stream=0) == 1
     assert _code(L, w, _mlp(L), FAKE, FAKE, 0, stream=0) == 0
+
+
+def test_index_set_check_arguments(L):
+    # Rejected before anything is enqueued (a valid call launches kernels).
+    c = L.chipmunk_check_index_sets
+    assert _code(L, c, FAKE, -1, 3, 10, FAKE, stream=0) == 2       # rows < 0
+    assert _code(L, c, FAKE, 4, 11, 10, FAKE, stream=0) == 2       # k > cols
+    assert _code(L, c, FAKE, 4, -1, 10, FAKE, stream=0) == 2       # k < 0
+    assert _code(L, c, FAKE, 4, 3, 0, FAKE, stream=0) == 2         # cols < 1
+    assert _code(L, c, FAKE, 4, 3, 10, None, stream=0) == 1        # no result buffer
+    assert _code(L, c, None, 4, 3, 10, FAKE, stream=0) == 1        # no index sets to check
+    assert _code(L, c, FAKE, 4, 3, 10, FAKE + 4, stream=0) == 4    # result not 8-byte aligned
+    assert _code(L, c, FAKE + 2, 4, 3, 10, FAKE, stream=0) == 4    # idx not 4-byte aligned
 
 
 def test_sparse_step_checks(L):

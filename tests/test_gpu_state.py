@@ -131,3 +131,30 @@ def test_refresh_recovers_from_corrupted_caches(gpu_lib):
     _equal(bad_m, fresh_m, "MLP after reset")
     _equal(bad_a, fresh_a, "attention after reset")
     assert torch.isfinite(bad_m.y).all() and torch.isfinite(bad_a.o).all()
+
+
+def test_loading_bad_index_sets_is_refused(gpu_lib):
+    # A checkpoint whose index sets break the contract (a repeated unit, a key
+    # past n) is refused when loaded, naming the first bad row.
+    from dynamic_column_sparse_amd.layers import AttnDelta, MLPDelta
+    n, d, h, k, H, kk = 300, 256, 640, 64, 2, 40
+    w1t_b, w2_b = syn.mlp_weights(2, d, h)
+    mlp = MLPDelta(up_bf16(w1t_b), up_bf16(w2_b), n, k)
+    att = AttnDelta(n, H, kk, "cuda")
+    x = up_bf16(syn.activations(2, "X", 0, n, d))
+    qkv = [up_bf16(syn.heads_activations(2, t, 0, H, n)) for t in "QKV"]
+    mlp.step(x, refresh=True)
+    att.step(*qkv, refresh=True)
+    torch.cuda.synchronize()
+    sm, sa = mlp.state_dict(), att.state_dict()
+    mlp.load_state_dict(sm)                       # a sound state loads
+    att.load_state_dict(sa)
+    bad_m = {key: v.clone() for key, v in sm.items()}
+    bad_m["idx"][1, 5] = bad_m["idx"][1, 4]
+    with pytest.raises(ValueError, match="row 1"):
+        mlp.load_state_dict(bad_m)
+    bad_a = {key: v.clone() for key, v in sa.items()}
+    bad_a["idx"][4, kk - 1] = n
+    bad_a["idx"][5, 0] = -3
+    with pytest.raises(ValueError, match="2 of 6 rows.*row 4"):
+        att.load_state_dict(bad_a)
