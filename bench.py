@@ -55,22 +55,22 @@ WORKLOADS = {
     # HunyuanVideo 720x1280x129: 33x45x80 latent patches, 93% sparse on the
     # sparse steps; MLP refresh every 10 steps, attention 6 dense of 50.
     "hunyuan": dict(n=118800, d=3072, h=12288, k=860, heads=24, kk=8316, loop=50, mlp_every=10, attn_every=9,
-                    inputs=10, mlp_sample=32, attn_sample=4),
+                    inputs=10, mlp_sample=32, attn_sample=4, steps=20),
     "hunyuan_mlp": dict(n=118800, d=3072, h=12288, k=860, heads=0, kk=0, loop=50, mlp_every=10, attn_every=9,
-                        inputs=10, mlp_sample=32, attn_sample=0),
+                        inputs=10, mlp_sample=32, attn_sample=0, steps=50),
     "hunyuan_attn": dict(n=118800, d=0, h=0, k=0, heads=24, kk=8316, loop=50, mlp_every=10, attn_every=9,
-                         inputs=10, mlp_sample=0, attn_sample=4),
+                         inputs=10, mlp_sample=0, attn_sample=4, steps=20),
     # FLUX.1-dev at 1280x768: 3840 image + 512 text tokens; MLP 70% sparse (keep
     # 3686 of 12288), attention 83.5% sparse (keep 718 of 4352 keys); 10 steps,
     # refresh at step 0.
     "flux": dict(n=4352, d=3072, h=12288, k=3686, heads=24, kk=718, loop=10, mlp_every=10, attn_every=10,
-                 inputs=10, mlp_sample=None, attn_sample=None),
+                 inputs=10, mlp_sample=None, attn_sample=None, steps=200),
     # FLUX.1-dev at 2304x1280: 144x80 = 11520 image + 512 text tokens, the same
     # sparsities (keep 3686 of 12288 hidden units, 16.5% = 1985 of 12032 keys).
     "flux_2304": dict(n=12032, d=3072, h=12288, k=3686, heads=24, kk=1985, loop=10, mlp_every=10, attn_every=10,
-                      inputs=10, mlp_sample=None, attn_sample=None),
+                      inputs=10, mlp_sample=None, attn_sample=None, steps=100),
     "tiny": dict(n=256, d=128, h=512, k=128, heads=0, kk=0, loop=2, mlp_every=2, attn_every=2, inputs=2,
-                 mlp_sample=None, attn_sample=0),
+                 mlp_sample=None, attn_sample=0, steps=200),
 }
 WORKLOAD_NAMES = {
     "hunyuan": "HunyuanVideo-shaped sparse step (MLP + attention delta)",
@@ -412,7 +412,9 @@ def cpu_baseline(w, host, budget_s, reident=False, fp8=False, fp8_w2=False, resc
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=0,
+                    help="timed sparse steps (0: the workload's default, enough steps of a short workload to make "
+                         "the first step's ramp negligible)")
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="hunyuan", choices=sorted(WORKLOADS))
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
@@ -463,6 +465,8 @@ def main():
     from dynamic_column_sparse_amd.layers import AttnDelta, MLPDelta, sparse_step
 
     w = WORKLOADS[args.workload]
+    if args.steps <= 0:
+        args.steps = w["steps"]
     dev = torch.device("cuda:0")
     T = w["loop"]
     D = max(2, min(T, args.inputs or w["inputs"]))
