@@ -170,28 +170,28 @@ __global__ __launch_bounds__(256, 2) void mlp_gemm1(const void* __restrict__ xv,
   const int KT = (int)(RB / ROWB);
   G1_ISSUE(0, 0);
   if (KT > 1) G1_ISSUE(1, 1);
-  // Fragments of 16-deep substep s_ (into buffer q_) from the stage at st_.
-#define G1_FRAG(st_, s_, q_)                                                                         \
+  for (int kt = 0; kt < KT; ++kt) {
+    if (kt + 1 < KT)
+      wait_vmcnt<L>();
+    else
+      wait_vmcnt<0>();
+    barrier();
+    if (kt + 2 < KT) G1_ISSUE(kt + 2, (kt + 2) % NS);
+    const unsigned char* st = smem + (kt % NS) * STAGE;
+    // Operand fragments of K-substep s+1 are read while substep s multiplies.
+    bf16x8_t af[2][MI], bfr[2][NI];
+#define G1_FRAG(s_, q_)                                                                              \
     {                                                                                                \
       const int coff = (((2 * (s_) + (lane >> 5)) ^ sw) << 4);                                       \
       _Pragma("unroll") for (int mi = 0; mi < MI; ++mi)                                              \
-        af[q_][mi] = *(const bf16x8_t*)((st_) + (wm * 64 + mi * 32 + (lane & 31)) * ROWB + coff);    \
+        af[q_][mi] = *(const bf16x8_t*)(st + (wm * 64 + mi * 32 + (lane & 31)) * ROWB + coff);       \
       _Pragma("unroll") for (int ni = 0; ni < NI; ++ni)                                              \
-        bfr[q_][ni] = *(const bf16x8_t*)((st_) + A_BYTES + (wn * WN + ni * 32 + (lane & 31)) * ROWB + coff); \
+        bfr[q_][ni] = *(const bf16x8_t*)(st + A_BYTES + (wn * WN + ni * 32 + (lane & 31)) * ROWB + coff); \
     }
-  bf16x8_t af[2][MI], bfr[2][NI];
-  if constexpr (F8) {
-    for (int kt = 0; kt < KT; ++kt) {
-      if (kt + 1 < KT)
-        wait_vmcnt<L>();
-      else
-        wait_vmcnt<0>();
-      barrier();
-      if (kt + 2 < KT) G1_ISSUE(kt + 2, (kt + 2) % NS);
-      const unsigned char* st = smem + (kt % NS) * STAGE;
+    G1_FRAG(0, 0);
+    if constexpr (F8) {
       // Both 16-byte halves form one 64-deep fp8 operand.
-      G1_FRAG(st, 0, 0);
-      G1_FRAG(st, 1, 1);
+      G1_FRAG(1, 1);
       typedef int i32x4_t __attribute__((ext_vector_type(4)));
       typedef int i32x8_t __attribute__((ext_vector_type(8)));
       auto cat = [](bf16x8_t lo, bf16x8_t hi) __attribute__((always_inline)) {
@@ -207,46 +207,18 @@ __global__ __launch_bounds__(256, 2) void mlp_gemm1(const void* __restrict__ xv,
           acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, cat(bfr[0][ni], bfr[1][ni]), acc[mi][ni],
                                                                         0, 0, 0, sa[mi], 0, sb[ni]);
       }
-    }
-  } else {
-    static_assert(NS == 3 && BK == 32, "three stages of two 16-deep substeps");
-    // The two 16-deep substeps of a chunk overlap the LDS reads of the other:
-    // iteration kt reads the second substep's fragments of chunk kt while the
-    // first substep multiplies; then, once chunk kt+1 has landed and every
-    // wave holds its fragments of chunk kt (the wait covers this wave's LDS
-    // reads too, the barrier every wave's), chunk kt's slot takes chunk kt+3
-    // and the first substep's fragments of chunk kt+1 are read while the
-    // second substep of chunk kt multiplies.
-    if (KT > 1)
-      wait_vmcnt<L>();
-    else
-      wait_vmcnt<0>();
-    barrier();
-    if (KT > 2) G1_ISSUE(2, 2);
-    G1_FRAG(smem, 0, 0);
-    for (int kt = 0; kt < KT; ++kt) {
-      G1_FRAG(smem + (kt % NS) * STAGE, 1, 1);
+    } else {
 #pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
+      for (int s = 0; s < BK / 16; ++s) {
+        if (s + 1 < BK / 16) G1_FRAG(s + 1, (s + 1) & 1);
 #pragma unroll
-        for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = mfma32(af[0][mi], bfr[0][ni], acc[mi][ni]);
-      if (kt + 1 < KT) {
-        // Newer than chunk kt+1: chunk kt+2's loads, if it exists.
-        if (kt + 2 < KT)
-          wait_vmcnt<L>();
-        else
-          wait_vmcnt<0>();
-        barrier();
-        if (kt + 3 < KT) G1_ISSUE(kt + 3, (kt + 3) % NS);   // chunk kt's slot
-        G1_FRAG(smem + ((kt + 1) % NS) * STAGE, 0, 0);
+        for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+          for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = mfma32(af[s & 1][mi], bfr[s & 1][ni], acc[mi][ni]);
       }
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = mfma32(af[1][mi], bfr[1][ni], acc[mi][ni]);
     }
-  }
 #undef G1_FRAG
+  }
 #undef G1_ISSUE
 
   // ---- epilogue ----
