@@ -165,8 +165,8 @@ __global__ __launch_bounds__(256, 4) void attn_stats(const uint16_t* __restrict_
       dma16_at(kh + (int64_t)(key < nn ? key : nn - 1) * 128 + geo.koff[i], st + (wave * kIns + i) * 1024);
     }
   };
-  auto issue_full = [&](int t) __attribute__((always_inline)) {
-    const uint32_t st = smem_lds + (t % NS) * kTile;
+  auto issue_full = [&](int t, int slot) __attribute__((always_inline)) {
+    const uint32_t st = smem_lds + slot * kTile;
     const unsigned char* base = (const unsigned char*)kh + (int64_t)t * kTile;
 #pragma unroll
     for (int i = 0; i < kIns; ++i) dma16_sa(base, kofs[i], st + (wave * kIns + i) * 1024);
@@ -188,9 +188,14 @@ __global__ __launch_bounds__(256, 4) void attn_stats(const uint16_t* __restrict_
   float mr = -INFINITY, lr = 0.f;
   // Iteration t issues chunk t+1's score products into `nxt`, then folds chunk
   // t (in `cur`) into the running (m, l).  Steady iterations issue a full
-  // chunk (t + NS - 1 < KF); their own chunk is full too.
-  auto body = [&](int t, f32x16_t& cur, f32x16_t& nxt, auto STEADY) __attribute__((always_inline)) {
+  // chunk (t + NS - 1 < KF); their own chunk is full too.  SLOT >= 0 is t % NS
+  // known at compile time (the unrolled steady loop), so the stage addresses
+  // become immediate offsets of the LDS reads.
+  auto body = [&](int t, f32x16_t& cur, f32x16_t& nxt, auto STEADY, auto SLOT) __attribute__((always_inline)) {
     constexpr bool steady = decltype(STEADY)::value;
+    constexpr int slot = decltype(SLOT)::value;
+    const int s1 = slot >= 0 ? (slot + 1) % NS : (t + 1) % NS;
+    const int sl = slot >= 0 ? (slot + NS - 1) % NS : (t + NS - 1) % NS;
     if (steady || t + 1 < KT) {
       // Stage t+1 must be complete; newer than it are the stages issued up to
       // min(t + NS - 2, KT - 1).
@@ -203,10 +208,10 @@ __global__ __launch_bounds__(256, 4) void attn_stats(const uint16_t* __restrict_
       barrier();
       // Stage t+NS-1 reuses the slot of chunk t-1, read at iteration t-2.
       if (steady)
-        issue_full(t + NS - 1);
+        issue_full(t + NS - 1, sl);
       else if (t + NS - 1 < KT)
         issue(t + NS - 1);
-      nxt = chunk_scores(smem + ((t + 1) % NS) * kTile, qf, lane);
+      nxt = chunk_scores(smem + s1 * kTile, qf, lane);
     }
     const bool full = steady || t * kSK + kSK <= nn;
     float mloc = -INFINITY;
@@ -231,15 +236,23 @@ __global__ __launch_bounds__(256, 4) void attn_stats(const uint16_t* __restrict_
       mr = mnew;
     }
   };
+  static_assert(NS == 4, "the steady loop is unrolled by the ring size");
+  using Dyn = std::integral_constant<int, -1>;
   int t = 0;
+  for (; t + 3 + NS < KF; t += 4) {
+    body(t, sa, sb, std::true_type{}, std::integral_constant<int, 0>{});
+    body(t + 1, sb, sa, std::true_type{}, std::integral_constant<int, 1>{});
+    body(t + 2, sa, sb, std::true_type{}, std::integral_constant<int, 2>{});
+    body(t + 3, sb, sa, std::true_type{}, std::integral_constant<int, 3>{});
+  }
   for (; t + NS < KF; t += 2) {
-    body(t, sa, sb, std::true_type{});
-    body(t + 1, sb, sa, std::true_type{});
+    body(t, sa, sb, std::true_type{}, Dyn{});
+    body(t + 1, sb, sa, std::true_type{}, Dyn{});
   }
   while (t < KT) {
-    body(t, sa, sb, std::false_type{});
+    body(t, sa, sb, std::false_type{}, Dyn{});
     if (++t >= KT) break;
-    body(t, sb, sa, std::false_type{});
+    body(t, sb, sa, std::false_type{}, Dyn{});
     ++t;
   }
 
@@ -346,8 +359,8 @@ __global__ __launch_bounds__(256, 2) void attn_dense(const uint16_t* __restrict_
     for (int i = 0; i < kIns; ++i)
       dma16_at(vh + (int64_t)key[i] * 128 + geo.voff[i], st + kTile + (wave * kIns + i) * 1024);
   };
-  auto issue_full = [&](int t) __attribute__((always_inline)) {
-    const uint32_t st = smem_lds + (t % NS) * STAGE;
+  auto issue_full = [&](int t, int slot) __attribute__((always_inline)) {
+    const uint32_t st = smem_lds + slot * STAGE;
     const unsigned char* kb = (const unsigned char*)kh + (int64_t)t * kTile;
     const unsigned char* vb = (const unsigned char*)vh + (int64_t)t * kTile;
 #pragma unroll
@@ -406,8 +419,14 @@ __global__ __launch_bounds__(256, 2) void attn_dense(const uint16_t* __restrict_
   const int pq = lane & 31, ph = lane >> 5;
   f32x16_t sa = chunk_scores(smem, qf, lane), sb;
 
-  auto body = [&](int t, f32x16_t& cur, f32x16_t& nxt, auto STEADY) __attribute__((always_inline)) {
+  // SLOT >= 0 is t % NS known at compile time (the unrolled steady loop), so
+  // the stage addresses become immediate offsets of the LDS reads.
+  auto body = [&](int t, f32x16_t& cur, f32x16_t& nxt, auto STEADY, auto SLOT) __attribute__((always_inline)) {
     constexpr bool steady = decltype(STEADY)::value;
+    constexpr int slot = decltype(SLOT)::value;
+    const int s0 = slot >= 0 ? slot : t % NS;
+    const int s1 = slot >= 0 ? (slot + 1) % NS : (t + 1) % NS;
+    const int sl = slot >= 0 ? (slot + NS - 1) % NS : (t + NS - 1) % NS;
     if (steady || t + 1 < KT) {
       if (steady) {
         wait_vmcnt<(NS - 3) * L>();
@@ -421,12 +440,12 @@ __global__ __launch_bounds__(256, 2) void attn_dense(const uint16_t* __restrict_
       // Stage t+NS-1 reuses the slot of chunk t-1: its keys were read at
       // iteration t-2 and its values at t-1, before this barrier.
       if (steady)
-        issue_full(t + NS - 1);
+        issue_full(t + NS - 1, sl);
       else if (t + NS - 1 < KT)
         issue(t + NS - 1);
-      nxt = chunk_scores(smem + ((t + 1) % NS) * STAGE, qf, lane);
+      nxt = chunk_scores(smem + s1 * STAGE, qf, lane);
     }
-    const unsigned char* st = smem + (t % NS) * STAGE;
+    const unsigned char* st = smem + s0 * STAGE;
     const bool full = steady || t * kSK + kSK <= nn;
     float p[16];
 #pragma unroll
@@ -458,15 +477,23 @@ __global__ __launch_bounds__(256, 2) void attn_dense(const uint16_t* __restrict_
     sc = mfma32h(wq[1], p_operand(pw, 16, lane), sc);
     if (lane < 32) sSc[(t / G) & 1][t % G][wave][lane] = sc[0] * (1.f / 32768.f);
   };
+  static_assert(NS == 4 && G == 4, "the steady loop is unrolled by the ring size");
+  using Dyn = std::integral_constant<int, -1>;
   int t = 0;
+  for (; t + 3 + NS < KF; t += 4) {
+    body(t, sa, sb, std::true_type{}, std::integral_constant<int, 0>{});
+    body(t + 1, sb, sa, std::true_type{}, std::integral_constant<int, 1>{});
+    body(t + 2, sa, sb, std::true_type{}, std::integral_constant<int, 2>{});
+    body(t + 3, sb, sa, std::true_type{}, std::integral_constant<int, 3>{});
+  }
   for (; t + NS < KF; t += 2) {
-    body(t, sa, sb, std::true_type{});
-    body(t + 1, sb, sa, std::true_type{});
+    body(t, sa, sb, std::true_type{}, Dyn{});
+    body(t + 1, sb, sa, std::true_type{}, Dyn{});
   }
   while (t < KT) {
-    body(t, sa, sb, std::false_type{});
+    body(t, sa, sb, std::false_type{}, Dyn{});
     if (++t >= KT) break;
-    body(t, sb, sa, std::false_type{});
+    body(t, sb, sa, std::false_type{}, Dyn{});
     ++t;
   }
 
@@ -682,8 +709,14 @@ __device__ __forceinline__ void attn_sparse_body(int lin, unsigned char* smem, i
     // happens, the chunk is full, the rest numerator is not yet issued, and the
     // loads newer than stage t+1 are one stage (L) plus, on wave 0 after the
     // first iteration, one id load.  They run without run-time conditions.
-    auto body = [&](int t, auto STEADY) __attribute__((always_inline)) {
+    // SLOT >= 0 is t % NSS known at compile time (the unrolled steady loop),
+    // so the stage addresses become immediate offsets of the LDS reads.
+    auto body = [&](int t, auto STEADY, auto SLOT) __attribute__((always_inline)) {
       constexpr bool steady = decltype(STEADY)::value;
+      constexpr int slot = decltype(SLOT)::value;
+      const int s0 = slot >= 0 ? slot : t % NSS;
+      const int s1 = slot >= 0 ? (slot + 1) % NSS : (t + 1) % NSS;
+      const int sl = slot >= 0 ? (slot + NSS - 1) % NSS : (t + NSS - 1) % NSS;
       f32x16_t snext;
       if (steady || t + 1 < KT) {
         if (steady) {
@@ -711,12 +744,12 @@ __device__ __forceinline__ void attn_sparse_body(int lin, unsigned char* smem, i
         // Slot of stage t+NSS-1 is stage t-1's: its keys were read at
         // iteration t-2 and its values at t-1, before this barrier.
         if (steady || t + DID < KT) id_dma(t + DID);
-        if (steady || t + NSS - 1 < KT) AS_ISSUE((t + NSS - 1) % NSS, ids_a);
+        if (steady || t + NSS - 1 < KT) AS_ISSUE(sl, ids_a);
         if (!steady && t == t_r) load_rest();
         if (steady || t + NSS < KT) load_ids(t + NSS, ids_b);
-        snext = scores((t + 1) % NSS);
+        snext = scores(s1);
       }
-      const unsigned char* st = smem + (t % NSS) * STAGE;
+      const unsigned char* st = smem + s0 * STAGE;
       // p = exp(s*scale - m) = 2^(s*scale*log2e - m*log2e): one FMA and one
       // exp2 per element.  Only the last chunk can hold positions past kk.
       // Query rows past the block end hold finite values (their loads are
@@ -753,9 +786,17 @@ __device__ __forceinline__ void attn_sparse_body(int lin, unsigned char* smem, i
         for (int i = 0; i < INS; ++i) ids_a[i] = ids_b[i];
       }
     };
+    static_assert(NSS == 4, "the steady loop is unrolled by the ring size");
+    using Dyn = std::integral_constant<int, -1>;
     int t = 0;
-    for (; t + DID < KT; ++t) body(t, std::true_type{});
-    for (; t < KT; ++t) body(t, std::false_type{});
+    for (; t + 3 + DID < KT; t += 4) {
+      body(t, std::true_type{}, std::integral_constant<int, 0>{});
+      body(t + 1, std::true_type{}, std::integral_constant<int, 1>{});
+      body(t + 2, std::true_type{}, std::integral_constant<int, 2>{});
+      body(t + 3, std::true_type{}, std::integral_constant<int, 3>{});
+    }
+    for (; t + DID < KT; ++t) body(t, std::true_type{}, Dyn{});
+    for (; t < KT; ++t) body(t, std::false_type{}, Dyn{});
   } else {
     load_qmd();
     load_rest();
