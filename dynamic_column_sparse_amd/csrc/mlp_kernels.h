@@ -170,14 +170,16 @@ __global__ __launch_bounds__(256, 2) void mlp_gemm1(const void* __restrict__ xv,
   const int KT = (int)(RB / ROWB);
   G1_ISSUE(0, 0);
   if (KT > 1) G1_ISSUE(1, 1);
-  for (int kt = 0; kt < KT; ++kt) {
+  // One K-chunk; `slot` is kt % NS (a constant in the unrolled loop below, so
+  // the stage base becomes an immediate offset of the LDS reads).
+  auto chunk = [&](int kt, int slot) __attribute__((always_inline)) {
     if (kt + 1 < KT)
       wait_vmcnt<L>();
     else
       wait_vmcnt<0>();
     barrier();
-    if (kt + 2 < KT) G1_ISSUE(kt + 2, (kt + 2) % NS);
-    const unsigned char* st = smem + (kt % NS) * STAGE;
+    if (kt + 2 < KT) G1_ISSUE(kt + 2, (slot + 2) % NS);
+    const unsigned char* st = smem + slot * STAGE;
     // Operand fragments of K-substep s+1 are read while substep s multiplies.
     bf16x8_t af[2][MI], bfr[2][NI];
 #define G1_FRAG(s_, q_)                                                                              \
@@ -218,7 +220,15 @@ __global__ __launch_bounds__(256, 2) void mlp_gemm1(const void* __restrict__ xv,
       }
     }
 #undef G1_FRAG
+  };
+  static_assert(NS == 3, "the K loop is unrolled by the ring size");
+  int kt = 0;
+  for (; kt + 2 < KT; kt += 3) {
+    chunk(kt, 0);
+    chunk(kt + 1, 1);
+    chunk(kt + 2, 2);
   }
+  for (; kt < KT; ++kt) chunk(kt, kt % NS);
 #undef G1_ISSUE
 
   // ---- epilogue ----
@@ -671,7 +681,9 @@ __device__ __forceinline__ void gemm2_rows_body(int lin, unsigned char* smem, in
       }
 
   const int sw = swz4(lane & 31);
-  for (int kt = 0; kt < KT; ++kt) {
+  // One K-chunk; `slot` is kt % NS (a constant in the unrolled loop below, so
+  // the stage base becomes an immediate offset of the LDS reads).
+  auto chunk = [&](int kt, int slot) __attribute__((always_inline)) {
     // Outstanding loads of this wave, newest first: stage kt+1 (L) and, on wave
     // 0, the id load of chunk kt+5 if the previous iteration issued one.
     // Everything older (stage kt, and y) must be complete.
@@ -685,9 +697,9 @@ __device__ __forceinline__ void gemm2_rows_body(int lin, unsigned char* smem, in
     }
     barrier();
     if (kt + 6 < KT) id_dma(kt + 6);
-    if (kt + 2 < KT) G2R_ISSUE(kt + 2, (kt + 2) % NS, ids_a);
+    if (kt + 2 < KT) G2R_ISSUE(kt + 2, (slot + 2) % NS, ids_a);
     if (kt + 3 < KT) load_ids(kt + 3, ids_b);
-    const unsigned char* st = smem + (kt % NS) * STAGE;
+    const unsigned char* st = smem + slot * STAGE;
 #pragma unroll
     for (int s = 0; s < BK / 16; ++s) {
       const int coff = (((2 * s + (lane >> 5)) ^ sw) << 4);
@@ -703,7 +715,15 @@ __device__ __forceinline__ void gemm2_rows_body(int lin, unsigned char* smem, in
     }
 #pragma unroll
     for (int i = 0; i < W_INS; ++i) ids_a[i] = ids_b[i];
+  };
+  static_assert(NS == 3, "the K loop is unrolled by the ring size");
+  int kt = 0;
+  for (; kt + 2 < KT; kt += 3) {
+    chunk(kt, 0);
+    chunk(kt + 1, 1);
+    chunk(kt + 2, 2);
   }
+  for (; kt < KT; ++kt) chunk(kt, kt % NS);
 #undef G2R_ISSUE
 
   // y = acc (which started from the old y).
