@@ -223,10 +223,12 @@ __global__ __launch_bounds__(256, 2) void mlp_gemm1(const void* __restrict__ xv,
   };
   static_assert(NS == 3, "the K loop is unrolled by the ring size");
   int kt = 0;
-  for (; kt + 2 < KT; kt += 3) {
-    chunk(kt, 0);
-    chunk(kt + 1, 1);
-    chunk(kt + 2, 2);
+  if constexpr (!F8) {   // the fp8 body, unrolled, would spill
+    for (; kt + 2 < KT; kt += 3) {
+      chunk(kt, 0);
+      chunk(kt + 1, 1);
+      chunk(kt + 2, 2);
+    }
   }
   for (; kt < KT; ++kt) chunk(kt, kt % NS);
 #undef G1_ISSUE
@@ -476,7 +478,9 @@ __global__ __launch_bounds__(256, 2) void mlp_gemm2(const uint16_t* __restrict__
   load_ids(1, ids_b);
   if (KT > 1) G2_ISSUE(1, 1, ids_b);
   load_ids(2, ids_a);
-  for (int kt = 0; kt < KT; ++kt) {
+  // One K-chunk; `slot` is kt % NS (a constant in the unrolled loop below, so
+  // the stage base becomes an immediate offset of the LDS reads).
+  auto chunk = [&](int kt, int slot) __attribute__((always_inline)) {
     // Outstanding loads of this wave, newest first: stage kt+1 (L) and, on wave
     // 0 of the sparse step, the id load of chunk kt+5 if the previous
     // iteration issued one.  Everything older (stage kt) must be complete.
@@ -490,9 +494,9 @@ __global__ __launch_bounds__(256, 2) void mlp_gemm2(const uint16_t* __restrict__
     }
     barrier();
     if (kt + 6 < KT) id_dma(kt + 6);
-    if (kt + 2 < KT) G2_ISSUE(kt + 2, (kt + 2) % NS, ids_a);
+    if (kt + 2 < KT) G2_ISSUE(kt + 2, (slot + 2) % NS, ids_a);
     load_ids(kt + 3, ids_b);
-    const unsigned char* st = smem + (kt % NS) * STAGE;
+    const unsigned char* st = smem + slot * STAGE;
     bf16x8_t af[2][MI], bfr[2][NI];
 #define G2_FRAG(s_, q_)                                                                              \
     {                                                                                                \
@@ -513,7 +517,15 @@ __global__ __launch_bounds__(256, 2) void mlp_gemm2(const uint16_t* __restrict__
 #undef G2_FRAG
 #pragma unroll
     for (int i = 0; i < W_INS; ++i) ids_a[i] = ids_b[i];
+  };
+  static_assert(NS == 3, "the K loop is unrolled by the ring size");
+  int kt = 0;
+  for (; kt + 2 < KT; kt += 3) {
+    chunk(kt, 0);
+    chunk(kt + 1, 1);
+    chunk(kt + 2, 2);
   }
+  for (; kt < KT; ++kt) chunk(kt, kt % NS);
 #undef G2_ISSUE
 
   // Epilogue in two phases (every old y value or bias loaded, then every sum
