@@ -548,7 +548,8 @@ int check_step_overlap(const chipmunk_mlp* M, const uint16_t* x, const int32_t* 
                         {M->w2, (size_t)M->h * M->d * 2, "w2"},
                         {M->b1, M->b1 ? (size_t)M->h * 4 : 0, "b1"},
                         {mlp_idx, nb * mk * 4, "mlp idx"}};
-  const int64_t groups = (k > 0 ? (int64_t)(M->d / 128) * (int64_t)nb + 8 : 0) + attn_groups;
+  // Each part of the grid is at most 7 workgroups of padding above its units.
+  const int64_t groups = (k > 0 ? (int64_t)(M->d / 128) * (int64_t)nb + 8 : 0) + attn_groups + 8;
   if (groups > kMaxGroups) return fail(CHIPMUNK_E_SHAPE, "the fused grid exceeds %lld workgroups", (long long)kMaxGroups);
   for (const Span& w : mlp_w) {
     for (const Span& r : att_w)

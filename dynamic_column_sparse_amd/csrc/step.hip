@@ -1,15 +1,15 @@
 // The sparse step of one transformer block as two launches: the MLP's sparse
-// phase 1, then ONE kernel whose first workgroups run the MLP's phase-2 tiles
-// and whose remaining workgroups run the attention delta (the fixed-set step,
-// or the step that re-identifies its keys every step).
+// phase 1, then ONE kernel whose workgroups run the MLP's phase-2 tiles and the
+// attention delta (the fixed-set step, or the step that re-identifies its keys
+// every step).
 //
 // The attention delta and the MLP delta of a step read different inputs and
 // write different outputs, so nothing orders them.  Run one after the other,
-// the phase-2 tiles (one wave of long units) leave part of the chip idle at
-// their tail and the attention units (1.6 waves of short ones) leave a ragged
-// tail of their own.  Sharing one grid lets the short attention units fill the
-// workgroup slots beside the long phase-2 units (longest work first), and the
-// two kernels' tails overlap.
+// each leaves a ragged tail (at FLUX the phase-2 tiles are one wave of long
+// units, the attention units 1.6 waves of short ones).  Sharing one grid
+// overlaps the tails, and the longer kind of unit goes first so that the
+// shorter kind fills the grid's end: the phase-2 tiles at FLUX, the attention
+// units (8316 keys each) at HunyuanVideo.
 //
 // Both bodies are the single-kernel ones (same tiles, same order of sums), so
 // the fused step gives bit-identical results to the two separate calls.
@@ -21,13 +21,17 @@ namespace {
 
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
-// blockIdx.x < g2: phase-2 unit blockIdx.x of xcd_grid(ntn * nb) units.
-// Otherwise: attention unit blockIdx.x - g2.  g2 is a multiple of 8, so both
-// bodies keep their own unit -> XCD mapping (unit id mod 8).  F8W: the phase-2
-// tiles run the fp8 second product (fp8 D from phase 1, fp8 W2 rows).
+// With ga_first == 0: blockIdx.x < g2 is phase-2 unit blockIdx.x of
+// xcd_grid(ntn * nb) units, and the rest are attention units.  With
+// ga_first > 0 (the attention units are the longer ones): the first ga_first
+// workgroups (the heads * nb attention units, rounded up to a multiple of 8)
+// are attention units and the rest phase-2 units, so the short phase-2 tiles
+// fill the grid's tail.  g2 and ga_first are multiples of 8, so both bodies
+// keep their own unit -> XCD mapping (unit id mod 8).  F8W: the phase-2 tiles
+// run the fp8 second product (fp8 D from phase 1, fp8 W2 rows).
 template <int BN, bool F8W>
 __global__ __launch_bounds__(256, 2) void sparse_step_fused(
-    int g2, const uint16_t* __restrict__ dsrc, const uint16_t* __restrict__ w2, const uint8_t* __restrict__ w2f8,
+    int g2, int ga_first, const uint16_t* __restrict__ dsrc, const uint16_t* __restrict__ w2, const uint8_t* __restrict__ w2f8,
     const uint8_t* __restrict__ w2s, const int32_t* __restrict__ midx, float* __restrict__ y, int64_t n, int d, int h,
     int k, int kp, const uint16_t* __restrict__ q, const uint16_t* __restrict__ kx, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ aidx, const float* __restrict__ m, const float* __restrict__ num,
@@ -40,15 +44,19 @@ __global__ __launch_bounds__(256, 2) void sparse_step_fused(
   __shared__ float sDenRest[kRowBlock];
   static_assert(AttnSparseLds::kIds == 8 * 32, "id ring size");
   const int bid = blockIdx.x;
-  if (bid < g2) {
+  const bool phase2 = ga_first > 0 ? bid >= ga_first : bid < g2;
+  if (phase2) {
+    const int lin = ga_first > 0 ? bid - ga_first : bid;
     if constexpr (F8W)
-      gemm2_rows_body_f8<BN>(bid, smem, reinterpret_cast<int(*)[64]>(sIdx), (const unsigned char*)dsrc, w2f8, w2s,
+      gemm2_rows_body_f8<BN>(lin, smem, reinterpret_cast<int(*)[64]>(sIdx), (const unsigned char*)dsrc, w2f8, w2s,
                              midx, y, n, d, h, k, kp);
     else
-      gemm2_rows_body<BN>(bid, smem, reinterpret_cast<int(*)[32]>(sIdx), dsrc, w2, midx, y, n, d, h, k, kp);
+      gemm2_rows_body<BN>(lin, smem, reinterpret_cast<int(*)[32]>(sIdx), dsrc, w2, midx, y, n, d, h, k, kp);
   } else {
+    const int lin = ga_first > 0 ? bid : bid - g2;
+    if (lin >= (int)row_blocks(na) * heads) return;   // padding up to a multiple of 8
     // The sparse (non-refresh) body only reads num and den.
-    attn_sparse_body<false>(bid - g2, smem, reinterpret_cast<int(*)[32]>(sIdx), sDen, sDenRest, q, kx, v, aidx, m,
+    attn_sparse_body<false>(lin, smem, reinterpret_cast<int(*)[32]>(sIdx), sDen, sDenRest, q, kx, v, aidx, m,
                             const_cast<float*>(num), const_cast<float*>(den), o, na, heads, kk, scale);
   }
 }
@@ -153,13 +161,20 @@ hipError_t launch_sparse_step(const uint16_t* x, const uint16_t* w1t, const floa
     g2 = xcd_grid(d / bn * (int)row_blocks(n));
   }
   const int ga = (int)(row_blocks(na) * heads);
-  const dim3 grid((unsigned)(g2 + ga));
+  // Longest units first: the attention units lead when each streams more
+  // operand bytes through LDS than a phase-2 tile (ceil(kk/32) chunks of
+  // 16 KB against the tile's K-chunks of D and W2 rows).
+  const int64_t attn_bytes = (int64_t)((kk + 31) / 32) * 16384;
+  const int64_t g2_bytes = f8w ? (int64_t)(kp / 64) * (kRowBlock * 64 + 64 * bn)
+                               : (int64_t)(kp / 32) * (kRowBlock * 64 + 32 * bn * 2);
+  const int ga_first = (g2 > 0 && ga > 0 && attn_bytes > g2_bytes) ? xcd_grid(ga) : 0;
+  const dim3 grid((unsigned)(ga_first > 0 ? ga_first + g2 : g2 + ga));
   timing_before(K_SPARSE_STEP_FUSED, s);
   const uint8_t* w2f8 = f8w ? f8w->w : nullptr;
   const uint8_t* w2s = f8w ? f8w->w_scale : nullptr;
 #define FUSED_LAUNCH(BN_, F8W_)                                                                                      \
-  hipLaunchKernelGGL((sparse_step_fused<BN_, F8W_>), grid, dim3(256), 0, s, g2, dbuf, w2, w2f8, w2s, midx, y, n, d, h, \
-                     k, kp, q, kx, v, aidx, m, num, den, o, na, heads, kk, scale)
+  hipLaunchKernelGGL((sparse_step_fused<BN_, F8W_>), grid, dim3(256), 0, s, g2, ga_first, dbuf, w2, w2f8, w2s, midx, \
+                     y, n, d, h, k, kp, q, kx, v, aidx, m, num, den, o, na, heads, kk, scale)
   if (bn == 256) {
     if (f8w)
       FUSED_LAUNCH(256, true);
