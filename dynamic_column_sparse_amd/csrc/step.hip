@@ -75,10 +75,11 @@ union ReidentStepLds {
 
 // The same shared grid with the re-identifying attention step (num, den hold
 // totals; the previous step's q, k, v give the share taken out) in place of
-// the fixed-set one.  The two bodies' LDS overlay each other.
+// the fixed-set one, with the same ordering (ga_first).  The two bodies' LDS
+// overlay each other.
 template <int BN, bool F8W>
 __global__ __launch_bounds__(256, 2) void sparse_step_reident_fused(
-    int g2, const uint16_t* __restrict__ dsrc, const uint16_t* __restrict__ w2, const uint8_t* __restrict__ w2f8,
+    int g2, int ga_first, const uint16_t* __restrict__ dsrc, const uint16_t* __restrict__ w2, const uint8_t* __restrict__ w2f8,
     const uint8_t* __restrict__ w2s, const int32_t* __restrict__ midx, float* __restrict__ y, int64_t n, int d, int h,
     int k, int kp, const uint16_t* __restrict__ q_prev, const uint16_t* __restrict__ k_prev,
     const uint16_t* __restrict__ v_prev, const uint16_t* __restrict__ q, const uint16_t* __restrict__ kx,
@@ -87,16 +88,20 @@ __global__ __launch_bounds__(256, 2) void sparse_step_reident_fused(
     int heads, int kk, float scale) {
   __shared__ __align__(16) ReidentStepLds<BN, F8W> lds;
   const int bid = blockIdx.x;
-  if (bid < g2) {
+  const bool phase2 = ga_first > 0 ? bid >= ga_first : bid < g2;
+  if (phase2) {
+    const int lin = ga_first > 0 ? bid - ga_first : bid;
     if constexpr (F8W)
-      gemm2_rows_body_f8<BN>(bid, lds.g2.ring, reinterpret_cast<int(*)[64]>(lds.g2.ids),
+      gemm2_rows_body_f8<BN>(lin, lds.g2.ring, reinterpret_cast<int(*)[64]>(lds.g2.ids),
                              (const unsigned char*)dsrc, w2f8, w2s, midx, y, n, d, h, k, kp);
     else
-      gemm2_rows_body<BN>(bid, lds.g2.ring, reinterpret_cast<int(*)[32]>(lds.g2.ids), dsrc, w2, midx, y, n, d, h, k,
+      gemm2_rows_body<BN>(lin, lds.g2.ring, reinterpret_cast<int(*)[32]>(lds.g2.ids), dsrc, w2, midx, y, n, d, h, k,
                           kp);
   } else {
-    attn_reident_body(bid - g2, lds.at, q_prev, k_prev, v_prev, q, kx, v, aidx, m, num, den, ascore, o, na, heads,
-                      kk, scale);
+    const int lin = ga_first > 0 ? bid : bid - g2;
+    if (lin >= (int)row_blocks(na) * heads) return;   // padding up to a multiple of 8
+    attn_reident_body(lin, lds.at, q_prev, k_prev, v_prev, q, kx, v, aidx, m, num, den, ascore, o, na, heads, kk,
+                      scale);
   }
 }
 
@@ -120,14 +125,20 @@ hipError_t launch_sparse_step_reident(const uint16_t* x, const uint16_t* w1t, co
     g2 = xcd_grid(d / bn * (int)row_blocks(n));
   }
   const int ga = (int)(row_blocks(na) * heads);
-  const dim3 grid((unsigned)(g2 + ga));
+  // Longest units first (see launch_sparse_step); a re-identifying unit
+  // streams its key chunks twice, once per step's inputs.
+  const int64_t attn_bytes = 2 * (int64_t)((kk + 31) / 32) * 16384;
+  const int64_t g2_bytes = f8w ? (int64_t)(kp / 64) * (kRowBlock * 64 + 64 * bn)
+                               : (int64_t)(kp / 32) * (kRowBlock * 64 + 32 * bn * 2);
+  const int ga_first = (g2 > 0 && ga > 0 && attn_bytes > g2_bytes) ? xcd_grid(ga) : 0;
+  const dim3 grid((unsigned)(ga_first > 0 ? ga_first + g2 : g2 + ga));
   timing_before(K_SPARSE_STEP_REIDENT_FUSED, s);
   const uint8_t* w2f8 = f8w ? f8w->w : nullptr;
   const uint8_t* w2s = f8w ? f8w->w_scale : nullptr;
 #define REID_LAUNCH(BN_, F8W_)                                                                                       \
-  hipLaunchKernelGGL((sparse_step_reident_fused<BN_, F8W_>), grid, dim3(256), 0, s, g2, dbuf, w2, w2f8, w2s, midx, y, \
-                     n, d, h, k, kp, q_prev, k_prev, v_prev, q, kx, v, aidx, m, num, den, ascore, o, na, heads, kk,  \
-                     scale)
+  hipLaunchKernelGGL((sparse_step_reident_fused<BN_, F8W_>), grid, dim3(256), 0, s, g2, ga_first, dbuf, w2, w2f8,   \
+                     w2s, midx, y, n, d, h, k, kp, q_prev, k_prev, v_prev, q, kx, v, aidx, m, num, den, ascore, o,   \
+                     na, heads, kk, scale)
   if (bn == 256) {
     if (f8w)
       REID_LAUNCH(256, true);
