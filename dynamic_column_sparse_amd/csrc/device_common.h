@@ -46,6 +46,11 @@ __device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c) {
 __device__ __forceinline__ f32x16_t mfma32h(f16x8_t a, f16x8_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
+// 16x16x32 fp16 product: lane l holds A[l%16][8*(l/16) .. +7] and
+// B[8*(l/16) .. +7][l%16]; the result D[4*(l/16) + e][l%16] is element e.
+__device__ __forceinline__ f32x4_t mfma16h(f16x8_t a, f16x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
 
 // Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
 // lane i receives element i%4 of the 4-element vector read by lane 4e + i/4, for
