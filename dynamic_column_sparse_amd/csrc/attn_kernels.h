@@ -268,31 +268,11 @@ __global__ __launch_bounds__(256, 4) void attn_stats(const uint16_t* __restrict_
 }
 
 // The p tile of one wave for the score products: [32 queries][32 keys] fp16,
-// 64-byte rows, 8-byte unit u of row r stored at unit u ^ ((r / 4) % 8): the 32
-// rows written at one unit then cover all 64 banks once, and the 4 rows x 4
-// units of one transposing read are distinct banks too.
-__device__ __forceinline__ int p_unit(int u, int r) { return u ^ ((r >> 2) & 7); }
-
-// Reads the p tile as the right operand of a 32x32x16 product with the QUERIES
-// as the reduction index: lane l gets key l%32 and queries k0 + (l/32)*8 .. +7
-// in order.
-__device__ __forceinline__ f16x8_t p_operand(const unsigned char* tile, int k0, int lane) {
-  const int G = lane >> 4, i = lane & 15;
-  const int u = (G & 1) * 4 + (i & 3);          // 8-byte unit of keys 4u .. 4u+3
-  const int kr = k0 + (G >> 1) * 8 + (i >> 2);  // query row; the second read is 4 rows on
-  i16x4_t lo = lds_read_tr16((const uint16_t*)(tile + kr * 64 + (p_unit(u, kr) << 3)));
-  i16x4_t hi = lds_read_tr16((const uint16_t*)(tile + (kr + 4) * 64 + (p_unit(u, kr + 4) << 3)));
-  typedef short i16x8_t __attribute__((ext_vector_type(8)));
-  i16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  return __builtin_bit_cast(f16x8_t, v);
-}
-
-// The dense pass's p tile for 16x16x32 score products: the same [32 queries]
-// [32 keys] fp16 rows of 64 bytes, with 8-byte unit u of row r stored at unit
+// rows of 64 bytes, with 8-byte unit u of row r stored at unit
 // u ^ g(r / 4), g(x) = x ^ ((x & 2) << 1).  The 32 rows written at one
 // unit cover all 64 banks once, and the two 16-lane groups of each half of a
 // transposing read (query rows 8 apart) land on opposite halves of the row.
-__device__ __forceinline__ int p_unit16(int u, int r) {
+__device__ __forceinline__ int p_unit(int u, int r) {
   const int x = (r >> 2) & 7;
   return u ^ x ^ ((x & 2) << 1);
 }
@@ -300,12 +280,12 @@ __device__ __forceinline__ int p_unit16(int u, int r) {
 // Reads the p tile as the right operand of a 16x16x32 product with the QUERIES
 // as the reduction index: lane l gets key 16*half + l%16 and queries
 // 8*(l/16) .. +7 in order.
-__device__ __forceinline__ f16x8_t p_operand16(const unsigned char* tile, int half, int lane) {
+__device__ __forceinline__ f16x8_t p_operand(const unsigned char* tile, int half, int lane) {
   const int G = lane >> 4, i = lane & 15;
   const int u = half * 4 + (i & 3);   // 8-byte unit of keys 4u .. 4u+3
   const int kr = G * 8 + (i >> 2);    // query row; the second read is 4 rows on
-  i16x4_t lo = lds_read_tr16((const uint16_t*)(tile + kr * 64 + (p_unit16(u, kr) << 3)));
-  i16x4_t hi = lds_read_tr16((const uint16_t*)(tile + (kr + 4) * 64 + (p_unit16(u, kr + 4) << 3)));
+  i16x4_t lo = lds_read_tr16((const uint16_t*)(tile + kr * 64 + (p_unit(u, kr) << 3)));
+  i16x4_t hi = lds_read_tr16((const uint16_t*)(tile + (kr + 4) * 64 + (p_unit(u, kr + 4) << 3)));
   typedef short i16x8_t __attribute__((ext_vector_type(8)));
   i16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   return __builtin_bit_cast(f16x8_t, v);
@@ -424,7 +404,7 @@ __global__ __launch_bounds__(256, 2) void attn_dense(const uint16_t* __restrict_
     barrier();
   }
   // Left operand of the score products: every row holds 2^15/l of the wave's
-  // 32 queries, in the order p_operand16 delivers them.
+  // 32 queries, in the order p_operand delivers them.
   f16x8_t wq;
   {
     const float* w = sInv + wave * 32 + (lane >> 4) * 8;
@@ -483,9 +463,9 @@ __global__ __launch_bounds__(256, 2) void attn_dense(const uint16_t* __restrict_
                                   pack2(p[hf * 8 + 4], p[hf * 8 + 5]), pack2(p[hf * 8 + 6], p[hf * 8 + 7]));
       // This lane's keys 8*(2hf) + 4*ph .. +3 and 8*(2hf+1) + 4*ph .. +3 of query
       // pq, in fp16 for the score products.
-      *(uint2*)(pw + pq * 64 + (p_unit16(4 * hf + ph, pq) << 3)) =
+      *(uint2*)(pw + pq * 64 + (p_unit(4 * hf + ph, pq) << 3)) =
           make_uint2(pack2h(p[hf * 8 + 0], p[hf * 8 + 1]), pack2h(p[hf * 8 + 2], p[hf * 8 + 3]));
-      *(uint2*)(pw + pq * 64 + (p_unit16(4 * hf + 2 + ph, pq) << 3)) =
+      *(uint2*)(pw + pq * 64 + (p_unit(4 * hf + 2 + ph, pq) << 3)) =
           make_uint2(pack2h(p[hf * 8 + 4], p[hf * 8 + 5]), pack2h(p[hf * 8 + 6], p[hf * 8 + 7]));
       const bf16x8_t pa = __builtin_bit_cast(bf16x8_t, pk);
 #pragma unroll
@@ -497,8 +477,8 @@ __global__ __launch_bounds__(256, 2) void attn_dense(const uint16_t* __restrict_
     // Keys 0..15 and 16..31 of the chunk, each summed over the wave's 32
     // queries by one 16x16x32 product (every output row is the same).
     const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
-    const f32x4_t sc0 = mfma16h(wq, p_operand16(pw, 0, lane), z);
-    const f32x4_t sc1 = mfma16h(wq, p_operand16(pw, 1, lane), z);
+    const f32x4_t sc0 = mfma16h(wq, p_operand(pw, 0, lane), z);
+    const f32x4_t sc1 = mfma16h(wq, p_operand(pw, 1, lane), z);
     if (lane < 16) {
       sSc[(t / G) & 1][t % G][wave][lane] = sc0[0] * (1.f / 32768.f);
       sSc[(t / G) & 1][t % G][wave][16 + lane] = sc1[0] * (1.f / 32768.f);
@@ -1048,13 +1028,12 @@ __device__ __forceinline__ void attn_reident_body(
     // in the order p_operand delivers the queries; written and read back by
     // the same wave.
     if (lane < 32) sInv[qi] = qok ? 1.f / drow : 0.f;
-    f16x8_t wq[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const float* w = sInv + wave * 32 + kb * 16 + (lane >> 5) * 8;
+    f16x8_t wq;
+    {
+      const float* w = sInv + wave * 32 + (lane >> 4) * 8;
       const uint4 pk = make_uint4(pack2h(w[0] * kW, w[1] * kW), pack2h(w[2] * kW, w[3] * kW),
                                   pack2h(w[4] * kW, w[5] * kW), pack2h(w[6] * kW, w[7] * kW));
-      wq[kb] = __builtin_bit_cast(f16x8_t, pk);
+      wq = __builtin_bit_cast(f16x8_t, pk);
     }
     const float sl2 = scale * 1.4426950408889634f, ml2 = mrow * 1.4426950408889634f;
     f32x16_t sacc = chunk_scores(smem, qf, lane);
@@ -1144,12 +1123,13 @@ __device__ __forceinline__ void attn_reident_body(
         }
       }
       if (cur_new) {
-        f32x16_t sc;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sc[r] = 0.f;
-        sc = mfma32h(wq[0], p_operand(pw, 0, lane), sc);
-        sc = mfma32h(wq[1], p_operand(pw, 16, lane), sc);
-        if (lane < 32) sSc[c & 1][wave][lane] = sc[0] * (1.f / kW);
+        const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+        const f32x4_t sc0 = mfma16h(wq, p_operand(pw, 0, lane), z);
+        const f32x4_t sc1 = mfma16h(wq, p_operand(pw, 1, lane), z);
+        if (lane < 16) {
+          sSc[c & 1][wave][lane] = sc0[0] * (1.f / kW);
+          sSc[c & 1][wave][16 + lane] = sc1[0] * (1.f / kW);
+        }
       }
       if (steady || t + 1 < KT) {
         sacc = snext;
