@@ -185,7 +185,13 @@ __global__ __launch_bounds__(256, 4) void attn_stats(const uint16_t* __restrict_
     barrier();
   }
   f32x16_t sa = chunk_scores(smem, qf, lane), sb;
-  float mr = -INFINITY, lr = 0.f;
+  // mr: the lane's running maximum of raw scores (exact).  lr: the sum of
+  // 2^(s*sl2 - ms2) over the lane's keys so far, where the base ms2 moves only
+  // when the scaled running maximum passes it by more than kLazy, so every
+  // exponent stays <= kLazy (terms <= 2^kLazy, far inside fp32) and rescaling
+  // lr (one more exp2) is rare instead of once per chunk.
+  constexpr float kLazy = 8.f;
+  float mr = -INFINITY, lr = 0.f, ms2 = -INFINITY;
   // Iteration t issues chunk t+1's score products into `nxt`, then folds chunk
   // t (in `cur`) into the running (m, l).  Steady iterations issue a full
   // chunk (t + NS - 1 < KF); their own chunk is full too.  SLOT >= 0 is t % NS
@@ -214,27 +220,36 @@ __global__ __launch_bounds__(256, 4) void attn_stats(const uint16_t* __restrict_
       nxt = chunk_scores(smem + s1 * kTile, qf, lane);
     }
     const bool full = steady || t * kSK + kSK <= nn;
-    float mloc = -INFINITY;
+    float mloc;
+    if (steady) {
+      mloc = cur[0];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const bool ok = full || t * kSK + acc_key(r, lane) < nn;
-      mloc = ok ? fmaxf(mloc, cur[r]) : mloc;
+      for (int r = 1; r < 16; ++r) mloc = fmaxf(mloc, cur[r]);
+    } else {
+      mloc = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const bool ok = full || t * kSK + acc_key(r, lane) < nn;
+        mloc = ok ? fmaxf(mloc, cur[r]) : mloc;
+      }
     }
-    const float mnew = fmaxf(mr, mloc);
-    const float ml2 = mnew * sl2;
+    // A lane whose keys so far are all masked (only when n < 32) keeps
+    // mr = ms2 = -inf and lr = 0: its comparison below is false.
+    mr = fmaxf(mr, mloc);
+    const float mr2 = mr * sl2;
+    if (__ballot(mr2 > ms2 + kLazy)) {
+      const bool up = mr2 > ms2 + kLazy;
+      lr *= up ? __builtin_amdgcn_exp2f(ms2 - mr2) : 1.f;   // 2^-inf = 0 on a lane's first keys
+      ms2 = up ? mr2 : ms2;
+    }
     float sum = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const bool ok = full || t * kSK + acc_key(r, lane) < nn;
-      const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(cur[r], sl2, -ml2));
+      const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(cur[r], sl2, -ms2));
       sum += ok ? e : 0.f;
     }
-    // A lane whose keys so far are all masked (only when n < 32) keeps (-inf, 0).
-    const float resc = mr > -INFINITY ? __builtin_amdgcn_exp2f(__builtin_fmaf(mr, sl2, -ml2)) : 0.f;
-    if (steady || mnew > -INFINITY) {
-      lr = __builtin_fmaf(lr, resc, sum);
-      mr = mnew;
-    }
+    lr += sum;
   };
   static_assert(NS == 4, "the steady loop is unrolled by the ring size");
   using Dyn = std::integral_constant<int, -1>;
@@ -256,11 +271,12 @@ __global__ __launch_bounds__(256, 4) void attn_stats(const uint16_t* __restrict_
     ++t;
   }
 
-  // Lanes l and l^32 hold the same query (different keys).
-  const float m2 = __shfl_xor(mr, 32), l2 = __shfl_xor(lr, 32);
+  // Lanes l and l^32 hold the same query (different keys).  Each lane's sum
+  // is taken from its base ms2 to the row maximum M.
+  const float m2 = __shfl_xor(mr, 32), l2 = __shfl_xor(lr, 32), s2 = __shfl_xor(ms2, 32);
   const float M = fmaxf(mr, m2), M2 = M * sl2;
-  const float la = mr > -INFINITY ? lr * __builtin_amdgcn_exp2f(__builtin_fmaf(mr, sl2, -M2)) : 0.f;
-  const float lb = m2 > -INFINITY ? l2 * __builtin_amdgcn_exp2f(__builtin_fmaf(m2, sl2, -M2)) : 0.f;
+  const float la = mr > -INFINITY ? lr * __builtin_amdgcn_exp2f(ms2 - M2) : 0.f;
+  const float lb = m2 > -INFINITY ? l2 * __builtin_amdgcn_exp2f(s2 - M2) : 0.f;
   if (lane < 32 && qi < rows) {
     m_out[hoff + r0 + qi] = M * as;
     l_out[hoff + r0 + qi] = la + lb;
