@@ -293,3 +293,41 @@ def test_attention_no_keys_returns_cached_output(L):
     assert torch.equal(att.num.view(torch.int32), num_b.view(torch.int32))
     assert torch.equal(att.den.view(torch.int32), den_b.view(torch.int32))
     assert torch.equal(att.o.view(torch.int32), o_ref.view(torch.int32))
+
+
+@pytest.mark.parametrize("order", ["rising", "falling", "wide"])
+def test_attention_statistics_over_wide_score_ranges(L, order):
+    """Row max and denominator of the refresh when the scores span a wide range
+    along the keys: rising scores move the running maximum on nearly every
+    chunk (the statistics pass re-bases its sum many times), falling scores
+    never after the first chunk, and wide Gaussian scores (inputs x 6) put
+    single keys far above the rest.  m, den and the key-mass score are checked
+    against the oracle per query block, on 1000 tokens (7 full blocks and a
+    104-row tail) and two heads."""
+    from dynamic_column_sparse_amd.layers import AttnDelta
+    n, H = 1000, 2
+    g = np.random.default_rng(7)
+    q = 0.5 + 0.05 * g.standard_normal((H, n, 128))
+    ramp = np.arange(n, dtype=np.float64)[None, :, None] / 40.0
+    if order == "rising":
+        k = ramp * (1.0 + 0.05 * g.standard_normal((H, n, 128)))
+    elif order == "falling":
+        k = ramp[:, ::-1] * (1.0 + 0.05 * g.standard_normal((H, n, 128)))
+    else:
+        q = 6.0 * g.standard_normal((H, n, 128))
+        k = 6.0 * g.standard_normal((H, n, 128))
+    v = g.standard_normal((H, n, 128))
+    qb, kb, vb = (syn.f32_to_bf16_bits(a.astype(np.float32)) for a in (q, k, v))
+    att = AttnDelta(n, H, 64, "cuda")
+    att.dense(up_bf16(qb), up_bf16(kb), up_bf16(vb))
+    torch.cuda.synchronize()
+    m_g, den_g, sc_g = att.m.cpu().numpy(), att.den.cpu().numpy(), att.score.cpu().numpy()
+    sizes = [min(n, (b + 1) * 128) - b * 128 for b in range((n + 127) // 128)]
+    for hh in range(H):
+        q0, k0, v0 = (oracle.from_bf16_bits(a[hh]) for a in (qb, kb, vb))
+        m, den, _, _, score = oracle.attn_dense(q0, k0, v0, SCALE)
+        np.testing.assert_allclose(m_g[hh], m, rtol=1e-5, atol=1e-5)
+        e, i, _ = worst_block_error(den_g[hh][:, None], den[:, None], sizes)
+        assert e < 1e-3, f"{order} head {hh} block {i}: den rel-F {e:.2e}"
+        e_s = oracle.rel_frobenius(sc_g[hh], score)
+        assert e_s < 1e-3, f"{order} head {hh}: score rel-F {e_s:.2e}"
