@@ -623,6 +623,14 @@ def main():
                 "distinct_inputs": D}
         log(f"loop of {T} steps: {total_ms:.1f} ms ({len(dn)} with a refresh, {ncached} cached)")
 
+    # The outputs the timed steps left behind must be finite: a NaN or an Inf in
+    # y or o marks a broken step, whatever its speed (checked after the timing).
+    finite = {}
+    if mlp:
+        finite["y"] = bool(torch.isfinite(mlp.y).all().item())
+    if att:
+        finite["o"] = bool(torch.isfinite(att.o).all().item())
+
     fl = flops_mlp(w) + flops_attn(w, args.attn_reident)
     tflops = fl / (ms_per_step * 1e-3) / 1e12
 
@@ -680,6 +688,7 @@ def main():
         "roofline": roof,
         "kernels": table,
         "loop": loop,
+        "outputs_finite": finite,
         "source_digest": source_digest(),
     }
     if not args.no_cpu_baseline:
@@ -687,6 +696,9 @@ def main():
         out["cpu_baseline"] = cpu_baseline(w, host, args.cpu_budget, args.attn_reident, args.fp8, args.fp8_w2,
                                           args.mlp_rescore)
     print(json.dumps(out), flush=True)
+    if not all(finite.values()):
+        print(f"bench.py: non-finite values in the step outputs {finite}", file=sys.stderr)
+        sys.exit(3)
 
 
 if __name__ == "__main__":
