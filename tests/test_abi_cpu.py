@@ -313,3 +313,22 @@ def test_noalloc_entry_checks_before_any_hip_call(L):
     assert _code(L, f, lay, FAKE, FAKE, 10, FAKE + 4, None, stream=0) == 4    # y misaligned
     assert _code(L, f, _mlp(L, a_cache=None), FAKE, FAKE, 10, FAKE, None, stream=0) == 1
     assert _code(L, f, lay, FAKE, None, 0, FAKE, None, stream=0) == 0         # k = 0: no-op, nothing enqueued
+
+
+def test_plain_c_caller_compiles_links_and_runs(tmp_path):
+    """The header is valid C99 (warnings are errors) and a C program links the
+    library and gets the documented results from the calls that need no GPU
+    (tests/c/abi_client.c)."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    exe = str(tmp_path / "abi_client")
+    libdir = os.path.dirname(LIBSO)
+    r = subprocess.run([cc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic", "-I", os.path.join(ROOT, "include"),
+                        os.path.join(ROOT, "tests", "c", "abi_client.c"), "-o", exe, "-L", libdir, "-lchipmunk",
+                        f"-Wl,-rpath,{libdir}"], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-3000:]
+    r = subprocess.run([exe, source_digest()], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0 and r.stdout.strip() == "ok", (r.stdout, r.stderr[-3000:])
