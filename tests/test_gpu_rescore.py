@@ -2,7 +2,8 @@
 
 Every sparse step rewrites the scores of the units it recomputed with that
 step's column L1 of D, so the next identification can pick a different S.
-  * Against the oracle over several steps: the GPU's index sets equal the
+  * Against the oracle over several steps (small, FLUX.1-dev and HunyuanVideo
+    shapes, the large ones on seeded blocks and the tail block): the GPU's index sets equal the
     oracle's top-k of the GPU's own score bits (bit-exact); the GPU's scores
     after each step equal the oracle's rescored scores within 1e-3 (rel.
     Frobenius; the sums run in a different order); y and the cache within the
@@ -104,3 +105,11 @@ def test_rescore_shared_grid_matches_separate_calls(gpu_lib):
             if a.dtype == torch.float32:
                 a, b = a.view(torch.int32), b.view(torch.int32)
             assert torch.equal(a, b), f"step {t}: {name}"
+
+
+def test_rescore_hunyuan_sampled(gpu_lib):
+    # HunyuanVideo MLP shape (118 800 tokens, 16-row tail block, keep 860 of
+    # 12 288 units), seeded blocks and the tail followed by the oracle.
+    n = 118800
+    blocks = _sample_blocks(929, 3, 41, n)
+    _loop(n, 3072, 12288, 860, steps=3, blocks=blocks, seed=0)
