@@ -101,7 +101,7 @@ int check_bf16_in(const void* p, const char* name) {
   return CHIPMUNK_OK;
 }
 
-// D tiles [nb][128][kp], row-major per block (kp = k rounded up to 64).
+// D tiles [nb][kp/32][128][32] bf16 (kp = k rounded up to 64).
 size_t sparse_mlp_ws(int64_t n, int32_t k) {
   return (size_t)chipmunk::row_blocks(n) * (size_t)chipmunk::padded_k(k) * chipmunk::kRowBlock * sizeof(uint16_t);
 }

@@ -14,9 +14,9 @@
 //   dense:  D = a_new; score[b][j] = sum over real rows |a_new - a_cache|;
 //           a_new -> cache.
 // Phase 2 (mlp_gemm2): one workgroup per (block b, BN output columns); the
-// reduction runs over the block's gathered hidden units: D tile rows
-// ([nb][kp][128], or the activation cache itself for the dense step) times the
-// gathered W2 rows ([h][d], contiguous per unit).  Both tiles are copied into
+// reduction runs over the block's hidden units: the activation cache
+// ([nb][h][128]) of the dense step times the W2 rows ([h][d], contiguous per
+// unit).  (The sparse step's gathered product is gemm2_rows_body below.)  Both tiles are copied into
 // LDS as they lie in memory ([unit][column]) by direct global->LDS loads and
 // read back with the transposing LDS read, so no register staging is needed.
 // y rows are read, added to and written once (no atomics: every output element
@@ -323,8 +323,9 @@ __global__ __launch_bounds__(256, 2) void mlp_gemm1(const void* __restrict__ xv,
     }
   }
   if (!DENSE) {
-    // D leaves row-major ([block][128 rows][kp]) so phase 2 reads it as a plain
-    // K-contiguous operand.  A 16-lane group transposes 8 units x 16 rows out of
+    // D leaves K-contiguous in 32-unit chunks ([block][kp/32][128 rows][32];
+    // fp8: row-major [block][128 rows][kp]) so phase 2 reads it as a plain
+    // K-contiguous operand, each chunk's tile as 8 KB in one piece.  A 16-lane group transposes 8 units x 16 rows out of
     // the [unit][row] tile with two transposing reads (units u..u+3, u+4..u+7):
     // lane j points at unit row u + j/4, tokens 4(j%4)..+3 of its 16-row block,
     // and receives the 4 units of token j.  Units k..kp of the tile are zero
@@ -362,7 +363,9 @@ __global__ __launch_bounds__(256, 2) void mlp_gemm1(const void* __restrict__ xv,
           }
         }
       } else {
-        if (p < kp) *(uint4*)(dbuf + ((int64_t)b * BM + m) * kp + p) = v;
+        // [block][kp/32][128 rows][32 units]: a wave's four groups write one
+        // row's 64 bytes each for 16 rows, 1 KB contiguous.
+        if (p < kp) *(uint4*)(dbuf + (int64_t)b * BM * kp + (p >> 5) * (BM * 32) + m * 32 + (p & 31)) = v;
       }
     }
   }
@@ -561,8 +564,8 @@ __global__ __launch_bounds__(256, 2) void mlp_gemm2(const uint16_t* __restrict__
   }
 }
 
-// Sparse phase 2 over row-major D tiles ([block][128 rows][kp], written by the
-// sparse phase 1).  Four waves side by side (1x4): each wave owns all 128 rows
+// Sparse phase 2 over the D tiles ([block][kp/32][128 rows][32], written by
+// the sparse phase 1: chunk t of a block is 8 KB in one piece).  Four waves side by side (1x4): each wave owns all 128 rows
 // and BN/4 output columns, so per 16-deep K-substep it reads four D fragments
 // with plain 16-byte LDS reads and only BN/128 W2 fragments with the (slower)
 // transposing read.  32-deep K-chunks in a 3-stage ring (72 KB) leave room for
@@ -620,7 +623,7 @@ __device__ __forceinline__ void gemm2_rows_body(int lin, unsigned char* smem, in
 #pragma unroll
   for (int i = 0; i < D_INS; ++i) {
     const int r = (wave * D_INS + i) * D_RPI + d_lr;
-    dsrc_l[i] = dblk + (int64_t)r * kp + ((d_pc ^ swz4(r)) << 3);
+    dsrc_l[i] = dblk + r * BK + ((d_pc ^ swz4(r)) << 3);
   }
   int w_row[W_INS], w_off[W_INS];
 #pragma unroll
@@ -647,7 +650,7 @@ __device__ __forceinline__ void gemm2_rows_body(int lin, unsigned char* smem, in
   {                                                                                         \
     const uint32_t st_ = smem_lds + (buf_) * STAGE;                                         \
     _Pragma("unroll") for (int i = 0; i < D_INS; ++i)                                       \
-        dma16_at(dsrc_l[i] + (kt_) * BK, st_ + (wave * D_INS + i) * 1024);                  \
+        dma16_at(dsrc_l[i] + (int64_t)(kt_) * BK * BM, st_ + (wave * D_INS + i) * 1024);    \
     _Pragma("unroll") for (int i = 0; i < W_INS; ++i)                                       \
         dma16_at(w2 + (int64_t)ids_[i] * d + n0 + w_off[i], st_ + D_BYTES + (wave * W_INS + i) * 1024); \
   }

@@ -228,9 +228,10 @@ int chipmunk_check_index_sets(const int32_t* idx, int64_t rows, int32_t k, int64
  * order, for chipmunk_cache_writeback) leaving the cache unchanged.
  * x [n][d] bf16, idx [nb][k] int32, y [n][d] fp32.  0 <= k <= h; k = 0 leaves
  * every buffer bit-unchanged.  ws must hold chipmunk_workspace_bytes(
- * CHIPMUNK_OP_SPARSE_MLP, n, d, h, k) bytes: the D tiles, [nb][128][kp] bf16
- * (row-major per block: token row, then the block's kept units in idx order;
- * kp = k rounded up to 64, units past k are written as zero); for a
+ * CHIPMUNK_OP_SPARSE_MLP, n, d, h, k) bytes: the D tiles, [nb][kp/32][128][32]
+ * bf16 (per block, 32-unit chunks of the kept units in idx order, each chunk
+ * token row by token row; kp = k rounded up to 64, units past k are written as
+ * zero); for a
  * CHIPMUNK_MLP_FP8 layer, chipmunk_workspace_bytes(CHIPMUNK_OP_SPARSE_MLP_FP8,
  * n, d, h, k) bytes: the D tiles, then the fp8 copy of x. */
 int chipmunk_sparse_mlp_delta(const chipmunk_mlp* layer, const uint16_t* x, const int32_t* idx,
