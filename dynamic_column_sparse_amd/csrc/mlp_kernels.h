@@ -51,7 +51,7 @@ constexpr int kGroupTiles = MLP_GROUP_TILES;   // column tiles of one row block 
 // register for the whole loop; the products come out scaled.
 //
 // FD (sparse only): D leaves as e4m3 codes for the fp8 second product instead
-// of bf16: dbuf holds [nb][128][kp] codes, followed by one E8M0 scale byte per
+// of bf16: dbuf holds [nb][kp/64][128][64] codes, followed by one E8M0 scale byte per
 // (row, 32 consecutive units), stored per 64-unit chunk as [nb][kp/64][128][2]
 // so that the second product streams a chunk's scales with its codes.  D is
 // first rounded to bf16, as the bf16 path stores it.
@@ -323,9 +323,10 @@ __global__ __launch_bounds__(256, 2) void mlp_gemm1(const void* __restrict__ xv,
     }
   }
   if (!DENSE) {
-    // D leaves K-contiguous in 32-unit chunks ([block][kp/32][128 rows][32];
-    // fp8: row-major [block][128 rows][kp]) so phase 2 reads it as a plain
-    // K-contiguous operand, each chunk's tile as 8 KB in one piece.  A 16-lane group transposes 8 units x 16 rows out of
+    // D leaves K-contiguous in chunks of one phase-2 K-step ([block][kp/32]
+    // [128 rows][32] bf16; fp8 codes [block][kp/64][128 rows][64]) so phase 2
+    // reads it as a plain K-contiguous operand, each chunk's tile as 8 KB in
+    // one piece.  A 16-lane group transposes 8 units x 16 rows out of
     // the [unit][row] tile with two transposing reads (units u..u+3, u+4..u+7):
     // lane j points at unit row u + j/4, tokens 4(j%4)..+3 of its 16-row block,
     // and receives the 4 units of token j.  Units k..kp of the tile are zero
@@ -356,7 +357,7 @@ __global__ __launch_bounds__(256, 2) void mlp_gemm1(const void* __restrict__ xv,
         const int e = fp8_exponent(mx);
         if (p < kp) {
           unsigned char* d8 = (unsigned char*)dbuf;
-          *(uint2*)(d8 + ((int64_t)b * BM + m) * kp + p) = bf16x8_to_fp8(v, e);
+          *(uint2*)(d8 + (int64_t)b * BM * kp + (p >> 6) * (BM * 64) + m * 64 + (p & 63)) = bf16x8_to_fp8(v, e);
           if (grp == 0) {
             unsigned char* dsc = d8 + (int64_t)nb * BM * kp;
             dsc[(((int64_t)b * (kp / 64) + p / 64) * BM + m) * 2 + ((p >> 5) & 1)] = (unsigned char)(127 + e);
@@ -830,7 +831,7 @@ __device__ __forceinline__ void gemm2_rows_body_f8(int lin, unsigned char* smem,
 #pragma unroll
   for (int i = 0; i < D_INS; ++i) {
     const int r = (wave * D_INS + i) * D_RPI + d_lr;
-    dsrc_l[i] = dblk + (int64_t)r * kp + ((d_pc ^ swz4(r)) << 4);
+    dsrc_l[i] = dblk + r * BK + ((d_pc ^ swz4(r)) << 4);
   }
   int w_row[W_INS], w_off[W_INS];
 #pragma unroll
@@ -853,7 +854,7 @@ __device__ __forceinline__ void gemm2_rows_body_f8(int lin, unsigned char* smem,
   {                                                                                                 \
     const uint32_t st_ = smem_lds + (buf_) * STAGE;                                                 \
     _Pragma("unroll") for (int i = 0; i < D_INS; ++i)                                               \
-        dma16_at(dsrc_l[i] + (kt_) * BK, st_ + (wave * D_INS + i) * 1024);                          \
+        dma16_at(dsrc_l[i] + (int64_t)(kt_) * BK * BM, st_ + (wave * D_INS + i) * 1024);            \
     _Pragma("unroll") for (int i = 0; i < W_INS; ++i)                                               \
         dma16_at(w2 + (int64_t)ids_[i] * d + w_off[i], st_ + D_BYTES + (wave * W_INS + i) * 1024);  \
     if (lane < 16) dma4_at(sblk + (kt_) * 256 + wave * 64 + lane * 4, st_ + D_BYTES + W_BYTES + wave * 64); \

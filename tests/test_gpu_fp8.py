@@ -194,11 +194,11 @@ def test_quantize_cols_bit_exact(gpu_lib, rows, cols):
 
 def _fp8_d_from_ws(lay, n, kp):
     """(codes [nb,128,kp], scale bytes [nb,128,kp/32]) of the fp8 D the first
-    product left in the workspace ([nb][128][kp] codes, then per 64-unit chunk
-    [nb][kp/64][128][2] scale bytes)."""
+    product left in the workspace (codes in 64-unit chunks [nb][kp/64][128][64],
+    then per 64-unit chunk [nb][kp/64][128][2] scale bytes)."""
     nb = lay.nb
     ws = lay.ws.cpu().numpy()
-    codes = ws[:nb * 128 * kp].reshape(nb, 128, kp)
+    codes = ws[:nb * 128 * kp].reshape(nb, kp // 64, 128, 64).transpose(0, 2, 1, 3).reshape(nb, 128, kp)
     sc = ws[nb * 128 * kp:nb * 128 * kp + nb * (kp // 64) * 256].reshape(nb, kp // 64, 128, 2)
     return codes, sc.transpose(0, 2, 1, 3).reshape(nb, 128, kp // 32)
 
